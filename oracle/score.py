@@ -1,0 +1,229 @@
+"""Scoring steps of the selection path.  Test infrastructure only.
+
+All arithmetic in float64.  Callers round to float32 with
+``numerics.round_to_f32`` when comparing with the GPU's float32 outputs.
+
+Layouts (row-major, last index fastest):
+  window queries   q      [L][Hq][W][D]     (post-RoPE, the last W positions)
+  contiguous keys  k      [L][Hkv][N][D]
+  query memory     M      [L][Hq][D]
+  block queries    q      [S][L][Hq][Wq][D] (pre-RoPE)
+  Mean-K index     mu     [L][Hkv][NB][D]
+"""
+import numpy as np
+
+
+def gqa_group(h, n_q_heads, n_kv_heads):
+    """KV head serving query head ``h`` under grouped-query attention.
+
+    ActKV §7.1 (Algorithm 3 reduces over the query heads of one KV head's
+    group) and IntentKV §4 minimum check 1 (KV heads expanded to the query
+    heads): consecutive blocks of Hq/Hkv query heads share one KV head.
+    """
+    return h // (n_q_heads // n_kv_heads)
+
+
+def _logsumexp(s, allowed):
+    """log sum_j exp(s_j) over allowed j, max-shifted (ActKV §7.1, the LSE)."""
+    neg = np.where(allowed, s, -np.inf)
+    m = np.max(neg, axis=-1, keepdims=True)
+    m_safe = np.where(np.isfinite(m), m, 0.0)
+    tot = np.sum(np.where(allowed, np.exp(neg - m_safe), 0.0), axis=-1, keepdims=True)
+    return (m_safe + np.log(tot))[..., 0]
+
+
+def _reduce(x, how, axis):
+    if how == "sum":
+        return np.sum(x, axis=axis)
+    if how == "mean":
+        return np.mean(x, axis=axis)
+    if how == "max":
+        return np.max(x, axis=axis)
+    raise ValueError(how)
+
+
+def window_scores(q, k, *, scale=None, causal=True, lse_in=None,
+                  head_agg="sum", row_agg="sum"):
+    """Token scores of every cached key against a query window.
+
+    ActKV §2: the attention score of a cached key is its softmax weight,
+    softmax(q . k / sqrt(D)) over the keys the query can see.  ActKV §7.1: the
+    same probabilities are recovered as exp(s - LSE) from a log-sum-exp that
+    the attention pass already produced; ``lse_in`` ([L][Hq][W]) takes that
+    form, otherwise the LSE is computed here over the allowed keys.
+
+    Window row t sits at position N - W + t and (if ``causal``) sees keys
+    j <= N - W + t.  Per unit (layer l, KV head g) the probabilities of the
+    group's query heads are combined with ``head_agg`` and then the window
+    rows with ``row_agg`` (sum/sum is the SnapKV/H2O accumulation named in
+    ActKV §2; max over the GQA group then mean over query tokens is
+    Algorithm 3's form).
+
+    Returns (scores [L][Hkv][N], lse [L][Hq][W]).
+    """
+    q = np.asarray(q, dtype=np.float64)
+    k = np.asarray(k, dtype=np.float64)
+    L, Hq, W, D = q.shape
+    Lk, Hkv, N, Dk = k.shape
+    assert Lk == L and Dk == D and Hq % Hkv == 0 and W <= N
+    G = Hq // Hkv
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    pos = N - W + np.arange(W)
+    if causal:
+        allowed = np.arange(N)[None, :] <= pos[:, None]          # [W][N]
+    else:
+        allowed = np.ones((W, N), dtype=bool)
+    scores = np.zeros((L, Hkv, N))
+    lse_all = np.zeros((L, Hq, W))
+    for l in range(L):
+        for g in range(Hkv):
+            heads = [h for h in range(Hq) if gqa_group(h, Hq, Hkv) == g]
+            s = np.stack([q[l, h] @ k[l, g].T for h in heads]) * scale   # [G][W][N]
+            if lse_in is None:
+                lse = _logsumexp(s, allowed[None])                      # [G][W]
+            else:
+                lse = np.asarray(lse_in, dtype=np.float64)[l, heads]
+            p = np.where(allowed[None], np.exp(s - lse[..., None]), 0.0)
+            scores[l, g] = _reduce(_reduce(p, head_agg, 0), row_agg, 0)
+            lse_all[l, heads] = lse
+    assert len(heads) == G
+    return scores, lse_all
+
+
+def pool1d(a, kind, ksize):
+    """Centred 1-D pooling along the last axis, stride 1, same length.
+
+    ``kind`` "avg": (1/ksize) * sum of the in-range window (out-of-range terms
+    count as zero); "max": maximum over the in-range window.  ``ksize`` odd.
+    """
+    a = np.asarray(a, dtype=np.float64)
+    assert ksize % 2 == 1
+    if kind == "none" or ksize == 1:
+        return a.copy()
+    r = ksize // 2
+    N = a.shape[-1]
+    idx = np.arange(N)
+    if kind == "avg":
+        out = np.zeros_like(a)
+        for off in range(-r, r + 1):
+            src = idx + off
+            ok = (src >= 0) & (src < N)
+            out[..., ok] += a[..., src[ok]]
+        return out / ksize
+    if kind == "max":
+        out = np.full_like(a, -np.inf)
+        for off in range(-r, r + 1):
+            src = idx + off
+            ok = (src >= 0) & (src < N)
+            out[..., ok] = np.maximum(out[..., ok], a[..., src[ok]])
+        return out
+    raise ValueError(kind)
+
+
+def memory_update(m_prev, q_turn, decay=0.9):
+    """One turn of the session query memory.
+
+    IntentKV §4 (memory recurrence) and §7 (unit-norm projection):
+    M_t = normalise(decay * M_{t-1} + Enc(q_t)), normalised to unit L2 norm
+    along the head dimension.  Enc is read as the mean of the turn's query
+    rows per (layer, query head); a zero vector stays zero.
+
+    m_prev: [L][Hq][D]; q_turn: [L][Hq][W][D].  Returns [L][Hq][D].
+    """
+    m_prev = np.asarray(m_prev, dtype=np.float64)
+    e = np.mean(np.asarray(q_turn, dtype=np.float64), axis=2)
+    m = decay * m_prev + e
+    n = np.sqrt(np.sum(m * m, axis=-1, keepdims=True))
+    return np.where(n > 0, m / np.where(n > 0, n, 1.0), 0.0)
+
+
+def history_mask(n, n_sink, n_recent, slot_map=None, dead_slot=None):
+    """Positions that are neither forced (sink, recent) nor dead."""
+    j = np.arange(n)
+    forced = (j < n_sink) | (j >= n - n_recent)
+    alive = np.ones(n, dtype=bool) if slot_map is None else \
+        (np.asarray(slot_map, dtype=np.int64) != dead_slot)
+    return alive & ~forced
+
+
+def memory_scores(m, k_pool, page_table, page_size, n, *, slot_map=None,
+                  dead_slot=None, n_sink=0, n_recent=0, scale=None,
+                  reduce="global"):
+    """Memory-attention rule score over a paged KV pool.
+
+    IntentKV §4 (rule score): for every layer l and query head h,
+    a[l,h,j] = softmax over the history set H of M[l,h] . K[l,g(h),j] / sqrt(D),
+    and rule_j = sum over (l, h) of a[l,h,j].  H excludes the forced set
+    (sink and recent) and positions already redirected to the dead slot
+    (IntentKV §3: eviction is one-way).  Positions outside H score 0.
+
+    m: [L][Hq][D]; k_pool: [L][P][page_size][Hkv][D]; page_table: logical page
+    -> physical page.  ``reduce`` "global" returns [N]; "per_unit" returns
+    [L][Hkv][N] (sum over the group's heads only).
+    """
+    m = np.asarray(m, dtype=np.float64)
+    L, Hq, D = m.shape
+    Hkv = k_pool.shape[3]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    H = history_mask(n, n_sink, n_recent, slot_map, dead_slot)
+    pt = np.asarray(page_table, dtype=np.int64)
+    j = np.arange(n)
+    phys_page = pt[j // page_size]
+    in_page = j % page_size
+    out = np.zeros(n) if reduce == "global" else np.zeros((L, Hkv, n))
+    for l in range(L):
+        kl = np.asarray(k_pool[l], dtype=np.float64)[phys_page, in_page]   # [N][Hkv][D]
+        for h in range(Hq):
+            g = gqa_group(h, Hq, Hkv)
+            s = (kl[:, g, :] @ m[l, h]) * scale
+            lse = _logsumexp(s, H)
+            p = np.where(H, np.exp(s - lse), 0.0)
+            if reduce == "global":
+                out += p
+            else:
+                out[l, g] += p
+    return out
+
+
+def query_reduce(q, n_kv_heads):
+    """q-bar[s,l,g] = sum over window tokens t and heads h of group g of q.
+
+    KVMem (query-conditioned retrieval) scores blocks in the model's own
+    attention space with pre-RoPE queries; summing the queries first is the
+    linearity of the dot product.  q: [S][L][Hq][Wq][D] -> [S][L][Hkv][D].
+    """
+    q = np.asarray(q, dtype=np.float64)
+    S, L, Hq, Wq, D = q.shape
+    out = np.zeros((S, L, n_kv_heads, D))
+    for h in range(Hq):
+        out[:, :, gqa_group(h, Hq, n_kv_heads)] += q[:, :, h].sum(axis=2)
+    return out
+
+
+def block_scores(qbar, mu, scale=None):
+    """Block score s[s,l,g,b] = q-bar[s,l,g] . mu[l,g,b] / sqrt(D).
+
+    KVMem (query-conditioned retrieval): one RoPE-stripped Mean-K vector per
+    (layer, KV head, 32-token block), scored by a dot product with the query.
+    qbar: [S][L][Hkv][D]; mu: [L][Hkv][NB][D].  Returns [S][L][Hkv][NB].
+    """
+    qbar = np.asarray(qbar, dtype=np.float64)
+    mu = np.asarray(mu, dtype=np.float64)
+    D = qbar.shape[-1]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    return np.einsum("slgd,lgbd->slgb", qbar, mu) * scale
+
+
+def residual_score(rule, features, fc1_w, fc1_b, fc2_w, fc2_b, alpha=1.0):
+    """s_j = rule_j + alpha * MLP(features_j) (IntentKV §4, residual).
+
+    A two-layer GELU MLP.  With fc2 initialised to zero the residual is zero
+    and the score is the rule score exactly (IntentKV §4 minimum check 2).
+    """
+    x = np.asarray(features, dtype=np.float64) @ np.asarray(fc1_w, dtype=np.float64).T + fc1_b
+    gelu = 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
+    r = gelu @ np.asarray(fc2_w, dtype=np.float64).T + fc2_b
+    return np.asarray(rule, dtype=np.float64) + alpha * r[..., 0]

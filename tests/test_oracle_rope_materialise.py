@@ -1,0 +1,218 @@
+"""Pins for RoPE, gather, incremental view update, redirect and the dead-slot
+mask (CPU only)."""
+import math
+
+import numpy as np
+import pytest
+
+from oracle import materialise as om
+from oracle import numerics
+from oracle.rope import inv_freq, rope_rotate
+
+
+# ---------------------------------------------------------------- RoPE
+
+def test_rope_d2_theta1_is_rotation_by_p_radians():
+    for p in [0, 1, 2, 7, 100, 12345]:
+        y = rope_rotate(np.array([1.0, 0.0]), p, theta=1.0)
+        np.testing.assert_allclose(y, [math.cos(p), math.sin(p)], atol=1e-12)
+        y = rope_rotate(np.array([0.0, 1.0]), p, theta=1.0)
+        np.testing.assert_allclose(y, [-math.sin(p), math.cos(p)], atol=1e-12)
+
+
+def test_rope_pairs_and_frequencies_d4():
+    # theta = 100, D = 4: inv_freq = (1, 0.1); rotate-half pairs (0,2) and (1,3)
+    np.testing.assert_allclose(inv_freq(4, 100.0), [1.0, 0.1], rtol=1e-15)
+    x = np.array([1.0, 2.0, 3.0, 4.0])
+    p = 3
+    c0, s0, c1, s1 = math.cos(3), math.sin(3), math.cos(0.3), math.sin(0.3)
+    want = [1 * c0 - 3 * s0, 2 * c1 - 4 * s1, 1 * s0 + 3 * c0, 2 * s1 + 4 * c1]
+    np.testing.assert_allclose(rope_rotate(x, p, 100.0), want, atol=1e-12)
+    want_il = [1 * c0 - 2 * s0, 1 * s0 + 2 * c0, 3 * c1 - 4 * s1, 3 * s1 + 4 * c1]
+    np.testing.assert_allclose(rope_rotate(x, p, 100.0, style="interleaved"), want_il, atol=1e-12)
+
+
+def test_rope_partial_rotary_dim_leaves_tail():
+    x = np.arange(1.0, 9.0)
+    y = rope_rotate(x, 5, 1e4, rotary_dim=4)
+    np.testing.assert_array_equal(y[4:], x[4:])
+    np.testing.assert_allclose(y[:4], rope_rotate(x[:4], 5, 1e4), atol=1e-15)
+
+
+def test_rope_identity_norm_composition_relative():
+    r = np.random.default_rng(30)
+    x = r.standard_normal((6, 128))
+    np.testing.assert_array_equal(rope_rotate(x, 0, 1e6), x)
+    for a, b in [(3, 5), (1000, 65000), (123456, 7)]:
+        ya = rope_rotate(x, a, 1e6)
+        np.testing.assert_allclose(np.linalg.norm(ya, axis=1), np.linalg.norm(x, axis=1), rtol=1e-13)
+        np.testing.assert_allclose(rope_rotate(ya, b, 1e6), rope_rotate(x, a + b, 1e6), atol=1e-10)
+        q, k = x[0], x[1]
+        d1 = rope_rotate(q, a, 1e6) @ rope_rotate(k, b, 1e6)
+        d2 = rope_rotate(q, a + 17, 1e6) @ rope_rotate(k, b + 17, 1e6)
+        assert abs(d1 - d2) < 1e-9
+
+
+def _pair_ulp(x):
+    """bf16 ULP of each rotate-half pair's magnitude, per element.
+
+    Rotation mixes a pair's two components, so a rounding error made in one
+    component shows up in the other: bounds are stated against the pair."""
+    h = x.shape[-1] // 2
+    r = np.sqrt(x[..., :h] ** 2 + x[..., h:] ** 2)
+    r = np.concatenate([r, r], axis=-1)
+    return np.ldexp(1.0, np.frexp(r)[1] - 8)
+
+
+# ---------------------------------------------------------------- gather
+
+def test_gather_plain_copies_bit_for_bit():
+    r = np.random.default_rng(31)
+    bt, D, NB = 3, 4, 7
+    sk = numerics.round_to_bf16(r.standard_normal((NB * bt, D)))
+    sv = numerics.round_to_bf16(r.standard_normal((NB * bt, D)))
+    idx = np.array([0, 2, 3, 6])
+    k, v = om.gather_view(sk, sv, idx, bt)
+    for i, b in enumerate(idx):
+        for o in range(bt):
+            assert np.array_equal(k[i * bt + o], sk[b * bt + o])
+            assert np.array_equal(v[i * bt + o], sv[b * bt + o])
+
+
+def test_gather_raw_rerope_equals_baked_at_new_position():
+    # raw K re-rotated at its new slot equals K baked at that position
+    r = np.random.default_rng(32)
+    bt, D, NB = 4, 8, 6
+    raw = numerics.round_to_bf16(r.standard_normal((NB * bt, D)))
+    idx = np.array([1, 4, 5])
+    k, v = om.gather_view(raw, raw, idx, bt, rope="raw", theta=1e6, pos0=10)
+    for i, b in enumerate(idx):
+        for o in range(bt):
+            baked = rope_rotate(raw[b * bt + o], 10 + i * bt + o, 1e6)
+            np.testing.assert_array_equal(k[i * bt + o], numerics.round_to_bf16(baked))
+    np.testing.assert_array_equal(v, raw[(idx[:, None] * bt + np.arange(bt)).ravel()])
+
+
+def test_gather_delta_on_baked_matches_raw_within_two_ulp():
+    r = np.random.default_rng(33)
+    bt, D, NB = 32, 128, 40
+    raw = numerics.round_to_bf16(r.standard_normal((NB * bt, D)))
+    baked = numerics.round_to_bf16(rope_rotate(raw, np.arange(NB * bt), 1e6))
+    idx = np.array([0, 3, 17, 39])
+    k_raw, _ = om.gather_view(raw, raw, idx, bt, rope="raw")
+    k_del, _ = om.gather_view(baked, baked, idx, bt, rope="delta")
+    assert np.all(np.abs(k_del - k_raw) <= 2 * _pair_ulp(k_raw))
+
+
+# ---------------------------------------------------------------- incremental view
+
+def _incremental_case(seed, nb=60, k=12, overlap=6, bt=4, D=8, spare=3):
+    r = np.random.default_rng(seed)
+    raw_k = numerics.round_to_bf16(r.standard_normal((nb, bt, D)))
+    raw_v = numerics.round_to_bf16(r.standard_normal((nb, bt, D)))
+    new_idx = np.sort(r.choice(nb, k, replace=False))
+    outside = np.setdiff1d(np.arange(nb), new_idx)
+    prev_idx = np.sort(np.concatenate([r.choice(new_idx, overlap, replace=False),
+                                       r.choice(outside, k - overlap, replace=False)]))
+    P = k + spare
+    prev_page = r.permutation(P)[:k]
+    pool_k = numerics.round_to_bf16(r.standard_normal((P, bt, D)))
+    pool_v = numerics.round_to_bf16(r.standard_normal((P, bt, D)))
+    o = np.arange(bt)
+    for i, b in enumerate(prev_idx):               # previous view: baked at its old slots
+        pool_k[prev_page[i]] = numerics.round_to_bf16(rope_rotate(raw_k[b], i * bt + o, 1e6))
+        pool_v[prev_page[i]] = raw_v[b]
+    return raw_k, raw_v, new_idx, prev_idx, prev_page, pool_k, pool_v
+
+
+@pytest.mark.parametrize("seed", [40, 41, 42])
+def test_incremental_equals_fresh_build(seed):
+    raw_k, raw_v, new_idx, prev_idx, prev_page, pool_k, pool_v = _incremental_case(seed)
+    bt, D = raw_k.shape[1], raw_k.shape[2]
+    pk, pv, pt, n_miss = om.incremental_view(prev_idx, prev_page, new_idx, pool_k, pool_v,
+                                             raw_k, raw_v, bt, theta=1e6)
+    fk, fv = om.gather_view(raw_k.reshape(-1, D), raw_v.reshape(-1, D), new_idx, bt, rope="raw")
+    view_k = pk[pt].reshape(-1, D)
+    view_v = pv[pt].reshape(-1, D)
+    np.testing.assert_array_equal(view_v, fv)
+    assert np.all(np.abs(view_k - fk) <= 2 * _pair_ulp(fk))
+    hits = np.intersect1d(prev_idx, new_idx)
+    assert n_miss == len(new_idx) - len(hits)
+    assert len(set(pt.tolist())) == len(pt)                       # each page once
+    freed = set(prev_page[~np.isin(prev_idx, new_idx)].tolist())
+    hit_pages = set(prev_page[np.isin(prev_idx, new_idx)].tolist())
+    miss_pages = set(pt[~np.isin(new_idx, prev_idx)].tolist())
+    assert not (hit_pages & freed) and miss_pages == freed        # misses fill freed pages
+    # untouched pages keep their bytes
+    other = np.setdiff1d(np.arange(pool_k.shape[0]), pt)
+    np.testing.assert_array_equal(pk[other], pool_k[other])
+
+
+def test_incremental_unmoved_hit_is_bitwise():
+    raw_k, raw_v, new_idx, prev_idx, prev_page, pool_k, pool_v = _incremental_case(43, overlap=12)
+    pk, pv, pt, n_miss = om.incremental_view(prev_idx, prev_page, new_idx, pool_k, pool_v,
+                                             raw_k, raw_v, raw_k.shape[1])
+    assert n_miss == 0
+    np.testing.assert_array_equal(pk, pool_k)
+    np.testing.assert_array_equal(pv, pool_v)
+
+
+# ---------------------------------------------------------------- redirect and dead slot
+
+def test_redirect_invariants():
+    r = np.random.default_rng(50)
+    N, dead = 64, 999
+    sm = r.permutation(N * 2)[:N]
+    sm[[3, 9]] = dead
+    keep = r.random(N) > 0.5
+    keep[[3]] = True                                   # a kept-but-dead entry stays dead
+    out = om.redirect(sm, keep, dead)
+    np.testing.assert_array_equal(out[keep], sm[keep])
+    assert np.all(out[~keep] == dead)
+    assert out[3] == dead and out[9] == dead
+    np.testing.assert_array_equal(om.redirect(out, keep, dead), out)     # idempotent
+
+
+def _dead_slot_case(q_sign, D=128, N=40, seed=51):
+    r = np.random.default_rng(seed)
+    kb, vb = om.sentinel_rows("bf16", D)
+    n_slots = N + 1
+    dead = N
+    pool_k = numerics.round_to_bf16(r.standard_normal((n_slots, D)))
+    pool_v = numerics.round_to_bf16(r.standard_normal((n_slots, D)))
+    pool_k[dead], pool_v[dead] = kb, vb
+    slot_map = np.arange(N)
+    keep = r.random(N) > 0.4
+    redirected = om.redirect(slot_map, keep, dead)
+    q = r.standard_normal(D) * 0.1 + q_sign * 0.05
+    return q, pool_k, pool_v, slot_map, redirected, keep, dead
+
+
+@pytest.mark.parametrize("q_sign", [1.0, -1.0, 0.0])
+def test_dead_slot_closed_form(q_sign):
+    q, pool_k, pool_v, slot_map, redirected, keep, dead = _dead_slot_case(q_sign)
+    D = q.shape[0]
+    o_dead = om.decode_attention_slots(q, pool_k, pool_v, redirected)
+    o_hard = om.decode_attention_hard(q, pool_k, pool_v, slot_map, keep)
+    logits = pool_k[slot_map[keep]] @ q / math.sqrt(D)
+    l_dead = -9984.0 * q.sum() / math.sqrt(D)
+    m = max(logits.max(), l_dead)
+    z = np.exp(logits - m).sum()
+    n_dead = int((~keep).sum())
+    factor = z / (z + n_dead * math.exp(l_dead - m))
+    np.testing.assert_allclose(o_dead, o_hard * factor, rtol=1e-12, atol=1e-15)
+
+
+def test_dead_slot_is_a_hard_mask_only_with_margin():
+    # sum(q) large and positive: the sentinel's weight underflows -> equal bitwise
+    q, pool_k, pool_v, slot_map, redirected, keep, dead = _dead_slot_case(1.0)
+    q = q + 0.5
+    o_dead = om.decode_attention_slots(q, pool_k, pool_v, redirected)
+    o_hard = om.decode_attention_hard(q, pool_k, pool_v, slot_map, keep)
+    np.testing.assert_array_equal(o_dead, o_hard)
+    # sum(q) < 0: the sentinel logit is large and positive; V = 0 rows swamp
+    # the softmax, so the output collapses toward zero rather than matching
+    q2 = -np.abs(q)
+    o2 = om.decode_attention_slots(q2, pool_k, pool_v, redirected)
+    h2 = om.decode_attention_hard(q2, pool_k, pool_v, slot_map, keep)
+    assert np.linalg.norm(o2) < 1e-6 * np.linalg.norm(h2)
