@@ -1,0 +1,324 @@
+/*
+ * kvsel.h -- C ABI of libkvsel: attention-score-driven KV-cache selection on
+ * AMD MI355X (gfx950).
+ *
+ * The three steps follow the workflow ActKV §3.3 (three primitives) describes:
+ * attention calculation (kvsel_score), entry eviction to a keep mask
+ * (kvsel_select), and materialisation of the kept set -- either a compact
+ * re-RoPEd view (kvsel_gather_rerope, KVMem "tiered movement") or a slot-map
+ * redirect to a dead slot with survivors left in place (kvsel_redirect,
+ * IntentKV §2 Q2 and §4 "redirect").  kvsel_memory_update maintains the
+ * session query memory that IntentKV §4 scores against.
+ *
+ * Conventions shared by every call
+ * --------------------------------
+ * - Plain C types only.  Every args struct begins with `struct_size`
+ *   (set it to sizeof(the struct)) so the ABI can grow.
+ * - Ownership: the caller allocates every buffer (device memory unless
+ *   stated) and keeps it alive until the stream reaches the call.  The
+ *   library allocates no device memory; scratch comes from the caller's
+ *   workspace, sized by the *_workspace queries.  Outputs must not alias
+ *   inputs except where an argument is documented "in/out".
+ * - Execution: each call validates its arguments on the host, then enqueues
+ *   kernels on `stream` (a hipStream_t; NULL = the default stream) and
+ *   returns without synchronising.  Results are valid once the stream
+ *   reaches that point.  With the environment variable KVSEL_DEBUG=1 each
+ *   call synchronises its stream and reports kernel errors.
+ * - Errors: on any status other than KVSEL_OK nothing was enqueued and
+ *   kvsel_last_error() describes why.  No C++ exception crosses the ABI.
+ * - Device pointers must be 16-byte aligned; sizes are element counts.
+ *   Inputs must be finite (NaN/Inf scores are outside the contract).
+ * - Layouts are row-major, last index fastest.
+ */
+#ifndef KVSEL_H
+#define KVSEL_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVSEL_ABI_VERSION 1
+
+typedef enum kvsel_status {
+  KVSEL_OK = 0,
+  KVSEL_E_ARG = 1,         /* null pointer, bad shape/enum, misalignment, N >= 2^31 */
+  KVSEL_E_BUDGET = 2,      /* n_sink + n_recent > k_total while k_total < N */
+  KVSEL_E_UNSUPPORTED = 3, /* dtype/shape combination not built, device is not gfx950 */
+  KVSEL_E_WORKSPACE = 4,   /* workspace missing or smaller than the query returned */
+  KVSEL_E_DEVICE = 5       /* a HIP call failed; the message carries hipGetErrorString */
+} kvsel_status;
+
+typedef enum kvsel_dtype { KVSEL_F32 = 0, KVSEL_BF16 = 1, KVSEL_F16 = 2 } kvsel_dtype;
+
+typedef enum kvsel_score_mode {
+  KVSEL_SCORE_WINDOW = 0, /* token level: softmax of a query window against every key */
+  KVSEL_SCORE_MEMORY = 1, /* token level: softmax of the session memory row over history */
+  KVSEL_SCORE_BLOCK = 2   /* block level: dot product with a RoPE-stripped Mean-K index */
+} kvsel_score_mode;
+
+typedef enum kvsel_agg { KVSEL_AGG_SUM = 0, KVSEL_AGG_MEAN = 1, KVSEL_AGG_MAX = 2 } kvsel_agg;
+typedef enum kvsel_pool { KVSEL_POOL_NONE = 0, KVSEL_POOL_AVG = 1, KVSEL_POOL_MAX = 2 } kvsel_pool;
+typedef enum kvsel_reduce { KVSEL_REDUCE_PER_UNIT = 0, KVSEL_REDUCE_GLOBAL = 1 } kvsel_reduce;
+typedef enum kvsel_rope { KVSEL_ROPE_NONE = 0, KVSEL_ROPE_RAW = 1, KVSEL_ROPE_DELTA = 2 } kvsel_rope;
+typedef enum kvsel_rope_style { KVSEL_ROPE_HALF = 0, KVSEL_ROPE_INTERLEAVED = 1 } kvsel_rope_style;
+typedef enum kvsel_gather_mode { KVSEL_GATHER_FRESH = 0, KVSEL_GATHER_INCREMENTAL = 1 } kvsel_gather_mode;
+
+/* ABI version of the loaded library (KVSEL_ABI_VERSION it was built with). */
+int32_t kvsel_version(void);
+
+/* Message for the last non-OK status returned on the calling thread ("" if
+ * none).  The pointer stays valid until the next kvsel_* call on that thread. */
+const char* kvsel_last_error(void);
+
+/* ------------------------------------------------------------------ score
+ *
+ * Window mode -- ActKV §2 (attention score of a cached key = its softmax
+ * weight) and §7.1 (probabilities recovered as exp(s - LSE) from the
+ * log-sum-exp an attention pass already produced):
+ *   s[r,j] = scale * q_r . k_j, rows r = (query head h of KV group g, window
+ *   row t).  Window row t sits at position N-W+t; with `causal` it sees keys
+ *   j <= N-W+t.  p = exp(s - LSE_r), LSE from `lse_in` if given, else
+ *   computed (and written to `lse_out` if given; with `scores` NULL and
+ *   `lse_out` given, the call computes only the LSE).  Per unit u = (l, g):
+ *   a[u,j] = row_agg over t of (head_agg over h in g of p), then 1-D pooling.
+ *   q: [L][Hq][W][D] (F32/BF16/F16, post-RoPE); k: [L][Hkv][N][D] (same
+ *   dtype); lse_in/lse_out: [L][Hq][W] F32.  Output `scores`: [L*Hkv][N] F32.
+ *
+ * Memory mode -- IntentKV §4 (rule score): for every layer l and query head h,
+ *   a[l,h,j] = softmax over the history H of scale * M[l,h] . K[l,g(h),j];
+ *   H = positions that are neither forced (j < n_sink, j >= N - n_recent)
+ *   nor redirected to the dead slot (slot_map[j] == dead_slot, IntentKV §3
+ *   one-way eviction).  reduce GLOBAL: rule_j = sum over (l,h), summed in a
+ *   fixed order (deterministic); PER_UNIT: sum over h in g per (l,g).
+ *   q = M: [L][Hq][D] F32.  k = paged pool [L][pool_pages][page_size][Hkv][D]
+ *   (BF16/F16), logical page p at physical page page_table[p] (ActKV §2
+ *   paging).  Positions outside H score 0.  Output [N] (GLOBAL) or
+ *   [L*Hkv][N] (PER_UNIT), F32.
+ *
+ * Block mode -- KVMem (query-conditioned retrieval): per unit u = (l, g),
+ *   q-bar[s,u] = sum over the W query tokens and the group's heads of the
+ *   pre-RoPE query, and s[s,u,b] = scale * q-bar[s,u] . mu[u,b] against the
+ *   F16 RoPE-stripped Mean-K index mu: [L][Hkv][N][D] (N = blocks per unit).
+ *   Only index columns [n_begin, n_begin + n_count) are scored (bounded
+ *   tiles).  q: [S][L][Hq][W][D] (BF16/F16/F32).  q-bar is computed into
+ *   `qbar` ([S][L][Hkv][D] F32, or the workspace when NULL); with
+ *   `qbar_valid` = 1 the call reads `qbar` instead and `q` may be NULL.
+ *   Output `scores`: [S][L*Hkv][n_count] F32.
+ *
+ * scale = 0 means 1/sqrt(D).  Pooling (window/memory-per-unit): centred,
+ * odd `pool_k`, stride 1; AVG divides by pool_k counting out-of-range terms
+ * as zero, MAX takes the in-range maximum.
+ */
+typedef struct kvsel_score_args {
+  uint32_t struct_size;
+  int32_t mode;         /* kvsel_score_mode */
+  int32_t q_dtype;      /* kvsel_dtype of q */
+  int32_t k_dtype;      /* kvsel_dtype of k / pool / index */
+  int32_t L, Hq, Hkv, D;/* layers, query heads, KV heads, head dim (64 or 128) */
+  int32_t W;            /* window rows (window) or query tokens per head (block) */
+  int32_t S;            /* sessions (block mode); 1 otherwise */
+  int64_t N;            /* cached positions (window/memory) or index blocks per unit (block) */
+  const void* q;
+  const void* k;
+  /* memory mode: paging and history */
+  const int32_t* page_table; /* [ceil(N/page_size)] logical page -> physical page */
+  int32_t page_size;
+  int32_t n_sink, n_recent;  /* forced set excluded from the history */
+  int64_t pool_pages;        /* physical pages per layer in the pool */
+  const int32_t* slot_map;   /* [N] or NULL: positions equal to dead_slot are dead */
+  int64_t dead_slot;
+  /* block mode: tile and query reduction */
+  int64_t n_begin, n_count;
+  float* qbar;
+  int32_t qbar_valid;
+  /* window mode */
+  int32_t causal;
+  const float* lse_in;  /* nullable */
+  float* lse_out;       /* nullable */
+  int32_t head_agg, row_agg; /* kvsel_agg */
+  int32_t reduce;       /* kvsel_reduce (memory mode) */
+  int32_t pool, pool_k; /* kvsel_pool, odd kernel size */
+  float scale;
+  float* scores;        /* output, F32 */
+} kvsel_score_args;
+
+/* Bytes of device workspace kvsel_score needs for `args` (may be 0). */
+kvsel_status kvsel_score_workspace(const kvsel_score_args* args, size_t* bytes);
+
+kvsel_status kvsel_score(const kvsel_score_args* args, void* workspace,
+                         size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ select
+ *
+ * Budgeted top-k with a forced set -- IntentKV §4 (top-k selection: the
+ * forced set plus the highest-scoring rest of the budget), KVMem
+ * (query-conditioned retrieval: sink and recent always kept, the rest by
+ * score, restored to chronological order), ActKV §3.3 (entry eviction
+ * yields a Boolean keep mask).
+ *
+ * Per unit: F = [0, n_sink) U [n_total - n_recent, n_total); alive A = all
+ * positions, or those with slot_map[j] != dead_slot.  The kept set is
+ * (F n A) plus the k_total - |F n A| best positions of A \ F, ordered by
+ * score descending with ties to the lower index (-0.0 equals +0.0); if
+ * |A| <= k_total every alive position is kept.  Output in ascending order.
+ *
+ * scores: [U] rows of `n` F32 values, row u at scores + u*row_stride,
+ * holding positions [base, base + n) of each unit.  One call with base = 0
+ * and n = n_total selects directly.  Tiled use (KVMem scores its index in
+ * bounded tiles): call once per tile in ascending `base`, passing running
+ * candidate buffers cand_score/cand_idx ([U][k_total] each) and cand_count
+ * ([U], zeroed by the caller before the first tile); the last tile sets
+ * `finalize` = 1.  The tiled result equals the untiled one.
+ * Outputs (written when finalize = 1, or on an untiled call): kept_idx
+ * [U][k_total] int32 ascending, -1 past n_kept; n_kept [U] (nullable);
+ * keep_mask [U][n_total] u8 (nullable; untiled calls only).
+ * Optional pooling (untiled calls only): with pool != KVSEL_POOL_NONE the
+ * selection ranks pool(scores) instead of the scores themselves, the same
+ * centred 1-D pooling kvsel_score offers (odd pool_k; AVG counts
+ * out-of-range terms as zero, MAX takes the in-range maximum), computed on
+ * the fly while the keys are formed.
+ * Errors: KVSEL_E_BUDGET if n_sink + n_recent > k_total and k_total < n_total.
+ */
+typedef struct kvsel_select_args {
+  uint32_t struct_size;
+  int32_t U;
+  int64_t n;
+  int64_t row_stride;
+  const float* scores;
+  int64_t base;
+  int64_t n_total;
+  int32_t k_total, n_sink, n_recent;
+  const int32_t* slot_map;   /* [n_total] or NULL, shared by all units */
+  int64_t dead_slot;
+  float* cand_score;         /* [U][k_total] or NULL (tiled use) */
+  int32_t* cand_idx;         /* [U][k_total] or NULL */
+  int32_t* cand_count;       /* [U] or NULL */
+  int32_t finalize;
+  int32_t* kept_idx;         /* [U][k_total] */
+  uint8_t* keep_mask;        /* [U][n_total] or NULL */
+  int32_t* n_kept;           /* [U] or NULL */
+  int32_t pool, pool_k;      /* kvsel_pool and odd kernel size (untiled calls) */
+} kvsel_select_args;
+
+kvsel_status kvsel_select_workspace(const kvsel_select_args* args, size_t* bytes);
+
+kvsel_status kvsel_select(const kvsel_select_args* args, void* workspace,
+                          size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ gather
+ *
+ * Materialise a selection as a compact view -- KVMem (tiered movement):
+ * kept blocks are packed into contiguous logical positions; K is rotated
+ * for the new position and V is copied as is.
+ *
+ * FRESH: for unit u and kept entry i (ascending), rows o < bt:
+ *   dst[u][i*bt + o] = R(p) src[u][idx[u][i]*bt + o], with
+ *   rope NONE: no rotation (bitwise copy); RAW: p = pos0 + i*bt + o (raw,
+ *   position-free K); DELTA: p = (pos0 + i*bt + o) - (idx*bt + o) (K already
+ *   rotated at its old position).  V is always copied bitwise.
+ *   Rotation: rotate-half (pairs m, m + rotary_dim/2) or interleaved (pairs
+ *   2m, 2m+1), inv_freq[m] = theta^(-2m/rotary_dim); angles are formed in
+ *   float64.  src of unit u starts at src_k + src_offsets[u] elements
+ *   (src_offsets: device int64 [U], or NULL for u * src_unit_stride), so
+ *   several units may alias one buffer.  dst: [U][k*bt][D].
+ *   Entries with i >= n_idx[u] (when n_idx is given) are left untouched.
+ *
+ * INCREMENTAL (reuse of overlapping pages across steps): per unit the
+ *   previous view holds blocks prev_idx[u][:k] (ascending) in pages
+ *   prev_page[u][:k] of a pool [U][pool_pages][bt][D] (pool_k/pool_v, in/out).
+ *   A block in both views keeps its page and V; its K is rotated in place
+ *   by (i_new - i_old)*bt when its position moved.  Pages of blocks that left
+ *   the view are taken in ascending page order by the new blocks in
+ *   ascending block order; those get K = R(pos0 + i_new*bt + o) raw K and
+ *   V copied, both read from src (as in FRESH).  Out: page_table [U][k]
+ *   (page of each kept block, chronological), n_miss [U].
+ *   idx holds the new selection [U][k] (ascending, all valid).
+ */
+typedef struct kvsel_gather_args {
+  uint32_t struct_size;
+  int32_t mode;          /* kvsel_gather_mode */
+  int32_t U, D;
+  int32_t dtype;         /* kvsel_dtype of K/V (BF16, F16 or F32) */
+  int32_t bt;            /* rows per selected entry (1 = tokens, 32 = blocks) */
+  int32_t k;             /* entries per unit */
+  const void* src_k;
+  const void* src_v;
+  const int64_t* src_offsets; /* device [U] element offsets, or NULL */
+  int64_t src_unit_stride;    /* elements, used when src_offsets is NULL */
+  int64_t src_rows;           /* rows available per unit source (bounds check) */
+  const int32_t* idx;         /* [U][k] */
+  const int32_t* n_idx;       /* [U] or NULL (FRESH only) */
+  void* dst_k;                /* FRESH: [U][k*bt][D] */
+  void* dst_v;
+  int32_t rope;               /* kvsel_rope */
+  int32_t style;              /* kvsel_rope_style */
+  int32_t rotary_dim;         /* 0 = D */
+  double theta;
+  int64_t pos0;
+  /* INCREMENTAL */
+  const int32_t* prev_idx;    /* [U][k] */
+  const int32_t* prev_page;   /* [U][k] */
+  void* pool_k;               /* [U][pool_pages][bt][D], in/out */
+  void* pool_v;
+  int64_t pool_pages;
+  int32_t* page_table;        /* out [U][k] */
+  int32_t* n_miss;            /* out [U] */
+} kvsel_gather_args;
+
+kvsel_status kvsel_gather_workspace(const kvsel_gather_args* args, size_t* bytes);
+
+kvsel_status kvsel_gather_rerope(const kvsel_gather_args* args, void* workspace,
+                                 size_t workspace_bytes, void* stream);
+
+/* ------------------------------------------------------------------ redirect
+ *
+ * IntentKV §4 (redirect) and §2 Q2: every dropped logical position is
+ * pointed at one sentinel dead slot; kept positions keep their slot ids and
+ * nothing moves.  slot_map [N] int32 in/out; keep_mask [N] u8 (1 = keep).
+ * Already-dead entries stay dead.
+ * Sentinel init (optional, when k_pool is non-NULL): writes the dead slot's
+ * rows in every layer and KV head: K = -1e4 rounded to the pool dtype
+ * (bf16 -9984, f16 -10000), V = 0.  Pools are [L][pool_slots][Hkv][D] with
+ * pool_slots = pool_pages * page_size, i.e. the paged layout flattened.
+ */
+typedef struct kvsel_redirect_args {
+  uint32_t struct_size;
+  int64_t N;
+  int32_t* slot_map;
+  const uint8_t* keep_mask;
+  int64_t dead_slot;
+  void* k_pool;          /* nullable: skip the sentinel write */
+  void* v_pool;
+  int32_t L, Hkv, D;
+  int32_t dtype;         /* BF16 or F16 */
+  int64_t pool_slots;    /* slots per layer */
+} kvsel_redirect_args;
+
+kvsel_status kvsel_redirect(const kvsel_redirect_args* args, void* stream);
+
+/* ------------------------------------------------------------------ memory
+ *
+ * IntentKV §4 (memory recurrence) and §7 (unit-norm projection): one turn
+ *   M <- normalise(decay * M + mean over the turn's W query rows of q),
+ * normalised to unit L2 norm along D per (layer, query head); a zero vector
+ * stays zero.  q_turn: [L][Hq][W][D] (BF16/F16/F32); M: [L][Hq][D] F32 in/out.
+ */
+typedef struct kvsel_memupd_args {
+  uint32_t struct_size;
+  int32_t L, Hq, D, W;
+  int32_t q_dtype;
+  const void* q_turn;
+  float* M;
+  float decay;
+} kvsel_memupd_args;
+
+kvsel_status kvsel_memory_update(const kvsel_memupd_args* args, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* KVSEL_H */

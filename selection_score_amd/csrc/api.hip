@@ -1,0 +1,469 @@
+// C ABI of libkvsel: argument validation, workspace sizing and dispatch.
+//
+// Every entry point validates its arguments on the host before touching the
+// HIP runtime, so argument errors are reported without a device.  Kernels
+// are then enqueued on the caller's stream; nothing synchronises unless
+// KVSEL_DEBUG=1.  No exception crosses the ABI.
+#include <math.h>
+#include <stdarg.h>
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include <mutex>
+#include <string>
+#include <vector>
+
+#include "common.h"
+
+using namespace kvsel;
+
+namespace {
+
+thread_local std::string g_err;
+
+kvsel_status fail(kvsel_status st, const char* fmt, ...) {
+  char buf[512];
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(buf, sizeof(buf), fmt, ap);
+  va_end(ap);
+  g_err = buf;
+  return st;
+}
+
+kvsel_status hip_fail(hipError_t e, const char* what) {
+  return fail(KVSEL_E_DEVICE, "%s: %s", what, hipGetErrorString(e));
+}
+
+bool debug_mode() {
+  static const bool on = [] {
+    const char* v = getenv("KVSEL_DEBUG");
+    return v != nullptr && v[0] == '1';
+  }();
+  return on;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool valid_dtype(int dt) { return dt == KVSEL_F32 || dt == KVSEL_BF16 || dt == KVSEL_F16; }
+int dtype_size(int dt) { return dt == KVSEL_F32 ? 4 : 2; }
+bool valid_agg(int a) { return a == KVSEL_AGG_SUM || a == KVSEL_AGG_MEAN || a == KVSEL_AGG_MAX; }
+
+constexpr int64_t kMaxN = (int64_t(1) << 31) - 1;
+
+// Per-device check that the device is gfx950 (cached).
+kvsel_status check_device() {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  static std::mutex mu;
+  static std::vector<int> state;   // 0 unknown, 1 ok, 2 unsupported
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<int>(state.size()) <= dev) state.resize(dev + 1, 0);
+  if (state[dev] == 0) {
+    hipDeviceProp_t prop;
+    e = hipGetDeviceProperties(&prop, dev);
+    if (e != hipSuccess) return hip_fail(e, "hipGetDeviceProperties");
+    state[dev] = (strncmp(prop.gcnArchName, "gfx950", 6) == 0) ? 1 : 2;
+    if (state[dev] == 2) return fail(KVSEL_E_UNSUPPORTED, "device %d is %s, not gfx950", dev, prop.gcnArchName);
+  }
+  if (state[dev] == 2) return fail(KVSEL_E_UNSUPPORTED, "device %d is not gfx950", dev);
+  return KVSEL_OK;
+}
+
+kvsel_status finish(hipError_t e, hipStream_t st, const char* what) {
+  if (e != hipSuccess) return hip_fail(e, what);
+  if (debug_mode()) {
+    e = hipStreamSynchronize(st);
+    if (e != hipSuccess) return hip_fail(e, what);
+    e = hipGetLastError();
+    if (e != hipSuccess) return hip_fail(e, what);
+  }
+  g_err.clear();
+  return KVSEL_OK;
+}
+
+size_t round256(size_t b) { return (b + 255) / 256 * 256; }
+
+// ------------------------------------------------------------------ score
+
+struct ScorePlan {
+  size_t lse_off = 0, part_off = 0, raw_off = 0, mem_off = 0, qbar_off = 0, total = 0;
+  bool mfma = false;
+  bool own_lse = false;
+  bool pooled = false;
+  bool lse_only = false;
+};
+
+kvsel_status validate_score(const kvsel_score_args* a, ScorePlan* plan) {
+  if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+  if (a->struct_size < sizeof(kvsel_score_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->mode < KVSEL_SCORE_WINDOW || a->mode > KVSEL_SCORE_BLOCK) return fail(KVSEL_E_ARG, "bad mode");
+  if (a->L <= 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0)
+    return fail(KVSEL_E_ARG, "need L, Hq, Hkv > 0 and Hkv dividing Hq");
+  if (a->D != 64 && a->D != 128) return fail(KVSEL_E_UNSUPPORTED, "D must be 64 or 128");
+  if (a->N <= 0 || a->N > kMaxN) return fail(KVSEL_E_ARG, "N must be in [1, 2^31)");
+  const bool lse_only = a->mode == KVSEL_SCORE_WINDOW && a->scores == nullptr && a->lse_out != nullptr &&
+                        a->lse_in == nullptr;
+  if (a->scores == nullptr && !lse_only) return fail(KVSEL_E_ARG, "scores is NULL");
+  if (!valid_dtype(a->q_dtype) || !valid_dtype(a->k_dtype)) return fail(KVSEL_E_ARG, "bad dtype");
+  if (a->pool < KVSEL_POOL_NONE || a->pool > KVSEL_POOL_MAX) return fail(KVSEL_E_ARG, "bad pool");
+  if (a->pool != KVSEL_POOL_NONE && (a->pool_k < 1 || a->pool_k % 2 == 0))
+    return fail(KVSEL_E_ARG, "pool_k must be odd and >= 1");
+  const int G = a->Hq / a->Hkv;
+  const int U = a->L * a->Hkv;
+  size_t off = 0;
+  auto take = [&](size_t bytes) {
+    const size_t o = off;
+    off += round256(bytes);
+    return o;
+  };
+  plan->pooled = a->pool != KVSEL_POOL_NONE && a->pool_k > 1 && !lse_only;
+  plan->lse_only = lse_only;
+
+  if (a->mode == KVSEL_SCORE_WINDOW) {
+    if (a->q == nullptr || a->k == nullptr) return fail(KVSEL_E_ARG, "q or k is NULL");
+    if (!aligned16(a->q) || !aligned16(a->k)) return fail(KVSEL_E_ARG, "q and k must be 16-byte aligned");
+    if (a->q_dtype != a->k_dtype) return fail(KVSEL_E_UNSUPPORTED, "window mode needs q and k of one dtype");
+    if (a->W < 1 || a->W > a->N) return fail(KVSEL_E_ARG, "W must be in [1, N]");
+    if (!valid_agg(a->head_agg) || !valid_agg(a->row_agg)) return fail(KVSEL_E_ARG, "bad aggregation");
+    WindowParams p{a->L, a->Hq, a->Hkv, a->D, a->W, G, a->N, a->causal ? 1 : 0, 1.f, a->head_agg, a->row_agg};
+    plan->mfma = window_mfma_supported(p, a->k_dtype);
+    if (!plan->mfma && static_cast<int64_t>(G) * a->W * a->D > 32768)
+      return fail(KVSEL_E_UNSUPPORTED, "window of G*W*D > 32768 needs bf16/f16 with SUM/MEAN aggregation");
+    plan->own_lse = a->lse_in == nullptr && a->lse_out == nullptr;
+    if (plan->own_lse) plan->lse_off = take(static_cast<size_t>(a->L) * a->Hq * a->W * 4);
+    if (a->lse_in == nullptr && plan->mfma) plan->part_off = take(window_mfma_partials_bytes(p));
+    if (plan->pooled) plan->raw_off = take(static_cast<size_t>(U) * a->N * 4);
+  } else if (a->mode == KVSEL_SCORE_MEMORY) {
+    if (a->q == nullptr || a->k == nullptr || a->page_table == nullptr)
+      return fail(KVSEL_E_ARG, "q (memory), k (pool) or page_table is NULL");
+    if (!aligned16(a->k)) return fail(KVSEL_E_ARG, "pool must be 16-byte aligned");
+    if (a->q_dtype != KVSEL_F32) return fail(KVSEL_E_UNSUPPORTED, "memory rows must be F32");
+    if (a->k_dtype == KVSEL_F32) return fail(KVSEL_E_UNSUPPORTED, "memory mode needs a BF16/F16 pool");
+    if (256 % a->Hq != 0) return fail(KVSEL_E_UNSUPPORTED, "memory mode needs Hq dividing 256");
+    if (a->page_size < 1 || a->page_size > 64 || a->pool_pages < 1)
+      return fail(KVSEL_E_ARG, "bad page_size or pool_pages");
+    if (a->n_sink < 0 || a->n_recent < 0) return fail(KVSEL_E_ARG, "negative forced-set size");
+    if (a->reduce != KVSEL_REDUCE_GLOBAL && a->reduce != KVSEL_REDUCE_PER_UNIT)
+      return fail(KVSEL_E_ARG, "bad reduce");
+    MemoryParams mp{};
+    mp.L = a->L; mp.Hq = a->Hq; mp.Hkv = a->Hkv; mp.D = a->D; mp.page_size = a->page_size;
+    mp.N = a->N; mp.pool_pages = a->pool_pages;
+    plan->mem_off = take(memory_workspace_bytes(mp));
+    const int64_t rows = a->reduce == KVSEL_REDUCE_GLOBAL ? 1 : U;
+    if (plan->pooled) plan->raw_off = take(static_cast<size_t>(rows) * a->N * 4);
+  } else {
+    if (a->k == nullptr) return fail(KVSEL_E_ARG, "index (k) is NULL");
+    if (!aligned16(a->k)) return fail(KVSEL_E_ARG, "index must be 16-byte aligned");
+    if (a->k_dtype != KVSEL_F16) return fail(KVSEL_E_UNSUPPORTED, "block mode needs an F16 Mean-K index");
+    if (a->S < 1 || a->S > 8) return fail(KVSEL_E_ARG, "S must be in [1, 8]");
+    if (a->n_begin < 0 || a->n_count < 0 || a->n_begin + a->n_count > a->N)
+      return fail(KVSEL_E_ARG, "tile [n_begin, n_begin + n_count) outside [0, N)");
+    if (a->qbar_valid) {
+      if (a->qbar == nullptr) return fail(KVSEL_E_ARG, "qbar_valid with a NULL qbar");
+    } else {
+      if (a->q == nullptr) return fail(KVSEL_E_ARG, "q is NULL");
+      if (!aligned16(a->q)) return fail(KVSEL_E_ARG, "q must be 16-byte aligned");
+      if (a->W < 1) return fail(KVSEL_E_ARG, "W must be >= 1");
+    }
+    if (a->pool != KVSEL_POOL_NONE) return fail(KVSEL_E_UNSUPPORTED, "block mode has no pooling");
+    if (a->qbar == nullptr) plan->qbar_off = take(static_cast<size_t>(a->S) * U * a->D * 4);
+  }
+  plan->total = off;
+  return KVSEL_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvsel_version(void) { return KVSEL_ABI_VERSION; }
+
+const char* kvsel_last_error(void) { return g_err.c_str(); }
+
+kvsel_status kvsel_score_workspace(const kvsel_score_args* args, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return fail(KVSEL_E_ARG, "bytes is NULL");
+    ScorePlan plan;
+    kvsel_status s = validate_score(args, &plan);
+    if (s != KVSEL_OK) return s;
+    *bytes = plan.total;
+    g_err.clear();
+    return KVSEL_OK;
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+kvsel_status kvsel_score(const kvsel_score_args* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    ScorePlan plan;
+    kvsel_status s = validate_score(a, &plan);
+    if (s != KVSEL_OK) return s;
+    if (plan.total > 0 && (ws == nullptr || ws_bytes < plan.total))
+      return fail(KVSEL_E_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.total, ws_bytes);
+    if ((s = check_device()) != KVSEL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    uint8_t* w = static_cast<uint8_t*>(ws);
+    const float scale = (a->scale != 0.f) ? a->scale : static_cast<float>(1.0 / sqrt(static_cast<double>(a->D)));
+    const int G = a->Hq / a->Hkv;
+    const int U = a->L * a->Hkv;
+    hipError_t e = hipSuccess;
+    float* dst = plan.pooled ? reinterpret_cast<float*>(w + plan.raw_off) : a->scores;
+    int64_t pool_rows = U;
+
+    if (a->mode == KVSEL_SCORE_WINDOW) {
+      WindowParams p{a->L, a->Hq, a->Hkv, a->D, a->W, G, a->N, a->causal ? 1 : 0, scale,
+                     a->head_agg, a->row_agg};
+      const float* lse = a->lse_in;
+      if (lse == nullptr) {
+        float* lo = plan.own_lse ? reinterpret_cast<float*>(w + plan.lse_off) : a->lse_out;
+        if (plan.mfma)
+          e = launch_window_lse_mfma(p, a->k_dtype, a->q, a->k, reinterpret_cast<float*>(w + plan.part_off), lo, st);
+        else
+          e = launch_window_lse_valu(p, a->k_dtype, a->q, a->k, lo, st);
+        if (e != hipSuccess) return hip_fail(e, "window lse");
+        lse = lo;
+      }
+      if (plan.lse_only) return finish(hipSuccess, st, "window lse");
+      if (plan.mfma) e = launch_window_scores_mfma(p, a->k_dtype, a->q, a->k, lse, dst, st);
+      else e = launch_window_scores_valu(p, a->k_dtype, a->q, a->k, lse, dst, st);
+      if (e != hipSuccess) return hip_fail(e, "window scores");
+    } else if (a->mode == KVSEL_SCORE_MEMORY) {
+      MemoryParams p{};
+      p.L = a->L; p.Hq = a->Hq; p.Hkv = a->Hkv; p.D = a->D; p.page_size = a->page_size;
+      p.N = a->N; p.pool_pages = a->pool_pages; p.n_sink = a->n_sink; p.n_recent = a->n_recent;
+      p.page_table = a->page_table; p.slot_map = a->slot_map; p.dead_slot = a->dead_slot;
+      p.scale = scale; p.reduce = a->reduce;
+      e = launch_memory_scores(p, a->k_dtype, static_cast<const float*>(a->q), a->k, w + plan.mem_off, dst, st);
+      if (e != hipSuccess) return hip_fail(e, "memory scores");
+      pool_rows = (a->reduce == KVSEL_REDUCE_GLOBAL) ? 1 : U;
+    } else {
+      BlockParams p{a->S, a->L, a->Hq, a->Hkv, a->D, a->W, a->N, a->n_begin, a->n_count, scale};
+      float* qbar = a->qbar ? a->qbar : reinterpret_cast<float*>(w + plan.qbar_off);
+      if (!a->qbar_valid) {
+        e = launch_query_reduce(p, a->q_dtype, a->q, qbar, st);
+        if (e != hipSuccess) return hip_fail(e, "query reduce");
+      }
+      e = launch_block_scores(p, qbar, a->k, a->scores, st);
+      return finish(e, st, "block scores");
+    }
+    if (plan.pooled) e = launch_pool1d(dst, a->scores, pool_rows, a->N, a->pool, a->pool_k, st);
+    return finish(e, st, "score pooling");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+// ------------------------------------------------------------------ select
+
+static kvsel_status validate_select(const kvsel_select_args* a) {
+  if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+  if (a->struct_size < sizeof(kvsel_select_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->U < 0 || a->n < 0 || a->base < 0 || a->k_total < 0 || a->n_sink < 0 || a->n_recent < 0)
+    return fail(KVSEL_E_ARG, "negative size");
+  if (a->n_total > kMaxN || a->base + a->n > a->n_total)
+    return fail(KVSEL_E_ARG, "need base + n <= n_total < 2^31");
+  if (a->U > 0 && a->n > 0 && (a->scores == nullptr || a->row_stride < a->n))
+    return fail(KVSEL_E_ARG, "scores NULL or row_stride < n");
+  if (a->k_total < a->n_total && static_cast<int64_t>(a->n_sink) + a->n_recent > a->k_total)
+    return fail(KVSEL_E_BUDGET, "n_sink + n_recent (%d) exceeds k_total (%d) < n_total", a->n_sink + a->n_recent,
+                a->k_total);
+  const int ncand = (a->cand_score != nullptr) + (a->cand_idx != nullptr) + (a->cand_count != nullptr);
+  if (ncand != 0 && ncand != 3) return fail(KVSEL_E_ARG, "give all of cand_score, cand_idx, cand_count or none");
+  const bool tiled = ncand == 3;
+  if (!tiled && (a->base != 0 || a->n != a->n_total))
+    return fail(KVSEL_E_ARG, "a partial range needs the running-candidate buffers");
+  if (!tiled && !a->finalize) return fail(KVSEL_E_ARG, "an untiled call must finalize");
+  if (a->keep_mask != nullptr && (tiled || a->base != 0 || a->n != a->n_total))
+    return fail(KVSEL_E_ARG, "keep_mask needs an untiled call");
+  if (a->finalize && a->kept_idx == nullptr) return fail(KVSEL_E_ARG, "kept_idx is NULL");
+  if (a->pool < KVSEL_POOL_NONE || a->pool > KVSEL_POOL_MAX) return fail(KVSEL_E_ARG, "bad pool");
+  if (a->pool != KVSEL_POOL_NONE && (a->pool_k < 1 || a->pool_k % 2 == 0 || a->pool_k > 255))
+    return fail(KVSEL_E_ARG, "pool_k must be odd, in [1, 255]");
+  if (a->pool != KVSEL_POOL_NONE && tiled) return fail(KVSEL_E_ARG, "pooling needs an untiled call");
+  if (tiled && static_cast<int64_t>(a->k_total) * 8 > 64 * 1024)
+    return fail(KVSEL_E_UNSUPPORTED, "tiled selection supports k_total <= 8192");
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_select_workspace(const kvsel_select_args* a, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return fail(KVSEL_E_ARG, "bytes is NULL");
+    kvsel_status s = validate_select(a);
+    if (s != KVSEL_OK) return s;
+    *bytes = 0;
+    g_err.clear();
+    return KVSEL_OK;
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+kvsel_status kvsel_select(const kvsel_select_args* a, void* ws, size_t ws_bytes, void* stream) {
+  (void)ws;
+  (void)ws_bytes;
+  try {
+    kvsel_status s = validate_select(a);
+    if (s != KVSEL_OK) return s;
+    if ((s = check_device()) != KVSEL_OK) return s;
+    SelectParams p{};
+    p.U = a->U; p.n = a->n; p.row_stride = a->row_stride; p.base = a->base; p.n_total = a->n_total;
+    p.k_total = a->k_total; p.n_sink = a->n_sink; p.n_recent = a->n_recent;
+    p.slot_map = a->slot_map; p.dead_slot = a->dead_slot;
+    p.cand_score = a->cand_score; p.cand_idx = a->cand_idx; p.cand_count = a->cand_count;
+    p.finalize = a->finalize ? 1 : 0;
+    if (a->cand_count == nullptr) p.finalize = 1;
+    p.kept_idx = a->kept_idx; p.keep_mask = a->keep_mask; p.n_kept = a->n_kept;
+    p.pool = (a->pool_k > 1) ? a->pool : KVSEL_POOL_NONE;
+    p.pool_k = a->pool_k;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish(launch_select(p, a->scores, st), st, "select");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+// ------------------------------------------------------------------ gather
+
+static kvsel_status validate_gather(const kvsel_gather_args* a, GatherParams* gp, RopeTable* rt) {
+  if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+  if (a->struct_size < sizeof(kvsel_gather_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->mode != KVSEL_GATHER_FRESH && a->mode != KVSEL_GATHER_INCREMENTAL) return fail(KVSEL_E_ARG, "bad mode");
+  if (!valid_dtype(a->dtype)) return fail(KVSEL_E_ARG, "bad dtype");
+  if (a->U < 0 || a->k < 0 || a->bt < 1) return fail(KVSEL_E_ARG, "need U, k >= 0 and bt >= 1");
+  const int esz = dtype_size(a->dtype);
+  const int elems16 = 16 / esz;
+  const int lpr = (a->D > 0) ? a->D * esz / 16 : 0;
+  if (a->D <= 0 || (a->D * esz) % 16 != 0 || lpr > 64 || (lpr & (lpr - 1)) != 0)
+    return fail(KVSEL_E_UNSUPPORTED, "D*elem_size must be 16 * a power of two <= 1024 bytes");
+  if (a->rope < KVSEL_ROPE_NONE || a->rope > KVSEL_ROPE_DELTA) return fail(KVSEL_E_ARG, "bad rope");
+  const int rd = a->rotary_dim == 0 ? a->D : a->rotary_dim;
+  if (a->rope != KVSEL_ROPE_NONE) {
+    if (a->style != KVSEL_ROPE_HALF && a->style != KVSEL_ROPE_INTERLEAVED) return fail(KVSEL_E_ARG, "bad style");
+    if (rd < 2 || rd > a->D || rd % 2 != 0) return fail(KVSEL_E_ARG, "bad rotary_dim");
+    const int need = (a->style == KVSEL_ROPE_HALF) ? 2 * elems16 : elems16;
+    if (rd % need != 0) return fail(KVSEL_E_UNSUPPORTED, "rotary_dim must be a multiple of %d", need);
+    if (rd / 2 > 128) return fail(KVSEL_E_UNSUPPORTED, "rotary_dim must be <= 256");
+    if (!(a->theta > 0.0)) return fail(KVSEL_E_ARG, "theta must be > 0");
+  }
+  if (a->src_k == nullptr || a->src_v == nullptr || a->idx == nullptr)
+    return fail(KVSEL_E_ARG, "src_k, src_v or idx is NULL");
+  if (!aligned16(a->src_k) || !aligned16(a->src_v)) return fail(KVSEL_E_ARG, "sources must be 16-byte aligned");
+  if (a->src_rows < 0) return fail(KVSEL_E_ARG, "src_rows < 0");
+  if (a->mode == KVSEL_GATHER_FRESH) {
+    if (a->dst_k == nullptr || a->dst_v == nullptr) return fail(KVSEL_E_ARG, "dst_k or dst_v is NULL");
+    if (!aligned16(a->dst_k) || !aligned16(a->dst_v)) return fail(KVSEL_E_ARG, "destinations must be 16-byte aligned");
+  } else {
+    if (a->prev_idx == nullptr || a->prev_page == nullptr || a->pool_k == nullptr || a->pool_v == nullptr ||
+        a->page_table == nullptr || a->n_miss == nullptr)
+      return fail(KVSEL_E_ARG, "incremental mode needs prev_idx, prev_page, pools, page_table, n_miss");
+    if (!aligned16(a->pool_k) || !aligned16(a->pool_v)) return fail(KVSEL_E_ARG, "pools must be 16-byte aligned");
+    if (a->pool_pages < a->k) return fail(KVSEL_E_ARG, "pool_pages < k");
+    if (a->rope == KVSEL_ROPE_DELTA) return fail(KVSEL_E_ARG, "incremental mode rotates raw K (rope RAW or NONE)");
+    if (a->k > 8192 || a->pool_pages > (int64_t(1) << 18))
+      return fail(KVSEL_E_UNSUPPORTED, "incremental mode supports k <= 8192 and pool_pages <= 2^18");
+    if (a->rope == KVSEL_ROPE_RAW && (rd != a->D || static_cast<int64_t>(a->bt) * (a->D / 2) > 2048))
+      return fail(KVSEL_E_UNSUPPORTED, "incremental re-RoPE needs rotary_dim == D and bt * D/2 <= 2048");
+  }
+  gp->U = a->U; gp->D = a->D; gp->bt = a->bt; gp->k = a->k; gp->dtype = a->dtype; gp->rope = a->rope;
+  gp->style = a->style; gp->rotary_dim = rd; gp->src_unit_stride = a->src_unit_stride;
+  gp->src_rows = a->src_rows; gp->pos0 = a->pos0; gp->pool_pages = a->pool_pages; gp->src_offsets = a->src_offsets;
+  for (int m = 0; m < 128; ++m) rt->inv_freq[m] = (m < rd / 2) ? pow(a->theta, -2.0 * m / rd) : 0.0;
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_gather_workspace(const kvsel_gather_args* a, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return fail(KVSEL_E_ARG, "bytes is NULL");
+    GatherParams gp{};
+    RopeTable rt;
+    kvsel_status s = validate_gather(a, &gp, &rt);
+    if (s != KVSEL_OK) return s;
+    *bytes = (a->mode == KVSEL_GATHER_INCREMENTAL) ? incremental_workspace_bytes(gp) : 0;
+    g_err.clear();
+    return KVSEL_OK;
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+kvsel_status kvsel_gather_rerope(const kvsel_gather_args* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    GatherParams gp{};
+    RopeTable rt;
+    kvsel_status s = validate_gather(a, &gp, &rt);
+    if (s != KVSEL_OK) return s;
+    const size_t need = (a->mode == KVSEL_GATHER_INCREMENTAL) ? incremental_workspace_bytes(gp) : 0;
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+      return fail(KVSEL_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
+    if ((s = check_device()) != KVSEL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e;
+    if (a->mode == KVSEL_GATHER_FRESH)
+      e = launch_gather_fresh(gp, rt, a->src_k, a->src_v, a->idx, a->n_idx, a->dst_k, a->dst_v, st);
+    else
+      e = launch_gather_incremental(gp, rt, a->src_k, a->src_v, a->idx, a->prev_idx, a->prev_page, a->pool_k,
+                                    a->pool_v, a->page_table, a->n_miss, ws, st);
+    return finish(e, st, "gather");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+// ------------------------------------------------------------------ redirect
+
+kvsel_status kvsel_redirect(const kvsel_redirect_args* a, void* stream) {
+  try {
+    if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+    if (a->struct_size < sizeof(kvsel_redirect_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+    if (a->N < 0 || a->N > kMaxN) return fail(KVSEL_E_ARG, "N must be in [0, 2^31)");
+    if (a->N > 0 && (a->slot_map == nullptr || a->keep_mask == nullptr))
+      return fail(KVSEL_E_ARG, "slot_map or keep_mask is NULL");
+    if (a->dead_slot < 0 || a->dead_slot > kMaxN) return fail(KVSEL_E_ARG, "dead_slot outside int32");
+    const bool sentinel = a->k_pool != nullptr;
+    if (sentinel) {
+      if (a->v_pool == nullptr) return fail(KVSEL_E_ARG, "v_pool is NULL");
+      if (a->dtype != KVSEL_BF16 && a->dtype != KVSEL_F16)
+        return fail(KVSEL_E_UNSUPPORTED, "the sentinel needs a BF16/F16 pool (-1e4 is not an fp8 value)");
+      if (a->L <= 0 || a->Hkv <= 0 || a->D <= 0 || a->pool_slots <= a->dead_slot)
+        return fail(KVSEL_E_ARG, "bad pool shape or dead_slot outside the pool");
+    }
+    kvsel_status s = check_device();
+    if (s != KVSEL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    hipError_t e = hipSuccess;
+    if (sentinel) {
+      e = launch_sentinel(a->k_pool, a->v_pool, a->L, a->Hkv, a->D, a->dtype, a->pool_slots, a->dead_slot, st);
+      if (e != hipSuccess) return hip_fail(e, "sentinel");
+    }
+    e = launch_redirect(a->N, a->slot_map, a->keep_mask, a->dead_slot, st);
+    return finish(e, st, "redirect");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+// ------------------------------------------------------------------ memory
+
+kvsel_status kvsel_memory_update(const kvsel_memupd_args* a, void* stream) {
+  try {
+    if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+    if (a->struct_size < sizeof(kvsel_memupd_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+    if (a->L <= 0 || a->Hq <= 0 || a->D <= 0 || a->D > 256 || a->W <= 0)
+      return fail(KVSEL_E_ARG, "need L, Hq, W > 0 and 0 < D <= 256");
+    if (a->q_turn == nullptr || a->M == nullptr) return fail(KVSEL_E_ARG, "q_turn or M is NULL");
+    if (!valid_dtype(a->q_dtype)) return fail(KVSEL_E_ARG, "bad dtype");
+    kvsel_status s = check_device();
+    if (s != KVSEL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish(launch_memory_update(a->L, a->Hq, a->D, a->W, a->q_dtype, a->q_turn, a->M, a->decay, st), st,
+                  "memory update");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+}  // extern "C"

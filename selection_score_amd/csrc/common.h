@@ -1,0 +1,166 @@
+// Internal helpers shared by the libkvsel translation units (gfx950 only).
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "kvsel.h"
+
+namespace kvsel {
+
+// ---------------------------------------------------------------- element access
+
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
+  return __uint_as_float(static_cast<uint32_t>(b) << 16);
+}
+
+// Round-to-nearest-even float -> bfloat16 (finite inputs).
+__device__ __forceinline__ uint16_t f32_to_bf16(float f) {
+  uint32_t u = __float_as_uint(f);
+  u += 0x7FFFu + ((u >> 16) & 1u);
+  return static_cast<uint16_t>(u >> 16);
+}
+
+__device__ __forceinline__ float f16_to_f32(uint16_t h) {
+  _Float16 v;
+  __builtin_memcpy(&v, &h, 2);
+  return static_cast<float>(v);
+}
+
+__device__ __forceinline__ uint16_t f32_to_f16(float f) {
+  _Float16 v = static_cast<_Float16>(f);
+  uint16_t h;
+  __builtin_memcpy(&h, &v, 2);
+  return h;
+}
+
+// Load element i of a buffer of the given storage type as float.
+template <int DT>
+__device__ __forceinline__ float load_elem(const void* p, int64_t i) {
+  if constexpr (DT == KVSEL_F32) {
+    return static_cast<const float*>(p)[i];
+  } else if constexpr (DT == KVSEL_BF16) {
+    return bf16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  } else {
+    return f16_to_f32(static_cast<const uint16_t*>(p)[i]);
+  }
+}
+
+template <int DT>
+__device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
+  if constexpr (DT == KVSEL_F32) {
+    static_cast<float*>(p)[i] = v;
+  } else if constexpr (DT == KVSEL_BF16) {
+    static_cast<uint16_t*>(p)[i] = f32_to_bf16(v);
+  } else {
+    static_cast<uint16_t*>(p)[i] = f32_to_f16(v);
+  }
+}
+
+// Order-preserving map of a finite float to uint32 (larger score -> larger
+// key); -0.0 is folded onto +0.0 first.  Key 0 never arises from a finite
+// value and marks "not a candidate".
+__device__ __forceinline__ uint32_t score_key(float s) {
+  uint32_t u = __float_as_uint(s + 0.0f);
+  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+__device__ __forceinline__ float key_score(uint32_t k) {
+  uint32_t u = (k & 0x80000000u) ? (k & 0x7FFFFFFFu) : ~k;
+  return __uint_as_float(u);
+}
+
+__host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// ---------------------------------------------------------------- launchers
+// Each returns the status of the launch (hipGetLastError after enqueueing).
+
+struct WindowParams {
+  int L, Hq, Hkv, D, W, G;  // G = Hq / Hkv
+  int64_t N;
+  int causal;
+  float scale;
+  int head_agg, row_agg;
+};
+
+hipError_t launch_window_lse_valu(const WindowParams& p, int dt, const void* q, const void* k,
+                                  float* lse, hipStream_t st);
+hipError_t launch_window_scores_valu(const WindowParams& p, int dt, const void* q, const void* k,
+                                     const float* lse, float* out, hipStream_t st);
+bool window_mfma_supported(const WindowParams& p, int dt);
+size_t window_mfma_partials_bytes(const WindowParams& p);
+hipError_t launch_window_lse_mfma(const WindowParams& p, int dt, const void* q, const void* k,
+                                  float* partials, float* lse, hipStream_t st);
+hipError_t launch_window_scores_mfma(const WindowParams& p, int dt, const void* q, const void* k,
+                                     const float* lse, float* out, hipStream_t st);
+
+hipError_t launch_pool1d(const float* in, float* out, int64_t rows, int64_t n, int kind, int ksize,
+                         hipStream_t st);
+
+struct MemoryParams {
+  int L, Hq, Hkv, D, page_size;
+  int64_t N, pool_pages;
+  int n_sink, n_recent;
+  const int32_t* page_table;
+  const int32_t* slot_map;
+  int64_t dead_slot;
+  float scale;
+  int reduce;
+};
+size_t memory_workspace_bytes(const MemoryParams& p);
+hipError_t launch_memory_scores(const MemoryParams& p, int dt, const float* M, const void* pool,
+                                void* ws, float* out, hipStream_t st);
+
+struct BlockParams {
+  int S, L, Hq, Hkv, D, W;
+  int64_t NB, n_begin, n_count;
+  float scale;
+};
+hipError_t launch_query_reduce(const BlockParams& p, int dt, const void* q, float* qbar,
+                               hipStream_t st);
+hipError_t launch_block_scores(const BlockParams& p, const float* qbar, const void* mu, float* out,
+                               hipStream_t st);
+
+struct SelectParams {
+  int U;
+  int64_t n, row_stride, base, n_total;
+  int k_total, n_sink, n_recent;
+  const int32_t* slot_map;
+  int64_t dead_slot;
+  float* cand_score;
+  int32_t* cand_idx;
+  int32_t* cand_count;
+  int finalize;
+  int32_t* kept_idx;
+  uint8_t* keep_mask;
+  int32_t* n_kept;
+  int pool, pool_k;
+};
+hipError_t launch_select(const SelectParams& p, const float* scores, hipStream_t st);
+
+struct RopeTable {
+  double inv_freq[128];
+};
+struct GatherParams {
+  int U, D, bt, k, dtype, rope, style, rotary_dim;
+  int64_t src_unit_stride, src_rows, pos0, pool_pages;
+  const int64_t* src_offsets;
+};
+hipError_t launch_gather_fresh(const GatherParams& p, const RopeTable& rt, const void* src_k,
+                               const void* src_v, const int32_t* idx, const int32_t* n_idx,
+                               void* dst_k, void* dst_v, hipStream_t st);
+size_t incremental_workspace_bytes(const GatherParams& p);
+hipError_t launch_gather_incremental(const GatherParams& p, const RopeTable& rt, const void* src_k,
+                                     const void* src_v, const int32_t* idx, const int32_t* prev_idx,
+                                     const int32_t* prev_page, void* pool_k, void* pool_v,
+                                     int32_t* page_table, int32_t* n_miss, void* ws,
+                                     hipStream_t st);
+
+hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, int64_t dead,
+                           hipStream_t st);
+hipError_t launch_sentinel(void* k_pool, void* v_pool, int L, int Hkv, int D, int dtype,
+                           int64_t pool_slots, int64_t dead, hipStream_t st);
+hipError_t launch_memory_update(int L, int Hq, int D, int W, int dt, const void* q, float* M,
+                                float decay, hipStream_t st);
+
+}  // namespace kvsel

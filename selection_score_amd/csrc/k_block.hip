@@ -1,0 +1,129 @@
+// Block scores against a RoPE-stripped Mean-K index.
+//
+// KVMem (query-conditioned retrieval): one Mean-K vector per (layer, KV
+// head, 32-token block) is scored with the query in the model's own
+// attention space.  With pre-RoPE queries on both sides the per-query dot
+// products sum to one dot product with the summed query (linearity), so the
+// path is: reduce the prefill queries of each KV group to q-bar (one HBM
+// pass over q), then stream the index once, a GEMV per unit for all
+// sessions at the same time.
+#include "common.h"
+
+namespace kvsel {
+
+// q: [S][L][Hq][W][D] -> qbar [S][L][Hkv][D], summed over the group's heads
+// and the W tokens.  One workgroup per (s, l, g); 16-byte loads, per-slot
+// float accumulators, slots reduced in a fixed order.
+template <int DT>
+__global__ __launch_bounds__(256) void query_reduce_kernel(BlockParams p, const void* __restrict__ q,
+                                                           float* __restrict__ qbar) {
+  constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
+  constexpr int E = 16 / esz;
+  __shared__ float part[256][8];
+  const int unit = blockIdx.x;                  // (s, l, g)
+  const int g = unit % p.Hkv;
+  const int sl = unit / p.Hkv;                  // s * L + l
+  const int G = p.Hq / p.Hkv;
+  const int lpr = p.D / E;                      // lanes per row
+  const int slots = 256 / lpr;
+  const int tid = threadIdx.x;
+  const int slot = tid / lpr, rl = tid % lpr;
+  const int64_t rows = static_cast<int64_t>(G) * p.W;
+  const uint8_t* base = static_cast<const uint8_t*>(q) +
+                        ((static_cast<int64_t>(sl) * p.Hq + static_cast<int64_t>(g) * G) * p.W * p.D) * esz;
+  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  for (int64_t r = slot; r < rows; r += slots) {
+    const uint4 v = *reinterpret_cast<const uint4*>(base + (r * p.D + rl * E) * esz);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    if constexpr (DT == KVSEL_F32) {
+      for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(w[i]);
+    } else {
+      for (int i = 0; i < 4; ++i) {
+        const uint16_t lo = static_cast<uint16_t>(w[i] & 0xFFFFu), hi = static_cast<uint16_t>(w[i] >> 16);
+        acc[2 * i] += (DT == KVSEL_BF16) ? bf16_to_f32(lo) : f16_to_f32(lo);
+        acc[2 * i + 1] += (DT == KVSEL_BF16) ? bf16_to_f32(hi) : f16_to_f32(hi);
+      }
+    }
+  }
+  for (int i = 0; i < 8; ++i) part[tid][i] = acc[i];
+  __syncthreads();
+  for (int d = tid; d < p.D; d += 256) {
+    const int l2 = d / E, i = d % E;
+    float s = 0.f;
+    for (int sl2 = 0; sl2 < slots; ++sl2) s += part[sl2 * lpr + l2][i];
+    qbar[static_cast<int64_t>(unit) * p.D + d] = s;
+  }
+}
+
+// out[s][u][b - n_begin] = scale * qbar[s][u] . mu[u][b] for b in the tile.
+// 16 bytes of a row per lane (D*2/16 lanes per row), S sessions at once, the
+// row dot finished with an xor-shuffle tree across the row's lanes.
+template <int S_MAX>
+__global__ __launch_bounds__(256) void block_scores_kernel(BlockParams p, const float* __restrict__ qbar,
+                                                           const uint16_t* __restrict__ mu,
+                                                           float* __restrict__ out) {
+  const int U = p.L * p.Hkv;
+  const int u = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int lpr = p.D / 8;                      // f16: 8 elements per 16 bytes
+  const int rows_per_wave = 64 / lpr;
+  const int rl = lane % lpr, rsub = lane / lpr;
+  float qb[S_MAX][8];
+  for (int s = 0; s < S_MAX; ++s)
+    for (int i = 0; i < 8; ++i)
+      qb[s][i] = (s < p.S) ? qbar[(static_cast<int64_t>(s) * U + u) * p.D + rl * 8 + i] : 0.f;
+  const uint16_t* mu_u = mu + (static_cast<int64_t>(u) * p.NB) * p.D;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
+  for (int64_t r0 = wave * rows_per_wave; r0 < p.n_count; r0 += n_waves * rows_per_wave) {
+    const int64_t r = r0 + rsub;
+    const bool ok = r < p.n_count;
+    uint4 v = make_uint4(0, 0, 0, 0);
+    if (ok) v = *reinterpret_cast<const uint4*>(mu_u + (p.n_begin + r) * p.D + rl * 8);
+    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+    float x[8];
+    for (int i = 0; i < 4; ++i) {
+      x[2 * i] = f16_to_f32(static_cast<uint16_t>(w[i] & 0xFFFFu));
+      x[2 * i + 1] = f16_to_f32(static_cast<uint16_t>(w[i] >> 16));
+    }
+    float acc[S_MAX];
+    for (int s = 0; s < S_MAX; ++s) {
+      float a = 0.f;
+      for (int i = 0; i < 8; ++i) a = fmaf(qb[s][i], x[i], a);
+      acc[s] = a;
+    }
+    for (int o = lpr / 2; o > 0; o >>= 1)
+      for (int s = 0; s < S_MAX; ++s) acc[s] += __shfl_xor(acc[s], o, 64);
+    if (ok) {
+      for (int s = 0; s < S_MAX; ++s)
+        if (s < p.S && rl == s) out[(static_cast<int64_t>(s) * U + u) * p.n_count + r] = acc[s] * p.scale;
+    }
+  }
+}
+
+hipError_t launch_query_reduce(const BlockParams& p, int dt, const void* q, float* qbar,
+                               hipStream_t st) {
+  const int units = p.S * p.L * p.Hkv;
+  if (units == 0) return hipSuccess;
+  if (dt == KVSEL_BF16) query_reduce_kernel<KVSEL_BF16><<<units, 256, 0, st>>>(p, q, qbar);
+  else if (dt == KVSEL_F16) query_reduce_kernel<KVSEL_F16><<<units, 256, 0, st>>>(p, q, qbar);
+  else query_reduce_kernel<KVSEL_F32><<<units, 256, 0, st>>>(p, q, qbar);
+  return hipGetLastError();
+}
+
+hipError_t launch_block_scores(const BlockParams& p, const float* qbar, const void* mu, float* out,
+                               hipStream_t st) {
+  const int U = p.L * p.Hkv;
+  if (U == 0 || p.n_count == 0 || p.S == 0) return hipSuccess;
+  const int rows_per_wave = 64 / (p.D / 8);
+  // ~8 rows per wave per block iteration, capped grid; the kernel strides
+  const int64_t blocks_x = ceil_div(p.n_count, static_cast<int64_t>(rows_per_wave) * 4 * 8);
+  dim3 grid(static_cast<unsigned>(blocks_x < 1 ? 1 : (blocks_x > 4096 ? 4096 : blocks_x)), U);
+  const uint16_t* m = static_cast<const uint16_t*>(mu);
+  if (p.S <= 1) block_scores_kernel<1><<<grid, 256, 0, st>>>(p, qbar, m, out);
+  else if (p.S <= 4) block_scores_kernel<4><<<grid, 256, 0, st>>>(p, qbar, m, out);
+  else block_scores_kernel<8><<<grid, 256, 0, st>>>(p, qbar, m, out);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -1,0 +1,229 @@
+// Gather of kept entries into a compact view, with optional re-RoPE of K.
+//
+// KVMem (tiered movement): selected blocks are packed into contiguous
+// logical positions; raw, position-free K is rotated for its new position
+// and V is copied unchanged.
+//
+// Two kernels:
+//  * rows: one row (D elements) per group of D*esz/16 lanes, 16 bytes per
+//    lane.  Any bt; RoPE angles computed per lane.  Used for token gathers.
+//  * blocks: one wavefront per (unit, kept entry) of bt >= 8 rows with RoPE.
+//    The rotation of row o at base position b is composed from a per-entry
+//    base rotation (one sincos per frequency and lane) and a per-workgroup
+//    table of the offsets o (angle addition), so trigonometry is amortised
+//    over bt rows.  Angles are formed and range-reduced in float64.
+#include "rope_dev.h"
+
+namespace kvsel {
+
+using namespace rope;
+
+namespace {
+
+__device__ __forceinline__ const uint8_t* unit_src(const void* base, const GatherParams& p, int u,
+                                                   int esz) {
+  const int64_t off = p.src_offsets ? p.src_offsets[u] : static_cast<int64_t>(u) * p.src_unit_stride;
+  return static_cast<const uint8_t*>(base) + off * esz;
+}
+
+}  // namespace
+
+// ------------------------------------------------------------------ rows kernel
+template <int DT>
+__global__ __launch_bounds__(256) void gather_rows_kernel(GatherParams p, RopeTable rt,
+                                                          const void* __restrict__ src_k,
+                                                          const void* __restrict__ src_v,
+                                                          const int32_t* __restrict__ idx,
+                                                          const int32_t* __restrict__ n_idx,
+                                                          void* __restrict__ dst_k,
+                                                          void* __restrict__ dst_v) {
+  constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
+  constexpr int E = Vec16<DT>::kElems;
+  const int lpr = p.D * esz / 16;          // lanes per row
+  const int rows_per_wave = 64 / lpr;
+  const int lane = threadIdx.x & 63;
+  const int rlane = lane % lpr;            // lane within its row
+  const int rsub = lane / lpr;             // row slot within the wave
+  const int64_t rows_per_unit = static_cast<int64_t>(p.k) * p.bt;
+  const int64_t total_rows = rows_per_unit * p.U;
+  const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
+  const int rd = p.rotary_dim;
+  const int d0 = rlane * E;
+  const bool interleaved = p.style == KVSEL_ROPE_INTERLEAVED;
+  const int half_lanes = (rd / 2) / E;
+  const bool in_rot = d0 < rd;
+  const bool first = d0 < rd / 2;
+  const int partner = first ? lane + half_lanes : lane - half_lanes;
+
+  for (int64_t r0 = wave_global * rows_per_wave; r0 < total_rows; r0 += n_waves * rows_per_wave) {
+    const int64_t r = r0 + rsub;
+    bool active = r < total_rows && rsub < rows_per_wave;
+    int u = 0;
+    int64_t i = 0, o = 0, srow = 0;
+    if (active) {
+      u = static_cast<int>(r / rows_per_unit);
+      const int64_t rr = r - static_cast<int64_t>(u) * rows_per_unit;
+      i = rr / p.bt;
+      o = rr - i * p.bt;
+      const int32_t b = idx[static_cast<int64_t>(u) * p.k + i];
+      const bool valid_i = n_idx == nullptr || i < n_idx[u];
+      srow = static_cast<int64_t>(b) * p.bt + o;
+      active = valid_i && b >= 0 && srow < p.src_rows;
+    }
+    uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+    if (active) {
+      const int64_t off = (srow * p.D) * esz + static_cast<int64_t>(d0) * esz;
+      kv = *reinterpret_cast<const uint4*>(unit_src(src_k, p, u, esz) + off);
+      vv = *reinterpret_cast<const uint4*>(unit_src(src_v, p, u, esz) + off);
+    }
+    if (p.rope != KVSEL_ROPE_NONE) {
+      const uint4 other = interleaved ? kv : shfl16(kv, partner);
+      if (active && in_rot) {
+        const int64_t pnew = p.pos0 + i * p.bt + o;
+        const double pos = (p.rope == KVSEL_ROPE_RAW) ? static_cast<double>(pnew)
+                                                      : static_cast<double>(pnew - srow);
+        float cs[E], sn[E];
+        const int npair = interleaved ? E / 2 : E;
+        for (int e = 0; e < npair; ++e) {
+          const int m = interleaved ? (d0 / 2 + e) : ((d0 % (rd / 2)) + e);
+          angle_sincos(pos, rt.inv_freq[m], &cs[e], &sn[e]);
+        }
+        kv = rotate_chunk<DT>(kv, other, first, interleaved, cs, sn);
+      }
+    }
+    if (active) {
+      const int64_t doff = ((static_cast<int64_t>(u) * rows_per_unit + i * p.bt + o) * p.D) * esz +
+                           static_cast<int64_t>(d0) * esz;
+      *reinterpret_cast<uint4*>(static_cast<uint8_t*>(dst_k) + doff) = kv;
+      *reinterpret_cast<uint4*>(static_cast<uint8_t*>(dst_v) + doff) = vv;
+    }
+  }
+}
+
+// ------------------------------------------------------------------ blocks kernel
+// Requires rotary_dim == D, bt * (D/2) <= kMaxOffTable, bt rows per entry.
+constexpr int kMaxOffTable = 32 * 64;
+
+template <int DT>
+__global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, RopeTable rt,
+                                                            const void* __restrict__ src_k,
+                                                            const void* __restrict__ src_v,
+                                                            const int32_t* __restrict__ idx,
+                                                            const int32_t* __restrict__ n_idx,
+                                                            void* __restrict__ dst_k,
+                                                            void* __restrict__ dst_v) {
+  constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
+  constexpr int E = Vec16<DT>::kElems;
+  __shared__ float2 off_tab[kMaxOffTable];   // (cos, sin) of o * inv_freq[m], [o][m]
+  const int half = p.D / 2;
+  const bool raw = p.rope == KVSEL_ROPE_RAW;
+  if (raw) {
+    for (int t = threadIdx.x; t < p.bt * half; t += blockDim.x) {
+      const int o = t / half, m = t - (t / half) * half;
+      float c, s;
+      angle_sincos(static_cast<double>(o), rt.inv_freq[m], &c, &s);
+      off_tab[t] = make_float2(c, s);
+    }
+  }
+  __syncthreads();
+
+  const int lane = threadIdx.x & 63;
+  const int lpr = p.D * esz / 16;               // lanes per row
+  const int rows_per_pass = 64 / lpr;
+  const int rlane = lane % lpr;
+  const int rsub = lane / lpr;
+  const int d0 = rlane * E;
+  const bool interleaved = p.style == KVSEL_ROPE_INTERLEAVED;
+  const bool first = d0 < half;
+  const int partner = first ? lane + lpr / 2 : lane - lpr / 2;
+  const int m0 = interleaved ? d0 / 2 : (d0 % half);
+  constexpr int NP = E;                          // pairs touched by this lane (upper bound)
+  const int npair = interleaved ? E / 2 : E;
+  const int64_t items = static_cast<int64_t>(p.U) * p.k;
+  const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
+  const int64_t row_bytes = static_cast<int64_t>(p.D) * esz;
+  const int64_t item_bytes = row_bytes * p.bt;
+
+  for (int64_t it = wave_global; it < items; it += n_waves) {
+    const int u = static_cast<int>(it / p.k);
+    const int64_t i = it - static_cast<int64_t>(u) * p.k;
+    if (n_idx != nullptr && i >= n_idx[u]) continue;
+    const int32_t b = idx[it];
+    if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
+    const int64_t base_pos = raw ? p.pos0 + i * p.bt : p.pos0 + (i - b) * p.bt;
+    float cb[NP], sb[NP];
+    for (int e = 0; e < npair; ++e)
+      angle_sincos(static_cast<double>(base_pos), rt.inv_freq[m0 + e], &cb[e], &sb[e]);
+    const uint8_t* sk = unit_src(src_k, p, u, esz) + static_cast<int64_t>(b) * item_bytes;
+    const uint8_t* sv = unit_src(src_v, p, u, esz) + static_cast<int64_t>(b) * item_bytes;
+    uint8_t* dk = static_cast<uint8_t*>(dst_k) + it * item_bytes;
+    uint8_t* dv = static_cast<uint8_t*>(dst_v) + it * item_bytes;
+    for (int o0 = 0; o0 < p.bt; o0 += rows_per_pass) {
+      const int o = o0 + rsub;
+      const bool act = o < p.bt;
+      const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
+      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+      if (act) {
+        kv = *reinterpret_cast<const uint4*>(sk + off);
+        vv = *reinterpret_cast<const uint4*>(sv + off);
+      }
+      const uint4 other = interleaved ? kv : shfl16(kv, partner);
+      if (act) {
+        float cs[NP], sn[NP];
+        for (int e = 0; e < npair; ++e) {
+          if (raw) {
+            const float2 t = off_tab[o * half + m0 + e];
+            cs[e] = cb[e] * t.x - sb[e] * t.y;
+            sn[e] = sb[e] * t.x + cb[e] * t.y;
+          } else {
+            cs[e] = cb[e];
+            sn[e] = sb[e];
+          }
+        }
+        kv = rotate_chunk<DT>(kv, other, first, interleaved, cs, sn);
+        *reinterpret_cast<uint4*>(dk + off) = kv;
+        *reinterpret_cast<uint4*>(dv + off) = vv;
+      }
+    }
+  }
+}
+
+static int grid_for(int64_t waves_wanted) {
+  const int64_t blocks = ceil_div(waves_wanted, 4);
+  return static_cast<int>(blocks < 1 ? 1 : (blocks > 65536 ? 65536 : blocks));
+}
+
+hipError_t launch_gather_fresh(const GatherParams& p, const RopeTable& rt, const void* src_k,
+                               const void* src_v, const int32_t* idx, const int32_t* n_idx,
+                               void* dst_k, void* dst_v, hipStream_t st) {
+  if (p.U == 0 || p.k == 0) return hipSuccess;
+  const int esz = p.dtype == KVSEL_F32 ? 4 : 2;
+  const int lpr = p.D * esz / 16;
+  const bool blocks_path = p.rope != KVSEL_ROPE_NONE && p.bt >= 8 && p.rotary_dim == p.D &&
+                           p.bt * (p.D / 2) <= kMaxOffTable && lpr <= 64;
+  if (blocks_path) {
+    const int grid = grid_for(static_cast<int64_t>(p.U) * p.k);
+#define KVSEL_GB(DTV)                                                                           \
+  gather_blocks_kernel<DTV><<<grid, 256, 0, st>>>(p, rt, src_k, src_v, idx, n_idx, dst_k, dst_v)
+    if (p.dtype == KVSEL_BF16) KVSEL_GB(KVSEL_BF16);
+    else if (p.dtype == KVSEL_F16) KVSEL_GB(KVSEL_F16);
+    else KVSEL_GB(KVSEL_F32);
+#undef KVSEL_GB
+  } else {
+    const int64_t rows = static_cast<int64_t>(p.U) * p.k * p.bt;
+    const int rows_per_wave = 64 / lpr;
+    // a few rows per wave in flight; grid capped, kernel strides
+    const int grid = grid_for(ceil_div(rows, static_cast<int64_t>(rows_per_wave) * 4));
+#define KVSEL_GR(DTV)                                                                         \
+  gather_rows_kernel<DTV><<<grid, 256, 0, st>>>(p, rt, src_k, src_v, idx, n_idx, dst_k, dst_v)
+    if (p.dtype == KVSEL_BF16) KVSEL_GR(KVSEL_BF16);
+    else if (p.dtype == KVSEL_F16) KVSEL_GR(KVSEL_F16);
+    else KVSEL_GR(KVSEL_F32);
+#undef KVSEL_GR
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -1,0 +1,278 @@
+// Incremental update of a paged execution view between consecutive steps.
+//
+// KVMem (tiered movement): pages that overlap across consecutive steps stay
+// on the GPU; missed blocks are scattered in and re-RoPEd at their new
+// positions.  Reading taken here (the pages give no placement rule):
+//  * a block in both views keeps its page and V; its K is rotated in place by
+//    the change of its logical position, (i_new - i_old) * bt;
+//  * pages of blocks that left the view are freed and handed, in ascending
+//    page order, to the missed blocks in ascending block order;
+//  * a missed block gets raw K rotated to pos0 + i_new*bt + o and V copied.
+// Hit pages, freed pages and miss pages are disjoint, so all moves run in one
+// pass with no conflicts (the concern ActKV §7.2 plans around for in-place
+// compaction).
+//
+// plan kernel: one workgroup per unit.  Membership by binary search over the
+// two ascending index lists staged in LDS; freed pages ordered by a bitmap
+// over page ids and a prefix count of its words; misses ranked with a
+// ballot prefix.  data kernel: one wavefront per (unit, kept entry).
+#include "rope_dev.h"
+
+namespace kvsel {
+
+using namespace rope;
+
+namespace {
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+constexpr int64_t kMaxPoolPages = 1 << 18;      // bitmap <= 32 KiB
+constexpr int kMaxK = 8192;
+constexpr int kMaxOffTable = 32 * 64;
+
+__device__ __forceinline__ int find_sorted(const int32_t* a, int n, int32_t x) {
+  int lo = 0, hi = n - 1;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    const int32_t v = a[mid];
+    if (v == x) return mid;
+    if (v < x) lo = mid + 1;
+    else hi = mid - 1;
+  }
+  return -1;
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+}
+}  // namespace
+
+size_t incremental_workspace_bytes(const GatherParams& p) {
+  return static_cast<size_t>(p.U) * p.k * sizeof(int32_t);   // i_old per new entry (-1 = miss)
+}
+
+__global__ __launch_bounds__(kPlanThreads) void incremental_plan_kernel(
+    GatherParams p, const int32_t* __restrict__ idx, const int32_t* __restrict__ prev_idx,
+    const int32_t* __restrict__ prev_page, int32_t* __restrict__ page_table,
+    int32_t* __restrict__ n_miss, int32_t* __restrict__ plan_old) {
+  extern __shared__ uint32_t sm[];
+  __shared__ uint32_t wave_cnt[kPlanWaves];
+  __shared__ uint32_t word_scan[kPlanThreads];
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int k = p.k;
+  const int64_t nw = (p.pool_pages + 31) / 32;
+  int32_t* s_new = reinterpret_cast<int32_t*>(sm);
+  int32_t* s_prev = s_new + k;
+  int32_t* s_freed = s_prev + k;
+  uint32_t* bitmap = reinterpret_cast<uint32_t*>(s_freed + k);
+  const int32_t* new_u = idx + static_cast<int64_t>(u) * k;
+  const int32_t* prev_u = prev_idx + static_cast<int64_t>(u) * k;
+  const int32_t* ppage_u = prev_page + static_cast<int64_t>(u) * k;
+  for (int i = tid; i < k; i += kPlanThreads) {
+    s_new[i] = new_u[i];
+    s_prev[i] = prev_u[i];
+    s_freed[i] = -1;
+  }
+  for (int64_t w = tid; w < nw; w += kPlanThreads) bitmap[w] = 0u;
+  __syncthreads();
+  // pages of previous blocks that are not in the new view
+  for (int i = tid; i < k; i += kPlanThreads) {
+    if (find_sorted(s_new, k, s_prev[i]) < 0) {
+      const int32_t pg = ppage_u[i];
+      if (pg >= 0 && pg < p.pool_pages) atomicOr(&bitmap[pg >> 5], 1u << (pg & 31));
+    }
+  }
+  __syncthreads();
+  // rank of each freed page = number of freed pages with a smaller id
+  const int64_t wpt = (nw + kPlanThreads - 1) / kPlanThreads;
+  const int64_t w0 = min(nw, static_cast<int64_t>(tid) * wpt), w1 = min(nw, w0 + wpt);
+  uint32_t cnt = 0;
+  for (int64_t w = w0; w < w1; ++w) cnt += __popc(bitmap[w]);
+  word_scan[tid] = cnt;
+  __syncthreads();
+  for (int off = 1; off < kPlanThreads; off <<= 1) {       // inclusive scan
+    const uint32_t v = (tid >= off) ? word_scan[tid - off] : 0u;
+    __syncthreads();
+    word_scan[tid] += v;
+    __syncthreads();
+  }
+  uint32_t rank = word_scan[tid] - cnt;
+  for (int64_t w = w0; w < w1; ++w) {
+    uint32_t bits = bitmap[w];
+    while (bits) {
+      const int b = __ffs(bits) - 1;
+      bits &= bits - 1;
+      if (rank < static_cast<uint32_t>(k)) s_freed[rank] = static_cast<int32_t>(w * 32 + b);
+      ++rank;
+    }
+  }
+  __syncthreads();
+  // misses in ascending order take the freed pages in ascending order
+  const int seg = ((k + kPlanWaves - 1) / kPlanWaves + 63) / 64 * 64;
+  const int s_beg = min(k, wave * seg), s_end = min(k, s_beg + seg);
+  uint32_t nm = 0;
+  for (int i0 = s_beg; i0 < s_end; i0 += 64) {
+    const int i = i0 + lane;
+    const bool miss = i < s_end && find_sorted(s_prev, k, s_new[i]) < 0;
+    nm += __popcll(__ballot(miss));
+  }
+  if (lane == 0) wave_cnt[wave] = nm;
+  __syncthreads();
+  uint32_t base = 0;
+  for (int w = 0; w < wave; ++w) base += wave_cnt[w];
+  int32_t* pt_u = page_table + static_cast<int64_t>(u) * k;
+  int32_t* old_u = plan_old + static_cast<int64_t>(u) * k;
+  for (int i0 = s_beg; i0 < s_end; i0 += 64) {
+    const int i = i0 + lane;
+    int io = -1;
+    if (i < s_end) io = find_sorted(s_prev, k, s_new[i]);
+    const bool miss = i < s_end && io < 0;
+    const uint64_t b = __ballot(miss);
+    if (i < s_end) {
+      if (miss) {
+        const uint32_t r = base + __popcll(b & lanemask_lt(lane));
+        pt_u[i] = (r < static_cast<uint32_t>(k)) ? s_freed[r] : -1;
+        old_u[i] = -1;
+      } else {
+        pt_u[i] = ppage_u[io];
+        old_u[i] = io;
+      }
+    }
+    base += __popcll(b);
+  }
+  if (tid == 0) {
+    uint32_t t = 0;
+    for (int w = 0; w < kPlanWaves; ++w) t += wave_cnt[w];
+    n_miss[u] = static_cast<int32_t>(t);
+  }
+}
+
+template <int DT>
+__global__ __launch_bounds__(256) void incremental_data_kernel(
+    GatherParams p, RopeTable rt, const void* __restrict__ src_k, const void* __restrict__ src_v,
+    const int32_t* __restrict__ idx, const int32_t* __restrict__ page_table,
+    const int32_t* __restrict__ plan_old, void* __restrict__ pool_k, void* __restrict__ pool_v) {
+  constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
+  constexpr int E = Vec16<DT>::kElems;
+  __shared__ float2 off_tab[kMaxOffTable];
+  const int half = p.D / 2;
+  const bool rot = p.rope == KVSEL_ROPE_RAW;
+  if (rot) {
+    for (int t = threadIdx.x; t < p.bt * half; t += blockDim.x) {
+      const int o = t / half, m = t - (t / half) * half;
+      float c, s;
+      angle_sincos(static_cast<double>(o), rt.inv_freq[m], &c, &s);
+      off_tab[t] = make_float2(c, s);
+    }
+  }
+  __syncthreads();
+  const int lane = threadIdx.x & 63;
+  const int lpr = p.D * esz / 16;
+  const int rows_per_pass = 64 / lpr;
+  const int rlane = lane % lpr, rsub = lane / lpr;
+  const int d0 = rlane * E;
+  const bool interleaved = p.style == KVSEL_ROPE_INTERLEAVED;
+  const bool first = d0 < half;
+  const int partner = first ? lane + lpr / 2 : lane - lpr / 2;
+  const int m0 = interleaved ? d0 / 2 : (d0 % half);
+  const int npair = interleaved ? E / 2 : E;
+  const int64_t items = static_cast<int64_t>(p.U) * p.k;
+  const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
+  const int64_t row_bytes = static_cast<int64_t>(p.D) * esz;
+  const int64_t item_bytes = row_bytes * p.bt;
+
+  for (int64_t it = wave_global; it < items; it += n_waves) {
+    const int u = static_cast<int>(it / p.k);
+    const int64_t i = it - static_cast<int64_t>(u) * p.k;
+    const int32_t page = page_table[it];
+    if (page < 0 || page >= p.pool_pages) continue;
+    const int32_t io = plan_old[it];
+    uint8_t* pk = static_cast<uint8_t*>(pool_k) + (static_cast<int64_t>(u) * p.pool_pages + page) * item_bytes;
+    uint8_t* pv = static_cast<uint8_t*>(pool_v) + (static_cast<int64_t>(u) * p.pool_pages + page) * item_bytes;
+    if (io >= 0) {
+      // hit: rotate K in place by the position change (V untouched)
+      const int64_t delta = (i - io) * p.bt;
+      if (delta == 0 || !rot) continue;
+      float cb[E], sb[E];
+      for (int e = 0; e < npair; ++e)
+        angle_sincos(static_cast<double>(delta), rt.inv_freq[m0 + e], &cb[e], &sb[e]);
+      for (int o0 = 0; o0 < p.bt; o0 += rows_per_pass) {
+        const int o = o0 + rsub;
+        const bool act = o < p.bt;
+        const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
+        uint4 kv = act ? *reinterpret_cast<const uint4*>(pk + off) : make_uint4(0, 0, 0, 0);
+        const uint4 other = interleaved ? kv : shfl16(kv, partner);
+        if (act) *reinterpret_cast<uint4*>(pk + off) = rotate_chunk<DT>(kv, other, first, interleaved, cb, sb);
+      }
+    } else {
+      // miss: raw K rotated to its new position, V copied
+      const int32_t b = idx[it];
+      if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
+      const int64_t soff = p.src_offsets ? p.src_offsets[u] : static_cast<int64_t>(u) * p.src_unit_stride;
+      const uint8_t* sk = static_cast<const uint8_t*>(src_k) + soff * esz + static_cast<int64_t>(b) * item_bytes;
+      const uint8_t* sv = static_cast<const uint8_t*>(src_v) + soff * esz + static_cast<int64_t>(b) * item_bytes;
+      float cb[E], sb[E];
+      if (rot)
+        for (int e = 0; e < npair; ++e)
+          angle_sincos(static_cast<double>(p.pos0 + i * p.bt), rt.inv_freq[m0 + e], &cb[e], &sb[e]);
+      for (int o0 = 0; o0 < p.bt; o0 += rows_per_pass) {
+        const int o = o0 + rsub;
+        const bool act = o < p.bt;
+        const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
+        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
+        if (act) {
+          kv = *reinterpret_cast<const uint4*>(sk + off);
+          vv = *reinterpret_cast<const uint4*>(sv + off);
+        }
+        if (rot) {
+          const uint4 other = interleaved ? kv : shfl16(kv, partner);
+          if (act) {
+            float cs[E], sn[E];
+            for (int e = 0; e < npair; ++e) {
+              const float2 t = off_tab[o * half + m0 + e];
+              cs[e] = cb[e] * t.x - sb[e] * t.y;
+              sn[e] = sb[e] * t.x + cb[e] * t.y;
+            }
+            kv = rotate_chunk<DT>(kv, other, first, interleaved, cs, sn);
+          }
+        }
+        if (act) {
+          *reinterpret_cast<uint4*>(pk + off) = kv;
+          *reinterpret_cast<uint4*>(pv + off) = vv;
+        }
+      }
+    }
+  }
+}
+
+hipError_t launch_gather_incremental(const GatherParams& p, const RopeTable& rt, const void* src_k,
+                                     const void* src_v, const int32_t* idx, const int32_t* prev_idx,
+                                     const int32_t* prev_page, void* pool_k, void* pool_v,
+                                     int32_t* page_table, int32_t* n_miss, void* ws, hipStream_t st) {
+  if (p.U == 0 || p.k == 0) return hipSuccess;
+  if (p.k > kMaxK || p.pool_pages > kMaxPoolPages || p.rotary_dim != p.D ||
+      (p.rope == KVSEL_ROPE_RAW && p.bt * (p.D / 2) > kMaxOffTable))
+    return hipErrorNotSupported;
+  int32_t* plan_old = static_cast<int32_t*>(ws);
+  const size_t sh = static_cast<size_t>(p.k) * 3 * 4 + static_cast<size_t>((p.pool_pages + 31) / 32) * 4;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&incremental_plan_kernel),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(sh));
+  if (e != hipSuccess) return e;
+  incremental_plan_kernel<<<p.U, kPlanThreads, sh, st>>>(p, idx, prev_idx, prev_page, page_table, n_miss,
+                                                         plan_old);
+  if ((e = hipGetLastError()) != hipSuccess) return e;
+  const int64_t items = static_cast<int64_t>(p.U) * p.k;
+  const int64_t blocks = ceil_div(items, 4);
+  const int grid = static_cast<int>(blocks > 65536 ? 65536 : blocks);
+#define KVSEL_ID(DTV)                                                                              \
+  incremental_data_kernel<DTV><<<grid, 256, 0, st>>>(p, rt, src_k, src_v, idx, page_table, plan_old, \
+                                                     pool_k, pool_v)
+  if (p.dtype == KVSEL_BF16) KVSEL_ID(KVSEL_BF16);
+  else if (p.dtype == KVSEL_F16) KVSEL_ID(KVSEL_F16);
+  else KVSEL_ID(KVSEL_F32);
+#undef KVSEL_ID
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

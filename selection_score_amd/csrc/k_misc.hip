@@ -1,0 +1,89 @@
+// Slot-map redirect, dead-slot sentinel rows, and the session memory update.
+#include "common.h"
+
+#include <math.h>
+
+namespace kvsel {
+
+// IntentKV §4 (redirect): dropped positions point at the dead slot; kept
+// positions keep their slot ids.
+__global__ void redirect_kernel(int64_t N, int32_t* __restrict__ slot_map,
+                                const uint8_t* __restrict__ keep, int32_t dead) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j < N && keep[j] == 0) slot_map[j] = dead;
+}
+
+// IntentKV §2 Q2: the dead slot holds K = -1e4 (rounded to the pool's
+// 16-bit format) and V = 0 in every layer and KV head.
+__global__ void sentinel_kernel(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
+                                int L, int Hkv, int D, uint16_t k_bits, int64_t pool_slots,
+                                int64_t dead) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t per_layer = static_cast<int64_t>(Hkv) * D;
+  if (i >= per_layer * L) return;
+  const int64_t l = i / per_layer, r = i % per_layer;
+  const int64_t off = (l * pool_slots + dead) * per_layer + r;
+  k_pool[off] = k_bits;
+  v_pool[off] = 0;
+}
+
+// IntentKV §4 (memory recurrence) and §7 (unit-norm projection): one
+// wavefront per (layer, query head).
+template <int DT>
+__global__ __launch_bounds__(256) void memory_update_kernel(int LH, int D, int W,
+                                                            const void* __restrict__ q,
+                                                            float* __restrict__ M, float decay) {
+  const int lane = threadIdx.x & 63;
+  const int lh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (lh >= LH) return;
+  float m[4];
+  float nn = 0.f;
+  for (int c = 0; c < 4; ++c) {
+    const int d = lane + 64 * c;
+    m[c] = 0.f;
+    if (d >= D) continue;
+    float s = 0.f;
+    for (int t = 0; t < W; ++t) s += load_elem<DT>(q, (static_cast<int64_t>(lh) * W + t) * D + d);
+    m[c] = decay * M[static_cast<int64_t>(lh) * D + d] + s / static_cast<float>(W);
+    nn += m[c] * m[c];
+  }
+  for (int o = 32; o > 0; o >>= 1) nn += __shfl_xor(nn, o, 64);
+  const float inv = (nn > 0.f) ? 1.0f / sqrtf(nn) : 0.f;
+  for (int c = 0; c < 4; ++c) {
+    const int d = lane + 64 * c;
+    if (d < D) M[static_cast<int64_t>(lh) * D + d] = m[c] * inv;
+  }
+}
+
+hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, int64_t dead,
+                           hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  redirect_kernel<<<static_cast<int>(ceil_div(N, 256)), 256, 0, st>>>(N, slot_map, keep,
+                                                                     static_cast<int32_t>(dead));
+  return hipGetLastError();
+}
+
+hipError_t launch_sentinel(void* k_pool, void* v_pool, int L, int Hkv, int D, int dtype,
+                           int64_t pool_slots, int64_t dead, hipStream_t st) {
+  const int64_t n = static_cast<int64_t>(L) * Hkv * D;
+  if (n == 0) return hipSuccess;
+  // -1e4 rounded to the storage format: bf16 -9984 (0xC61C), f16 -10000 (0xF0E2)
+  const uint16_t bits = (dtype == KVSEL_BF16) ? 0xC61Cu : 0xF0E2u;
+  sentinel_kernel<<<static_cast<int>(ceil_div(n, 256)), 256, 0, st>>>(
+      static_cast<uint16_t*>(k_pool), static_cast<uint16_t*>(v_pool), L, Hkv, D, bits, pool_slots,
+      dead);
+  return hipGetLastError();
+}
+
+hipError_t launch_memory_update(int L, int Hq, int D, int W, int dt, const void* q, float* M,
+                                float decay, hipStream_t st) {
+  const int LH = L * Hq;
+  if (LH == 0) return hipSuccess;
+  const int grid = static_cast<int>(ceil_div(LH, 4));
+  if (dt == KVSEL_BF16) memory_update_kernel<KVSEL_BF16><<<grid, 256, 0, st>>>(LH, D, W, q, M, decay);
+  else if (dt == KVSEL_F16) memory_update_kernel<KVSEL_F16><<<grid, 256, 0, st>>>(LH, D, W, q, M, decay);
+  else memory_update_kernel<KVSEL_F32><<<grid, 256, 0, st>>>(LH, D, W, q, M, decay);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -1,0 +1,352 @@
+// Budgeted top-k with a forced set, restored to chronological order.
+//
+// IntentKV §4 (top-k selection): keep the forced set plus the best of the
+// rest up to the budget.  KVMem (query-conditioned retrieval): sink and
+// recent entries are forced, the rest is filled by score, and the result is
+// listed in chronological order.  IntentKV §3: dead positions are never
+// candidates.
+//
+// One workgroup (16 wavefronts) per unit.  Scores become order-preserving
+// uint32 keys; an MSB-first 8-bit radix select over LDS histograms finds the
+// threshold key T and how many entries equal to T to take.  Ties at T go to
+// the lower index: the candidate sequence (running candidates from earlier
+// tiles, then this tile's columns) is in ascending global index, and a
+// ballot-based prefix count over it ranks the T-valued entries.  A second
+// ballot prefix places the selected entries, which therefore come out in
+// ascending index order without a sort.
+#include "common.h"
+
+namespace kvsel {
+
+namespace {
+
+constexpr int kThreads = 1024;
+constexpr int kWaves = kThreads / 64;
+constexpr int64_t kLdsKeysMax = 32768;   // tile keys kept in LDS up to this many
+
+struct SelShared {
+  uint32_t hist[256];
+  uint32_t wave_eq[kWaves];
+  uint32_t wave_gt[kWaves];
+  uint32_t wave_cnt[kWaves];
+  uint32_t prefix;
+  int32_t remaining;
+  int32_t forced_sink_alive;
+  int32_t forced_recent_alive;
+};
+
+struct Ctx {
+  const float* row;
+  int pool, pool_r;      // on-the-fly pooling of the row (untiled calls)
+  const uint32_t* ckey;  // running candidates (LDS)
+  const int32_t* cidx;
+  const uint32_t* tkey;  // tile keys (LDS) or nullptr
+  int c0;
+  int64_t n, base, sink_end, rec_begin;
+  const int32_t* slot_map;
+  int64_t dead;
+};
+
+__device__ __forceinline__ bool alive_at(const Ctx& c, int64_t g) {
+  return c.slot_map == nullptr || static_cast<int64_t>(c.slot_map[g]) != c.dead;
+}
+
+__device__ __forceinline__ bool forced_at(const Ctx& c, int64_t g) {
+  return g < c.sink_end || g >= c.rec_begin;
+}
+
+// Score of tile column j, pooled over the in-range window if asked.
+__device__ __forceinline__ float column_score(const Ctx& c, int64_t j) {
+  if (c.pool == KVSEL_POOL_NONE) return c.row[j];
+  const int64_t lo = max(static_cast<int64_t>(0), j - c.pool_r);
+  const int64_t hi = min(c.n - 1, j + c.pool_r);
+  if (c.pool == KVSEL_POOL_MAX) {
+    float m = c.row[lo];
+    for (int64_t i = lo + 1; i <= hi; ++i) m = fmaxf(m, c.row[i]);
+    return m;
+  }
+  float s = 0.f;
+  for (int64_t i = j - c.pool_r; i <= j + c.pool_r; ++i) s += (i >= lo && i <= hi) ? c.row[i] : 0.f;
+  return s / static_cast<float>(2 * c.pool_r + 1);
+}
+
+// Key of virtual entry e (0 = not a candidate) and its global index.
+__device__ __forceinline__ uint32_t entry_key(const Ctx& c, int64_t e, int64_t* gidx) {
+  if (e < c.c0) {
+    *gidx = c.cidx[e];
+    return c.ckey[e];
+  }
+  const int64_t j = e - c.c0;
+  const int64_t g = c.base + j;
+  *gidx = g;
+  if (c.tkey != nullptr) return c.tkey[j];
+  if (forced_at(c, g) || !alive_at(c, g)) return 0u;
+  return score_key(column_score(c, j));
+}
+
+__device__ __forceinline__ uint64_t lanemask_lt(int lane) {
+  return (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+}
+
+// Block-wide sum of a per-thread value (all threads must call).
+__device__ uint32_t block_sum(uint32_t v, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) v += __shfl_xor(v, o, 64);
+  __syncthreads();
+  if (lane == 0) scratch[wave] = v;
+  __syncthreads();
+  uint32_t t = 0;
+  for (int w = 0; w < kWaves; ++w) t += scratch[w];
+  __syncthreads();
+  return t;
+}
+
+}  // namespace
+
+template <bool KEYS_IN_LDS>
+__global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const float* scores) {
+  extern __shared__ uint32_t dyn[];
+  __shared__ SelShared sh;
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+  Ctx c;
+  c.row = scores + static_cast<int64_t>(u) * p.row_stride;
+  c.pool = p.pool;
+  c.pool_r = p.pool_k / 2;
+  c.n = p.n;
+  c.base = p.base;
+  c.sink_end = min(static_cast<int64_t>(p.n_sink), p.n_total);
+  c.rec_begin = max(c.sink_end, p.n_total - static_cast<int64_t>(p.n_recent));
+  c.slot_map = p.slot_map;
+  c.dead = p.dead_slot;
+  c.c0 = (p.cand_count != nullptr) ? min(max(p.cand_count[u], 0), p.k_total) : 0;
+  const int kcap = p.k_total;
+  uint32_t* ckey = dyn;
+  int32_t* cidx = reinterpret_cast<int32_t*>(dyn + (p.cand_count != nullptr ? kcap : 0));
+  uint32_t* tkey = dyn + (p.cand_count != nullptr ? 2 * kcap : 0);
+  c.ckey = ckey;
+  c.cidx = cidx;
+  c.tkey = KEYS_IN_LDS ? tkey : nullptr;
+
+  // ---- alive forced positions of the whole unit
+  uint32_t fs = 0, fr = 0;
+  for (int64_t g = tid; g < c.sink_end; g += kThreads) fs += alive_at(c, g) ? 1u : 0u;
+  for (int64_t g = c.rec_begin + tid; g < p.n_total; g += kThreads) fr += alive_at(c, g) ? 1u : 0u;
+  const uint32_t fsum = block_sum(fs, sh.wave_cnt);
+  const uint32_t rsum = block_sum(fr, sh.wave_cnt);
+  const int32_t room = p.k_total - static_cast<int32_t>(fsum + rsum);
+
+  // ---- stage running candidates and (optionally) this tile's keys in LDS
+  for (int e = tid; e < c.c0; e += kThreads) {
+    const int64_t o = static_cast<int64_t>(u) * kcap + e;
+    ckey[e] = score_key(p.cand_score[o]);
+    cidx[e] = p.cand_idx[o];
+  }
+  if constexpr (KEYS_IN_LDS) {
+    for (int64_t j = tid; j < c.n; j += kThreads) {
+      const int64_t g = c.base + j;
+      tkey[j] = (forced_at(c, g) || !alive_at(c, g)) ? 0u : score_key(column_score(c, j));
+    }
+  }
+  __syncthreads();
+
+  const int64_t M = c.c0 + c.n;
+  uint32_t cc = 0;
+  for (int64_t e = tid; e < M; e += kThreads) {
+    int64_t g;
+    cc += entry_key(c, e, &g) != 0u ? 1u : 0u;
+  }
+  const uint32_t n_cand = block_sum(cc, sh.wave_cnt);
+
+  // ---- radix select of the room-th largest key
+  uint32_t T;
+  int32_t remaining;
+  if (static_cast<int64_t>(n_cand) <= static_cast<int64_t>(room)) {
+    T = 1u;                 // no finite score maps to key 1: every candidate is "> T"
+    remaining = 0;
+  } else if (room <= 0) {
+    T = 0xFFFFFFFFu;        // no finite score maps to this key: nothing is selected
+    remaining = 0;
+  } else {
+    if (tid == 0) {
+      sh.prefix = 0u;
+      sh.remaining = room;
+    }
+    for (int shift = 24; shift >= 0; shift -= 8) {
+      const uint32_t hi_mask = (shift == 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
+      for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0u;
+      __syncthreads();
+      const uint32_t prefix = sh.prefix;
+      for (int64_t e = tid; e < M; e += kThreads) {
+        int64_t g;
+        const uint32_t key = entry_key(c, e, &g);
+        if (key != 0u && ((key ^ prefix) & hi_mask) == 0u)
+          atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) {
+        // lane l owns bins 4l..4l+3; find the bin where the count from the top
+        // reaches `remaining`
+        uint32_t h[4];
+        uint32_t own = 0;
+        for (int i = 0; i < 4; ++i) {
+          h[i] = sh.hist[4 * lane + i];
+          own += h[i];
+        }
+        // inclusive suffix sum over lanes (lanes above me plus mine)
+        uint32_t suf = own;
+        for (int o = 1; o < 64; o <<= 1) {
+          const uint32_t v = __shfl_down(suf, o, 64);
+          if (lane + o < 64) suf += v;
+        }
+        const uint32_t above_lane = suf - own;   // bins above my range
+        const int32_t rem = sh.remaining;
+        uint32_t acc = above_lane;
+        int found = -1;
+        uint32_t above_bin = 0;
+        if (above_lane < static_cast<uint32_t>(rem) && suf >= static_cast<uint32_t>(rem)) {
+          for (int i = 3; i >= 0; --i) {
+            if (acc + h[i] >= static_cast<uint32_t>(rem)) {
+              found = 4 * lane + i;
+              above_bin = acc;
+              break;
+            }
+            acc += h[i];
+          }
+        }
+        if (found >= 0) {
+          sh.prefix = prefix | (static_cast<uint32_t>(found) << shift);
+          sh.remaining = rem - static_cast<int32_t>(above_bin);
+        }
+      }
+      __syncthreads();
+    }
+    T = sh.prefix;
+    remaining = sh.remaining;
+  }
+
+  // ---- sweep A: per-wave counts of keys == T and > T over contiguous segments
+  const int64_t seg = ((M + kWaves - 1) / kWaves + 63) / 64 * 64;
+  const int64_t s_beg = min(M, static_cast<int64_t>(wave) * seg);
+  const int64_t s_end = min(M, s_beg + seg);
+  uint32_t n_eq = 0, n_gt = 0;
+  for (int64_t e0 = s_beg; e0 < s_end; e0 += 64) {
+    const int64_t e = e0 + lane;
+    uint32_t key = 0u;
+    if (e < s_end) {
+      int64_t g;
+      key = entry_key(c, e, &g);
+    }
+    n_eq += __popcll(__ballot(key != 0u && key == T));
+    n_gt += __popcll(__ballot(key != 0u && key > T));
+  }
+  if (lane == 0) {
+    sh.wave_eq[wave] = n_eq;
+    sh.wave_gt[wave] = n_gt;
+  }
+  __syncthreads();
+  uint32_t eq_base = 0, sel_base = 0;
+  for (int w = 0; w < wave; ++w) {
+    const int32_t take_eq = max(0, min(static_cast<int32_t>(sh.wave_eq[w]),
+                                       remaining - static_cast<int32_t>(eq_base)));
+    sel_base += sh.wave_gt[w] + static_cast<uint32_t>(take_eq);
+    eq_base += sh.wave_eq[w];
+  }
+  uint32_t n_sel_total = 0;
+  {
+    uint32_t eb = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int32_t take_eq = max(0, min(static_cast<int32_t>(sh.wave_eq[w]),
+                                         remaining - static_cast<int32_t>(eb)));
+      n_sel_total += sh.wave_gt[w] + static_cast<uint32_t>(take_eq);
+      eb += sh.wave_eq[w];
+    }
+  }
+
+  // ---- sweep B: place the selected entries in ascending index order
+  const int64_t sink_alive = static_cast<int64_t>(fsum);
+  const bool untiled_mask = p.finalize && p.keep_mask != nullptr;
+  int32_t* kept = p.kept_idx + static_cast<int64_t>(u) * p.k_total;
+  for (int64_t e0 = s_beg; e0 < s_end; e0 += 64) {
+    const int64_t e = e0 + lane;
+    uint32_t key = 0u;
+    int64_t g = -1;
+    if (e < s_end) key = entry_key(c, e, &g);
+    const bool is_eq = key != 0u && key == T;
+    const bool is_gt = key != 0u && key > T;
+    const uint64_t beq = __ballot(is_eq);
+    const uint32_t eq_rank = eq_base + __popcll(beq & lanemask_lt(lane));
+    const bool sel = is_gt || (is_eq && static_cast<int32_t>(eq_rank) < remaining);
+    const uint64_t bsel = __ballot(sel);
+    const uint32_t pos = sel_base + __popcll(bsel & lanemask_lt(lane));
+    if (sel) {
+      if (p.finalize) {
+        kept[sink_alive + pos] = static_cast<int32_t>(g);
+      } else {
+        const int64_t o = static_cast<int64_t>(u) * p.k_total + pos;
+        p.cand_score[o] = key_score(key);
+        p.cand_idx[o] = static_cast<int32_t>(g);
+      }
+    }
+    if (untiled_mask && e < s_end) {
+      const bool keep = sel || (forced_at(c, g) && alive_at(c, g));
+      p.keep_mask[static_cast<int64_t>(u) * p.n_total + g] = keep ? 1 : 0;
+    }
+    eq_base += __popcll(beq);
+    sel_base += __popcll(bsel);
+  }
+
+  if (!p.finalize) {
+    if (tid == 0) p.cand_count[u] = static_cast<int32_t>(n_sel_total);
+    return;
+  }
+
+  // ---- forced entries: alive sink first, alive recent last
+  if (wave == 0) {
+    uint32_t r = 0;
+    for (int64_t g0 = 0; g0 < c.sink_end; g0 += 64) {
+      const int64_t g = g0 + lane;
+      const bool a = g < c.sink_end && alive_at(c, g);
+      const uint64_t b = __ballot(a);
+      if (a) kept[r + __popcll(b & lanemask_lt(lane))] = static_cast<int32_t>(g);
+      r += __popcll(b);
+    }
+  } else if (wave == 1) {
+    uint32_t r = static_cast<uint32_t>(sink_alive) + n_sel_total;
+    for (int64_t g0 = c.rec_begin; g0 < p.n_total; g0 += 64) {
+      const int64_t g = g0 + lane;
+      const bool a = g < p.n_total && alive_at(c, g);
+      const uint64_t b = __ballot(a);
+      if (a) kept[r + __popcll(b & lanemask_lt(lane))] = static_cast<int32_t>(g);
+      r += __popcll(b);
+    }
+  }
+  const int64_t total = sink_alive + n_sel_total + rsum;
+  for (int64_t i = total + tid; i < p.k_total; i += kThreads) kept[i] = -1;
+  if (tid == 0 && p.n_kept != nullptr) p.n_kept[u] = static_cast<int32_t>(total);
+}
+
+hipError_t launch_select(const SelectParams& p, const float* scores, hipStream_t st) {
+  if (p.U == 0) return hipSuccess;
+  const bool tiled = p.cand_count != nullptr;
+  const size_t cand_bytes = tiled ? static_cast<size_t>(p.k_total) * 8 : 0;
+  const bool lds_keys = p.n <= kLdsKeysMax && cand_bytes + static_cast<size_t>(p.n) * 4 <= 150 * 1024;
+  const size_t shmem = cand_bytes + (lds_keys ? static_cast<size_t>(p.n) * 4 : 0);
+  if (lds_keys) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<true>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(shmem));
+    if (e != hipSuccess) return e;
+    select_kernel<true><<<p.U, kThreads, shmem, st>>>(p, scores);
+  } else {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<false>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(shmem));
+    if (e != hipSuccess) return e;
+    select_kernel<false><<<p.U, kThreads, shmem, st>>>(p, scores);
+  }
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -1,0 +1,525 @@
+// Token-level window scores: softmax of a query window against every cached
+// key, aggregated over the GQA group and the window rows.
+//
+// ActKV §2: the score of a cached key is its attention weight
+// softmax(q.k / sqrt(D)).  ActKV §7.1: the weights are recovered as
+// exp(s - LSE) from the log-sum-exp of each query row, so a score pass only
+// needs the LSE and fresh q.k products.  Two passes therefore: the LSE of
+// every window row (unless the caller supplies it), then the recovered
+// probabilities summed per key.
+//
+// MFMA path (bf16/f16, D in {64, 128}, W >= 16, G*W <= 256): one workgroup
+// per (unit, chunk of keys), one wavefront per 64 query rows held in
+// registers as MFMA operands; 64-key tiles of K are staged through LDS
+// (double buffered, padded rows) and contracted with
+// v_mfma_f32_32x32x16.  The score pass keeps keys on the MFMA output's
+// column axis so the sum over query rows is a per-lane register sum plus
+// one cross-half shuffle; the LSE pass swaps the operands so each lane owns
+// one query row and keeps an online max/sum in registers.
+//
+// VALU path: any dtype/shape/aggregation, one lane per key.
+#include "common.h"
+
+#include <math.h>
+
+namespace kvsel {
+
+namespace {
+constexpr float kLog2e = 1.4426950408889634f;
+constexpr float kLn2 = 0.6931471805599453f;
+}  // namespace
+
+// =================================================================== VALU path
+
+template <int DT>
+__global__ __launch_bounds__(256) void lse_valu_kernel(WindowParams p, const void* __restrict__ q,
+                                                       const void* __restrict__ k,
+                                                       float* __restrict__ lse) {
+  __shared__ float qs[4][256];
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
+  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + w;   // (l, h, t)
+  const int64_t n_rows = static_cast<int64_t>(p.L) * p.Hq * p.W;
+  const bool valid = row < n_rows;
+  const int64_t rr = valid ? row : 0;
+  const int t = static_cast<int>(rr % p.W);
+  const int h = static_cast<int>((rr / p.W) % p.Hq);
+  const int l = static_cast<int>(rr / (static_cast<int64_t>(p.W) * p.Hq));
+  const int g = h / p.G;
+  for (int d = lane; d < p.D; d += 64) qs[w][d] = load_elem<DT>(q, rr * p.D + d);
+  __syncthreads();
+  if (!valid) return;
+  const int64_t n_allowed = p.causal ? (p.N - p.W + t + 1) : p.N;
+  const int64_t kbase = (static_cast<int64_t>(l) * p.Hkv + g) * p.N * p.D;
+  float m = -INFINITY, s = 0.f;
+  for (int64_t j = lane; j < n_allowed; j += 64) {
+    float acc = 0.f;
+    for (int d = 0; d < p.D; ++d) acc += qs[w][d] * load_elem<DT>(k, kbase + j * p.D + d);
+    const float x = acc * p.scale;
+    if (x > m) {
+      s = s * expf(m - x) + 1.f;
+      m = x;
+    } else {
+      s += expf(x - m);
+    }
+  }
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64);
+    const float s2 = __shfl_xor(s, o, 64);
+    const float mn = fmaxf(m, m2);
+    const float a = (m == -INFINITY) ? 0.f : s * expf(m - mn);
+    const float b = (m2 == -INFINITY) ? 0.f : s2 * expf(m2 - mn);
+    m = mn;
+    s = a + b;
+  }
+  if (lane == 0) lse[row] = m + logf(s);
+}
+
+template <int DT, int D>
+__global__ __launch_bounds__(256) void scores_valu_kernel(WindowParams p, const void* __restrict__ q,
+                                                          const void* __restrict__ k,
+                                                          const float* __restrict__ lse,
+                                                          float* __restrict__ out) {
+  extern __shared__ float sm[];          // [G*W][D] queries, then [G*W] lse
+  const int u = blockIdx.y;
+  const int l = u / p.Hkv, g = u % p.Hkv;
+  const int R = p.G * p.W;
+  float* qs = sm;
+  float* ls = sm + static_cast<int64_t>(R) * D;
+  for (int64_t e = threadIdx.x; e < static_cast<int64_t>(R) * D; e += blockDim.x) {
+    const int r = static_cast<int>(e / D), d = static_cast<int>(e % D);
+    const int h = g * p.G + r / p.W, t = r % p.W;
+    qs[e] = load_elem<DT>(q, ((static_cast<int64_t>(l) * p.Hq + h) * p.W + t) * D + d);
+  }
+  for (int r = threadIdx.x; r < R; r += blockDim.x) {
+    const int h = g * p.G + r / p.W, t = r % p.W;
+    ls[r] = lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t];
+  }
+  __syncthreads();
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= p.N) return;
+  float kr[D];
+  const int64_t kb = ((static_cast<int64_t>(l) * p.Hkv + g) * p.N + j) * D;
+  for (int d = 0; d < D; ++d) kr[d] = load_elem<DT>(k, kb + d);
+  float racc = 0.f;
+  for (int t = 0; t < p.W; ++t) {
+    const bool allowed = !p.causal || j <= p.N - p.W + t;
+    float hacc = 0.f;
+    for (int hl = 0; hl < p.G; ++hl) {
+      const int r = hl * p.W + t;
+      float pr = 0.f;
+      if (allowed) {
+        float acc = 0.f;
+        const float* qr = qs + static_cast<int64_t>(r) * D;
+        for (int d = 0; d < D; ++d) acc += qr[d] * kr[d];
+        pr = expf(acc * p.scale - ls[r]);
+      }
+      hacc = (p.head_agg == KVSEL_AGG_MAX) ? fmaxf(hacc, pr) : hacc + pr;
+    }
+    if (p.head_agg == KVSEL_AGG_MEAN) hacc /= static_cast<float>(p.G);
+    racc = (p.row_agg == KVSEL_AGG_MAX) ? fmaxf(racc, hacc) : racc + hacc;
+  }
+  if (p.row_agg == KVSEL_AGG_MEAN) racc /= static_cast<float>(p.W);
+  out[static_cast<int64_t>(u) * p.N + j] = racc;
+}
+
+hipError_t launch_window_lse_valu(const WindowParams& p, int dt, const void* q, const void* k,
+                                  float* lse, hipStream_t st) {
+  const int64_t rows = static_cast<int64_t>(p.L) * p.Hq * p.W;
+  const int grid = static_cast<int>(ceil_div(rows, 4));
+  if (grid == 0) return hipSuccess;
+  if (dt == KVSEL_F32) lse_valu_kernel<KVSEL_F32><<<grid, 256, 0, st>>>(p, q, k, lse);
+  else if (dt == KVSEL_BF16) lse_valu_kernel<KVSEL_BF16><<<grid, 256, 0, st>>>(p, q, k, lse);
+  else lse_valu_kernel<KVSEL_F16><<<grid, 256, 0, st>>>(p, q, k, lse);
+  return hipGetLastError();
+}
+
+template <int DT, int D>
+static hipError_t launch_scores_valu_t(const WindowParams& p, const void* q, const void* k,
+                                       const float* lse, float* out, hipStream_t st) {
+  const size_t sh = (static_cast<size_t>(p.G) * p.W * D + static_cast<size_t>(p.G) * p.W) * 4;
+  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scores_valu_kernel<DT, D>),
+                                     hipFuncAttributeMaxDynamicSharedMemorySize,
+                                     static_cast<int>(sh));
+  if (e != hipSuccess) return e;
+  dim3 grid(static_cast<unsigned>(ceil_div(p.N, 256)), static_cast<unsigned>(p.L * p.Hkv));
+  scores_valu_kernel<DT, D><<<grid, 256, sh, st>>>(p, q, k, lse, out);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_scores_valu(const WindowParams& p, int dt, const void* q, const void* k,
+                                     const float* lse, float* out, hipStream_t st) {
+  if (p.N == 0 || p.L * p.Hkv == 0) return hipSuccess;
+#define KVSEL_SV(DTV)                                                                   \
+  return (p.D == 64) ? launch_scores_valu_t<DTV, 64>(p, q, k, lse, out, st)             \
+                     : launch_scores_valu_t<DTV, 128>(p, q, k, lse, out, st)
+  if (dt == KVSEL_F32) { KVSEL_SV(KVSEL_F32); }
+  if (dt == KVSEL_BF16) { KVSEL_SV(KVSEL_BF16); }
+  KVSEL_SV(KVSEL_F16);
+#undef KVSEL_SV
+}
+
+// =================================================================== MFMA path
+
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 f16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x16 __attribute__((ext_vector_type(16)));
+
+constexpr int kTileKeys = 64;          // keys per LDS tile (two 32-wide MFMA column blocks)
+constexpr int kChunkKeys = 2048;       // keys per workgroup
+
+template <int DT>
+__device__ __forceinline__ f32x16 mfma32(const uint4& a, const uint4& b, const f32x16& c) {
+  if constexpr (DT == KVSEL_BF16) {
+    return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                   __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+  } else {
+    return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(f16x8, a),
+                                                  __builtin_bit_cast(f16x8, b), c, 0, 0, 0);
+  }
+}
+
+// Shared layout of both MFMA kernels.
+template <int D>
+struct MfmaTile {
+  static constexpr int kRowBytes = D * 2 + 16;                 // padded K row in LDS
+  static constexpr int kTileBytes = kTileKeys * kRowBytes;
+  static constexpr int kKSteps = D / 16;                       // MFMA k-steps per dot product
+  static constexpr int kChunksPerRow = D * 2 / 16;             // 16-byte pieces per K row
+  static constexpr int kLoadsPerThread = kTileKeys * kChunksPerRow / 256;
+};
+
+// Query operand fragments of this wavefront's 64 rows.  Lane l holds, for row
+// block rb and k-step ks, the 8 elements d = 16*ks + 8*(l/32) .. +7 of row
+// 64*w + 32*rb + l%32.  The same registers serve as the A operand (rows on
+// the output's row axis) and as the B operand (rows on the column axis).
+template <int DT, int D>
+__device__ __forceinline__ void load_q_frags(const WindowParams& p, const void* q, int l, int g,
+                                             int wave, int lane, uint4 (&qf)[2][D / 16]) {
+  const int R = p.G * p.W;
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = 64 * wave + 32 * rb + (lane & 31);
+    const bool ok = r < R;
+    const int h = g * p.G + (ok ? r / p.W : 0), t = ok ? r % p.W : 0;
+    const uint8_t* src = static_cast<const uint8_t*>(q) +
+                         (((static_cast<int64_t>(l) * p.Hq + h) * p.W + t) * D) * 2;
+    for (int ks = 0; ks < D / 16; ++ks) {
+      const int d = 16 * ks + 8 * (lane >> 5);
+      qf[rb][ks] = ok ? *reinterpret_cast<const uint4*>(src + d * 2) : make_uint4(0, 0, 0, 0);
+    }
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void load_k_tile_regs(const uint8_t* kunit, int64_t key0, int64_t N,
+                                                 uint4 (&reg)[MfmaTile<D>::kLoadsPerThread]) {
+  using T = MfmaTile<D>;
+  for (int i = 0; i < T::kLoadsPerThread; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int key = c / T::kChunksPerRow, piece = c % T::kChunksPerRow;
+    const int64_t j = key0 + key;
+    reg[i] = (j < N) ? *reinterpret_cast<const uint4*>(kunit + (j * D) * 2 + piece * 16)
+                     : make_uint4(0, 0, 0, 0);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void store_k_tile_lds(uint8_t* buf,
+                                                 const uint4 (&reg)[MfmaTile<D>::kLoadsPerThread]) {
+  using T = MfmaTile<D>;
+  for (int i = 0; i < T::kLoadsPerThread; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int key = c / T::kChunksPerRow, piece = c % T::kChunksPerRow;
+    *reinterpret_cast<uint4*>(buf + key * T::kRowBytes + piece * 16) = reg[i];
+  }
+}
+
+// K operand fragment: key 32*cb + l%32 of the tile, elements d = 16*ks + 8*(l/32) ..
+template <int D>
+__device__ __forceinline__ uint4 k_frag(const uint8_t* buf, int cb, int ks, int lane) {
+  using T = MfmaTile<D>;
+  const int key = 32 * cb + (lane & 31);
+  const int d = 16 * ks + 8 * (lane >> 5);
+  return *reinterpret_cast<const uint4*>(buf + key * T::kRowBytes + d * 2);
+}
+
+}  // namespace
+
+// ---- pass 1: per-(unit, chunk) partial (max, sum) of every row, log2 domain
+template <int DT, int D>
+__global__ __launch_bounds__(256) void lse_mfma_kernel(WindowParams p, const void* __restrict__ q,
+                                                       const void* __restrict__ k,
+                                                       float2* __restrict__ partials) {
+  using T = MfmaTile<D>;
+  __shared__ __align__(16) uint8_t kbuf[2][T::kTileBytes];
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  const int l = u / p.Hkv, g = u % p.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int R = p.G * p.W;
+  const int64_t key_begin = static_cast<int64_t>(chunk) * kChunkKeys;
+  const int64_t key_end = min(p.N, key_begin + kChunkKeys);
+  const uint8_t* kunit = static_cast<const uint8_t*>(k) +
+                         ((static_cast<int64_t>(l) * p.Hkv + g) * p.N * D) * 2;
+  uint4 qf[2][D / 16];
+  load_q_frags<DT, D>(p, q, l, g, wave, lane, qf);
+  const float c1 = p.scale * kLog2e;
+  // this lane's query rows (one per row block) and their causal limits
+  int64_t lim[2];
+  for (int rb = 0; rb < 2; ++rb) {
+    const int r = 64 * wave + 32 * rb + (lane & 31);
+    const int t = (r < R) ? r % p.W : 0;
+    lim[rb] = p.causal ? (p.N - p.W + t) : (p.N - 1);   // last allowed key
+    if (r >= R) lim[rb] = -1;
+  }
+  float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.f, 0.f};
+
+  uint4 kreg[T::kLoadsPerThread];
+  load_k_tile_regs<D>(kunit, key_begin, p.N, kreg);
+  store_k_tile_lds<D>(kbuf[0], kreg);
+  __syncthreads();
+  const int n_tiles = static_cast<int>(ceil_div(key_end - key_begin, kTileKeys));
+  for (int ti = 0; ti < n_tiles; ++ti) {
+    const int64_t key0 = key_begin + static_cast<int64_t>(ti) * kTileKeys;
+    if (ti + 1 < n_tiles) load_k_tile_regs<D>(kunit, key0 + kTileKeys, p.N, kreg);
+    const uint8_t* buf = kbuf[ti & 1];
+    f32x16 acc[2][2];                          // [cb][rb]: rows = keys, cols = query rows
+    for (int cb = 0; cb < 2; ++cb)
+      for (int rb = 0; rb < 2; ++rb) acc[cb][rb] = f32x16{};
+    for (int ks = 0; ks < T::kKSteps; ++ks) {
+      const uint4 kf0 = k_frag<D>(buf, 0, ks, lane);
+      const uint4 kf1 = k_frag<D>(buf, 1, ks, lane);
+      for (int rb = 0; rb < 2; ++rb) {
+        acc[0][rb] = mfma32<DT>(kf0, qf[rb][ks], acc[0][rb]);
+        acc[1][rb] = mfma32<DT>(kf1, qf[rb][ks], acc[1][rb]);
+      }
+    }
+    const bool full = (key0 + kTileKeys - 1 <= min(lim[0], lim[1])) && (key0 + kTileKeys <= key_end);
+    for (int rb = 0; rb < 2; ++rb) {
+      float tmax = -INFINITY;
+      for (int cb = 0; cb < 2; ++cb)
+        for (int v = 0; v < 16; ++v) {
+          const int64_t key = key0 + 32 * cb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const bool ok = full || (key <= lim[rb] && key < key_end);
+          tmax = ok ? fmaxf(tmax, acc[cb][rb][v]) : tmax;
+        }
+      if (tmax == -INFINITY) continue;
+      const float mt = tmax * c1;
+      const float mn = fmaxf(m[rb], mt);
+      float sum = 0.f;
+      for (int cb = 0; cb < 2; ++cb)
+        for (int v = 0; v < 16; ++v) {
+          const int64_t key = key0 + 32 * cb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+          const bool ok = full || (key <= lim[rb] && key < key_end);
+          const float e = exp2f(fmaf(acc[cb][rb][v], c1, -mn));
+          sum += ok ? e : 0.f;
+        }
+      s[rb] = ((m[rb] == -INFINITY) ? 0.f : s[rb] * exp2f(m[rb] - mn)) + sum;
+      m[rb] = mn;
+    }
+    if (ti + 1 < n_tiles) store_k_tile_lds<D>(kbuf[(ti + 1) & 1], kreg);
+    __syncthreads();
+  }
+  // combine the two lane halves (they hold the other half of each tile's keys)
+  for (int rb = 0; rb < 2; ++rb) {
+    const float m2 = __shfl_xor(m[rb], 32, 64);
+    const float s2 = __shfl_xor(s[rb], 32, 64);
+    const float mn = fmaxf(m[rb], m2);
+    const float a = (m[rb] == -INFINITY) ? 0.f : s[rb] * exp2f(m[rb] - mn);
+    const float b = (m2 == -INFINITY) ? 0.f : s2 * exp2f(m2 - mn);
+    const int r = 64 * wave + 32 * rb + (lane & 31);
+    if (lane < 32 && r < R) {
+      const int64_t o = (static_cast<int64_t>(u) * gridDim.x + chunk) * R + r;
+      partials[o] = make_float2(mn, a + b);
+    }
+  }
+}
+
+// ---- combine chunk partials into LSE [L][Hq][W] (natural log)
+__global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* __restrict__ partials,
+                                   float* __restrict__ lse) {
+  const int R = p.G * p.W;
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  const int64_t n = static_cast<int64_t>(p.L) * p.Hkv * R;
+  if (i >= n) return;
+  const int64_t u = i / R;
+  const int r = static_cast<int>(i % R);
+  float m = -INFINITY;
+  for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, partials[(u * n_chunks + c) * R + r].x);
+  float s = 0.f;
+  for (int c = 0; c < n_chunks; ++c) {
+    const float2 v = partials[(u * n_chunks + c) * R + r];
+    s += (v.x == -INFINITY) ? 0.f : v.y * exp2f(v.x - m);
+  }
+  const int l = static_cast<int>(u / p.Hkv), g = static_cast<int>(u % p.Hkv);
+  const int h = g * p.G + r / p.W, t = r % p.W;
+  lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t] = (m + log2f(s)) * kLn2;
+}
+
+// ---- pass 2: recovered probabilities summed over the unit's rows, per key
+template <int DT, int D>
+__global__ __launch_bounds__(256) void scores_mfma_kernel(WindowParams p, const void* __restrict__ q,
+                                                          const void* __restrict__ k,
+                                                          const float* __restrict__ lse,
+                                                          float* __restrict__ out) {
+  using T = MfmaTile<D>;
+  __shared__ __align__(16) uint8_t kbuf[2][T::kTileBytes];
+  __shared__ float red[2][4][kTileKeys];
+  const int u = blockIdx.y, chunk = blockIdx.x;
+  const int l = u / p.Hkv, g = u % p.Hkv;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  constexpr int n_waves = 4;
+  const int R = p.G * p.W;
+  const int64_t key_begin = static_cast<int64_t>(chunk) * kChunkKeys;
+  const int64_t key_end = min(p.N, key_begin + kChunkKeys);
+  const uint8_t* kunit = static_cast<const uint8_t*>(k) +
+                         ((static_cast<int64_t>(l) * p.Hkv + g) * p.N * D) * 2;
+  uint4 qf[2][D / 16];
+  load_q_frags<DT, D>(p, q, l, g, wave, lane, qf);
+  const float c1 = p.scale * kLog2e;
+  // log2-domain LSE of the 32 rows whose outputs this lane holds
+  float lse2[2][16];
+  for (int rb = 0; rb < 2; ++rb)
+    for (int v = 0; v < 16; ++v) {
+      const int r = 64 * wave + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+      const bool ok = r < R;
+      const int h = g * p.G + (ok ? r / p.W : 0), t = ok ? r % p.W : 0;
+      lse2[rb][v] = ok ? lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t] * kLog2e : INFINITY;
+    }
+  float factor = 1.f;
+  if (p.head_agg == KVSEL_AGG_MEAN) factor /= static_cast<float>(p.G);
+  if (p.row_agg == KVSEL_AGG_MEAN) factor /= static_cast<float>(p.W);
+  const int64_t first_masked = p.causal ? (p.N - p.W + 1) : p.N;   // keys >= this need a check
+
+  uint4 kreg[T::kLoadsPerThread];
+  load_k_tile_regs<D>(kunit, key_begin, p.N, kreg);
+  store_k_tile_lds<D>(kbuf[0], kreg);
+  __syncthreads();
+  const int n_tiles = static_cast<int>(ceil_div(key_end - key_begin, kTileKeys));
+  for (int ti = 0; ti < n_tiles; ++ti) {
+    const int64_t key0 = key_begin + static_cast<int64_t>(ti) * kTileKeys;
+    if (ti + 1 < n_tiles) load_k_tile_regs<D>(kunit, key0 + kTileKeys, p.N, kreg);
+    const uint8_t* buf = kbuf[ti & 1];
+    f32x16 acc[2][2];                          // [rb][cb]: rows = query rows, cols = keys
+    for (int rb = 0; rb < 2; ++rb)
+      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16{};
+    for (int ks = 0; ks < T::kKSteps; ++ks) {
+      const uint4 kf0 = k_frag<D>(buf, 0, ks, lane);
+      const uint4 kf1 = k_frag<D>(buf, 1, ks, lane);
+      for (int rb = 0; rb < 2; ++rb) {
+        acc[rb][0] = mfma32<DT>(qf[rb][ks], kf0, acc[rb][0]);
+        acc[rb][1] = mfma32<DT>(qf[rb][ks], kf1, acc[rb][1]);
+      }
+    }
+    const bool full = key0 + kTileKeys <= min(first_masked, key_end);
+    float cs[2];
+    for (int cb = 0; cb < 2; ++cb) {
+      const int64_t key = key0 + 32 * cb + (lane & 31);
+      float sum = 0.f;
+      for (int rb = 0; rb < 2; ++rb)
+        for (int v = 0; v < 16; ++v) {
+          const float e = exp2f(fmaf(acc[rb][cb][v], c1, -lse2[rb][v]));
+          bool ok = true;
+          if (!full) {
+            const int r = 64 * wave + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
+            ok = key < key_end && (!p.causal || key <= p.N - p.W + r % p.W);
+          }
+          sum += ok ? e : 0.f;
+        }
+      sum += __shfl_xor(sum, 32, 64);
+      cs[cb] = sum;
+    }
+    if (lane < 32) {
+      red[ti & 1][wave][lane] = cs[0];
+      red[ti & 1][wave][32 + lane] = cs[1];
+    }
+    if (ti + 1 < n_tiles) store_k_tile_lds<D>(kbuf[(ti + 1) & 1], kreg);
+    __syncthreads();
+    if (threadIdx.x < kTileKeys) {
+      const int64_t key = key0 + threadIdx.x;
+      if (key < key_end) {
+        float v = 0.f;
+        for (int w = 0; w < n_waves; ++w) v += red[ti & 1][w][threadIdx.x];
+        out[static_cast<int64_t>(u) * p.N + key] = v * factor;
+      }
+    }
+  }
+}
+
+bool window_mfma_supported(const WindowParams& p, int dt) {
+  const int R = p.G * p.W;
+  return (dt == KVSEL_BF16 || dt == KVSEL_F16) && (p.D == 64 || p.D == 128) && p.W >= 16 &&
+         R <= 256 && p.head_agg != KVSEL_AGG_MAX && p.row_agg != KVSEL_AGG_MAX;
+}
+
+size_t window_mfma_partials_bytes(const WindowParams& p) {
+  const int64_t n_chunks = ceil_div(p.N, kChunkKeys);
+  return static_cast<size_t>(p.L) * p.Hkv * n_chunks * p.G * p.W * sizeof(float2);
+}
+
+hipError_t launch_window_lse_mfma(const WindowParams& p, int dt, const void* q, const void* k,
+                                  float* partials, float* lse, hipStream_t st) {
+  const int n_chunks = static_cast<int>(ceil_div(p.N, kChunkKeys));
+  const int U = p.L * p.Hkv;
+  if (n_chunks == 0 || U == 0) return hipSuccess;
+  const int threads = 256;   // one wavefront per 64 rows; rows >= G*W are masked
+  dim3 grid(n_chunks, U);
+  float2* part = reinterpret_cast<float2*>(partials);
+#define KVSEL_LM(DTV, DV) lse_mfma_kernel<DTV, DV><<<grid, threads, 0, st>>>(p, q, k, part)
+  if (dt == KVSEL_BF16) {
+    if (p.D == 64) KVSEL_LM(KVSEL_BF16, 64); else KVSEL_LM(KVSEL_BF16, 128);
+  } else {
+    if (p.D == 64) KVSEL_LM(KVSEL_F16, 64); else KVSEL_LM(KVSEL_F16, 128);
+  }
+#undef KVSEL_LM
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = static_cast<int64_t>(U) * p.G * p.W;
+  lse_combine_kernel<<<static_cast<int>(ceil_div(n, 256)), 256, 0, st>>>(p, n_chunks, part, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_scores_mfma(const WindowParams& p, int dt, const void* q, const void* k,
+                                     const float* lse, float* out, hipStream_t st) {
+  const int n_chunks = static_cast<int>(ceil_div(p.N, kChunkKeys));
+  const int U = p.L * p.Hkv;
+  if (n_chunks == 0 || U == 0) return hipSuccess;
+  const int threads = 256;
+  dim3 grid(n_chunks, U);
+#define KVSEL_SM(DTV, DV) scores_mfma_kernel<DTV, DV><<<grid, threads, 0, st>>>(p, q, k, lse, out)
+  if (dt == KVSEL_BF16) {
+    if (p.D == 64) KVSEL_SM(KVSEL_BF16, 64); else KVSEL_SM(KVSEL_BF16, 128);
+  } else {
+    if (p.D == 64) KVSEL_SM(KVSEL_F16, 64); else KVSEL_SM(KVSEL_F16, 128);
+  }
+#undef KVSEL_SM
+  return hipGetLastError();
+}
+
+// =================================================================== pooling
+
+__global__ void pool1d_kernel(const float* __restrict__ in, float* __restrict__ out, int64_t rows,
+                              int64_t n, int kind, int ksize) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i >= rows * n) return;
+  const int64_t r = i / n, j = i % n;
+  const float* row = in + r * n;
+  const int h = ksize / 2;
+  float acc = (kind == KVSEL_POOL_MAX) ? -INFINITY : 0.f;
+  for (int o = -h; o <= h; ++o) {
+    const int64_t jj = j + o;
+    if (jj < 0 || jj >= n) continue;
+    acc = (kind == KVSEL_POOL_MAX) ? fmaxf(acc, row[jj]) : acc + row[jj];
+  }
+  out[i] = (kind == KVSEL_POOL_MAX) ? acc : acc / static_cast<float>(ksize);
+}
+
+hipError_t launch_pool1d(const float* in, float* out, int64_t rows, int64_t n, int kind, int ksize,
+                         hipStream_t st) {
+  const int64_t total = rows * n;
+  if (total == 0) return hipSuccess;
+  pool1d_kernel<<<static_cast<int>(ceil_div(total, 256)), 256, 0, st>>>(in, out, rows, n, kind, ksize);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -1,0 +1,255 @@
+"""Python binding of libkvsel: argument marshalling only.
+
+Each function checks the torch tensors it is handed (device, dtype,
+contiguity), fills the C args struct with their data pointers, sizes and
+allocates the workspace the library asks for (torch owns device memory), and
+calls the C entry point of the same name on the current torch stream.  All
+computation runs in the library's HIP kernels; a non-OK status raises
+``KvselError`` with the library's message.
+"""
+import ctypes
+
+import torch
+
+from . import _abi
+
+_DT = {torch.float32: _abi.F32, torch.bfloat16: _abi.BF16, torch.float16: _abi.F16}
+
+
+class KvselError(RuntimeError):
+    def __init__(self, status, msg):
+        super().__init__("%s: %s" % (_abi.STATUS_NAMES.get(status, status), msg))
+        self.status = status
+
+
+def _check(status):
+    if status != _abi.KVSEL_OK:
+        raise KvselError(status, _abi.load().kvsel_last_error().decode())
+
+
+def _ptr(t):
+    if t is None:
+        return None
+    if not t.is_cuda:
+        raise ValueError("tensors must live on the GPU")
+    if not t.is_contiguous():
+        raise ValueError("tensors must be contiguous")
+    return t.data_ptr()
+
+
+def _dtype(t):
+    if t.dtype not in _DT:
+        raise ValueError("unsupported dtype %s" % t.dtype)
+    return _DT[t.dtype]
+
+
+def _stream(stream):
+    s = stream if stream is not None else torch.cuda.current_stream()
+    return ctypes.c_void_p(s.cuda_stream)
+
+
+def _workspace(nbytes, device, workspace):
+    if nbytes == 0:
+        return None, 0
+    if workspace is not None and workspace.numel() >= nbytes:
+        return workspace, workspace.numel()
+    w = torch.empty(nbytes, dtype=torch.uint8, device=device)
+    return w, nbytes
+
+
+def version():
+    return int(_abi.load().kvsel_version())
+
+
+# ------------------------------------------------------------------ score
+
+def _score_call(a, device, workspace, stream):
+    lib = _abi.load()
+    nb = ctypes.c_size_t(0)
+    _check(lib.kvsel_score_workspace(ctypes.byref(a), ctypes.byref(nb)))
+    ws, wsz = _workspace(nb.value, device, workspace)
+    _check(lib.kvsel_score(ctypes.byref(a), _ptr(ws), wsz, _stream(stream)))
+    return ws
+
+
+def score_window(q, k, out, *, causal=True, lse_in=None, lse_out=None, head_agg="sum",
+                 row_agg="sum", pool="none", pool_k=1, scale=0.0, workspace=None, stream=None):
+    """kvsel_score, window mode.  q [L][Hq][W][D], k [L][Hkv][N][D] (one dtype),
+    out [L*Hkv][N] float32 (or None to compute only lse_out); lse_in/lse_out
+    [L][Hq][W] float32 (optional)."""
+    L, Hq, W, D = q.shape
+    _, Hkv, N, _ = k.shape
+    a = _abi.ScoreArgs()
+    a.struct_size = ctypes.sizeof(_abi.ScoreArgs)
+    a.mode = _abi.SCORE_WINDOW
+    a.q_dtype, a.k_dtype = _dtype(q), _dtype(k)
+    a.L, a.Hq, a.Hkv, a.D, a.W, a.S, a.N = L, Hq, Hkv, D, W, 1, N
+    a.q, a.k = _ptr(q), _ptr(k)
+    a.causal = 1 if causal else 0
+    a.lse_in, a.lse_out = _ptr(lse_in), _ptr(lse_out)
+    a.head_agg, a.row_agg = _abi.AGG[head_agg], _abi.AGG[row_agg]
+    a.pool, a.pool_k = _abi.POOL[pool], pool_k
+    a.scale = scale
+    a.scores = _ptr(out)      # None with lse_out given: compute the LSE only
+    return _score_call(a, q.device, workspace, stream)
+
+
+def score_memory(m, k_pool, page_table, n, out, *, page_size, slot_map=None, dead_slot=0, n_sink=0,
+                 n_recent=0, reduce="global", pool="none", pool_k=1, scale=0.0, workspace=None,
+                 stream=None):
+    """kvsel_score, memory mode.  m [L][Hq][D] float32; k_pool
+    [L][pool_pages][page_size][Hkv][D]; page_table int32; out [N] (global)
+    or [L*Hkv][N] (per_unit) float32."""
+    L, Hq, D = m.shape
+    _, P, ps, Hkv, _ = k_pool.shape
+    assert ps == page_size
+    a = _abi.ScoreArgs()
+    a.struct_size = ctypes.sizeof(_abi.ScoreArgs)
+    a.mode = _abi.SCORE_MEMORY
+    a.q_dtype, a.k_dtype = _dtype(m), _dtype(k_pool)
+    a.L, a.Hq, a.Hkv, a.D, a.W, a.S, a.N = L, Hq, Hkv, D, 1, 1, n
+    a.q, a.k = _ptr(m), _ptr(k_pool)
+    a.page_table, a.page_size, a.pool_pages = _ptr(page_table), page_size, P
+    a.slot_map, a.dead_slot = _ptr(slot_map), dead_slot
+    a.n_sink, a.n_recent = n_sink, n_recent
+    a.reduce = _abi.REDUCE[reduce]
+    a.pool, a.pool_k = _abi.POOL[pool], pool_k
+    a.scale = scale
+    a.scores = _ptr(out)
+    return _score_call(a, m.device, workspace, stream)
+
+
+def score_block(q, mu, out, *, n_kv_heads, n_begin=0, n_count=None, qbar=None, qbar_valid=False,
+                scale=0.0, workspace=None, stream=None):
+    """kvsel_score, block mode.  q [S][L][Hq][W][D] (or None with a valid qbar),
+    mu [L][Hkv][NB][D] float16, out [S][L*Hkv][n_count] float32,
+    qbar [S][L][Hkv][D] float32 (optional)."""
+    L, Hkv, NB, D = mu.shape
+    assert Hkv == n_kv_heads
+    if n_count is None:
+        n_count = NB - n_begin
+    a = _abi.ScoreArgs()
+    a.struct_size = ctypes.sizeof(_abi.ScoreArgs)
+    a.mode = _abi.SCORE_BLOCK
+    if q is not None:
+        S, _, Hq, W, _ = q.shape
+        a.q_dtype = _dtype(q)
+    else:
+        S, Hq, W = qbar.shape[0], n_kv_heads, 1
+        a.q_dtype = _abi.F32
+    a.k_dtype = _dtype(mu)
+    a.L, a.Hq, a.Hkv, a.D, a.W, a.S, a.N = L, Hq, Hkv, D, W, S, NB
+    a.q, a.k = _ptr(q), _ptr(mu)
+    a.n_begin, a.n_count = n_begin, n_count
+    a.qbar, a.qbar_valid = _ptr(qbar), 1 if qbar_valid else 0
+    a.scale = scale
+    a.scores = _ptr(out)
+    return _score_call(a, mu.device, workspace, stream)
+
+
+# ------------------------------------------------------------------ select
+
+def select(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0, keep_mask=None,
+           n_kept=None, slot_map=None, dead_slot=0, cand_score=None, cand_idx=None, cand_count=None,
+           finalize=True, pool="none", pool_k=1, stream=None):
+    """kvsel_select.  scores [U][n] float32 (rows may be a strided view of
+    contiguous memory: pass the 2-D tensor); kept_idx [U][k_total] int32.
+    pool/pool_k rank pooled scores (untiled calls)."""
+    U, n = scores.shape
+    if n_total is None:
+        n_total = base + n
+    if scores.stride(1) != 1:
+        raise ValueError("score rows must be contiguous")
+    a = _abi.SelectArgs()
+    a.struct_size = ctypes.sizeof(_abi.SelectArgs)
+    a.U, a.n, a.row_stride = U, n, scores.stride(0)
+    a.scores = scores.data_ptr() if scores.is_cuda else None
+    a.base, a.n_total = base, n_total
+    a.k_total, a.n_sink, a.n_recent = k_total, n_sink, n_recent
+    a.slot_map, a.dead_slot = _ptr(slot_map), dead_slot
+    a.cand_score, a.cand_idx, a.cand_count = _ptr(cand_score), _ptr(cand_idx), _ptr(cand_count)
+    a.finalize = 1 if finalize else 0
+    a.kept_idx, a.keep_mask, a.n_kept = _ptr(kept_idx), _ptr(keep_mask), _ptr(n_kept)
+    a.pool, a.pool_k = _abi.POOL[pool], pool_k
+    lib = _abi.load()
+    _check(lib.kvsel_select(ctypes.byref(a), None, 0, _stream(stream)))
+
+
+# ------------------------------------------------------------------ gather
+
+def _gather_args(src_k, src_v, idx, *, bt, D, src_rows, src_offsets, src_unit_stride, rope, theta,
+                 pos0, style, rotary_dim):
+    a = _abi.GatherArgs()
+    a.struct_size = ctypes.sizeof(_abi.GatherArgs)
+    a.U, a.k = idx.shape
+    a.D, a.dtype, a.bt = D, _dtype(src_k), bt
+    a.src_k, a.src_v = _ptr(src_k), _ptr(src_v)
+    a.src_offsets, a.src_unit_stride, a.src_rows = _ptr(src_offsets), src_unit_stride, src_rows
+    a.idx = _ptr(idx)
+    a.rope, a.style, a.rotary_dim = _abi.ROPE[rope], _abi.STYLE[style], rotary_dim
+    a.theta, a.pos0 = theta, pos0
+    return a
+
+
+def gather_rerope(src_k, src_v, idx, dst_k, dst_v, *, bt, D, src_rows, src_offsets=None,
+                  src_unit_stride=0, n_idx=None, rope="none", theta=1e6, pos0=0, style="half",
+                  rotary_dim=0, stream=None):
+    """kvsel_gather_rerope, FRESH mode.  idx [U][k] int32; dst [U][k*bt][D]."""
+    a = _gather_args(src_k, src_v, idx, bt=bt, D=D, src_rows=src_rows, src_offsets=src_offsets,
+                     src_unit_stride=src_unit_stride, rope=rope, theta=theta, pos0=pos0, style=style,
+                     rotary_dim=rotary_dim)
+    a.mode = _abi.GATHER_FRESH
+    a.n_idx = _ptr(n_idx)
+    a.dst_k, a.dst_v = _ptr(dst_k), _ptr(dst_v)
+    lib = _abi.load()
+    _check(lib.kvsel_gather_rerope(ctypes.byref(a), None, 0, _stream(stream)))
+
+
+def gather_incremental(src_k, src_v, idx, prev_idx, prev_page, pool_k, pool_v, page_table, n_miss, *,
+                       bt, D, src_rows, src_offsets=None, src_unit_stride=0, rope="raw", theta=1e6,
+                       pos0=0, style="half", rotary_dim=0, workspace=None, stream=None):
+    """kvsel_gather_rerope, INCREMENTAL mode.  pool_k/pool_v
+    [U][pool_pages][bt][D] updated in place; page_table [U][k], n_miss [U] out."""
+    a = _gather_args(src_k, src_v, idx, bt=bt, D=D, src_rows=src_rows, src_offsets=src_offsets,
+                     src_unit_stride=src_unit_stride, rope=rope, theta=theta, pos0=pos0, style=style,
+                     rotary_dim=rotary_dim)
+    a.mode = _abi.GATHER_INCREMENTAL
+    a.prev_idx, a.prev_page = _ptr(prev_idx), _ptr(prev_page)
+    a.pool_k, a.pool_v, a.pool_pages = _ptr(pool_k), _ptr(pool_v), pool_k.shape[1]
+    a.page_table, a.n_miss = _ptr(page_table), _ptr(n_miss)
+    lib = _abi.load()
+    nb = ctypes.c_size_t(0)
+    _check(lib.kvsel_gather_workspace(ctypes.byref(a), ctypes.byref(nb)))
+    ws, wsz = _workspace(nb.value, pool_k.device, workspace)
+    _check(lib.kvsel_gather_rerope(ctypes.byref(a), _ptr(ws), wsz, _stream(stream)))
+    return ws
+
+
+# ------------------------------------------------------------------ redirect / memory
+
+def redirect(slot_map, keep_mask, dead_slot, *, k_pool=None, v_pool=None, stream=None):
+    """kvsel_redirect.  slot_map [N] int32 (in place), keep_mask [N] uint8.
+    With k_pool/v_pool ([L][pool_slots][Hkv][D] views of the paged pools)
+    the dead slot's sentinel rows are written first."""
+    a = _abi.RedirectArgs()
+    a.struct_size = ctypes.sizeof(_abi.RedirectArgs)
+    a.N = slot_map.numel()
+    a.slot_map, a.keep_mask, a.dead_slot = _ptr(slot_map), _ptr(keep_mask), dead_slot
+    if k_pool is not None:
+        L, slots, Hkv, D = k_pool.shape
+        a.k_pool, a.v_pool = _ptr(k_pool), _ptr(v_pool)
+        a.L, a.Hkv, a.D, a.dtype, a.pool_slots = L, Hkv, D, _dtype(k_pool), slots
+    lib = _abi.load()
+    _check(lib.kvsel_redirect(ctypes.byref(a), _stream(stream)))
+
+
+def memory_update(q_turn, m, *, decay=0.9, stream=None):
+    """kvsel_memory_update.  q_turn [L][Hq][W][D]; m [L][Hq][D] float32 in place."""
+    L, Hq, W, D = q_turn.shape
+    a = _abi.MemUpdArgs()
+    a.struct_size = ctypes.sizeof(_abi.MemUpdArgs)
+    a.L, a.Hq, a.D, a.W = L, Hq, D, W
+    a.q_dtype = _dtype(q_turn)
+    a.q_turn, a.M, a.decay = _ptr(q_turn), _ptr(m), decay
+    lib = _abi.load()
+    _check(lib.kvsel_memory_update(ctypes.byref(a), _stream(stream)))

@@ -1,0 +1,145 @@
+"""Host-side checks of the C ABI (no GPU): the library loads, exports every
+function include/kvsel.h declares, the ctypes structs match the C layout,
+and argument validation reports errors before any device work."""
+import ctypes
+import os
+import re
+import shutil
+import subprocess
+
+import pytest
+
+from selection_score_amd import _abi
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "kvsel.h")
+
+
+def _declared_functions():
+    text = open(HEADER).read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?[\w\s\*]*?\b(kvsel_\w+)\s*\(", text, re.M)))
+
+
+def test_library_exports_every_declared_function():
+    lib = _abi.load()
+    names = _declared_functions()
+    assert len(names) >= 10, names
+    for n in names:
+        assert hasattr(lib, n), n
+    assert set(names) == set(_abi.EXPORTS)
+    assert lib.kvsel_version() == 1
+
+
+STRUCTS = {
+    "kvsel_score_args": _abi.ScoreArgs,
+    "kvsel_select_args": _abi.SelectArgs,
+    "kvsel_gather_args": _abi.GatherArgs,
+    "kvsel_redirect_args": _abi.RedirectArgs,
+    "kvsel_memupd_args": _abi.MemUpdArgs,
+}
+
+
+@pytest.mark.skipif(shutil.which("gcc") is None, reason="gcc not available")
+def test_ctypes_layout_matches_header(tmp_path):
+    lines = ['#include <stdio.h>', '#include <stddef.h>', '#include "kvsel.h"', "int main(void) {"]
+    for cname, cls in STRUCTS.items():
+        lines.append('printf("%s %%zu\\n", sizeof(%s));' % (cname, cname))
+        for f, _ in cls._fields_:
+            lines.append('printf("%s.%s %%zu\\n", offsetof(%s, %s));' % (cname, f, cname, f))
+    lines.append("return 0; }")
+    src = tmp_path / "layout.c"
+    src.write_text("\n".join(lines))
+    exe = tmp_path / "layout"
+    subprocess.check_call(["gcc", "-I" + os.path.join(ROOT, "include"), str(src), "-o", str(exe)])
+    out = dict(line.split() for line in subprocess.check_output([str(exe)], text=True).splitlines())
+    for cname, cls in STRUCTS.items():
+        assert int(out[cname]) == ctypes.sizeof(cls), cname
+        for f, _ in cls._fields_:
+            assert int(out["%s.%s" % (cname, f)]) == getattr(cls, f).offset, (cname, f)
+
+
+def _select_args(**kw):
+    a = _abi.SelectArgs()
+    a.struct_size = ctypes.sizeof(a)
+    a.U, a.n, a.row_stride, a.n_total, a.k_total = 1, 100, 100, 100, 10
+    a.scores, a.kept_idx = 0x1000, 0x2000
+    a.finalize = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def _status(fn, a, *extra):
+    return fn(ctypes.byref(a), *extra)
+
+
+def test_select_validation_errors_without_device():
+    lib = _abi.load()
+    nb = ctypes.c_size_t(0)
+    assert lib.kvsel_select_workspace(None, ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert _status(lib.kvsel_select_workspace, _select_args(n_sink=6, n_recent=5), ctypes.byref(nb)) \
+        == _abi.KVSEL_E_BUDGET
+    assert b"exceeds" in lib.kvsel_last_error()
+    assert _status(lib.kvsel_select_workspace, _select_args(), ctypes.byref(nb)) == _abi.KVSEL_OK
+    # a partial range without candidate buffers, or an oversize range
+    assert _status(lib.kvsel_select_workspace, _select_args(n=50), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert _status(lib.kvsel_select_workspace, _select_args(base=60), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert _status(lib.kvsel_select_workspace, _select_args(struct_size=8), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    # k >= N with an oversized forced set is not a budget error
+    assert _status(lib.kvsel_select_workspace, _select_args(k_total=100, n_sink=80, n_recent=80),
+                   ctypes.byref(nb)) == _abi.KVSEL_OK
+
+
+def _score_args(**kw):
+    a = _abi.ScoreArgs()
+    a.struct_size = ctypes.sizeof(a)
+    a.mode, a.q_dtype, a.k_dtype = _abi.SCORE_WINDOW, _abi.BF16, _abi.BF16
+    a.L, a.Hq, a.Hkv, a.D, a.W, a.S, a.N = 36, 32, 8, 128, 64, 1, 32768
+    a.q, a.k, a.scores = 0x1000, 0x2000, 0x3000
+    a.causal = 1
+    for k, v in kw.items():
+        setattr(a, k, v)
+    return a
+
+
+def test_score_validation_and_workspace_without_device():
+    lib = _abi.load()
+    nb = ctypes.c_size_t(0)
+    assert _status(lib.kvsel_score_workspace, _score_args(), ctypes.byref(nb)) == _abi.KVSEL_OK
+    # own LSE (36*32*64 floats) + per-chunk partials (36*8*16 chunks*256 rows*8 bytes)
+    assert nb.value >= 36 * 32 * 64 * 4 + 36 * 8 * 16 * 256 * 8
+    assert _status(lib.kvsel_score_workspace, _score_args(D=96), ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
+    assert _status(lib.kvsel_score_workspace, _score_args(Hq=30), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert _status(lib.kvsel_score_workspace, _score_args(q=0x1004), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert _status(lib.kvsel_score_workspace, _score_args(pool=_abi.POOL["max"], pool_k=4),
+                   ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    # max aggregation on a window too large for the VALU path
+    assert _status(lib.kvsel_score_workspace, _score_args(head_agg=_abi.AGG["max"], W=128),
+                   ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
+    blk = _score_args(mode=_abi.SCORE_BLOCK, k_dtype=_abi.F16, N=1000, n_begin=900, n_count=200)
+    assert _status(lib.kvsel_score_workspace, blk, ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    # a score call with a too-small workspace fails before touching the device
+    assert lib.kvsel_score(ctypes.byref(_score_args()), None, 0, None) == _abi.KVSEL_E_WORKSPACE
+
+
+def test_gather_and_redirect_validation_without_device():
+    lib = _abi.load()
+    a = _abi.GatherArgs()
+    a.struct_size = ctypes.sizeof(a)
+    a.mode, a.U, a.D, a.dtype, a.bt, a.k = _abi.GATHER_FRESH, 4, 128, _abi.BF16, 32, 16
+    a.src_k, a.src_v, a.idx, a.dst_k, a.dst_v, a.src_rows = 0x1000, 0x2000, 0x3000, 0x4000, 0x5000, 10
+    a.rope, a.theta = 7, 1e6
+    nb = ctypes.c_size_t(0)
+    assert lib.kvsel_gather_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    a.rope, a.D = _abi.ROPE["raw"], 100
+    assert lib.kvsel_gather_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
+    a.D, a.theta = 128, 0.0
+    assert lib.kvsel_gather_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    a.theta = 1e6
+    assert lib.kvsel_gather_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_OK
+    r = _abi.RedirectArgs()
+    r.struct_size = ctypes.sizeof(r)
+    r.N, r.slot_map, r.keep_mask, r.dead_slot = 10, 0x1000, 0x2000, 5
+    r.k_pool, r.v_pool, r.L, r.Hkv, r.D, r.dtype, r.pool_slots = 0x3000, 0x4000, 1, 1, 128, _abi.F32, 6
+    assert lib.kvsel_redirect(ctypes.byref(r), None) == _abi.KVSEL_E_UNSUPPORTED
+    assert b"fp8" in lib.kvsel_last_error()

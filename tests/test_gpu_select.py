@@ -1,0 +1,129 @@
+"""GPU parity of kvsel_select against the oracle's select_topk (bit-exact on
+identical float32 scores)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import select as osel
+from parity import require_gpu
+
+import selection_score_amd as kv
+
+pytestmark = pytest.mark.gpu
+
+
+def _scores(rng, U, n, ties=False):
+    s = rng.standard_normal((U, n)).astype(np.float32)
+    if ties:
+        # coarse values: many exact ties, some -0.0 / +0.0
+        s = np.round(s * 4) / 4
+        z = rng.random((U, n)) < 0.05
+        s[z] = np.where(rng.random(int(z.sum())) < 0.5, -0.0, 0.0)
+    return s
+
+
+def _run(dev, s, k, n_sink, n_recent, slot_map=None, dead=0):
+    U, n = s.shape
+    st = torch.from_numpy(s).to(dev)
+    kept = torch.full((U, k), -7, dtype=torch.int32, device=dev)
+    mask = torch.zeros((U, n), dtype=torch.uint8, device=dev)
+    nk = torch.zeros(U, dtype=torch.int32, device=dev)
+    sm = None if slot_map is None else torch.from_numpy(slot_map.astype(np.int32)).to(dev)
+    kv.select(st, kept, k_total=k, n_sink=n_sink, n_recent=n_recent, keep_mask=mask, n_kept=nk,
+              slot_map=sm, dead_slot=dead)
+    torch.cuda.synchronize()
+    return kept.cpu().numpy(), mask.cpu().numpy(), nk.cpu().numpy()
+
+
+def _check(s, kept, mask, nk, k, n_sink, n_recent, alive=None):
+    for u in range(s.shape[0]):
+        ok, om = osel.select_topk(s[u], k, n_sink, n_recent, alive)
+        assert nk[u] == len(ok), (u, nk[u], len(ok))
+        np.testing.assert_array_equal(kept[u, : len(ok)], ok)
+        assert np.all(kept[u, len(ok):] == -1)
+        np.testing.assert_array_equal(mask[u].astype(bool), om)
+
+
+@pytest.mark.parametrize("U,n,k,n_sink,n_recent,ties", [
+    (3, 1000, 100, 4, 64, False),        # ragged, several tiles of 64
+    (5, 2048, 512, 4, 64, True),         # ties and signed zeros
+    (4, 32768, 8192, 4, 256, False),     # LDS-resident keys at the full per-unit size
+    (2, 40000, 5000, 3, 7, True),        # keys streamed from global memory
+    (1, 7, 3, 1, 1, True),
+])
+def test_select_matches_oracle(U, n, k, n_sink, n_recent, ties):
+    dev = require_gpu()
+    rng = np.random.default_rng(100 + n)
+    s = _scores(rng, U, n, ties)
+    kept, mask, nk = _run(dev, s, k, n_sink, n_recent)
+    _check(s, kept, mask, nk, k, n_sink, n_recent)
+
+
+def test_select_global_unit_with_dead_slots():
+    # the session-memory shape: one unit of 65536 with redirected positions
+    dev = require_gpu()
+    rng = np.random.default_rng(7)
+    n, k, dead = 65536, 8192, 65536
+    s = _scores(rng, 1, n)
+    slot_map = rng.permutation(n).astype(np.int64)
+    dead_pos = rng.choice(n, 3000, replace=False)
+    slot_map[dead_pos] = dead
+    dead_pos = np.concatenate([dead_pos, [0, n - 1]])  # dead positions inside the forced set too
+    slot_map[[0, n - 1]] = dead
+    alive = slot_map != dead
+    kept, mask, nk = _run(dev, s, k, 4, 64, slot_map, dead)
+    _check(s, kept, mask, nk, k, 4, 64, alive)
+
+
+@pytest.mark.parametrize("k,n_sink,n_recent", [(2048, 5, 5), (10, 4, 6), (3000, 0, 0)])
+def test_select_edge_budgets(k, n_sink, n_recent):
+    dev = require_gpu()
+    rng = np.random.default_rng(k)
+    s = _scores(rng, 2, 2048, ties=True)
+    kept, mask, nk = _run(dev, s, k, n_sink, n_recent)
+    _check(s, kept, mask, nk, k, n_sink, n_recent)
+
+
+def test_select_all_dead_and_empty():
+    dev = require_gpu()
+    n = 300
+    s = np.zeros((1, n), np.float32)
+    slot_map = np.full(n, 9, np.int64)
+    kept, mask, nk = _run(dev, s, 50, 2, 2, slot_map, 9)
+    assert nk[0] == 0 and np.all(kept == -1) and not mask.any()
+    # U = 0 is a no-op
+    kv.select(torch.zeros((0, 10), device=dev), torch.zeros((0, 4), dtype=torch.int32, device=dev),
+              k_total=4, n_sink=0, n_recent=0)
+
+
+def test_select_budget_error():
+    dev = require_gpu()
+    s = torch.zeros((1, 100), device=dev)
+    kept = torch.zeros((1, 8), dtype=torch.int32, device=dev)
+    with pytest.raises(kv.KvselError) as e:
+        kv.select(s, kept, k_total=8, n_sink=5, n_recent=5)
+    assert e.value.status == 2
+
+
+@pytest.mark.parametrize("n,tile,k", [(100000, 30000, 4096), (70001, 65536, 4096), (5000, 977, 300)])
+def test_select_tiled_equals_untiled(n, tile, k):
+    dev = require_gpu()
+    rng = np.random.default_rng(n)
+    U = 3
+    s = _scores(rng, U, n, ties=True)
+    st = torch.from_numpy(s).to(dev)
+    cs = torch.zeros((U, k), dtype=torch.float32, device=dev)
+    ci = torch.zeros((U, k), dtype=torch.int32, device=dev)
+    cc = torch.zeros(U, dtype=torch.int32, device=dev)
+    kept = torch.full((U, k), -7, dtype=torch.int32, device=dev)
+    nk = torch.zeros(U, dtype=torch.int32, device=dev)
+    for b in range(0, n, tile):
+        e = min(n, b + tile)
+        kv.select(st[:, b:e], kept, k_total=k, n_sink=1, n_recent=4, n_total=n, base=b,
+                  cand_score=cs, cand_idx=ci, cand_count=cc, finalize=(e == n), n_kept=nk)
+    torch.cuda.synchronize()
+    kept, nk = kept.cpu().numpy(), nk.cpu().numpy()
+    for u in range(U):
+        ok, _ = osel.select_topk(s[u], k, 1, 4)
+        assert nk[u] == len(ok)
+        np.testing.assert_array_equal(kept[u, : len(ok)], ok)
