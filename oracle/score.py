@@ -173,11 +173,13 @@ def memory_scores(m, k_pool, page_table, page_size, n, *, slot_map=None,
     phys_page = pt[j // page_size]
     in_page = j % page_size
     out = np.zeros(n) if reduce == "global" else np.zeros((L, Hkv, n))
+    # logical position j lives in physical slot page_table[j // ps] * ps + j % ps
+    slot = phys_page * page_size + in_page
     for l in range(L):
-        kl = np.asarray(k_pool[l], dtype=np.float64)[phys_page, in_page]   # [N][Hkv][D]
+        flat = np.asarray(k_pool[l], dtype=np.float64).reshape(-1, Hkv, D)   # [slots][Hkv][D]
         for h in range(Hq):
             g = gqa_group(h, Hq, Hkv)
-            s = (kl[:, g, :] @ m[l, h]) * scale
+            s = ((flat[:, g, :] @ m[l, h]) * scale)[slot]      # logits in logical order
             lse = _logsumexp(s, H)
             p = np.where(H, np.exp(s - lse), 0.0)
             if reduce == "global":

@@ -279,7 +279,7 @@ static kvsel_status validate_select(const kvsel_select_args* a) {
   if (!tiled && !a->finalize) return fail(KVSEL_E_ARG, "an untiled call must finalize");
   if (a->keep_mask != nullptr && (tiled || a->base != 0 || a->n != a->n_total))
     return fail(KVSEL_E_ARG, "keep_mask needs an untiled call");
-  if (a->finalize && a->kept_idx == nullptr) return fail(KVSEL_E_ARG, "kept_idx is NULL");
+  if (a->U > 0 && a->finalize && a->kept_idx == nullptr) return fail(KVSEL_E_ARG, "kept_idx is NULL");
   if (a->pool < KVSEL_POOL_NONE || a->pool > KVSEL_POOL_MAX) return fail(KVSEL_E_ARG, "bad pool");
   if (a->pool != KVSEL_POOL_NONE && (a->pool_k < 1 || a->pool_k % 2 == 0 || a->pool_k > 255))
     return fail(KVSEL_E_ARG, "pool_k must be odd, in [1, 255]");

@@ -247,40 +247,41 @@ __device__ __forceinline__ uint4 k_frag(const uint8_t* buf, int cb, int ks, int 
 }  // namespace
 
 // ---- pass 1: per-(unit, chunk) partial (max, sum) of every row, log2 domain
+// Tiles whose keys every row may see take a branch-free path; only the
+// causal tail and the ragged end check keys one by one.
 template <int DT, int D>
-__global__ __launch_bounds__(256) void lse_mfma_kernel(WindowParams p, const void* __restrict__ q,
-                                                       const void* __restrict__ k,
-                                                       float2* __restrict__ partials) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void lse_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __restrict__ k,
+                     float2* __restrict__ partials) {
   using T = MfmaTile<D>;
   __shared__ __align__(16) uint8_t kbuf[2][T::kTileBytes];
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int l = u / p.Hkv, g = u % p.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int R = p.G * p.W;
-  const int64_t key_begin = static_cast<int64_t>(chunk) * kChunkKeys;
-  const int64_t key_end = min(p.N, key_begin + kChunkKeys);
+  const int N = static_cast<int>(p.N);
+  const int key_begin = chunk * kChunkKeys;
+  const int key_end = min(N, key_begin + kChunkKeys);
   const uint8_t* kunit = static_cast<const uint8_t*>(k) +
                          ((static_cast<int64_t>(l) * p.Hkv + g) * p.N * D) * 2;
   uint4 qf[2][D / 16];
   load_q_frags<DT, D>(p, q, l, g, wave, lane, qf);
   const float c1 = p.scale * kLog2e;
-  // this lane's query rows (one per row block) and their causal limits
-  int64_t lim[2];
+  int lim[2];                       // last key each of this lane's two rows may see
   for (int rb = 0; rb < 2; ++rb) {
     const int r = 64 * wave + 32 * rb + (lane & 31);
-    const int t = (r < R) ? r % p.W : 0;
-    lim[rb] = p.causal ? (p.N - p.W + t) : (p.N - 1);   // last allowed key
-    if (r >= R) lim[rb] = -1;
+    lim[rb] = (r >= R) ? -1 : (p.causal ? N - p.W + r % p.W : N - 1);
   }
+  const int first_masked = p.causal ? N - p.W + 1 : N;
   float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.f, 0.f};
 
   uint4 kreg[T::kLoadsPerThread];
   load_k_tile_regs<D>(kunit, key_begin, p.N, kreg);
   store_k_tile_lds<D>(kbuf[0], kreg);
   __syncthreads();
-  const int n_tiles = static_cast<int>(ceil_div(key_end - key_begin, kTileKeys));
+  const int n_tiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
   for (int ti = 0; ti < n_tiles; ++ti) {
-    const int64_t key0 = key_begin + static_cast<int64_t>(ti) * kTileKeys;
+    const int key0 = key_begin + ti * kTileKeys;
     if (ti + 1 < n_tiles) load_k_tile_regs<D>(kunit, key0 + kTileKeys, p.N, kreg);
     const uint8_t* buf = kbuf[ti & 1];
     f32x16 acc[2][2];                          // [cb][rb]: rows = keys, cols = query rows
@@ -294,27 +295,36 @@ __global__ __launch_bounds__(256) void lse_mfma_kernel(WindowParams p, const voi
         acc[1][rb] = mfma32<DT>(kf1, qf[rb][ks], acc[1][rb]);
       }
     }
-    const bool full = (key0 + kTileKeys - 1 <= min(lim[0], lim[1])) && (key0 + kTileKeys <= key_end);
+    const bool full = key0 + kTileKeys <= min(first_masked, key_end);     // uniform
+    const int kl = key0 + 4 * (lane >> 5);
     for (int rb = 0; rb < 2; ++rb) {
+      if (lim[rb] < 0) continue;
       float tmax = -INFINITY;
-      for (int cb = 0; cb < 2; ++cb)
-        for (int v = 0; v < 16; ++v) {
-          const int64_t key = key0 + 32 * cb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const bool ok = full || (key <= lim[rb] && key < key_end);
-          tmax = ok ? fmaxf(tmax, acc[cb][rb][v]) : tmax;
-        }
-      if (tmax == -INFINITY) continue;
-      const float mt = tmax * c1;
-      const float mn = fmaxf(m[rb], mt);
+      if (full) {
+        for (int cb = 0; cb < 2; ++cb)
+          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, acc[cb][rb][v]);
+      } else {
+        for (int cb = 0; cb < 2; ++cb)
+          for (int v = 0; v < 16; ++v) {
+            const int key = kl + 32 * cb + 8 * (v >> 2) + (v & 3);
+            if (key <= lim[rb] && key < key_end) tmax = fmaxf(tmax, acc[cb][rb][v]);
+          }
+        if (tmax == -INFINITY) continue;
+      }
+      const float mn = fmaxf(m[rb], tmax * c1);
       float sum = 0.f;
-      for (int cb = 0; cb < 2; ++cb)
-        for (int v = 0; v < 16; ++v) {
-          const int64_t key = key0 + 32 * cb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-          const bool ok = full || (key <= lim[rb] && key < key_end);
-          const float e = exp2f(fmaf(acc[cb][rb][v], c1, -mn));
-          sum += ok ? e : 0.f;
-        }
-      s[rb] = ((m[rb] == -INFINITY) ? 0.f : s[rb] * exp2f(m[rb] - mn)) + sum;
+      if (full) {
+        for (int cb = 0; cb < 2; ++cb)
+          for (int v = 0; v < 16; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[cb][rb][v], c1, -mn));
+      } else {
+        for (int cb = 0; cb < 2; ++cb)
+          for (int v = 0; v < 16; ++v) {
+            const int key = kl + 32 * cb + 8 * (v >> 2) + (v & 3);
+            const float e = __builtin_amdgcn_exp2f(fmaf(acc[cb][rb][v], c1, -mn));
+            sum += (key <= lim[rb] && key < key_end) ? e : 0.f;
+          }
+      }
+      s[rb] = s[rb] * __builtin_amdgcn_exp2f(m[rb] - mn) + sum;
       m[rb] = mn;
     }
     if (ti + 1 < n_tiles) store_k_tile_lds<D>(kbuf[(ti + 1) & 1], kreg);
@@ -325,8 +335,8 @@ __global__ __launch_bounds__(256) void lse_mfma_kernel(WindowParams p, const voi
     const float m2 = __shfl_xor(m[rb], 32, 64);
     const float s2 = __shfl_xor(s[rb], 32, 64);
     const float mn = fmaxf(m[rb], m2);
-    const float a = (m[rb] == -INFINITY) ? 0.f : s[rb] * exp2f(m[rb] - mn);
-    const float b = (m2 == -INFINITY) ? 0.f : s2 * exp2f(m2 - mn);
+    const float a = (m[rb] == -INFINITY) ? 0.f : s[rb] * __builtin_amdgcn_exp2f(m[rb] - mn);
+    const float b = (m2 == -INFINITY) ? 0.f : s2 * __builtin_amdgcn_exp2f(m2 - mn);
     const int r = 64 * wave + 32 * rb + (lane & 31);
     if (lane < 32 && r < R) {
       const int64_t o = (static_cast<int64_t>(u) * gridDim.x + chunk) * R + r;
@@ -358,26 +368,25 @@ __global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* _
 
 // ---- pass 2: recovered probabilities summed over the unit's rows, per key
 template <int DT, int D>
-__global__ __launch_bounds__(256) void scores_mfma_kernel(WindowParams p, const void* __restrict__ q,
-                                                          const void* __restrict__ k,
-                                                          const float* __restrict__ lse,
-                                                          float* __restrict__ out) {
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void scores_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __restrict__ k,
+                        const float* __restrict__ lse, float* __restrict__ out) {
   using T = MfmaTile<D>;
   __shared__ __align__(16) uint8_t kbuf[2][T::kTileBytes];
   __shared__ float red[2][4][kTileKeys];
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int l = u / p.Hkv, g = u % p.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
-  constexpr int n_waves = 4;
   const int R = p.G * p.W;
-  const int64_t key_begin = static_cast<int64_t>(chunk) * kChunkKeys;
-  const int64_t key_end = min(p.N, key_begin + kChunkKeys);
+  const int N = static_cast<int>(p.N);
+  const int key_begin = chunk * kChunkKeys;
+  const int key_end = min(N, key_begin + kChunkKeys);
   const uint8_t* kunit = static_cast<const uint8_t*>(k) +
                          ((static_cast<int64_t>(l) * p.Hkv + g) * p.N * D) * 2;
   uint4 qf[2][D / 16];
   load_q_frags<DT, D>(p, q, l, g, wave, lane, qf);
   const float c1 = p.scale * kLog2e;
-  // log2-domain LSE of the 32 rows whose outputs this lane holds
+  // log2-domain LSE of the 32 rows whose outputs this lane holds (+inf: no row)
   float lse2[2][16];
   for (int rb = 0; rb < 2; ++rb)
     for (int v = 0; v < 16; ++v) {
@@ -389,15 +398,15 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(WindowParams p, const 
   float factor = 1.f;
   if (p.head_agg == KVSEL_AGG_MEAN) factor /= static_cast<float>(p.G);
   if (p.row_agg == KVSEL_AGG_MEAN) factor /= static_cast<float>(p.W);
-  const int64_t first_masked = p.causal ? (p.N - p.W + 1) : p.N;   // keys >= this need a check
+  const int first_masked = p.causal ? N - p.W + 1 : N;   // keys >= this need a per-row check
 
   uint4 kreg[T::kLoadsPerThread];
   load_k_tile_regs<D>(kunit, key_begin, p.N, kreg);
   store_k_tile_lds<D>(kbuf[0], kreg);
   __syncthreads();
-  const int n_tiles = static_cast<int>(ceil_div(key_end - key_begin, kTileKeys));
+  const int n_tiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
   for (int ti = 0; ti < n_tiles; ++ti) {
-    const int64_t key0 = key_begin + static_cast<int64_t>(ti) * kTileKeys;
+    const int key0 = key_begin + ti * kTileKeys;
     if (ti + 1 < n_tiles) load_k_tile_regs<D>(kunit, key0 + kTileKeys, p.N, kreg);
     const uint8_t* buf = kbuf[ti & 1];
     f32x16 acc[2][2];                          // [rb][cb]: rows = query rows, cols = keys
@@ -411,21 +420,24 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(WindowParams p, const 
         acc[rb][1] = mfma32<DT>(qf[rb][ks], kf1, acc[rb][1]);
       }
     }
-    const bool full = key0 + kTileKeys <= min(first_masked, key_end);
+    const bool full = key0 + kTileKeys <= min(first_masked, key_end);     // uniform
     float cs[2];
     for (int cb = 0; cb < 2; ++cb) {
-      const int64_t key = key0 + 32 * cb + (lane & 31);
+      const int key = key0 + 32 * cb + (lane & 31);
       float sum = 0.f;
-      for (int rb = 0; rb < 2; ++rb)
-        for (int v = 0; v < 16; ++v) {
-          const float e = exp2f(fmaf(acc[rb][cb][v], c1, -lse2[rb][v]));
-          bool ok = true;
-          if (!full) {
+      if (full) {
+        for (int rb = 0; rb < 2; ++rb)
+          for (int v = 0; v < 16; ++v)
+            sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][v], c1, -lse2[rb][v]));
+      } else {
+        for (int rb = 0; rb < 2; ++rb)
+          for (int v = 0; v < 16; ++v) {
             const int r = 64 * wave + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            ok = key < key_end && (!p.causal || key <= p.N - p.W + r % p.W);
+            const bool ok = key < key_end && (!p.causal || key <= N - p.W + r % p.W);
+            const float e = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][v], c1, -lse2[rb][v]));
+            sum += ok ? e : 0.f;
           }
-          sum += ok ? e : 0.f;
-        }
+      }
       sum += __shfl_xor(sum, 32, 64);
       cs[cb] = sum;
     }
@@ -435,11 +447,12 @@ __global__ __launch_bounds__(256) void scores_mfma_kernel(WindowParams p, const 
     }
     if (ti + 1 < n_tiles) store_k_tile_lds<D>(kbuf[(ti + 1) & 1], kreg);
     __syncthreads();
-    if (threadIdx.x < kTileKeys) {
-      const int64_t key = key0 + threadIdx.x;
+    // the column sums of tile ti are final: one wave per 16 keys finishes them
+    const int kk = (threadIdx.x & 15) + 16 * wave;
+    if ((threadIdx.x & 63) < 16) {
+      const int key = key0 + kk;
       if (key < key_end) {
-        float v = 0.f;
-        for (int w = 0; w < n_waves; ++w) v += red[ti & 1][w][threadIdx.x];
+        const float v = red[ti & 1][0][kk] + red[ti & 1][1][kk] + red[ti & 1][2][kk] + red[ti & 1][3][kk];
         out[static_cast<int64_t>(u) * p.N + key] = v * factor;
       }
     }

@@ -1,0 +1,206 @@
+"""GPU parity of the block-level (Mean-K) path: kvsel_score in block mode,
+per-unit and tiled kvsel_select over blocks, the raw-K gather with re-RoPE,
+and the incremental view update -- at small sizes and at the full 1M- and
+10M-token workload sizes (sampled units checked against the oracle)."""
+import numpy as np
+import pytest
+import torch
+
+from oracle import materialise as om
+from oracle import numerics
+from oracle import score as osc
+from oracle import select as osel
+from oracle.rope import rope_rotate
+from parity import assert_rope_close, assert_scores_close, check_selection, f64, require_gpu
+
+import selection_score_amd as kv
+from selection_score_amd import workloads as wl
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("S,W,NB,n_begin,n_count", [(2, 16, 3000, 0, 3000), (1, 7, 5000, 1000, 777),
+                                                    (4, 32, 1200, 1100, 100)])
+def test_block_scores_match_oracle(S, W, NB, n_begin, n_count):
+    dev = require_gpu()
+    g = torch.Generator(device=dev).manual_seed(NB)
+    L, Hq, Hkv, D = 2, 8, 2, 128
+    q = torch.randn((S, L, Hq, W, D), generator=g, device=dev).to(torch.bfloat16)
+    mu = (torch.randn((L, Hkv, NB, D), generator=g, device=dev) * 0.3).to(torch.float16)
+    out = torch.empty((S, L * Hkv, n_count), dtype=torch.float32, device=dev)
+    qbar = torch.empty((S, L, Hkv, D), dtype=torch.float32, device=dev)
+    kv.score_block(q, mu, out, n_kv_heads=Hkv, n_begin=n_begin, n_count=n_count, qbar=qbar)
+    torch.cuda.synchronize()
+    qb = osc.query_reduce(f64(q), Hkv)
+    np.testing.assert_allclose(f64(qbar), qb, rtol=1e-5, atol=1e-4)
+    want = osc.block_scores(qb, f64(mu))[..., n_begin:n_begin + n_count].reshape(S, L * Hkv, n_count)
+    mag = osc.block_scores(np.abs(qb), np.abs(f64(mu)))[..., n_begin:n_begin + n_count]
+    assert_scores_close(f64(out).reshape(-1, n_count), want.reshape(-1, n_count), mag=mag)
+    # a second tile from the cached q-bar
+    out2 = torch.empty((S, L * Hkv, 50), dtype=torch.float32, device=dev)
+    kv.score_block(None, mu, out2, n_kv_heads=Hkv, n_begin=NB - 50, n_count=50, qbar=qbar, qbar_valid=True)
+    torch.cuda.synchronize()
+    want2 = osc.block_scores(qb, f64(mu))[..., NB - 50:].reshape(S * L * Hkv, 50)
+    mag2 = osc.block_scores(np.abs(qb), np.abs(f64(mu)))[..., NB - 50:]
+    assert_scores_close(f64(out2).reshape(-1, 50), want2, mag=mag2)
+
+
+def _oracle_unit_scores(q, mu, s, u, Hkv):
+    """Oracle block scores of one (session, unit) and their sum of |terms|."""
+    l, g = divmod(u, Hkv)
+    G = q.shape[2] // Hkv
+    qb = osc.query_reduce(f64(q[s:s + 1, l:l + 1, g * G:(g + 1) * G]), 1)     # [1][1][1][D]
+    m = f64(mu[l, g])[None, None]
+    return osc.block_scores(qb, m)[0, 0, 0], osc.block_scores(np.abs(qb), np.abs(m))[0, 0, 0]
+
+
+def test_kvmem_1m_workload_full_size():
+    """64 layers x 8 KV heads x 32768 blocks: block scores, top-2048 with block 0
+    and the last 4 forced, raw-K gather re-RoPEd to contiguous positions."""
+    dev = require_gpu()
+    cfg = wl.CONFIGS["kvmem1m"]
+    mu, w, _ = wl.kvmem_index(cfg, dev)
+    q = wl.kvmem_queries(cfg, dev, w, 0)[None]
+    raw_k, raw_v, offs = wl.kvmem_raw_store(cfg, dev)
+    U, NB, k, D, bt = cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt
+    scores = torch.empty((1, U, NB), dtype=torch.float32, device=dev)
+    kv.score_block(q, mu, scores, n_kv_heads=cfg.Hkv)
+    kept = torch.empty((U, k), dtype=torch.int32, device=dev)
+    kv.select(scores[0], kept, k_total=k, n_sink=cfg.n_sink, n_recent=cfg.n_recent)
+    vk = torch.empty((U, k * bt, D), dtype=torch.bfloat16, device=dev)
+    vv = torch.empty_like(vk)
+    kv.gather_rerope(raw_k, raw_v, kept, vk, vv, bt=bt, D=D, src_rows=NB * bt, src_offsets=offs,
+                     rope="raw", theta=cfg.theta)
+    torch.cuda.synchronize()
+    kept_h = kept.cpu().numpy()
+    for u in [0, 300, U - 1]:
+        want, mag = _oracle_unit_scores(q, mu, 0, u, cfg.Hkv)
+        assert_scores_close(f64(scores[0, u])[None], want[None], "unit %d" % u, mag=mag[None])
+        s32 = numerics.round_to_f32(want)
+        verdict = check_selection(kept_h[u], s32, k, cfg.n_sink, cfg.n_recent, what="unit %d" % u)
+        if verdict == "exact":
+            l, g = divmod(u, cfg.Hkv)
+            buf = l % cfg.raw_layers
+            ok, _ = osel.select_topk(s32, k, cfg.n_sink, cfg.n_recent)
+            # only the kept blocks, in kept order: raw-mode positions depend on
+            # the entry's rank in the view, not on its block id
+            sel = torch.from_numpy(ok).to(dev)
+            rk = f64(raw_k[buf, g][sel]).reshape(k * bt, D)
+            rv = f64(raw_v[buf, g][sel]).reshape(k * bt, D)
+            gk, gv = om.gather_view(rk, rv, np.arange(k), bt, rope="raw", theta=cfg.theta)
+            assert_rope_close(f64(vk[u]), gk, "unit %d" % u)
+            np.testing.assert_array_equal(f64(vv[u]), gv)
+    assert np.all(kept_h[:, 0] == 0) and np.all(kept_h[:, -4:] == np.arange(NB - 4, NB))
+    assert np.all(np.diff(kept_h, axis=1) > 0)
+
+
+@pytest.mark.timeout(600)
+def test_kvmem_10m_workload_full_size():
+    """312500 blocks per unit scored in 65536-block tiles for 4 sessions,
+    tiled top-4096, and the in-place incremental update of each session's
+    4096-page view (previous view shares about half its blocks)."""
+    dev = require_gpu()
+    cfg = wl.CONFIGS["kvmem10m"]
+    S, U, NB, k, D, bt, tile = cfg.S, cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt, cfg.tile
+    room = k - cfg.n_sink - cfg.n_recent
+    mu, w, planted = wl.kvmem_index(cfg, dev, n_dirs=S, planted=(room, 10.0))
+    qs = torch.stack([wl.kvmem_queries(cfg, dev, w, s) for s in range(S)])
+    qbar = torch.empty((S, cfg.L, cfg.Hkv, D), dtype=torch.float32, device=dev)
+    SU = S * U
+    cs = torch.empty((SU, k), dtype=torch.float32, device=dev)
+    ci = torch.empty((SU, k), dtype=torch.int32, device=dev)
+    cc = torch.zeros(SU, dtype=torch.int32, device=dev)
+    kept = torch.empty((SU, k), dtype=torch.int32, device=dev)
+    nk = torch.empty(SU, dtype=torch.int32, device=dev)
+    tile_out = torch.empty((S, U, tile), dtype=torch.float32, device=dev)
+    sample = [(0, 0), (1, 257), (3, U - 1)]
+    sampled_scores = {su: [] for su in sample}
+    for b in range(0, NB, tile):
+        n = min(tile, NB - b)
+        out = tile_out[:, :, :n]
+        kv.score_block(qs if b == 0 else None, mu, tile_out.view(-1)[: S * U * n].view(S, U, n),
+                       n_kv_heads=cfg.Hkv, n_begin=b, n_count=n, qbar=qbar, qbar_valid=b > 0)
+        out = tile_out.view(-1)[: S * U * n].view(SU, n)
+        kv.select(out, kept, k_total=k, n_sink=cfg.n_sink, n_recent=cfg.n_recent, n_total=NB, base=b,
+                  cand_score=cs, cand_idx=ci, cand_count=cc, finalize=b + n == NB, n_kept=nk)
+        for (s, u) in sample:
+            sampled_scores[(s, u)].append(f64(out[s * U + u]))
+    torch.cuda.synchronize()
+    kept_h = kept.cpu().numpy()
+    assert np.all(nk.cpu().numpy() == k)
+    verdicts = {}
+    for (s, u) in sample:
+        got = np.concatenate(sampled_scores[(s, u)])
+        want, mag = _oracle_unit_scores(qs, mu, s, u, cfg.Hkv)
+        assert_scores_close(got[None], want[None], "session %d unit %d" % (s, u), mag=mag[None])
+        s32 = numerics.round_to_f32(want)
+        verdicts[(s, u)] = (check_selection(kept_h[s * U + u], s32, k, cfg.n_sink, cfg.n_recent,
+                                            what="session %d unit %d" % (s, u)), s32)
+    del tile_out, cs, ci
+
+    # ---- incremental view update
+    raw_k = torch.empty((cfg.Hkv, NB, bt, D), dtype=torch.bfloat16, device=dev)
+    raw_v = torch.empty_like(raw_k)
+    gen = torch.Generator(device=dev).manual_seed(77)
+    for h in range(cfg.Hkv):
+        raw_k[h].normal_(generator=gen)
+        raw_v[h].normal_(generator=gen)
+    offs = torch.tensor([((i % U) % cfg.Hkv) * NB * bt * D for i in range(SU)], dtype=torch.int64,
+                        device=dev)
+    rng = np.random.default_rng(5)
+    prev_idx = np.empty((SU, k), np.int32)
+    prev_page = np.empty((SU, k), np.int32)
+    planted_h = planted.cpu().numpy()                        # [S][L][Hkv][room]
+    for i in range(SU):
+        s, u = divmod(i, U)
+        l, g = divmod(u, cfg.Hkv)
+        inside = rng.choice(planted_h[s, l, g], k // 2, replace=False)
+        taken = np.zeros(NB, bool)
+        taken[planted_h[s, l, g]] = True
+        draw = np.unique(rng.integers(0, NB, 3 * k))
+        draw = draw[~taken[draw]]
+        outside = rng.choice(draw, k - k // 2, replace=False)
+        prev_idx[i] = np.sort(np.concatenate([inside, outside]))
+        prev_page[i] = rng.permutation(k)
+    pool_k = torch.full((SU, k, bt, D), 0.5, dtype=torch.bfloat16, device=dev)
+    pool_v = torch.full((SU, k, bt, D), -0.25, dtype=torch.bfloat16, device=dev)
+    o = np.arange(bt)
+    baked = {}
+    for (s, u) in sample:                                    # sampled views hold real baked K
+        verdict, s32 = verdicts[(s, u)]
+        if verdict != "exact":
+            continue
+        i = s * U + u
+        g = u % cfg.Hkv
+        new_idx, _ = osel.select_topk(s32, k, cfg.n_sink, cfg.n_recent)
+        # only the blocks the update touches, renumbered by rank (order kept)
+        need = np.union1d(prev_idx[i], new_idx)
+        sel = torch.from_numpy(need).to(dev)
+        rk, rv = f64(raw_k[g][sel]), f64(raw_v[g][sel])
+        prev_r = np.searchsorted(need, prev_idx[i])
+        new_r = np.searchsorted(need, new_idx)
+        pk = np.empty((k, bt, D))
+        pv = np.empty((k, bt, D))
+        for j, b in enumerate(prev_r):
+            pk[prev_page[i, j]] = numerics.round_to_bf16(rope_rotate(rk[b], j * bt + o, cfg.theta))
+            pv[prev_page[i, j]] = rv[b]
+        pool_k[i] = torch.from_numpy(pk.astype(np.float32)).to(torch.bfloat16).to(dev)
+        pool_v[i] = torch.from_numpy(pv.astype(np.float32)).to(torch.bfloat16).to(dev)
+        baked[(s, u)] = (pk, pv, rk, rv, prev_r, new_r)
+    pt = torch.empty((SU, k), dtype=torch.int32, device=dev)
+    nm = torch.empty(SU, dtype=torch.int32, device=dev)
+    kv.gather_incremental(raw_k, raw_v, kept, torch.from_numpy(prev_idx).to(dev),
+                          torch.from_numpy(prev_page).to(dev), pool_k, pool_v, pt, nm, bt=bt, D=D,
+                          src_rows=NB * bt, src_offsets=offs, rope="raw", theta=cfg.theta)
+    torch.cuda.synchronize()
+    pt_h, nm_h = pt.cpu().numpy(), nm.cpu().numpy()
+    assert 0.4 * k < nm_h.mean() < 0.6 * k                 # about half the view is new
+    assert np.all(np.sort(pt_h, axis=1) == np.arange(k))   # each page used once per view
+    for (s, u), (pk, pv, rk, rv, prev_r, new_r) in baked.items():
+        i = s * U + u
+        ok, ov, opt, onm = om.incremental_view(prev_r, prev_page[i], new_r, pk, pv, rk, rv, bt,
+                                               theta=cfg.theta)
+        assert nm_h[i] == onm
+        np.testing.assert_array_equal(pt_h[i], opt)
+        np.testing.assert_array_equal(f64(pool_v[i]), ov)
+        assert_rope_close(f64(pool_k[i]), ok, "session %d unit %d" % (s, u))
