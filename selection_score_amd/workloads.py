@@ -5,7 +5,7 @@ to the CPU oracle) and by ``bench.py``.  Nothing here computes any step of
 the selection method: these functions only draw random tensors with the
 stated structure and round them to the storage dtype.
 
-Workloads (sizes as the pages' settings suggest; see the design doc for the recipe):
+Workloads (shapes of the settings the three pages describe):
   tiny        1 layer, 2 KV / 8 query heads, D 64, fp32, N 2048, window 16,
               16 planted keys scaled x8, avg-pool 7, budget 512 (4 sink, 64 recent)
   snapkv      36 layers, 8 KV / 32 query heads, D 128, bf16, N 32768, window 64,
