@@ -21,6 +21,7 @@
 #include "common.h"
 
 #include <math.h>
+#include <climits>
 
 namespace kvsel {
 
@@ -248,7 +249,93 @@ __device__ __forceinline__ uint4 k_frag(const uint8_t* buf, int cb, int ks, int 
 
 // ---- pass 1: per-(unit, chunk) partial (max, sum) of every row, log2 domain
 // Tiles whose keys every row may see take a branch-free path; only the
-// causal tail and the ragged end check keys one by one.
+// causal tail and the ragged end check keys one by one.  K streams through
+// the same three register staging sets as the score pass.
+typedef unsigned int u32x4 __attribute__((ext_vector_type(4)));
+
+template <int D>
+struct DeepStage {
+  static constexpr int kN = MfmaTile<D>::kLoadsPerThread;        // 16-byte pieces per thread
+  u32x4 r[kN];
+};
+
+template <int D>
+__device__ __forceinline__ void deep_load(const uint8_t* kunit, int key0, int N, DeepStage<D>& st) {
+  using T = MfmaTile<D>;
+#pragma unroll
+  for (int i = 0; i < DeepStage<D>::kN; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    const int j = min(key0 + c / T::kChunksPerRow, N - 1);
+    st.r[i] = *reinterpret_cast<const u32x4*>(kunit + static_cast<int64_t>(j) * (D * 2) + (c % T::kChunksPerRow) * 16);
+  }
+}
+
+template <int D>
+__device__ __forceinline__ void deep_store(uint8_t* buf, const DeepStage<D>& st) {
+  using T = MfmaTile<D>;
+#pragma unroll
+  for (int i = 0; i < DeepStage<D>::kN; ++i) {
+    const int c = threadIdx.x + 256 * i;
+    *reinterpret_cast<u32x4*>(buf + (c / T::kChunksPerRow) * T::kRowBytes + (c % T::kChunksPerRow) * 16) = st.r[i];
+  }
+}
+
+#define KVSEL_LSE_TILE(TI, SET)                                                                  \
+  do {                                                                                           \
+    const int ti_ = (TI);                                                                        \
+    if (ti_ < n_tiles) {                                                                         \
+      const int key0 = key_begin + ti_ * kTileKeys;                                              \
+      const uint8_t* buf = kbuf[ti_ & 1];                                                        \
+      f32x16 acc[2][2];                                                                          \
+      for (int cb = 0; cb < 2; ++cb)                                                             \
+        for (int rb = 0; rb < 2; ++rb) acc[cb][rb] = f32x16{};                                   \
+      for (int ks = 0; ks < T::kKSteps; ++ks) {                                                  \
+        const uint4 kf0 = k_frag<D>(buf, 0, ks, lane);                                           \
+        const uint4 kf1 = k_frag<D>(buf, 1, ks, lane);                                           \
+        for (int rb = 0; rb < 2; ++rb) {                                                         \
+          acc[0][rb] = mfma32<DT>(kf0, qf[rb][ks], acc[0][rb]);                                  \
+          acc[1][rb] = mfma32<DT>(kf1, qf[rb][ks], acc[1][rb]);                                  \
+        }                                                                                        \
+      }                                                                                          \
+      const bool full = key0 + kTileKeys <= min(first_masked, key_end);                          \
+      const int kl = key0 + 4 * (lane >> 5);                                                     \
+      for (int rb = 0; rb < 2; ++rb) {                                                           \
+        if (lim[rb] < 0) continue;                                                               \
+        float tmax = -INFINITY;                                                                  \
+        if (full) {                                                                              \
+          for (int cb = 0; cb < 2; ++cb)                                                         \
+            for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, acc[cb][rb][v]);                     \
+        } else {                                                                                 \
+          for (int cb = 0; cb < 2; ++cb)                                                         \
+            for (int v = 0; v < 16; ++v) {                                                       \
+              const int key = kl + 32 * cb + 8 * (v >> 2) + (v & 3);                             \
+              if (key <= lim[rb] && key < key_end) tmax = fmaxf(tmax, acc[cb][rb][v]);           \
+            }                                                                                    \
+          if (tmax == -INFINITY) continue;                                                       \
+        }                                                                                        \
+        const float mn = fmaxf(m[rb], tmax * c1);                                                \
+        float sum = 0.f;                                                                         \
+        if (full) {                                                                              \
+          for (int cb = 0; cb < 2; ++cb)                                                         \
+            for (int v = 0; v < 16; ++v)                                                         \
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[cb][rb][v], c1, -mn));                      \
+        } else {                                                                                 \
+          for (int cb = 0; cb < 2; ++cb)                                                         \
+            for (int v = 0; v < 16; ++v) {                                                       \
+              const int key = kl + 32 * cb + 8 * (v >> 2) + (v & 3);                             \
+              const float e = __builtin_amdgcn_exp2f(fmaf(acc[cb][rb][v], c1, -mn));             \
+              sum += (key <= lim[rb] && key < key_end) ? e : 0.f;                                \
+            }                                                                                    \
+        }                                                                                        \
+        s[rb] = s[rb] * __builtin_amdgcn_exp2f(m[rb] - mn) + sum;                                \
+        m[rb] = mn;                                                                              \
+      }                                                                                          \
+    }                                                                                            \
+    deep_store<D>(kbuf[(ti_ + 1) & 1], SET);                                                     \
+    deep_load<D>(kunit, key_begin + min(ti_ + 4, n_tiles - 1) * kTileKeys, N, SET);              \
+    __syncthreads();                                                                             \
+  } while (0)
+
 template <int DT, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void lse_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __restrict__ k,
@@ -264,6 +351,7 @@ void lse_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __r
   const int key_end = min(N, key_begin + kChunkKeys);
   const uint8_t* kunit = static_cast<const uint8_t*>(k) +
                          ((static_cast<int64_t>(l) * p.Hkv + g) * p.N * D) * 2;
+  const int n_tiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
   uint4 qf[2][D / 16];
   load_q_frags<DT, D>(p, q, l, g, wave, lane, qf);
   const float c1 = p.scale * kLog2e;
@@ -274,69 +362,26 @@ void lse_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __r
   }
   const int first_masked = p.causal ? N - p.W + 1 : N;
   float m[2] = {-INFINITY, -INFINITY}, s[2] = {0.f, 0.f};
-
-  uint4 kreg[T::kLoadsPerThread];
-  load_k_tile_regs<D>(kunit, key_begin, p.N, kreg);
-  store_k_tile_lds<D>(kbuf[0], kreg);
+  // the K prefetches are issued after the query loads; tile t waits in set t % 3
+  DeepStage<D> s0, s1, s2;
+  deep_load<D>(kunit, key_begin, N, s0);
+  deep_load<D>(kunit, key_begin + min(1, n_tiles - 1) * kTileKeys, N, s1);
+  deep_load<D>(kunit, key_begin + min(2, n_tiles - 1) * kTileKeys, N, s2);
+  deep_store<D>(kbuf[0], s0);
+  deep_load<D>(kunit, key_begin + min(3, n_tiles - 1) * kTileKeys, N, s0);
   __syncthreads();
-  const int n_tiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
-  for (int ti = 0; ti < n_tiles; ++ti) {
-    const int key0 = key_begin + ti * kTileKeys;
-    if (ti + 1 < n_tiles) load_k_tile_regs<D>(kunit, key0 + kTileKeys, p.N, kreg);
-    const uint8_t* buf = kbuf[ti & 1];
-    f32x16 acc[2][2];                          // [cb][rb]: rows = keys, cols = query rows
-    for (int cb = 0; cb < 2; ++cb)
-      for (int rb = 0; rb < 2; ++rb) acc[cb][rb] = f32x16{};
-    for (int ks = 0; ks < T::kKSteps; ++ks) {
-      const uint4 kf0 = k_frag<D>(buf, 0, ks, lane);
-      const uint4 kf1 = k_frag<D>(buf, 1, ks, lane);
-      for (int rb = 0; rb < 2; ++rb) {
-        acc[0][rb] = mfma32<DT>(kf0, qf[rb][ks], acc[0][rb]);
-        acc[1][rb] = mfma32<DT>(kf1, qf[rb][ks], acc[1][rb]);
-      }
-    }
-    const bool full = key0 + kTileKeys <= min(first_masked, key_end);     // uniform
-    const int kl = key0 + 4 * (lane >> 5);
-    for (int rb = 0; rb < 2; ++rb) {
-      if (lim[rb] < 0) continue;
-      float tmax = -INFINITY;
-      if (full) {
-        for (int cb = 0; cb < 2; ++cb)
-          for (int v = 0; v < 16; ++v) tmax = fmaxf(tmax, acc[cb][rb][v]);
-      } else {
-        for (int cb = 0; cb < 2; ++cb)
-          for (int v = 0; v < 16; ++v) {
-            const int key = kl + 32 * cb + 8 * (v >> 2) + (v & 3);
-            if (key <= lim[rb] && key < key_end) tmax = fmaxf(tmax, acc[cb][rb][v]);
-          }
-        if (tmax == -INFINITY) continue;
-      }
-      const float mn = fmaxf(m[rb], tmax * c1);
-      float sum = 0.f;
-      if (full) {
-        for (int cb = 0; cb < 2; ++cb)
-          for (int v = 0; v < 16; ++v) sum += __builtin_amdgcn_exp2f(fmaf(acc[cb][rb][v], c1, -mn));
-      } else {
-        for (int cb = 0; cb < 2; ++cb)
-          for (int v = 0; v < 16; ++v) {
-            const int key = kl + 32 * cb + 8 * (v >> 2) + (v & 3);
-            const float e = __builtin_amdgcn_exp2f(fmaf(acc[cb][rb][v], c1, -mn));
-            sum += (key <= lim[rb] && key < key_end) ? e : 0.f;
-          }
-      }
-      s[rb] = s[rb] * __builtin_amdgcn_exp2f(m[rb] - mn) + sum;
-      m[rb] = mn;
-    }
-    if (ti + 1 < n_tiles) store_k_tile_lds<D>(kbuf[(ti + 1) & 1], kreg);
-    __syncthreads();
+  for (int ti = 0; ti < n_tiles; ti += 3) {
+    KVSEL_LSE_TILE(ti, s1);
+    KVSEL_LSE_TILE(ti + 1, s2);
+    KVSEL_LSE_TILE(ti + 2, s0);
   }
   // combine the two lane halves (they hold the other half of each tile's keys)
   for (int rb = 0; rb < 2; ++rb) {
     const float m2 = __shfl_xor(m[rb], 32, 64);
-    const float s2 = __shfl_xor(s[rb], 32, 64);
+    const float s2v = __shfl_xor(s[rb], 32, 64);
     const float mn = fmaxf(m[rb], m2);
     const float a = (m[rb] == -INFINITY) ? 0.f : s[rb] * __builtin_amdgcn_exp2f(m[rb] - mn);
-    const float b = (m2 == -INFINITY) ? 0.f : s2 * __builtin_amdgcn_exp2f(m2 - mn);
+    const float b = (m2 == -INFINITY) ? 0.f : s2v * __builtin_amdgcn_exp2f(m2 - mn);
     const int r = 64 * wave + 32 * rb + (lane & 31);
     if (lane < 32 && r < R) {
       const int64_t o = (static_cast<int64_t>(u) * gridDim.x + chunk) * R + r;
@@ -344,6 +389,7 @@ void lse_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __r
     }
   }
 }
+#undef KVSEL_LSE_TILE
 
 // ---- combine chunk partials into LSE [L][Hq][W] (natural log)
 __global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* __restrict__ partials,
@@ -367,6 +413,78 @@ __global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* _
 }
 
 // ---- pass 2: recovered probabilities summed over the unit's rows, per key
+// Three register staging sets keep three 64-key tiles in flight from HBM per
+// workgroup on top of the two LDS tile buffers.  Column sums collect in LDS
+// and leave in one coalesced store after the last K load, so no global store
+// sits between the prefetches; every load is issued unconditionally (past
+// the end it re-reads the last tile) so the wait counts stay exact.
+#define KVSEL_SC_TILE(TI, SET)                                                                   \
+  do {                                                                                           \
+    const int ti_ = (TI);                                                                        \
+    if (ti_ < n_tiles) {                                                                         \
+      const int key0 = key_begin + ti_ * kTileKeys;                                              \
+      const uint8_t* buf = kbuf[ti_ & 1];                                                        \
+      f32x16 acc[2][2];                                                                          \
+      for (int rb = 0; rb < 2; ++rb)                                                             \
+        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16{};                                   \
+      for (int ks = 0; ks < T::kKSteps; ++ks) {                                                  \
+        const uint4 kf0 = k_frag<D>(buf, 0, ks, lane);                                           \
+        const uint4 kf1 = k_frag<D>(buf, 1, ks, lane);                                           \
+        for (int rb = 0; rb < 2; ++rb) {                                                         \
+          acc[rb][0] = mfma32<DT>(qf[rb][ks], kf0, acc[rb][0]);                                  \
+          acc[rb][1] = mfma32<DT>(qf[rb][ks], kf1, acc[rb][1]);                                  \
+        }                                                                                        \
+      }                                                                                          \
+      const bool full = key0 + kTileKeys <= min(first_masked, key_end);                          \
+      float cs[2];                                                                               \
+      for (int cb = 0; cb < 2; ++cb) {                                                           \
+        const int key = key0 + 32 * cb + (lane & 31);                                            \
+        const int kk = key < key_end ? key : INT_MAX;                                            \
+        float sum = 0.f;                                                                         \
+        if (full) {                                                                              \
+          for (int rb = 0; rb < 2; ++rb)                                                         \
+            for (int g4 = 0; g4 < 4; ++g4) {                                                     \
+              const int r0 = 64 * wave + 32 * rb + 8 * g4 + 4 * (lane >> 5);                     \
+              const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[r0]);                    \
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 0], c1, -l4.x));           \
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 1], c1, -l4.y));           \
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 2], c1, -l4.z));           \
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 3], c1, -l4.w));           \
+            }                                                                                    \
+        } else {                                                                                 \
+          for (int rb = 0; rb < 2; ++rb)                                                         \
+            for (int g4 = 0; g4 < 4; ++g4) {                                                     \
+              const int r0 = 64 * wave + 32 * rb + 8 * g4 + 4 * (lane >> 5);                     \
+              const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[r0]);                    \
+              const int4 m4 = *reinterpret_cast<const int4*>(&lim_s[r0]);                        \
+              const float e0 = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 0], c1, -l4.x)); \
+              const float e1 = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 1], c1, -l4.y)); \
+              const float e2 = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 2], c1, -l4.z)); \
+              const float e3 = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 3], c1, -l4.w)); \
+              sum += kk <= m4.x ? e0 : 0.f;                                                      \
+              sum += kk <= m4.y ? e1 : 0.f;                                                      \
+              sum += kk <= m4.z ? e2 : 0.f;                                                      \
+              sum += kk <= m4.w ? e3 : 0.f;                                                      \
+            }                                                                                    \
+        }                                                                                        \
+        sum += __shfl_xor(sum, 32, 64);                                                          \
+        cs[cb] = sum;                                                                            \
+      }                                                                                          \
+      if (lane < 32) {                                                                           \
+        red[ti_ & 1][wave][lane] = cs[0];                                                        \
+        red[ti_ & 1][wave][32 + lane] = cs[1];                                                   \
+      }                                                                                          \
+    }                                                                                            \
+    deep_store<D>(kbuf[(ti_ + 1) & 1], SET);                                                     \
+    deep_load<D>(kunit, key_begin + min(ti_ + 4, n_tiles - 1) * kTileKeys, N, SET);              \
+    __syncthreads();                                                                             \
+    if (ti_ < n_tiles && threadIdx.x < kTileKeys) {                                              \
+      outbuf[ti_ * kTileKeys + threadIdx.x] =                                                    \
+          (red[ti_ & 1][0][threadIdx.x] + red[ti_ & 1][1][threadIdx.x] +                         \
+           red[ti_ & 1][2][threadIdx.x] + red[ti_ & 1][3][threadIdx.x]) * factor;                \
+    }                                                                                            \
+  } while (0)
+
 template <int DT, int D>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void scores_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __restrict__ k,
@@ -374,6 +492,9 @@ void scores_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* 
   using T = MfmaTile<D>;
   __shared__ __align__(16) uint8_t kbuf[2][T::kTileBytes];
   __shared__ float red[2][4][kTileKeys];
+  __shared__ __align__(16) float lse_s[256];
+  __shared__ __align__(16) int lim_s[256];      // last key each row may see (-1: no row)
+  __shared__ __align__(16) float outbuf[kChunkKeys];
   const int u = blockIdx.y, chunk = blockIdx.x;
   const int l = u / p.Hkv, g = u % p.Hkv;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -383,81 +504,41 @@ void scores_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* 
   const int key_end = min(N, key_begin + kChunkKeys);
   const uint8_t* kunit = static_cast<const uint8_t*>(k) +
                          ((static_cast<int64_t>(l) * p.Hkv + g) * p.N * D) * 2;
+  const int n_tiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
   uint4 qf[2][D / 16];
   load_q_frags<DT, D>(p, q, l, g, wave, lane, qf);
   const float c1 = p.scale * kLog2e;
-  // log2-domain LSE of the 32 rows whose outputs this lane holds (+inf: no row)
-  float lse2[2][16];
-  for (int rb = 0; rb < 2; ++rb)
-    for (int v = 0; v < 16; ++v) {
-      const int r = 64 * wave + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-      const bool ok = r < R;
-      const int h = g * p.G + (ok ? r / p.W : 0), t = ok ? r % p.W : 0;
-      lse2[rb][v] = ok ? lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t] * kLog2e : INFINITY;
-    }
+  {
+    const int r = threadIdx.x;                   // 256 threads, one row each
+    const bool ok = r < R;
+    const int h = g * p.G + (ok ? r / p.W : 0), t = ok ? r % p.W : 0;
+    lse_s[r] = ok ? lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t] * kLog2e : INFINITY;
+    lim_s[r] = !ok ? -1 : p.causal ? N - p.W + t : N - 1;
+  }
+  // the K prefetches are issued after every other load, so waiting for a
+  // tile never waits for more than the loads in front of it
+  DeepStage<D> s0, s1, s2;
+  deep_load<D>(kunit, key_begin, N, s0);
+  deep_load<D>(kunit, key_begin + min(1, n_tiles - 1) * kTileKeys, N, s1);
+  deep_load<D>(kunit, key_begin + min(2, n_tiles - 1) * kTileKeys, N, s2);
   float factor = 1.f;
   if (p.head_agg == KVSEL_AGG_MEAN) factor /= static_cast<float>(p.G);
   if (p.row_agg == KVSEL_AGG_MEAN) factor /= static_cast<float>(p.W);
   const int first_masked = p.causal ? N - p.W + 1 : N;   // keys >= this need a per-row check
-
-  uint4 kreg[T::kLoadsPerThread];
-  load_k_tile_regs<D>(kunit, key_begin, p.N, kreg);
-  store_k_tile_lds<D>(kbuf[0], kreg);
+  deep_store<D>(kbuf[0], s0);
+  deep_load<D>(kunit, key_begin + min(3, n_tiles - 1) * kTileKeys, N, s0);
   __syncthreads();
-  const int n_tiles = (key_end - key_begin + kTileKeys - 1) / kTileKeys;
-  for (int ti = 0; ti < n_tiles; ++ti) {
-    const int key0 = key_begin + ti * kTileKeys;
-    if (ti + 1 < n_tiles) load_k_tile_regs<D>(kunit, key0 + kTileKeys, p.N, kreg);
-    const uint8_t* buf = kbuf[ti & 1];
-    f32x16 acc[2][2];                          // [rb][cb]: rows = query rows, cols = keys
-    for (int rb = 0; rb < 2; ++rb)
-      for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16{};
-    for (int ks = 0; ks < T::kKSteps; ++ks) {
-      const uint4 kf0 = k_frag<D>(buf, 0, ks, lane);
-      const uint4 kf1 = k_frag<D>(buf, 1, ks, lane);
-      for (int rb = 0; rb < 2; ++rb) {
-        acc[rb][0] = mfma32<DT>(qf[rb][ks], kf0, acc[rb][0]);
-        acc[rb][1] = mfma32<DT>(qf[rb][ks], kf1, acc[rb][1]);
-      }
-    }
-    const bool full = key0 + kTileKeys <= min(first_masked, key_end);     // uniform
-    float cs[2];
-    for (int cb = 0; cb < 2; ++cb) {
-      const int key = key0 + 32 * cb + (lane & 31);
-      float sum = 0.f;
-      if (full) {
-        for (int rb = 0; rb < 2; ++rb)
-          for (int v = 0; v < 16; ++v)
-            sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][v], c1, -lse2[rb][v]));
-      } else {
-        for (int rb = 0; rb < 2; ++rb)
-          for (int v = 0; v < 16; ++v) {
-            const int r = 64 * wave + 32 * rb + 8 * (v >> 2) + 4 * (lane >> 5) + (v & 3);
-            const bool ok = key < key_end && (!p.causal || key <= N - p.W + r % p.W);
-            const float e = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][v], c1, -lse2[rb][v]));
-            sum += ok ? e : 0.f;
-          }
-      }
-      sum += __shfl_xor(sum, 32, 64);
-      cs[cb] = sum;
-    }
-    if (lane < 32) {
-      red[ti & 1][wave][lane] = cs[0];
-      red[ti & 1][wave][32 + lane] = cs[1];
-    }
-    if (ti + 1 < n_tiles) store_k_tile_lds<D>(kbuf[(ti + 1) & 1], kreg);
-    __syncthreads();
-    // the column sums of tile ti are final: one wave per 16 keys finishes them
-    const int kk = (threadIdx.x & 15) + 16 * wave;
-    if ((threadIdx.x & 63) < 16) {
-      const int key = key0 + kk;
-      if (key < key_end) {
-        const float v = red[ti & 1][0][kk] + red[ti & 1][1][kk] + red[ti & 1][2][kk] + red[ti & 1][3][kk];
-        out[static_cast<int64_t>(u) * p.N + key] = v * factor;
-      }
-    }
+  // tile t waits in set t % 3
+  for (int ti = 0; ti < n_tiles; ti += 3) {
+    KVSEL_SC_TILE(ti, s1);
+    KVSEL_SC_TILE(ti + 1, s2);
+    KVSEL_SC_TILE(ti + 2, s0);
   }
+  __syncthreads();
+  for (int i = threadIdx.x; i < key_end - key_begin; i += 256)
+    out[static_cast<int64_t>(u) * p.N + key_begin + i] = outbuf[i];
 }
+#undef KVSEL_SC_TILE
 
 bool window_mfma_supported(const WindowParams& p, int dt) {
   const int R = p.G * p.W;
