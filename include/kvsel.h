@@ -180,7 +180,11 @@ kvsel_status kvsel_score(const kvsel_score_args* args, void* workspace,
  * centred 1-D pooling kvsel_score offers (odd pool_k; AVG counts
  * out-of-range terms as zero, MAX takes the in-range maximum), computed on
  * the fly while the keys are formed.
- * Errors: KVSEL_E_BUDGET if n_sink + n_recent > k_total and k_total < n_total.
+ * Workspace: an untiled call needs kvsel_select_workspace() bytes (16-byte
+ * aligned; it holds the pooled ordering key of every position and small
+ * per-slice histograms, about 4 bytes per position); tiled calls need none.
+ * Errors: KVSEL_E_BUDGET if n_sink + n_recent > k_total and k_total < n_total;
+ * KVSEL_E_WORKSPACE if the workspace is missing or too small.
  */
 typedef struct kvsel_select_args {
   uint32_t struct_size;

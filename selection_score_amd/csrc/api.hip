@@ -289,12 +289,26 @@ static kvsel_status validate_select(const kvsel_select_args* a) {
   return KVSEL_OK;
 }
 
+static SelectParams select_params(const kvsel_select_args* a) {
+  SelectParams p{};
+  p.U = a->U; p.n = a->n; p.row_stride = a->row_stride; p.base = a->base; p.n_total = a->n_total;
+  p.k_total = a->k_total; p.n_sink = a->n_sink; p.n_recent = a->n_recent;
+  p.slot_map = a->slot_map; p.dead_slot = a->dead_slot;
+  p.cand_score = a->cand_score; p.cand_idx = a->cand_idx; p.cand_count = a->cand_count;
+  p.finalize = a->finalize ? 1 : 0;
+  if (a->cand_count == nullptr) p.finalize = 1;
+  p.kept_idx = a->kept_idx; p.keep_mask = a->keep_mask; p.n_kept = a->n_kept;
+  p.pool = (a->pool_k > 1) ? a->pool : KVSEL_POOL_NONE;
+  p.pool_k = a->pool_k;
+  return p;
+}
+
 kvsel_status kvsel_select_workspace(const kvsel_select_args* a, size_t* bytes) {
   try {
     if (bytes == nullptr) return fail(KVSEL_E_ARG, "bytes is NULL");
     kvsel_status s = validate_select(a);
     if (s != KVSEL_OK) return s;
-    *bytes = 0;
+    *bytes = select_workspace_bytes(select_params(a));
     g_err.clear();
     return KVSEL_OK;
   } catch (...) {
@@ -303,24 +317,17 @@ kvsel_status kvsel_select_workspace(const kvsel_select_args* a, size_t* bytes) {
 }
 
 kvsel_status kvsel_select(const kvsel_select_args* a, void* ws, size_t ws_bytes, void* stream) {
-  (void)ws;
-  (void)ws_bytes;
   try {
     kvsel_status s = validate_select(a);
     if (s != KVSEL_OK) return s;
+    const SelectParams p = select_params(a);
+    const size_t need = select_workspace_bytes(p);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+      return fail(KVSEL_E_WORKSPACE, "select needs %zu bytes of workspace, got %zu", need, ws == nullptr ? 0 : ws_bytes);
+    if (need > 0 && !aligned16(ws)) return fail(KVSEL_E_ARG, "workspace must be 16-byte aligned");
     if ((s = check_device()) != KVSEL_OK) return s;
-    SelectParams p{};
-    p.U = a->U; p.n = a->n; p.row_stride = a->row_stride; p.base = a->base; p.n_total = a->n_total;
-    p.k_total = a->k_total; p.n_sink = a->n_sink; p.n_recent = a->n_recent;
-    p.slot_map = a->slot_map; p.dead_slot = a->dead_slot;
-    p.cand_score = a->cand_score; p.cand_idx = a->cand_idx; p.cand_count = a->cand_count;
-    p.finalize = a->finalize ? 1 : 0;
-    if (a->cand_count == nullptr) p.finalize = 1;
-    p.kept_idx = a->kept_idx; p.keep_mask = a->keep_mask; p.n_kept = a->n_kept;
-    p.pool = (a->pool_k > 1) ? a->pool : KVSEL_POOL_NONE;
-    p.pool_k = a->pool_k;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    return finish(launch_select(p, a->scores, st), st, "select");
+    return finish(launch_select(p, a->scores, ws, st), st, "select");
   } catch (...) {
     return fail(KVSEL_E_ARG, "internal error");
   }

@@ -136,7 +136,10 @@ struct SelectParams {
   int32_t* n_kept;
   int pool, pool_k;
 };
-hipError_t launch_select(const SelectParams& p, const float* scores, hipStream_t st);
+// Untiled calls need select_workspace_bytes(p) of workspace (pooled keys and
+// per-slice histograms); tiled calls need none.
+size_t select_workspace_bytes(const SelectParams& p);
+hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, hipStream_t st);
 
 struct RopeTable {
   double inv_freq[128];

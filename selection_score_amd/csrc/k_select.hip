@@ -14,6 +14,16 @@
 // ballot-based prefix count over it ranks the T-valued entries.  A second
 // ballot prefix places the selected entries, which therefore come out in
 // ascending index order without a sort.
+//
+// Untiled calls run in two launches.  select_keys_kernel spreads the unit
+// over many workgroups: it stages a 4096-column slice of the score row (plus
+// the pooling halo) in LDS, writes the pooled key of every column to the
+// workspace and a 256-bin histogram of the keys' top byte per slice.  The
+// per-unit workgroup of select_kernel then sums those histograms (the first
+// radix pass), runs the remaining passes and both sweeps over the keys in
+// the workspace, and needs no large LDS, so every unit is resident at once.
+// Tiled calls (running candidates) keep the keys of a tile in LDS when they
+// fit, else recompute them from the scores.
 #include "common.h"
 
 namespace kvsel {
@@ -29,6 +39,7 @@ struct SelShared {
   uint32_t wave_eq[kWaves];
   uint32_t wave_gt[kWaves];
   uint32_t wave_cnt[kWaves];
+  uint32_t wave_sums[3 * kWaves];
   uint32_t prefix;
   int32_t remaining;
   int32_t forced_sink_alive;
@@ -101,10 +112,134 @@ __device__ uint32_t block_sum(uint32_t v, uint32_t* scratch) {
   return t;
 }
 
+// Block-wide sums of three per-thread values with one exchange (all threads
+// must call).  scratch holds 3 * kWaves words.
+__device__ uint3 block_sum3(uint32_t a, uint32_t b, uint32_t c, uint32_t* scratch) {
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  for (int o = 32; o > 0; o >>= 1) {
+    a += __shfl_xor(a, o, 64);
+    b += __shfl_xor(b, o, 64);
+    c += __shfl_xor(c, o, 64);
+  }
+  __syncthreads();
+  if (lane == 0) {
+    scratch[wave] = a;
+    scratch[kWaves + wave] = b;
+    scratch[2 * kWaves + wave] = c;
+  }
+  __syncthreads();
+  uint3 t = make_uint3(0u, 0u, 0u);
+  for (int w = 0; w < kWaves; ++w) {
+    t.x += scratch[w];
+    t.y += scratch[kWaves + w];
+    t.z += scratch[2 * kWaves + w];
+  }
+  return t;
+}
+
+constexpr int kPrepKeys = 4096;       // columns per select_keys_kernel workgroup
+constexpr int kPrepThreads = 256;
+constexpr int kMaxPoolR = 127;        // pool_k <= 255
+
+// Wave 0 of the workgroup: the bin of digit `shift` that holds the
+// sh.remaining-th largest candidate among keys matching `prefix` above it
+// (sh.hist holds the digit's histogram); updates sh.prefix and sh.remaining.
+__device__ __forceinline__ void find_bin(SelShared& sh, uint32_t prefix, int shift, int lane) {
+  // lane l owns bins 4l..4l+3
+  uint32_t h[4];
+  uint32_t own = 0;
+  for (int i = 0; i < 4; ++i) {
+    h[i] = sh.hist[4 * lane + i];
+    own += h[i];
+  }
+  // inclusive suffix sum over lanes (lanes above me plus mine)
+  uint32_t suf = own;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_down(suf, o, 64);
+    if (lane + o < 64) suf += v;
+  }
+  const uint32_t above_lane = suf - own;   // bins above my range
+  const int32_t rem = sh.remaining;
+  uint32_t acc = above_lane;
+  int found = -1;
+  uint32_t above_bin = 0;
+  if (above_lane < static_cast<uint32_t>(rem) && suf >= static_cast<uint32_t>(rem)) {
+    for (int i = 3; i >= 0; --i) {
+      if (acc + h[i] >= static_cast<uint32_t>(rem)) {
+        found = 4 * lane + i;
+        above_bin = acc;
+        break;
+      }
+      acc += h[i];
+    }
+  }
+  if (found >= 0) {
+    sh.prefix = prefix | (static_cast<uint32_t>(found) << shift);
+    sh.remaining = rem - static_cast<int32_t>(above_bin);
+  }
+}
+
 }  // namespace
 
-template <bool KEYS_IN_LDS>
-__global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const float* scores) {
+// Keys of one 4096-column slice of a unit (0 = not a candidate: forced,
+// dead, or outside the row) and the histogram of their top byte.
+__global__ __launch_bounds__(kPrepThreads) void select_keys_kernel(SelectParams p, const float* scores,
+                                                                    uint32_t* keys, uint32_t* hist) {
+  __shared__ float row_s[kPrepKeys + 2 * kMaxPoolR];
+  __shared__ uint32_t h[256];
+  const int u = blockIdx.y;
+  const int tid = threadIdx.x;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * kPrepKeys;
+  const int jn = static_cast<int>(min(static_cast<int64_t>(kPrepKeys), p.n - j0));
+  const int r = (p.pool == KVSEL_POOL_NONE) ? 0 : p.pool_k / 2;
+  const float* row = scores + static_cast<int64_t>(u) * p.row_stride;
+  const int64_t sink_end = min(static_cast<int64_t>(p.n_sink), p.n_total);
+  const int64_t rec_begin = max(sink_end, p.n_total - static_cast<int64_t>(p.n_recent));
+  for (int b = tid; b < 256; b += kPrepThreads) h[b] = 0u;
+  // row[j0 - r, j0 + jn + r), out-of-range columns as 0 (the AVG convention)
+  for (int i = tid; i < jn + 2 * r; i += kPrepThreads) {
+    const int64_t j = j0 - r + i;
+    row_s[i] = (j >= 0 && j < p.n) ? row[j] : 0.f;
+  }
+  __syncthreads();
+  uint32_t* kout = keys + static_cast<int64_t>(u) * p.n + j0;
+  for (int i = tid; i < jn; i += kPrepThreads) {
+    const int64_t j = j0 + i;                       // untiled: global index = column
+    uint32_t key = 0u;
+    const bool alive = p.slot_map == nullptr || static_cast<int64_t>(p.slot_map[j]) != p.dead_slot;
+    if (j >= sink_end && j < rec_begin && alive) {
+      float v;
+      if (p.pool == KVSEL_POOL_MAX) {
+        const int lo = static_cast<int>(max(static_cast<int64_t>(0), j - r) - (j0 - r));
+        const int hi = static_cast<int>(min(p.n - 1, j + r) - (j0 - r));
+        v = row_s[lo];
+        for (int t = lo + 1; t <= hi; ++t) v = fmaxf(v, row_s[t]);
+      } else if (p.pool == KVSEL_POOL_AVG) {
+        v = 0.f;
+        for (int t = i; t <= i + 2 * r; ++t) v += row_s[t];
+        v = v / static_cast<float>(2 * r + 1);
+      } else {
+        v = row_s[i];
+      }
+      key = score_key(v);
+      atomicAdd(&h[key >> 24], 1u);
+    }
+    kout[i] = key;
+  }
+  __syncthreads();
+  uint32_t* hout = hist + (static_cast<int64_t>(u) * gridDim.x + blockIdx.x) * 256;
+  for (int b = tid; b < 256; b += kPrepThreads) hout[b] = h[b];
+}
+
+// Per-unit selection.  MODE: kPrepared (keys and top-byte histograms from
+// select_keys_kernel), kLdsKeys (tiled, tile keys staged in LDS), kOnTheFly
+// (tiled, keys recomputed from the scores at every sweep).
+enum SelectMode { kPrepared = 0, kLdsKeys = 1, kOnTheFly = 2 };
+
+template <int MODE>
+__global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const float* scores,
+                                                          const uint32_t* prep_keys,
+                                                          const uint32_t* prep_hist, int n_slices) {
   extern __shared__ uint32_t dyn[];
   __shared__ SelShared sh;
   const int u = blockIdx.x;
@@ -127,7 +262,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
   uint32_t* tkey = dyn + (p.cand_count != nullptr ? 2 * kcap : 0);
   c.ckey = ckey;
   c.cidx = cidx;
-  c.tkey = KEYS_IN_LDS ? tkey : nullptr;
+  c.tkey = (MODE == kLdsKeys) ? tkey : (MODE == kPrepared) ? prep_keys + static_cast<int64_t>(u) * p.n : nullptr;
 
   // ---- alive forced positions of the whole unit
   uint32_t fs = 0, fr = 0;
@@ -143,7 +278,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
     ckey[e] = score_key(p.cand_score[o]);
     cidx[e] = p.cand_idx[o];
   }
-  if constexpr (KEYS_IN_LDS) {
+  if constexpr (MODE == kLdsKeys) {
     for (int64_t j = tid; j < c.n; j += kThreads) {
       const int64_t g = c.base + j;
       tkey[j] = (forced_at(c, g) || !alive_at(c, g)) ? 0u : score_key(column_score(c, j));
@@ -153,9 +288,19 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
 
   const int64_t M = c.c0 + c.n;
   uint32_t cc = 0;
-  for (int64_t e = tid; e < M; e += kThreads) {
-    int64_t g;
-    cc += entry_key(c, e, &g) != 0u ? 1u : 0u;
+  if constexpr (MODE == kPrepared) {
+    // the first radix pass: the slices' top-byte histograms, summed in order
+    for (int b = tid; b < 256; b += kThreads) {
+      uint32_t t = 0;
+      for (int sl = 0; sl < n_slices; ++sl) t += prep_hist[(static_cast<int64_t>(u) * n_slices + sl) * 256 + b];
+      sh.hist[b] = t;
+      cc += t;
+    }
+  } else {
+    for (int64_t e = tid; e < M; e += kThreads) {
+      int64_t g;
+      cc += entry_key(c, e, &g) != 0u ? 1u : 0u;
+    }
   }
   const uint32_t n_cand = block_sum(cc, sh.wave_cnt);
 
@@ -175,51 +320,20 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
     }
     for (int shift = 24; shift >= 0; shift -= 8) {
       const uint32_t hi_mask = (shift == 24) ? 0u : (0xFFFFFFFFu << (shift + 8));
-      for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0u;
-      __syncthreads();
       const uint32_t prefix = sh.prefix;
-      for (int64_t e = tid; e < M; e += kThreads) {
-        int64_t g;
-        const uint32_t key = entry_key(c, e, &g);
-        if (key != 0u && ((key ^ prefix) & hi_mask) == 0u)
-          atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      if (MODE != kPrepared || shift != 24) {       // prepared: the top-byte histogram is summed above
+        __syncthreads();
+        for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0u;
+        __syncthreads();
+        for (int64_t e = tid; e < M; e += kThreads) {
+          int64_t g;
+          const uint32_t key = entry_key(c, e, &g);
+          if (key != 0u && ((key ^ prefix) & hi_mask) == 0u)
+            atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+        }
       }
       __syncthreads();
-      if (wave == 0) {
-        // lane l owns bins 4l..4l+3; find the bin where the count from the top
-        // reaches `remaining`
-        uint32_t h[4];
-        uint32_t own = 0;
-        for (int i = 0; i < 4; ++i) {
-          h[i] = sh.hist[4 * lane + i];
-          own += h[i];
-        }
-        // inclusive suffix sum over lanes (lanes above me plus mine)
-        uint32_t suf = own;
-        for (int o = 1; o < 64; o <<= 1) {
-          const uint32_t v = __shfl_down(suf, o, 64);
-          if (lane + o < 64) suf += v;
-        }
-        const uint32_t above_lane = suf - own;   // bins above my range
-        const int32_t rem = sh.remaining;
-        uint32_t acc = above_lane;
-        int found = -1;
-        uint32_t above_bin = 0;
-        if (above_lane < static_cast<uint32_t>(rem) && suf >= static_cast<uint32_t>(rem)) {
-          for (int i = 3; i >= 0; --i) {
-            if (acc + h[i] >= static_cast<uint32_t>(rem)) {
-              found = 4 * lane + i;
-              above_bin = acc;
-              break;
-            }
-            acc += h[i];
-          }
-        }
-        if (found >= 0) {
-          sh.prefix = prefix | (static_cast<uint32_t>(found) << shift);
-          sh.remaining = rem - static_cast<int32_t>(above_bin);
-        }
-      }
+      if (wave == 0) find_bin(sh, prefix, shift, lane);
       __syncthreads();
     }
     T = sh.prefix;
@@ -327,24 +441,200 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
   if (tid == 0 && p.n_kept != nullptr) p.n_kept[u] = static_cast<int32_t>(total);
 }
 
-hipError_t launch_select(const SelectParams& p, const float* scores, hipStream_t st) {
+// Per-unit selection over prepared keys held in registers.  Wavefront w owns
+// the contiguous segment [w*seg, (w+1)*seg) of the unit in rows of 64
+// columns (KPT rows), so the ballot sweeps see columns in ascending order.
+// Requires n <= KPT * kThreads.
+template <int KPT>
+__global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, const uint32_t* keys,
+                                                               const uint32_t* hist, int n_slices) {
+  __shared__ SelShared sh;
+  const int u = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int n = static_cast<int>(p.n);              // untiled: n == n_total, base == 0
+  const int sink_end = static_cast<int>(min(static_cast<int64_t>(p.n_sink), p.n_total));
+  const int rec_begin = static_cast<int>(max(static_cast<int64_t>(sink_end), p.n_total - p.n_recent));
+  auto alive = [&](int g) {
+    return p.slot_map == nullptr || static_cast<int64_t>(p.slot_map[g]) != p.dead_slot;
+  };
+
+  // ---- alive forced positions, summed top-byte histogram, candidate count
+  uint32_t fs = 0, fr = 0, cc = 0;
+  for (int g = tid; g < sink_end; g += kThreads) fs += alive(g) ? 1u : 0u;
+  for (int g = rec_begin + tid; g < n; g += kThreads) fr += alive(g) ? 1u : 0u;
+  for (int b = tid; b < 256; b += kThreads) {
+    uint32_t t = 0;
+    for (int sl = 0; sl < n_slices; ++sl) t += hist[(static_cast<int64_t>(u) * n_slices + sl) * 256 + b];
+    sh.hist[b] = t;
+    cc += t;
+  }
+  const uint3 sums = block_sum3(fs, fr, cc, sh.wave_sums);
+  const uint32_t fsum = sums.x, rsum = sums.y, n_cand = sums.z;
+  const int32_t room = p.k_total - static_cast<int32_t>(fsum + rsum);
+
+  // ---- this wavefront's keys (0 past the segment)
+  const int seg = ((n + kWaves - 1) / kWaves + 63) / 64 * 64;
+  const int s_beg = min(n, wave * seg);
+  const int s_end = min(n, s_beg + seg);
+  const uint32_t* ku = keys + static_cast<int64_t>(u) * n;
+  uint32_t kr[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int e = s_beg + 64 * i + lane;
+    kr[i] = (e < s_end) ? ku[e] : 0u;
+  }
+
+  // ---- radix select of the room-th largest key (top byte already counted)
+  uint32_t T;
+  int32_t remaining;
+  if (static_cast<int64_t>(n_cand) <= static_cast<int64_t>(room)) {
+    T = 1u;                 // no finite score maps to key 1: every candidate is "> T"
+    remaining = 0;
+  } else if (room <= 0) {
+    T = 0xFFFFFFFFu;        // no finite score maps to this key: nothing is selected
+    remaining = 0;
+  } else {
+    if (tid == 0) {
+      sh.prefix = 0u;
+      sh.remaining = room;
+    }
+    __syncthreads();
+    if (wave == 0) find_bin(sh, 0u, 24, lane);
+    __syncthreads();
+    for (int shift = 16; shift >= 0; shift -= 8) {
+      const uint32_t hi_mask = 0xFFFFFFFFu << (shift + 8);
+      const uint32_t prefix = sh.prefix;
+      for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0u;
+      __syncthreads();
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const uint32_t key = kr[i];
+        if (key != 0u && ((key ^ prefix) & hi_mask) == 0u) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+      }
+      __syncthreads();
+      if (wave == 0) find_bin(sh, prefix, shift, lane);
+      __syncthreads();
+    }
+    T = sh.prefix;
+    remaining = sh.remaining;
+  }
+
+  // ---- sweep A: per-wave counts of keys == T and > T
+  uint32_t n_eq = 0, n_gt = 0;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const uint32_t key = kr[i];
+    n_eq += __popcll(__ballot(key != 0u && key == T));
+    n_gt += __popcll(__ballot(key != 0u && key > T));
+  }
+  if (lane == 0) {
+    sh.wave_eq[wave] = n_eq;
+    sh.wave_gt[wave] = n_gt;
+  }
+  __syncthreads();
+  uint32_t eq_base = 0, sel_base = 0, n_sel_total = 0;
+  {
+    uint32_t eb = 0;
+    for (int w = 0; w < kWaves; ++w) {
+      const int32_t take_eq = max(0, min(static_cast<int32_t>(sh.wave_eq[w]), remaining - static_cast<int32_t>(eb)));
+      if (w == wave) {
+        eq_base = eb;
+        sel_base = n_sel_total;
+      }
+      n_sel_total += sh.wave_gt[w] + static_cast<uint32_t>(take_eq);
+      eb += sh.wave_eq[w];
+    }
+  }
+
+  // ---- sweep B: place the selected entries in ascending index order
+  int32_t* kept = p.kept_idx + static_cast<int64_t>(u) * p.k_total;
+  uint8_t* mask = (p.keep_mask != nullptr) ? p.keep_mask + static_cast<int64_t>(u) * p.n_total : nullptr;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const int e = s_beg + 64 * i + lane;
+    const uint32_t key = kr[i];
+    const bool is_eq = key != 0u && key == T;
+    const bool is_gt = key != 0u && key > T;
+    const uint64_t beq = __ballot(is_eq);
+    const uint32_t eq_rank = eq_base + __popcll(beq & lanemask_lt(lane));
+    const bool sel = is_gt || (is_eq && static_cast<int32_t>(eq_rank) < remaining);
+    const uint64_t bsel = __ballot(sel);
+    const uint32_t pos = sel_base + __popcll(bsel & lanemask_lt(lane));
+    if (sel) kept[fsum + pos] = e;
+    if (mask != nullptr && e < s_end) {
+      const bool keep = sel || ((e < sink_end || e >= rec_begin) && alive(e));
+      mask[e] = keep ? 1 : 0;
+    }
+    eq_base += __popcll(beq);
+    sel_base += __popcll(bsel);
+  }
+
+  // ---- forced entries: alive sink first, alive recent last
+  if (wave == 0) {
+    uint32_t r = 0;
+    for (int g0 = 0; g0 < sink_end; g0 += 64) {
+      const int g = g0 + lane;
+      const bool a = g < sink_end && alive(g);
+      const uint64_t b = __ballot(a);
+      if (a) kept[r + __popcll(b & lanemask_lt(lane))] = g;
+      r += __popcll(b);
+    }
+  } else if (wave == 1) {
+    uint32_t r = fsum + n_sel_total;
+    for (int g0 = rec_begin; g0 < n; g0 += 64) {
+      const int g = g0 + lane;
+      const bool a = g < n && alive(g);
+      const uint64_t b = __ballot(a);
+      if (a) kept[r + __popcll(b & lanemask_lt(lane))] = g;
+      r += __popcll(b);
+    }
+  }
+  const int64_t total = static_cast<int64_t>(fsum) + n_sel_total + rsum;
+  for (int64_t i = total + tid; i < p.k_total; i += kThreads) kept[i] = -1;
+  if (tid == 0 && p.n_kept != nullptr) p.n_kept[u] = static_cast<int32_t>(total);
+}
+
+size_t select_workspace_bytes(const SelectParams& p) {
+  if (p.cand_count != nullptr || p.U == 0 || p.n == 0) return 0;
+  const int64_t slices = ceil_div(p.n, kPrepKeys);
+  const int64_t key_bytes = (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 256;
+  return static_cast<size_t>(key_bytes + static_cast<int64_t>(p.U) * slices * 256 * 4);
+}
+
+hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, hipStream_t st) {
   if (p.U == 0) return hipSuccess;
   const bool tiled = p.cand_count != nullptr;
-  const size_t cand_bytes = tiled ? static_cast<size_t>(p.k_total) * 8 : 0;
+  if (!tiled) {
+    uint32_t* keys = static_cast<uint32_t*>(ws);
+    const int n_slices = static_cast<int>(ceil_div(p.n, kPrepKeys));
+    uint32_t* hist = keys + (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 64;
+    if (n_slices > 0) {
+      dim3 grid(n_slices, p.U);
+      select_keys_kernel<<<grid, kPrepThreads, 0, st>>>(p, scores, keys, hist);
+    }
+    if (p.n <= 32 * kThreads)
+      select_regs_kernel<32><<<p.U, kThreads, 0, st>>>(p, keys, hist, n_slices);
+    else if (p.n <= 64 * kThreads)
+      select_regs_kernel<64><<<p.U, kThreads, 0, st>>>(p, keys, hist, n_slices);
+    else
+      select_kernel<kPrepared><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
+    return hipGetLastError();
+  }
+  const size_t cand_bytes = static_cast<size_t>(p.k_total) * 8;
   const bool lds_keys = p.n <= kLdsKeysMax && cand_bytes + static_cast<size_t>(p.n) * 4 <= 150 * 1024;
   const size_t shmem = cand_bytes + (lds_keys ? static_cast<size_t>(p.n) * 4 : 0);
   if (lds_keys) {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<true>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<kLdsKeys>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(shmem));
     if (e != hipSuccess) return e;
-    select_kernel<true><<<p.U, kThreads, shmem, st>>>(p, scores);
+    select_kernel<kLdsKeys><<<p.U, kThreads, shmem, st>>>(p, scores, nullptr, nullptr, 0);
   } else {
-    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<false>),
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<kOnTheFly>),
                                        hipFuncAttributeMaxDynamicSharedMemorySize,
                                        static_cast<int>(shmem));
     if (e != hipSuccess) return e;
-    select_kernel<false><<<p.U, kThreads, shmem, st>>>(p, scores);
+    select_kernel<kOnTheFly><<<p.U, kThreads, shmem, st>>>(p, scores, nullptr, nullptr, 0);
   }
   return hipGetLastError();
 }

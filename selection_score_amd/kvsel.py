@@ -151,10 +151,11 @@ def score_block(q, mu, out, *, n_kv_heads, n_begin=0, n_count=None, qbar=None, q
 
 def select(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0, keep_mask=None,
            n_kept=None, slot_map=None, dead_slot=0, cand_score=None, cand_idx=None, cand_count=None,
-           finalize=True, pool="none", pool_k=1, stream=None):
+           finalize=True, pool="none", pool_k=1, workspace=None, stream=None):
     """kvsel_select.  scores [U][n] float32 (rows may be a strided view of
     contiguous memory: pass the 2-D tensor); kept_idx [U][k_total] int32.
-    pool/pool_k rank pooled scores (untiled calls)."""
+    pool/pool_k rank pooled scores (untiled calls).  Returns the workspace
+    (untiled calls need one; pass it back to reuse it)."""
     U, n = scores.shape
     if n_total is None:
         n_total = base + n
@@ -172,7 +173,11 @@ def select(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0,
     a.kept_idx, a.keep_mask, a.n_kept = _ptr(kept_idx), _ptr(keep_mask), _ptr(n_kept)
     a.pool, a.pool_k = _abi.POOL[pool], pool_k
     lib = _abi.load()
-    _check(lib.kvsel_select(ctypes.byref(a), None, 0, _stream(stream)))
+    nb = ctypes.c_size_t(0)
+    _check(lib.kvsel_select_workspace(ctypes.byref(a), ctypes.byref(nb)))
+    ws, wsz = _workspace(nb.value, scores.device, workspace)
+    _check(lib.kvsel_select(ctypes.byref(a), _ptr(ws), wsz, _stream(stream)))
+    return ws
 
 
 # ------------------------------------------------------------------ gather
