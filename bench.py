@@ -50,6 +50,8 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample for the CPU baseline")
+    ap.add_argument("--workload", default="snapkv", choices=["snapkv", "intentkv", "kvmem1m", "kvmem10m"],
+                    help="which workload one step runs (the default line is snapkv)")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
     ap.add_argument("--command", default="", help="profiling commands recorded in the traffic summary")
@@ -200,6 +202,313 @@ def cpu_baseline(inp, cfg, seconds):
                       "excluded" % (done, cfg.U, cfg.N, busy)}
 
 
+class SnapKV:
+    """Token scoring against a 64-query window: LSE pass, score pass, select
+    (max-pool 7 fused), gather of the kept K and V rows."""
+    stages = ["lse", "score", "select", "gather"]
+    kernels = {"score": KERNELS["score"], "gather": KERNELS["gather"]}
+    launches = {"lse": 2, "score": 1, "select": 2, "gather": 1}
+    score_stage = "score"
+    materialise_stages = ["select", "gather"]
+    dtype = "bf16"
+
+    def __init__(self, torch, kv, wl, dev):
+        self.kv, cfg = kv, wl.CONFIGS["snapkv"]
+        self.cfg = cfg
+        self.inp = wl.snapkv_inputs(cfg, dev)
+        q, k, v = self.inp["q"], self.inp["k"], self.inp["v"]
+        U, N, D = cfg.U, cfg.N, cfg.D
+        self.lse = torch.empty((cfg.L, cfg.Hq, cfg.W), dtype=torch.float32, device=dev)
+        self.scores = torch.empty((U, N), dtype=torch.float32, device=dev)
+        self.kept = torch.empty((U, cfg.k), dtype=torch.int32, device=dev)
+        self.dk = torch.empty((U, cfg.k, D), dtype=k.dtype, device=dev)
+        self.dv = torch.empty_like(self.dk)
+        self.k3, self.v3 = k.view(U, N, D), v.view(U, N, D)
+        self.ws = kv.score_window(q, k, None, lse_out=self.lse)
+        self.sel_ws = kv.select(self.scores, self.kept, k_total=cfg.k, n_sink=cfg.n_sink,
+                                n_recent=cfg.n_recent, pool=cfg.pool, pool_k=cfg.pool_k)
+        self.tokens = cfg.L * cfg.Hkv * N
+
+    def step(self, ev, stream, it):
+        kv, cfg, q, k = self.kv, self.cfg, self.inp["q"], self.inp["k"]
+        ev[0].record(stream)
+        kv.score_window(q, k, None, lse_out=self.lse, workspace=self.ws)
+        ev[1].record(stream)
+        kv.score_window(q, k, self.scores, lse_in=self.lse)
+        ev[2].record(stream)
+        kv.select(self.scores, self.kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                  pool=cfg.pool, pool_k=cfg.pool_k, workspace=self.sel_ws)
+        ev[3].record(stream)
+        kv.gather_rerope(self.k3, self.v3, self.kept, self.dk, self.dv, bt=1, D=cfg.D, src_rows=cfg.N,
+                         src_unit_stride=cfg.N * cfg.D)
+        ev[4].record(stream)
+
+    def algo_bytes(self):
+        cfg = self.cfg
+        kb = cfg.L * cfg.Hkv * cfg.N * cfg.D * 2
+        qb = cfg.L * cfg.Hq * cfg.W * cfg.D * 2
+        lb = cfg.L * cfg.Hq * cfg.W * 4
+        sb = cfg.U * cfg.N * 4
+        kept_b = cfg.U * cfg.k * 4
+        gb = 2 * 2 * cfg.U * cfg.k * cfg.D * 2
+        return {"lse": kb + qb + lb, "score": kb + qb + lb + sb, "select": sb + kept_b, "gather": kept_b + gb}
+
+    def config(self):
+        cfg = self.cfg
+        return {"workload": "snapkv-h2o token scoring: 36 layers x 8 KV heads (32 query heads) x "
+                            "32768 tokens x D128 bf16, window 64, max-pool 7, top 8192 per (layer, KV "
+                            "head) with 4 sink + 256 recent, gather K+V",
+                "units": cfg.U, "tokens_per_unit": cfg.N, "budget": cfg.k}
+
+    def extra(self):
+        return {}
+
+
+class IntentKV:
+    """Session-memory scoring over a paged pool: one turn's memory update,
+    memory-attention rule scores summed over every layer and head, a global
+    top-8192 (dead slots excluded), and the slot-map redirect with sentinel
+    rows.  The slot map is reset from the original before each step (a 256 KiB
+    copy outside the stage events) so every step does the same work."""
+    stages = ["update", "score", "select", "redirect"]
+    kernels = {"update": ("memory_update_kernel", "k_misc.hip")}
+    launches = {"update": 1, "score": 4, "select": 2, "redirect": 2}
+    score_stage = "score"
+    materialise_stages = ["select", "redirect"]
+    dtype = "bf16"
+
+    def __init__(self, torch, kv, wl, dev):
+        self.kv, self.cfg = kv, wl.CONFIGS["intentkv"]
+        cfg = self.cfg
+        self.inp = wl.intentkv_inputs(cfg, dev)
+        L, Hq, D, N = cfg.L, cfg.Hq, cfg.D, cfg.N
+        self.m = torch.zeros((L, Hq, D), dtype=torch.float32, device=dev)
+        self.rule = torch.empty(N, dtype=torch.float32, device=dev)
+        self.kept = torch.empty((1, cfg.k), dtype=torch.int32, device=dev)
+        self.mask = torch.empty((1, N), dtype=torch.uint8, device=dev)
+        self.sm = self.inp["slot_map"].clone()
+        self.kflat = self.inp["k_pool"].view(L, -1, cfg.Hkv, D)
+        self.vflat = self.inp["v_pool"].view(L, -1, cfg.Hkv, D)
+        kv.memory_update(self.inp["turns"][0], self.m, decay=cfg.decay)
+        self.ws = kv.score_memory(self.m, self.inp["k_pool"], self.inp["page_table"], N, self.rule,
+                                  page_size=cfg.page_size, slot_map=self.sm, dead_slot=self.inp["dead_slot"],
+                                  n_sink=cfg.n_sink, n_recent=cfg.n_recent)
+        self.sel_ws = kv.select(self.rule[None], self.kept, k_total=cfg.k, n_sink=cfg.n_sink,
+                                n_recent=cfg.n_recent, keep_mask=self.mask, slot_map=self.sm,
+                                dead_slot=self.inp["dead_slot"])
+        self.tokens = cfg.L * cfg.Hkv * N
+
+    def step(self, ev, stream, it):
+        kv, cfg, inp = self.kv, self.cfg, self.inp
+        self.sm.copy_(inp["slot_map"])
+        ev[0].record(stream)
+        kv.memory_update(inp["turns"][it % cfg.turns], self.m, decay=cfg.decay)
+        ev[1].record(stream)
+        kv.score_memory(self.m, inp["k_pool"], inp["page_table"], cfg.N, self.rule, page_size=cfg.page_size,
+                        slot_map=self.sm, dead_slot=inp["dead_slot"], n_sink=cfg.n_sink,
+                        n_recent=cfg.n_recent, workspace=self.ws)
+        ev[2].record(stream)
+        kv.select(self.rule[None], self.kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                  keep_mask=self.mask, slot_map=self.sm, dead_slot=inp["dead_slot"], workspace=self.sel_ws)
+        ev[3].record(stream)
+        kv.redirect(self.sm, self.mask[0], inp["dead_slot"], k_pool=self.kflat, v_pool=self.vflat)
+        ev[4].record(stream)
+
+    def algo_bytes(self):
+        cfg = self.cfg
+        N, L, Hq, Hkv, D = cfg.N, cfg.L, cfg.Hq, cfg.Hkv, cfg.D
+        mb = L * Hq * D * 4
+        return {"update": L * Hq * cfg.W * D * 2 + 2 * mb,
+                "score": L * N * Hkv * D * 2 + mb + 4 * N + 4 * (N // cfg.page_size) + 4 * N,
+                "select": 4 * N + 4 * N + N + 4 * cfg.k,
+                "redirect": 2 * 4 * N + N + 2 * L * Hkv * D * 2}
+
+    def config(self):
+        cfg = self.cfg
+        return {"workload": "intentkv session-memory scoring: 36 layers x 8 KV heads (32 query heads) x "
+                            "65536 tokens x D128 bf16 in 16-token pages, memory update over a 64-query "
+                            "turn (decay 0.9), global top 8192 with 4 sink + 64 recent, dead-slot redirect",
+                "units": 1, "tokens_per_unit": cfg.N, "budget": cfg.k}
+
+    def extra(self):
+        return {}
+
+
+class KVMem1M:
+    """Block retrieval over a 1M-token workspace: query reduction and Mean-K
+    block scores, per-unit top-2048 blocks, raw-K gather re-RoPEd to
+    contiguous positions with V copied."""
+    stages = ["score", "select", "gather"]
+    kernels = {"gather": ("gather_blocks_kernel", "k_gather.hip")}
+    launches = {"score": 2, "select": 2, "gather": 1}
+    score_stage = "score"
+    materialise_stages = ["select", "gather"]
+    dtype = "bf16"
+
+    def __init__(self, torch, kv, wl, dev):
+        self.kv, self.cfg = kv, wl.CONFIGS["kvmem1m"]
+        cfg = self.cfg
+        self.mu, w, _ = wl.kvmem_index(cfg, dev)
+        self.q = wl.kvmem_queries(cfg, dev, w, 0)[None]
+        self.raw_k, self.raw_v, self.offs = wl.kvmem_raw_store(cfg, dev)
+        U, NB, k, D, bt = cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt
+        self.scores = torch.empty((1, U, NB), dtype=torch.float32, device=dev)
+        self.qbar = torch.empty((1, cfg.L, cfg.Hkv, D), dtype=torch.float32, device=dev)
+        self.kept = torch.empty((U, k), dtype=torch.int32, device=dev)
+        self.vk = torch.empty((U, k * bt, D), dtype=torch.bfloat16, device=dev)
+        self.vv = torch.empty_like(self.vk)
+        self.ws = kv.score_block(self.q, self.mu, self.scores, n_kv_heads=cfg.Hkv, qbar=self.qbar)
+        self.sel_ws = kv.select(self.scores[0], self.kept, k_total=k, n_sink=cfg.n_sink, n_recent=cfg.n_recent)
+        self.tokens = U * NB * bt
+
+    def step(self, ev, stream, it):
+        kv, cfg = self.kv, self.cfg
+        ev[0].record(stream)
+        kv.score_block(self.q, self.mu, self.scores, n_kv_heads=cfg.Hkv, qbar=self.qbar, workspace=self.ws)
+        ev[1].record(stream)
+        kv.select(self.scores[0], self.kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                  workspace=self.sel_ws)
+        ev[2].record(stream)
+        kv.gather_rerope(self.raw_k, self.raw_v, self.kept, self.vk, self.vv, bt=cfg.bt, D=cfg.D,
+                         src_rows=cfg.N * cfg.bt, src_offsets=self.offs, rope="raw", theta=cfg.theta)
+        ev[3].record(stream)
+
+    def algo_bytes(self):
+        cfg = self.cfg
+        U, NB, k, D, bt = cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt
+        sb = U * NB * 4
+        return {"score": cfg.L * cfg.Hq * cfg.W * D * 2 + U * NB * D * 2 + sb,
+                "select": sb + U * k * 4,
+                "gather": U * k * 4 + 2 * 2 * U * k * bt * D * 2}
+
+    def config(self):
+        cfg = self.cfg
+        return {"workload": "kvmem 1M-token block retrieval: 64 layers x 8 KV heads (64 query heads), "
+                            "32768 32-token blocks per unit, fp16 Mean-K, 512-token query, top 2048 blocks "
+                            "(block 0 + last 4 forced), raw-K gather re-RoPEd at theta 1e6, V copied",
+                "units": cfg.U, "blocks_per_unit": cfg.N, "budget_blocks": cfg.k}
+
+    def extra(self):
+        return {}
+
+
+class KVMem10M:
+    """Scale-out block retrieval: a 10M-token Mean-K index scored in
+    65536-block tiles for 4 sessions with a running tiled top-4096, then the
+    in-place incremental update of each session's 4096-page view (the
+    previous view shares about half its blocks with the new selection).
+    The previous-view lists are inputs, so every step does the same work."""
+    stages = ["tiles", "update"]
+    kernels = {}
+    launches = {"tiles": 11, "update": 2}
+    score_stage = "tiles"
+    materialise_stages = ["update"]
+    dtype = "bf16"
+
+    def __init__(self, torch, kv, wl, dev):
+        import numpy as np
+        self.torch, self.kv, self.cfg = torch, kv, wl.CONFIGS["kvmem10m"]
+        cfg = self.cfg
+        S, U, NB, k, D, bt, tile = cfg.S, cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt, cfg.tile
+        room = k - cfg.n_sink - cfg.n_recent
+        self.mu, w, planted = wl.kvmem_index(cfg, dev, n_dirs=S, planted=(room, 10.0))
+        self.qs = torch.stack([wl.kvmem_queries(cfg, dev, w, s) for s in range(S)])
+        SU = S * U
+        self.qbar = torch.empty((S, cfg.L, cfg.Hkv, D), dtype=torch.float32, device=dev)
+        self.cs = torch.empty((SU, k), dtype=torch.float32, device=dev)
+        self.ci = torch.empty((SU, k), dtype=torch.int32, device=dev)
+        self.cc = torch.zeros(SU, dtype=torch.int32, device=dev)
+        self.kept = torch.empty((SU, k), dtype=torch.int32, device=dev)
+        self.tile_out = torch.empty((S, U, tile), dtype=torch.float32, device=dev)
+        self.raw_k = torch.empty((cfg.Hkv, NB, bt, D), dtype=torch.bfloat16, device=dev)
+        self.raw_v = torch.empty_like(self.raw_k)
+        gen = torch.Generator(device=dev).manual_seed(cfg.seed + 77)
+        for h in range(cfg.Hkv):
+            self.raw_k[h].normal_(generator=gen)
+            self.raw_v[h].normal_(generator=gen)
+        self.offs = torch.tensor([((i % U) % cfg.Hkv) * NB * bt * D for i in range(SU)], dtype=torch.int64,
+                                 device=dev)
+        rng = np.random.default_rng(cfg.seed)
+        prev_idx = np.empty((SU, k), np.int32)
+        prev_page = np.empty((SU, k), np.int32)
+        planted_h = planted.cpu().numpy()
+        for i in range(SU):
+            s, u = divmod(i, U)
+            l, g = divmod(u, cfg.Hkv)
+            inside = rng.choice(planted_h[s, l, g], k // 2, replace=False)
+            taken = np.zeros(NB, bool)
+            taken[planted_h[s, l, g]] = True
+            draw = np.unique(rng.integers(0, NB, 3 * k))
+            draw = draw[~taken[draw]]
+            outside = rng.choice(draw, k - k // 2, replace=False)
+            prev_idx[i] = np.sort(np.concatenate([inside, outside]))
+            prev_page[i] = rng.permutation(k)
+        self.prev_idx_h = prev_idx
+        self.prev_idx = torch.from_numpy(prev_idx).to(dev)
+        self.prev_page = torch.from_numpy(prev_page).to(dev)
+        self.pool_k = torch.full((SU, k, bt, D), 0.5, dtype=torch.bfloat16, device=dev)
+        self.pool_v = torch.full((SU, k, bt, D), -0.25, dtype=torch.bfloat16, device=dev)
+        self.pt = torch.empty((SU, k), dtype=torch.int32, device=dev)
+        self.nm = torch.empty(SU, dtype=torch.int32, device=dev)
+        self.tokens = S * U * NB * bt
+        self.ws = None
+        self.inc_ws = None
+
+    def step(self, ev, stream, it):
+        kv, cfg = self.kv, self.cfg
+        S, U, NB, k, tile = cfg.S, cfg.U, cfg.N, cfg.k, cfg.tile
+        SU = S * U
+        ev[0].record(stream)
+        self.cc.zero_()
+        for b in range(0, NB, tile):
+            n = min(tile, NB - b)
+            out = self.tile_out.view(-1)[: SU * n]
+            self.ws = kv.score_block(self.qs if b == 0 else None, self.mu, out.view(S, U, n), n_kv_heads=cfg.Hkv,
+                                     n_begin=b, n_count=n, qbar=self.qbar, qbar_valid=b > 0, workspace=self.ws)
+            kv.select(out.view(SU, n), self.kept, k_total=k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                      n_total=NB, base=b, cand_score=self.cs, cand_idx=self.ci, cand_count=self.cc,
+                      finalize=b + n == NB)
+        ev[1].record(stream)
+        self.inc_ws = kv.gather_incremental(self.raw_k, self.raw_v, self.kept, self.prev_idx, self.prev_page,
+                                            self.pool_k, self.pool_v, self.pt, self.nm, bt=cfg.bt, D=cfg.D,
+                                            src_rows=NB * cfg.bt, src_offsets=self.offs, rope="raw",
+                                            theta=cfg.theta, workspace=self.inc_ws)
+        ev[2].record(stream)
+
+    def _moves(self):
+        import numpy as np
+        new = self.kept.cpu().numpy()
+        misses = int(self.nm.sum())
+        moved = 0
+        for i in range(new.shape[0]):
+            common, ia, ib = np.intersect1d(self.prev_idx_h[i], new[i], assume_unique=True, return_indices=True)
+            moved += int(np.count_nonzero(ia != ib))
+        return misses, moved
+
+    def algo_bytes(self):
+        cfg = self.cfg
+        S, U, NB, k, D, bt, tile = cfg.S, cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt, cfg.tile
+        SU = S * U
+        misses, moved = self._moves()
+        blk = bt * D * 2
+        return {"tiles": U * NB * D * 2 + S * cfg.L * cfg.Hq * cfg.W * D * 2 + 2 * SU * NB * 4,
+                "update": misses * 2 * 2 * blk + moved * 2 * blk + 3 * SU * k * 4}
+
+    def config(self):
+        cfg = self.cfg
+        return {"workload": "kvmem 10M-token scale-out retrieval: 64 layers x 8 KV heads, 312500 32-token "
+                            "blocks per unit scored in 65536-block tiles for 4 sessions, tiled top 4096, "
+                            "in-place incremental update of 4096-page views with about half the blocks reused",
+                "units": cfg.U, "sessions": cfg.S, "blocks_per_unit": cfg.N, "budget_blocks": cfg.k}
+
+    def extra(self):
+        misses, moved = self._moves()
+        return {"update_misses": misses, "update_moved_hits": moved}
+
+
+WORKLOADS = {"snapkv": SnapKV, "intentkv": IntentKV, "kvmem1m": KVMem1M, "kvmem10m": KVMem10M}
+
+
 def main():
     args = _args()
     if args.gpus != 1:
@@ -217,66 +526,34 @@ def main():
     from selection_score_amd import workloads as wl
 
     dev = torch.device("cuda:0")
-    cfg = wl.CONFIGS["snapkv"]
-    inp = wl.snapkv_inputs(cfg, dev)
-    q, k, v = inp["q"], inp["k"], inp["v"]
-    U, N, D = cfg.U, cfg.N, cfg.D
-    lse = torch.empty((cfg.L, cfg.Hq, cfg.W), dtype=torch.float32, device=dev)
-    scores = torch.empty((U, N), dtype=torch.float32, device=dev)
-    kept = torch.empty((U, cfg.k), dtype=torch.int32, device=dev)
-    dk = torch.empty((U, cfg.k, D), dtype=k.dtype, device=dev)
-    dv = torch.empty_like(dk)
-    k3, v3 = k.view(U, N, D), v.view(U, N, D)
-    ws = kv.score_window(q, k, None, lse_out=lse)          # sizes and keeps the LSE workspace
-    sel_ws = kv.select(scores, kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
-                       pool=cfg.pool, pool_k=cfg.pool_k)       # sizes and keeps the select workspace
+    wk = WORKLOADS[args.workload](torch, kv, wl, dev)
     stream = torch.cuda.current_stream()
     copy_gbps = copy_reference(stream)
-
-    def step(ev):
-        ev[0].record(stream)
-        kv.score_window(q, k, None, lse_out=lse, workspace=ws)
-        ev[1].record(stream)
-        kv.score_window(q, k, scores, lse_in=lse)
-        ev[2].record(stream)
-        kv.select(scores, kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
-                  pool=cfg.pool, pool_k=cfg.pool_k, workspace=sel_ws)
-        ev[3].record(stream)
-        kv.gather_rerope(k3, v3, kept, dk, dv, bt=1, D=D, src_rows=N, src_unit_stride=N * D)
-        ev[4].record(stream)
-
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(5)] for _ in range(args.steps)]
-    warm = [torch.cuda.Event(enable_timing=True) for _ in range(5)]
-    for _ in range(args.warmup):
-        step(warm)
+    n_ev = len(wk.stages) + 1
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(n_ev)] for _ in range(args.steps)]
+    warm = [torch.cuda.Event(enable_timing=True) for _ in range(n_ev)]
+    for i in range(args.warmup):
+        wk.step(warm, stream, i)
     torch.cuda.synchronize()
     t_start, t_end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t_start.record(stream)
     for i in range(args.steps):
-        step(evs[i])
+        wk.step(evs[i], stream, args.warmup + i)
     t_end.record(stream)
     torch.cuda.synchronize()
     ms_step = t_start.elapsed_time(t_end) / args.steps
-    names = ["lse", "score", "select", "gather"]
-    per = {n: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, n in enumerate(names)}
+    per = {n: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, n in enumerate(wk.stages)}
     stage = {n: sum(t) / len(t) for n, t in per.items()}
-
-    # algorithmic bytes per launch of each stage
-    kb = cfg.L * cfg.Hkv * N * D * k.element_size()
-    qb = q.numel() * q.element_size()
-    sb = U * N * 4
-    lb = lse.numel() * 4
-    kept_b = U * cfg.k * 4
-    gb = 2 * 2 * U * cfg.k * D * k.element_size()
-    algo = {"lse": kb + qb + lb, "score": kb + qb + lb + sb, "select": sb + kept_b, "gather": kept_b + gb}
+    algo = wk.algo_bytes()
     step_bytes = sum(algo.values())
-    # the roofline covers the slowest single-launch stage
-    dom = max(["score", "gather"], key=lambda n: stage[n])
+    # the roofline covers the slowest stage that is one kernel launch, if any
+    singles = [n for n in wk.stages if n in wk.kernels]
+    dom = max(singles or wk.stages, key=lambda n: stage[n])
     achieved = algo[dom] / (stage[dom] * 1e-3) / 1e9
-    tokens = cfg.L * cfg.Hkv * N
+    stem, src = wk.kernels.get(dom, ("%s stage (%d launches)" % (dom, wk.launches[dom]), None))
     out = {
         "metric": METRIC,
-        "value": tokens / (ms_step * 1e-3),
+        "value": wk.tokens / (ms_step * 1e-3),
         "unit": "tokens/s",
         "n_gpus": 1,
         "steps": args.steps,
@@ -285,31 +562,28 @@ def main():
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
-        "dtype": "bf16",
+        "dtype": wk.dtype,
         "data": "synthetic",
-        "config": {"workload": "snapkv-h2o token scoring: 36 layers x 8 KV heads (32 query heads) x "
-                               "32768 tokens x D128 bf16, window 64, max-pool 7, top 8192 per (layer, KV "
-                               "head) with 4 sink + 256 recent, gather K+V",
-                   "units": U, "tokens_per_unit": N, "budget": cfg.k},
+        "config": wk.config(),
         "stages_ms": stage,
         "stages_ms_median": {n: statistics.median(t) for n, t in per.items()},
         "stages_ms_min": {n: min(t) for n, t in per.items()},
-        "stage_gbps": {n: algo[n] / (stage[n] * 1e-3) / 1e9 for n in names},
-        "score_pass_tokens_per_s": tokens / (stage["score"] * 1e-3),
+        "stage_gbps": {n: algo[n] / (stage[n] * 1e-3) / 1e9 for n in wk.stages},
+        "score_pass_tokens_per_s": wk.tokens / (stage[wk.score_stage] * 1e-3),
         "step_hbm_gbps": step_bytes / (ms_step * 1e-3) / 1e9,
         "step_hbm_frac": step_bytes / (ms_step * 1e-3) / 1e9 / HBM_PEAK_GBPS,
-        "select_gather_ms": stage["select"] + stage["gather"],
+        "select_gather_ms": sum(stage[n] for n in wk.materialise_stages),
         "copy_reference_gbps": copy_gbps,
-        "roofline": {"bound": "hbm", "kernel": KERNELS[dom][0], "achieved": achieved,
+        "roofline": {"bound": "hbm", "kernel": stem, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": _traffic(*KERNELS[dom]), "algorithmic_bytes": algo[dom],
+                     "traffic": _traffic(stem, src) if src else None, "algorithmic_bytes": algo[dom],
                      "launch_ms": stage[dom]},
         "cpu_baseline": None,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(inp, cfg, args.cpu_seconds)
+    out.update(wk.extra())
+    if not args.no_cpu_baseline and args.workload == "snapkv":
+        out["cpu_baseline"] = cpu_baseline(wk.inp, wk.cfg, args.cpu_seconds)
     print(json.dumps(out), flush=True)
-
 
 if __name__ == "__main__":
     main()
