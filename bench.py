@@ -20,7 +20,7 @@ Other modes:
                        the FETCH_SIZE / WRITE_SIZE counters to bytes
   --traffic-summary    turns four rocprofv3 --pmc CSV directories (kernel run
                        with FETCH_SIZE, with WRITE_SIZE; copy run with each)
-                       into profiles/traffic_<kernel>.json
+                       into profiles/traffic_<kernel>_<workload>.json
 """
 import argparse
 import hashlib
@@ -40,6 +40,19 @@ COPY_BYTES = 1 << 30
 # stage -> (kernel symbol stem, source file)
 KERNELS = {"lse": ("lse_mfma_kernel", "k_window.hip"), "score": ("scores_mfma_kernel", "k_window.hip"),
            "select": ("select_kernel", "k_select.hip"), "gather": ("gather_rows_kernel", "k_gather.hip")}
+# every kernel of the library -> its source file (traffic summaries)
+KERNEL_SOURCES = {
+    "lse_mfma_kernel": "k_window.hip", "lse_combine_kernel": "k_window.hip",
+    "scores_mfma_kernel": "k_window.hip", "lse_valu_kernel": "k_window.hip",
+    "scores_valu_kernel": "k_window.hip", "pool1d_kernel": "k_window.hip",
+    "select_keys_kernel": "k_select.hip", "select_regs_kernel": "k_select.hip", "select_kernel": "k_select.hip",
+    "gather_rows_kernel": "k_gather.hip", "gather_blocks_kernel": "k_gather.hip",
+    "incremental_plan_kernel": "k_incremental.hip", "incremental_data_kernel": "k_incremental.hip",
+    "memory_logits_kernel": "k_memory.hip", "memory_lse_kernel": "k_memory.hip",
+    "memory_rule_kernel": "k_memory.hip", "memory_layer_sum_kernel": "k_memory.hip",
+    "query_reduce_kernel": "k_block.hip", "block_scores_kernel": "k_block.hip",
+    "memory_update_kernel": "k_misc.hip", "redirect_kernel": "k_misc.hip", "sentinel_kernel": "k_misc.hip",
+}
 
 
 def _args():
@@ -64,10 +77,10 @@ def _source_sha(name):
         return hashlib.sha256(f.read()).hexdigest()[:16]
 
 
-def _traffic(kernel, source):
+def _traffic(kernel, source, workload):
     """HBM bytes per launch from the committed counter summary, if it was taken
     on the current source of the kernel; else None."""
-    path = os.path.join(ROOT, "profiles", "traffic_%s.json" % kernel)
+    path = os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (kernel, workload))
     if not os.path.exists(path):
         return None
     with open(path) as f:
@@ -131,7 +144,7 @@ def _counter_per_dispatch(d, counter):
     return per
 
 
-def traffic_summary(dirs, command):
+def traffic_summary(dirs, command, workload):
     """FETCH_SIZE / WRITE_SIZE (KiB per dispatch) of each kernel, scaled by
     what the same counter reads for the 1 GiB copy, written per kernel to
     profiles/traffic_<kernel>.json."""
@@ -145,20 +158,25 @@ def traffic_summary(dirs, command):
 
     f_scale = (COPY_BYTES / 1024) / copy_kib(cfetch)
     w_scale = (COPY_BYTES / 1024) / copy_kib(cwrite)
+    import re
     os.makedirs(os.path.join(ROOT, "profiles"), exist_ok=True)
-    for stage, (stem, src) in KERNELS.items():
-        names = [n for n in fetch if stem in n]
-        if not names:
-            continue
+    stems = {}
+    for n in fetch:
+        mt = re.search(r"kvsel::(\w+)", n)
+        if mt and mt.group(1) in KERNEL_SOURCES:
+            stems.setdefault(mt.group(1), []).append(n)
+    for stem, names in sorted(stems.items()):
+        src = KERNEL_SOURCES[stem]
         fk = statistics.median(v for n in names for v in fetch[n])
         wk = statistics.median(v for n in names for v in write.get(n, [0.0]))
         rec = {"kernel": stem, "source": "selection_score_amd/csrc/" + src, "source_sha": _source_sha(src),
+               "workload": workload,
                "fetch_kib_raw": fk, "write_kib_raw": wk,
                "copy_scale_fetch": f_scale, "copy_scale_write": w_scale,
                "bytes_per_launch": (fk * f_scale + wk * w_scale) * 1024,
                "fetch_bytes": fk * f_scale * 1024, "write_bytes": wk * w_scale * 1024,
                "command": command}
-        with open(os.path.join(ROOT, "profiles", "traffic_%s.json" % stem), "w") as f:
+        with open(os.path.join(ROOT, "profiles", "traffic_%s_%s.json" % (stem, workload)), "w") as f:
             json.dump(rec, f, indent=1)
             f.write("\n")
         print(json.dumps(rec))
@@ -516,7 +534,7 @@ def main():
               "(the (layer, KV head) units would shard across GPUs without any exchange)", file=sys.stderr)
         sys.exit(2)
     if args.traffic_summary:
-        traffic_summary(args.traffic_summary, args.command)
+        traffic_summary(args.traffic_summary, args.command, args.workload)
         return
     if args.copy_calib:
         copy_calibration()
@@ -576,7 +594,7 @@ def main():
         "copy_reference_gbps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": stem, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": _traffic(stem, src) if src else None, "algorithmic_bytes": algo[dom],
+                     "traffic": _traffic(stem, src, args.workload) if src else None, "algorithmic_bytes": algo[dom],
                      "launch_ms": stage[dom]},
         "cpu_baseline": None,
     }

@@ -105,7 +105,7 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherParams p, RopeTa
 // Requires rotary_dim == D, bt * (D/2) <= kMaxOffTable, bt rows per entry.
 constexpr int kMaxOffTable = 32 * 64;
 
-template <int DT>
+template <int DT, bool kInter, bool kRaw>
 __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, RopeTable rt,
                                                             const void* __restrict__ src_k,
                                                             const void* __restrict__ src_v,
@@ -115,18 +115,19 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
                                                             void* __restrict__ dst_v) {
   constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
   constexpr int E = Vec16<DT>::kElems;
+  constexpr int NP = kInter ? E / 2 : E;     // pairs touched by this lane
+  constexpr int kBatch = 8;                  // row passes whose loads are in flight together
   __shared__ float2 off_tab[kMaxOffTable];   // (cos, sin) of o * inv_freq[m], [o][m]
   const int half = p.D / 2;
-  const bool raw = p.rope == KVSEL_ROPE_RAW;
-  if (raw) {
+  if constexpr (kRaw) {
     for (int t = threadIdx.x; t < p.bt * half; t += blockDim.x) {
       const int o = t / half, m = t - (t / half) * half;
       float c, s;
       angle_sincos(static_cast<double>(o), rt.inv_freq[m], &c, &s);
       off_tab[t] = make_float2(c, s);
     }
+    __syncthreads();
   }
-  __syncthreads();
 
   const int lane = threadIdx.x & 63;
   const int lpr = p.D * esz / 16;               // lanes per row
@@ -134,17 +135,16 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
   const int rlane = lane % lpr;
   const int rsub = lane / lpr;
   const int d0 = rlane * E;
-  const bool interleaved = p.style == KVSEL_ROPE_INTERLEAVED;
   const bool first = d0 < half;
+  const float sgn = first ? -1.f : 1.f;
   const int partner = first ? lane + lpr / 2 : lane - lpr / 2;
-  const int m0 = interleaved ? d0 / 2 : (d0 % half);
-  constexpr int NP = E;                          // pairs touched by this lane (upper bound)
-  const int npair = interleaved ? E / 2 : E;
+  const int m0 = kInter ? d0 / 2 : (d0 % half);
   const int64_t items = static_cast<int64_t>(p.U) * p.k;
   const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
   const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
   const int64_t row_bytes = static_cast<int64_t>(p.D) * esz;
   const int64_t item_bytes = row_bytes * p.bt;
+  const int passes = (p.bt + rows_per_pass - 1) / rows_per_pass;
 
   for (int64_t it = wave_global; it < items; it += n_waves) {
     const int u = static_cast<int>(it / p.k);
@@ -152,39 +152,69 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
     if (n_idx != nullptr && i >= n_idx[u]) continue;
     const int32_t b = idx[it];
     if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
-    const int64_t base_pos = raw ? p.pos0 + i * p.bt : p.pos0 + (i - b) * p.bt;
-    float cb[NP], sb[NP];
-    for (int e = 0; e < npair; ++e)
-      angle_sincos(static_cast<double>(base_pos), rt.inv_freq[m0 + e], &cb[e], &sb[e]);
     const uint8_t* sk = unit_src(src_k, p, u, esz) + static_cast<int64_t>(b) * item_bytes;
     const uint8_t* sv = unit_src(src_v, p, u, esz) + static_cast<int64_t>(b) * item_bytes;
     uint8_t* dk = static_cast<uint8_t*>(dst_k) + it * item_bytes;
     uint8_t* dv = static_cast<uint8_t*>(dst_v) + it * item_bytes;
-    for (int o0 = 0; o0 < p.bt; o0 += rows_per_pass) {
-      const int o = o0 + rsub;
-      const bool act = o < p.bt;
-      const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-      uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-      if (act) {
-        kv = *reinterpret_cast<const uint4*>(sk + off);
-        vv = *reinterpret_cast<const uint4*>(sv + off);
-      }
-      const uint4 other = interleaved ? kv : shfl16(kv, partner);
-      if (act) {
-        float cs[NP], sn[NP];
-        for (int e = 0; e < npair; ++e) {
-          if (raw) {
-            const float2 t = off_tab[o * half + m0 + e];
-            cs[e] = cb[e] * t.x - sb[e] * t.y;
-            sn[e] = sb[e] * t.x + cb[e] * t.y;
-          } else {
-            cs[e] = cb[e];
-            sn[e] = sb[e];
-          }
+    // rotation of the item's base position: lane m evaluates frequency m once,
+    // the lanes that need it read it across the wavefront
+    const int64_t base_pos = kRaw ? p.pos0 + i * p.bt : p.pos0 + (i - b) * p.bt;
+    float cl = 1.f, sl = 0.f;
+    if (lane < half) angle_sincos(static_cast<double>(base_pos), rt.inv_freq[lane], &cl, &sl);
+    float cb[NP], sb[NP];
+#pragma unroll
+    for (int e = 0; e < NP; ++e) {
+      cb[e] = __shfl(cl, m0 + e, 64);
+      sb[e] = __shfl(sl, m0 + e, 64);
+    }
+    for (int q0 = 0; q0 < passes; q0 += kBatch) {
+      uint4 kv[kBatch], vv[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int o = (q0 + j) * rows_per_pass + rsub;
+        kv[j] = make_uint4(0, 0, 0, 0);
+        vv[j] = make_uint4(0, 0, 0, 0);
+        if (q0 + j < passes && o < p.bt) {
+          const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
+          kv[j] = *reinterpret_cast<const uint4*>(sk + off);
+          vv[j] = *reinterpret_cast<const uint4*>(sv + off);
         }
-        kv = rotate_chunk<DT>(kv, other, first, interleaved, cs, sn);
-        *reinterpret_cast<uint4*>(dk + off) = kv;
-        *reinterpret_cast<uint4*>(dv + off) = vv;
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int o = (q0 + j) * rows_per_pass + rsub;
+        if (q0 + j < passes && o < p.bt) {
+          const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
+          *reinterpret_cast<uint4*>(dv + off) = vv[j];
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (q0 + j >= passes) break;                    // uniform
+        const int o = (q0 + j) * rows_per_pass + rsub;
+        const uint4 other = kInter ? kv[j] : shfl16(kv[j], partner);
+        if (o < p.bt) {
+          float cs[NP], sn[NP];
+          if constexpr (kRaw) {
+            const float4* t4 = reinterpret_cast<const float4*>(&off_tab[o * half + m0]);
+#pragma unroll
+            for (int e = 0; e < NP; e += 2) {
+              const float4 t = t4[e / 2];
+              cs[e] = cb[e] * t.x - sb[e] * t.y;
+              sn[e] = sb[e] * t.x + cb[e] * t.y;
+              cs[e + 1] = cb[e + 1] * t.z - sb[e + 1] * t.w;
+              sn[e + 1] = sb[e + 1] * t.z + cb[e + 1] * t.w;
+            }
+          } else {
+#pragma unroll
+            for (int e = 0; e < NP; ++e) {
+              cs[e] = cb[e];
+              sn[e] = sb[e];
+            }
+          }
+          const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
+          *reinterpret_cast<uint4*>(dk + off) = rotate16<DT, kInter>(kv[j], other, sgn, cs, sn);
+        }
       }
     }
   }
@@ -205,12 +235,22 @@ hipError_t launch_gather_fresh(const GatherParams& p, const RopeTable& rt, const
                            p.bt * (p.D / 2) <= kMaxOffTable && lpr <= 64;
   if (blocks_path) {
     const int grid = grid_for(static_cast<int64_t>(p.U) * p.k);
+#define KVSEL_GB3(DTV, INTER, RAW)                                                              \
+  gather_blocks_kernel<DTV, INTER, RAW><<<grid, 256, 0, st>>>(p, rt, src_k, src_v, idx, n_idx, dst_k, dst_v)
 #define KVSEL_GB(DTV)                                                                           \
-  gather_blocks_kernel<DTV><<<grid, 256, 0, st>>>(p, rt, src_k, src_v, idx, n_idx, dst_k, dst_v)
+  do {                                                                                          \
+    const bool inter = p.style == KVSEL_ROPE_INTERLEAVED, raw = p.rope == KVSEL_ROPE_RAW;       \
+    if (inter) {                                                                                \
+      if (raw) KVSEL_GB3(DTV, true, true); else KVSEL_GB3(DTV, true, false);                    \
+    } else {                                                                                    \
+      if (raw) KVSEL_GB3(DTV, false, true); else KVSEL_GB3(DTV, false, false);                  \
+    }                                                                                           \
+  } while (0)
     if (p.dtype == KVSEL_BF16) KVSEL_GB(KVSEL_BF16);
     else if (p.dtype == KVSEL_F16) KVSEL_GB(KVSEL_F16);
     else KVSEL_GB(KVSEL_F32);
 #undef KVSEL_GB
+#undef KVSEL_GB3
   } else {
     const int64_t rows = static_cast<int64_t>(p.U) * p.k * p.bt;
     const int rows_per_wave = 64 / lpr;

@@ -147,40 +147,41 @@ __global__ __launch_bounds__(kPlanThreads) void incremental_plan_kernel(
   }
 }
 
-template <int DT>
+template <int DT, bool kInter, bool kRot>
 __global__ __launch_bounds__(256) void incremental_data_kernel(
     GatherParams p, RopeTable rt, const void* __restrict__ src_k, const void* __restrict__ src_v,
     const int32_t* __restrict__ idx, const int32_t* __restrict__ page_table,
     const int32_t* __restrict__ plan_old, void* __restrict__ pool_k, void* __restrict__ pool_v) {
   constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
   constexpr int E = Vec16<DT>::kElems;
+  constexpr int NP = kInter ? E / 2 : E;     // pairs touched by this lane
+  constexpr int kBatch = 8;                  // row passes whose loads are in flight together
   __shared__ float2 off_tab[kMaxOffTable];
   const int half = p.D / 2;
-  const bool rot = p.rope == KVSEL_ROPE_RAW;
-  if (rot) {
+  if constexpr (kRot) {
     for (int t = threadIdx.x; t < p.bt * half; t += blockDim.x) {
       const int o = t / half, m = t - (t / half) * half;
       float c, s;
       angle_sincos(static_cast<double>(o), rt.inv_freq[m], &c, &s);
       off_tab[t] = make_float2(c, s);
     }
+    __syncthreads();
   }
-  __syncthreads();
   const int lane = threadIdx.x & 63;
   const int lpr = p.D * esz / 16;
   const int rows_per_pass = 64 / lpr;
   const int rlane = lane % lpr, rsub = lane / lpr;
   const int d0 = rlane * E;
-  const bool interleaved = p.style == KVSEL_ROPE_INTERLEAVED;
   const bool first = d0 < half;
+  const float sgn = first ? -1.f : 1.f;
   const int partner = first ? lane + lpr / 2 : lane - lpr / 2;
-  const int m0 = interleaved ? d0 / 2 : (d0 % half);
-  const int npair = interleaved ? E / 2 : E;
+  const int m0 = kInter ? d0 / 2 : (d0 % half);
   const int64_t items = static_cast<int64_t>(p.U) * p.k;
   const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
   const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
   const int64_t row_bytes = static_cast<int64_t>(p.D) * esz;
   const int64_t item_bytes = row_bytes * p.bt;
+  const int passes = (p.bt + rows_per_pass - 1) / rows_per_pass;
 
   for (int64_t it = wave_global; it < items; it += n_waves) {
     const int u = static_cast<int>(it / p.k);
@@ -190,56 +191,87 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
     const int32_t io = plan_old[it];
     uint8_t* pk = static_cast<uint8_t*>(pool_k) + (static_cast<int64_t>(u) * p.pool_pages + page) * item_bytes;
     uint8_t* pv = static_cast<uint8_t*>(pool_v) + (static_cast<int64_t>(u) * p.pool_pages + page) * item_bytes;
-    if (io >= 0) {
-      // hit: rotate K in place by the position change (V untouched)
-      const int64_t delta = (i - io) * p.bt;
-      if (delta == 0 || !rot) continue;
-      float cb[E], sb[E];
-      for (int e = 0; e < npair; ++e)
-        angle_sincos(static_cast<double>(delta), rt.inv_freq[m0 + e], &cb[e], &sb[e]);
-      for (int o0 = 0; o0 < p.bt; o0 += rows_per_pass) {
-        const int o = o0 + rsub;
-        const bool act = o < p.bt;
-        const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-        uint4 kv = act ? *reinterpret_cast<const uint4*>(pk + off) : make_uint4(0, 0, 0, 0);
-        const uint4 other = interleaved ? kv : shfl16(kv, partner);
-        if (act) *reinterpret_cast<uint4*>(pk + off) = rotate_chunk<DT>(kv, other, first, interleaved, cb, sb);
-      }
-    } else {
-      // miss: raw K rotated to its new position, V copied
+    const bool hit = io >= 0;
+    // a hit moves by (i - io) * bt positions (V untouched); a miss is raw K
+    // rotated to its new position, with V copied
+    const int64_t angle_pos = hit ? (i - io) * p.bt : p.pos0 + i * p.bt;
+    if (hit && (angle_pos == 0 || !kRot)) continue;
+    const uint8_t* sk = nullptr;
+    const uint8_t* sv = nullptr;
+    if (!hit) {
       const int32_t b = idx[it];
       if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
       const int64_t soff = p.src_offsets ? p.src_offsets[u] : static_cast<int64_t>(u) * p.src_unit_stride;
-      const uint8_t* sk = static_cast<const uint8_t*>(src_k) + soff * esz + static_cast<int64_t>(b) * item_bytes;
-      const uint8_t* sv = static_cast<const uint8_t*>(src_v) + soff * esz + static_cast<int64_t>(b) * item_bytes;
-      float cb[E], sb[E];
-      if (rot)
-        for (int e = 0; e < npair; ++e)
-          angle_sincos(static_cast<double>(p.pos0 + i * p.bt), rt.inv_freq[m0 + e], &cb[e], &sb[e]);
-      for (int o0 = 0; o0 < p.bt; o0 += rows_per_pass) {
-        const int o = o0 + rsub;
-        const bool act = o < p.bt;
-        const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-        uint4 kv = make_uint4(0, 0, 0, 0), vv = make_uint4(0, 0, 0, 0);
-        if (act) {
-          kv = *reinterpret_cast<const uint4*>(sk + off);
-          vv = *reinterpret_cast<const uint4*>(sv + off);
-        }
-        if (rot) {
-          const uint4 other = interleaved ? kv : shfl16(kv, partner);
-          if (act) {
-            float cs[E], sn[E];
-            for (int e = 0; e < npair; ++e) {
-              const float2 t = off_tab[o * half + m0 + e];
-              cs[e] = cb[e] * t.x - sb[e] * t.y;
-              sn[e] = sb[e] * t.x + cb[e] * t.y;
-            }
-            kv = rotate_chunk<DT>(kv, other, first, interleaved, cs, sn);
+      sk = static_cast<const uint8_t*>(src_k) + soff * esz + static_cast<int64_t>(b) * item_bytes;
+      sv = static_cast<const uint8_t*>(src_v) + soff * esz + static_cast<int64_t>(b) * item_bytes;
+    }
+    float cb[NP], sb[NP];
+    if constexpr (kRot) {
+      float cl = 1.f, sl = 0.f;
+      if (lane < half) angle_sincos(static_cast<double>(angle_pos), rt.inv_freq[lane], &cl, &sl);
+#pragma unroll
+      for (int e = 0; e < NP; ++e) {
+        cb[e] = __shfl(cl, m0 + e, 64);
+        sb[e] = __shfl(sl, m0 + e, 64);
+      }
+    }
+    for (int q0 = 0; q0 < passes; q0 += kBatch) {
+      uint4 kv[kBatch], vv[kBatch];
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        const int o = (q0 + j) * rows_per_pass + rsub;
+        kv[j] = make_uint4(0, 0, 0, 0);
+        vv[j] = make_uint4(0, 0, 0, 0);
+        if (q0 + j < passes && o < p.bt) {
+          const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
+          if (hit) {
+            kv[j] = *reinterpret_cast<const uint4*>(pk + off);
+          } else {
+            kv[j] = *reinterpret_cast<const uint4*>(sk + off);
+            vv[j] = *reinterpret_cast<const uint4*>(sv + off);
           }
         }
-        if (act) {
-          *reinterpret_cast<uint4*>(pk + off) = kv;
-          *reinterpret_cast<uint4*>(pv + off) = vv;
+      }
+      if (!hit) {
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int o = (q0 + j) * rows_per_pass + rsub;
+          if (q0 + j < passes && o < p.bt) {
+            const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
+            *reinterpret_cast<uint4*>(pv + off) = vv[j];
+          }
+        }
+      }
+#pragma unroll
+      for (int j = 0; j < kBatch; ++j) {
+        if (q0 + j >= passes) break;                    // uniform
+        const int o = (q0 + j) * rows_per_pass + rsub;
+        uint4 out = kv[j];
+        if constexpr (kRot) {
+          const uint4 other = kInter ? kv[j] : shfl16(kv[j], partner);
+          float cs[NP], sn[NP];
+          if (hit) {
+#pragma unroll
+            for (int e = 0; e < NP; ++e) {
+              cs[e] = cb[e];
+              sn[e] = sb[e];
+            }
+          } else {
+            const float4* t4 = reinterpret_cast<const float4*>(&off_tab[(o < p.bt ? o : 0) * half + m0]);
+#pragma unroll
+            for (int e = 0; e < NP; e += 2) {
+              const float4 t = t4[e / 2];
+              cs[e] = cb[e] * t.x - sb[e] * t.y;
+              sn[e] = sb[e] * t.x + cb[e] * t.y;
+              cs[e + 1] = cb[e + 1] * t.z - sb[e + 1] * t.w;
+              sn[e + 1] = sb[e + 1] * t.z + cb[e + 1] * t.w;
+            }
+          }
+          out = rotate16<DT, kInter>(kv[j], other, sgn, cs, sn);
+        }
+        if (o < p.bt) {
+          const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
+          *reinterpret_cast<uint4*>(pk + off) = out;
         }
       }
     }
@@ -265,13 +297,23 @@ hipError_t launch_gather_incremental(const GatherParams& p, const RopeTable& rt,
   const int64_t items = static_cast<int64_t>(p.U) * p.k;
   const int64_t blocks = ceil_div(items, 4);
   const int grid = static_cast<int>(blocks > 65536 ? 65536 : blocks);
+#define KVSEL_ID3(DTV, INTER, ROT)                                                                 \
+  incremental_data_kernel<DTV, INTER, ROT><<<grid, 256, 0, st>>>(p, rt, src_k, src_v, idx, page_table,  \
+                                                                 plan_old, pool_k, pool_v)
 #define KVSEL_ID(DTV)                                                                              \
-  incremental_data_kernel<DTV><<<grid, 256, 0, st>>>(p, rt, src_k, src_v, idx, page_table, plan_old, \
-                                                     pool_k, pool_v)
+  do {                                                                                             \
+    const bool inter = p.style == KVSEL_ROPE_INTERLEAVED, rot = p.rope == KVSEL_ROPE_RAW;          \
+    if (inter) {                                                                                   \
+      if (rot) KVSEL_ID3(DTV, true, true); else KVSEL_ID3(DTV, true, false);                       \
+    } else {                                                                                       \
+      if (rot) KVSEL_ID3(DTV, false, true); else KVSEL_ID3(DTV, false, false);                     \
+    }                                                                                              \
+  } while (0)
   if (p.dtype == KVSEL_BF16) KVSEL_ID(KVSEL_BF16);
   else if (p.dtype == KVSEL_F16) KVSEL_ID(KVSEL_F16);
   else KVSEL_ID(KVSEL_F32);
 #undef KVSEL_ID
+#undef KVSEL_ID3
   return hipGetLastError();
 }
 

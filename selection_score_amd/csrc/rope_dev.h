@@ -58,17 +58,18 @@ __device__ __forceinline__ uint4 pack16(const float* x) {
     v.z = __float_as_uint(x[2]);
     v.w = __float_as_uint(x[3]);
   } else {
+    // round-to-nearest-even conversions, two elements per instruction
+    typedef float f32x2 __attribute__((ext_vector_type(2)));
+    typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
+    typedef _Float16 f16x2 __attribute__((ext_vector_type(2)));
     uint32_t w[4];
     for (int i = 0; i < 4; ++i) {
-      uint16_t lo, hi;
+      const f32x2 pr = {x[2 * i], x[2 * i + 1]};
       if constexpr (DT == KVSEL_BF16) {
-        lo = f32_to_bf16(x[2 * i]);
-        hi = f32_to_bf16(x[2 * i + 1]);
+        w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, bf16x2));
       } else {
-        lo = f32_to_f16(x[2 * i]);
-        hi = f32_to_f16(x[2 * i + 1]);
+        w[i] = __builtin_bit_cast(uint32_t, __builtin_convertvector(pr, f16x2));
       }
-      w[i] = static_cast<uint32_t>(lo) | (static_cast<uint32_t>(hi) << 16);
     }
     v.x = w[0];
     v.y = w[1];
@@ -106,6 +107,29 @@ __device__ __forceinline__ uint4 rotate_chunk(const uint4& own, const uint4& oth
     for (int i = 0; i < E; ++i) {
       y[i] = first ? (a[i] * cs[i] - b[i] * sn[i]) : (b[i] * sn[i] + a[i] * cs[i]);
     }
+  }
+  return pack16<DT>(y);
+}
+
+// One lane's 16-byte chunk rotated by (c, s) per pair.  Rotate-half: `own`
+// holds dims [d0, d0+E) of one half, `other` the matching dims of the other
+// half, and `sgn` is -1 for the first half (x_m c - x_{m+D/2} s) and +1 for
+// the second (x_{m+D/2} c + x_m s).  Interleaved: pairs are adjacent in `own`.
+template <int DT, bool kInter>
+__device__ __forceinline__ uint4 rotate16(const uint4& own, const uint4& other, float sgn, const float* c,
+                                          const float* s) {
+  constexpr int E = Vec16<DT>::kElems;
+  float a[E], y[E];
+  unpack16<DT>(own, a);
+  if constexpr (kInter) {
+    for (int i = 0; i < E; i += 2) {
+      y[i] = a[i] * c[i / 2] - a[i + 1] * s[i / 2];
+      y[i + 1] = a[i] * s[i / 2] + a[i + 1] * c[i / 2];
+    }
+  } else {
+    float b[E];
+    unpack16<DT>(other, b);
+    for (int i = 0; i < E; ++i) y[i] = fmaf(b[i], sgn * s[i], a[i] * c[i]);
   }
   return pack16<DT>(y);
 }
