@@ -101,6 +101,86 @@ __global__ __launch_bounds__(256) void block_scores_kernel(BlockParams p, const 
   }
 }
 
+// The same scores on the matrix cores: v_mfma_f32_16x16x16_f16 with 16
+// index rows as the A operand and the sessions' q-bar as the B columns.
+// q-bar is float32; it enters the f16 products as hi + lo parts after a
+// per-session power-of-two scaling (exact), so the products carry about 22
+// significant bits.  The contraction over d is split into k-steps in a
+// permuted but consistent order on both operands: lane quarter q, k-step
+// 2t+h covers d = 8q + 32t + 4h .. +3, so each lane reads 16 contiguous
+// bytes of its index row per pair of k-steps.
+typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+__global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, const float* __restrict__ qbar,
+                                                                const uint16_t* __restrict__ mu,
+                                                                float* __restrict__ out) {
+  const int U = p.L * p.Hkv;
+  const int u = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int col = lane & 15, quarter = lane >> 4;
+  // B fragments: session `col`, d = 8*quarter + 32t + 4h + j; scaled by 2^-e
+  const bool live = col < p.S;
+  const float* qb = qbar + (static_cast<int64_t>(col < p.S ? col : 0) * U + u) * 128;
+  float qv[4][8];
+  float amax = 0.f;
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      qv[t][j] = live ? qb[8 * quarter + 32 * t + j] : 0.f;
+      amax = fmaxf(amax, fabsf(qv[t][j]));
+    }
+  amax = fmaxf(amax, __shfl_xor(amax, 16, 64));
+  amax = fmaxf(amax, __shfl_xor(amax, 32, 64));
+  int e2 = 0;
+  frexpf(amax, &e2);                             // amax < 2^e2
+  const float down = ldexpf(1.f, 14 - e2), up = ldexpf(p.scale, e2 - 14);
+  f16x4 bh[4][2], bl[4][2];
+#pragma unroll
+  for (int t = 0; t < 4; ++t)
+#pragma unroll
+    for (int h = 0; h < 2; ++h)
+#pragma unroll
+      for (int j = 0; j < 4; ++j) {
+        const float x = qv[t][4 * h + j] * down;
+        const _Float16 hi = static_cast<_Float16>(x);
+        bh[t][h][j] = hi;
+        bl[t][h][j] = static_cast<_Float16>(x - static_cast<float>(hi));
+      }
+  const uint16_t* mu_u = mu + (static_cast<int64_t>(u) * p.NB + p.n_begin) * 128;
+  const int64_t n_tiles = (p.n_count + 15) / 16;
+  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
+  float* out_s = out + (static_cast<int64_t>(col) * U + u) * p.n_count;
+  for (int64_t tile = wave; tile < n_tiles; tile += n_waves) {
+    const int64_t r = tile * 16 + col;           // A row of this lane
+    uint4 a[4];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+      a[t] = (r < p.n_count) ? *reinterpret_cast<const uint4*>(mu_u + r * 128 + 8 * quarter + 32 * t)
+                             : make_uint4(0, 0, 0, 0);
+    f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int t = 0; t < 4; ++t) {
+      const f16x4 a0 = __builtin_bit_cast(f16x4, make_uint2(a[t].x, a[t].y));
+      const f16x4 a1 = __builtin_bit_cast(f16x4, make_uint2(a[t].z, a[t].w));
+      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, bh[t][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a0, bl[t][0], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, bh[t][1], acc, 0, 0, 0);
+      acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, bl[t][1], acc, 0, 0, 0);
+    }
+    // lane holds session `col`, index rows tile*16 + 4*quarter + i
+    if (live) {
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t rr = tile * 16 + 4 * quarter + i;
+        if (rr < p.n_count) out_s[rr] = acc[i] * up;
+      }
+    }
+  }
+}
+
 hipError_t launch_query_reduce(const BlockParams& p, int dt, const void* q, float* qbar,
                                hipStream_t st) {
   const int units = p.S * p.L * p.Hkv;
@@ -120,6 +200,12 @@ hipError_t launch_block_scores(const BlockParams& p, const float* qbar, const vo
   const int64_t blocks_x = ceil_div(p.n_count, static_cast<int64_t>(rows_per_wave) * 4 * 8);
   dim3 grid(static_cast<unsigned>(blocks_x < 1 ? 1 : (blocks_x > 4096 ? 4096 : blocks_x)), U);
   const uint16_t* m = static_cast<const uint16_t*>(mu);
+  if (p.D == 128) {
+    const int64_t bx = ceil_div(ceil_div(p.n_count, 16), 4 * 4);   // ~4 tiles per wave
+    dim3 g2(static_cast<unsigned>(bx < 1 ? 1 : (bx > 8192 ? 8192 : bx)), U);
+    block_scores_mfma_kernel<<<g2, 256, 0, st>>>(p, qbar, m, out);
+    return hipGetLastError();
+  }
   if (p.S <= 1) block_scores_kernel<1><<<grid, 256, 0, st>>>(p, qbar, m, out);
   else if (p.S <= 4) block_scores_kernel<4><<<grid, 256, 0, st>>>(p, qbar, m, out);
   else block_scores_kernel<8><<<grid, 256, 0, st>>>(p, qbar, m, out);

@@ -6,13 +6,14 @@
 // is paged (ActKV §2: physical page of logical page p = page_table[p]).
 //
 // Kernels:
-//  1. logits: one workgroup per (layer, group of logical pages).  Each thread
-//     keeps one query head's memory row in registers and dots it with K rows
-//     of a page staged in LDS (double buffered, padded rows); logits go to a
-//     float32 scratch [L][Hq][N] and each workgroup leaves a partial
+//  1. logits: one workgroup per (layer, group of logical pages); logits go to
+//     a float32 scratch [L][Hq][N] and each workgroup leaves a partial
 //     (max, sum of exp) per head over the history positions it saw.  K is
-//     read from HBM exactly once.
-//  2. combine the partials into LSE[l][h].
+//     read from HBM exactly once.  bf16 pools with D = 128, 16-token pages
+//     and GQA groups of 4, 8 or 16 use the matrix cores
+//     (memory_logits_mfma_kernel); other shapes dot on the vector ALUs with
+//     pages staged in LDS (memory_logits_kernel).
+//  2. combine the partials into LSE[l][h], one wavefront per (layer, head).
 //  3. per (layer, 256 positions): sum over the layer's heads of
 //     exp(logit - LSE) over H -> per-layer partial rule (or the per-unit
 //     output directly).
@@ -25,6 +26,7 @@ namespace kvsel {
 
 namespace {
 constexpr int kPagesPerGroup = 16;
+constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxHq = 64;
 
 __device__ __forceinline__ bool in_history(const MemoryParams& p, int64_t j) {
@@ -153,19 +155,146 @@ __global__ __launch_bounds__(256) void memory_logits_kernel(MemoryParams p, cons
   }
 }
 
-__global__ void memory_lse_kernel(MemoryParams p, int n_groups, const float2* __restrict__ part,
-                                  float* __restrict__ lse) {
-  const int i = blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= p.L * p.Hq) return;
+// The logits on the matrix cores (bf16 pool, D = 128, 16-token pages, up to
+// 32 query heads, GQA group G >= 4): v_mfma_f32_16x16x32_bf16 with the 16
+// tokens of a page (one KV head) as A rows and 16 query heads as B columns;
+// the columns of the KV head's own group are kept.  The float32 memory rows
+// enter as bf16 hi + lo parts (about 16 significant bits; the logits keep
+// ~2^-18 of the sum of |terms|).  Lane quarter q covers d = 32*ks + 8q .. +7
+// of k-step ks on both operands.  Each wavefront serves one block of 16
+// query heads (NG = 16 / G KV heads) and a share of the pages, reading all
+// NG rows of a page straight into its A operands before multiplying.
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+
+template <int NCB, int NG>
+__global__ __launch_bounds__(256) void memory_logits_mfma_kernel(MemoryParams p, const float* __restrict__ M,
+                                                                 const void* __restrict__ pool,
+                                                                 float* __restrict__ logits,
+                                                                 float2* __restrict__ part) {
+  constexpr int D = 128, PS = 16;
+  constexpr int kWavesPerCb = 4 / NCB;
+  __shared__ float2 red[4][64];
+  const int l = blockIdx.y, grp = blockIdx.x;
+  const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+  const int col = lane & 15, qd = lane >> 4;
+  const int G = p.Hq / p.Hkv;
+  const int cb = wave / kWavesPerCb, wsub = wave % kWavesPerCb;
+  const int h = 16 * cb + col;                       // this lane's query head
+  const int gi_own = col / G;                        // its KV head within the block
+  // B operands: head h, d = 32*ks + 8*qd + j, as bf16 hi + lo
+  bf16x8 bh[4], bl[4];
+  {
+    const float* row = M + (static_cast<int64_t>(l) * p.Hq + (h < p.Hq ? h : 0)) * D;
+#pragma unroll
+    for (int ks = 0; ks < 4; ++ks)
+#pragma unroll
+      for (int j = 0; j < 8; ++j) {
+        const float x = (h < p.Hq) ? row[32 * ks + 8 * qd + j] : 0.f;
+        const __bf16 hi = static_cast<__bf16>(x);
+        bh[ks][j] = hi;
+        bl[ks][j] = static_cast<__bf16>(x - static_cast<float>(hi));
+      }
+  }
   float m = -INFINITY, s = 0.f;
-  for (int gi = 0; gi < n_groups; ++gi) {
+  const int64_t n_lpages = ceil_div(p.N, PS);
+  const int64_t lp_begin = static_cast<int64_t>(grp) * kPagesPerGroup;
+  const int64_t lp_end = min(n_lpages, lp_begin + kPagesPerGroup);
+  const int64_t page_bytes = static_cast<int64_t>(PS) * p.Hkv * D * 2;
+  const uint8_t* lpool = static_cast<const uint8_t*>(pool) + static_cast<int64_t>(l) * p.pool_pages * page_bytes;
+  for (int64_t lp = lp_begin + wsub; lp < lp_end; lp += kWavesPerCb) {
+    const int64_t pp = p.page_table[lp];
+    const bool ok = pp >= 0 && pp < p.pool_pages;
+    const uint8_t* base = lpool + (ok ? pp : 0) * page_bytes + (static_cast<int64_t>(col) * p.Hkv) * D * 2 + 16 * qd;
+    uint4 a[NG][4];
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      const int g = cb * NG + gi;
+      const bool okg = ok && g < p.Hkv;
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks)
+        a[gi][ks] = okg ? *reinterpret_cast<const uint4*>(base + static_cast<int64_t>(g) * D * 2 + 64 * ks)
+                        : make_uint4(0, 0, 0, 0);
+    }
+    const int64_t j0 = lp * PS + 4 * qd;
+#pragma unroll
+    for (int gi = 0; gi < NG; ++gi) {
+      f32x4 acc = {0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int ks = 0; ks < 4; ++ks) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a[gi][ks]);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bh[ks], acc, 0, 0, 0);
+        acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bl[ks], acc, 0, 0, 0);
+      }
+      // lane: head h, tokens 4*qd .. +3 of the page, kept if h is in KV head gi's group
+      if (gi == gi_own && h < p.Hq) {
+        float x[4];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) x[i] = acc[i] * p.scale;
+        float* dst = logits + (static_cast<int64_t>(l) * p.Hq + h) * p.N + j0;
+        if (j0 + 3 < p.N) {
+          *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
+        } else {
+          for (int i = 0; i < 4; ++i)
+            if (j0 + i < p.N) dst[i] = x[i];
+        }
+        for (int i = 0; i < 4; ++i) {
+          if (j0 + i >= p.N || !in_history(p, j0 + i)) continue;
+          if (x[i] > m) {
+            s = s * __builtin_amdgcn_exp2f((m - x[i]) * kLog2e) + 1.f;
+            m = x[i];
+          } else {
+            s += __builtin_amdgcn_exp2f((x[i] - m) * kLog2e);
+          }
+        }
+      }
+    }
+  }
+  // combine the lane quarters and the wavefronts that share a head
+  red[wave][lane] = make_float2(m, s);
+  __syncthreads();
+  if (threadIdx.x < 16 * NCB) {
+    const int cbh = threadIdx.x / 16, c = threadIdx.x % 16;
+    const int hh = 16 * cbh + c;
+    float mm = -INFINITY, ss = 0.f;
+    for (int w = cbh * kWavesPerCb; w < (cbh + 1) * kWavesPerCb; ++w)
+      for (int q = 0; q < 4; ++q) {
+        const float2 v = red[w][16 * q + c];
+        if (v.x == -INFINITY) continue;
+        const float mn = fmaxf(mm, v.x);
+        ss = ((mm == -INFINITY) ? 0.f : ss * __builtin_amdgcn_exp2f((mm - mn) * kLog2e)) +
+             v.y * __builtin_amdgcn_exp2f((v.x - mn) * kLog2e);
+        mm = mn;
+      }
+    if (hh < p.Hq) part[(static_cast<int64_t>(l) * p.Hq + hh) * gridDim.x + grp] = make_float2(mm, ss);
+  }
+}
+
+// One wavefront per (layer, head): lanes merge strided partials, then a
+// fixed-order butterfly merges the lanes (deterministic).
+__global__ __launch_bounds__(256) void memory_lse_kernel(MemoryParams p, int n_groups,
+                                                         const float2* __restrict__ part,
+                                                         float* __restrict__ lse) {
+  const int i = (blockIdx.x * blockDim.x + threadIdx.x) / 64;
+  const int lane = threadIdx.x & 63;
+  if (i >= p.L * p.Hq) return;                         // whole wavefronts leave together
+  float m = -INFINITY, s = 0.f;
+  for (int gi = lane; gi < n_groups; gi += 64) {
     const float2 v = part[static_cast<int64_t>(i) * n_groups + gi];
     if (v.x == -INFINITY) continue;
     const float mn = fmaxf(m, v.x);
     s = ((m == -INFINITY) ? 0.f : s * expf(m - mn)) + v.y * expf(v.x - mn);
     m = mn;
   }
-  lse[i] = (m == -INFINITY) ? INFINITY : m + logf(s);   // empty history: every weight is 0
+  for (int o = 32; o > 0; o >>= 1) {
+    const float m2 = __shfl_xor(m, o, 64), s2 = __shfl_xor(s, o, 64);
+    const float mn = fmaxf(m, m2);
+    if (mn != -INFINITY) {
+      s = ((m == -INFINITY) ? 0.f : s * expf(m - mn)) + ((m2 == -INFINITY) ? 0.f : s2 * expf(m2 - mn));
+      m = mn;
+    }
+  }
+  if (lane == 0) lse[i] = (m == -INFINITY) ? INFINITY : m + logf(s);   // empty history: every weight is 0
 }
 
 // per (256 positions, layer): sum over the layer's heads (global) or over each
@@ -222,7 +351,20 @@ hipError_t launch_memory_scores(const MemoryParams& p, int dt, const float* M, c
   float* layer = reinterpret_cast<float*>(base + w.layer);
   const int n_groups = static_cast<int>(ceil_div(ceil_div(p.N, p.page_size), kPagesPerGroup));
   hipError_t e;
-  if (dt == KVSEL_BF16) {
+  const int G = p.Hq / p.Hkv;
+  if (dt == KVSEL_BF16 && p.D == 128 && p.page_size == 16 && p.Hq <= 32 && (G == 4 || G == 8 || G == 16)) {
+    dim3 grid(n_groups, p.L);
+#define KVSEL_MLM(NCB)                                                                     \
+  do {                                                                                     \
+    if (G == 4) memory_logits_mfma_kernel<NCB, 4><<<grid, 256, 0, st>>>(p, M, pool, logits, part); \
+    else if (G == 8) memory_logits_mfma_kernel<NCB, 2><<<grid, 256, 0, st>>>(p, M, pool, logits, part); \
+    else memory_logits_mfma_kernel<NCB, 1><<<grid, 256, 0, st>>>(p, M, pool, logits, part); \
+  } while (0)
+    if (p.Hq <= 16) KVSEL_MLM(1);
+    else KVSEL_MLM(2);
+#undef KVSEL_MLM
+    e = hipGetLastError();
+  } else if (dt == KVSEL_BF16) {
     e = (p.D == 64) ? launch_logits_t<KVSEL_BF16, 64>(p, n_groups, M, pool, logits, part, st)
                     : launch_logits_t<KVSEL_BF16, 128>(p, n_groups, M, pool, logits, part, st);
   } else {
@@ -230,7 +372,7 @@ hipError_t launch_memory_scores(const MemoryParams& p, int dt, const float* M, c
                     : launch_logits_t<KVSEL_F16, 128>(p, n_groups, M, pool, logits, part, st);
   }
   if (e != hipSuccess) return e;
-  memory_lse_kernel<<<static_cast<int>(ceil_div(p.L * p.Hq, 256)), 256, 0, st>>>(p, n_groups, part, lse);
+  memory_lse_kernel<<<static_cast<int>(ceil_div(p.L * p.Hq, 4)), 256, 0, st>>>(p, n_groups, part, lse);
   if ((e = hipGetLastError()) != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(ceil_div(p.N, 256)), p.L);
   float* dst = (p.reduce == KVSEL_REDUCE_GLOBAL) ? layer : out;
