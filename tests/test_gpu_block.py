@@ -19,12 +19,17 @@ from selection_score_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-@pytest.mark.parametrize("S,W,NB,n_begin,n_count", [(2, 16, 3000, 0, 3000), (1, 7, 5000, 1000, 777),
-                                                    (4, 32, 1200, 1100, 100)])
-def test_block_scores_match_oracle(S, W, NB, n_begin, n_count):
+@pytest.mark.parametrize("S,W,NB,n_begin,n_count,D", [
+    (2, 16, 3000, 0, 3000, 128),          # matrix cores
+    (1, 7, 5000, 1000, 777, 128),         # ragged tile inside the index
+    (4, 32, 1200, 1100, 100, 128),
+    (8, 5, 999, 0, 999, 128),             # eight sessions, a partial 16-row MFMA tile
+    (3, 9, 1500, 17, 1001, 64),           # D 64: vector ALUs
+])
+def test_block_scores_match_oracle(S, W, NB, n_begin, n_count, D):
     dev = require_gpu()
     g = torch.Generator(device=dev).manual_seed(NB)
-    L, Hq, Hkv, D = 2, 8, 2, 128
+    L, Hq, Hkv = 2, 8, 2
     q = torch.randn((S, L, Hq, W, D), generator=g, device=dev).to(torch.bfloat16)
     mu = (torch.randn((L, Hkv, NB, D), generator=g, device=dev) * 0.3).to(torch.float16)
     out = torch.empty((S, L * Hkv, n_count), dtype=torch.float32, device=dev)

@@ -19,11 +19,11 @@ from selection_score_amd import workloads as wl
 pytestmark = pytest.mark.gpu
 
 
-def _small_pool(dev, L=2, Hq=8, Hkv=2, D=128, N=1000, ps=16, seed=0):
+def _small_pool(dev, L=2, Hq=8, Hkv=2, D=128, N=1000, ps=16, seed=0, dtype=torch.bfloat16):
     g = torch.Generator(device=dev).manual_seed(seed)
     n_pages = (N + ps - 1) // ps
     P = n_pages + 3
-    k_pool = torch.randn((L, P, ps, Hkv, D), generator=g, device=dev).to(torch.bfloat16)
+    k_pool = torch.randn((L, P, ps, Hkv, D), generator=g, device=dev).to(dtype)
     perm = torch.randperm(P, generator=g, device=dev)[:n_pages].to(torch.int32)
     return k_pool, perm, n_pages
 
@@ -44,11 +44,18 @@ def test_memory_update_matches_oracle(dtype, W):
     np.testing.assert_allclose(np.linalg.norm(f64(m), axis=-1), 1.0, atol=1e-5)
 
 
-@pytest.mark.parametrize("reduce", ["global", "per_unit"])
-def test_memory_scores_match_oracle(reduce):
+@pytest.mark.parametrize("reduce,Hq,Hkv,D,ps,dtype", [
+    ("global", 8, 2, 128, 16, torch.bfloat16),      # matrix cores, GQA 4, one 16-head block
+    ("per_unit", 8, 2, 128, 16, torch.bfloat16),
+    ("global", 32, 4, 128, 16, torch.bfloat16),     # matrix cores, GQA 8, two head blocks
+    ("per_unit", 16, 1, 128, 16, torch.bfloat16),   # matrix cores, GQA 16
+    ("global", 8, 4, 128, 16, torch.bfloat16),      # GQA 2: vector ALUs
+    ("global", 8, 2, 64, 8, torch.float16),         # fp16, D 64, 8-token pages: vector ALUs
+])
+def test_memory_scores_match_oracle(reduce, Hq, Hkv, D, ps, dtype):
     dev = require_gpu()
-    L, Hq, Hkv, D, N, ps = 2, 8, 2, 128, 1000, 16
-    k_pool, perm, n_pages = _small_pool(dev, L, Hq, Hkv, D, N, ps)
+    L, N = 2, 1000
+    k_pool, perm, n_pages = _small_pool(dev, L, Hq, Hkv, D, N, ps, dtype=dtype)
     rng = np.random.default_rng(1)
     mo = osc.memory_update(np.zeros((L, Hq, D)), rng.standard_normal((L, Hq, 3, D)))
     m32 = numerics.round_to_f32(mo)

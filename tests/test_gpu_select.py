@@ -5,7 +5,7 @@ import pytest
 import torch
 
 from oracle import select as osel
-from parity import require_gpu
+from parity import check_selection, require_gpu
 
 import selection_score_amd as kv
 
@@ -47,8 +47,10 @@ def _check(s, kept, mask, nk, k, n_sink, n_recent, alive=None):
 @pytest.mark.parametrize("U,n,k,n_sink,n_recent,ties", [
     (3, 1000, 100, 4, 64, False),        # ragged, several tiles of 64
     (5, 2048, 512, 4, 64, True),         # ties and signed zeros
-    (4, 32768, 8192, 4, 256, False),     # LDS-resident keys at the full per-unit size
-    (2, 40000, 5000, 3, 7, True),        # keys streamed from global memory
+    (4, 32768, 8192, 4, 256, False),     # 32 keys per thread in registers, full per-unit size
+    (2, 40000, 5000, 3, 7, True),        # 64 keys per thread in registers
+    (2, 65536, 20000, 4, 64, True),      # the register path's largest unit
+    (1, 70001, 9000, 2, 9, True),        # beyond the register path: keys streamed from the workspace
     (1, 7, 3, 1, 1, True),
 ])
 def test_select_matches_oracle(U, n, k, n_sink, n_recent, ties):
@@ -127,3 +129,28 @@ def test_select_tiled_equals_untiled(n, tile, k):
         ok, _ = osel.select_topk(s[u], k, 1, 4)
         assert nk[u] == len(ok)
         np.testing.assert_array_equal(kept[u, : len(ok)], ok)
+
+
+@pytest.mark.parametrize("pool,n", [("max", 4099), ("avg", 4097), ("max", 40000)])
+def test_select_pooled_slices(pool, n):
+    """Pooling across the 4096-column slices of the key preparation (halo at
+    both slice edges, ragged last slice), against pool1d + select_topk."""
+    from oracle import numerics
+    from oracle import score as osc
+    dev = require_gpu()
+    rng = np.random.default_rng(7 + n)
+    U, k, n_sink, n_recent = 3, n // 5, 4, 64
+    s = rng.standard_normal((U, n)).astype(np.float32)
+    st = torch.from_numpy(s).to(dev)
+    kept = torch.empty((U, k), dtype=torch.int32, device=dev)
+    kv.select(st, kept, k_total=k, n_sink=n_sink, n_recent=n_recent, pool=pool, pool_k=7)
+    torch.cuda.synchronize()
+    got = kept.cpu().numpy()
+    for u in range(U):
+        # max-pooling is exact in float32; the average may differ from the
+        # float64 mean by rounding, so near-ties follow the shared rule
+        pooled = numerics.round_to_f32(osc.pool1d(s[u].astype(np.float64), pool, 7))
+        verdict = check_selection(got[u], pooled, k, n_sink, n_recent, what="unit %d" % u)
+        if pool == "max":
+            assert verdict == "exact"
+
