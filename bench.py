@@ -420,7 +420,7 @@ class KVMem10M:
     The previous-view lists are inputs, so every step does the same work."""
     stages = ["tiles", "update"]
     kernels = {}
-    launches = {"tiles": 11, "update": 2}
+    launches = {"tiles": 16, "update": 2}
     score_stage = "tiles"
     materialise_stages = ["update"]
     dtype = "bf16"
@@ -472,6 +472,7 @@ class KVMem10M:
         self.nm = torch.empty(SU, dtype=torch.int32, device=dev)
         self.tokens = S * U * NB * bt
         self.ws = None
+        self.sel_ws = None
         self.inc_ws = None
 
     def step(self, ev, stream, it):
@@ -485,9 +486,10 @@ class KVMem10M:
             out = self.tile_out.view(-1)[: SU * n]
             self.ws = kv.score_block(self.qs if b == 0 else None, self.mu, out.view(S, U, n), n_kv_heads=cfg.Hkv,
                                      n_begin=b, n_count=n, qbar=self.qbar, qbar_valid=b > 0, workspace=self.ws)
-            kv.select(out.view(SU, n), self.kept, k_total=k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
-                      n_total=NB, base=b, cand_score=self.cs, cand_idx=self.ci, cand_count=self.cc,
-                      finalize=b + n == NB)
+            self.sel_ws = kv.select(out.view(SU, n), self.kept, k_total=k, n_sink=cfg.n_sink,
+                                    n_recent=cfg.n_recent, n_total=NB, base=b, cand_score=self.cs,
+                                    cand_idx=self.ci, cand_count=self.cc, finalize=b + n == NB,
+                                    workspace=self.sel_ws)
         ev[1].record(stream)
         self.inc_ws = kv.gather_incremental(self.raw_k, self.raw_v, self.kept, self.prev_idx, self.prev_page,
                                             self.pool_k, self.pool_v, self.pt, self.nm, bt=cfg.bt, D=cfg.D,

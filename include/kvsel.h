@@ -180,9 +180,9 @@ kvsel_status kvsel_score(const kvsel_score_args* args, void* workspace,
  * centred 1-D pooling kvsel_score offers (odd pool_k; AVG counts
  * out-of-range terms as zero, MAX takes the in-range maximum), computed on
  * the fly while the keys are formed.
- * Workspace: an untiled call needs kvsel_select_workspace() bytes (16-byte
- * aligned; it holds the pooled ordering key of every position and small
- * per-slice histograms, about 4 bytes per position); tiled calls need none.
+ * Workspace: kvsel_select_workspace() bytes, 16-byte aligned (the ordering
+ * key of every position of the call and small per-slice histograms, about
+ * 4 bytes per position); 0 only when U or n is 0.
  * Errors: KVSEL_E_BUDGET if n_sink + n_recent > k_total and k_total < n_total;
  * KVSEL_E_WORKSPACE if the workspace is missing or too small.
  */

@@ -15,15 +15,15 @@
 // ballot prefix places the selected entries, which therefore come out in
 // ascending index order without a sort.
 //
-// Untiled calls run in two launches.  select_keys_kernel spreads the unit
+// Every call runs in two launches.  select_keys_kernel spreads the unit
 // over many workgroups: it stages a 4096-column slice of the score row (plus
 // the pooling halo) in LDS, writes the pooled key of every column to the
 // workspace and a 256-bin histogram of the keys' top byte per slice.  The
-// per-unit workgroup of select_kernel then sums those histograms (the first
-// radix pass), runs the remaining passes and both sweeps over the keys in
-// the workspace, and needs no large LDS, so every unit is resident at once.
-// Tiled calls (running candidates) keep the keys of a tile in LDS when they
-// fit, else recompute them from the scores.
+// per-unit workgroup then sums those histograms (the first radix pass) and
+// runs the remaining passes and both sweeps: with up to 64 keys per thread
+// held in registers (select_regs_kernel, untiled calls), otherwise reading
+// the workspace (select_kernel; tiled calls stage their running candidates
+// in LDS ahead of the tile's keys).
 #include "common.h"
 
 namespace kvsel {
@@ -204,10 +204,11 @@ __global__ __launch_bounds__(kPrepThreads) void select_keys_kernel(SelectParams 
   __syncthreads();
   uint32_t* kout = keys + static_cast<int64_t>(u) * p.n + j0;
   for (int i = tid; i < jn; i += kPrepThreads) {
-    const int64_t j = j0 + i;                       // untiled: global index = column
+    const int64_t j = j0 + i;                       // column of the tile
+    const int64_t gj = p.base + j;                  // global position
     uint32_t key = 0u;
-    const bool alive = p.slot_map == nullptr || static_cast<int64_t>(p.slot_map[j]) != p.dead_slot;
-    if (j >= sink_end && j < rec_begin && alive) {
+    const bool alive = p.slot_map == nullptr || static_cast<int64_t>(p.slot_map[gj]) != p.dead_slot;
+    if (gj >= sink_end && gj < rec_begin && alive) {
       float v;
       if (p.pool == KVSEL_POOL_MAX) {
         const int lo = static_cast<int>(max(static_cast<int64_t>(0), j - r) - (j0 - r));
@@ -289,12 +290,21 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
   const int64_t M = c.c0 + c.n;
   uint32_t cc = 0;
   if constexpr (MODE == kPrepared) {
-    // the first radix pass: the slices' top-byte histograms, summed in order
+    // the first radix pass: the slices' top-byte histograms summed in order,
+    // plus the running candidates' top bytes
     for (int b = tid; b < 256; b += kThreads) {
       uint32_t t = 0;
       for (int sl = 0; sl < n_slices; ++sl) t += prep_hist[(static_cast<int64_t>(u) * n_slices + sl) * 256 + b];
       sh.hist[b] = t;
       cc += t;
+    }
+    __syncthreads();
+    for (int e = tid; e < c.c0; e += kThreads) {
+      const uint32_t key = ckey[e];
+      if (key != 0u) {
+        atomicAdd(&sh.hist[key >> 24], 1u);
+        ++cc;
+      }
     }
   } else {
     for (int64_t e = tid; e < M; e += kThreads) {
@@ -325,11 +335,28 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
         __syncthreads();
         for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0u;
         __syncthreads();
-        for (int64_t e = tid; e < M; e += kThreads) {
-          int64_t g;
-          const uint32_t key = entry_key(c, e, &g);
-          if (key != 0u && ((key ^ prefix) & hi_mask) == 0u)
-            atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+        if constexpr (MODE == kPrepared) {
+          // candidates from LDS, tile keys from the workspace four at a time
+          for (int e = tid; e < c.c0; e += kThreads) {
+            const uint32_t key = ckey[e];
+            if (key != 0u && ((key ^ prefix) & hi_mask) == 0u) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+          }
+          for (int64_t j0 = tid; j0 < c.n; j0 += 4 * kThreads) {
+            uint32_t kq[4];
+#pragma unroll
+            for (int q = 0; q < 4; ++q) kq[q] = (j0 + q * kThreads < c.n) ? c.tkey[j0 + q * kThreads] : 0u;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+              if (kq[q] != 0u && ((kq[q] ^ prefix) & hi_mask) == 0u)
+                atomicAdd(&sh.hist[(kq[q] >> shift) & 255u], 1u);
+          }
+        } else {
+          for (int64_t e = tid; e < M; e += kThreads) {
+            int64_t g;
+            const uint32_t key = entry_key(c, e, &g);
+            if (key != 0u && ((key ^ prefix) & hi_mask) == 0u)
+              atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+          }
         }
       }
       __syncthreads();
@@ -345,15 +372,22 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
   const int64_t s_beg = min(M, static_cast<int64_t>(wave) * seg);
   const int64_t s_end = min(M, s_beg + seg);
   uint32_t n_eq = 0, n_gt = 0;
-  for (int64_t e0 = s_beg; e0 < s_end; e0 += 64) {
-    const int64_t e = e0 + lane;
-    uint32_t key = 0u;
-    if (e < s_end) {
-      int64_t g;
-      key = entry_key(c, e, &g);
+  for (int64_t e0 = s_beg; e0 < s_end; e0 += 4 * 64) {
+    uint32_t kq[4];
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t e = e0 + 64 * q + lane;
+      kq[q] = 0u;
+      if (e < s_end) {
+        int64_t g;
+        kq[q] = entry_key(c, e, &g);
+      }
     }
-    n_eq += __popcll(__ballot(key != 0u && key == T));
-    n_gt += __popcll(__ballot(key != 0u && key > T));
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      n_eq += __popcll(__ballot(kq[q] != 0u && kq[q] == T));
+      n_gt += __popcll(__ballot(kq[q] != 0u && kq[q] > T));
+    }
   }
   if (lane == 0) {
     sh.wave_eq[wave] = n_eq;
@@ -382,11 +416,21 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
   const int64_t sink_alive = static_cast<int64_t>(fsum);
   const bool untiled_mask = p.finalize && p.keep_mask != nullptr;
   int32_t* kept = p.kept_idx + static_cast<int64_t>(u) * p.k_total;
-  for (int64_t e0 = s_beg; e0 < s_end; e0 += 64) {
-    const int64_t e = e0 + lane;
-    uint32_t key = 0u;
-    int64_t g = -1;
-    if (e < s_end) key = entry_key(c, e, &g);
+  for (int64_t e00 = s_beg; e00 < s_end; e00 += 4 * 64) {
+   uint32_t kq[4];
+   int64_t gq[4];
+#pragma unroll
+   for (int q = 0; q < 4; ++q) {
+     const int64_t e = e00 + 64 * q + lane;
+     kq[q] = 0u;
+     gq[q] = -1;
+     if (e < s_end) kq[q] = entry_key(c, e, &gq[q]);
+   }
+#pragma unroll
+   for (int q = 0; q < 4; ++q) {
+    const int64_t e = e00 + 64 * q + lane;
+    const uint32_t key = kq[q];
+    const int64_t g = gq[q];
     const bool is_eq = key != 0u && key == T;
     const bool is_gt = key != 0u && key > T;
     const uint64_t beq = __ballot(is_eq);
@@ -409,6 +453,7 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
     }
     eq_base += __popcll(beq);
     sel_base += __popcll(bsel);
+   }
   }
 
   if (!p.finalize) {
@@ -595,7 +640,7 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
 }
 
 size_t select_workspace_bytes(const SelectParams& p) {
-  if (p.cand_count != nullptr || p.U == 0 || p.n == 0) return 0;
+  if (p.U == 0 || p.n == 0) return 0;
   const int64_t slices = ceil_div(p.n, kPrepKeys);
   const int64_t key_bytes = (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 256;
   return static_cast<size_t>(key_bytes + static_cast<int64_t>(p.U) * slices * 256 * 4);
@@ -621,6 +666,21 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
     return hipGetLastError();
   }
   const size_t cand_bytes = static_cast<size_t>(p.k_total) * 8;
+  if (p.n > 0) {
+    // tiled, prepared: keys and top-byte histograms of the tile, then the
+    // per-unit merge with the running candidates staged in LDS
+    uint32_t* keys = static_cast<uint32_t*>(ws);
+    const int n_slices = static_cast<int>(ceil_div(p.n, kPrepKeys));
+    uint32_t* hist = keys + (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 64;
+    dim3 grid(n_slices, p.U);
+    select_keys_kernel<<<grid, kPrepThreads, 0, st>>>(p, scores, keys, hist);
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_kernel<kPrepared>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize,
+                                       static_cast<int>(cand_bytes));
+    if (e != hipSuccess) return e;
+    select_kernel<kPrepared><<<p.U, kThreads, cand_bytes, st>>>(p, scores, keys, hist, n_slices);
+    return hipGetLastError();
+  }
   const bool lds_keys = p.n <= kLdsKeysMax && cand_bytes + static_cast<size_t>(p.n) * 4 <= 150 * 1024;
   const size_t shmem = cand_bytes + (lds_keys ? static_cast<size_t>(p.n) * 4 : 0);
   if (lds_keys) {
