@@ -424,20 +424,16 @@ __global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* _
     if (ti_ < n_tiles) {                                                                         \
       const int key0 = key_begin + ti_ * kTileKeys;                                              \
       const uint8_t* buf = kbuf[ti_ & 1];                                                        \
-      f32x16 acc[2][2];                                                                          \
-      for (int rb = 0; rb < 2; ++rb)                                                             \
-        for (int cb = 0; cb < 2; ++cb) acc[rb][cb] = f32x16{};                                   \
-      for (int ks = 0; ks < T::kKSteps; ++ks) {                                                  \
-        const uint4 kf0 = k_frag<D>(buf, 0, ks, lane);                                           \
-        const uint4 kf1 = k_frag<D>(buf, 1, ks, lane);                                           \
-        for (int rb = 0; rb < 2; ++rb) {                                                         \
-          acc[rb][0] = mfma32<DT>(qf[rb][ks], kf0, acc[rb][0]);                                  \
-          acc[rb][1] = mfma32<DT>(qf[rb][ks], kf1, acc[rb][1]);                                  \
-        }                                                                                        \
-      }                                                                                          \
       const bool full = key0 + kTileKeys <= min(first_masked, key_end);                          \
-      float cs[2];                                                                               \
       for (int cb = 0; cb < 2; ++cb) {                                                           \
+        f32x16 acc[2];                                                                           \
+        acc[0] = f32x16{};                                                                       \
+        acc[1] = f32x16{};                                                                       \
+        for (int ks = 0; ks < T::kKSteps; ++ks) {                                                \
+          const uint4 kf = k_frag<D>(buf, cb, ks, lane);                                         \
+          acc[0] = mfma32<DT>(qf[0][ks], kf, acc[0]);                                            \
+          acc[1] = mfma32<DT>(qf[1][ks], kf, acc[1]);                                            \
+        }                                                                                        \
         const int key = key0 + 32 * cb + (lane & 31);                                            \
         const int kk = key < key_end ? key : INT_MAX;                                            \
         float sum = 0.f;                                                                         \
@@ -446,10 +442,10 @@ __global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* _
             for (int g4 = 0; g4 < 4; ++g4) {                                                     \
               const int r0 = 64 * wave + 32 * rb + 8 * g4 + 4 * (lane >> 5);                     \
               const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[r0]);                    \
-              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 0], c1, -l4.x));           \
-              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 1], c1, -l4.y));           \
-              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 2], c1, -l4.z));           \
-              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 3], c1, -l4.w));           \
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][4 * g4 + 0], c1, -l4.x));               \
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][4 * g4 + 1], c1, -l4.y));               \
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][4 * g4 + 2], c1, -l4.z));               \
+              sum += __builtin_amdgcn_exp2f(fmaf(acc[rb][4 * g4 + 3], c1, -l4.w));               \
             }                                                                                    \
         } else {                                                                                 \
           for (int rb = 0; rb < 2; ++rb)                                                         \
@@ -457,10 +453,10 @@ __global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* _
               const int r0 = 64 * wave + 32 * rb + 8 * g4 + 4 * (lane >> 5);                     \
               const float4 l4 = *reinterpret_cast<const float4*>(&lse_s[r0]);                    \
               const int4 m4 = *reinterpret_cast<const int4*>(&lim_s[r0]);                        \
-              const float e0 = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 0], c1, -l4.x)); \
-              const float e1 = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 1], c1, -l4.y)); \
-              const float e2 = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 2], c1, -l4.z)); \
-              const float e3 = __builtin_amdgcn_exp2f(fmaf(acc[rb][cb][4 * g4 + 3], c1, -l4.w)); \
+              const float e0 = __builtin_amdgcn_exp2f(fmaf(acc[rb][4 * g4 + 0], c1, -l4.x));    \
+              const float e1 = __builtin_amdgcn_exp2f(fmaf(acc[rb][4 * g4 + 1], c1, -l4.y));    \
+              const float e2 = __builtin_amdgcn_exp2f(fmaf(acc[rb][4 * g4 + 2], c1, -l4.z));    \
+              const float e3 = __builtin_amdgcn_exp2f(fmaf(acc[rb][4 * g4 + 3], c1, -l4.w));    \
               sum += kk <= m4.x ? e0 : 0.f;                                                      \
               sum += kk <= m4.y ? e1 : 0.f;                                                      \
               sum += kk <= m4.z ? e2 : 0.f;                                                      \
@@ -468,15 +464,11 @@ __global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* _
             }                                                                                    \
         }                                                                                        \
         sum += __shfl_xor(sum, 32, 64);                                                          \
-        cs[cb] = sum;                                                                            \
-      }                                                                                          \
-      if (lane < 32) {                                                                           \
-        red[ti_ & 1][wave][lane] = cs[0];                                                        \
-        red[ti_ & 1][wave][32 + lane] = cs[1];                                                   \
+        if (lane < 32) red[ti_ & 1][wave][32 * cb + lane] = sum;                                 \
       }                                                                                          \
     }                                                                                            \
     deep_store<D>(kbuf[(ti_ + 1) & 1], SET);                                                     \
-    deep_load<D>(kunit, key_begin + min(ti_ + 4, n_tiles - 1) * kTileKeys, N, SET);              \
+    deep_load<D>(kunit, key_begin + min(ti_ + 2 + 1, n_tiles - 1) * kTileKeys, N, SET);       \
     __syncthreads();                                                                             \
     if (ti_ < n_tiles && threadIdx.x < kTileKeys) {                                              \
       outbuf[ti_ * kTileKeys + threadIdx.x] =                                                    \
@@ -486,7 +478,7 @@ __global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* _
   } while (0)
 
 template <int DT, int D>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2, 2)))
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3, 3)))
 void scores_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __restrict__ k,
                         const float* __restrict__ lse, float* __restrict__ out) {
   using T = MfmaTile<D>;
@@ -517,22 +509,19 @@ void scores_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* 
   }
   // the K prefetches are issued after every other load, so waiting for a
   // tile never waits for more than the loads in front of it
-  DeepStage<D> s0, s1, s2;
+  DeepStage<D> s0, s1;
   deep_load<D>(kunit, key_begin, N, s0);
   deep_load<D>(kunit, key_begin + min(1, n_tiles - 1) * kTileKeys, N, s1);
-  deep_load<D>(kunit, key_begin + min(2, n_tiles - 1) * kTileKeys, N, s2);
   float factor = 1.f;
   if (p.head_agg == KVSEL_AGG_MEAN) factor /= static_cast<float>(p.G);
   if (p.row_agg == KVSEL_AGG_MEAN) factor /= static_cast<float>(p.W);
   const int first_masked = p.causal ? N - p.W + 1 : N;   // keys >= this need a per-row check
   deep_store<D>(kbuf[0], s0);
-  deep_load<D>(kunit, key_begin + min(3, n_tiles - 1) * kTileKeys, N, s0);
+  deep_load<D>(kunit, key_begin + min(2, n_tiles - 1) * kTileKeys, N, s0);
   __syncthreads();
-  // tile t waits in set t % 3
-  for (int ti = 0; ti < n_tiles; ti += 3) {
+  for (int ti = 0; ti < n_tiles; ti += 2) {
     KVSEL_SC_TILE(ti, s1);
-    KVSEL_SC_TILE(ti + 1, s2);
-    KVSEL_SC_TILE(ti + 2, s0);
+    KVSEL_SC_TILE(ti + 1, s0);
   }
   __syncthreads();
   for (int i = threadIdx.x; i < key_end - key_begin; i += 256)
