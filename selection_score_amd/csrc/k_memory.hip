@@ -202,8 +202,11 @@ __global__ __launch_bounds__(256) void memory_logits_mfma_kernel(MemoryParams p,
   const int64_t lp_end = min(n_lpages, lp_begin + kPagesPerGroup);
   const int64_t page_bytes = static_cast<int64_t>(PS) * p.Hkv * D * 2;
   const uint8_t* lpool = static_cast<const uint8_t*>(pool) + static_cast<int64_t>(l) * p.pool_pages * page_bytes;
+  // the page table entry of the next page is read one page ahead
+  int64_t pp_next = (lp_begin + wsub < lp_end) ? p.page_table[lp_begin + wsub] : -1;
   for (int64_t lp = lp_begin + wsub; lp < lp_end; lp += kWavesPerCb) {
-    const int64_t pp = p.page_table[lp];
+    const int64_t pp = pp_next;
+    if (lp + kWavesPerCb < lp_end) pp_next = p.page_table[lp + kWavesPerCb];
     const bool ok = pp >= 0 && pp < p.pool_pages;
     const uint8_t* base = lpool + (ok ? pp : 0) * page_bytes + (static_cast<int64_t>(col) * p.Hkv) * D * 2 + 16 * qd;
     uint4 a[NG][4];
@@ -217,6 +220,25 @@ __global__ __launch_bounds__(256) void memory_logits_mfma_kernel(MemoryParams p,
                         : make_uint4(0, 0, 0, 0);
     }
     const int64_t j0 = lp * PS + 4 * qd;
+    // history membership of this lane's four tokens, loaded with the page
+    bool hist[4];
+    {
+      int32_t sm[4] = {0, 0, 0, 0};
+      if (p.slot_map != nullptr) {
+        if (j0 + 3 < p.N && (reinterpret_cast<uintptr_t>(p.slot_map) & 15) == 0) {
+          const int4 v = *reinterpret_cast<const int4*>(p.slot_map + j0);
+          sm[0] = v.x; sm[1] = v.y; sm[2] = v.z; sm[3] = v.w;
+        } else {
+          for (int i = 0; i < 4; ++i) sm[i] = (j0 + i < p.N) ? p.slot_map[j0 + i] : 0;
+        }
+      }
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        const int64_t j = j0 + i;
+        hist[i] = j < p.N && j >= p.n_sink && j < p.N - p.n_recent &&
+                  (p.slot_map == nullptr || static_cast<int64_t>(sm[i]) != p.dead_slot);
+      }
+    }
 #pragma unroll
     for (int gi = 0; gi < NG; ++gi) {
       f32x4 acc = {0.f, 0.f, 0.f, 0.f};
@@ -239,7 +261,7 @@ __global__ __launch_bounds__(256) void memory_logits_mfma_kernel(MemoryParams p,
             if (j0 + i < p.N) dst[i] = x[i];
         }
         for (int i = 0; i < 4; ++i) {
-          if (j0 + i >= p.N || !in_history(p, j0 + i)) continue;
+          if (!hist[i]) continue;
           if (x[i] > m) {
             s = s * __builtin_amdgcn_exp2f((m - x[i]) * kLog2e) + 1.f;
             m = x[i];
@@ -308,9 +330,10 @@ __global__ __launch_bounds__(256) void memory_rule_kernel(MemoryParams p, const 
   const bool hist = in_history(p, j);
   const int G = p.Hq / p.Hkv;
   float acc = 0.f;
+#pragma unroll 8
   for (int h = 0; h < p.Hq; ++h) {
     const float x = logits[(static_cast<int64_t>(l) * p.Hq + h) * p.N + j];
-    acc += hist ? expf(x - lse[l * p.Hq + h]) : 0.f;
+    acc += hist ? __builtin_amdgcn_exp2f((x - lse[l * p.Hq + h]) * kLog2e) : 0.f;
     if (p.reduce == KVSEL_REDUCE_PER_UNIT && (h % G) == G - 1) {
       dst[(static_cast<int64_t>(l) * p.Hkv + h / G) * p.N + j] = acc;
       acc = 0.f;
