@@ -72,6 +72,15 @@ __device__ __forceinline__ float key_score(uint32_t k) {
 
 __host__ __device__ inline int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
 
+// 16-byte store marked non-temporal (global_store_dwordx4 ... nt): for outputs
+// that the same launch never reads back, such as gathered or re-rotated K/V
+// rows.  Streaming them past the caches keeps the write path at copy speed.
+typedef unsigned int stream_u32x4 __attribute__((ext_vector_type(4)));
+__device__ __forceinline__ void store16_stream(void* dst, const uint4& v) {
+  __builtin_nontemporal_store(stream_u32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<stream_u32x4*>(dst));
+}
+
+
 // ---------------------------------------------------------------- launchers
 // Each returns the status of the launch (hipGetLastError after enqueueing).
 

@@ -153,6 +153,7 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
   const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
   const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
   float* out_s = out + (static_cast<int64_t>(col) * U + u) * p.n_count;
+  const bool vec_out = (reinterpret_cast<uintptr_t>(out_s) & 15) == 0;
   for (int64_t tile = wave; tile < n_tiles; tile += n_waves) {
     const int64_t r = tile * 16 + col;           // A row of this lane
     uint4 a[4];
@@ -172,10 +173,15 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
     }
     // lane holds session `col`, index rows tile*16 + 4*quarter + i
     if (live) {
+      const int64_t rr0 = tile * 16 + 4 * quarter;
+      if (vec_out && rr0 + 3 < p.n_count) {
+        // four consecutive scores in one non-temporal 16-byte store
+        __builtin_nontemporal_store(f32x4{acc[0] * up, acc[1] * up, acc[2] * up, acc[3] * up},
+                                    reinterpret_cast<f32x4*>(out_s + rr0));
+      } else {
 #pragma unroll
-      for (int i = 0; i < 4; ++i) {
-        const int64_t rr = tile * 16 + 4 * quarter + i;
-        if (rr < p.n_count) out_s[rr] = acc[i] * up;
+        for (int i = 0; i < 4; ++i)
+          if (rr0 + i < p.n_count) out_s[rr0 + i] = acc[i] * up;
       }
     }
   }

@@ -95,8 +95,8 @@ __global__ __launch_bounds__(256) void gather_rows_kernel(GatherParams p, RopeTa
     if (active) {
       const int64_t doff = ((static_cast<int64_t>(u) * rows_per_unit + i * p.bt + o) * p.D) * esz +
                            static_cast<int64_t>(d0) * esz;
-      *reinterpret_cast<uint4*>(static_cast<uint8_t*>(dst_k) + doff) = kv;
-      *reinterpret_cast<uint4*>(static_cast<uint8_t*>(dst_v) + doff) = vv;
+      store16_stream(static_cast<uint8_t*>(dst_k) + doff, kv);
+      store16_stream(static_cast<uint8_t*>(dst_v) + doff, vv);
     }
   }
 }
@@ -185,7 +185,7 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
         const int o = (q0 + j) * rows_per_pass + rsub;
         if (q0 + j < passes && o < p.bt) {
           const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-          *reinterpret_cast<uint4*>(dv + off) = vv[j];
+          store16_stream(dv + off, vv[j]);
         }
       }
 #pragma unroll
@@ -213,7 +213,7 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
             }
           }
           const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-          *reinterpret_cast<uint4*>(dk + off) = rotate16<DT, kInter>(kv[j], other, sgn, cs, sn);
+          store16_stream(dk + off, rotate16<DT, kInter>(kv[j], other, sgn, cs, sn));
         }
       }
     }

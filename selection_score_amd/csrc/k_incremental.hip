@@ -238,7 +238,7 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
           const int o = (q0 + j) * rows_per_pass + rsub;
           if (q0 + j < passes && o < p.bt) {
             const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-            *reinterpret_cast<uint4*>(pv + off) = vv[j];
+            store16_stream(pv + off, vv[j]);
           }
         }
       }
@@ -271,7 +271,7 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
         }
         if (o < p.bt) {
           const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-          *reinterpret_cast<uint4*>(pk + off) = out;
+          store16_stream(pk + off, out);
         }
       }
     }
