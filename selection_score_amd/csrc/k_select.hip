@@ -15,15 +15,17 @@
 // ballot prefix places the selected entries, which therefore come out in
 // ascending index order without a sort.
 //
-// Every call runs in two launches.  select_keys_kernel spreads the unit
-// over many workgroups: it stages a 4096-column slice of the score row (plus
-// the pooling halo) in LDS, writes the pooled key of every column to the
+// Most calls run in two launches.  select_keys_kernel spreads the unit over
+// many workgroups: it stages a 4096-column slice of the score row (plus the
+// pooling halo) in LDS, writes the pooled key of every column to the
 // workspace and a 256-bin histogram of the keys' top byte per slice.  The
 // per-unit workgroup then sums those histograms (the first radix pass) and
 // runs the remaining passes and both sweeps: with up to 64 keys per thread
 // held in registers (select_regs_kernel, untiled calls), otherwise reading
 // the workspace (select_kernel; tiled calls stage their running candidates
-// in LDS ahead of the tile's keys).
+// in LDS ahead of the tile's keys).  Unpooled untiled calls with at least
+// 128 units of up to 32768 columns skip the first launch: each unit's
+// workgroup reads its scores and makes its keys itself.
 #include "common.h"
 
 namespace kvsel {
@@ -138,6 +140,7 @@ __device__ uint3 block_sum3(uint32_t a, uint32_t b, uint32_t c, uint32_t* scratc
 }
 
 constexpr int kPrepKeys = 4096;       // columns per select_keys_kernel workgroup
+constexpr int kFusedMinUnits = 128;   // unpooled untiled calls with this many units make their own keys
 constexpr int kPrepThreads = 256;
 constexpr int kMaxPoolR = 127;        // pool_k <= 255
 
@@ -486,12 +489,16 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
   if (tid == 0 && p.n_kept != nullptr) p.n_kept[u] = static_cast<int32_t>(total);
 }
 
-// Per-unit selection over prepared keys held in registers.  Wavefront w owns
-// the contiguous segment [w*seg, (w+1)*seg) of the unit in rows of 64
-// columns (KPT rows), so the ballot sweeps see columns in ascending order.
-// Requires n <= KPT * kThreads.
-template <int KPT>
-__global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, const uint32_t* keys,
+// Per-unit selection over keys held in registers.  Wavefront w owns the
+// contiguous segment [w*seg, (w+1)*seg) of the unit in rows of 64 columns
+// (KPT rows), so the ballot sweeps see columns in ascending order.  Requires
+// n <= KPT * kThreads.  With kFused (unpooled calls) the keys are made here
+// from the score row and the first radix pass runs here too; otherwise they
+// come prepared, with the slices' top-byte histograms, from
+// select_keys_kernel.
+template <int KPT, bool kFused>
+__global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, const float* scores,
+                                                               const uint32_t* keys,
                                                                const uint32_t* hist, int n_slices) {
   __shared__ SelShared sh;
   const int u = blockIdx.x;
@@ -503,31 +510,53 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
     return p.slot_map == nullptr || static_cast<int64_t>(p.slot_map[g]) != p.dead_slot;
   };
 
-  // ---- alive forced positions, summed top-byte histogram, candidate count
+  // ---- alive forced positions, top-byte histogram, candidate count
   uint32_t fs = 0, fr = 0, cc = 0;
   for (int g = tid; g < sink_end; g += kThreads) fs += alive(g) ? 1u : 0u;
   for (int g = rec_begin + tid; g < n; g += kThreads) fr += alive(g) ? 1u : 0u;
-  for (int b = tid; b < 256; b += kThreads) {
-    uint32_t t = 0;
-    for (int sl = 0; sl < n_slices; ++sl) t += hist[(static_cast<int64_t>(u) * n_slices + sl) * 256 + b];
-    sh.hist[b] = t;
-    cc += t;
+  const int seg = ((n + kWaves - 1) / kWaves + 63) / 64 * 64;
+  const int s_beg = min(n, wave * seg);
+  const int s_end = min(n, s_beg + seg);
+  uint32_t kr[KPT];
+  if constexpr (!kFused) {
+    for (int b = tid; b < 256; b += kThreads) {
+      uint32_t t = 0;
+      for (int sl = 0; sl < n_slices; ++sl) t += hist[(static_cast<int64_t>(u) * n_slices + sl) * 256 + b];
+      sh.hist[b] = t;
+      cc += t;
+    }
+    // this wavefront's keys (0 past the segment)
+    const uint32_t* ku = keys + static_cast<int64_t>(u) * n;
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = s_beg + 64 * i + lane;
+      kr[i] = (e < s_end) ? ku[e] : 0u;
+    }
+  } else {
+    for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0u;
+    const float* row = scores + static_cast<int64_t>(u) * p.row_stride;
+    float v[KPT];
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = s_beg + 64 * i + lane;
+      v[i] = (e < s_end) ? row[e] : 0.f;
+    }
+    __syncthreads();                                // histogram cleared
+#pragma unroll
+    for (int i = 0; i < KPT; ++i) {
+      const int e = s_beg + 64 * i + lane;
+      uint32_t key = 0u;
+      if (e < s_end && e >= sink_end && e < rec_begin && alive(e)) {
+        key = score_key(v[i]);
+        atomicAdd(&sh.hist[key >> 24], 1u);
+        ++cc;
+      }
+      kr[i] = key;
+    }
   }
   const uint3 sums = block_sum3(fs, fr, cc, sh.wave_sums);
   const uint32_t fsum = sums.x, rsum = sums.y, n_cand = sums.z;
   const int32_t room = p.k_total - static_cast<int32_t>(fsum + rsum);
-
-  // ---- this wavefront's keys (0 past the segment)
-  const int seg = ((n + kWaves - 1) / kWaves + 63) / 64 * 64;
-  const int s_beg = min(n, wave * seg);
-  const int s_end = min(n, s_beg + seg);
-  const uint32_t* ku = keys + static_cast<int64_t>(u) * n;
-  uint32_t kr[KPT];
-#pragma unroll
-  for (int i = 0; i < KPT; ++i) {
-    const int e = s_beg + 64 * i + lane;
-    kr[i] = (e < s_end) ? ku[e] : 0u;
-  }
 
   // ---- radix select of the room-th largest key (top byte already counted)
   uint32_t T;
@@ -653,14 +682,21 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
     uint32_t* keys = static_cast<uint32_t*>(ws);
     const int n_slices = static_cast<int>(ceil_div(p.n, kPrepKeys));
     uint32_t* hist = keys + (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 64;
+    if (p.n <= 32 * kThreads && p.U >= kFusedMinUnits && (p.pool == KVSEL_POOL_NONE || p.pool_k == 1)) {
+      // enough units to fill the device and no pooling: keys and all radix
+      // passes in the per-unit workgroup (pooled rows keep the two launches,
+      // whose key kernel spreads the window work over many workgroups)
+      select_regs_kernel<32, true><<<p.U, kThreads, 0, st>>>(p, scores, nullptr, nullptr, 0);
+      return hipGetLastError();
+    }
     if (n_slices > 0) {
       dim3 grid(n_slices, p.U);
       select_keys_kernel<<<grid, kPrepThreads, 0, st>>>(p, scores, keys, hist);
     }
     if (p.n <= 32 * kThreads)
-      select_regs_kernel<32><<<p.U, kThreads, 0, st>>>(p, keys, hist, n_slices);
+      select_regs_kernel<32, false><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
     else if (p.n <= 64 * kThreads)
-      select_regs_kernel<64><<<p.U, kThreads, 0, st>>>(p, keys, hist, n_slices);
+      select_regs_kernel<64, false><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
     else
       select_kernel<kPrepared><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
     return hipGetLastError();

@@ -154,3 +154,50 @@ def test_select_pooled_slices(pool, n):
         if pool == "max":
             assert verdict == "exact"
 
+
+
+@pytest.mark.parametrize("U,n,k,pool,pool_k,ties,dead", [
+    (130, 5000, 700, "none", 1, True, False),      # ragged rows, exact ties and signed zeros
+    (128, 32768, 8192, "none", 1, False, True),    # the per-unit maximum with dead positions
+    (129, 4099, 800, "max", 7, False, False),      # max-pool halo at every wavefront segment edge
+    (130, 3001, 500, "avg", 5, False, True),
+    (128, 2000, 300, "max", 1, True, False),       # a window of one
+    (128, 6000, 900, "avg", 255, False, False),    # the widest window
+])
+def test_select_many_units(U, n, k, pool, pool_k, ties, dead):
+    """Many units: unpooled rows (and windows of one) take the single-launch
+    path where each unit's workgroup makes its own keys; pooled rows keep the
+    two launches.  Against pool1d + select_topk."""
+    from oracle import numerics
+    from oracle import score as osc
+    dev = require_gpu()
+    rng = np.random.default_rng(U * 7 + n)
+    n_sink, n_recent = 4, 64
+    s = _scores(rng, U, n, ties)
+    slot_map, alive, dead_slot = None, None, n
+    if dead:
+        slot_map = np.arange(n, dtype=np.int64)
+        slot_map[rng.choice(n, n // 10, replace=False)] = dead_slot
+        slot_map[[1, n - 2]] = dead_slot                 # dead inside the forced set too
+        alive = slot_map != dead_slot
+    st = torch.from_numpy(s).to(dev)
+    kept = torch.full((U, k), -7, dtype=torch.int32, device=dev)
+    nk = torch.zeros(U, dtype=torch.int32, device=dev)
+    mask = torch.zeros((U, n), dtype=torch.uint8, device=dev)
+    sm = None if slot_map is None else torch.from_numpy(slot_map.astype(np.int32)).to(dev)
+    kv.select(st, kept, k_total=k, n_sink=n_sink, n_recent=n_recent, keep_mask=mask, n_kept=nk,
+              slot_map=sm, dead_slot=dead_slot, pool=pool, pool_k=pool_k)
+    torch.cuda.synchronize()
+    got, nk, mask = kept.cpu().numpy(), nk.cpu().numpy(), mask.cpu().numpy()
+    if pool == "none" or pool_k == 1:
+        _check(s, got, mask, nk, k, n_sink, n_recent, alive)
+        return
+    pooled = numerics.round_to_f32(osc.pool1d(s.astype(np.float64), pool, pool_k))
+    for u in range(U):
+        verdict = check_selection(got[u], pooled[u], k, n_sink, n_recent, alive, what="unit %d" % u)
+        if pool == "max":
+            assert verdict == "exact"
+        ok, om = osel.select_topk(pooled[u].astype(np.float64), k, n_sink, n_recent, alive)
+        assert nk[u] == len(ok)
+        assert mask[u].sum() == len(ok)
+        np.testing.assert_array_equal(np.flatnonzero(mask[u]), np.sort(got[u][got[u] >= 0]))
