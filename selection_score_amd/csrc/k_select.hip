@@ -20,7 +20,7 @@
 // pooling halo) in LDS, writes the pooled key of every column to the
 // workspace and a 256-bin histogram of the keys' top byte per slice.  The
 // per-unit workgroup then sums those histograms (the first radix pass) and
-// runs the remaining passes and both sweeps: with up to 64 keys per thread
+// runs the remaining passes and both sweeps: with up to 32 keys per thread
 // held in registers (select_regs_kernel, untiled calls), otherwise reading
 // the workspace (select_kernel; tiled calls stage their running candidates
 // in LDS ahead of the tile's keys).  Unpooled untiled calls with at least
@@ -693,10 +693,10 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
       dim3 grid(n_slices, p.U);
       select_keys_kernel<<<grid, kPrepThreads, 0, st>>>(p, scores, keys, hist);
     }
+    // up to 32 keys per thread stay in registers; larger units stream their
+    // keys from the workspace (64 per thread no longer fit without spilling)
     if (p.n <= 32 * kThreads)
       select_regs_kernel<32, false><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
-    else if (p.n <= 64 * kThreads)
-      select_regs_kernel<64, false><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
     else
       select_kernel<kPrepared><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
     return hipGetLastError();

@@ -48,9 +48,9 @@ def _check(s, kept, mask, nk, k, n_sink, n_recent, alive=None):
     (3, 1000, 100, 4, 64, False),        # ragged, several tiles of 64
     (5, 2048, 512, 4, 64, True),         # ties and signed zeros
     (4, 32768, 8192, 4, 256, False),     # 32 keys per thread in registers, full per-unit size
-    (2, 40000, 5000, 3, 7, True),        # 64 keys per thread in registers
-    (2, 65536, 20000, 4, 64, True),      # the register path's largest unit
-    (1, 70001, 9000, 2, 9, True),        # beyond the register path: keys streamed from the workspace
+    (2, 40000, 5000, 3, 7, True),        # beyond 32 keys per thread: keys streamed from the workspace
+    (2, 65536, 20000, 4, 64, True),      # the session-memory unit size
+    (1, 70001, 9000, 2, 9, True),        # a ragged last slice
     (1, 7, 3, 1, 1, True),
 ])
 def test_select_matches_oracle(U, n, k, n_sink, n_recent, ties):
