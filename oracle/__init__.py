@@ -44,6 +44,8 @@ PIN_STATUS = {
     "score.memory_update": "pinned (EMA closed forms, unit norm, fixed point)",
     "score.memory_scores": "pinned (cross-formulation with window_scores at W=1; sum = L*Hq)",
     "score.query_reduce / block_scores": "pinned (per-query brute force by linearity; hand example)",
+    "score.mean_k_index": "pinned (hand-computed means over two blocks, fp16 RNE halfway cases, "
+                          "constant blocks, linearity of the block score)",
     "score.residual_score": "pinned (zero-initialised fc2 gives the rule score exactly)",
     "select.select_topk": "pinned (exhaustive max-sum brute force on tiny inputs; invariants)",
     "select.select_topk_tiled": "pinned (equal to select_topk for every tile size)",

@@ -9,8 +9,11 @@ Layouts (row-major, last index fastest):
   query memory     M      [L][Hq][D]
   block queries    q      [S][L][Hq][Wq][D] (pre-RoPE)
   Mean-K index     mu     [L][Hkv][NB][D]
+  raw keys         raw_k  [..., NB*bt, D]   (pre-RoPE, bt-token blocks)
 """
 import numpy as np
+
+from . import numerics
 
 
 def gqa_group(h, n_q_heads, n_kv_heads):
@@ -217,6 +220,23 @@ def block_scores(qbar, mu, scale=None):
     if scale is None:
         scale = 1.0 / np.sqrt(D)
     return np.einsum("slgd,lgbd->slgb", qbar, mu) * scale
+
+
+def mean_k_index(raw_k, bt=32):
+    """Mean-K index: mu[..., b, :] = (1/bt) * sum of the bt raw key rows of
+    block b, rounded once (round-to-nearest-even) to float16.
+
+    KVMem (query-conditioned retrieval paragraph): every (layer, KV head)
+    keeps one RoPE-stripped mean key per 32-token block, stored in HBM as an
+    fp16 index that grows as blocks fill.  raw_k: [..., N, D] with N >= 0;
+    only the floor(N / bt) complete blocks are indexed.  Returns
+    [..., N // bt, D] as float64 values representable in float16.
+    """
+    raw = np.asarray(raw_k, dtype=np.float64)
+    *lead, n, d = raw.shape
+    nb = n // bt
+    blocks = raw[..., : nb * bt, :].reshape(*lead, nb, bt, d)
+    return numerics.round_to_f16(blocks.sum(axis=-2) / bt)
 
 
 def residual_score(rule, features, fc1_w, fc1_b, fc2_w, fc2_b, alpha=1.0):

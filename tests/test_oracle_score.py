@@ -278,3 +278,47 @@ def test_block_score_hand_example():
     got = score.block_scores(score.query_reduce(q, 1), mu)[0, 0, 0]
     # q-bar = (2, 1, 2, -1); / sqrt(4) = 2
     np.testing.assert_allclose(got, [4.0 / 2, -4.0 / 2], atol=0)
+
+
+# ---------------------------------------------------------------- Mean-K index
+
+def test_mean_k_hand_example_two_blocks():
+    # bt = 4, D = 2: block 0 rows (1,2),(3,4),(5,6),(7,8) -> (4,5);
+    # block 1 rows (0,-1),(0,-1),(2,1),(2,-3) -> (1,-1); a trailing partial row is ignored
+    raw = np.array([[1, 2], [3, 4], [5, 6], [7, 8],
+                    [0, -1], [0, -1], [2, 1], [2, -3],
+                    [100, 100]], dtype=np.float64)
+    mu = score.mean_k_index(raw, bt=4)
+    assert mu.shape == (2, 2)
+    np.testing.assert_array_equal(mu, [[4.0, 5.0], [1.0, -1.0]])
+
+
+def test_mean_k_rounds_once_to_float16_nearest_even():
+    # half spacing at 1.0 is 2^-10.  Means exactly between two halves go to the
+    # even one; the fp16 value of 0.1 is 0x2E66 = 0.0999755859375.
+    u = 2.0 ** -10
+    raw = np.array([[1.0], [1.0 + u],              # mean 1 + u/2 -> 1.0 (even)
+                    [1.0 + u], [1.0 + 2 * u],      # mean 1 + 3u/2 -> 1 + 2u (even)
+                    [0.1], [0.1],                  # constant block
+                    [70000.0], [70000.0]])         # beyond the half range -> inf
+    mu = score.mean_k_index(raw, bt=2)[:, 0]
+    assert mu[0] == 1.0 and mu[1] == 1.0 + 2 * u
+    assert mu[2] == 0.0999755859375
+    assert np.isinf(mu[3]) and mu[3] > 0
+    # below the halfway point of the subnormal spacing 2^-24 the mean flushes to zero
+    tiny = score.mean_k_index(np.array([[2.0 ** -26], [2.0 ** -26]]), bt=2)
+    assert tiny[0, 0] == 0.0
+
+
+def test_mean_k_block_score_equals_mean_of_token_scores():
+    # linearity: scoring the mean key of a block is scoring each of its tokens
+    # and averaging; raw values on a 2^-4 grid keep every mean exact in fp16
+    r = _rng(21)
+    L, Hkv, NB, bt, D = 1, 2, 3, 32, 8
+    raw = r.integers(-64, 64, size=(L, Hkv, NB * bt, D)) / 16.0
+    mu = score.mean_k_index(raw, bt=bt)
+    np.testing.assert_array_equal(mu, raw.reshape(L, Hkv, NB, bt, D).mean(axis=3))
+    qbar = r.standard_normal((1, L, Hkv, D))
+    got = score.block_scores(qbar, mu)
+    tok = np.einsum("slgd,lgnd->slgn", qbar, raw).reshape(1, L, Hkv, NB, bt).mean(axis=-1) / math.sqrt(D)
+    np.testing.assert_allclose(got, tok, rtol=1e-12, atol=1e-12)
