@@ -303,6 +303,43 @@ typedef struct kvsel_redirect_args {
 
 kvsel_status kvsel_redirect(const kvsel_redirect_args* args, void* stream);
 
+/* ------------------------------------------------------------------ index
+ *
+ * KVMem (query-conditioned retrieval paragraph): the block scorer reads one
+ * RoPE-stripped mean key per (layer, KV head, bt-token block), kept in HBM as
+ * an fp16 index that grows as blocks fill.  kvsel_build_index writes
+ *   mu[u][b][:] = fp16_rne( (1/bt) * sum over the bt raw rows of block b )
+ * for blocks b in [b_begin, b_begin + b_count) of every unit u.  The sum is
+ * taken in float64 and rounded once to fp16 (round to nearest even), so the
+ * index is bit-exact whenever the float64 sum of a block is exact (any block
+ * whose raw values span fewer than 2^45 in magnitude).
+ *
+ *   src_k       raw (pre-RoPE) keys of unit u at src_k + offset(u) elements,
+ *               rows [src_rows][D] of `dtype` (BF16, F16 or F32);
+ *               offset(u) = src_offsets[u] (device int64 [U]) if given, else
+ *               u * src_unit_stride (units may alias one buffer)
+ *   mu          out: F16 [U][NB][D]; only the requested blocks are written
+ *   D           64 or 128; bt in [1, 256]; 0 <= b_begin, b_count >= 0,
+ *               b_begin + b_count <= NB and (b_begin + b_count) * bt <= src_rows
+ * Errors: E_ARG (NULL pointers, ranges, alignment of src_k/mu to 16 bytes,
+ * bad dtype), E_UNSUPPORTED (D), E_DEVICE.  b_count = 0 or U = 0 is a no-op.
+ */
+typedef struct kvsel_index_args {
+  uint32_t struct_size;
+  int32_t U, D;
+  int32_t dtype;              /* kvsel_dtype of the raw keys */
+  int32_t bt;                 /* rows per block (32 in KVMem) */
+  const void* src_k;
+  const int64_t* src_offsets; /* device [U] element offsets, or NULL */
+  int64_t src_unit_stride;    /* elements, used when src_offsets is NULL */
+  int64_t src_rows;           /* rows available per unit */
+  int64_t NB;                 /* blocks per unit in mu */
+  int64_t b_begin, b_count;   /* block range to (re)build */
+  uint16_t* mu;               /* out: fp16 bit patterns [U][NB][D] */
+} kvsel_index_args;
+
+kvsel_status kvsel_build_index(const kvsel_index_args* args, void* stream);
+
 /* ------------------------------------------------------------------ memory
  *
  * IntentKV §4 (memory recurrence) and §7 (unit-norm projection): one turn

@@ -79,9 +79,17 @@ class MemUpdArgs(ctypes.Structure):
     ]
 
 
+class IndexArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("U", c_i32), ("D", c_i32), ("dtype", c_i32), ("bt", c_i32),
+        ("src_k", c_vp), ("src_offsets", c_vp), ("src_unit_stride", c_i64), ("src_rows", c_i64),
+        ("NB", c_i64), ("b_begin", c_i64), ("b_count", c_i64), ("mu", c_vp),
+    ]
+
+
 EXPORTS = ["kvsel_version", "kvsel_last_error", "kvsel_score_workspace", "kvsel_score",
            "kvsel_select_workspace", "kvsel_select", "kvsel_gather_workspace", "kvsel_gather_rerope",
-           "kvsel_redirect", "kvsel_memory_update"]
+           "kvsel_redirect", "kvsel_memory_update", "kvsel_build_index"]
 
 _lib = None
 
@@ -108,6 +116,7 @@ def load(path=LIB_PATH):
     lib.kvsel_gather_rerope.argtypes = [P(GatherArgs), c_vp, ctypes.c_size_t, c_vp]
     lib.kvsel_redirect.argtypes = [P(RedirectArgs), c_vp]
     lib.kvsel_memory_update.argtypes = [P(MemUpdArgs), c_vp]
+    lib.kvsel_build_index.argtypes = [P(IndexArgs), c_vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = c_i32
     _lib = lib

@@ -455,6 +455,37 @@ kvsel_status kvsel_redirect(const kvsel_redirect_args* a, void* stream) {
 
 // ------------------------------------------------------------------ memory
 
+kvsel_status kvsel_build_index(const kvsel_index_args* a, void* stream) {
+  try {
+    if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+    if (a->struct_size < sizeof(kvsel_index_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+    if (a->U < 0) return fail(KVSEL_E_ARG, "U must be >= 0");
+    if (!valid_dtype(a->dtype)) return fail(KVSEL_E_ARG, "bad dtype");
+    if (a->D != 64 && a->D != 128) return fail(KVSEL_E_UNSUPPORTED, "D must be 64 or 128");
+    if (a->bt < 1 || a->bt > 256) return fail(KVSEL_E_ARG, "bt must be in [1, 256]");
+    if (a->NB < 0 || a->b_begin < 0 || a->b_count < 0 || a->b_begin + a->b_count > a->NB)
+      return fail(KVSEL_E_ARG, "need 0 <= b_begin, 0 <= b_count, b_begin + b_count <= NB");
+    if ((a->b_begin + a->b_count) * a->bt > a->src_rows)
+      return fail(KVSEL_E_ARG, "the block range reaches past src_rows");
+    if (a->U == 0 || a->b_count == 0) return KVSEL_OK;
+    if (a->src_k == nullptr || a->mu == nullptr) return fail(KVSEL_E_ARG, "src_k or mu is NULL");
+    const int esz = (a->dtype == KVSEL_F32) ? 4 : 2;
+    if (!aligned16(a->src_k) || !aligned16(a->mu)) return fail(KVSEL_E_ARG, "src_k and mu must be 16-byte aligned");
+    if (a->src_offsets == nullptr && (a->src_unit_stride < 0 || (a->src_unit_stride * esz) % 16 != 0))
+      return fail(KVSEL_E_ARG, "src_unit_stride must be >= 0 and keep units 16-byte aligned");
+    kvsel_status s = check_device();
+    if (s != KVSEL_OK) return s;
+    IndexParams p;
+    p.U = a->U; p.D = a->D; p.bt = a->bt; p.dtype = a->dtype;
+    p.src_unit_stride = a->src_unit_stride; p.src_rows = a->src_rows; p.NB = a->NB;
+    p.b_begin = a->b_begin; p.b_count = a->b_count; p.src_offsets = a->src_offsets;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish(launch_build_index(p, a->src_k, a->mu, st), st, "index build");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
 kvsel_status kvsel_memory_update(const kvsel_memupd_args* a, void* stream) {
   try {
     if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");

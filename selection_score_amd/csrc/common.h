@@ -168,6 +168,13 @@ hipError_t launch_gather_incremental(const GatherParams& p, const RopeTable& rt,
                                      int32_t* page_table, int32_t* n_miss, void* ws,
                                      hipStream_t st);
 
+struct IndexParams {
+  int U, D, bt, dtype;
+  int64_t src_unit_stride, src_rows, NB, b_begin, b_count;
+  const int64_t* src_offsets;
+};
+hipError_t launch_build_index(const IndexParams& p, const void* src_k, uint16_t* mu, hipStream_t st);
+
 hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, int64_t dead,
                            hipStream_t st);
 hipError_t launch_sentinel(void* k_pool, void* v_pool, int L, int Hkv, int D, int dtype,

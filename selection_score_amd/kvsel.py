@@ -258,3 +258,22 @@ def memory_update(q_turn, m, *, decay=0.9, stream=None):
     a.q_turn, a.M, a.decay = _ptr(q_turn), _ptr(m), decay
     lib = _abi.load()
     _check(lib.kvsel_memory_update(ctypes.byref(a), _stream(stream)))
+
+
+def build_index(raw_k, mu, *, bt, D, src_rows, NB=None, b_begin=0, b_count=None, src_offsets=None,
+                src_unit_stride=0, stream=None):
+    """kvsel_build_index.  raw_k: the raw-key store (any shape; unit u starts
+    at element src_offsets[u], or u * src_unit_stride); mu: float16 [U][NB][D],
+    written for blocks [b_begin, b_begin + b_count) of every unit."""
+    if mu.dtype != torch.float16:
+        raise TypeError("mu must be float16")
+    U = mu.shape[0]
+    NB = mu.shape[1] if NB is None else NB
+    b_count = NB - b_begin if b_count is None else b_count
+    a = _abi.IndexArgs()
+    a.struct_size = ctypes.sizeof(_abi.IndexArgs)
+    a.U, a.D, a.dtype, a.bt = U, D, _dtype(raw_k), bt
+    a.src_k, a.src_offsets, a.src_unit_stride, a.src_rows = _ptr(raw_k), _ptr(src_offsets), src_unit_stride, src_rows
+    a.NB, a.b_begin, a.b_count, a.mu = NB, b_begin, b_count, _ptr(mu)
+    lib = _abi.load()
+    _check(lib.kvsel_build_index(ctypes.byref(a), _stream(stream)))

@@ -36,6 +36,7 @@ STRUCTS = {
     "kvsel_gather_args": _abi.GatherArgs,
     "kvsel_redirect_args": _abi.RedirectArgs,
     "kvsel_memupd_args": _abi.MemUpdArgs,
+    "kvsel_index_args": _abi.IndexArgs,
 }
 
 
@@ -153,3 +154,29 @@ def test_gather_and_redirect_validation_without_device():
     r.k_pool, r.v_pool, r.L, r.Hkv, r.D, r.dtype, r.pool_slots = 0x3000, 0x4000, 1, 1, 128, _abi.F32, 6
     assert lib.kvsel_redirect(ctypes.byref(r), None) == _abi.KVSEL_E_UNSUPPORTED
     assert b"fp8" in lib.kvsel_last_error()
+
+
+def test_index_validation_without_device():
+    lib = _abi.load()
+    a = _abi.IndexArgs()
+    a.struct_size = ctypes.sizeof(a)
+    a.U, a.D, a.dtype, a.bt = 4, 128, _abi.BF16, 32
+    a.src_k, a.mu, a.src_unit_stride, a.src_rows = 0x1000, 0x2000, 32 * 64 * 128, 32 * 64
+    a.NB, a.b_begin, a.b_count = 64, 0, 64
+    call = lambda: lib.kvsel_build_index(ctypes.byref(a), None)
+    a.D = 96
+    assert call() == _abi.KVSEL_E_UNSUPPORTED
+    a.D, a.b_count = 128, 65                      # past NB
+    assert call() == _abi.KVSEL_E_ARG
+    a.NB, a.b_count = 65, 65                      # past src_rows
+    assert call() == _abi.KVSEL_E_ARG and b"src_rows" in lib.kvsel_last_error()
+    a.NB, a.b_count, a.bt = 64, 64, 0
+    assert call() == _abi.KVSEL_E_ARG
+    a.bt, a.mu = 32, 0x2004                       # misaligned output
+    assert call() == _abi.KVSEL_E_ARG
+    a.mu, a.src_unit_stride = 0x2000, 3           # units not 16-byte aligned
+    assert call() == _abi.KVSEL_E_ARG
+    a.src_unit_stride, a.b_count = 0, 0           # nothing to do
+    assert call() == _abi.KVSEL_OK
+    a.struct_size = 8
+    assert call() == _abi.KVSEL_E_ARG
