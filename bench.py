@@ -15,6 +15,11 @@ kernel plus a small combine kernel) and select (a key-preparation kernel
 plus the per-unit selection kernel) is one kernel launch, so its stage time
 is that kernel's launch duration.
 
+--workload picks another workload: intentkv (session memory over a paged pool
+with the dead-slot redirect), kvmem1m (1M-token block retrieval and re-RoPE
+gather), kvmem10m (10M-token tiled retrieval and the incremental view
+update), meank1m (building the Mean-K index of the 1M-token workspace).
+
 Other modes:
   --copy-calib         a plain elementwise copy of 1 GiB (5 launches), to scale
                        the FETCH_SIZE / WRITE_SIZE counters to bytes
@@ -54,6 +59,7 @@ KERNEL_SOURCES = {
     "query_reduce_kernel": "k_block.hip", "block_scores_kernel": "k_block.hip",
     "block_scores_mfma_kernel": "k_block.hip",
     "memory_update_kernel": "k_misc.hip", "redirect_kernel": "k_misc.hip", "sentinel_kernel": "k_misc.hip",
+    "mean_k_kernel": "k_index.hip",
 }
 
 
@@ -65,7 +71,7 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample for the CPU baseline")
-    ap.add_argument("--workload", default="snapkv", choices=["snapkv", "intentkv", "kvmem1m", "kvmem10m"],
+    ap.add_argument("--workload", default="snapkv", choices=["snapkv", "intentkv", "kvmem1m", "kvmem10m", "meank1m"],
                     help="which workload one step runs (the default line is snapkv)")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -528,7 +534,45 @@ class KVMem10M:
         return {"update_misses": misses, "update_moved_hits": moved}
 
 
-WORKLOADS = {"snapkv": SnapKV, "intentkv": IntentKV, "kvmem1m": KVMem1M, "kvmem10m": KVMem10M}
+class MeanK1M:
+    """Building the whole Mean-K index of the 1M-token workspace: the fp16
+    mean of every 32-token block of raw keys, for 64 layers x 8 KV heads x
+    32768 blocks (the layers read 8 aliased raw buffers, as in kvmem1m)."""
+    stages = ["index"]
+    kernels = {"index": ("mean_k_kernel", "k_index.hip")}
+    launches = {"index": 1}
+    score_stage = "index"
+    materialise_stages = []
+    dtype = "bf16"
+
+    def __init__(self, torch, kv, wl, dev):
+        self.kv, self.cfg = kv, wl.CONFIGS["kvmem1m"]
+        cfg = self.cfg
+        self.raw_k, _, self.offs = wl.kvmem_raw_store(cfg, dev)
+        self.mu = torch.empty((cfg.U, cfg.N, cfg.D), dtype=torch.float16, device=dev)
+        self.tokens = cfg.U * cfg.N * cfg.bt
+
+    def step(self, ev, stream, it):
+        cfg = self.cfg
+        ev[0].record(stream)
+        self.kv.build_index(self.raw_k, self.mu, bt=cfg.bt, D=cfg.D, src_rows=cfg.N * cfg.bt, src_offsets=self.offs)
+        ev[1].record(stream)
+
+    def algo_bytes(self):
+        cfg = self.cfg
+        return {"index": cfg.U * cfg.N * cfg.bt * cfg.D * 2 + cfg.U * cfg.N * cfg.D * 2}
+
+    def config(self):
+        cfg = self.cfg
+        return {"workload": "kvmem Mean-K index build over the 1M-token workspace: 64 layers x 8 KV heads x "
+                            "32768 blocks of 32 raw bf16 keys (D128) -> fp16 block means",
+                "units": cfg.U, "blocks_per_unit": cfg.N, "block_tokens": cfg.bt}
+
+    def extra(self):
+        return {}
+
+
+WORKLOADS = {"snapkv": SnapKV, "intentkv": IntentKV, "kvmem1m": KVMem1M, "kvmem10m": KVMem10M, "meank1m": MeanK1M}
 
 
 def main():

@@ -2,12 +2,13 @@
 //
 // KVMem (query-conditioned retrieval paragraph): the block scorer reads one
 // RoPE-stripped mean key per (layer, KV head, 32-token block), kept in HBM as
-// an fp16 index that grows as blocks fill.  Every wavefront takes one block
-// at a time: its 64 lanes cover the block's rows D * esz / 16 lanes per row,
-// all rows' 16-byte pieces in flight together, and accumulate in float64
-// (exact for a block's 32 bf16 or f16 rows, and for float32 rows spanning
-// fewer than 2^29 in magnitude).  The row groups are summed across lanes,
-// divided by the block size in float64 and rounded once to fp16.
+// an fp16 index that grows as blocks fill.  A wavefront takes 64 / (D * esz
+// / 16) consecutive blocks at a time (4 for bf16 rows of 128): each lane owns
+// one 16-byte column piece of one block and sums that piece over all the
+// block's rows in float64, eight rows in flight at a time, so no cross-lane
+// reduction is needed.  The float64 sum is exact for a block's 32 bf16 or
+// f16 rows (and for float32 rows spanning fewer than 2^29 in magnitude); it
+// is divided by the block size in float64 and rounded once to fp16.
 #include "common.h"
 
 namespace kvsel {
@@ -59,37 +60,35 @@ __global__ __launch_bounds__(256) void mean_k_kernel(IndexParams p, const void* 
   constexpr int E = 16 / esz;                     // elements per 16-byte piece
   const int lane = threadIdx.x & 63;
   const int lpr = p.D * esz / 16;                 // lanes per row: 8, 16 or 32
-  const int rows_per_pass = 64 / lpr;             // 8, 4 or 2
-  const int rlane = lane % lpr, rsub = lane / lpr;
+  const int bpw = 64 / lpr;                       // blocks per wavefront at a time: 8, 4 or 2
+  const int rlane = lane % lpr, slot = lane / lpr;
   const int64_t row_bytes = static_cast<int64_t>(p.D) * esz;
   const int64_t items = static_cast<int64_t>(p.U) * p.b_count;
   const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
   const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
   const double count = static_cast<double>(p.bt);
-  for (int64_t it = wave_global; it < items; it += n_waves) {
-    const int u = static_cast<int>(it / p.b_count);
-    const int64_t b = p.b_begin + (it - static_cast<int64_t>(u) * p.b_count);
+  for (int64_t it0 = wave_global * bpw; it0 < items; it0 += n_waves * bpw) {
+    const int64_t it = it0 + slot;
+    const bool live = it < items;
+    const int64_t itc = live ? it : items - 1;
+    const int u = static_cast<int>(itc / p.b_count);
+    const int64_t b = p.b_begin + (itc - static_cast<int64_t>(u) * p.b_count);
     const int64_t off = p.src_offsets ? p.src_offsets[u] : static_cast<int64_t>(u) * p.src_unit_stride;
     const uint8_t* blk = static_cast<const uint8_t*>(src) + off * esz + b * p.bt * row_bytes + rlane * 16;
     double acc[E];
 #pragma unroll
     for (int e = 0; e < E; ++e) acc[e] = 0.0;       // the sum starts from 0: a block of -0 rows gives +0
-    for (int r0 = 0; r0 < p.bt; r0 += rows_per_pass * kIndexBatch) {
+    for (int r0 = 0; r0 < p.bt; r0 += kIndexBatch) {
       ix_u32x4 v[kIndexBatch];
 #pragma unroll
-      for (int j = 0; j < kIndexBatch; ++j) {
-        const int row = r0 + j * rows_per_pass + rsub;
-        v[j] = (row < p.bt) ? *reinterpret_cast<const ix_u32x4*>(blk + row * row_bytes) : ix_u32x4{0u, 0u, 0u, 0u};
-      }
+      for (int j = 0; j < kIndexBatch; ++j)
+        v[j] = (r0 + j < p.bt) ? *reinterpret_cast<const ix_u32x4*>(blk + (r0 + j) * row_bytes)
+                               : ix_u32x4{0u, 0u, 0u, 0u};
 #pragma unroll
       for (int j = 0; j < kIndexBatch; ++j)
-        if (r0 + j * rows_per_pass + rsub < p.bt) add_piece<DT>(acc, v[j]);
+        if (r0 + j < p.bt) add_piece<DT>(acc, v[j]);
     }
-    // the row groups (lanes rlane + lpr * k) hold the same columns
-    for (int o = lpr; o < 64; o <<= 1)
-#pragma unroll
-      for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
-    if (rsub == 0) {
+    if (live) {
       uint16_t h[E];
 #pragma unroll
       for (int e = 0; e < E; ++e) h[e] = f64_to_f16_bits(acc[e] / count);   // IEEE float64 division
@@ -116,7 +115,7 @@ __global__ __launch_bounds__(256) void mean_k_kernel(IndexParams p, const void* 
 hipError_t launch_build_index(const IndexParams& p, const void* src_k, uint16_t* mu, hipStream_t st) {
   const int64_t items = static_cast<int64_t>(p.U) * p.b_count;
   if (items == 0) return hipSuccess;
-  const int64_t blocks = ceil_div(items, 4);       // one block per wavefront at a time
+  const int64_t blocks = ceil_div(items, 4 * 4);   // a few blocks per wavefront at a time
   const int grid = static_cast<int>(blocks > 65536 ? 65536 : blocks);
   if (p.dtype == KVSEL_BF16) mean_k_kernel<KVSEL_BF16><<<grid, 256, 0, st>>>(p, src_k, mu);
   else if (p.dtype == KVSEL_F16) mean_k_kernel<KVSEL_F16><<<grid, 256, 0, st>>>(p, src_k, mu);
