@@ -32,16 +32,27 @@ __global__ __launch_bounds__(256) void query_reduce_kernel(BlockParams p, const 
   const uint8_t* base = static_cast<const uint8_t*>(q) +
                         ((static_cast<int64_t>(sl) * p.Hq + static_cast<int64_t>(g) * G) * p.W * p.D) * esz;
   float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-  for (int64_t r = slot; r < rows; r += slots) {
-    const uint4 v = *reinterpret_cast<const uint4*>(base + (r * p.D + rl * E) * esz);
-    const uint32_t w[4] = {v.x, v.y, v.z, v.w};
-    if constexpr (DT == KVSEL_F32) {
-      for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(w[i]);
-    } else {
-      for (int i = 0; i < 4; ++i) {
-        const uint16_t lo = static_cast<uint16_t>(w[i] & 0xFFFFu), hi = static_cast<uint16_t>(w[i] >> 16);
-        acc[2 * i] += (DT == KVSEL_BF16) ? bf16_to_f32(lo) : f16_to_f32(lo);
-        acc[2 * i + 1] += (DT == KVSEL_BF16) ? bf16_to_f32(hi) : f16_to_f32(hi);
+  // rows slot, slot + slots, ... in order, kRowBatch loads in flight at a time
+  constexpr int kRowBatch = 8;
+  for (int64_t r0 = slot; r0 < rows; r0 += static_cast<int64_t>(slots) * kRowBatch) {
+    uint4 vb[kRowBatch];
+#pragma unroll
+    for (int j = 0; j < kRowBatch; ++j) {
+      const int64_t r = r0 + static_cast<int64_t>(j) * slots;
+      vb[j] = (r < rows) ? *reinterpret_cast<const uint4*>(base + (r * p.D + rl * E) * esz) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kRowBatch; ++j) {
+      if (r0 + static_cast<int64_t>(j) * slots >= rows) break;
+      const uint32_t w[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
+      if constexpr (DT == KVSEL_F32) {
+        for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(w[i]);
+      } else {
+        for (int i = 0; i < 4; ++i) {
+          const uint16_t lo = static_cast<uint16_t>(w[i] & 0xFFFFu), hi = static_cast<uint16_t>(w[i] >> 16);
+          acc[2 * i] += (DT == KVSEL_BF16) ? bf16_to_f32(lo) : f16_to_f32(lo);
+          acc[2 * i + 1] += (DT == KVSEL_BF16) ? bf16_to_f32(hi) : f16_to_f32(hi);
+        }
       }
     }
   }
