@@ -319,27 +319,50 @@ __global__ __launch_bounds__(256) void memory_lse_kernel(MemoryParams p, int n_g
   if (lane == 0) lse[i] = (m == -INFINITY) ? INFINITY : m + logf(s);   // empty history: every weight is 0
 }
 
-// per (256 positions, layer): sum over the layer's heads (global) or over each
-// KV group's heads (per unit)
+// per (1024 positions, layer): sum over the layer's heads (global) or over
+// each KV group's heads (per unit), in head order; each thread takes four
+// consecutive positions with 16-byte loads
 __global__ __launch_bounds__(256) void memory_rule_kernel(MemoryParams p, const float* __restrict__ logits,
                                                           const float* __restrict__ lse,
                                                           float* __restrict__ dst) {
   const int l = blockIdx.y;
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x;
-  if (j >= p.N) return;
-  const bool hist = in_history(p, j);
+  const int64_t j0 = (static_cast<int64_t>(blockIdx.x) * 256 + threadIdx.x) * 4;
+  if (j0 >= p.N) return;
+  const bool vec = (p.N % 4) == 0 && ((reinterpret_cast<uintptr_t>(logits) |
+                                       reinterpret_cast<uintptr_t>(dst)) & 15) == 0;   // aligned rows, j0 + 3 < N
+  bool hist[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) hist[i] = j0 + i < p.N && in_history(p, j0 + i);
   const int G = p.Hq / p.Hkv;
-  float acc = 0.f;
+  float acc[4] = {0.f, 0.f, 0.f, 0.f};
+  auto put = [&](float* row) {
+    if (vec) {
+      *reinterpret_cast<float4*>(row + j0) = make_float4(acc[0], acc[1], acc[2], acc[3]);
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (j0 + i < p.N) row[j0 + i] = acc[i];
+    }
+  };
 #pragma unroll 8
   for (int h = 0; h < p.Hq; ++h) {
-    const float x = logits[(static_cast<int64_t>(l) * p.Hq + h) * p.N + j];
-    acc += hist ? __builtin_amdgcn_exp2f((x - lse[l * p.Hq + h]) * kLog2e) : 0.f;
+    const float* row = logits + (static_cast<int64_t>(l) * p.Hq + h) * p.N;
+    float x[4];
+    if (vec) {
+      const float4 v = *reinterpret_cast<const float4*>(row + j0);
+      x[0] = v.x; x[1] = v.y; x[2] = v.z; x[3] = v.w;
+    } else {
+      for (int i = 0; i < 4; ++i) x[i] = (j0 + i < p.N) ? row[j0 + i] : 0.f;
+    }
+    const float ls = lse[l * p.Hq + h];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) acc[i] += hist[i] ? __builtin_amdgcn_exp2f((x[i] - ls) * kLog2e) : 0.f;
     if (p.reduce == KVSEL_REDUCE_PER_UNIT && (h % G) == G - 1) {
-      dst[(static_cast<int64_t>(l) * p.Hkv + h / G) * p.N + j] = acc;
-      acc = 0.f;
+      put(dst + (static_cast<int64_t>(l) * p.Hkv + h / G) * p.N);
+#pragma unroll
+      for (int i = 0; i < 4; ++i) acc[i] = 0.f;
     }
   }
-  if (p.reduce == KVSEL_REDUCE_GLOBAL) dst[static_cast<int64_t>(l) * p.N + j] = acc;
+  if (p.reduce == KVSEL_REDUCE_GLOBAL) put(dst + static_cast<int64_t>(l) * p.N);
 }
 
 __global__ void memory_layer_sum_kernel(int L, int64_t N, const float* __restrict__ layer,
@@ -397,7 +420,7 @@ hipError_t launch_memory_scores(const MemoryParams& p, int dt, const float* M, c
   if (e != hipSuccess) return e;
   memory_lse_kernel<<<static_cast<int>(ceil_div(p.L * p.Hq, 4)), 256, 0, st>>>(p, n_groups, part, lse);
   if ((e = hipGetLastError()) != hipSuccess) return e;
-  dim3 grid(static_cast<unsigned>(ceil_div(p.N, 256)), p.L);
+  dim3 grid(static_cast<unsigned>(ceil_div(p.N, 1024)), p.L);
   float* dst = (p.reduce == KVSEL_REDUCE_GLOBAL) ? layer : out;
   memory_rule_kernel<<<grid, 256, 0, st>>>(p, logits, lse, dst);
   if ((e = hipGetLastError()) != hipSuccess) return e;

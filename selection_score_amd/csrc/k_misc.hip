@@ -55,6 +55,71 @@ __global__ __launch_bounds__(256) void memory_update_kernel(int LH, int D, int W
   }
 }
 
+// The same update with 16-byte loads: lane (row group rs, column piece rl)
+// sums its piece over rows rs, rs + 64 / lpr, ... with eight loads in flight;
+// the row groups are then summed across lanes.  Needs D * esz in
+// {128, 256, 512, 1024} and 16-byte aligned query rows.
+template <int DT>
+__global__ __launch_bounds__(256) void memory_update_vec_kernel(int LH, int D, int W,
+                                                                const void* __restrict__ q,
+                                                                float* __restrict__ M, float decay) {
+  constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
+  constexpr int E = 16 / esz;
+  constexpr int kRowBatch = 8;
+  const int lane = threadIdx.x & 63;
+  const int lh = blockIdx.x * 4 + (threadIdx.x >> 6);
+  if (lh >= LH) return;                           // the whole wavefront
+  const int lpr = D * esz / 16;                   // 8, 16, 32 or 64 lanes per row
+  const int rpp = 64 / lpr;                       // rows per pass
+  const int rl = lane % lpr, rs = lane / lpr;
+  const int64_t row_bytes = static_cast<int64_t>(D) * esz;
+  const uint8_t* base = static_cast<const uint8_t*>(q) + static_cast<int64_t>(lh) * W * row_bytes + rl * 16;
+  float acc[E];
+#pragma unroll
+  for (int e = 0; e < E; ++e) acc[e] = 0.f;
+  for (int t0 = rs; t0 < W; t0 += rpp * kRowBatch) {
+    uint4 v[kRowBatch];
+#pragma unroll
+    for (int j = 0; j < kRowBatch; ++j) {
+      const int t = t0 + j * rpp;
+      v[j] = (t < W) ? *reinterpret_cast<const uint4*>(base + t * row_bytes) : make_uint4(0, 0, 0, 0);
+    }
+#pragma unroll
+    for (int j = 0; j < kRowBatch; ++j) {
+      if (t0 + j * rpp >= W) break;
+      const uint32_t w[4] = {v[j].x, v[j].y, v[j].z, v[j].w};
+      if constexpr (DT == KVSEL_F32) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(w[i]);
+      } else {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const uint16_t lo = static_cast<uint16_t>(w[i] & 0xFFFFu), hi = static_cast<uint16_t>(w[i] >> 16);
+          acc[2 * i] += (DT == KVSEL_BF16) ? bf16_to_f32(lo) : f16_to_f32(lo);
+          acc[2 * i + 1] += (DT == KVSEL_BF16) ? bf16_to_f32(hi) : f16_to_f32(hi);
+        }
+      }
+    }
+  }
+  for (int o = lpr; o < 64; o <<= 1)              // every lane of a column piece ends with its total
+#pragma unroll
+    for (int e = 0; e < E; ++e) acc[e] += __shfl_xor(acc[e], o, 64);
+  float m[E];
+  float nn = 0.f;
+  float* mrow = M + static_cast<int64_t>(lh) * D + rl * E;
+#pragma unroll
+  for (int e = 0; e < E; ++e) {
+    m[e] = decay * mrow[e] + acc[e] / static_cast<float>(W);
+    nn += m[e] * m[e];
+  }
+  for (int o = 1; o < lpr; o <<= 1) nn += __shfl_xor(nn, o, 64);
+  const float inv = (nn > 0.f) ? 1.0f / sqrtf(nn) : 0.f;
+  if (rs == 0) {
+#pragma unroll
+    for (int e = 0; e < E; ++e) mrow[e] = m[e] * inv;
+  }
+}
+
 hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, int64_t dead,
                            hipStream_t st) {
   if (N == 0) return hipSuccess;
@@ -80,6 +145,14 @@ hipError_t launch_memory_update(int L, int Hq, int D, int W, int dt, const void*
   const int LH = L * Hq;
   if (LH == 0) return hipSuccess;
   const int grid = static_cast<int>(ceil_div(LH, 4));
+  const int esz = (dt == KVSEL_F32) ? 4 : 2;
+  const int row = D * esz;
+  if ((row == 128 || row == 256 || row == 512 || row == 1024) && (reinterpret_cast<uintptr_t>(q) & 15) == 0) {
+    if (dt == KVSEL_BF16) memory_update_vec_kernel<KVSEL_BF16><<<grid, 256, 0, st>>>(LH, D, W, q, M, decay);
+    else if (dt == KVSEL_F16) memory_update_vec_kernel<KVSEL_F16><<<grid, 256, 0, st>>>(LH, D, W, q, M, decay);
+    else memory_update_vec_kernel<KVSEL_F32><<<grid, 256, 0, st>>>(LH, D, W, q, M, decay);
+    return hipGetLastError();
+  }
   if (dt == KVSEL_BF16) memory_update_kernel<KVSEL_BF16><<<grid, 256, 0, st>>>(LH, D, W, q, M, decay);
   else if (dt == KVSEL_F16) memory_update_kernel<KVSEL_F16><<<grid, 256, 0, st>>>(LH, D, W, q, M, decay);
   else memory_update_kernel<KVSEL_F32><<<grid, 256, 0, st>>>(LH, D, W, q, M, decay);
