@@ -23,9 +23,9 @@
 // runs the remaining passes and both sweeps: with up to 32 keys per thread
 // held in registers (select_regs_kernel, untiled calls), otherwise reading
 // the workspace (select_kernel; tiled calls stage their running candidates
-// in LDS ahead of the tile's keys).  Unpooled untiled calls with at least
-// 128 units of up to 32768 columns skip the first launch: each unit's
-// workgroup reads its scores and makes its keys itself.
+// in LDS ahead of the tile's keys).  Unpooled untiled calls without a slot
+// map, with at least 128 units of up to 32768 columns, skip the first
+// launch: each unit's workgroup reads its scores and makes its keys itself.
 #include "common.h"
 
 namespace kvsel {
@@ -535,18 +535,17 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
   } else {
     for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0u;
     const float* row = scores + static_cast<int64_t>(u) * p.row_stride;
+    // unconditional loads (a clamped column past the segment) keep all KPT
+    // in flight; a conditional load would wait for each one in turn
     float v[KPT];
 #pragma unroll
-    for (int i = 0; i < KPT; ++i) {
-      const int e = s_beg + 64 * i + lane;
-      v[i] = (e < s_end) ? row[e] : 0.f;
-    }
+    for (int i = 0; i < KPT; ++i) v[i] = row[min(s_beg + 64 * i + lane, n - 1)];
     __syncthreads();                                // histogram cleared
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
       const int e = s_beg + 64 * i + lane;
       uint32_t key = 0u;
-      if (e < s_end && e >= sink_end && e < rec_begin && alive(e)) {
+      if (e < s_end && e >= sink_end && e < rec_begin) {   // no slot map on this path
         key = score_key(v[i]);
         atomicAdd(&sh.hist[key >> 24], 1u);
         ++cc;
@@ -682,10 +681,12 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
     uint32_t* keys = static_cast<uint32_t*>(ws);
     const int n_slices = static_cast<int>(ceil_div(p.n, kPrepKeys));
     uint32_t* hist = keys + (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 64;
-    if (p.n <= 32 * kThreads && p.U >= kFusedMinUnits && (p.pool == KVSEL_POOL_NONE || p.pool_k == 1)) {
-      // enough units to fill the device and no pooling: keys and all radix
-      // passes in the per-unit workgroup (pooled rows keep the two launches,
-      // whose key kernel spreads the window work over many workgroups)
+    if (p.n <= 32 * kThreads && p.U >= kFusedMinUnits && (p.pool == KVSEL_POOL_NONE || p.pool_k == 1) &&
+        p.slot_map == nullptr) {
+      // enough units to fill the device, no pooling and no dead slots: keys
+      // and all radix passes in the per-unit workgroup (pooled rows keep the
+      // two launches, whose key kernel spreads the window work over many
+      // workgroups)
       select_regs_kernel<32, true><<<p.U, kThreads, 0, st>>>(p, scores, nullptr, nullptr, 0);
       return hipGetLastError();
     }

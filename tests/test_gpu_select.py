@@ -165,9 +165,10 @@ def test_select_pooled_slices(pool, n):
     (128, 6000, 900, "avg", 255, False, False),    # the widest window
 ])
 def test_select_many_units(U, n, k, pool, pool_k, ties, dead):
-    """Many units: unpooled rows (and windows of one) take the single-launch
-    path where each unit's workgroup makes its own keys; pooled rows keep the
-    two launches.  Against pool1d + select_topk."""
+    """Many units: unpooled rows (and windows of one) without a slot map take
+    the single-launch path where each unit's workgroup makes its own keys;
+    pooled rows and dead slots keep the two launches.  Against pool1d +
+    select_topk."""
     from oracle import numerics
     from oracle import score as osc
     dev = require_gpu()
