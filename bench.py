@@ -58,7 +58,8 @@ KERNEL_SOURCES = {
     "memory_rule_kernel": "k_memory.hip", "memory_layer_sum_kernel": "k_memory.hip",
     "query_reduce_kernel": "k_block.hip", "block_scores_kernel": "k_block.hip",
     "block_scores_mfma_kernel": "k_block.hip",
-    "memory_update_kernel": "k_misc.hip", "redirect_kernel": "k_misc.hip", "sentinel_kernel": "k_misc.hip",
+    "memory_update_kernel": "k_misc.hip", "memory_update_vec_kernel": "k_misc.hip",
+    "redirect_kernel": "k_misc.hip", "sentinel_kernel": "k_misc.hip",
     "mean_k_kernel": "k_index.hip",
 }
 

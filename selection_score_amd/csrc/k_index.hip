@@ -53,6 +53,8 @@ __device__ __forceinline__ void add_piece(double* acc, const ix_u32x4& v) {
   }
 }
 
+}  // namespace
+
 template <int DT>
 __global__ __launch_bounds__(256) void mean_k_kernel(IndexParams p, const void* __restrict__ src,
                                                      uint16_t* __restrict__ mu) {
@@ -109,8 +111,6 @@ __global__ __launch_bounds__(256) void mean_k_kernel(IndexParams p, const void* 
     }
   }
 }
-
-}  // namespace
 
 hipError_t launch_build_index(const IndexParams& p, const void* src_k, uint16_t* mu, hipStream_t st) {
   const int64_t items = static_cast<int64_t>(p.U) * p.b_count;
