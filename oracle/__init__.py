@@ -53,5 +53,7 @@ PIN_STATUS = {
     "materialise.gather_view": "pinned (bitwise element loops on tiny inputs; raw->baked identity)",
     "materialise.incremental_view": "pinned (equals a fresh build of the new selection; disjointness)",
     "materialise.redirect": "pinned (invariants: kept bitwise, dropped -> dead, idempotent, one-way)",
+    "materialise.free_list": "pinned (hand-worked slot maps with aliases, prior redirects and a "
+                             "protected prefix; reusing freed slots never changes a kept or sibling read)",
     "materialise.decode_attention_*": "pinned (dead-slot closed form in both sign regimes)",
 }

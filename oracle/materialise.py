@@ -103,6 +103,28 @@ def redirect(slot_map, keep_mask, dead_slot):
     return np.where(np.asarray(keep_mask, dtype=bool), sm, dead_slot)
 
 
+def free_list(slot_map, keep_mask, dead_slot, protected_len=0):
+    """Physical slots a compression step may return to the allocator
+    (IntentKV §7, alias-aware deallocation; §4 minimum check 6).
+
+    A dropped logical position j (keep_mask[j] false) frees its slot
+    u = slot_map[j] only if (a) j is outside the radix-protected prefix
+    (j >= protected_len), (b) u is not the dead slot, and (c) no kept
+    position maps to u.  slot_map is the map before the redirect.  Returns
+    the distinct freed slots in ascending order (int64).
+    """
+    sm = np.asarray(slot_map, dtype=np.int64)
+    keep = np.asarray(keep_mask, dtype=bool)
+    kept_slots = set(int(u) for u in sm[keep])
+    freed = set()
+    for j in range(sm.shape[0]):
+        u = int(sm[j])
+        if keep[j] or j < protected_len or u == dead_slot or u in kept_slots:
+            continue
+        freed.add(u)
+    return np.array(sorted(freed), dtype=np.int64)
+
+
 def sentinel_rows(dtype, D):
     """K and V rows of the dead slot (IntentKV §2 Q2): K = -1e4, V = 0,
     each rounded once to the pool's storage format ("bf16" or "f16")."""

@@ -216,3 +216,48 @@ def test_dead_slot_is_a_hard_mask_only_with_margin():
     o2 = om.decode_attention_slots(q2, pool_k, pool_v, redirected)
     h2 = om.decode_attention_hard(q2, pool_k, pool_v, slot_map, keep)
     assert np.linalg.norm(o2) < 1e-6 * np.linalg.norm(h2)
+
+
+# ---------------------------------------------------------------- alias-aware free list
+
+def test_free_list_hand_example():
+    # slots: j0 5 (kept), j1 6 (dropped, but j2 keeps 6: aliased), j3 7 (freed),
+    # j4 dead (prior redirect), j5 9 (freed), j6 5 (dropped, kept by j0), j7 10 (kept),
+    # j8 and j9 both 11 (dropped twice: freed once)
+    D = 99
+    sm = [5, 6, 6, 7, D, 9, 5, 10, 11, 11]
+    keep = [1, 0, 1, 0, 0, 0, 0, 1, 0, 0]
+    np.testing.assert_array_equal(om.free_list(sm, keep, D), [7, 9, 11])
+    # a radix-protected prefix of 4 positions keeps slot 7 allocated
+    np.testing.assert_array_equal(om.free_list(sm, keep, D, protected_len=4), [9, 11])
+    # nothing dropped, or everything protected: nothing freed
+    assert om.free_list(sm, [1] * 10, D).size == 0
+    assert om.free_list(sm, keep, D, protected_len=10).size == 0
+
+
+def test_reusing_freed_slots_never_changes_a_kept_or_sibling_read():
+    # Two requests share a radix-protected prefix of physical slots; each has
+    # its own tail, with aliases from earlier rounds.  After request 0 drops
+    # entries and its freed slots are handed to new data, every position that
+    # request 0 keeps and every position of request 1 reads what it read before.
+    rng = np.random.default_rng(3)
+    dead = 1000
+    pool = rng.standard_normal((dead + 1, 4))
+    P = 16
+    prefix = rng.permutation(200)[:P]
+    tail0 = rng.integers(200, 400, size=48)          # duplicates: slots shared inside the tail
+    tail1 = rng.integers(400, 600, size=48)
+    sm0 = np.concatenate([prefix, tail0]); sm1 = np.concatenate([prefix, tail1])
+    sm0[rng.choice(np.arange(P, 64), 6, replace=False)] = dead   # redirected in an earlier round
+    keep0 = rng.random(64) < 0.4
+    keep0[sm0 == dead] = False
+    before0 = pool[sm0[keep0]].copy(); before1 = pool[sm1].copy()
+    freed = om.free_list(sm0, keep0, dead, protected_len=P)
+    assert dead not in freed and not set(freed) & set(prefix.tolist())
+    pool2 = pool.copy()
+    pool2[freed] = 12345.0                            # the allocator hands them out again
+    np.testing.assert_array_equal(pool2[sm0[keep0]], before0)
+    np.testing.assert_array_equal(pool2[sm1], before1)
+    # and every slot that only dropped, unprotected positions referenced is freed
+    only_dropped = set(sm0[P:][~keep0[P:]].tolist()) - set(sm0[keep0].tolist()) - {dead}
+    assert set(freed.tolist()) == only_dropped
