@@ -303,6 +303,44 @@ typedef struct kvsel_redirect_args {
 
 kvsel_status kvsel_redirect(const kvsel_redirect_args* args, void* stream);
 
+/* ------------------------------------------------------------------ free list
+ *
+ * IntentKV §7 (alias-aware deallocation) and §4 minimum check 6: after a
+ * compression step, the physical slot u = slot_map[j] of a dropped position
+ * j may go back to the allocator only if (a) j >= protected_len (outside the
+ * radix-protected prefix), (b) u != dead_slot, and (c) no kept position
+ * maps to u (this catches slots shared by aliases).  Call it with the slot
+ * map as it was BEFORE kvsel_redirect overwrites the dropped positions.
+ *
+ *   slot_map    [N] int32 (not modified); keep_mask [N] u8 (1 = kept)
+ *   n_slots     physical slot ids lie in [0, n_slots); ids outside are never
+ *               freed (nor the dead slot)
+ *   free_slots  out [N] int32: the distinct freed slots in ascending order,
+ *               then -1 up to N
+ *   n_free      out [1] int32: how many were freed
+ * Workspace: kvsel_free_list_workspace (two bitmaps over the slot ids).
+ * Errors: E_ARG (NULL pointers, N outside [0, 2^31), n_slots outside
+ * [1, 2^31), protected_len < 0, pointers not 4-byte aligned),
+ * E_WORKSPACE, E_DEVICE.  N = 0 writes n_free = 0.
+ */
+typedef struct kvsel_freelist_args {
+  uint32_t struct_size;
+  int32_t reserved;          /* 0 */
+  int64_t N;
+  const int32_t* slot_map;
+  const uint8_t* keep_mask;
+  int64_t dead_slot;
+  int64_t protected_len;
+  int64_t n_slots;
+  int32_t* free_slots;
+  int32_t* n_free;
+} kvsel_freelist_args;
+
+kvsel_status kvsel_free_list_workspace(const kvsel_freelist_args* args, size_t* bytes);
+
+kvsel_status kvsel_free_list(const kvsel_freelist_args* args, void* workspace, size_t workspace_bytes,
+                             void* stream);
+
 /* ------------------------------------------------------------------ index
  *
  * KVMem (query-conditioned retrieval paragraph): the block scorer reads one

@@ -87,9 +87,18 @@ class IndexArgs(ctypes.Structure):
     ]
 
 
+class FreeListArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("reserved", c_i32), ("N", c_i64), ("slot_map", c_vp), ("keep_mask", c_vp),
+        ("dead_slot", c_i64), ("protected_len", c_i64), ("n_slots", c_i64), ("free_slots", c_vp),
+        ("n_free", c_vp),
+    ]
+
+
 EXPORTS = ["kvsel_version", "kvsel_last_error", "kvsel_score_workspace", "kvsel_score",
            "kvsel_select_workspace", "kvsel_select", "kvsel_gather_workspace", "kvsel_gather_rerope",
-           "kvsel_redirect", "kvsel_memory_update", "kvsel_build_index"]
+           "kvsel_redirect", "kvsel_memory_update", "kvsel_build_index", "kvsel_free_list_workspace",
+           "kvsel_free_list"]
 
 _lib = None
 
@@ -117,6 +126,8 @@ def load(path=LIB_PATH):
     lib.kvsel_redirect.argtypes = [P(RedirectArgs), c_vp]
     lib.kvsel_memory_update.argtypes = [P(MemUpdArgs), c_vp]
     lib.kvsel_build_index.argtypes = [P(IndexArgs), c_vp]
+    lib.kvsel_free_list_workspace.argtypes = [P(FreeListArgs), P(ctypes.c_size_t)]
+    lib.kvsel_free_list.argtypes = [P(FreeListArgs), c_vp, ctypes.c_size_t, c_vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = c_i32
     _lib = lib

@@ -455,6 +455,50 @@ kvsel_status kvsel_redirect(const kvsel_redirect_args* a, void* stream) {
 
 // ------------------------------------------------------------------ memory
 
+static kvsel_status check_free_list(const kvsel_freelist_args* a) {
+  if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+  if (a->struct_size < sizeof(kvsel_freelist_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->N < 0 || a->N > kMaxN) return fail(KVSEL_E_ARG, "N must be in [0, 2^31)");
+  if (a->n_slots < 1 || a->n_slots > kMaxN) return fail(KVSEL_E_ARG, "n_slots must be in [1, 2^31)");
+  if (a->protected_len < 0) return fail(KVSEL_E_ARG, "protected_len must be >= 0");
+  if (a->n_free == nullptr) return fail(KVSEL_E_ARG, "n_free is NULL");
+  if (a->N > 0 && (a->slot_map == nullptr || a->keep_mask == nullptr || a->free_slots == nullptr))
+    return fail(KVSEL_E_ARG, "slot_map, keep_mask or free_slots is NULL");
+  const uintptr_t mis = reinterpret_cast<uintptr_t>(a->slot_map) | reinterpret_cast<uintptr_t>(a->free_slots) |
+                        reinterpret_cast<uintptr_t>(a->n_free);
+  if ((mis & 3u) != 0) return fail(KVSEL_E_ARG, "slot_map, free_slots and n_free must be 4-byte aligned");
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_free_list_workspace(const kvsel_freelist_args* a, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return fail(KVSEL_E_ARG, "bytes is NULL");
+    kvsel_status s = check_free_list(a);
+    if (s != KVSEL_OK) return s;
+    *bytes = free_list_workspace_bytes(a->n_slots);
+    return KVSEL_OK;
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+kvsel_status kvsel_free_list(const kvsel_freelist_args* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    kvsel_status s = check_free_list(a);
+    if (s != KVSEL_OK) return s;
+    const size_t need = free_list_workspace_bytes(a->n_slots);
+    if (ws == nullptr || ws_bytes < need) return fail(KVSEL_E_WORKSPACE, "workspace too small (see kvsel_free_list_workspace)");
+    if (!aligned16(ws)) return fail(KVSEL_E_ARG, "workspace must be 16-byte aligned");
+    if ((s = check_device()) != KVSEL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish(launch_free_list(a->N, a->slot_map, a->keep_mask, a->dead_slot, a->protected_len, a->n_slots,
+                                   a->free_slots, a->n_free, ws, st),
+                  st, "free list");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
 kvsel_status kvsel_build_index(const kvsel_index_args* a, void* stream) {
   try {
     if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");

@@ -175,6 +175,10 @@ struct IndexParams {
 };
 hipError_t launch_build_index(const IndexParams& p, const void* src_k, uint16_t* mu, hipStream_t st);
 
+size_t free_list_workspace_bytes(int64_t n_slots);
+hipError_t launch_free_list(int64_t N, const int32_t* slot_map, const uint8_t* keep, int64_t dead,
+                            int64_t protected_len, int64_t n_slots, int32_t* free_slots, int32_t* n_free,
+                            void* ws, hipStream_t st);
 hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, int64_t dead,
                            hipStream_t st);
 hipError_t launch_sentinel(void* k_pool, void* v_pool, int L, int Hkv, int D, int dtype,

@@ -120,6 +120,97 @@ __global__ __launch_bounds__(256) void memory_update_vec_kernel(int LH, int D, i
   }
 }
 
+// ---- alias-aware free list (IntentKV §7): bitmaps over the slot ids of the
+// kept positions and of the freeable ones, then one workgroup lists the set
+// bits in ascending order.
+__global__ void free_clear_kernel(uint32_t* bits, int64_t n_words) {
+  const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (i < n_words) bits[i] = 0u;
+}
+
+__global__ void free_mark_kept_kernel(int64_t N, const int32_t* __restrict__ slot_map,
+                                      const uint8_t* __restrict__ keep, int64_t n_slots,
+                                      uint32_t* __restrict__ kept_bits) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= N || keep[j] == 0) return;
+  const int64_t u = slot_map[j];
+  if (u >= 0 && u < n_slots) atomicOr(&kept_bits[u >> 5], 1u << (u & 31));
+}
+
+__global__ void free_mark_kernel(int64_t N, const int32_t* __restrict__ slot_map,
+                                 const uint8_t* __restrict__ keep, int64_t dead, int64_t protected_len,
+                                 int64_t n_slots, const uint32_t* __restrict__ kept_bits,
+                                 uint32_t* __restrict__ free_bits) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= N || j < protected_len || keep[j] != 0) return;
+  const int64_t u = slot_map[j];
+  if (u == dead || u < 0 || u >= n_slots) return;
+  const uint32_t bit = 1u << (u & 31);
+  if ((kept_bits[u >> 5] & bit) == 0u) atomicOr(&free_bits[u >> 5], bit);
+}
+
+// One workgroup: thread t owns a contiguous run of bitmap words, so the
+// exclusive scan of the per-thread counts gives every set bit its place.
+constexpr int kFreeThreads = 1024;
+__global__ __launch_bounds__(kFreeThreads) void free_compact_kernel(int64_t N, int64_t n_words,
+                                                                    const uint32_t* __restrict__ free_bits,
+                                                                    int32_t* __restrict__ free_slots,
+                                                                    int32_t* __restrict__ n_free) {
+  __shared__ uint32_t wave_tot[kFreeThreads / 64];
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t per = (n_words + kFreeThreads - 1) / kFreeThreads;
+  const int64_t w0 = min(n_words, static_cast<int64_t>(tid) * per);
+  const int64_t w1 = min(n_words, w0 + per);
+  uint32_t cnt = 0;
+  for (int64_t w = w0; w < w1; ++w) cnt += __popc(free_bits[w]);
+  // exclusive scan over the workgroup: within the wavefront, then across
+  uint32_t incl = cnt;
+  for (int o = 1; o < 64; o <<= 1) {
+    const uint32_t v = __shfl_up(incl, o, 64);
+    if (lane >= o) incl += v;
+  }
+  if (lane == 63) wave_tot[wave] = incl;
+  __syncthreads();
+  uint32_t base = incl - cnt, total = 0;
+  for (int w = 0; w < kFreeThreads / 64; ++w) {
+    if (w < wave) base += wave_tot[w];
+    total += wave_tot[w];
+  }
+  uint32_t pos = base;
+  for (int64_t w = w0; w < w1; ++w) {
+    uint32_t b = free_bits[w];
+    while (b != 0u) {
+      const int i = __ffs(b) - 1;
+      free_slots[pos++] = static_cast<int32_t>(w * 32 + i);
+      b &= b - 1u;
+    }
+  }
+  for (int64_t i = static_cast<int64_t>(total) + tid; i < N; i += kFreeThreads) free_slots[i] = -1;
+  if (tid == 0) n_free[0] = static_cast<int32_t>(total);
+}
+
+size_t free_list_workspace_bytes(int64_t n_slots) {
+  const int64_t words = (n_slots + 31) / 32;
+  return static_cast<size_t>(2 * ((words * 4 + 255) / 256 * 256));
+}
+
+hipError_t launch_free_list(int64_t N, const int32_t* slot_map, const uint8_t* keep, int64_t dead,
+                            int64_t protected_len, int64_t n_slots, int32_t* free_slots, int32_t* n_free,
+                            void* ws, hipStream_t st) {
+  const int64_t words = (n_slots + 31) / 32;
+  uint32_t* kept_bits = static_cast<uint32_t*>(ws);
+  uint32_t* free_bits = kept_bits + (words * 4 + 255) / 256 * 64;
+  const int64_t all_words = (free_bits - kept_bits) + words;   // both bitmaps, one clear
+  free_clear_kernel<<<static_cast<int>(ceil_div(all_words, 256)), 256, 0, st>>>(kept_bits, all_words);
+  if (N > 0) {
+    const int g = static_cast<int>(ceil_div(N, 256));
+    free_mark_kept_kernel<<<g, 256, 0, st>>>(N, slot_map, keep, n_slots, kept_bits);
+    free_mark_kernel<<<g, 256, 0, st>>>(N, slot_map, keep, dead, protected_len, n_slots, kept_bits, free_bits);
+  }
+  free_compact_kernel<<<1, kFreeThreads, 0, st>>>(N, words, free_bits, free_slots, n_free);
+  return hipGetLastError();
+}
+
 hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, int64_t dead,
                            hipStream_t st) {
   if (N == 0) return hipSuccess;

@@ -277,3 +277,21 @@ def build_index(raw_k, mu, *, bt, D, src_rows, NB=None, b_begin=0, b_count=None,
     a.NB, a.b_begin, a.b_count, a.mu = NB, b_begin, b_count, _ptr(mu)
     lib = _abi.load()
     _check(lib.kvsel_build_index(ctypes.byref(a), _stream(stream)))
+
+
+def free_list(slot_map, keep_mask, dead_slot, free_slots, n_free, *, n_slots, protected_len=0, workspace=None,
+              stream=None):
+    """kvsel_free_list.  slot_map [N] int32 (before the redirect); keep_mask [N]
+    uint8; free_slots [N] int32 and n_free [1] int32 are written.  Returns the
+    workspace it used."""
+    N = slot_map.shape[0]
+    a = _abi.FreeListArgs()
+    a.struct_size = ctypes.sizeof(_abi.FreeListArgs)
+    a.N, a.slot_map, a.keep_mask, a.dead_slot = N, _ptr(slot_map), _ptr(keep_mask), dead_slot
+    a.protected_len, a.n_slots, a.free_slots, a.n_free = protected_len, n_slots, _ptr(free_slots), _ptr(n_free)
+    lib = _abi.load()
+    nb = ctypes.c_size_t(0)
+    _check(lib.kvsel_free_list_workspace(ctypes.byref(a), ctypes.byref(nb)))
+    ws, wsz = _workspace(nb.value, slot_map.device, workspace)
+    _check(lib.kvsel_free_list(ctypes.byref(a), _ptr(ws), wsz, _stream(stream)))
+    return ws

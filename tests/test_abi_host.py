@@ -37,6 +37,7 @@ STRUCTS = {
     "kvsel_redirect_args": _abi.RedirectArgs,
     "kvsel_memupd_args": _abi.MemUpdArgs,
     "kvsel_index_args": _abi.IndexArgs,
+    "kvsel_freelist_args": _abi.FreeListArgs,
 }
 
 
@@ -180,3 +181,19 @@ def test_index_validation_without_device():
     assert call() == _abi.KVSEL_OK
     a.struct_size = 8
     assert call() == _abi.KVSEL_E_ARG
+
+
+def test_free_list_validation_without_device():
+    lib = _abi.load()
+    a = _abi.FreeListArgs()
+    a.struct_size = ctypes.sizeof(a)
+    a.N, a.slot_map, a.keep_mask, a.free_slots, a.n_free = 100, 0x1000, 0x2000, 0x3000, 0x4000
+    a.dead_slot, a.protected_len, a.n_slots = 50, 0, 64
+    nb = ctypes.c_size_t(0)
+    assert lib.kvsel_free_list_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_OK
+    assert nb.value >= 2 * 2 * 4                  # two bitmaps of 64 bits
+    assert lib.kvsel_free_list(ctypes.byref(a), None, 0, None) == _abi.KVSEL_E_WORKSPACE
+    for field, bad in [("n_slots", 0), ("protected_len", -1), ("N", -5), ("n_free", 0), ("slot_map", 0x1002)]:
+        setattr(a, field, bad)
+        assert lib.kvsel_free_list_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_E_ARG, field
+        a.N, a.slot_map, a.n_free, a.n_slots, a.protected_len = 100, 0x1000, 0x4000, 64, 0
