@@ -294,14 +294,16 @@ class SnapKV:
 class IntentKV:
     """Session-memory scoring over a paged pool: one turn's memory update,
     memory-attention rule scores summed over every layer and head, a global
-    top-8192 (dead slots excluded), and the slot-map redirect with sentinel
-    rows.  The slot map is reset from the original before each step (a 256 KiB
-    copy outside the stage events) so every step does the same work."""
-    stages = ["update", "score", "select", "redirect"]
-    kernels = {"update": ("memory_update_kernel", "k_misc.hip")}
-    launches = {"update": 1, "score": 4, "select": 2, "redirect": 2}
+    top-8192 (dead slots excluded), the alias-aware free list of the step
+    (the 4-token sink prefix as the radix-protected prefix), and the slot-map redirect
+    with sentinel rows.  The slot map is reset from the original before each
+    step (a 256 KiB copy outside the stage events) so every step does the
+    same work."""
+    stages = ["update", "score", "select", "free", "redirect"]
+    kernels = {"update": ("memory_update_vec_kernel", "k_misc.hip")}
+    launches = {"update": 1, "score": 4, "select": 2, "free": 4, "redirect": 2}
     score_stage = "score"
-    materialise_stages = ["select", "redirect"]
+    materialise_stages = ["select", "free", "redirect"]
     dtype = "bf16"
 
     def __init__(self, torch, kv, wl, dev):
@@ -323,6 +325,11 @@ class IntentKV:
         self.sel_ws = kv.select(self.rule[None], self.kept, k_total=cfg.k, n_sink=cfg.n_sink,
                                 n_recent=cfg.n_recent, keep_mask=self.mask, slot_map=self.sm,
                                 dead_slot=self.inp["dead_slot"])
+        self.freed = torch.empty(N, dtype=torch.int32, device=dev)
+        self.n_freed = torch.empty(1, dtype=torch.int32, device=dev)
+        self.n_slots = (self.inp["page_table"].numel() + 1) * cfg.page_size   # pages + the dead page
+        self.free_ws = kv.free_list(self.sm, self.mask[0], self.inp["dead_slot"], self.freed, self.n_freed,
+                                    n_slots=self.n_slots, protected_len=0)
         self.tokens = cfg.L * cfg.Hkv * N
 
     def step(self, ev, stream, it):
@@ -338,8 +345,11 @@ class IntentKV:
         kv.select(self.rule[None], self.kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
                   keep_mask=self.mask, slot_map=self.sm, dead_slot=inp["dead_slot"], workspace=self.sel_ws)
         ev[3].record(stream)
-        kv.redirect(self.sm, self.mask[0], inp["dead_slot"], k_pool=self.kflat, v_pool=self.vflat)
+        kv.free_list(self.sm, self.mask[0], inp["dead_slot"], self.freed, self.n_freed, n_slots=self.n_slots,
+                     protected_len=cfg.n_sink, workspace=self.free_ws)
         ev[4].record(stream)
+        kv.redirect(self.sm, self.mask[0], inp["dead_slot"], k_pool=self.kflat, v_pool=self.vflat)
+        ev[5].record(stream)
 
     def algo_bytes(self):
         cfg = self.cfg
@@ -348,14 +358,16 @@ class IntentKV:
         return {"update": L * Hq * cfg.W * D * 2 + 2 * mb,
                 "score": L * N * Hkv * D * 2 + mb + 4 * N + 4 * (N // cfg.page_size) + 4 * N,
                 "select": 4 * N + 4 * N + N + 4 * cfg.k,
+                "free": 2 * (4 * N + N) + 4 * N,
                 "redirect": 2 * 4 * N + N + 2 * L * Hkv * D * 2}
 
     def config(self):
         cfg = self.cfg
         return {"workload": "intentkv session-memory scoring: 36 layers x 8 KV heads (32 query heads) x "
                             "65536 tokens x D128 bf16 in 16-token pages, memory update over a 64-query "
-                            "turn (decay 0.9), global top 8192 with 4 sink + 64 recent, dead-slot redirect",
-                "units": 1, "tokens_per_unit": cfg.N, "budget": cfg.k}
+                            "turn (decay 0.9), global top 8192 with 4 sink + 64 recent, alias-aware free list, "
+                            "dead-slot redirect",
+                "units": 1, "tokens_per_unit": cfg.N, "budget": cfg.k, "protected_prefix": cfg.n_sink}
 
     def extra(self):
         return {}

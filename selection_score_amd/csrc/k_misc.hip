@@ -121,68 +121,93 @@ __global__ __launch_bounds__(256) void memory_update_vec_kernel(int LH, int D, i
 }
 
 // ---- alias-aware free list (IntentKV §7): bitmaps over the slot ids of the
-// kept positions and of the freeable ones, then one workgroup lists the set
-// bits in ascending order.
+// kept positions and of the dropped ones, then one workgroup lists the slots
+// that are dropped and not kept in ascending order.
 __global__ void free_clear_kernel(uint32_t* bits, int64_t n_words) {
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   if (i < n_words) bits[i] = 0u;
 }
 
-__global__ void free_mark_kept_kernel(int64_t N, const int32_t* __restrict__ slot_map,
-                                      const uint8_t* __restrict__ keep, int64_t n_slots,
-                                      uint32_t* __restrict__ kept_bits) {
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (j >= N || keep[j] == 0) return;
-  const int64_t u = slot_map[j];
-  if (u >= 0 && u < n_slots) atomicOr(&kept_bits[u >> 5], 1u << (u & 31));
+// kept_bits: slots of kept positions; drop_bits: slots of dropped positions
+// outside the protected prefix, other than the dead slot.  A slot is freed
+// when it is in drop_bits and not in kept_bits.
+// Lanes whose slots share a bitmap word are merged into one atomicOr: the
+// leading active lane's word is OR-reduced over the wavefront, up to
+// kOrRounds distinct words; lanes left after that add their bit alone.
+// Every lane of the wavefront must take part.
+constexpr int kOrRounds = 8;
+__device__ __forceinline__ void wave_or_bit(uint32_t* bits, int64_t word, uint32_t bit, bool active) {
+  const int lane = threadIdx.x & 63;
+  uint64_t left = __ballot(active);
+  for (int round = 0; round < kOrRounds && left != 0ull; ++round) {
+    const int leader = __ffsll(static_cast<long long>(left)) - 1;
+    const int64_t w = __shfl(word, leader, 64);
+    const bool mine = active && word == w;
+    uint32_t m = mine ? bit : 0u;
+    for (int o = 1; o < 64; o <<= 1) m |= __shfl_xor(m, o, 64);
+    if (lane == leader) atomicOr(&bits[w], m);
+    left &= ~__ballot(mine);
+    if (mine) active = false;
+  }
+  if (active) atomicOr(&bits[word], bit);
 }
 
-__global__ void free_mark_kernel(int64_t N, const int32_t* __restrict__ slot_map,
-                                 const uint8_t* __restrict__ keep, int64_t dead, int64_t protected_len,
-                                 int64_t n_slots, const uint32_t* __restrict__ kept_bits,
-                                 uint32_t* __restrict__ free_bits) {
+__global__ __launch_bounds__(256) void free_mark_kernel(int64_t N, const int32_t* __restrict__ slot_map,
+                                                        const uint8_t* __restrict__ keep, int64_t dead,
+                                                        int64_t protected_len, int64_t n_slots,
+                                                        uint32_t* __restrict__ kept_bits,
+                                                        uint32_t* __restrict__ drop_bits) {
   const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (j >= N || j < protected_len || keep[j] != 0) return;
-  const int64_t u = slot_map[j];
-  if (u == dead || u < 0 || u >= n_slots) return;
+  const bool in = j < N;                            // every lane stays for the wavefront-wide merges
+  const int64_t u = in ? slot_map[j] : -1;
+  const bool valid = in && u >= 0 && u < n_slots;
+  const bool kept = valid && keep[j] != 0;
+  const bool dropped = valid && !kept && j >= protected_len && u != dead;
   const uint32_t bit = 1u << (u & 31);
-  if ((kept_bits[u >> 5] & bit) == 0u) atomicOr(&free_bits[u >> 5], bit);
+  wave_or_bit(kept_bits, u >> 5, bit, kept);
+  wave_or_bit(drop_bits, u >> 5, bit, dropped);
 }
 
-// One workgroup: thread t owns a contiguous run of bitmap words, so the
-// exclusive scan of the per-thread counts gives every set bit its place.
+// One workgroup: wavefront w owns a contiguous run of bitmap words.  The
+// wavefronts' counts give each run its first output index; each wavefront
+// then walks its words two at a time (lane l looks at bit l % 32 of word
+// l / 32) and stores the set bits' slot ids with a ballot prefix, so every
+// store instruction writes consecutive outputs.
 constexpr int kFreeThreads = 1024;
+constexpr int kFreeWaves = kFreeThreads / 64;
 __global__ __launch_bounds__(kFreeThreads) void free_compact_kernel(int64_t N, int64_t n_words,
-                                                                    const uint32_t* __restrict__ free_bits,
+                                                                    const uint32_t* __restrict__ kept_bits,
+                                                                    const uint32_t* __restrict__ drop_bits,
                                                                     int32_t* __restrict__ free_slots,
                                                                     int32_t* __restrict__ n_free) {
-  __shared__ uint32_t wave_tot[kFreeThreads / 64];
+  __shared__ uint32_t wave_tot[kFreeWaves];
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
-  const int64_t per = (n_words + kFreeThreads - 1) / kFreeThreads;
-  const int64_t w0 = min(n_words, static_cast<int64_t>(tid) * per);
+  const int64_t per = (n_words + kFreeWaves - 1) / kFreeWaves;
+  const int64_t w0 = min(n_words, static_cast<int64_t>(wave) * per);
   const int64_t w1 = min(n_words, w0 + per);
   uint32_t cnt = 0;
-  for (int64_t w = w0; w < w1; ++w) cnt += __popc(free_bits[w]);
-  // exclusive scan over the workgroup: within the wavefront, then across
-  uint32_t incl = cnt;
-  for (int o = 1; o < 64; o <<= 1) {
-    const uint32_t v = __shfl_up(incl, o, 64);
-    if (lane >= o) incl += v;
-  }
-  if (lane == 63) wave_tot[wave] = incl;
+  for (int64_t w = w0 + lane; w < w1; w += 64) cnt += __popc(drop_bits[w] & ~kept_bits[w]);
+  for (int o = 32; o > 0; o >>= 1) cnt += __shfl_xor(cnt, o, 64);
+  if (lane == 0) wave_tot[wave] = cnt;
   __syncthreads();
-  uint32_t base = incl - cnt, total = 0;
-  for (int w = 0; w < kFreeThreads / 64; ++w) {
+  uint32_t base = 0, total = 0;
+  for (int w = 0; w < kFreeWaves; ++w) {
     if (w < wave) base += wave_tot[w];
     total += wave_tot[w];
   }
-  uint32_t pos = base;
-  for (int64_t w = w0; w < w1; ++w) {
-    uint32_t b = free_bits[w];
-    while (b != 0u) {
-      const int i = __ffs(b) - 1;
-      free_slots[pos++] = static_cast<int32_t>(w * 32 + i);
-      b &= b - 1u;
+  const uint64_t lt = (lane == 0) ? 0ull : (~0ull >> (64 - lane));
+  for (int64_t c0 = w0; c0 < w1; c0 += 64) {
+    // 64 words in registers (one per lane), handed out two per step
+    const int64_t mine = c0 + lane;
+    const uint32_t word = (mine < w1) ? (drop_bits[mine] & ~kept_bits[mine]) : 0u;
+    const int steps = static_cast<int>((min(w1 - c0, static_cast<int64_t>(64)) + 1) / 2);
+    for (int t = 0; t < steps; ++t) {
+      const int src = 2 * t + (lane >> 5);
+      const uint32_t wv = __shfl(word, src, 64);            // word c0 + src (0 past w1)
+      const bool set = ((wv >> (lane & 31)) & 1u) != 0u;
+      const uint64_t b = __ballot(set);
+      if (set) free_slots[base + __popcll(b & lt)] = static_cast<int32_t>((c0 + src) * 32 + (lane & 31));
+      base += static_cast<uint32_t>(__popcll(b));
     }
   }
   for (int64_t i = static_cast<int64_t>(total) + tid; i < N; i += kFreeThreads) free_slots[i] = -1;
@@ -199,15 +224,14 @@ hipError_t launch_free_list(int64_t N, const int32_t* slot_map, const uint8_t* k
                             void* ws, hipStream_t st) {
   const int64_t words = (n_slots + 31) / 32;
   uint32_t* kept_bits = static_cast<uint32_t*>(ws);
-  uint32_t* free_bits = kept_bits + (words * 4 + 255) / 256 * 64;
-  const int64_t all_words = (free_bits - kept_bits) + words;   // both bitmaps, one clear
+  uint32_t* drop_bits = kept_bits + (words * 4 + 255) / 256 * 64;
+  const int64_t all_words = (drop_bits - kept_bits) + words;   // both bitmaps, one clear
   free_clear_kernel<<<static_cast<int>(ceil_div(all_words, 256)), 256, 0, st>>>(kept_bits, all_words);
   if (N > 0) {
-    const int g = static_cast<int>(ceil_div(N, 256));
-    free_mark_kept_kernel<<<g, 256, 0, st>>>(N, slot_map, keep, n_slots, kept_bits);
-    free_mark_kernel<<<g, 256, 0, st>>>(N, slot_map, keep, dead, protected_len, n_slots, kept_bits, free_bits);
+    free_mark_kernel<<<static_cast<int>(ceil_div(N, 256)), 256, 0, st>>>(N, slot_map, keep, dead, protected_len,
+                                                                        n_slots, kept_bits, drop_bits);
   }
-  free_compact_kernel<<<1, kFreeThreads, 0, st>>>(N, words, free_bits, free_slots, n_free);
+  free_compact_kernel<<<1, kFreeThreads, 0, st>>>(N, words, kept_bits, drop_bits, free_slots, n_free);
   return hipGetLastError();
 }
 

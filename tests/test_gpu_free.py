@@ -108,3 +108,19 @@ def test_free_list_after_select_then_redirect():
     np.testing.assert_array_equal(freed, want)
     assert not set(freed.tolist()) & set(after.tolist())
     assert len(freed) == N - 300 - int(mask.sum().item()) - 0   # every dropped live slot is distinct here
+
+
+def test_free_list_large_slot_space():
+    # more slot ids than the single-workgroup LDS bitmaps hold: the
+    # multi-launch path with bitmaps in the workspace
+    dev = require_gpu()
+    rng = np.random.default_rng(4)
+    N, n_slots = 20000, (1 << 20) + 77
+    dead = n_slots - 1
+    sm = rng.integers(0, n_slots - 1, size=N)
+    sm[rng.choice(N, 3000, replace=False)] = sm[rng.choice(N, 3000)]   # aliases
+    sm[rng.choice(N, 500, replace=False)] = dead
+    keep = rng.random(N) < 0.25
+    keep[sm == dead] = False
+    got, nf, _ = _run(dev, sm, keep, dead, n_slots, protected_len=100)
+    _check(got, nf, om.free_list(sm, keep, dead, 100), N)
