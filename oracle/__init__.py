@@ -55,5 +55,8 @@ PIN_STATUS = {
     "materialise.redirect": "pinned (invariants: kept bitwise, dropped -> dead, idempotent, one-way)",
     "materialise.free_list": "pinned (hand-worked slot maps with aliases, prior redirects and a "
                              "protected prefix; reusing freed slots never changes a kept or sibling read)",
+    "materialise.tail_compact": "pinned (hand-worked plan; kept (position, K, V) multiset preserved; "
+                                "sources and destinations disjoint; freed count Y - X); the pairing "
+                                "order is a reading (the page's formula is lost)",
     "materialise.decode_attention_*": "pinned (dead-slot closed form in both sign regimes)",
 }

@@ -125,6 +125,55 @@ def free_list(slot_map, keep_mask, dead_slot, protected_len=0):
     return np.array(sorted(freed), dtype=np.int64)
 
 
+def tail_compact(keep_mask, block_table, block_size, k_pool, v_pool):
+    """In-place compaction of one request's paged KV into its tail blocks
+    (ActKV §7.2, conflict-free slot planning; Algorithm 4).
+
+    The request holds Y logical blocks (block_table[y] is the physical block
+    of logical block y) and N = len(keep_mask) <= Y * block_size positions.
+    With K kept positions, the target region is the last X = ceil(K / bs)
+    logical blocks, starting at slot t0 = (Y - X) * bs.  Sources are the kept
+    positions before t0, destinations the slots from t0 on that hold no kept
+    entry (dropped positions, or empty slots past N), both in ascending order;
+    the i-th source moves to the i-th destination.  Sources and destinations
+    are disjoint, so one pass of copies suffices.
+
+    k_pool, v_pool: [pool_blocks][bs][...] arrays, not modified.  Returns
+    (k_pool', v_pool', slot_pos, freed): the pools after the copies;
+    slot_pos [Y * bs] = the original logical position each slot holds
+    afterwards (-1 for empty slots and for the freed blocks); freed = the
+    physical blocks of logical blocks [0, Y - X), in order.
+    """
+    keep = np.asarray(keep_mask, dtype=bool)
+    bt = np.asarray(block_table, dtype=np.int64)
+    bs = int(block_size)
+    Y, N = bt.shape[0], keep.shape[0]
+    assert N <= Y * bs
+    n_kept = int(keep.sum())
+    X = -(-n_kept // bs)
+    t0 = (Y - X) * bs
+    kept_slot = np.zeros(Y * bs, dtype=bool)
+    kept_slot[:N] = keep
+    sources = [p for p in range(min(t0, N)) if keep[p]]
+    dests = [s for s in range(t0, Y * bs) if not kept_slot[s]]
+    assert len(dests) >= len(sources)
+    kp, vp = np.array(k_pool, copy=True), np.array(v_pool, copy=True)
+
+    def phys(s):
+        return bt[s // bs], s % bs
+
+    slot_pos = np.full(Y * bs, -1, dtype=np.int64)
+    for s in range(t0, Y * bs):
+        if kept_slot[s]:
+            slot_pos[s] = s
+    for src, dst in zip(sources, dests):
+        (bs_, os_), (bd, od) = phys(src), phys(dst)
+        kp[bd, od] = k_pool[bs_, os_]
+        vp[bd, od] = v_pool[bs_, os_]
+        slot_pos[dst] = src
+    return kp, vp, slot_pos, bt[: Y - X].copy()
+
+
 def sentinel_rows(dtype, D):
     """K and V rows of the dead slot (IntentKV §2 Q2): K = -1e4, V = 0,
     each rounded once to the pool's storage format ("bf16" or "f16")."""

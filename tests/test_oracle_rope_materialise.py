@@ -261,3 +261,53 @@ def test_reusing_freed_slots_never_changes_a_kept_or_sibling_read():
     # and every slot that only dropped, unprotected positions referenced is freed
     only_dropped = set(sm0[P:][~keep0[P:]].tolist()) - set(sm0[keep0].tolist()) - {dead}
     assert set(freed.tolist()) == only_dropped
+
+
+# ---------------------------------------------------------------- tail compaction
+
+def test_tail_compact_hand_example():
+    # bs = 4, Y = 4 blocks (physical 7, 2, 9, 5), N = 14 positions, 6 kept:
+    # X = ceil(6/4) = 2, target = logical blocks 2..3 = slots 8..15.
+    # kept 0, 3, 6 (sources), 9, 10, 13 (stay); destinations: 8, 11, 12
+    # (14, 15 are empty slots past N and remain unused).
+    keep = np.zeros(14, bool); keep[[0, 3, 6, 9, 10, 13]] = True
+    bt = [7, 2, 9, 5]
+    pool_k = np.arange(10 * 4, dtype=np.float64).reshape(10, 4, 1)
+    pool_v = -pool_k
+    kp, vp, slot_pos, freed = om.tail_compact(keep, bt, 4, pool_k, pool_v)
+    np.testing.assert_array_equal(freed, [7, 2])
+    want_pos = [-1] * 8 + [0, 9, 10, 3, 6, 13, -1, -1]
+    np.testing.assert_array_equal(slot_pos, want_pos)
+    # slot 8 = physical (9, 0) now holds position 0 = physical (7, 0); slot 11 =
+    # (9, 3) holds position 3 = (7, 3); slot 12 = (5, 0) holds position 6 = (2, 2)
+    assert kp[9, 0, 0] == pool_k[7, 0, 0] and kp[9, 3, 0] == pool_k[7, 3, 0]
+    assert kp[5, 0, 0] == pool_k[2, 2, 0] and vp[5, 0, 0] == pool_v[2, 2, 0]
+    # everything else is untouched
+    changed = np.argwhere(kp[..., 0] != pool_k[..., 0])
+    assert sorted(map(tuple, changed)) == [(5, 0), (9, 0), (9, 3)]
+
+
+@pytest.mark.parametrize("seed", [0, 1, 2])
+def test_tail_compact_preserves_kept_entries(seed):
+    rng = np.random.default_rng(seed)
+    bs, Y = 16, 24
+    N = Y * bs - rng.integers(0, bs)
+    keep = rng.random(N) < rng.uniform(0.2, 0.9)
+    keep[-16:] = True                                   # recent entries forced, as a selection would
+    P = 64
+    bt = rng.permutation(P)[:Y]
+    pool_k = rng.standard_normal((P, bs, 3)); pool_v = rng.standard_normal((P, bs, 3))
+    kp, vp, slot_pos, freed = om.tail_compact(keep, bt, bs, pool_k, pool_v)
+    n_kept = int(keep.sum()); X = -(-n_kept // bs)
+    assert len(freed) == Y - X and set(freed) == set(bt[: Y - X])
+    # the multiset of kept (position, K, V) equals what the target region holds
+    held = slot_pos[slot_pos >= 0]
+    assert sorted(held.tolist()) == np.flatnonzero(keep).tolist()
+    assert np.all(slot_pos[: (Y - X) * bs] == -1)
+    for s in np.flatnonzero(slot_pos >= 0):
+        p = slot_pos[s]
+        np.testing.assert_array_equal(kp[bt[s // bs], s % bs], pool_k[bt[p // bs], p % bs])
+        np.testing.assert_array_equal(vp[bt[s // bs], s % bs], pool_v[bt[p // bs], p % bs])
+    # blocks outside the request are untouched
+    others = np.setdiff1d(np.arange(P), bt)
+    np.testing.assert_array_equal(kp[others], pool_k[others])
