@@ -341,6 +341,56 @@ kvsel_status kvsel_free_list_workspace(const kvsel_freelist_args* args, size_t* 
 kvsel_status kvsel_free_list(const kvsel_freelist_args* args, void* workspace, size_t workspace_bytes,
                              void* stream);
 
+/* ------------------------------------------------------------------ compaction
+ *
+ * ActKV §7.2 (conflict-free slot planning) and Algorithm 4 (in-place
+ * compaction): after eviction, each request's kept entries move into its last
+ * X = ceil(kept / block_size) logical blocks, and the blocks before them are
+ * returned.  Slots are planned first: the i-th kept position before the
+ * target region (ascending) goes to the i-th slot of the region that holds
+ * no kept entry (ascending; slots past N count as empty).  Sources and
+ * destinations are disjoint physical slots, so every copy runs in one pass
+ * with no buffer for KV.  (The page's formula for the region is lost; this is
+ * the reading used.)
+ *
+ *   keep_mask    [R][N] u8 (1 = kept)
+ *   block_table  [R][Y] int32: physical block of each logical block; a
+ *                request's blocks must be distinct and not shared with other
+ *                requests (entries outside [0, pool_blocks) are not copied)
+ *   k_pool/v_pool [L][pool_blocks][block_size][Hkv][D] of dtype, in place
+ *   slot_pos     out [R][Y * block_size] int32: the original logical position
+ *                each slot holds afterwards, -1 for empty slots and for the
+ *                freed blocks
+ *   freed_blocks out [R][Y] int32: physical blocks of logical blocks
+ *                [0, Y - X) in order, then -1; n_freed out [R] = Y - X
+ * Requirements: 0 <= N <= Y * block_size, Hkv * D * element size a multiple
+ * of 16 bytes, pools 16-byte aligned.  Workspace: kvsel_compact_workspace.
+ * Errors: E_ARG, E_WORKSPACE, E_DEVICE.  R = 0 or Y = 0 is a no-op.
+ */
+typedef struct kvsel_compact_args {
+  uint32_t struct_size;
+  int32_t R;
+  int32_t L, Hkv, D;
+  int32_t dtype;              /* BF16, F16 or F32 */
+  int32_t block_size;
+  int32_t Y;                  /* logical blocks per request */
+  int32_t reserved;           /* 0 */
+  int64_t N;                  /* positions per request */
+  int64_t pool_blocks;        /* physical blocks per layer */
+  const uint8_t* keep_mask;
+  const int32_t* block_table;
+  void* k_pool;
+  void* v_pool;
+  int32_t* slot_pos;
+  int32_t* freed_blocks;
+  int32_t* n_freed;
+} kvsel_compact_args;
+
+kvsel_status kvsel_compact_workspace(const kvsel_compact_args* args, size_t* bytes);
+
+kvsel_status kvsel_compact(const kvsel_compact_args* args, void* workspace, size_t workspace_bytes,
+                           void* stream);
+
 /* ------------------------------------------------------------------ index
  *
  * KVMem (query-conditioned retrieval paragraph): the block scorer reads one

@@ -95,10 +95,19 @@ class FreeListArgs(ctypes.Structure):
     ]
 
 
+class CompactArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("R", c_i32), ("L", c_i32), ("Hkv", c_i32), ("D", c_i32), ("dtype", c_i32),
+        ("block_size", c_i32), ("Y", c_i32), ("reserved", c_i32), ("N", c_i64), ("pool_blocks", c_i64),
+        ("keep_mask", c_vp), ("block_table", c_vp), ("k_pool", c_vp), ("v_pool", c_vp), ("slot_pos", c_vp),
+        ("freed_blocks", c_vp), ("n_freed", c_vp),
+    ]
+
+
 EXPORTS = ["kvsel_version", "kvsel_last_error", "kvsel_score_workspace", "kvsel_score",
            "kvsel_select_workspace", "kvsel_select", "kvsel_gather_workspace", "kvsel_gather_rerope",
            "kvsel_redirect", "kvsel_memory_update", "kvsel_build_index", "kvsel_free_list_workspace",
-           "kvsel_free_list"]
+           "kvsel_free_list", "kvsel_compact_workspace", "kvsel_compact"]
 
 _lib = None
 
@@ -128,6 +137,8 @@ def load(path=LIB_PATH):
     lib.kvsel_build_index.argtypes = [P(IndexArgs), c_vp]
     lib.kvsel_free_list_workspace.argtypes = [P(FreeListArgs), P(ctypes.c_size_t)]
     lib.kvsel_free_list.argtypes = [P(FreeListArgs), c_vp, ctypes.c_size_t, c_vp]
+    lib.kvsel_compact_workspace.argtypes = [P(CompactArgs), P(ctypes.c_size_t)]
+    lib.kvsel_compact.argtypes = [P(CompactArgs), c_vp, ctypes.c_size_t, c_vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = c_i32
     _lib = lib

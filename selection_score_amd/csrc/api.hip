@@ -455,6 +455,65 @@ kvsel_status kvsel_redirect(const kvsel_redirect_args* a, void* stream) {
 
 // ------------------------------------------------------------------ memory
 
+static kvsel_status check_compact(const kvsel_compact_args* a, CompactParams* p) {
+  if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+  if (a->struct_size < sizeof(kvsel_compact_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->R < 0 || a->Y < 0) return fail(KVSEL_E_ARG, "R and Y must be >= 0");
+  if (a->L < 1 || a->Hkv < 1 || a->D < 1 || a->block_size < 1 || a->pool_blocks < 1)
+    return fail(KVSEL_E_ARG, "L, Hkv, D, block_size and pool_blocks must be >= 1");
+  if (!valid_dtype(a->dtype)) return fail(KVSEL_E_ARG, "bad dtype");
+  const int64_t slots = static_cast<int64_t>(a->Y) * a->block_size;
+  if (slots > kMaxN) return fail(KVSEL_E_ARG, "Y * block_size must be below 2^31");
+  if (a->N < 0 || a->N > slots) return fail(KVSEL_E_ARG, "N must be in [0, Y * block_size]");
+  const int esz = (a->dtype == KVSEL_F32) ? 4 : 2;
+  if ((static_cast<int64_t>(a->Hkv) * a->D * esz) % 16 != 0)
+    return fail(KVSEL_E_ARG, "Hkv * D * element size must be a multiple of 16 bytes");
+  if (a->R > 0 && a->Y > 0) {
+    if (a->keep_mask == nullptr || a->block_table == nullptr || a->k_pool == nullptr || a->v_pool == nullptr ||
+        a->slot_pos == nullptr || a->freed_blocks == nullptr || a->n_freed == nullptr)
+      return fail(KVSEL_E_ARG, "a pointer is NULL");
+    if (!aligned16(a->k_pool) || !aligned16(a->v_pool)) return fail(KVSEL_E_ARG, "pools must be 16-byte aligned");
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(a->block_table) | reinterpret_cast<uintptr_t>(a->slot_pos) |
+                          reinterpret_cast<uintptr_t>(a->freed_blocks) | reinterpret_cast<uintptr_t>(a->n_freed);
+    if ((mis & 3u) != 0) return fail(KVSEL_E_ARG, "int32 arrays must be 4-byte aligned");
+  }
+  p->R = a->R; p->L = a->L; p->Hkv = a->Hkv; p->D = a->D; p->dtype = a->dtype;
+  p->block_size = a->block_size; p->Y = a->Y; p->N = a->N; p->pool_blocks = a->pool_blocks;
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_compact_workspace(const kvsel_compact_args* a, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return fail(KVSEL_E_ARG, "bytes is NULL");
+    CompactParams p;
+    kvsel_status s = check_compact(a, &p);
+    if (s != KVSEL_OK) return s;
+    *bytes = compact_workspace_bytes(p);
+    return KVSEL_OK;
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+kvsel_status kvsel_compact(const kvsel_compact_args* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    CompactParams p;
+    kvsel_status s = check_compact(a, &p);
+    if (s != KVSEL_OK) return s;
+    if (p.R == 0 || p.Y == 0) return KVSEL_OK;
+    const size_t need = compact_workspace_bytes(p);
+    if (ws == nullptr || ws_bytes < need) return fail(KVSEL_E_WORKSPACE, "workspace too small (see kvsel_compact_workspace)");
+    if (!aligned16(ws)) return fail(KVSEL_E_ARG, "workspace must be 16-byte aligned");
+    if ((s = check_device()) != KVSEL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish(launch_compact(p, a->keep_mask, a->block_table, a->k_pool, a->v_pool, a->slot_pos,
+                                 a->freed_blocks, a->n_freed, ws, st),
+                  st, "compaction");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
 static kvsel_status check_free_list(const kvsel_freelist_args* a) {
   if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
   if (a->struct_size < sizeof(kvsel_freelist_args)) return fail(KVSEL_E_ARG, "struct_size too small");

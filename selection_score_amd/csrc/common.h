@@ -179,6 +179,15 @@ size_t free_list_workspace_bytes(int64_t n_slots);
 hipError_t launch_free_list(int64_t N, const int32_t* slot_map, const uint8_t* keep, int64_t dead,
                             int64_t protected_len, int64_t n_slots, int32_t* free_slots, int32_t* n_free,
                             void* ws, hipStream_t st);
+struct CompactParams {
+  int R, L, Hkv, D, dtype, block_size, Y;
+  int64_t N, pool_blocks;
+};
+size_t compact_workspace_bytes(const CompactParams& p);
+hipError_t launch_compact(const CompactParams& p, const uint8_t* keep, const int32_t* block_table, void* k_pool,
+                          void* v_pool, int32_t* slot_pos, int32_t* freed_blocks, int32_t* n_freed, void* ws,
+                          hipStream_t st);
+
 hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, int64_t dead,
                            hipStream_t st);
 hipError_t launch_sentinel(void* k_pool, void* v_pool, int L, int Hkv, int D, int dtype,

@@ -1,0 +1,185 @@
+// In-place tail compaction of paged KV.
+//
+// ActKV §7.2 and Algorithm 4: after eviction the kept entries of a request
+// move into its last X = ceil(kept / block_size) logical blocks, so the
+// blocks before them can be returned.  The slots are planned first: sources
+// are the kept positions before the target region, destinations the slots
+// of the region that hold no kept entry, both in ascending order and paired
+// by rank.  Sources and destinations are disjoint, so all copies run in one
+// pass without a buffer for KV.
+//
+// compact_plan_kernel: one workgroup per request.  Wavefront w owns a
+// contiguous segment of the request's slots; a counting sweep gives each
+// segment its first source and destination rank, a second sweep lists them
+// with ballot prefixes.  compact_copy_kernel: every wavefront moves whole
+// slots (Hkv * D elements of K and of V per layer) for its share of the
+// (request, pair, layer) copies.
+#include "common.h"
+
+namespace kvsel {
+
+namespace {
+
+constexpr int kPlanThreads = 1024;
+constexpr int kPlanWaves = kPlanThreads / 64;
+
+struct CompactWs {
+  int32_t* src;     // [R][Y * block_size] source slots by rank
+  int32_t* dst;     // [R][Y * block_size] destination slots by rank
+  int32_t* n_pairs; // [R]
+};
+
+CompactWs compact_ws(const CompactParams& p, void* ws) {
+  const int64_t slots = static_cast<int64_t>(p.Y) * p.block_size;
+  const int64_t list = (static_cast<int64_t>(p.R) * slots * 4 + 255) / 256 * 256;
+  uint8_t* b = static_cast<uint8_t*>(ws);
+  return CompactWs{reinterpret_cast<int32_t*>(b), reinterpret_cast<int32_t*>(b + list),
+                   reinterpret_cast<int32_t*>(b + 2 * list)};
+}
+
+__device__ __forceinline__ uint64_t lanes_below(int lane) { return lane == 0 ? 0ull : (~0ull >> (64 - lane)); }
+
+}  // namespace
+
+__global__ __launch_bounds__(kPlanThreads) void compact_plan_kernel(CompactParams p, const uint8_t* __restrict__ keep,
+                                                                    const int32_t* __restrict__ block_table,
+                                                                    int32_t* __restrict__ slot_pos,
+                                                                    int32_t* __restrict__ freed_blocks,
+                                                                    int32_t* __restrict__ n_freed, CompactWs w) {
+  __shared__ uint32_t wave_src[kPlanWaves], wave_dst[kPlanWaves], wave_kept[kPlanWaves];
+  const int r = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int64_t slots = static_cast<int64_t>(p.Y) * p.block_size;
+  const uint8_t* kr = keep + static_cast<int64_t>(r) * p.N;
+  auto kept_at = [&](int64_t s) { return s < p.N && kr[s] != 0; };
+  // kept count of the request: each wavefront counts its own segment
+  const int64_t seg = ((slots + kPlanWaves - 1) / kPlanWaves + 63) / 64 * 64;
+  const int64_t s_beg = min(slots, static_cast<int64_t>(wave) * seg);
+  const int64_t s_end = min(slots, s_beg + seg);
+  uint32_t nk = 0;
+  for (int64_t s0 = s_beg; s0 < s_end; s0 += 64) {
+    const int64_t s = s0 + lane;
+    nk += __popcll(__ballot(s < s_end && kept_at(s)));
+  }
+  if (lane == 0) wave_kept[wave] = nk;
+  __syncthreads();
+  int64_t kept = 0;
+  for (int i = 0; i < kPlanWaves; ++i) kept += wave_kept[i];
+  const int64_t X = (kept + p.block_size - 1) / p.block_size;
+  const int64_t t0 = (static_cast<int64_t>(p.Y) - X) * p.block_size;
+  // counting sweep: sources (kept, before t0) and destinations (no kept entry, from t0)
+  uint32_t ns = 0, nd = 0;
+  for (int64_t s0 = s_beg; s0 < s_end; s0 += 64) {
+    const int64_t s = s0 + lane;
+    const bool in = s < s_end;
+    const bool k = in && kept_at(s);
+    ns += __popcll(__ballot(in && s < t0 && k));
+    nd += __popcll(__ballot(in && s >= t0 && !k));
+  }
+  if (lane == 0) {
+    wave_src[wave] = ns;
+    wave_dst[wave] = nd;
+  }
+  __syncthreads();
+  uint32_t src_base = 0, dst_base = 0, m = 0;
+  for (int i = 0; i < kPlanWaves; ++i) {
+    if (i < wave) {
+      src_base += wave_src[i];
+      dst_base += wave_dst[i];
+    }
+    m += wave_src[i];                              // pairs = sources (destinations are at least as many)
+  }
+  // listing sweep
+  int32_t* src = w.src + static_cast<int64_t>(r) * slots;
+  int32_t* dst = w.dst + static_cast<int64_t>(r) * slots;
+  int32_t* pos = slot_pos + static_cast<int64_t>(r) * slots;
+  const uint64_t lt = lanes_below(lane);
+  for (int64_t s0 = s_beg; s0 < s_end; s0 += 64) {
+    const int64_t s = s0 + lane;
+    const bool in = s < s_end;
+    const bool k = in && kept_at(s);
+    const bool is_src = in && s < t0 && k;
+    const bool is_dst = in && s >= t0 && !k;
+    const uint64_t bs_ = __ballot(is_src), bd = __ballot(is_dst);
+    if (is_src) src[src_base + __popcll(bs_ & lt)] = static_cast<int32_t>(s);
+    if (is_dst) {
+      const uint32_t rank = dst_base + __popcll(bd & lt);
+      if (rank < m) dst[rank] = static_cast<int32_t>(s);
+    }
+    // after the copies: a kept slot of the region holds itself; the paired
+    // destinations are filled in by the copy kernel
+    if (in) pos[s] = (s >= t0 && k) ? static_cast<int32_t>(s) : -1;
+    src_base += __popcll(bs_);
+    dst_base += __popcll(bd);
+  }
+  // freed blocks and counts
+  const int32_t* btr = block_table + static_cast<int64_t>(r) * p.Y;
+  int32_t* fr = freed_blocks + static_cast<int64_t>(r) * p.Y;
+  const int64_t n_free = static_cast<int64_t>(p.Y) - X;
+  for (int64_t y = tid; y < p.Y; y += kPlanThreads) fr[y] = (y < n_free) ? btr[y] : -1;
+  if (tid == 0) {
+    n_freed[r] = static_cast<int32_t>(n_free);
+    w.n_pairs[r] = static_cast<int32_t>(m);
+  }
+}
+
+template <int ESZ>
+__global__ __launch_bounds__(256) void compact_copy_kernel(CompactParams p, const int32_t* __restrict__ block_table,
+                                                           uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
+                                                           int32_t* __restrict__ slot_pos, CompactWs w) {
+  const int r = blockIdx.y;
+  const int lane = threadIdx.x & 63;
+  const int64_t slots = static_cast<int64_t>(p.Y) * p.block_size;
+  const int32_t m = w.n_pairs[r];
+  const int64_t row = static_cast<int64_t>(p.Hkv) * p.D * ESZ;           // bytes of one slot per layer
+  const int pieces = static_cast<int>(row / 16);
+  const int64_t items = static_cast<int64_t>(m) * p.L;                 // (pair, layer)
+  const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
+  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
+  const int32_t* src = w.src + static_cast<int64_t>(r) * slots;
+  const int32_t* dst = w.dst + static_cast<int64_t>(r) * slots;
+  const int32_t* btr = block_table + static_cast<int64_t>(r) * p.Y;
+  for (int64_t it = wave_global; it < items; it += n_waves) {
+    const int64_t i = it / p.L;
+    const int l = static_cast<int>(it - i * p.L);
+    const int32_t s = src[i], d = dst[i];
+    const int64_t bs = btr[s / p.block_size], bd = btr[d / p.block_size];
+    if (bs < 0 || bs >= p.pool_blocks || bd < 0 || bd >= p.pool_blocks) continue;
+    const int64_t so = ((static_cast<int64_t>(l) * p.pool_blocks + bs) * p.block_size + s % p.block_size) * row;
+    const int64_t dof = ((static_cast<int64_t>(l) * p.pool_blocks + bd) * p.block_size + d % p.block_size) * row;
+    for (int c = lane; c < pieces; c += 64) {
+      const uint4 kv = *reinterpret_cast<const uint4*>(k_pool + so + 16 * c);
+      const uint4 vv = *reinterpret_cast<const uint4*>(v_pool + so + 16 * c);
+      store16_stream(k_pool + dof + 16 * c, kv);
+      store16_stream(v_pool + dof + 16 * c, vv);
+    }
+    if (l == 0 && lane == 0) slot_pos[static_cast<int64_t>(r) * slots + d] = s;
+  }
+}
+
+size_t compact_workspace_bytes(const CompactParams& p) {
+  const int64_t slots = static_cast<int64_t>(p.Y) * p.block_size;
+  const int64_t list = (static_cast<int64_t>(p.R) * slots * 4 + 255) / 256 * 256;
+  return static_cast<size_t>(2 * list + (static_cast<int64_t>(p.R) * 4 + 255) / 256 * 256);
+}
+
+hipError_t launch_compact(const CompactParams& p, const uint8_t* keep, const int32_t* block_table, void* k_pool,
+                          void* v_pool, int32_t* slot_pos, int32_t* freed_blocks, int32_t* n_freed, void* ws,
+                          hipStream_t st) {
+  if (p.R == 0 || p.Y == 0) return hipSuccess;
+  const CompactWs w = compact_ws(p, ws);
+  compact_plan_kernel<<<p.R, kPlanThreads, 0, st>>>(p, keep, block_table, slot_pos, freed_blocks, n_freed, w);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  // enough wavefronts for the largest possible plan of a request
+  const int64_t max_items = static_cast<int64_t>(p.Y) * p.block_size * p.L;
+  const int64_t bx = ceil_div(max_items, 4 * 4);   // about four (pair, layer) copies per wavefront
+  dim3 grid(static_cast<unsigned>(bx < 1 ? 1 : (bx > 4096 ? 4096 : bx)), p.R);
+  uint8_t* kp = static_cast<uint8_t*>(k_pool);
+  uint8_t* vp = static_cast<uint8_t*>(v_pool);
+  if (p.dtype == KVSEL_F32) compact_copy_kernel<4><<<grid, 256, 0, st>>>(p, block_table, kp, vp, slot_pos, w);
+  else compact_copy_kernel<2><<<grid, 256, 0, st>>>(p, block_table, kp, vp, slot_pos, w);
+  return hipGetLastError();
+}
+
+}  // namespace kvsel

@@ -295,3 +295,28 @@ def free_list(slot_map, keep_mask, dead_slot, free_slots, n_free, *, n_slots, pr
     ws, wsz = _workspace(nb.value, slot_map.device, workspace)
     _check(lib.kvsel_free_list(ctypes.byref(a), _ptr(ws), wsz, _stream(stream)))
     return ws
+
+
+def compact(keep_mask, block_table, k_pool, v_pool, slot_pos, freed_blocks, n_freed, *, block_size,
+            workspace=None, stream=None):
+    """kvsel_compact.  keep_mask [R][N] uint8; block_table [R][Y] int32;
+    k_pool, v_pool [L][pool_blocks][block_size][Hkv][D] (in place); slot_pos
+    [R][Y*block_size], freed_blocks [R][Y], n_freed [R] int32 are written.
+    Returns the workspace it used."""
+    R, N = keep_mask.shape
+    Y = block_table.shape[1]
+    L, P, bs, Hkv, D = k_pool.shape
+    if bs != block_size:
+        raise ValueError("k_pool's block dimension must equal block_size")
+    a = _abi.CompactArgs()
+    a.struct_size = ctypes.sizeof(_abi.CompactArgs)
+    a.R, a.L, a.Hkv, a.D, a.dtype, a.block_size, a.Y = R, L, Hkv, D, _dtype(k_pool), block_size, Y
+    a.N, a.pool_blocks = N, P
+    a.keep_mask, a.block_table, a.k_pool, a.v_pool = _ptr(keep_mask), _ptr(block_table), _ptr(k_pool), _ptr(v_pool)
+    a.slot_pos, a.freed_blocks, a.n_freed = _ptr(slot_pos), _ptr(freed_blocks), _ptr(n_freed)
+    lib = _abi.load()
+    nb = ctypes.c_size_t(0)
+    _check(lib.kvsel_compact_workspace(ctypes.byref(a), ctypes.byref(nb)))
+    ws, wsz = _workspace(nb.value, k_pool.device, workspace)
+    _check(lib.kvsel_compact(ctypes.byref(a), _ptr(ws), wsz, _stream(stream)))
+    return ws

@@ -38,6 +38,7 @@ STRUCTS = {
     "kvsel_memupd_args": _abi.MemUpdArgs,
     "kvsel_index_args": _abi.IndexArgs,
     "kvsel_freelist_args": _abi.FreeListArgs,
+    "kvsel_compact_args": _abi.CompactArgs,
 }
 
 
@@ -197,3 +198,27 @@ def test_free_list_validation_without_device():
         setattr(a, field, bad)
         assert lib.kvsel_free_list_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_E_ARG, field
         a.N, a.slot_map, a.n_free, a.n_slots, a.protected_len = 100, 0x1000, 0x4000, 64, 0
+
+
+def test_compact_validation_without_device():
+    lib = _abi.load()
+    a = _abi.CompactArgs()
+    a.struct_size = ctypes.sizeof(a)
+    a.R, a.L, a.Hkv, a.D, a.dtype, a.block_size, a.Y = 2, 3, 8, 128, _abi.BF16, 16, 10
+    a.N, a.pool_blocks = 150, 64
+    a.keep_mask, a.block_table, a.k_pool, a.v_pool = 0x1000, 0x2000, 0x3000, 0x4000
+    a.slot_pos, a.freed_blocks, a.n_freed = 0x5000, 0x6000, 0x7000
+    nb = ctypes.c_size_t(0)
+    assert lib.kvsel_compact_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_OK
+    assert nb.value >= 2 * 2 * 160 * 4                 # source and destination lists
+    assert lib.kvsel_compact(ctypes.byref(a), None, 0, None) == _abi.KVSEL_E_WORKSPACE
+    a.Hkv, a.D = 1, 3                                   # 6-byte slot rows cannot move as 16-byte pieces
+    assert lib.kvsel_compact_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    a.Hkv, a.D = 8, 128
+    for field, bad in [("N", 161), ("block_size", 0), ("k_pool", 0x3008), ("slot_pos", 0x5002)]:
+        good = getattr(a, field)
+        setattr(a, field, bad)
+        assert lib.kvsel_compact_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_E_ARG, field
+        setattr(a, field, good)
+    a.R = 0
+    assert lib.kvsel_compact(ctypes.byref(a), None, 0, None) == _abi.KVSEL_OK
