@@ -18,7 +18,8 @@ is that kernel's launch duration.
 --workload picks another workload: intentkv (session memory over a paged pool
 with the dead-slot redirect), kvmem1m (1M-token block retrieval and re-RoPE
 gather), kvmem10m (10M-token tiled retrieval and the incremental view
-update), meank1m (building the Mean-K index of the 1M-token workspace).
+update), meank1m (building the Mean-K index of the 1M-token workspace),
+actkv (ActKV's in-place tail compaction of paged KV, Table 1's shape).
 
 Other modes:
   --copy-calib         a plain elementwise copy of 1 GiB (5 launches), to scale
@@ -61,6 +62,8 @@ KERNEL_SOURCES = {
     "memory_update_kernel": "k_misc.hip", "memory_update_vec_kernel": "k_misc.hip",
     "redirect_kernel": "k_misc.hip", "sentinel_kernel": "k_misc.hip",
     "mean_k_kernel": "k_index.hip",
+    "free_clear_kernel": "k_misc.hip", "free_mark_kernel": "k_misc.hip", "free_compact_kernel": "k_misc.hip",
+    "compact_plan_kernel": "k_compact.hip", "compact_copy_kernel": "k_compact.hip",
 }
 
 
@@ -72,7 +75,7 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample for the CPU baseline")
-    ap.add_argument("--workload", default="snapkv", choices=["snapkv", "intentkv", "kvmem1m", "kvmem10m", "meank1m"],
+    ap.add_argument("--workload", default="snapkv", choices=["snapkv", "intentkv", "kvmem1m", "kvmem10m", "meank1m", "actkv"],
                     help="which workload one step runs (the default line is snapkv)")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -585,7 +588,63 @@ class MeanK1M:
         return {}
 
 
-WORKLOADS = {"snapkv": SnapKV, "intentkv": IntentKV, "kvmem1m": KVMem1M, "kvmem10m": KVMem10M, "meank1m": MeanK1M}
+class ActKVCompact:
+    """ActKV's in-place tail compaction with Table 1's shape: 64 requests of
+    6144 positions in 16-slot blocks, 4096 kept each, moved into their last
+    256 blocks for 36 layers of 8 KV heads (D 128, bf16).  The copies write
+    the pools in place; repeating the step on the same masks repeats the
+    same moves, so every step does the same work."""
+    stages = ["compact"]
+    kernels = {}
+    launches = {"compact": 2}
+    score_stage = "compact"
+    materialise_stages = ["compact"]
+    dtype = "bf16"
+
+    def __init__(self, torch, kv, wl, dev):
+        self.kv, self.cfg = kv, wl.CONFIGS["actkv"]
+        cfg = self.cfg
+        self.inp = wl.actkv_inputs(cfg, dev)
+        R, bs = cfg.S, cfg.page_size
+        Y = self.inp["block_table"].shape[1]
+        self.slot_pos = torch.empty((R, Y * bs), dtype=torch.int32, device=dev)
+        self.freed = torch.empty((R, Y), dtype=torch.int32, device=dev)
+        self.n_freed = torch.empty(R, dtype=torch.int32, device=dev)
+        self.ws = None
+        keep = self.inp["keep"].bool()
+        X = (keep.sum(dim=1) + bs - 1) // bs
+        t0 = (Y - X) * bs
+        pos = torch.arange(cfg.N, device=dev)[None]
+        self.pairs = int((keep & (pos < t0[:, None])).sum())      # one (source, destination) copy each
+        self.tokens = R * cfg.N * cfg.L * cfg.Hkv
+
+    def step(self, ev, stream, it):
+        inp, cfg = self.inp, self.cfg
+        ev[0].record(stream)
+        self.ws = self.kv.compact(inp["keep"], inp["block_table"], inp["k_pool"], inp["v_pool"], self.slot_pos,
+                                  self.freed, self.n_freed, block_size=cfg.page_size, workspace=self.ws)
+        ev[1].record(stream)
+
+    def algo_bytes(self):
+        cfg = self.cfg
+        R, N, bs = cfg.S, cfg.N, cfg.page_size
+        Y = self.inp["block_table"].shape[1]
+        row = cfg.Hkv * cfg.D * 2
+        moves = self.pairs * cfg.L * 2 * 2 * row                  # K and V, read and written
+        return {"compact": moves + R * N + R * Y * 4 + R * Y * bs * 4 + R * Y * 4}
+
+    def config(self):
+        cfg = self.cfg
+        return {"workload": "actkv in-place tail compaction: 64 requests x 6144 positions in 16-slot blocks -> "
+                            "4096 kept, 36 layers x 8 KV heads x D128 bf16 paged pools",
+                "requests": cfg.S, "positions": cfg.N, "kept": cfg.k, "block_size": cfg.page_size}
+
+    def extra(self):
+        return {"moved_entries": self.pairs}
+
+
+WORKLOADS = {"snapkv": SnapKV, "intentkv": IntentKV, "kvmem1m": KVMem1M, "kvmem10m": KVMem10M, "meank1m": MeanK1M,
+             "actkv": ActKVCompact}
 
 
 def main():

@@ -12,8 +12,8 @@
 // contiguous segment of the request's slots; a counting sweep gives each
 // segment its first source and destination rank, a second sweep lists them
 // with ballot prefixes.  compact_copy_kernel: every wavefront moves whole
-// slots (Hkv * D elements of K and of V per layer) for its share of the
-// (request, pair, layer) copies.
+// slots (Hkv * D elements of K and of V per layer) of its share of the pairs,
+// for every layer.
 #include "common.h"
 
 namespace kvsel {
@@ -123,6 +123,11 @@ __global__ __launch_bounds__(kPlanThreads) void compact_plan_kernel(CompactParam
   }
 }
 
+// A wavefront takes one (request, pair) at a time: it resolves both slots
+// once, then copies them for every layer, kLayerBatch layers' K and V pieces
+// in flight together.
+constexpr int kLayerBatch = 4;
+
 template <int ESZ>
 __global__ __launch_bounds__(256) void compact_copy_kernel(CompactParams p, const int32_t* __restrict__ block_table,
                                                            uint8_t* __restrict__ k_pool, uint8_t* __restrict__ v_pool,
@@ -133,27 +138,41 @@ __global__ __launch_bounds__(256) void compact_copy_kernel(CompactParams p, cons
   const int32_t m = w.n_pairs[r];
   const int64_t row = static_cast<int64_t>(p.Hkv) * p.D * ESZ;           // bytes of one slot per layer
   const int pieces = static_cast<int>(row / 16);
-  const int64_t items = static_cast<int64_t>(m) * p.L;                 // (pair, layer)
+  const int64_t layer_bytes = p.pool_blocks * p.block_size * row;
   const int64_t wave_global = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
   const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
   const int32_t* src = w.src + static_cast<int64_t>(r) * slots;
   const int32_t* dst = w.dst + static_cast<int64_t>(r) * slots;
   const int32_t* btr = block_table + static_cast<int64_t>(r) * p.Y;
-  for (int64_t it = wave_global; it < items; it += n_waves) {
-    const int64_t i = it / p.L;
-    const int l = static_cast<int>(it - i * p.L);
+  for (int64_t i = wave_global; i < m; i += n_waves) {
     const int32_t s = src[i], d = dst[i];
     const int64_t bs = btr[s / p.block_size], bd = btr[d / p.block_size];
     if (bs < 0 || bs >= p.pool_blocks || bd < 0 || bd >= p.pool_blocks) continue;
-    const int64_t so = ((static_cast<int64_t>(l) * p.pool_blocks + bs) * p.block_size + s % p.block_size) * row;
-    const int64_t dof = ((static_cast<int64_t>(l) * p.pool_blocks + bd) * p.block_size + d % p.block_size) * row;
-    for (int c = lane; c < pieces; c += 64) {
-      const uint4 kv = *reinterpret_cast<const uint4*>(k_pool + so + 16 * c);
-      const uint4 vv = *reinterpret_cast<const uint4*>(v_pool + so + 16 * c);
-      store16_stream(k_pool + dof + 16 * c, kv);
-      store16_stream(v_pool + dof + 16 * c, vv);
+    const int64_t so = (bs * p.block_size + s % p.block_size) * row;
+    const int64_t dof = (bd * p.block_size + d % p.block_size) * row;
+    for (int l0 = 0; l0 < p.L; l0 += kLayerBatch) {
+      for (int c0 = 0; c0 < pieces; c0 += 64) {
+        const int c = c0 + lane;
+        uint4 kv[kLayerBatch], vv[kLayerBatch];
+#pragma unroll
+        for (int j = 0; j < kLayerBatch; ++j) {
+          // past the last layer or piece: re-read piece 0 of layer 0 (never stored)
+          const bool ok = l0 + j < p.L && c < pieces;
+          const int64_t o = ok ? (l0 + j) * layer_bytes + so + 16 * c : so;
+          kv[j] = *reinterpret_cast<const uint4*>(k_pool + o);
+          vv[j] = *reinterpret_cast<const uint4*>(v_pool + o);
+        }
+#pragma unroll
+        for (int j = 0; j < kLayerBatch; ++j) {
+          if (l0 + j < p.L && c < pieces) {
+            const int64_t o = (l0 + j) * layer_bytes + dof + 16 * c;
+            store16_stream(k_pool + o, kv[j]);
+            store16_stream(v_pool + o, vv[j]);
+          }
+        }
+      }
     }
-    if (l == 0 && lane == 0) slot_pos[static_cast<int64_t>(r) * slots + d] = s;
+    if (lane == 0) slot_pos[static_cast<int64_t>(r) * slots + d] = s;
   }
 }
 
@@ -171,10 +190,10 @@ hipError_t launch_compact(const CompactParams& p, const uint8_t* keep, const int
   compact_plan_kernel<<<p.R, kPlanThreads, 0, st>>>(p, keep, block_table, slot_pos, freed_blocks, n_freed, w);
   hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
-  // enough wavefronts for the largest possible plan of a request
-  const int64_t max_items = static_cast<int64_t>(p.Y) * p.block_size * p.L;
-  const int64_t bx = ceil_div(max_items, 4 * 4);   // about four (pair, layer) copies per wavefront
-  dim3 grid(static_cast<unsigned>(bx < 1 ? 1 : (bx > 4096 ? 4096 : bx)), p.R);
+  // one wavefront per pair of the largest possible plan of a request, capped
+  const int64_t max_pairs = static_cast<int64_t>(p.Y) * p.block_size;
+  const int64_t bx = ceil_div(max_pairs, 4);
+  dim3 grid(static_cast<unsigned>(bx < 1 ? 1 : (bx > 256 ? 256 : bx)), p.R);
   uint8_t* kp = static_cast<uint8_t*>(k_pool);
   uint8_t* vp = static_cast<uint8_t*>(v_pool);
   if (p.dtype == KVSEL_F32) compact_copy_kernel<4><<<grid, 256, 0, st>>>(p, block_table, kp, vp, slot_pos, w);

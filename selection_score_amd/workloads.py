@@ -18,6 +18,10 @@ Workloads (shapes of the settings the three pages describe):
               (block 0 + last 4 forced), raw K/V in 8 aliased layer buffers, theta 1e6
   kvmem10m    same model, 312500 blocks per unit scored in 65536-block tiles,
               4 sessions, 4096-block views, 50% overlap with the previous view
+  actkv       in-place tail compaction of paged KV: 64 requests of 6144 positions
+              in 16-slot blocks compressed to 4096 kept entries (4 sink + 64
+              recent + the rest drawn denser toward the tail), 36 layers of
+              8 KV heads, D 128, bf16 pools
 """
 import dataclasses
 import math
@@ -76,6 +80,8 @@ CONFIGS = {
     "kvmem10m": Config("kvmem10m", 1005, L=64, Hkv=8, Hq=64, D=128, N=312500, k=4096, n_sink=1,
                        n_recent=4, dtype=torch.bfloat16, W=512, bt=32, theta=1e6, raw_layers=1,
                        S=4, tile=65536),
+    "actkv": Config("actkv", 1006, L=36, Hkv=8, Hq=32, D=128, N=6144, k=4096, n_sink=4, n_recent=64,
+                    page_size=16, S=64),
 }
 
 
@@ -244,3 +250,33 @@ def kvmem_raw_store(cfg, device):
     h = torch.arange(cfg.Hkv, device=device)[None, :]
     offsets = (((l % cfg.raw_layers) * cfg.Hkv + h) * unit_elems).reshape(-1).to(torch.int64)
     return k, v, offsets
+
+
+# ------------------------------------------------------------------ tail compaction
+
+def actkv_inputs(cfg, device, spare_blocks=64):
+    """S requests of N positions in page_size-slot blocks.  Keep masks: the
+    n_sink first and n_recent last positions, plus k - n_sink - n_recent more
+    drawn without replacement with weights exp(1.5 j / N) (denser toward the
+    tail).  Block tables: a seeded permutation of the pool's blocks.  Pools
+    [L][S*Y + spare][page_size][Hkv][D] ~ N(0, 1) in cfg.dtype."""
+    g = _gen(cfg, device)
+    R, N, bs = cfg.S, cfg.N, cfg.page_size
+    Y = (N + bs - 1) // bs
+    P = R * Y + spare_blocks
+    keep = torch.zeros((R, N), dtype=torch.uint8, device=device)
+    keep[:, : cfg.n_sink] = 1
+    keep[:, N - cfg.n_recent:] = 1
+    mid = torch.arange(cfg.n_sink, N - cfg.n_recent, device=device)
+    w = torch.exp(1.5 * mid.double() / N)
+    extra = cfg.k - cfg.n_sink - cfg.n_recent
+    for r in range(R):
+        pick = torch.multinomial(w, extra, replacement=False, generator=g)
+        keep[r, mid[pick]] = 1
+    block_table = torch.randperm(P, generator=g, device=device)[: R * Y].view(R, Y).to(torch.int32)
+    k_pool = torch.empty((cfg.L, P, bs, cfg.Hkv, cfg.D), dtype=cfg.dtype, device=device)
+    v_pool = torch.empty_like(k_pool)
+    for l in range(cfg.L):
+        k_pool[l] = _randn(k_pool.shape[1:], g, device).to(cfg.dtype)
+        v_pool[l] = _randn(v_pool.shape[1:], g, device).to(cfg.dtype)
+    return dict(keep=keep, block_table=block_table, k_pool=k_pool, v_pool=v_pool)
