@@ -18,8 +18,9 @@ Sources (pages, by title and section):
 * ActKV: Efficient LLM Agents through Action-Guided KV Cache Management --
   §2 (attention score and output; paged KV layout and the block-table
   example), §3.3 (the three primitives: attention calculation, entry
-  eviction to a Boolean keep mask, cache compaction), §7.1 (recovering
-  attention probabilities from the softmax log-sum-exp; Algorithm 3).
+  eviction to a Boolean keep mask, cache compaction), §5.2 (the LRFU keep
+  score with a top-p hit), §7.1 (recovering attention probabilities from
+  the softmax log-sum-exp; Algorithm 3, the decode-streaming scorer).
 * IntentKV: Cross-Turn Intent-Aware KV Cache Pruning for Agent Inference --
   §2 Q2 (retention/layout split, dead-slot sentinel), §3 (budget semantics,
   one-way eviction), §4 (top-k with forced set, memory recurrence, rule
@@ -46,6 +47,14 @@ PIN_STATUS = {
     "score.query_reduce / block_scores": "pinned (per-query brute force by linearity; hand example)",
     "score.mean_k_index": "pinned (hand-computed means over two blocks, fp16 RNE halfway cases, "
                           "constant blocks, linearity of the block score)",
+    "score.decode_recovery_step": "pinned (running mean over T tokens equals the batch window mean "
+                                  "with max over the group; LSE identity; hand two-token example; "
+                                  "region reset)",
+    "select.action_scores / top_p_hits": "pinned (hand-worked top-p sets, ties, top_p = 1; minimum "
+                                         "cardinality by brute force over all subsets; exact unit sum)",
+    "select.lrfu_keep_score": "partly unpinned: the page's update equation is lost; the reading "
+                              "lam*KS + hit*score is pinned to the page's lambda = 0 (recency) and "
+                              "lambda = 1 (frequency) limits only",
     "score.residual_score": "pinned (zero-initialised fc2 gives the rule score exactly)",
     "select.select_topk": "pinned (exhaustive max-sum brute force on tiny inputs; invariants)",
     "select.select_topk_tiled": "pinned (equal to select_topk for every tile size)",

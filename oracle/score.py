@@ -10,6 +10,9 @@ Layouts (row-major, last index fastest):
   block queries    q      [S][L][Hq][Wq][D] (pre-RoPE)
   Mean-K index     mu     [L][Hkv][NB][D]
   raw keys         raw_k  [..., NB*bt, D]   (pre-RoPE, bt-token blocks)
+  decode queries   q      [L][Ra][Hq][D]    (post-RoPE, one token per request)
+  paged KV pool    k_pool [L][P][BS][Hkv][D]
+  running means    state  [L][R][Hkv][n_cap]
 """
 import numpy as np
 
@@ -249,3 +252,62 @@ def residual_score(rule, features, fc1_w, fc1_b, fc2_w, fc2_b, alpha=1.0):
     gelu = 0.5 * x * (1.0 + np.tanh(np.sqrt(2.0 / np.pi) * (x + 0.044715 * x ** 3)))
     r = gelu @ np.asarray(fc2_w, dtype=np.float64).T + fc2_b
     return np.asarray(rule, dtype=np.float64) + alpha * r[..., 0]
+
+
+def decode_recovery_step(state, n_seen, q, lse, k_pool, block_table, n_ctx, *,
+                         req=None, scale=None):
+    """One decode step of the recovery-based action scorer.
+
+    ActKV §7.1 and its Algorithm 3: for the current query token of every
+    request that is generating an action, each cached key j of KV head g gets
+    p[h,j] = exp(s[h,j] - LSE[h]) for the query heads h of g's group, where
+    s = scale * q_h . k_j is recomputed from the paged keys and LSE is the
+    log-sum-exp the paged attention pass produced.  The probabilities are
+    reduced by a maximum over the group and folded into a running mean over
+    the action tokens of the current region; the mean restarts from zero when
+    a region begins.
+
+    Readings where the page is silent: the token sees the first n_ctx[r]
+    logical positions of its request; positions it cannot see (j >= n_ctx,
+    or a block-table entry outside the pool) count as probability 0, so the
+    running mean after T tokens equals the plain mean over those T tokens.
+    n_seen[r] is the number of action tokens of the region already in the
+    state; n_seen == 0 starts a region (the old state is not read).  The
+    update for t = n_seen is  state <- state + (p - state) / (t + 1)  over
+    every position j < n_cap.
+
+    state: [L][R][Hkv][n_cap]; q: [L][Ra][Hq][D]; lse: [L][Ra][Hq];
+    k_pool: [L][P][BS][Hkv][D]; block_table: [R][Y]; n_ctx, n_seen: [R];
+    req: [Ra] request of each query row (default 0..R-1).  Returns the new
+    state (float64); requests not in ``req`` are unchanged.
+    """
+    st = np.array(state, dtype=np.float64)
+    q = np.asarray(q, dtype=np.float64)
+    lse = np.asarray(lse, dtype=np.float64)
+    L, Ra, Hq, D = q.shape
+    _, P, BS, Hkv, _ = k_pool.shape
+    n_cap = st.shape[3]
+    if scale is None:
+        scale = 1.0 / np.sqrt(D)
+    req = np.arange(Ra) if req is None else np.asarray(req, dtype=np.int64)
+    bt = np.asarray(block_table, dtype=np.int64)
+    j = np.arange(n_cap)
+    for a in range(Ra):
+        r = int(req[a])
+        t = int(n_seen[r])
+        n = int(n_ctx[r])
+        lp = j // BS
+        page = np.where(lp < bt.shape[1], bt[r, np.minimum(lp, bt.shape[1] - 1)], -1)
+        visible = (j < n) & (page >= 0) & (page < P)
+        pg = np.where(visible, page, 0)
+        for l in range(L):
+            keys = np.asarray(k_pool[l], dtype=np.float64)[pg, j % BS]      # [n_cap][Hkv][D]
+            for g in range(Hkv):
+                heads = [h for h in range(Hq) if gqa_group(h, Hq, Hkv) == g]
+                probs = [np.exp(scale * (keys[:, g, :] @ q[l, a, h]) - lse[l, a, h]) for h in heads]
+                p = np.where(visible, np.max(np.stack(probs), axis=0), 0.0)
+                if t == 0:
+                    st[l, r, g] = p
+                else:
+                    st[l, r, g] = st[l, r, g] + (p - st[l, r, g]) / (t + 1)
+    return st
