@@ -19,7 +19,9 @@ is that kernel's launch duration.
 with the dead-slot redirect), kvmem1m (1M-token block retrieval and re-RoPE
 gather), kvmem10m (10M-token tiled retrieval and the incremental view
 update), meank1m (building the Mean-K index of the 1M-token workspace),
-actkv (ActKV's in-place tail compaction of paged KV, Table 1's shape).
+actkv (one ActKV compression step with Table 1's shape: LRFU keep score,
+eviction by keep score, in-place tail compaction of paged KV), actkv_decode
+(one decode token of ActKV's recovery-based action scorer over paged K).
 
 Other modes:
   --copy-calib         a plain elementwise copy of 1 GiB (5 launches), to scale
@@ -64,6 +66,8 @@ KERNEL_SOURCES = {
     "mean_k_kernel": "k_index.hip",
     "free_clear_kernel": "k_misc.hip", "free_mark_kernel": "k_misc.hip", "free_compact_kernel": "k_misc.hip",
     "compact_plan_kernel": "k_compact.hip", "compact_copy_kernel": "k_compact.hip",
+    "decode_score_kernel": "k_decode.hip", "action_reduce_kernel": "k_decode.hip",
+    "top_p_update_kernel": "k_decode.hip",
 }
 
 
@@ -75,7 +79,8 @@ def _args():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=15.0,
                     help="wall-clock budget of the oracle sample for the CPU baseline")
-    ap.add_argument("--workload", default="snapkv", choices=["snapkv", "intentkv", "kvmem1m", "kvmem10m", "meank1m", "actkv"],
+    ap.add_argument("--workload", default="snapkv", choices=["snapkv", "intentkv", "kvmem1m", "kvmem10m", "meank1m", "actkv",
+                                                           "actkv_decode"],
                     help="which workload one step runs (the default line is snapkv)")
     ap.add_argument("--copy-calib", action="store_true")
     ap.add_argument("--traffic-summary", nargs=4, metavar=("FETCH_DIR", "WRITE_DIR", "COPY_FETCH_DIR", "COPY_WRITE_DIR"))
@@ -589,62 +594,144 @@ class MeanK1M:
 
 
 class ActKVCompact:
-    """ActKV's in-place tail compaction with Table 1's shape: 64 requests of
-    6144 positions in 16-slot blocks, 4096 kept each, moved into their last
-    256 blocks for 36 layers of 8 KV heads (D 128, bf16).  The copies write
-    the pools in place; repeating the step on the same masks repeats the
-    same moves, so every step does the same work."""
-    stages = ["compact"]
+    """One ActKV compression step with Table 1's shape, for 64 requests that
+    just left an action region (6144 positions each, 16-slot blocks, 36
+    layers of 8 KV heads, D 128, bf16): the LRFU keep score from the action
+    scorer's running means (lambda 0.5, top-p 0.9), eviction to 4096 kept
+    entries by keep score (4 sink + 64 recent forced), and the in-place tail
+    compaction of K and V.  The keep scores start at the policy's fixed
+    point for this state (2 * score on hits, smaller tail-weighted values
+    elsewhere), so every step computes the same keep mask and repeats the
+    same moves."""
+    stages = ["keep_score", "select", "compact"]
     kernels = {}
-    launches = {"compact": 2}
-    score_stage = "compact"
-    materialise_stages = ["compact"]
+    launches = {"keep_score": 2, "select": 2, "compact": 2}
+    score_stage = "keep_score"
+    materialise_stages = ["select", "compact"]
     dtype = "bf16"
 
     def __init__(self, torch, kv, wl, dev):
         self.kv, self.cfg = kv, wl.CONFIGS["actkv"]
         cfg = self.cfg
         self.inp = wl.actkv_inputs(cfg, dev)
-        R, bs = cfg.S, cfg.page_size
+        R, N, bs = cfg.S, cfg.N, cfg.page_size
         Y = self.inp["block_table"].shape[1]
+        self.state = wl.actkv_state(cfg, dev)
+        self.n_len = torch.full((R,), N, dtype=torch.int32, device=dev)
+        # the fixed point of KS <- 0.5 KS + hit * score: 2 * score on hits;
+        # the other entries sit below every hit, ordered toward the tail
+        ks = torch.zeros((R, N), dtype=torch.float32, device=dev)
+        hit = torch.empty((R, N), dtype=torch.uint8, device=dev)
+        kv.keep_score(self.state, ks, self.n_len, lam=0.0, top_p=0.9, hit=hit)
+        floor = torch.where(hit.bool(), ks, torch.full_like(ks, float("inf"))).amin(dim=1, keepdim=True)
+        ramp = torch.linspace(0.1, 0.4, N, device=dev)[None]
+        self.ks = torch.where(hit.bool(), 2.0 * ks, floor * ramp).contiguous()
+        self.hits = int(hit.sum())
+        self.kept_idx = torch.empty((R, cfg.k), dtype=torch.int32, device=dev)
+        self.keep = torch.empty((R, N), dtype=torch.uint8, device=dev)
         self.slot_pos = torch.empty((R, Y * bs), dtype=torch.int32, device=dev)
         self.freed = torch.empty((R, Y), dtype=torch.int32, device=dev)
         self.n_freed = torch.empty(R, dtype=torch.int32, device=dev)
-        self.ws = None
-        keep = self.inp["keep"].bool()
-        X = (keep.sum(dim=1) + bs - 1) // bs
-        t0 = (Y - X) * bs
-        pos = torch.arange(cfg.N, device=dev)[None]
-        self.pairs = int((keep & (pos < t0[:, None])).sum())      # one (source, destination) copy each
+        self.ws_keep = self.ws_sel = self.ws = None
         self.tokens = R * cfg.N * cfg.L * cfg.Hkv
+        self.pairs = None
+        self.torch = torch
 
     def step(self, ev, stream, it):
-        inp, cfg = self.inp, self.cfg
+        inp, cfg, kv = self.inp, self.cfg, self.kv
         ev[0].record(stream)
-        self.ws = self.kv.compact(inp["keep"], inp["block_table"], inp["k_pool"], inp["v_pool"], self.slot_pos,
-                                  self.freed, self.n_freed, block_size=cfg.page_size, workspace=self.ws)
+        self.ws_keep = kv.keep_score(self.state, self.ks, self.n_len, lam=cfg.decay, top_p=0.9,
+                                     workspace=self.ws_keep)
         ev[1].record(stream)
+        self.ws_sel = kv.select(self.ks, self.kept_idx, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                                keep_mask=self.keep, workspace=self.ws_sel)
+        ev[2].record(stream)
+        self.ws = kv.compact(self.keep, inp["block_table"], inp["k_pool"], inp["v_pool"], self.slot_pos,
+                             self.freed, self.n_freed, block_size=cfg.page_size, workspace=self.ws)
+        ev[3].record(stream)
+
+    def _moved(self):
+        if self.pairs is None:
+            cfg, bs = self.cfg, self.cfg.page_size
+            Y = self.inp["block_table"].shape[1]
+            keep = self.keep.bool()
+            X = (keep.sum(dim=1) + bs - 1) // bs
+            t0 = (Y - X) * bs
+            pos = self.torch.arange(cfg.N, device=keep.device)[None]
+            self.pairs = int((keep & (pos < t0[:, None])).sum())      # one (source, destination) copy each
+        return self.pairs
 
     def algo_bytes(self):
         cfg = self.cfg
         R, N, bs = cfg.S, cfg.N, cfg.page_size
         Y = self.inp["block_table"].shape[1]
         row = cfg.Hkv * cfg.D * 2
-        moves = self.pairs * cfg.L * 2 * 2 * row                  # K and V, read and written
-        return {"compact": moves + R * N + R * Y * 4 + R * Y * bs * 4 + R * Y * 4}
+        moves = self._moved() * cfg.L * 2 * 2 * row                  # K and V, read and written
+        return {"keep_score": cfg.L * R * cfg.Hkv * N * 4 + R * N * 4 * 4,   # state; scores out, in; KS r/w
+                "select": R * N * 4 + R * N + R * cfg.k * 4,
+                "compact": moves + R * N + R * Y * 4 + R * Y * bs * 4 + R * Y * 4}
 
     def config(self):
         cfg = self.cfg
-        return {"workload": "actkv in-place tail compaction: 64 requests x 6144 positions in 16-slot blocks -> "
-                            "4096 kept, 36 layers x 8 KV heads x D128 bf16 paged pools",
-                "requests": cfg.S, "positions": cfg.N, "kept": cfg.k, "block_size": cfg.page_size}
+        return {"workload": "actkv compression step: LRFU keep score (lambda 0.5, top-p 0.9) from 36 layers x "
+                            "8 KV heads of running means, eviction to 4096 of 6144 positions by keep score, "
+                            "in-place tail compaction of 64 requests' 16-slot bf16 paged K/V (D128)",
+                "requests": cfg.S, "positions": cfg.N, "kept": cfg.k, "block_size": cfg.page_size,
+                "lambda": cfg.decay, "top_p": 0.9}
 
     def extra(self):
-        return {"moved_entries": self.pairs}
+        return {"moved_entries": self._moved(), "top_p_hits": self.hits}
+
+
+class ActKVDecode:
+    """One decode token of ActKV's recovery-based action scorer for 64
+    requests at 6144 positions (36 layers, 8 KV / 32 query heads, D 128,
+    bf16 paged K in 16-slot blocks): logits recomputed from the paged keys,
+    probabilities recovered with the attention pass's LSE, the maximum over
+    each GQA group folded into the running mean (5 tokens already in it).
+    Repeating the step with the same token count repeats the same work."""
+    stages = ["decode"]
+    kernels = {"decode": ("decode_score_kernel", "k_decode.hip")}
+    launches = {"decode": 1}
+    score_stage = "decode"
+    materialise_stages = []
+    dtype = "bf16"
+
+    def __init__(self, torch, kv, wl, dev):
+        self.kv, self.cfg = kv, wl.CONFIGS["actkv"]
+        self.inp = wl.actkv_decode_inputs(self.cfg, dev)
+        self.state = wl.actkv_state(self.cfg, dev)
+        cfg = self.cfg
+        self.tokens = cfg.S * cfg.N * cfg.L * cfg.Hkv
+
+    def step(self, ev, stream, it):
+        inp = self.inp
+        ev[0].record(stream)
+        self.kv.decode_score(inp["q"], inp["lse"], inp["k_pool"], inp["block_table"], inp["n_ctx"], inp["n_seen"],
+                             self.state)
+        ev[1].record(stream)
+
+    def algo_bytes(self):
+        cfg = self.cfg
+        R, N = cfg.S, cfg.N
+        keys = cfg.L * R * N * cfg.Hkv * cfg.D * 2
+        state = 2 * cfg.L * R * cfg.Hkv * N * 4                        # read and written (mid-region)
+        small = cfg.L * R * cfg.Hq * (cfg.D * 2 + 4) + R * (N // cfg.page_size) * 4
+        return {"decode": keys + state + small}
+
+    def config(self):
+        cfg = self.cfg
+        return {"workload": "actkv decode-streaming recovery scorer: one action token of 64 requests x 6144 "
+                            "positions, 36 layers x 8 KV / 32 query heads x D128 bf16 paged K (16-slot blocks), "
+                            "LSE from the attention pass, max over the GQA group, running mean",
+                "requests": cfg.S, "positions": cfg.N, "block_size": cfg.page_size, "tokens_in_mean": cfg.turns}
+
+    def extra(self):
+        return {}
 
 
 WORKLOADS = {"snapkv": SnapKV, "intentkv": IntentKV, "kvmem1m": KVMem1M, "kvmem10m": KVMem10M, "meank1m": MeanK1M,
-             "actkv": ActKVCompact}
+             "actkv": ActKVCompact, "actkv_decode": ActKVDecode}
 
 
 def main():

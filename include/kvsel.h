@@ -428,6 +428,115 @@ typedef struct kvsel_index_args {
 
 kvsel_status kvsel_build_index(const kvsel_index_args* args, void* stream);
 
+/* ------------------------------------------------------------------ decode scorer
+ *
+ * ActKV §7.1 and Algorithm 3 (recovery-based attention calculation): for the
+ * current query token of each request that is generating an action, every
+ * cached key j of KV head g gets
+ *   p[j] = max over the group's query heads h of exp(scale * q_h . k_j - LSE_h)
+ * with LSE_h the natural-log log-sum-exp the paged attention pass produced
+ * for that token and head, and p is folded into a running mean over the
+ * action tokens of the current region:
+ *   t = n_seen[r];  state <- (t == 0) ? p : state + (p - state) / (t + 1).
+ * Keys come straight from the paged pool through the block table (ActKV §2
+ * paging); nothing is gathered.  Readings where the page is silent: the
+ * token sees the first n_ctx[r] positions; a position it cannot see, or
+ * whose block-table entry lies outside [0, pool_blocks), has p = 0.
+ *
+ *   req          [Ra] int32 request (row of block_table, n_ctx, n_seen, state)
+ *                of each query row, or NULL for rows 0..Ra-1 (then Ra <= R);
+ *                entries outside [0, R) are skipped; a request may appear once
+ *   q            [L][Ra][Hq][D] of dtype (BF16 or F16), post-RoPE
+ *   lse          [L][Ra][Hq] F32, natural log
+ *   k_pool       [L][pool_blocks][block_size][Hkv][D] of dtype
+ *   block_table  [R][Y] int32
+ *   n_ctx        [R] int32, clamped to [0, min(n_cap, Y * block_size)]
+ *   n_seen       [R] int32, action tokens of the region already in the state
+ *                (0 = this token starts a region; negative counts as 0)
+ *   state        [L][R][Hkv][n_cap] F32, in/out
+ * At t = 0 every position [0, n_cap) of the request is written (p, or 0
+ * past n_ctx).  At t > 0 only positions in the 64-aligned tiles that hold
+ * visible keys are written; positions past n_ctx must then hold 0, as a
+ * region start leaves them (n_ctx does not decrease within a region), and
+ * the state equals the plain mean over the region's tokens.
+ * Requirements: D 64 or 128; G = Hq / Hkv integral and <= 16; block_size a
+ * multiple of 16; q, k_pool 16-byte aligned.  scale = 0 means 1/sqrt(D).
+ * Errors: E_ARG, E_UNSUPPORTED (D, dtype, G), E_DEVICE.  Ra = 0 is a no-op.
+ */
+typedef struct kvsel_decode_args {
+  uint32_t struct_size;
+  int32_t Ra, R;
+  int32_t L, Hq, Hkv, D;
+  int32_t dtype;              /* BF16 or F16 */
+  int32_t block_size;
+  int32_t Y;                  /* block-table columns per request */
+  float scale;                /* 0 = 1/sqrt(D) */
+  int64_t n_cap;              /* state positions per (layer, request, KV head) */
+  int64_t pool_blocks;
+  const int32_t* req;
+  const void* q;
+  const float* lse;
+  const void* k_pool;
+  const int32_t* block_table;
+  const int32_t* n_ctx;
+  const int32_t* n_seen;
+  float* state;
+} kvsel_decode_args;
+
+kvsel_status kvsel_decode_score(const kvsel_decode_args* args, void* stream);
+
+/* ------------------------------------------------------------------ keep score
+ *
+ * ActKV §5.2 (attention-aware LRFU) at a compression step, for the requests
+ * in `req` (those that just left an action region):
+ *   score[j] = float32( sum over layers l and KV heads g of state[l][r][g][j] )
+ *              (summed in float64 with compensation, rounded once);
+ *   hit[j]   = j is in the shortest prefix of the entries j < n_len[r], by
+ *              score descending with the lower index first on ties, whose
+ *              cumulative score reaches top_p * (sum of all scores); no hits
+ *              when that product is 0;
+ *   KS[j]    = lambda * KS[j] + (hit[j] ? score[j] : 0).
+ * The page's update equation is lost; this is the reading whose limits are
+ * the ones the page describes (lambda = 0: only the latest step counts;
+ * lambda = 1: hits accumulate without decay).  Cumulative sums are float64;
+ * where they fall within about 1e-15 of the target the boundary entry may
+ * differ from an exact sequential sum's.
+ *
+ *   req         [Rc] int32, or NULL for 0..Rc-1 (then Rc <= R); entries
+ *               outside [0, R) are skipped; a request may appear once
+ *   n_len       [R] int32 entries per request, clamped to [0, n_cap]
+ *   state       [L][R][Hkv][n_cap] F32 running means (kvsel_decode_score),
+ *               non-negative
+ *   keep_score  [R][n_cap] F32 in/out; entries j >= n_len keep their value
+ *   attn_score  [R][n_cap] F32 out or NULL: score[j], 0 for j >= n_len
+ *   hit         [R][n_cap] u8 out or NULL: 1 = hit (the entry's bit of the
+ *               action access vector of ActKV §5.1 for this region), 0 for
+ *               j >= n_len
+ * lambda in [0, 1], top_p in (0, 1].  Workspace: kvsel_keep_score_workspace
+ * (Rc * n_cap floats when attn_score is NULL, else 0).
+ * Errors: E_ARG, E_WORKSPACE, E_DEVICE.  Rc = 0 is a no-op.
+ */
+typedef struct kvsel_keep_score_args {
+  uint32_t struct_size;
+  int32_t Rc, R;
+  int32_t L, Hkv;
+  int32_t reserved;           /* 0 */
+  int64_t n_cap;
+  float lam;                  /* decay lambda in [0, 1] */
+  float top_p;
+  const int32_t* req;
+  const int32_t* n_len;
+  const float* state;
+  float* keep_score;
+  float* attn_score;
+  uint8_t* hit;
+} kvsel_keep_score_args;
+
+kvsel_status kvsel_keep_score_workspace(const kvsel_keep_score_args* args, size_t* bytes);
+
+kvsel_status kvsel_keep_score(const kvsel_keep_score_args* args, void* workspace, size_t workspace_bytes,
+                              void* stream);
+
 /* ------------------------------------------------------------------ memory
  *
  * IntentKV §4 (memory recurrence) and §7 (unit-norm projection): one turn

@@ -5,8 +5,8 @@ ABI of ``include/kvsel.h``); this package is a thin ctypes binding plus the
 seeded synthetic workload generators.  Importing the binding functions loads
 the library lazily and raises if it has not been built.
 """
-from .kvsel import (KvselError, build_index, compact, free_list, gather_incremental, gather_rerope, memory_update, redirect,
+from .kvsel import (KvselError, build_index, compact, decode_score, free_list, keep_score, gather_incremental, gather_rerope, memory_update, redirect,
                     score_block, score_memory, score_window, select, version)
 
-__all__ = ["KvselError", "build_index", "compact", "free_list", "gather_incremental", "gather_rerope", "memory_update", "redirect",
+__all__ = ["KvselError", "build_index", "compact", "decode_score", "free_list", "keep_score", "gather_incremental", "gather_rerope", "memory_update", "redirect",
            "score_block", "score_memory", "score_window", "select", "version"]

@@ -104,10 +104,28 @@ class CompactArgs(ctypes.Structure):
     ]
 
 
+class DecodeArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("Ra", c_i32), ("R", c_i32), ("L", c_i32), ("Hq", c_i32), ("Hkv", c_i32),
+        ("D", c_i32), ("dtype", c_i32), ("block_size", c_i32), ("Y", c_i32), ("scale", c_f32),
+        ("n_cap", c_i64), ("pool_blocks", c_i64), ("req", c_vp), ("q", c_vp), ("lse", c_vp), ("k_pool", c_vp),
+        ("block_table", c_vp), ("n_ctx", c_vp), ("n_seen", c_vp), ("state", c_vp),
+    ]
+
+
+class KeepScoreArgs(ctypes.Structure):
+    _fields_ = [
+        ("struct_size", c_u32), ("Rc", c_i32), ("R", c_i32), ("L", c_i32), ("Hkv", c_i32), ("reserved", c_i32),
+        ("n_cap", c_i64), ("lam", c_f32), ("top_p", c_f32), ("req", c_vp), ("n_len", c_vp), ("state", c_vp),
+        ("keep_score", c_vp), ("attn_score", c_vp), ("hit", c_vp),
+    ]
+
+
 EXPORTS = ["kvsel_version", "kvsel_last_error", "kvsel_score_workspace", "kvsel_score",
            "kvsel_select_workspace", "kvsel_select", "kvsel_gather_workspace", "kvsel_gather_rerope",
            "kvsel_redirect", "kvsel_memory_update", "kvsel_build_index", "kvsel_free_list_workspace",
-           "kvsel_free_list", "kvsel_compact_workspace", "kvsel_compact"]
+           "kvsel_free_list", "kvsel_compact_workspace", "kvsel_compact", "kvsel_decode_score",
+           "kvsel_keep_score_workspace", "kvsel_keep_score"]
 
 _lib = None
 
@@ -139,6 +157,9 @@ def load(path=LIB_PATH):
     lib.kvsel_free_list.argtypes = [P(FreeListArgs), c_vp, ctypes.c_size_t, c_vp]
     lib.kvsel_compact_workspace.argtypes = [P(CompactArgs), P(ctypes.c_size_t)]
     lib.kvsel_compact.argtypes = [P(CompactArgs), c_vp, ctypes.c_size_t, c_vp]
+    lib.kvsel_decode_score.argtypes = [P(DecodeArgs), c_vp]
+    lib.kvsel_keep_score_workspace.argtypes = [P(KeepScoreArgs), P(ctypes.c_size_t)]
+    lib.kvsel_keep_score.argtypes = [P(KeepScoreArgs), c_vp, ctypes.c_size_t, c_vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = c_i32
     _lib = lib

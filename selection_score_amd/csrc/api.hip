@@ -608,3 +608,111 @@ kvsel_status kvsel_memory_update(const kvsel_memupd_args* a, void* stream) {
 }
 
 }  // extern "C"
+
+// ------------------------------------------------------------------ decode scorer
+
+static kvsel_status check_decode(const kvsel_decode_args* a, DecodeParams* p) {
+  if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+  if (a->struct_size < sizeof(kvsel_decode_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->Ra < 0 || a->R < 0 || a->Ra > 65535) return fail(KVSEL_E_ARG, "Ra must be in [0, 65535] and R >= 0");
+  if (a->L < 1 || a->L > 65535 || a->Hq < 1 || a->Hkv < 1 || a->block_size < 1 || a->Y < 0 || a->pool_blocks < 1)
+    return fail(KVSEL_E_ARG, "L in [1, 65535], Hq, Hkv, block_size, pool_blocks >= 1 and Y >= 0 required");
+  if (a->dtype != KVSEL_BF16 && a->dtype != KVSEL_F16) return fail(KVSEL_E_UNSUPPORTED, "dtype must be BF16 or F16");
+  if (a->D != 64 && a->D != 128) return fail(KVSEL_E_UNSUPPORTED, "D must be 64 or 128");
+  if (a->Hq % a->Hkv != 0) return fail(KVSEL_E_ARG, "Hq must be a multiple of Hkv");
+  if (a->Hq / a->Hkv > 16) return fail(KVSEL_E_UNSUPPORTED, "query heads per KV head must be <= 16");
+  if (a->block_size % 16 != 0) return fail(KVSEL_E_UNSUPPORTED, "block_size must be a multiple of 16");
+  if (a->Hkv > 4096) return fail(KVSEL_E_UNSUPPORTED, "Hkv must be <= 4096");
+  if (a->n_cap < 0 || a->n_cap > (int64_t(1) << 30)) return fail(KVSEL_E_ARG, "n_cap must be in [0, 2^30]");
+  if (static_cast<int64_t>(a->Y) * a->block_size > kMaxN) return fail(KVSEL_E_ARG, "Y * block_size must be below 2^31");
+  if (!(a->scale >= 0.f) || isinf(a->scale)) return fail(KVSEL_E_ARG, "scale must be finite and >= 0");
+  if (a->req == nullptr && a->Ra > a->R) return fail(KVSEL_E_ARG, "Ra > R needs an explicit req list");
+  if (a->Ra > 0 && a->n_cap > 0) {
+    if (a->Y < 1) return fail(KVSEL_E_ARG, "Y must be >= 1");
+    if (a->q == nullptr || a->lse == nullptr || a->k_pool == nullptr || a->block_table == nullptr ||
+        a->n_ctx == nullptr || a->n_seen == nullptr || a->state == nullptr)
+      return fail(KVSEL_E_ARG, "a pointer is NULL");
+    if (!aligned16(a->q) || !aligned16(a->k_pool)) return fail(KVSEL_E_ARG, "q and k_pool must be 16-byte aligned");
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(a->lse) | reinterpret_cast<uintptr_t>(a->block_table) |
+                          reinterpret_cast<uintptr_t>(a->n_ctx) | reinterpret_cast<uintptr_t>(a->n_seen) |
+                          reinterpret_cast<uintptr_t>(a->state) | reinterpret_cast<uintptr_t>(a->req);
+    if ((mis & 3u) != 0) return fail(KVSEL_E_ARG, "lse, state and int32 arrays must be 4-byte aligned");
+  }
+  p->Ra = a->Ra; p->R = a->R; p->L = a->L; p->Hq = a->Hq; p->Hkv = a->Hkv; p->D = a->D;
+  p->G = a->Hq / a->Hkv; p->block_size = a->block_size; p->Y = a->Y;
+  const float scale = (a->scale == 0.f) ? 1.0f / sqrtf(static_cast<float>(a->D)) : a->scale;
+  p->scale2 = scale * 1.4426950408889634f;
+  p->n_cap = a->n_cap; p->pool_blocks = a->pool_blocks;
+  p->req = a->req; p->block_table = a->block_table; p->n_ctx = a->n_ctx; p->n_seen = a->n_seen;
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_decode_score(const kvsel_decode_args* a, void* stream) {
+  try {
+    DecodeParams p;
+    kvsel_status s = check_decode(a, &p);
+    if (s != KVSEL_OK) return s;
+    if (p.Ra == 0 || p.n_cap == 0) return KVSEL_OK;
+    if ((s = check_device()) != KVSEL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish(launch_decode_score(p, a->dtype, a->q, a->lse, a->k_pool, a->state, st), st, "decode score");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+// ------------------------------------------------------------------ keep score
+
+static kvsel_status check_keep_score(const kvsel_keep_score_args* a, KeepScoreParams* p) {
+  if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
+  if (a->struct_size < sizeof(kvsel_keep_score_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->Rc < 0 || a->R < 0 || a->Rc > 65535) return fail(KVSEL_E_ARG, "Rc must be in [0, 65535] and R >= 0");
+  if (a->L < 1 || a->Hkv < 1) return fail(KVSEL_E_ARG, "L and Hkv must be >= 1");
+  if (static_cast<int64_t>(a->L) * a->Hkv > kMaxN) return fail(KVSEL_E_ARG, "L * Hkv too large");
+  if (a->n_cap < 0 || a->n_cap > kMaxN) return fail(KVSEL_E_ARG, "n_cap must be in [0, 2^31)");
+  if (!(a->lam >= 0.f && a->lam <= 1.f)) return fail(KVSEL_E_ARG, "lambda must be in [0, 1]");
+  if (!(a->top_p > 0.f && a->top_p <= 1.f)) return fail(KVSEL_E_ARG, "top_p must be in (0, 1]");
+  if (a->req == nullptr && a->Rc > a->R) return fail(KVSEL_E_ARG, "Rc > R needs an explicit req list");
+  if (a->Rc > 0 && a->n_cap > 0) {
+    if (a->n_len == nullptr || a->state == nullptr || a->keep_score == nullptr)
+      return fail(KVSEL_E_ARG, "a pointer is NULL");
+    const uintptr_t mis = reinterpret_cast<uintptr_t>(a->req) | reinterpret_cast<uintptr_t>(a->n_len) |
+                          reinterpret_cast<uintptr_t>(a->state) | reinterpret_cast<uintptr_t>(a->keep_score) |
+                          reinterpret_cast<uintptr_t>(a->attn_score);
+    if ((mis & 3u) != 0) return fail(KVSEL_E_ARG, "float and int32 arrays must be 4-byte aligned");
+  }
+  p->Rc = a->Rc; p->R = a->R; p->L = a->L; p->Hkv = a->Hkv; p->n_cap = a->n_cap;
+  p->lambda = a->lam; p->top_p = a->top_p; p->req = a->req; p->n_len = a->n_len;
+  return KVSEL_OK;
+}
+
+kvsel_status kvsel_keep_score_workspace(const kvsel_keep_score_args* a, size_t* bytes) {
+  try {
+    if (bytes == nullptr) return fail(KVSEL_E_ARG, "bytes is NULL");
+    KeepScoreParams p;
+    kvsel_status s = check_keep_score(a, &p);
+    if (s != KVSEL_OK) return s;
+    *bytes = keep_score_workspace_bytes(p, a->attn_score != nullptr);
+    return KVSEL_OK;
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
+kvsel_status kvsel_keep_score(const kvsel_keep_score_args* a, void* ws, size_t ws_bytes, void* stream) {
+  try {
+    KeepScoreParams p;
+    kvsel_status s = check_keep_score(a, &p);
+    if (s != KVSEL_OK) return s;
+    if (p.Rc == 0 || p.n_cap == 0) return KVSEL_OK;
+    const size_t need = keep_score_workspace_bytes(p, a->attn_score != nullptr);
+    if (need > 0 && (ws == nullptr || ws_bytes < need))
+      return fail(KVSEL_E_WORKSPACE, "workspace too small (see kvsel_keep_score_workspace)");
+    if (need > 0 && !aligned16(ws)) return fail(KVSEL_E_ARG, "workspace must be 16-byte aligned");
+    if ((s = check_device()) != KVSEL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    return finish(launch_keep_score(p, a->state, a->keep_score, a->attn_score, a->hit, ws, st), st, "keep score");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}

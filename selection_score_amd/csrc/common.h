@@ -188,6 +188,29 @@ hipError_t launch_compact(const CompactParams& p, const uint8_t* keep, const int
                           void* v_pool, int32_t* slot_pos, int32_t* freed_blocks, int32_t* n_freed, void* ws,
                           hipStream_t st);
 
+struct DecodeParams {
+  int Ra, R, L, Hq, Hkv, D, G, block_size, Y;
+  float scale2;   // softmax scale * log2(e)
+  int64_t n_cap, pool_blocks;
+  const int32_t* req;
+  const int32_t* block_table;
+  const int32_t* n_ctx;
+  const int32_t* n_seen;
+};
+hipError_t launch_decode_score(const DecodeParams& p, int dt, const void* q, const float* lse, const void* k_pool,
+                               float* state, hipStream_t st);
+
+struct KeepScoreParams {
+  int Rc, R, L, Hkv;
+  int64_t n_cap;
+  float lambda, top_p;
+  const int32_t* req;
+  const int32_t* n_len;
+};
+size_t keep_score_workspace_bytes(const KeepScoreParams& p, bool attn_given);
+hipError_t launch_keep_score(const KeepScoreParams& p, const float* state, float* ks, float* attn_out,
+                             uint8_t* hit, void* ws, hipStream_t st);
+
 hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, int64_t dead,
                            hipStream_t st);
 hipError_t launch_sentinel(void* k_pool, void* v_pool, int L, int Hkv, int D, int dtype,

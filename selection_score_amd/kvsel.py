@@ -320,3 +320,47 @@ def compact(keep_mask, block_table, k_pool, v_pool, slot_pos, freed_blocks, n_fr
     ws, wsz = _workspace(nb.value, k_pool.device, workspace)
     _check(lib.kvsel_compact(ctypes.byref(a), _ptr(ws), wsz, _stream(stream)))
     return ws
+
+
+def decode_score(q, lse, k_pool, block_table, n_ctx, n_seen, state, *, req=None, scale=0.0, stream=None):
+    """kvsel_decode_score.  q [L][Ra][Hq][D] (bf16/f16, post-RoPE); lse
+    [L][Ra][Hq] float32 (natural log); k_pool [L][pool_blocks][block_size][Hkv][D];
+    block_table [R][Y], n_ctx [R], n_seen [R] int32; state [L][R][Hkv][n_cap]
+    float32, updated in place; req [Ra] int32 or None (rows 0..Ra-1)."""
+    L, Ra, Hq, D = q.shape
+    _, P, bs, Hkv, _ = k_pool.shape
+    R, Y = block_table.shape
+    if state.shape[:3] != (L, R, Hkv):
+        raise ValueError("state must be [L][R][Hkv][n_cap]")
+    if q.dtype != k_pool.dtype:
+        raise ValueError("q and k_pool must share a dtype")
+    a = _abi.DecodeArgs()
+    a.struct_size = ctypes.sizeof(_abi.DecodeArgs)
+    a.Ra, a.R, a.L, a.Hq, a.Hkv, a.D = Ra, R, L, Hq, Hkv, D
+    a.dtype, a.block_size, a.Y, a.scale = _dtype(k_pool), bs, Y, scale
+    a.n_cap, a.pool_blocks = state.shape[3], P
+    a.req, a.q, a.lse, a.k_pool = _ptr(req), _ptr(q), _ptr(lse), _ptr(k_pool)
+    a.block_table, a.n_ctx, a.n_seen, a.state = _ptr(block_table), _ptr(n_ctx), _ptr(n_seen), _ptr(state)
+    _check(_abi.load().kvsel_decode_score(ctypes.byref(a), _stream(stream)))
+
+
+def keep_score(state, keep, n_len, *, lam, top_p=0.9, req=None, attn_score=None, hit=None, workspace=None,
+               stream=None):
+    """kvsel_keep_score.  state [L][R][Hkv][n_cap] float32 running means;
+    keep [R][n_cap] float32 keep scores, updated in place; n_len [R] int32;
+    req [Rc] int32 or None (all R); attn_score [R][n_cap] float32 and hit
+    [R][n_cap] uint8 optional outputs.  Returns the workspace it used."""
+    L, R, Hkv, n_cap = state.shape
+    Rc = R if req is None else req.shape[0]
+    a = _abi.KeepScoreArgs()
+    a.struct_size = ctypes.sizeof(_abi.KeepScoreArgs)
+    a.Rc, a.R, a.L, a.Hkv, a.reserved, a.n_cap = Rc, R, L, Hkv, 0, n_cap
+    a.lam, a.top_p = lam, top_p
+    a.req, a.n_len, a.state, a.keep_score = _ptr(req), _ptr(n_len), _ptr(state), _ptr(keep)
+    a.attn_score, a.hit = _ptr(attn_score), _ptr(hit)
+    lib = _abi.load()
+    nb = ctypes.c_size_t(0)
+    _check(lib.kvsel_keep_score_workspace(ctypes.byref(a), ctypes.byref(nb)))
+    ws, wsz = _workspace(nb.value, state.device, workspace)
+    _check(lib.kvsel_keep_score(ctypes.byref(a), _ptr(ws), wsz, _stream(stream)))
+    return ws

@@ -21,7 +21,10 @@ Workloads (shapes of the settings the three pages describe):
   actkv       in-place tail compaction of paged KV: 64 requests of 6144 positions
               in 16-slot blocks compressed to 4096 kept entries (4 sink + 64
               recent + the rest drawn denser toward the tail), 36 layers of
-              8 KV heads, D 128, bf16 pools
+              8 KV heads, D 128, bf16 pools; the same shape for the action
+              scorer's running means (5 action tokens already folded in), the
+              LRFU keep score (lambda 0.5, top-p 0.9) and one decode token of
+              the recovery scorer over all 64 requests (32 query heads)
 """
 import dataclasses
 import math
@@ -81,7 +84,7 @@ CONFIGS = {
                        n_recent=4, dtype=torch.bfloat16, W=512, bt=32, theta=1e6, raw_layers=1,
                        S=4, tile=65536),
     "actkv": Config("actkv", 1006, L=36, Hkv=8, Hq=32, D=128, N=6144, k=4096, n_sink=4, n_recent=64,
-                    page_size=16, S=64),
+                    page_size=16, S=64, turns=5, decay=0.5),
 }
 
 
@@ -280,3 +283,63 @@ def actkv_inputs(cfg, device, spare_blocks=64):
         k_pool[l] = _randn(k_pool.shape[1:], g, device).to(cfg.dtype)
         v_pool[l] = _randn(v_pool.shape[1:], g, device).to(cfg.dtype)
     return dict(keep=keep, block_table=block_table, k_pool=k_pool, v_pool=v_pool)
+
+
+def actkv_state(cfg, device, salt=7):
+    """Running means of an action region, [L][S][Hkv][N] float32: per
+    (layer, request, KV head) row a softmax over positions of the logits
+    1.5 * j / N + z[r, j] + N(0, 0.75^2), with z ~ N(0, 1.5^2) shared by every
+    layer and head of a request (the same entries matter across heads), so
+    the rows are heavy-tailed, denser toward the tail and sum to 1, as the
+    recovery scorer leaves them."""
+    g = _gen(cfg, device, salt)
+    R, N = cfg.S, cfg.N
+    ramp = 1.5 * torch.arange(N, device=device, dtype=torch.float32) / N
+    shared = ramp + _randn((R, 1, N), g, device, std=1.5)
+    st = torch.empty((cfg.L, R, cfg.Hkv, N), dtype=torch.float32, device=device)
+    for l in range(cfg.L):
+        st[l] = torch.softmax(shared + _randn((R, cfg.Hkv, N), g, device, std=0.75), dim=-1)
+    return st
+
+
+def actkv_decode_inputs(cfg, device, spare_blocks=64):
+    """One decode token of every request for the recovery scorer.
+
+    Keys carry a per-(request, position) relevance rel ~ N(0, 4^2) along one
+    unit direction u[l, g] per (layer, KV head): K = e + rel * u with
+    e ~ N(0, I), in a pool of [L][S*Y + spare][page_size][Hkv][D] in blocks of
+    a seeded permutation.  Queries (post-RoPE) are N(0, I) + 8 u[l, g(h)], so
+    the logits spread with a standard deviation near 3 and attention is
+    heavy-tailed.  The LSE is what a paged attention pass returns for these
+    queries: the float32 log-sum-exp of the scaled logits over the first
+    n_ctx = N positions, computed here with torch on the device (input
+    synthesis; the scorer only consumes it).  n_seen = cfg.turns action
+    tokens are already in the state (``actkv_state``)."""
+    g = _gen(cfg, device, 11)
+    R, N, bs, L, Hkv, D, Hq = cfg.S, cfg.N, cfg.page_size, cfg.L, cfg.Hkv, cfg.D, cfg.Hq
+    G = Hq // Hkv
+    Y = (N + bs - 1) // bs
+    P = R * Y + spare_blocks
+    block_table = torch.randperm(P, generator=g, device=device)[: R * Y].view(R, Y).to(torch.int32)
+    rel = _randn((R, Y * bs), g, device, std=4.0)
+    # relevance of every physical slot (0 for the spare blocks)
+    rel_phys = torch.zeros((P, bs), dtype=torch.float32, device=device)
+    rel_phys[block_table.long().view(-1)] = rel.view(R * Y, bs)
+    u = _randn((L, Hkv, D), g, device)
+    u = u / u.norm(dim=-1, keepdim=True)
+    k_pool = torch.empty((L, P, bs, Hkv, D), dtype=cfg.dtype, device=device)
+    q = torch.empty((L, R, Hq, D), dtype=cfg.dtype, device=device)
+    lse = torch.empty((L, R, Hq), dtype=torch.float32, device=device)
+    scale = 1.0 / math.sqrt(D)
+    for l in range(L):
+        k_pool[l] = (_randn((P, bs, Hkv, D), g, device) + rel_phys[:, :, None, None] * u[l][None, None]).to(cfg.dtype)
+        q[l] = (_randn((R, Hq, D), g, device) + 8.0 * u[l].repeat_interleave(G, dim=0)[None]).to(cfg.dtype)
+        keys = k_pool[l][block_table.long()].reshape(R, Y * bs, Hkv, D)[:, :N].float()     # [R][N][Hkv][D]
+        keys = keys.permute(0, 2, 1, 3).contiguous()                                       # [R][Hkv][N][D]
+        qg = q[l].float().view(R, Hkv, G, D).transpose(2, 3).contiguous()                  # [R][Hkv][D][G]
+        logits = torch.matmul(keys, qg) * scale                                            # [R][Hkv][N][G]
+        lse[l] = torch.logsumexp(logits, dim=2).reshape(R, Hq)
+        del keys, logits
+    n_ctx = torch.full((R,), N, dtype=torch.int32, device=device)
+    n_seen = torch.full((R,), cfg.turns, dtype=torch.int32, device=device)
+    return dict(block_table=block_table, k_pool=k_pool, q=q, lse=lse, n_ctx=n_ctx, n_seen=n_seen)

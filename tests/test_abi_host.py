@@ -39,6 +39,8 @@ STRUCTS = {
     "kvsel_index_args": _abi.IndexArgs,
     "kvsel_freelist_args": _abi.FreeListArgs,
     "kvsel_compact_args": _abi.CompactArgs,
+    "kvsel_decode_args": _abi.DecodeArgs,
+    "kvsel_keep_score_args": _abi.KeepScoreArgs,
 }
 
 
@@ -222,3 +224,62 @@ def test_compact_validation_without_device():
         setattr(a, field, good)
     a.R = 0
     assert lib.kvsel_compact(ctypes.byref(a), None, 0, None) == _abi.KVSEL_OK
+
+
+def _decode_args():
+    a = _abi.DecodeArgs()
+    a.struct_size = ctypes.sizeof(a)
+    a.Ra, a.R, a.L, a.Hq, a.Hkv, a.D, a.dtype, a.block_size, a.Y = 4, 8, 2, 32, 8, 128, _abi.BF16, 16, 10
+    a.n_cap, a.pool_blocks = 160, 100
+    a.q, a.lse, a.k_pool, a.block_table = 0x1000, 0x2000, 0x3000, 0x4000
+    a.n_ctx, a.n_seen, a.state = 0x5000, 0x6000, 0x7000
+    return a
+
+
+def test_decode_score_validation_without_device():
+    lib = _abi.load()
+    for field, bad, want in [("D", 96, _abi.KVSEL_E_UNSUPPORTED), ("dtype", _abi.F32, _abi.KVSEL_E_UNSUPPORTED),
+                             ("Hq", 30, _abi.KVSEL_E_ARG), ("Hq", 8 * 17, _abi.KVSEL_E_UNSUPPORTED),
+                             ("block_size", 24, _abi.KVSEL_E_UNSUPPORTED), ("q", 0x1008, _abi.KVSEL_E_ARG),
+                             ("state", 0, _abi.KVSEL_E_ARG), ("lse", 0x2002, _abi.KVSEL_E_ARG),
+                             ("Ra", 9, _abi.KVSEL_E_ARG), ("n_cap", (1 << 30) + 1, _abi.KVSEL_E_ARG),
+                             ("scale", float("inf"), _abi.KVSEL_E_ARG), ("Y", 0, _abi.KVSEL_E_ARG)]:
+        a = _decode_args()
+        setattr(a, field, bad)
+        assert lib.kvsel_decode_score(ctypes.byref(a), None) == want, field
+    a = _decode_args()
+    a.Ra, a.req = 9, 0x8000                             # an explicit request list may exceed R
+    a.Hq = 8 * 17
+    assert lib.kvsel_decode_score(ctypes.byref(a), None) == _abi.KVSEL_E_UNSUPPORTED
+    a = _decode_args()
+    a.Ra = 0
+    assert lib.kvsel_decode_score(ctypes.byref(a), None) == _abi.KVSEL_OK
+
+
+def _keep_args():
+    a = _abi.KeepScoreArgs()
+    a.struct_size = ctypes.sizeof(a)
+    a.Rc, a.R, a.L, a.Hkv, a.n_cap = 3, 4, 2, 8, 100
+    a.lam, a.top_p = 0.5, 0.9
+    a.n_len, a.state, a.keep_score = 0x1000, 0x2000, 0x3000
+    return a
+
+
+def test_keep_score_validation_and_workspace_without_device():
+    lib = _abi.load()
+    nb = ctypes.c_size_t(0)
+    a = _keep_args()
+    assert lib.kvsel_keep_score_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_OK
+    assert nb.value == 3 * 100 * 4                       # scores of the compressing requests
+    assert lib.kvsel_keep_score(ctypes.byref(a), None, 0, None) == _abi.KVSEL_E_WORKSPACE
+    a.attn_score = 0x4000
+    assert lib.kvsel_keep_score_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_OK
+    assert nb.value == 0
+    for field, bad in [("lam", 1.5), ("lam", -0.1), ("top_p", 0.0), ("top_p", 1.01), ("Rc", 5),
+                       ("keep_score", 0), ("state", 0x2002), ("L", 0), ("n_cap", -1)]:
+        a = _keep_args()
+        setattr(a, field, bad)
+        assert lib.kvsel_keep_score_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_E_ARG, field
+    a = _keep_args()
+    a.Rc = 0
+    assert lib.kvsel_keep_score(ctypes.byref(a), None, 0, None) == _abi.KVSEL_OK
