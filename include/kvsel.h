@@ -8,7 +8,12 @@
  * re-RoPEd view (kvsel_gather_rerope, KVMem "tiered movement") or a slot-map
  * redirect to a dead slot with survivors left in place (kvsel_redirect,
  * IntentKV §2 Q2 and §4 "redirect").  kvsel_memory_update maintains the
- * session query memory that IntentKV §4 scores against.
+ * session query memory that IntentKV §4 scores against.  For ActKV's own
+ * policy, kvsel_decode_score keeps a running mean of recovered attention
+ * over each action region (§7.1, Algorithm 3), kvsel_keep_score turns it
+ * into LRFU keep scores at a compression step (§5.2), and kvsel_compact
+ * compacts the pool in place after eviction (§7.2).  kvsel_free_list and
+ * kvsel_build_index serve the redirect and block-scoring paths.
  *
  * Conventions shared by every call
  * --------------------------------

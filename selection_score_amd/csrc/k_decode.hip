@@ -166,61 +166,91 @@ hipError_t launch_decode_score(const DecodeParams& p, int dt, const void* q, con
 
 // ---------------------------------------------------------------- keep score
 
-constexpr int kReduceBatch = 8;   // units loaded ahead per step
+constexpr int kReduceQuads = 64;    // position quads per block (256 positions, 1 KiB per unit row)
+constexpr int kReduceGroups = 4;    // unit groups per block (thread = 64*group + quad)
+constexpr int kReduceBatch = 8;     // loads in flight per thread
 
 __device__ __forceinline__ void neumaier_add(double& s, double& c, double v) {
   const double t = s + v;
-  c += (s >= v) ? ((s - t) + v) : ((v - t) + s);
+  c += (fabs(s) >= fabs(v)) ? ((s - t) + v) : ((v - t) + s);
   s = t;
 }
 
 // attn[row][j] = float(sum over (l, g) of state[l][r][g][j]), j < n_len[r];
-// 0 for n_len[r] <= j < n_cap.  Four positions per thread.
+// 0 for n_len[r] <= j < n_cap.  A block covers 256 positions: 64 threads of
+// four positions each (1 KiB contiguous per unit row) times 4 groups of
+// units; each group keeps a compensated float64 partial and the first wave
+// merges the 4 partials in a fixed order.
 __global__ __launch_bounds__(256) void action_reduce_kernel(KeepScoreParams p, const float* __restrict__ state,
                                                             float* __restrict__ attn, int attn_by_req) {
+  __shared__ double part_s[kReduceGroups][4 * kReduceQuads], part_c[kReduceGroups][4 * kReduceQuads];
   const int a = blockIdx.y;
   const int r = (p.req != nullptr) ? p.req[a] : a;
   if (r < 0 || r >= p.R) return;
   const int64_t n = min(max(static_cast<int64_t>(p.n_len[r]), static_cast<int64_t>(0)), p.n_cap);
-  const int64_t j4 = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) * 4;
-  if (j4 >= p.n_cap) return;
+  const int quad = threadIdx.x % kReduceQuads, grp = threadIdx.x / kReduceQuads;
+  const int64_t j0 = static_cast<int64_t>(blockIdx.x) * 4 * kReduceQuads;
+  const int64_t j4 = j0 + 4 * quad;
   float* out = attn + static_cast<int64_t>(attn_by_req ? r : a) * p.n_cap;
-  float res[4] = {0.f, 0.f, 0.f, 0.f};
-  if (j4 < n) {
-    const int U = p.L * p.Hkv;
-    const bool vec = (p.n_cap % 4 == 0) && ((reinterpret_cast<uintptr_t>(state) & 15) == 0) && j4 + 3 < p.n_cap;
-    double s[4] = {0.0, 0.0, 0.0, 0.0}, c[4] = {0.0, 0.0, 0.0, 0.0};
-    for (int u0 = 0; u0 < U; u0 += kReduceBatch) {
-      float4 v[kReduceBatch];
+  if (j0 >= n) {
+    if (grp == 0)
+      for (int i = 0; i < 4; ++i)
+        if (j4 + i < p.n_cap) out[j4 + i] = 0.f;
+    return;
+  }
+  const int U = p.L * p.Hkv;
+  const bool vec = (p.n_cap % 4 == 0) && ((reinterpret_cast<uintptr_t>(state) & 15) == 0) && j4 + 3 < p.n_cap;
+  const int64_t jc = min(j4, p.n_cap - 1);
+  double s[4] = {0.0, 0.0, 0.0, 0.0}, c[4] = {0.0, 0.0, 0.0, 0.0};
+  for (int u0 = grp; u0 < U; u0 += kReduceGroups * kReduceBatch) {
+    float4 v[kReduceBatch];
 #pragma unroll
-      for (int b = 0; b < kReduceBatch; ++b) {
-        const int u = min(u0 + b, U - 1);
-        const int l = u / p.Hkv, g = u - l * p.Hkv;
-        const float* src = state + ((static_cast<int64_t>(l) * p.R + r) * p.Hkv + g) * p.n_cap;
-        if (vec) {
-          v[b] = *reinterpret_cast<const float4*>(src + j4);
-        } else {
-          v[b].x = src[j4];
-          v[b].y = src[min(j4 + 1, p.n_cap - 1)];
-          v[b].z = src[min(j4 + 2, p.n_cap - 1)];
-          v[b].w = src[min(j4 + 3, p.n_cap - 1)];
-        }
-      }
-#pragma unroll
-      for (int b = 0; b < kReduceBatch; ++b) {
-        if (u0 + b >= U) break;
-        neumaier_add(s[0], c[0], static_cast<double>(v[b].x));
-        neumaier_add(s[1], c[1], static_cast<double>(v[b].y));
-        neumaier_add(s[2], c[2], static_cast<double>(v[b].z));
-        neumaier_add(s[3], c[3], static_cast<double>(v[b].w));
+    for (int b = 0; b < kReduceBatch; ++b) {
+      const int u = min(u0 + kReduceGroups * b, U - 1);
+      const int l = u / p.Hkv, g = u - l * p.Hkv;
+      const float* src = state + ((static_cast<int64_t>(l) * p.R + r) * p.Hkv + g) * p.n_cap;
+      if (vec) {
+        v[b] = *reinterpret_cast<const float4*>(src + j4);
+      } else {
+        v[b].x = src[jc];
+        v[b].y = src[min(j4 + 1, p.n_cap - 1)];
+        v[b].z = src[min(j4 + 2, p.n_cap - 1)];
+        v[b].w = src[min(j4 + 3, p.n_cap - 1)];
       }
     }
 #pragma unroll
-    for (int i = 0; i < 4; ++i) res[i] = (j4 + i < n) ? static_cast<float>(s[i] + c[i]) : 0.f;
+    for (int b = 0; b < kReduceBatch; ++b) {
+      if (u0 + kReduceGroups * b >= U) break;
+      neumaier_add(s[0], c[0], static_cast<double>(v[b].x));
+      neumaier_add(s[1], c[1], static_cast<double>(v[b].y));
+      neumaier_add(s[2], c[2], static_cast<double>(v[b].z));
+      neumaier_add(s[3], c[3], static_cast<double>(v[b].w));
+    }
   }
 #pragma unroll
-  for (int i = 0; i < 4; ++i)
-    if (j4 + i < p.n_cap) out[j4 + i] = res[i];
+  for (int i = 0; i < 4; ++i) {
+    part_s[grp][4 * quad + i] = s[i];
+    part_c[grp][4 * quad + i] = c[i];
+  }
+  __syncthreads();
+  if (grp == 0) {
+    float res[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      double S = 0.0, C = 0.0;
+      for (int k = 0; k < kReduceGroups; ++k) {
+        neumaier_add(S, C, part_s[k][4 * quad + i]);
+        C += part_c[k][4 * quad + i];
+      }
+      res[i] = (j4 + i < n) ? static_cast<float>(S + C) : 0.f;
+    }
+    if (vec) {
+      *reinterpret_cast<float4*>(out + j4) = make_float4(res[0], res[1], res[2], res[3]);
+    } else {
+      for (int i = 0; i < 4; ++i)
+        if (j4 + i < p.n_cap) out[j4 + i] = res[i];
+    }
+  }
 }
 
 // Ordering bits of a non-negative score (anything not above zero maps to 0).
@@ -264,39 +294,49 @@ __global__ __launch_bounds__(kTopPThreads) void top_p_update_kernel(KeepScorePar
       if (match && key != 0u) atomicAdd(&wsum[(key >> shift) & 255u], static_cast<double>(v));
     }
     __syncthreads();
-    if (tid == 0) {
-      double rem;
-      if (pass == 0) {
-        double total = 0.0;
-        for (int b = 255; b >= 0; --b) total += wsum[b];
-        rem = static_cast<double>(p.top_p) * total;
-        if (!(rem > 0.0)) sh_none = 1;
-      } else {
-        rem = sh_rem;
+    if (wave == 0) {
+      // lane owns buckets 255 - 4*lane .. 252 - 4*lane (descending order)
+      double w[4];
+#pragma unroll
+      for (int i = 0; i < 4; ++i) w[i] = wsum[255 - 4 * lane - i];
+      const double loc = ((w[0] + w[1]) + w[2]) + w[3];
+      // weight above each lane's buckets, accumulated in lane order
+      double run = 0.0, above = 0.0;
+      for (int k = 0; k < 64; ++k) {
+        if (k == lane) above = run;
+        run += __shfl(loc, k);
       }
-      if (!sh_none) {
-        double cum = 0.0, cum_low = 0.0;
-        int chosen = -1, lowest = -1;
-        for (int b = 255; b >= 0; --b) {
-          const double w = wsum[b];
-          if (w > 0.0) {
-            if (cum + w >= rem) {
-              chosen = b;
-              break;
-            }
-            lowest = b;
-            cum_low = cum;
+      double rem = (pass == 0) ? static_cast<double>(p.top_p) * run : sh_rem;
+      const bool stop = !(rem > 0.0);
+      // first bucket (from the top) whose cumulative weight reaches rem, and
+      // the lowest non-empty bucket as the fallback when rounding leaves rem
+      // above every cumulative weight
+      int hit_i = -1, low_i = -1;
+      double hit_cum = 0.0, low_cum = 0.0, cb = above;
+#pragma unroll
+      for (int i = 0; i < 4; ++i) {
+        if (w[i] > 0.0) {
+          if (hit_i < 0 && cb + w[i] >= rem) {
+            hit_i = i;
+            hit_cum = cb;
           }
-          cum += w;
+          low_i = i;
+          low_cum = cb;
         }
-        if (chosen < 0) {
-          // rounding left the remainder above this bucket's entries: all of
-          // them are in, the boundary is the smallest
-          chosen = lowest;
-          cum = cum_low;
+        cb += w[i];
+      }
+      const uint64_t hits = __ballot(hit_i >= 0), lows = __ballot(low_i >= 0);
+      if (!stop && (hits | lows) != 0ull) {
+        const bool use_hit = hits != 0ull;
+        const int src = use_hit ? (__ffsll(static_cast<long long>(hits)) - 1) : (63 - __clzll(static_cast<long long>(lows)));
+        const int bi = __shfl(use_hit ? hit_i : low_i, src);
+        const double cum = __shfl(use_hit ? hit_cum : low_cum, src);
+        if (lane == 0) {
+          sh_prefix = prefix | (static_cast<uint32_t>(255 - 4 * src - bi) << shift);
+          sh_rem = rem - cum;
         }
-        sh_prefix = prefix | (static_cast<uint32_t>(chosen) << shift);
-        sh_rem = rem - cum;
+      } else if (lane == 0) {
+        sh_none = 1;
       }
     }
     __syncthreads();
@@ -362,7 +402,7 @@ hipError_t launch_keep_score(const KeepScoreParams& p, const float* state, float
   if (p.Rc == 0 || p.n_cap == 0) return hipSuccess;
   float* attn = attn_out ? attn_out : static_cast<float*>(ws);
   const int by_req = attn_out != nullptr;
-  const dim3 g1(static_cast<unsigned>(ceil_div(p.n_cap, 1024)), p.Rc);
+  const dim3 g1(static_cast<unsigned>(ceil_div(p.n_cap, 4 * kReduceQuads)), p.Rc);
   action_reduce_kernel<<<g1, 256, 0, st>>>(p, state, attn, by_req);
   top_p_update_kernel<<<p.Rc, kTopPThreads, 0, st>>>(p, attn, by_req, ks, hit);
   return hipGetLastError();
