@@ -274,3 +274,51 @@ def test_keep_score_full_size_sampled_requests():
         assert sub <= 1
         frac = hit_g[r].mean()
         assert 0.05 < frac < 0.95, frac                  # the top-p set is a real subset here
+
+
+def test_decode_edges_many_heads_clamps_and_skipped_rows():
+    # 16 KV heads (the workgroup loops over heads), an explicit scale, a
+    # request list with an out-of-range entry (skipped), n_ctx beyond the
+    # state and the block table (clamped), and a negative token count (a
+    # region start)
+    dev = require_gpu()
+    rng = np.random.default_rng(21)
+    L, R, Hq, Hkv, D, BS, n_cap = 2, 3, 32, 16, 64, 16, 100
+    G = Hq // Hkv
+    Y = 7                                                # 112 slots >= n_cap
+    P = R * Y + 2
+    bt = rng.permutation(P)[: R * Y].reshape(R, Y).astype(np.int32)
+    k_pool = torch.randn((L, P, BS, Hkv, D), generator=torch.Generator().manual_seed(2)).to(torch.bfloat16)
+    k64 = _f64(k_pool)
+    q = (torch.randn((L, 3, Hq, D), generator=torch.Generator().manual_seed(3)) * 2).to(torch.bfloat16)
+    q64 = _f64(q)
+    req = [2, 7, 0]                                      # row 1 names no request
+    n_ctx = np.array([500, 40, 60], dtype=np.int32)      # request 0 clamps to n_cap
+    n_seen = np.array([-3, 0, 2], dtype=np.int32)
+    scale = 0.3
+    lse = np.zeros((L, 3, Hq), dtype=np.float32)
+    for a, r in enumerate(req):
+        if r >= R:
+            lse[:, a] = 1.0
+            continue
+        n = min(int(n_ctx[r]), n_cap)
+        sm = paging.slot_map_from_block_table(bt[r], BS, n)
+        for l in range(L):
+            k = paging.logical_keys_from_pool(k64[l], sm, BS)
+            for h in range(Hq):
+                s = scale * (k[h // G] @ q64[l, a, h])
+                lse[l, a, h] = np.log(np.sum(np.exp(s - s.max()))) + s.max()
+    state0 = rng.random((L, R, Hkv, n_cap)).astype(np.float32)
+    state0[:, 2, :, 60:] = 0.0                           # request 2 is mid-region: zeros past its context
+    st = torch.from_numpy(state0.copy()).to(dev)
+    print("decode edges", flush=True)
+    kv.decode_score(q.to(dev), torch.from_numpy(lse).to(dev), k_pool.to(dev), torch.from_numpy(bt).to(dev),
+                    torch.from_numpy(n_ctx).to(dev), torch.from_numpy(n_seen).to(dev), st,
+                    req=torch.tensor(req, dtype=torch.int32, device=dev), scale=scale)
+    torch.cuda.synchronize()
+    rows = [2, 0]
+    want = osc.decode_recovery_step(state0.astype(np.float64), np.maximum(n_seen, 0), q64[:, [0, 2]],
+                                    lse[:, [0, 2]].astype(np.float64), k64, bt, np.minimum(n_ctx, n_cap),
+                                    req=rows, scale=scale)
+    _check_state(st.cpu().numpy(), want, "edges")
+    np.testing.assert_array_equal(st[:, 1].cpu().numpy(), state0[:, 1])    # untouched request
