@@ -142,7 +142,8 @@ def keep_score_step(state, ks, n_len, *, lam, top_p=0.9, req=None):
     """One compression step of the ActKV policy for the requests in ``req``.
 
     Per request r: AttnScore = action_scores (entries j < n_len[r]), hits =
-    top_p_hits, KS <- lrfu_keep_score.  Returns (ks [R][n_cap] float64,
+    top_p_hits, KS <- lrfu_keep_score; n_len is taken within [0, n_cap].
+    Returns (ks [R][n_cap] float64,
     hit [R][n_cap] bool, attn [R][n_cap] float64); entries j >= n_len[r]
     keep their KS and report no hit and score 0; requests not in ``req`` are
     unchanged with no hits and score 0.
@@ -154,7 +155,7 @@ def keep_score_step(state, ks, n_len, *, lam, top_p=0.9, req=None):
     req = np.arange(R) if req is None else np.asarray(req, dtype=np.int64)
     for r in req:
         r = int(r)
-        n = int(n_len[r])
+        n = min(max(int(n_len[r]), 0), n_cap)        # a row holds n_cap entries at most
         a = action_scores(state, r, n)
         h = top_p_hits(a, top_p)
         ks_new[r, :n] = lrfu_keep_score(ks_new[r, :n], a, h, lam)

@@ -322,3 +322,29 @@ def test_decode_edges_many_heads_clamps_and_skipped_rows():
                                     req=rows, scale=scale)
     _check_state(st.cpu().numpy(), want, "edges")
     np.testing.assert_array_equal(st[:, 1].cpu().numpy(), state0[:, 1])    # untouched request
+
+
+def test_keep_score_long_rows_odd_stride_and_misaligned_state():
+    # 100003 positions (the row stride is not a multiple of 4 and the state
+    # starts 4 bytes past a 16-byte boundary: the scalar load path), n_len
+    # past n_cap (clamped), 98 chunks of 1024 entries in the update pass
+    dev = require_gpu()
+    rng = np.random.default_rng(31)
+    L, R, Hkv, n_cap = 2, 2, 2, 100003
+    vals = (rng.random((L, R, Hkv, n_cap)) ** 8).astype(np.float32)
+    flat = torch.zeros(vals.size + 1, dtype=torch.float32, device=dev)
+    flat[1:] = torch.from_numpy(vals.reshape(-1)).to(dev)
+    sd = flat[1:].view(L, R, Hkv, n_cap)
+    assert sd.data_ptr() % 16 == 4
+    ks0 = (rng.random((R, n_cap)) * 1e-3).astype(np.float32)
+    ksd = torch.from_numpy(ks0.copy()).to(dev)
+    attn = torch.empty((R, n_cap), device=dev)
+    hit = torch.empty((R, n_cap), dtype=torch.uint8, device=dev)
+    n_len = [200000, 70001]
+    print("keep score long rows", flush=True)
+    kv.keep_score(sd, ksd, torch.tensor(n_len, dtype=torch.int32, device=dev), lam=0.5, top_p=0.9,
+                  attn_score=attn, hit=hit)
+    torch.cuda.synchronize()
+    near = _check_keep(vals.astype(np.float64), ks0.astype(np.float64), n_len, [0, 1], 0.5, 0.9,
+                       ksd.cpu().numpy(), hit.cpu().numpy(), attn.cpu().numpy())
+    assert near <= 1
