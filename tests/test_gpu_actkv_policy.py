@@ -348,3 +348,81 @@ def test_keep_score_long_rows_odd_stride_and_misaligned_state():
     near = _check_keep(vals.astype(np.float64), ks0.astype(np.float64), n_len, [0, 1], 0.5, 0.9,
                        ksd.cpu().numpy(), hit.cpu().numpy(), attn.cpu().numpy())
     assert near <= 1
+
+
+def test_compression_pipeline_decode_keep_select_compact():
+    # ActKV's chain on the GPU: three decode tokens of an action region, the
+    # LRFU keep score at the region's end, eviction to a budget by keep
+    # score, and the in-place tail compaction of K and V.  The oracle runs
+    # the same chain; the data has no near-ties, so the keep masks, slot maps
+    # and pools must agree exactly
+    from oracle import materialise as om
+    dev = require_gpu()
+    rng = np.random.default_rng(41)
+    L, R, Hq, Hkv, D, BS, N, T = 2, 3, 8, 2, 64, 16, 160, 3
+    G = Hq // Hkv
+    Y = N // BS
+    P = R * Y + 4
+    k_total, n_sink, n_recent, lam, top_p = 96, 4, 16, 0.5, 0.9
+    bt = rng.permutation(P)[: R * Y].reshape(R, Y).astype(np.int32)
+    gk = torch.Generator().manual_seed(42)
+    k_pool = torch.randn((L, P, BS, Hkv, D), generator=gk).to(torch.bfloat16)
+    v_pool = torch.randn((L, P, BS, Hkv, D), generator=gk).to(torch.bfloat16)
+    k64 = _f64(k_pool)
+    n_ctx = np.full(R, N, dtype=np.int32)
+    kd, vd, btd = k_pool.to(dev), v_pool.to(dev), torch.from_numpy(bt).to(dev)
+    st_gpu = torch.zeros((L, R, Hkv, N), device=dev)
+    st_ora = np.zeros((L, R, Hkv, N))
+    for t in range(T):
+        q = (torch.randn((L, R, Hq, D), generator=torch.Generator().manual_seed(50 + t)) * 2).to(torch.bfloat16)
+        q64 = _f64(q)
+        lse = _true_lse(q64, k64, bt, n_ctx, BS, G).astype(np.float32)
+        n_seen = np.full(R, t, dtype=np.int32)
+        kv.decode_score(q.to(dev), torch.from_numpy(lse).to(dev), kd, btd, torch.from_numpy(n_ctx).to(dev),
+                        torch.from_numpy(n_seen).to(dev), st_gpu)
+        st_ora = osc.decode_recovery_step(st_ora, n_seen, q64, lse.astype(np.float64), k64, bt, n_ctx)
+    ks0 = (rng.random((R, N)) * 0.02).astype(np.float32)
+    ks_gpu = torch.from_numpy(ks0.copy()).to(dev)
+    kv.keep_score(st_gpu, ks_gpu, torch.from_numpy(n_ctx).to(dev), lam=lam, top_p=top_p)
+    kept = torch.empty((R, k_total), dtype=torch.int32, device=dev)
+    keep = torch.empty((R, N), dtype=torch.uint8, device=dev)
+    kv.select(ks_gpu, kept, k_total=k_total, n_sink=n_sink, n_recent=n_recent, keep_mask=keep)
+    slot_pos = torch.empty((R, Y * BS), dtype=torch.int32, device=dev)
+    freed = torch.empty((R, Y), dtype=torch.int32, device=dev)
+    nfr = torch.empty(R, dtype=torch.int32, device=dev)
+    print("actkv pipeline", flush=True)
+    kv.compact(keep, btd, kd, vd, slot_pos, freed, nfr, block_size=BS)
+    torch.cuda.synchronize()
+
+    ks_ora, _, _ = osel.keep_score_step(st_ora, ks0.astype(np.float64), n_ctx, lam=lam,
+                                        top_p=float(np.float32(top_p)))
+    for r in range(R):
+        # the top-p boundary is also well clear: the GPU's running means differ
+        # from the oracle's by ~1e-6 relative, far below this margin
+        a = osel.action_scores(st_ora, r, N)
+        cum = np.cumsum(np.sort(a)[::-1])
+        target = float(np.float32(top_p)) * cum[-1]
+        m = int(np.searchsorted(cum, target)) + 1
+        assert cum[m - 1] - target > 1e-4 * cum[-1] and target - cum[m - 2] > 1e-4 * cum[-1]
+    ks32 = ks_ora.astype(np.float32).astype(np.float64)
+    np.testing.assert_allclose(ks_gpu.cpu().numpy(), ks32, rtol=1e-4, atol=0)
+    want_k, want_v = k_pool.clone(), v_pool.clone()
+    for r in range(R):
+        idx, mask = osel.select_topk(ks32[r], k_total, n_sink, n_recent)
+        # the oracle's boundary is well clear of ties, so the GPU's keep
+        # scores (within 1e-4) must pick the same set
+        cand = np.sort(ks32[r][n_sink:N - n_recent])[::-1]
+        room = k_total - n_sink - n_recent
+        assert (cand[room - 1] - cand[room]) > 1e-4 * cand[room - 1], (r, cand[room - 1], cand[room])
+        np.testing.assert_array_equal(keep[r].cpu().numpy().astype(bool), mask)
+        np.testing.assert_array_equal(kept[r].cpu().numpy(), idx)
+        for l in range(L):
+            kp, vp, pos, fb = om.tail_compact(mask, bt[r], BS, want_k[l].view(torch.int16).numpy(),
+                                              want_v[l].view(torch.int16).numpy())
+            want_k[l] = torch.from_numpy(kp).view(torch.bfloat16)
+            want_v[l] = torch.from_numpy(vp).view(torch.bfloat16)
+        np.testing.assert_array_equal(slot_pos[r].cpu().numpy(), pos)
+        assert nfr[r].item() == len(fb)
+        np.testing.assert_array_equal(freed[r, : len(fb)].cpu().numpy(), fb)
+    assert torch.equal(kd.cpu().view(torch.int16), want_k.view(torch.int16))
+    assert torch.equal(vd.cpu().view(torch.int16), want_v.view(torch.int16))
