@@ -188,6 +188,19 @@ def _dead_slot_case(q_sign, D=128, N=40, seed=51):
     return q, pool_k, pool_v, slot_map, redirected, keep, dead
 
 
+def test_decode_attention_two_key_closed_form():
+    # D = 4, q = (2,0,0,0): logits q.k/sqrt(4) are 1 for k0 = e0 and 0 for k1 = 0,
+    # so o = (e v0 + v1) / (e + 1); the slot map reads slots 3 and 1
+    pool_k = np.zeros((4, 4)); pool_k[3, 0] = 1.0
+    pool_v = np.zeros((4, 4)); pool_v[3] = [1.0, 2.0, 0.0, 0.0]; pool_v[1] = [0.0, 0.0, 4.0, 8.0]
+    q = np.array([2.0, 0.0, 0.0, 0.0])
+    e = math.e
+    want = (e * pool_v[3] + pool_v[1]) / (e + 1)
+    np.testing.assert_allclose(om.decode_attention_slots(q, pool_k, pool_v, [3, 1]), want, atol=1e-15)
+    np.testing.assert_allclose(om.decode_attention_hard(q, pool_k, pool_v, [3, 1, 2], [1, 1, 0]), want,
+                               atol=1e-15)
+
+
 @pytest.mark.parametrize("q_sign", [1.0, -1.0, 0.0])
 def test_dead_slot_closed_form(q_sign):
     q, pool_k, pool_v, slot_map, redirected, keep, dead = _dead_slot_case(q_sign)
@@ -228,8 +241,10 @@ def test_free_list_hand_example():
     sm = [5, 6, 6, 7, D, 9, 5, 10, 11, 11]
     keep = [1, 0, 1, 0, 0, 0, 0, 1, 0, 0]
     np.testing.assert_array_equal(om.free_list(sm, keep, D), [7, 9, 11])
-    # a radix-protected prefix of 4 positions keeps slot 7 allocated
+    # a radix-protected prefix of 4 positions keeps slot 7 (position 3) allocated;
+    # a prefix of 3 stops just before it
     np.testing.assert_array_equal(om.free_list(sm, keep, D, protected_len=4), [9, 11])
+    np.testing.assert_array_equal(om.free_list(sm, keep, D, protected_len=3), [7, 9, 11])
     # nothing dropped, or everything protected: nothing freed
     assert om.free_list(sm, [1] * 10, D).size == 0
     assert om.free_list(sm, keep, D, protected_len=10).size == 0

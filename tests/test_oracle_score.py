@@ -90,21 +90,27 @@ def test_lse_recovery_equals_self_normalised_and_shifts_scale():
 
 
 def test_max_over_group_then_mean_over_rows():
-    # two heads in one group, one window row each at W = 2 rows
-    N, D = 3, 2
+    # two heads in one group, W = 2 rows, one-hot queries and keys with
+    # logits 2, 1, 3 for the key each row prefers (0 elsewhere); head 0's two
+    # rows prefer different keys, so max-then-mean and mean-then-max differ
+    N, D = 3, 3
     q = np.zeros((1, 2, 2, D))
-    q[0, 0, :, 0] = 1.0           # head 0 prefers key 0
-    q[0, 1, :, 1] = 1.0           # head 1 prefers key 1
+    q[0, 0, 0, 0] = 1.0           # head 0, row 0 -> key 0
+    q[0, 0, 1, 2] = 1.0           # head 0, row 1 -> key 2
+    q[0, 1, :, 1] = 1.0           # head 1, both rows -> key 1
     k = np.zeros((1, 1, N, D))
-    k[0, 0, 0, 0] = math.sqrt(2) * 2.0
-    k[0, 0, 1, 1] = math.sqrt(2) * 1.0
+    for j, v in enumerate([2.0, 1.0, 3.0]):
+        k[0, 0, j, j] = math.sqrt(D) * v
     a, _ = score.window_scores(q, k, causal=False, head_agg="max", row_agg="mean")
-    e2, e1 = math.exp(2.0), math.exp(1.0)
-    h0 = np.array([e2, 1, 1]) / (e2 + 2)
-    h1 = np.array([1, e1, 1]) / (e1 + 2)
-    np.testing.assert_allclose(a[0, 0], np.maximum(h0, h1), atol=1e-15)
+    e = math.e
+    h0r0 = np.array([e ** 2, 1, 1]) / (e ** 2 + 2)
+    h0r1 = np.array([1, 1, e ** 3]) / (e ** 3 + 2)
+    h1 = np.array([1, e, 1]) / (e + 2)
+    want = (np.maximum(h0r0, h1) + np.maximum(h0r1, h1)) / 2
+    np.testing.assert_allclose(a[0, 0], want, atol=1e-15)
+    assert not np.allclose(want, np.maximum((h0r0 + h0r1) / 2, h1))      # the order matters here
     s, _ = score.window_scores(q, k, causal=False, head_agg="sum", row_agg="mean")
-    np.testing.assert_allclose(s[0, 0], h0 + h1, atol=1e-15)
+    np.testing.assert_allclose(s[0, 0], (h0r0 + h0r1) / 2 + h1, atol=1e-15)
 
 
 def test_planted_high_norm_keys_rank_first():
