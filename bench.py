@@ -107,6 +107,19 @@ def _traffic(kernel, source, workload):
     return t.get("bytes_per_launch")
 
 
+def _stage_traffic(wk, stage, workload):
+    """Counter bytes of a stage per step: its kernel's summary for a
+    one-launch stage, the sum over its launches' summaries otherwise (None
+    unless every one is current)."""
+    if stage in wk.kernels:
+        return _traffic(*wk.kernels[stage], workload)
+    parts = getattr(wk, "stage_kernels", {}).get(stage)
+    if not parts:
+        return None
+    vals = [_traffic(k, src, workload) for k, src in parts]
+    return None if any(v is None for v in vals) else sum(vals)
+
+
 def _copy_pair(device):
     import torch
     a = torch.empty(COPY_BYTES // 4, dtype=torch.float32, device=device)
@@ -310,6 +323,8 @@ class IntentKV:
     stages = ["update", "score", "select", "free", "redirect"]
     kernels = {"update": ("memory_update_vec_kernel", "k_misc.hip")}
     launches = {"update": 1, "score": 4, "select": 2, "free": 4, "redirect": 2}
+    stage_kernels = {"score": [("memory_logits_mfma_kernel", "k_memory.hip"), ("memory_lse_kernel", "k_memory.hip"),
+                               ("memory_rule_kernel", "k_memory.hip"), ("memory_layer_sum_kernel", "k_memory.hip")]}
     score_stage = "score"
     materialise_stages = ["select", "free", "redirect"]
     dtype = "bf16"
@@ -448,6 +463,8 @@ class KVMem10M:
     stages = ["tiles", "update"]
     kernels = {}
     launches = {"tiles": 16, "update": 2}
+    stage_kernels = {"update": [("incremental_plan_kernel", "k_incremental.hip"),
+                                ("incremental_data_kernel", "k_incremental.hip")]}
     score_stage = "tiles"
     materialise_stages = ["update"]
     dtype = "bf16"
@@ -606,6 +623,7 @@ class ActKVCompact:
     stages = ["keep_score", "select", "compact"]
     kernels = {}
     launches = {"keep_score": 2, "select": 2, "compact": 2}
+    stage_kernels = {"compact": [("compact_plan_kernel", "k_compact.hip"), ("compact_copy_kernel", "k_compact.hip")]}
     score_stage = "keep_score"
     materialise_stages = ["select", "compact"]
     dtype = "bf16"
@@ -805,7 +823,7 @@ def main():
         "copy_reference_gbps": copy_gbps,
         "roofline": {"bound": "hbm", "kernel": stem, "achieved": achieved,
                      "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": achieved / HBM_PEAK_GBPS,
-                     "traffic": _traffic(stem, src, args.workload) if src else None, "algorithmic_bytes": algo[dom],
+                     "traffic": _stage_traffic(wk, dom, args.workload), "algorithmic_bytes": algo[dom],
                      "launch_ms": stage[dom]},
         "cpu_baseline": None,
     }
