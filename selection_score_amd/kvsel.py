@@ -37,6 +37,26 @@ def _ptr(t):
     return t.data_ptr()
 
 
+def _want(t, name, dtype=None, shape=None, numel=None):
+    """Check a tensor the C call will address through a raw pointer: its
+    dtype, its exact shape, or at least `numel` elements.  A wrong size would
+    let a kernel read or write past the buffer, so it is refused here."""
+    if t is None:
+        return None
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError("%s must be %s, got %s" % (name, dtype, t.dtype))
+    if shape is not None and tuple(t.shape) != tuple(shape):
+        raise ValueError("%s must have shape %s, got %s" % (name, tuple(shape), tuple(t.shape)))
+    if numel is not None and t.numel() < numel:
+        raise ValueError("%s needs at least %d elements, has %d" % (name, numel, t.numel()))
+    return t
+
+
+def _wptr(t, name, dtype=None, shape=None, numel=None):
+    """_want, then the tensor's device pointer."""
+    return _ptr(_want(t, name, dtype, shape, numel))
+
+
 def _dtype(t):
     if t.dtype not in _DT:
         raise ValueError("unsupported dtype %s" % t.dtype)
@@ -86,11 +106,12 @@ def score_window(q, k, out, *, causal=True, lse_in=None, lse_out=None, head_agg=
     a.L, a.Hq, a.Hkv, a.D, a.W, a.S, a.N = L, Hq, Hkv, D, W, 1, N
     a.q, a.k = _ptr(q), _ptr(k)
     a.causal = 1 if causal else 0
-    a.lse_in, a.lse_out = _ptr(lse_in), _ptr(lse_out)
+    a.lse_in = _wptr(lse_in, "lse_in", torch.float32, (L, Hq, W))
+    a.lse_out = _wptr(lse_out, "lse_out", torch.float32, (L, Hq, W))
     a.head_agg, a.row_agg = _abi.AGG[head_agg], _abi.AGG[row_agg]
     a.pool, a.pool_k = _abi.POOL[pool], pool_k
     a.scale = scale
-    a.scores = _ptr(out)      # None with lse_out given: compute the LSE only
+    a.scores = _wptr(out, "out", torch.float32, numel=L * Hkv * N)   # None with lse_out: LSE only
     return _score_call(a, q.device, workspace, stream)
 
 
@@ -108,14 +129,15 @@ def score_memory(m, k_pool, page_table, n, out, *, page_size, slot_map=None, dea
     a.mode = _abi.SCORE_MEMORY
     a.q_dtype, a.k_dtype = _dtype(m), _dtype(k_pool)
     a.L, a.Hq, a.Hkv, a.D, a.W, a.S, a.N = L, Hq, Hkv, D, 1, 1, n
-    a.q, a.k = _ptr(m), _ptr(k_pool)
-    a.page_table, a.page_size, a.pool_pages = _ptr(page_table), page_size, P
-    a.slot_map, a.dead_slot = _ptr(slot_map), dead_slot
+    a.q, a.k = _wptr(m, "m", torch.float32), _ptr(k_pool)
+    a.page_table = _wptr(page_table, "page_table", torch.int32, numel=-(-n // page_size))
+    a.page_size, a.pool_pages = page_size, P
+    a.slot_map, a.dead_slot = _wptr(slot_map, "slot_map", torch.int32, numel=n), dead_slot
     a.n_sink, a.n_recent = n_sink, n_recent
     a.reduce = _abi.REDUCE[reduce]
     a.pool, a.pool_k = _abi.POOL[pool], pool_k
     a.scale = scale
-    a.scores = _ptr(out)
+    a.scores = _wptr(out, "out", torch.float32, numel=n if reduce == "global" else L * Hkv * n)
     return _score_call(a, m.device, workspace, stream)
 
 
@@ -139,11 +161,11 @@ def score_block(q, mu, out, *, n_kv_heads, n_begin=0, n_count=None, qbar=None, q
         a.q_dtype = _abi.F32
     a.k_dtype = _dtype(mu)
     a.L, a.Hq, a.Hkv, a.D, a.W, a.S, a.N = L, Hq, Hkv, D, W, S, NB
-    a.q, a.k = _ptr(q), _ptr(mu)
+    a.q, a.k = _ptr(q), _wptr(mu, "mu", torch.float16)
     a.n_begin, a.n_count = n_begin, n_count
-    a.qbar, a.qbar_valid = _ptr(qbar), 1 if qbar_valid else 0
+    a.qbar, a.qbar_valid = _wptr(qbar, "qbar", torch.float32, (S, L, Hkv, D)), 1 if qbar_valid else 0
     a.scale = scale
-    a.scores = _ptr(out)
+    a.scores = _wptr(out, "out", torch.float32, numel=S * L * Hkv * n_count)
     return _score_call(a, mu.device, workspace, stream)
 
 
@@ -161,12 +183,20 @@ def select(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0,
         n_total = base + n
     if scores.stride(1) != 1:
         raise ValueError("score rows must be contiguous")
+    if scores.dtype != torch.float32:
+        raise TypeError("scores must be float32")
     a = _abi.SelectArgs()
     a.struct_size = ctypes.sizeof(_abi.SelectArgs)
     a.U, a.n, a.row_stride = U, n, scores.stride(0)
     a.scores = scores.data_ptr() if scores.is_cuda else None
     a.base, a.n_total = base, n_total
     a.k_total, a.n_sink, a.n_recent = k_total, n_sink, n_recent
+    for t, name, dt, numel in ((slot_map, "slot_map", torch.int32, n_total),
+                               (cand_score, "cand_score", torch.float32, U * k_total),
+                               (cand_idx, "cand_idx", torch.int32, U * k_total), (cand_count, "cand_count", torch.int32, U),
+                               (kept_idx, "kept_idx", torch.int32, U * k_total),
+                               (keep_mask, "keep_mask", torch.uint8, U * n_total), (n_kept, "n_kept", torch.int32, U)):
+        _want(t, name, dt, numel=numel)
     a.slot_map, a.dead_slot = _ptr(slot_map), dead_slot
     a.cand_score, a.cand_idx, a.cand_count = _ptr(cand_score), _ptr(cand_idx), _ptr(cand_count)
     a.finalize = 1 if finalize else 0
@@ -189,8 +219,9 @@ def _gather_args(src_k, src_v, idx, *, bt, D, src_rows, src_offsets, src_unit_st
     a.U, a.k = idx.shape
     a.D, a.dtype, a.bt = D, _dtype(src_k), bt
     a.src_k, a.src_v = _ptr(src_k), _ptr(src_v)
-    a.src_offsets, a.src_unit_stride, a.src_rows = _ptr(src_offsets), src_unit_stride, src_rows
-    a.idx = _ptr(idx)
+    a.src_offsets = _wptr(src_offsets, "src_offsets", torch.int64, numel=a.U)
+    a.src_unit_stride, a.src_rows = src_unit_stride, src_rows
+    a.idx = _wptr(idx, "idx", torch.int32)
     a.rope, a.style, a.rotary_dim = _abi.ROPE[rope], _abi.STYLE[style], rotary_dim
     a.theta, a.pos0 = theta, pos0
     return a
@@ -204,8 +235,10 @@ def gather_rerope(src_k, src_v, idx, dst_k, dst_v, *, bt, D, src_rows, src_offse
                      src_unit_stride=src_unit_stride, rope=rope, theta=theta, pos0=pos0, style=style,
                      rotary_dim=rotary_dim)
     a.mode = _abi.GATHER_FRESH
-    a.n_idx = _ptr(n_idx)
-    a.dst_k, a.dst_v = _ptr(dst_k), _ptr(dst_v)
+    a.n_idx = _wptr(n_idx, "n_idx", torch.int32, numel=a.U)
+    rows = a.U * a.k * bt * D
+    a.dst_k = _wptr(dst_k, "dst_k", src_k.dtype, numel=rows)
+    a.dst_v = _wptr(dst_v, "dst_v", src_v.dtype, numel=rows)
     lib = _abi.load()
     _check(lib.kvsel_gather_rerope(ctypes.byref(a), None, 0, _stream(stream)))
 
@@ -219,9 +252,11 @@ def gather_incremental(src_k, src_v, idx, prev_idx, prev_page, pool_k, pool_v, p
                      src_unit_stride=src_unit_stride, rope=rope, theta=theta, pos0=pos0, style=style,
                      rotary_dim=rotary_dim)
     a.mode = _abi.GATHER_INCREMENTAL
-    a.prev_idx, a.prev_page = _ptr(prev_idx), _ptr(prev_page)
+    a.prev_idx = _wptr(prev_idx, "prev_idx", torch.int32, numel=a.U * a.k)
+    a.prev_page = _wptr(prev_page, "prev_page", torch.int32, numel=a.U * a.k)
     a.pool_k, a.pool_v, a.pool_pages = _ptr(pool_k), _ptr(pool_v), pool_k.shape[1]
-    a.page_table, a.n_miss = _ptr(page_table), _ptr(n_miss)
+    a.page_table = _wptr(page_table, "page_table", torch.int32, numel=a.U * a.k)
+    a.n_miss = _wptr(n_miss, "n_miss", torch.int32, numel=a.U)
     lib = _abi.load()
     nb = ctypes.c_size_t(0)
     _check(lib.kvsel_gather_workspace(ctypes.byref(a), ctypes.byref(nb)))
@@ -239,7 +274,9 @@ def redirect(slot_map, keep_mask, dead_slot, *, k_pool=None, v_pool=None, stream
     a = _abi.RedirectArgs()
     a.struct_size = ctypes.sizeof(_abi.RedirectArgs)
     a.N = slot_map.numel()
-    a.slot_map, a.keep_mask, a.dead_slot = _ptr(slot_map), _ptr(keep_mask), dead_slot
+    a.slot_map = _wptr(slot_map, "slot_map", torch.int32)
+    a.keep_mask = _wptr(keep_mask, "keep_mask", torch.uint8, numel=a.N)
+    a.dead_slot = dead_slot
     if k_pool is not None:
         L, slots, Hkv, D = k_pool.shape
         a.k_pool, a.v_pool = _ptr(k_pool), _ptr(v_pool)
@@ -255,7 +292,7 @@ def memory_update(q_turn, m, *, decay=0.9, stream=None):
     a.struct_size = ctypes.sizeof(_abi.MemUpdArgs)
     a.L, a.Hq, a.D, a.W = L, Hq, D, W
     a.q_dtype = _dtype(q_turn)
-    a.q_turn, a.M, a.decay = _ptr(q_turn), _ptr(m), decay
+    a.q_turn, a.M, a.decay = _ptr(q_turn), _wptr(m, "m", torch.float32, (L, Hq, D)), decay
     lib = _abi.load()
     _check(lib.kvsel_memory_update(ctypes.byref(a), _stream(stream)))
 
@@ -273,7 +310,8 @@ def build_index(raw_k, mu, *, bt, D, src_rows, NB=None, b_begin=0, b_count=None,
     a = _abi.IndexArgs()
     a.struct_size = ctypes.sizeof(_abi.IndexArgs)
     a.U, a.D, a.dtype, a.bt = U, D, _dtype(raw_k), bt
-    a.src_k, a.src_offsets, a.src_unit_stride, a.src_rows = _ptr(raw_k), _ptr(src_offsets), src_unit_stride, src_rows
+    a.src_k, a.src_unit_stride, a.src_rows = _ptr(raw_k), src_unit_stride, src_rows
+    a.src_offsets = _wptr(src_offsets, "src_offsets", torch.int64, numel=U)
     a.NB, a.b_begin, a.b_count, a.mu = NB, b_begin, b_count, _ptr(mu)
     lib = _abi.load()
     _check(lib.kvsel_build_index(ctypes.byref(a), _stream(stream)))
@@ -287,6 +325,9 @@ def free_list(slot_map, keep_mask, dead_slot, free_slots, n_free, *, n_slots, pr
     N = slot_map.shape[0]
     a = _abi.FreeListArgs()
     a.struct_size = ctypes.sizeof(_abi.FreeListArgs)
+    for t, name, dt, numel in ((slot_map, "slot_map", torch.int32, None), (keep_mask, "keep_mask", torch.uint8, N),
+                               (free_slots, "free_slots", torch.int32, N), (n_free, "n_free", torch.int32, 1)):
+        _want(t, name, dt, numel=numel)
     a.N, a.slot_map, a.keep_mask, a.dead_slot = N, _ptr(slot_map), _ptr(keep_mask), dead_slot
     a.protected_len, a.n_slots, a.free_slots, a.n_free = protected_len, n_slots, _ptr(free_slots), _ptr(n_free)
     lib = _abi.load()
@@ -312,6 +353,13 @@ def compact(keep_mask, block_table, k_pool, v_pool, slot_pos, freed_blocks, n_fr
     a.struct_size = ctypes.sizeof(_abi.CompactArgs)
     a.R, a.L, a.Hkv, a.D, a.dtype, a.block_size, a.Y = R, L, Hkv, D, _dtype(k_pool), block_size, Y
     a.N, a.pool_blocks = N, P
+    for t, name, dt, shape, numel in ((keep_mask, "keep_mask", torch.uint8, None, None),
+                                      (block_table, "block_table", torch.int32, (R, Y), None),
+                                      (v_pool, "v_pool", k_pool.dtype, tuple(k_pool.shape), None),
+                                      (slot_pos, "slot_pos", torch.int32, (R, Y * block_size), None),
+                                      (freed_blocks, "freed_blocks", torch.int32, (R, Y), None),
+                                      (n_freed, "n_freed", torch.int32, None, R)):
+        _want(t, name, dt, shape, numel)
     a.keep_mask, a.block_table, a.k_pool, a.v_pool = _ptr(keep_mask), _ptr(block_table), _ptr(k_pool), _ptr(v_pool)
     a.slot_pos, a.freed_blocks, a.n_freed = _ptr(slot_pos), _ptr(freed_blocks), _ptr(n_freed)
     lib = _abi.load()
@@ -339,6 +387,12 @@ def decode_score(q, lse, k_pool, block_table, n_ctx, n_seen, state, *, req=None,
     a.Ra, a.R, a.L, a.Hq, a.Hkv, a.D = Ra, R, L, Hq, Hkv, D
     a.dtype, a.block_size, a.Y, a.scale = _dtype(k_pool), bs, Y, scale
     a.n_cap, a.pool_blocks = state.shape[3], P
+    for t, name, dt, shape, numel in ((req, "req", torch.int32, (Ra,), None),
+                                      (lse, "lse", torch.float32, (L, Ra, Hq), None),
+                                      (block_table, "block_table", torch.int32, None, None),
+                                      (n_ctx, "n_ctx", torch.int32, None, R), (n_seen, "n_seen", torch.int32, None, R),
+                                      (state, "state", torch.float32, None, None)):
+        _want(t, name, dt, shape, numel)
     a.req, a.q, a.lse, a.k_pool = _ptr(req), _ptr(q), _ptr(lse), _ptr(k_pool)
     a.block_table, a.n_ctx, a.n_seen, a.state = _ptr(block_table), _ptr(n_ctx), _ptr(n_seen), _ptr(state)
     _check(_abi.load().kvsel_decode_score(ctypes.byref(a), _stream(stream)))
@@ -356,6 +410,12 @@ def keep_score(state, keep, n_len, *, lam, top_p=0.9, req=None, attn_score=None,
     a.struct_size = ctypes.sizeof(_abi.KeepScoreArgs)
     a.Rc, a.R, a.L, a.Hkv, a.reserved, a.n_cap = Rc, R, L, Hkv, 0, n_cap
     a.lam, a.top_p = lam, top_p
+    for t, name, dt, shape, numel in ((req, "req", torch.int32, (Rc,), None), (n_len, "n_len", torch.int32, None, R),
+                                      (state, "state", torch.float32, None, None),
+                                      (keep, "keep", torch.float32, (R, n_cap), None),
+                                      (attn_score, "attn_score", torch.float32, (R, n_cap), None),
+                                      (hit, "hit", torch.uint8, (R, n_cap), None)):
+        _want(t, name, dt, shape, numel)
     a.req, a.n_len, a.state, a.keep_score = _ptr(req), _ptr(n_len), _ptr(state), _ptr(keep)
     a.attn_score, a.hit = _ptr(attn_score), _ptr(hit)
     lib = _abi.load()
