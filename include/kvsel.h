@@ -113,6 +113,7 @@ const char* kvsel_last_error(void);
  *   `qbar_valid` = 1 the call reads `qbar` instead and `q` may be NULL.
  *   Output `scores`: [S][L*Hkv][n_count] F32.
  *
+ * Limits: L * Hkv <= 65535 (E_UNSUPPORTED beyond).
  * scale = 0 means 1/sqrt(D).  Pooling (window/memory-per-unit): centred,
  * odd `pool_k`, stride 1; AVG divides by pool_k counting out-of-range terms
  * as zero, MAX takes the in-range maximum.
@@ -189,7 +190,8 @@ kvsel_status kvsel_score(const kvsel_score_args* args, void* workspace,
  * key of every position of the call and small per-slice histograms, about
  * 4 bytes per position); 0 only when U or n is 0.
  * Errors: KVSEL_E_BUDGET if n_sink + n_recent > k_total and k_total < n_total;
- * KVSEL_E_WORKSPACE if the workspace is missing or too small.
+ * KVSEL_E_WORKSPACE if the workspace is missing or too small; KVSEL_E_UNSUPPORTED
+ * for U > 65535.
  */
 typedef struct kvsel_select_args {
   uint32_t struct_size;
@@ -370,7 +372,8 @@ kvsel_status kvsel_free_list(const kvsel_freelist_args* args, void* workspace, s
  *                [0, Y - X) in order, then -1; n_freed out [R] = Y - X
  * Requirements: 0 <= N <= Y * block_size, Hkv * D * element size a multiple
  * of 16 bytes, pools 16-byte aligned.  Workspace: kvsel_compact_workspace.
- * Errors: E_ARG, E_WORKSPACE, E_DEVICE.  R = 0 or Y = 0 is a no-op.
+ * Errors: E_ARG, E_WORKSPACE, E_UNSUPPORTED (R > 65535), E_DEVICE.  R = 0 or Y = 0 is a
+ * no-op.
  */
 typedef struct kvsel_compact_args {
   uint32_t struct_size;

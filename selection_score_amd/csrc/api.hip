@@ -103,6 +103,8 @@ kvsel_status validate_score(const kvsel_score_args* a, ScorePlan* plan) {
   if (a->L <= 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0)
     return fail(KVSEL_E_ARG, "need L, Hq, Hkv > 0 and Hkv dividing Hq");
   if (a->D != 64 && a->D != 128) return fail(KVSEL_E_UNSUPPORTED, "D must be 64 or 128");
+  if (static_cast<int64_t>(a->L) * a->Hkv > 65535)
+    return fail(KVSEL_E_UNSUPPORTED, "L * Hkv must be at most 65535 (one grid row per unit)");
   if (a->N <= 0 || a->N > kMaxN) return fail(KVSEL_E_ARG, "N must be in [1, 2^31)");
   const bool lse_only = a->mode == KVSEL_SCORE_WINDOW && a->scores == nullptr && a->lse_out != nullptr &&
                         a->lse_in == nullptr;
@@ -266,6 +268,7 @@ static kvsel_status validate_select(const kvsel_select_args* a) {
     return fail(KVSEL_E_ARG, "negative size");
   if (a->n_total > kMaxN || a->base + a->n > a->n_total)
     return fail(KVSEL_E_ARG, "need base + n <= n_total < 2^31");
+  if (a->U > 65535) return fail(KVSEL_E_UNSUPPORTED, "U must be at most 65535 (one grid row per unit)");
   if (a->U > 0 && a->n > 0 && (a->scores == nullptr || a->row_stride < a->n))
     return fail(KVSEL_E_ARG, "scores NULL or row_stride < n");
   if (a->k_total < a->n_total && static_cast<int64_t>(a->n_sink) + a->n_recent > a->k_total)
@@ -459,6 +462,7 @@ static kvsel_status check_compact(const kvsel_compact_args* a, CompactParams* p)
   if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
   if (a->struct_size < sizeof(kvsel_compact_args)) return fail(KVSEL_E_ARG, "struct_size too small");
   if (a->R < 0 || a->Y < 0) return fail(KVSEL_E_ARG, "R and Y must be >= 0");
+  if (a->R > 65535) return fail(KVSEL_E_UNSUPPORTED, "R must be at most 65535 (one grid row per request)");
   if (a->L < 1 || a->Hkv < 1 || a->D < 1 || a->block_size < 1 || a->pool_blocks < 1)
     return fail(KVSEL_E_ARG, "L, Hkv, D, block_size and pool_blocks must be >= 1");
   if (!valid_dtype(a->dtype)) return fail(KVSEL_E_ARG, "bad dtype");

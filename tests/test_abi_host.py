@@ -283,3 +283,15 @@ def test_keep_score_validation_and_workspace_without_device():
     a = _keep_args()
     a.Rc = 0
     assert lib.kvsel_keep_score(ctypes.byref(a), None, 0, None) == _abi.KVSEL_OK
+
+
+def test_grid_row_limits_are_reported_without_device():
+    lib = _abi.load()
+    a = _select_args(U=65536)
+    nb = ctypes.c_size_t(0)
+    assert lib.kvsel_select_workspace(ctypes.byref(a), ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
+    c = _abi.CompactArgs()
+    c.struct_size = ctypes.sizeof(c)
+    c.R, c.L, c.Hkv, c.D, c.dtype, c.block_size, c.Y = 65536, 1, 8, 128, _abi.BF16, 16, 1
+    c.N, c.pool_blocks = 16, 4
+    assert lib.kvsel_compact_workspace(ctypes.byref(c), ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
