@@ -295,3 +295,27 @@ def test_grid_row_limits_are_reported_without_device():
     c.R, c.L, c.Hkv, c.D, c.dtype, c.block_size, c.Y = 65536, 1, 8, 128, _abi.BF16, 16, 1
     c.N, c.pool_blocks = 16, 4
     assert lib.kvsel_compact_workspace(ctypes.byref(c), ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
+
+
+def test_error_messages_are_per_thread():
+    import threading
+    lib = _abi.load()
+    msgs = {}
+
+    def worker(name, budget):
+        a = _select_args()
+        if budget:
+            a.n_sink, a.n_recent = 8, 8                 # 16 forced > k_total 10
+        else:
+            a.pool, a.pool_k = 1, 4                     # even window
+        for _ in range(200):
+            lib.kvsel_select(ctypes.byref(a), None, 0, None)
+            msgs.setdefault(name, set()).add(lib.kvsel_last_error().decode())
+
+    threads = [threading.Thread(target=worker, args=("b", True)), threading.Thread(target=worker, args=("p", False))]
+    for t in threads:
+        t.start()
+    for t in threads:
+        t.join()
+    assert len(msgs["b"]) == 1 and "k_total" in next(iter(msgs["b"]))
+    assert len(msgs["p"]) == 1 and "pool_k" in next(iter(msgs["p"]))
