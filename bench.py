@@ -42,6 +42,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_BF16_PEAK_TFLOPS = 2500.0
 METRIC = "scored KV tokens/s & HBM GB/s vs peak; per-step select+gather latency"
 COPY_BYTES = 1 << 30
 
@@ -300,6 +301,11 @@ class SnapKV:
         kept_b = cfg.U * cfg.k * 4
         gb = 2 * 2 * cfg.U * cfg.k * cfg.D * 2
         return {"lse": kb + qb + lb, "score": kb + qb + lb + sb, "select": sb + kept_b, "gather": kept_b + gb}
+
+    def mfma_flops(self):
+        cfg = self.cfg
+        f = 2 * cfg.G * cfg.W * cfg.N * cfg.D * cfg.U      # q . k for every (row, key) of every unit
+        return {"lse": f, "score": f}
 
     def config(self):
         cfg = self.cfg
@@ -827,6 +833,13 @@ def main():
                      "launch_ms": stage[dom]},
         "cpu_baseline": None,
     }
+    flops = getattr(wk, "mfma_flops", lambda: {})()
+    if flops:
+        # the matrix-core side of the co-bound window passes: dense bf16 MFMA
+        # work per launch over the stage time, against the dense bf16 peak
+        out["mfma"] = {n: {"achieved": f / (stage[n] * 1e-3) / 1e12, "peak": MFMA_BF16_PEAK_TFLOPS,
+                           "unit": "TFLOP/s", "frac": f / (stage[n] * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS,
+                           "flops": f} for n, f in flops.items()}
     out.update(wk.extra())
     if not args.no_cpu_baseline and args.workload == "snapkv":
         out["cpu_baseline"] = cpu_baseline(wk.inp, wk.cfg, args.cpu_seconds)
