@@ -254,8 +254,9 @@ hipError_t launch_gather_fresh(const GatherParams& p, const RopeTable& rt, const
   } else {
     const int64_t rows = static_cast<int64_t>(p.U) * p.k * p.bt;
     const int rows_per_wave = 64 / lpr;
-    // a few rows per wave in flight; grid capped, kernel strides
-    const int grid = grid_for(ceil_div(rows, static_cast<int64_t>(rows_per_wave) * 4));
+    // one pass of rows per wavefront where the grid cap allows (more
+    // wavefronts in flight measured faster than longer strides per wavefront)
+    const int grid = grid_for(ceil_div(rows, static_cast<int64_t>(rows_per_wave)));
 #define KVSEL_GR(DTV)                                                                         \
   gather_rows_kernel<DTV><<<grid, 256, 0, st>>>(p, rt, src_k, src_v, idx, n_idx, dst_k, dst_v)
     if (p.dtype == KVSEL_BF16) KVSEL_GR(KVSEL_BF16);
