@@ -28,7 +28,9 @@
  *   kernels on `stream` (a hipStream_t; NULL = the default stream) and
  *   returns without synchronising.  Results are valid once the stream
  *   reaches that point.  With the environment variable KVSEL_DEBUG=1 each
- *   call synchronises its stream and reports kernel errors.
+ *   call synchronises its stream and reports kernel errors, and NaN or Inf
+ *   in the scores kvsel_select reads or kvsel_score writes is reported as
+ *   E_ARG (for kvsel_score the outputs have then been written).
  * - Errors: on any status other than KVSEL_OK nothing was enqueued and
  *   kvsel_last_error() describes why.  No C++ exception crosses the ABI.
  * - Device pointers must be 16-byte aligned; sizes are element counts.
@@ -468,8 +470,10 @@ kvsel_status kvsel_build_index(const kvsel_index_args* args, void* stream);
  * region start leaves them (n_ctx does not decrease within a region), and
  * the state equals the plain mean over the region's tokens.
  * Requirements: D 64 or 128; G = Hq / Hkv integral and <= 16; block_size a
- * multiple of 16; q, k_pool 16-byte aligned.  scale = 0 means 1/sqrt(D).
- * Errors: E_ARG, E_UNSUPPORTED (D, dtype, G), E_DEVICE.  Ra = 0 is a no-op.
+ * multiple of 16; Hkv <= 4096; Ra and L <= 65535; n_cap <= 2^30; q, k_pool
+ * 16-byte aligned.  scale = 0 means 1/sqrt(D).
+ * Errors: E_ARG (sizes, pointers, alignment), E_UNSUPPORTED (D, dtype,
+ * G > 16, block_size, Hkv > 4096), E_DEVICE.  Ra = 0 is a no-op.
  */
 typedef struct kvsel_decode_args {
   uint32_t struct_size;
@@ -520,8 +524,9 @@ kvsel_status kvsel_decode_score(const kvsel_decode_args* args, void* stream);
  *   hit         [R][n_cap] u8 out or NULL: 1 = hit (the entry's bit of the
  *               action access vector of ActKV §5.1 for this region), 0 for
  *               j >= n_len
- * lambda in [0, 1], top_p in (0, 1].  Workspace: kvsel_keep_score_workspace
- * (Rc * n_cap floats when attn_score is NULL, else 0).
+ * lambda in [0, 1], top_p in (0, 1], Rc <= 65535, n_cap < 2^31.
+ * Workspace: kvsel_keep_score_workspace (Rc * n_cap floats when attn_score
+ * is NULL, else 0).
  * Errors: E_ARG, E_WORKSPACE, E_DEVICE.  Rc = 0 is a no-op.
  */
 typedef struct kvsel_keep_score_args {

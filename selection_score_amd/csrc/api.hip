@@ -44,6 +44,19 @@ bool debug_mode() {
   return on;
 }
 
+// KVSEL_DEBUG=1: NaN or Inf in a score array is reported as E_ARG.
+kvsel_status debug_scores(const float* x, int64_t rows, int64_t cols, int64_t stride, hipStream_t st,
+                          const char* what) {
+  if (!debug_mode()) return KVSEL_OK;
+  uint64_t bad = 0;
+  const hipError_t e = debug_count_nonfinite(x, rows, cols, stride, st, &bad);
+  if (e != hipSuccess) return hip_fail(e, "debug check");
+  if (bad != 0)
+    return fail(KVSEL_E_ARG, "%s hold %llu NaN or Inf values (inputs must be finite)", what,
+                static_cast<unsigned long long>(bad));
+  return KVSEL_OK;
+}
+
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 bool valid_dtype(int dt) { return dt == KVSEL_F32 || dt == KVSEL_BF16 || dt == KVSEL_F16; }
@@ -250,10 +263,13 @@ kvsel_status kvsel_score(const kvsel_score_args* a, void* ws, size_t ws_bytes, v
         if (e != hipSuccess) return hip_fail(e, "query reduce");
       }
       e = launch_block_scores(p, qbar, a->k, a->scores, st);
-      return finish(e, st, "block scores");
+      if ((s = finish(e, st, "block scores")) != KVSEL_OK) return s;
+      return debug_scores(a->scores, static_cast<int64_t>(a->S) * U, a->n_count, a->n_count, st,
+                          "block scores (q or the index not finite?)");
     }
     if (plan.pooled) e = launch_pool1d(dst, a->scores, pool_rows, a->N, a->pool, a->pool_k, st);
-    return finish(e, st, "score pooling");
+    if ((s = finish(e, st, "score pooling")) != KVSEL_OK) return s;
+    return debug_scores(a->scores, pool_rows, a->N, a->N, st, "scores (q, k or lse_in not finite?)");
   } catch (...) {
     return fail(KVSEL_E_ARG, "internal error");
   }
@@ -330,6 +346,8 @@ kvsel_status kvsel_select(const kvsel_select_args* a, void* ws, size_t ws_bytes,
     if (need > 0 && !aligned16(ws)) return fail(KVSEL_E_ARG, "workspace must be 16-byte aligned");
     if ((s = check_device()) != KVSEL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.U > 0 && p.n > 0 && (s = debug_scores(a->scores, p.U, p.n, p.row_stride, st, "scores")) != KVSEL_OK)
+      return s;
     return finish(launch_select(p, a->scores, ws, st), st, "select");
   } catch (...) {
     return fail(KVSEL_E_ARG, "internal error");

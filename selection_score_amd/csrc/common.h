@@ -175,6 +175,10 @@ struct IndexParams {
 };
 hipError_t launch_build_index(const IndexParams& p, const void* src_k, uint16_t* mu, hipStream_t st);
 
+// KVSEL_DEBUG=1 only: the number of NaN/Inf floats of x[rows][cols] (row
+// stride `stride`); synchronises `st`.
+hipError_t debug_count_nonfinite(const float* x, int64_t rows, int64_t cols, int64_t stride, hipStream_t st,
+                                 uint64_t* count);
 size_t free_list_workspace_bytes(int64_t n_slots);
 hipError_t launch_free_list(int64_t N, const int32_t* slot_map, const uint8_t* keep, int64_t dead,
                             int64_t protected_len, int64_t n_slots, int32_t* free_slots, int32_t* n_free,

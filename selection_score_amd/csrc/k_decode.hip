@@ -63,7 +63,7 @@ __global__ __launch_bounds__(512) void decode_score_kernel(DecodeParams p, const
   const int64_t n_lim = min(p.n_cap, static_cast<int64_t>(p.Y) * p.block_size);
   const int64_t n = min(max(static_cast<int64_t>(p.n_ctx[r]), static_cast<int64_t>(0)), n_lim);
   const int t = max(p.n_seen[r], 0);
-  const float inv = 1.0f / static_cast<float>(t + 1);
+  const float inv = 1.0f / (static_cast<float>(t) + 1.0f);   // no int overflow at n_seen = INT_MAX
   const int64_t j = j0 + lane;
   const int64_t jc = min(j, p.n_cap - 1);
   const int64_t row_elems = static_cast<int64_t>(p.Hkv) * D;
