@@ -30,7 +30,11 @@
  *   reaches that point.  With the environment variable KVSEL_DEBUG=1 each
  *   call synchronises its stream and reports kernel errors, and NaN or Inf
  *   in the scores kvsel_select reads or kvsel_score writes is reported as
- *   E_ARG (for kvsel_score the outputs have then been written).
+ *   E_ARG (for kvsel_score the outputs have then been written).  Debug mode
+ *   also checks on the host the index lists in-place calls rely on
+ *   (ascending block lists and distinct pages of an incremental view,
+ *   blocks not shared between requests in a compaction, requests listed
+ *   once for the ActKV calls) and reports violations as E_ARG.
  * - Errors: on any status other than KVSEL_OK nothing was enqueued and
  *   kvsel_last_error() describes why.  No C++ exception crosses the ABI.
  * - Device pointers must be 16-byte aligned; sizes are element counts.

@@ -10,6 +10,7 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <algorithm>
 #include <mutex>
 #include <string>
 #include <vector>
@@ -54,6 +55,26 @@ kvsel_status debug_scores(const float* x, int64_t rows, int64_t cols, int64_t st
   if (bad != 0)
     return fail(KVSEL_E_ARG, "%s hold %llu NaN or Inf values (inputs must be finite)", what,
                 static_cast<unsigned long long>(bad));
+  return KVSEL_OK;
+}
+
+// KVSEL_DEBUG=1: copies a small device index array to the host.
+kvsel_status debug_fetch(const int32_t* d, size_t n, std::vector<int32_t>* h, hipStream_t st) {
+  h->assign(n, 0);
+  if (n == 0) return KVSEL_OK;
+  hipError_t e = hipMemcpyAsync(h->data(), d, n * sizeof(int32_t), hipMemcpyDeviceToHost, st);
+  if (e == hipSuccess) e = hipStreamSynchronize(st);
+  return (e == hipSuccess) ? KVSEL_OK : hip_fail(e, "debug check");
+}
+
+// KVSEL_DEBUG=1: the entries of v inside [0, limit) are pairwise distinct.
+kvsel_status debug_distinct(const std::vector<int32_t>& v, int64_t limit, const char* what) {
+  std::vector<int32_t> in;
+  for (const int32_t x : v)
+    if (x >= 0 && x < limit) in.push_back(x);
+  std::sort(in.begin(), in.end());
+  for (size_t i = 1; i < in.size(); ++i)
+    if (in[i] == in[i - 1]) return fail(KVSEL_E_ARG, "%s: %d appears more than once", what, in[i]);
   return KVSEL_OK;
 }
 
@@ -418,6 +439,34 @@ kvsel_status kvsel_gather_workspace(const kvsel_gather_args* a, size_t* bytes) {
   }
 }
 
+// KVSEL_DEBUG=1: the in-place view update relies on ascending, valid block
+// lists and on distinct pages per unit; a violation would race silently.
+static kvsel_status debug_incremental(const kvsel_gather_args* a, hipStream_t st) {
+  const size_t n = static_cast<size_t>(a->U) * a->k;
+  std::vector<int32_t> idx, prev, page;
+  kvsel_status s;
+  if ((s = debug_fetch(a->idx, n, &idx, st)) != KVSEL_OK || (s = debug_fetch(a->prev_idx, n, &prev, st)) != KVSEL_OK ||
+      (s = debug_fetch(a->prev_page, n, &page, st)) != KVSEL_OK)
+    return s;
+  const int64_t blocks = a->src_rows / a->bt;
+  for (int u = 0; u < a->U; ++u) {
+    for (int i = 0; i < a->k; ++i) {
+      const size_t o = static_cast<size_t>(u) * a->k + i;
+      if (idx[o] < 0 || idx[o] >= blocks || (i > 0 && idx[o] <= idx[o - 1]))
+        return fail(KVSEL_E_ARG, "idx of unit %d is not ascending within [0, %lld) at %d", u,
+                    static_cast<long long>(blocks), i);
+      if (prev[o] < 0 || (i > 0 && prev[o] <= prev[o - 1]))
+        return fail(KVSEL_E_ARG, "prev_idx of unit %d is not ascending and valid at %d", u, i);
+      if (page[o] < 0 || page[o] >= a->pool_pages)
+        return fail(KVSEL_E_ARG, "prev_page of unit %d is outside [0, pool_pages) at %d", u, i);
+    }
+    const std::vector<int32_t> row(page.begin() + static_cast<size_t>(u) * a->k,
+                                   page.begin() + static_cast<size_t>(u + 1) * a->k);
+    if ((s = debug_distinct(row, a->pool_pages, "prev_page")) != KVSEL_OK) return s;
+  }
+  return KVSEL_OK;
+}
+
 kvsel_status kvsel_gather_rerope(const kvsel_gather_args* a, void* ws, size_t ws_bytes, void* stream) {
   try {
     GatherParams gp{};
@@ -429,6 +478,7 @@ kvsel_status kvsel_gather_rerope(const kvsel_gather_args* a, void* ws, size_t ws
       return fail(KVSEL_E_WORKSPACE, "workspace needs %zu bytes, got %zu", need, ws_bytes);
     if ((s = check_device()) != KVSEL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_mode() && a->mode == KVSEL_GATHER_INCREMENTAL && (s = debug_incremental(a, st)) != KVSEL_OK) return s;
     hipError_t e;
     if (a->mode == KVSEL_GATHER_FRESH)
       e = launch_gather_fresh(gp, rt, a->src_k, a->src_v, a->idx, a->n_idx, a->dst_k, a->dst_v, st);
@@ -528,6 +578,12 @@ kvsel_status kvsel_compact(const kvsel_compact_args* a, void* ws, size_t ws_byte
     if (!aligned16(ws)) return fail(KVSEL_E_ARG, "workspace must be 16-byte aligned");
     if ((s = check_device()) != KVSEL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_mode()) {
+      std::vector<int32_t> bt;
+      if ((s = debug_fetch(a->block_table, static_cast<size_t>(a->R) * a->Y, &bt, st)) != KVSEL_OK ||
+          (s = debug_distinct(bt, a->pool_blocks, "block_table")) != KVSEL_OK)
+        return s;
+    }
     return finish(launch_compact(p, a->keep_mask, a->block_table, a->k_pool, a->v_pool, a->slot_pos,
                                  a->freed_blocks, a->n_freed, ws, st),
                   st, "compaction");
@@ -677,6 +733,12 @@ kvsel_status kvsel_decode_score(const kvsel_decode_args* a, void* stream) {
     if (p.Ra == 0 || p.n_cap == 0) return KVSEL_OK;
     if ((s = check_device()) != KVSEL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_mode() && a->req != nullptr) {
+      std::vector<int32_t> req;
+      if ((s = debug_fetch(a->req, static_cast<size_t>(a->Ra), &req, st)) != KVSEL_OK ||
+          (s = debug_distinct(req, a->R, "req")) != KVSEL_OK)
+        return s;
+    }
     return finish(launch_decode_score(p, a->dtype, a->q, a->lse, a->k_pool, a->state, st), st, "decode score");
   } catch (...) {
     return fail(KVSEL_E_ARG, "internal error");
@@ -733,6 +795,12 @@ kvsel_status kvsel_keep_score(const kvsel_keep_score_args* a, void* ws, size_t w
     if (need > 0 && !aligned16(ws)) return fail(KVSEL_E_ARG, "workspace must be 16-byte aligned");
     if ((s = check_device()) != KVSEL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_mode() && a->req != nullptr) {
+      std::vector<int32_t> req;
+      if ((s = debug_fetch(a->req, static_cast<size_t>(a->Rc), &req, st)) != KVSEL_OK ||
+          (s = debug_distinct(req, a->R, "req")) != KVSEL_OK)
+        return s;
+    }
     return finish(launch_keep_score(p, a->state, a->keep_score, a->attn_score, a->hit, ws, st), st, "keep score");
   } catch (...) {
     return fail(KVSEL_E_ARG, "internal error");
