@@ -54,7 +54,9 @@ PIN_STATUS = {
                                          "cardinality by brute force over all subsets; exact unit sum)",
     "select.lrfu_keep_score": "partly unpinned: the page's update equation is lost; the reading "
                               "lam*KS + hit*score is pinned to the page's lambda = 0 (recency) and "
-                              "lambda = 1 (frequency) limits only",
+                              "lambda = 1 (frequency) limits, and for 0 < lambda < 1 only to the "
+                              "behaviour the page describes (quiet intermittent entries survive, "
+                              "stale continuous ones are overtaken), not to a formula",
     "score.residual_score": "pinned (zero-initialised fc2 gives the rule score exactly)",
     "select.select_topk": "pinned (exhaustive max-sum brute force on tiny inputs; invariants)",
     "select.select_topk_tiled": "pinned (equal to select_topk for every tile size)",

@@ -131,8 +131,9 @@ def lrfu_keep_score(ks, scores, hits, lam):
         KS_t(i) = lam * KS_{t-1}(i) + hit_t(i) * AttnScore_t(i),
     which has the two limits the page describes: lam = 0 keeps only the
     latest step (recency), lam = 1 accumulates every hit without decay
-    (frequency).  Parity unpinned for 0 < lam < 1: only those two limits
-    are fixed by the page.
+    (frequency).  Parity unpinned for 0 < lam < 1: the page fixes those two
+    limits and, in between, only the behaviour (a quiet intermittent entry
+    with high attention survives, a stale continuous entry is overtaken).
     """
     ks = np.asarray(ks, dtype=np.float64)
     return lam * ks + np.where(hits, np.asarray(scores, dtype=np.float64), 0.0)

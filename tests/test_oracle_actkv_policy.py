@@ -204,6 +204,45 @@ def test_lambda_limits():
     assert k.tolist() == [0.25]
 
 
+def test_intermediate_lambda_behaviour_the_page_describes():
+    """ActKV §5.2 describes what each regime does to two kinds of entries: an
+    intermittent entry with high attention that goes quiet for a while, and a
+    continuous entry that stops being attended (stale).  At lambda = 0 the
+    quiet intermittent entry falls to the bottom; at lambda = 1 the stale
+    continuous entry keeps outranking a newly important one; with 0 < lambda
+    < 1 the intermittent entry survives its quiet steps and the stale entry
+    is overtaken.  The update equation itself is lost from the page, so this
+    pins the behaviour, not the formula."""
+    # entries: I (intermittent), O (continuous, stale from step 4), N (new,
+    # attended from step 4), Z (never attended); scores and hits per step
+    steps = [
+        ([1.0, 0.4, 0.0, 0.0], [True, True, False, False]),
+        ([0.01, 0.4, 0.0, 0.0], [False, True, False, False]),
+        ([0.01, 0.4, 0.0, 0.0], [False, True, False, False]),
+        ([0.01, 0.0, 0.5, 0.0], [False, False, True, False]),
+        ([0.01, 0.0, 0.5, 0.0], [False, False, True, False]),
+    ]
+    I, O, N, Z = range(4)
+
+    def run(lam, upto):
+        k = np.zeros(4)
+        for a, h in steps[:upto]:
+            k = select.lrfu_keep_score(k, np.array(a), np.array(h), lam)
+        return k
+
+    # after its two quiet steps, the intermittent entry
+    assert run(0.0, 3)[I] == run(0.0, 3)[Z] == 0.0          # lambda = 0: no better than never attended
+    for lam in (0.3, 0.5, 0.7):
+        k = run(lam, 3)
+        assert k[I] > k[Z] and k[I] > 0.0                    # 0 < lambda < 1: it survives
+    # after the new entry's two steps, the stale continuous entry
+    k = run(1.0, 5)
+    assert k[O] > k[N]                                       # lambda = 1: the stale entry is retained
+    for lam in (0.3, 0.5, 0.7):
+        k = run(lam, 5)
+        assert k[N] > k[O]                                   # 0 < lambda < 1: it decays below the new one
+
+
 def test_keep_score_step_per_request():
     rng = _rng(14)
     L, R, Hkv, n_cap = 2, 3, 2, 10

@@ -93,6 +93,9 @@ CASES = [
     ("select", "lrfu_keep_score", "return lam * ks +", "return (1.0 - lam) * ks +", [T_act.test_lambda_limits]),
     ("select", "lrfu_keep_score", "np.where(hits, np.asarray(scores, dtype=np.float64), 0.0)",
      "np.asarray(scores, dtype=np.float64)", [T_act.test_lambda_limits]),
+    # the decay dropped: hits accumulate at every lambda
+    ("select", "lrfu_keep_score", "return lam * ks +", "return ks +",
+     [T_act.test_intermediate_lambda_behaviour_the_page_describes]),
     ("select", "action_scores", "math.fsum(st[:, :, j].reshape(L * Hkv).tolist())", "float(np.max(st[:, :, j]))",
      [T_act.test_action_scores_sum_units_exactly_then_round_to_f32]),
     # RoPE
