@@ -91,3 +91,58 @@ def test_compact_partial_last_block_and_no_ops():
                torch.zeros((0, 32), dtype=torch.int32, device=dev), torch.zeros((0, 2), dtype=torch.int32, device=dev),
                torch.zeros(0, dtype=torch.int32, device=dev), block_size=16)
     torch.cuda.synchronize()
+
+
+def test_compact_actkv_workload_full_size_sampled():
+    """The benchmarked shape: 64 requests of 6144 positions in 16-slot blocks,
+    36 layers of 8 KV heads x 128 bf16, 4096 kept per request, one launch over
+    all of it.  Slot positions and freed blocks are checked for every
+    request; the pools bit for bit for sampled (request, layer) pairs, each
+    through the oracle on that request's own blocks (a request's blocks are
+    disjoint from every other's, so its compaction is local to them); blocks
+    of no request must be untouched."""
+    from selection_score_amd import workloads as wl
+    dev = require_gpu()
+    cfg = wl.CONFIGS["actkv"]
+    print("compact full size: inputs", flush=True)
+    inp = wl.actkv_inputs(cfg, dev)
+    R, N, bs, L = cfg.S, cfg.N, cfg.page_size, cfg.L
+    keep = inp["keep"].cpu().numpy().astype(bool)
+    bt = inp["block_table"].cpu().numpy().astype(np.int64)
+    Y = bt.shape[1]
+    P = inp["k_pool"].shape[1]
+    reqs, layers = (0, 29, 63), (0, 17, 35)
+    spare = np.setdiff1d(np.arange(P), bt.reshape(-1))
+    ib = torch.int16
+    before = {}
+    for l in layers:
+        for name in ("k_pool", "v_pool"):
+            pool = inp[name][l].view(ib)
+            before[(name, l, "spare")] = pool[torch.from_numpy(spare).to(dev)].cpu()
+            for r in reqs:
+                before[(name, l, r)] = pool[torch.from_numpy(bt[r]).to(dev)].cpu().numpy()
+    slot_pos = torch.full((R, Y * bs), -7, dtype=torch.int32, device=dev)
+    freed = torch.full((R, Y), -7, dtype=torch.int32, device=dev)
+    nfr = torch.full((R,), -7, dtype=torch.int32, device=dev)
+    print("compact full size: launch", flush=True)
+    kv.compact(inp["keep"], inp["block_table"], inp["k_pool"], inp["v_pool"], slot_pos, freed, nfr, block_size=bs)
+    torch.cuda.synchronize()
+    sp, fr, nf = slot_pos.cpu().numpy(), freed.cpu().numpy(), nfr.cpu().numpy()
+    local = np.arange(Y)
+    dummy = np.zeros((Y, bs, 1), dtype=np.int16)
+    print("compact full size: plans of all requests", flush=True)
+    for r in range(R):
+        _, _, pos, fb = om.tail_compact(keep[r], local, bs, dummy, dummy)
+        np.testing.assert_array_equal(sp[r], pos)
+        assert nf[r] == len(fb)
+        np.testing.assert_array_equal(fr[r, : len(fb)], bt[r][fb])
+        assert np.all(fr[r, len(fb):] == -1)
+    print("compact full size: sampled pools", flush=True)
+    for l in layers:
+        for name in ("k_pool", "v_pool"):
+            pool = inp[name][l].view(ib)
+            assert torch.equal(pool[torch.from_numpy(spare).to(dev)].cpu(), before[(name, l, "spare")])
+            for r in reqs:
+                kp, _, _, _ = om.tail_compact(keep[r], local, bs, before[(name, l, r)], before[(name, l, r)])
+                got = pool[torch.from_numpy(bt[r]).to(dev)].cpu().numpy()
+                np.testing.assert_array_equal(got, kp)
