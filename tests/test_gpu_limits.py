@@ -1,6 +1,6 @@
 """Calls at the largest sizes one launch allows: 65535 selection units, 65535
 window-score units (layers x KV heads), 65535 requests for the ActKV decode
-scorer and the keep score.  Sampled rows are compared with the oracle to the
+scorer, the keep score and the compaction.  Sampled rows are compared with the oracle to the
 usual bar; invariants are checked for every row."""
 import math
 
@@ -106,3 +106,38 @@ def test_decode_and_keep_score_at_the_request_limit():
     S = len(rows)
     _check_keep(st.astype(np.float64)[:, rows], ks0[rows], n_len[rows], list(range(S)), 0.5, 0.9,
                 ks.cpu().numpy()[rows], hit.cpu().numpy()[rows], attn.cpu().numpy()[rows])
+
+
+def test_compact_at_the_request_limit():
+    from oracle import materialise as om
+    dev = require_gpu()
+    rng = np.random.default_rng(35)
+    R, Y, bs, L, Hkv, D = MAX, 2, 16, 2, 1, 64
+    N = Y * bs - 5                                         # a partial last block
+    P = R * Y + 3
+    bt = rng.permutation(P)[: R * Y].reshape(R, Y).astype(np.int32)
+    keep = rng.random((R, N)) < 0.4
+    g = torch.Generator().manual_seed(36)
+    k_pool = torch.randn((L, P, bs, Hkv, D), generator=g).to(torch.bfloat16)
+    v_pool = torch.randn((L, P, bs, Hkv, D), generator=g).to(torch.bfloat16)
+    kd, vd = k_pool.to(dev), v_pool.to(dev)
+    slot_pos = torch.full((R, Y * bs), -7, dtype=torch.int32, device=dev)
+    freed = torch.full((R, Y), -7, dtype=torch.int32, device=dev)
+    nfr = torch.full((R,), -7, dtype=torch.int32, device=dev)
+    print("limits: compact R=%d" % R, flush=True)
+    kv.compact(torch.from_numpy(keep.astype(np.uint8)).to(dev), torch.from_numpy(bt).to(dev), kd, vd, slot_pos,
+               freed, nfr, block_size=bs)
+    torch.cuda.synchronize()
+    X = -(-keep.sum(axis=1) // bs)
+    np.testing.assert_array_equal(nfr.cpu().numpy(), Y - X)
+    sp, fr = slot_pos.cpu().numpy(), freed.cpu().numpy()
+    gk, gv = kd.cpu().view(torch.int16).numpy(), vd.cpu().view(torch.int16).numpy()
+    k0, v0 = k_pool.view(torch.int16).numpy(), v_pool.view(torch.int16).numpy()
+    for r in _sample(rng, R):
+        for l in range(L):
+            kp, vp, pos, fb = om.tail_compact(keep[r], np.arange(Y), bs, k0[l][bt[r]], v0[l][bt[r]])
+            np.testing.assert_array_equal(gk[l][bt[r]], kp)
+            np.testing.assert_array_equal(gv[l][bt[r]], vp)
+        np.testing.assert_array_equal(sp[r], pos)
+        np.testing.assert_array_equal(fr[r, : len(fb)], bt[r][fb])
+        assert np.all(fr[r, len(fb):] == -1)
