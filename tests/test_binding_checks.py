@@ -51,3 +51,15 @@ def test_select_compact_and_free_list_check_outputs():
     with pytest.raises(TypeError, match="keep_mask"):
         kv.free_list(torch.zeros(8, dtype=torch.int32), torch.zeros(8, dtype=torch.bool), 99,
                      torch.zeros(8, dtype=torch.int32), torch.zeros(1, dtype=torch.int32), n_slots=100)
+
+
+def test_missing_library_fails_loudly(monkeypatch, tmp_path):
+    """Without the built library every call raises: there is no fallback."""
+    from selection_score_amd import _abi
+    missing = str(tmp_path / "libkvsel.so")
+    monkeypatch.setattr(_abi, "_lib", None)
+    monkeypatch.setattr(_abi.load, "__defaults__", (missing,))
+    with pytest.raises(RuntimeError, match="not built"):
+        _abi.load()
+    with pytest.raises(RuntimeError, match="not built"):
+        kv.version()
