@@ -107,7 +107,8 @@ const char* kvsel_last_error(void);
  *   q = M: [L][Hq][D] F32.  k = paged pool [L][pool_pages][page_size][Hkv][D]
  *   (BF16/F16), logical page p at physical page page_table[p] (ActKV §2
  *   paging).  Positions outside H score 0.  Output [N] (GLOBAL) or
- *   [L*Hkv][N] (PER_UNIT), F32.
+ *   [L*Hkv][N] (PER_UNIT), F32.  page_size in [1, 64] with
+ *   2 * page_size * Hkv * (2 * D + 16) <= 160 KiB (E_UNSUPPORTED beyond).
  *
  * Block mode -- KVMem (query-conditioned retrieval): per unit u = (l, g),
  *   q-bar[s,u] = sum over the W query tokens and the group's heads of the

@@ -181,6 +181,9 @@ kvsel_status validate_score(const kvsel_score_args* a, ScorePlan* plan) {
     if (256 % a->Hq != 0) return fail(KVSEL_E_UNSUPPORTED, "memory mode needs Hq dividing 256");
     if (a->page_size < 1 || a->page_size > 64 || a->pool_pages < 1)
       return fail(KVSEL_E_ARG, "bad page_size or pool_pages");
+    // the logits kernels stage two pages of every KV head in LDS (160 KiB per workgroup)
+    if (2LL * a->page_size * a->Hkv * (2LL * a->D + 16) > 160 * 1024)
+      return fail(KVSEL_E_UNSUPPORTED, "memory mode needs 2 * page_size * Hkv * (2 * D + 16) <= 160 KiB");
     if (a->n_sink < 0 || a->n_recent < 0) return fail(KVSEL_E_ARG, "negative forced-set size");
     if (a->reduce != KVSEL_REDUCE_GLOBAL && a->reduce != KVSEL_REDUCE_PER_UNIT)
       return fail(KVSEL_E_ARG, "bad reduce");

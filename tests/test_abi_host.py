@@ -131,6 +131,10 @@ def test_score_validation_and_workspace_without_device():
     # max aggregation on a window too large for the VALU path
     assert _status(lib.kvsel_score_workspace, _score_args(head_agg=_abi.AGG["max"], W=128),
                    ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
+    # memory mode: two pages of every KV head must fit the 160 KiB of LDS
+    mem = dict(mode=_abi.SCORE_MEMORY, q_dtype=_abi.F32, page_table=0x4000, pool_pages=5000, page_size=64)
+    assert _status(lib.kvsel_score_workspace, _score_args(Hkv=2, **mem), ctypes.byref(nb)) == _abi.KVSEL_OK
+    assert _status(lib.kvsel_score_workspace, _score_args(**mem), ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
     blk = _score_args(mode=_abi.SCORE_BLOCK, k_dtype=_abi.F16, N=1000, n_begin=900, n_count=200)
     assert _status(lib.kvsel_score_workspace, blk, ctypes.byref(nb)) == _abi.KVSEL_E_ARG
     # a score call with a too-small workspace fails before touching the device

@@ -51,6 +51,8 @@ def test_memory_update_matches_oracle(dtype, W):
     ("per_unit", 16, 1, 128, 16, torch.bfloat16),   # matrix cores, GQA 16
     ("global", 8, 4, 128, 16, torch.bfloat16),      # GQA 2: vector ALUs
     ("global", 8, 2, 64, 8, torch.float16),         # fp16, D 64, 8-token pages: vector ALUs
+    ("per_unit", 8, 2, 128, 64, torch.bfloat16),    # 64-token pages: vector ALUs, 68 KiB of LDS staging
+    ("global", 4, 1, 128, 32, torch.float16),       # 32-token pages, one KV head
 ])
 def test_memory_scores_match_oracle(reduce, Hq, Hkv, D, ps, dtype):
     dev = require_gpu()
