@@ -143,7 +143,8 @@ def keep_score_step(state, ks, n_len, *, lam, top_p=0.9, req=None):
     """One compression step of the ActKV policy for the requests in ``req``.
 
     Per request r: AttnScore = action_scores (entries j < n_len[r]), hits =
-    top_p_hits, KS <- lrfu_keep_score; n_len is taken within [0, n_cap].
+    top_p_hits, KS <- lrfu_keep_score.  A request holds at most n_cap
+    entries, so an n_len of a listed request outside [0, n_cap] is an error.
     Returns (ks [R][n_cap] float64,
     hit [R][n_cap] bool, attn [R][n_cap] float64); entries j >= n_len[r]
     keep their KS and report no hit and score 0; requests not in ``req`` are
@@ -156,7 +157,9 @@ def keep_score_step(state, ks, n_len, *, lam, top_p=0.9, req=None):
     req = np.arange(R) if req is None else np.asarray(req, dtype=np.int64)
     for r in req:
         r = int(r)
-        n = min(max(int(n_len[r]), 0), n_cap)        # a row holds n_cap entries at most
+        n = int(n_len[r])
+        if not 0 <= n <= n_cap:
+            raise ValueError("n_len[%d] = %d lies outside [0, %d]" % (r, n, n_cap))
         a = action_scores(state, r, n)
         h = top_p_hits(a, top_p)
         ks_new[r, :n] = lrfu_keep_score(ks_new[r, :n], a, h, lam)

@@ -145,8 +145,8 @@ struct SelectParams {
   int32_t* n_kept;
   int pool, pool_k;
 };
-// Untiled calls need select_workspace_bytes(p) of workspace (pooled keys and
-// per-slice histograms); tiled calls need none.
+// select_workspace_bytes(p): the keys and per-slice top-byte histograms of
+// the two-launch paths (0 for the single-launch path and empty calls).
 size_t select_workspace_bytes(const SelectParams& p);
 hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, hipStream_t st);
 

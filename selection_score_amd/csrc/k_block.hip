@@ -13,13 +13,16 @@ namespace kvsel {
 
 // q: [S][L][Hq][W][D] -> qbar [S][L][Hkv][D], summed over the group's heads
 // and the W tokens.  One workgroup per (s, l, g); 16-byte loads, per-slot
-// float accumulators, slots reduced in a fixed order.
+// float64 accumulators, slots reduced in a fixed order, one rounding to
+// float32 at the end (the sum of a group's G*W bf16 rows is exact in float64
+// unless their magnitudes span more than about 2^30, so q-bar is then the
+// correctly rounded sum).
 template <int DT>
 __global__ __launch_bounds__(256) void query_reduce_kernel(BlockParams p, const void* __restrict__ q,
                                                            float* __restrict__ qbar) {
   constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
   constexpr int E = 16 / esz;
-  __shared__ float part[256][8];
+  __shared__ double part[256][8];
   const int unit = blockIdx.x;                  // (s, l, g)
   const int g = unit % p.Hkv;
   const int sl = unit / p.Hkv;                  // s * L + l
@@ -31,7 +34,7 @@ __global__ __launch_bounds__(256) void query_reduce_kernel(BlockParams p, const 
   const int64_t rows = static_cast<int64_t>(G) * p.W;
   const uint8_t* base = static_cast<const uint8_t*>(q) +
                         ((static_cast<int64_t>(sl) * p.Hq + static_cast<int64_t>(g) * G) * p.W * p.D) * esz;
-  float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};
   // rows slot, slot + slots, ... in order, kRowBatch loads in flight at a time
   constexpr int kRowBatch = 8;
   for (int64_t r0 = slot; r0 < rows; r0 += static_cast<int64_t>(slots) * kRowBatch) {
@@ -46,12 +49,12 @@ __global__ __launch_bounds__(256) void query_reduce_kernel(BlockParams p, const 
       if (r0 + static_cast<int64_t>(j) * slots >= rows) break;
       const uint32_t w[4] = {vb[j].x, vb[j].y, vb[j].z, vb[j].w};
       if constexpr (DT == KVSEL_F32) {
-        for (int i = 0; i < 4; ++i) acc[i] += __uint_as_float(w[i]);
+        for (int i = 0; i < 4; ++i) acc[i] += static_cast<double>(__uint_as_float(w[i]));
       } else {
         for (int i = 0; i < 4; ++i) {
           const uint16_t lo = static_cast<uint16_t>(w[i] & 0xFFFFu), hi = static_cast<uint16_t>(w[i] >> 16);
-          acc[2 * i] += (DT == KVSEL_BF16) ? bf16_to_f32(lo) : f16_to_f32(lo);
-          acc[2 * i + 1] += (DT == KVSEL_BF16) ? bf16_to_f32(hi) : f16_to_f32(hi);
+          acc[2 * i] += static_cast<double>((DT == KVSEL_BF16) ? bf16_to_f32(lo) : f16_to_f32(lo));
+          acc[2 * i + 1] += static_cast<double>((DT == KVSEL_BF16) ? bf16_to_f32(hi) : f16_to_f32(hi));
         }
       }
     }
@@ -60,9 +63,9 @@ __global__ __launch_bounds__(256) void query_reduce_kernel(BlockParams p, const 
   __syncthreads();
   for (int d = tid; d < p.D; d += 256) {
     const int l2 = d / E, i = d % E;
-    float s = 0.f;
+    double s = 0.0;
     for (int sl2 = 0; sl2 < slots; ++sl2) s += part[sl2 * lpr + l2][i];
-    qbar[static_cast<int64_t>(unit) * p.D + d] = s;
+    qbar[static_cast<int64_t>(unit) * p.D + d] = static_cast<float>(s);
   }
 }
 

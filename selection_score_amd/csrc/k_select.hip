@@ -667,8 +667,19 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
   if (tid == 0 && p.n_kept != nullptr) p.n_kept[u] = static_cast<int32_t>(total);
 }
 
+// Unpooled untiled calls without a slot map, with enough units to fill the
+// device and rows that fit the registers, run select_regs_kernel alone: each
+// unit's workgroup makes its keys from the scores, so no workspace is used.
+// (Pooled rows keep the two launches, whose key kernel spreads the window
+// work over many workgroups.)  An empty row (n = 0, scores possibly NULL)
+// takes the two-launch path, whose per-unit kernel reads no key when n is 0.
+static bool select_single_launch(const SelectParams& p) {
+  return p.cand_count == nullptr && p.n > 0 && p.n <= 32 * kThreads && p.U >= kFusedMinUnits &&
+         (p.pool == KVSEL_POOL_NONE || p.pool_k == 1) && p.slot_map == nullptr;
+}
+
 size_t select_workspace_bytes(const SelectParams& p) {
-  if (p.U == 0 || p.n == 0) return 0;
+  if (p.U == 0 || p.n == 0 || select_single_launch(p)) return 0;
   const int64_t slices = ceil_div(p.n, kPrepKeys);
   const int64_t key_bytes = (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 256;
   return static_cast<size_t>(key_bytes + static_cast<int64_t>(p.U) * slices * 256 * 4);
@@ -681,12 +692,7 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
     uint32_t* keys = static_cast<uint32_t*>(ws);
     const int n_slices = static_cast<int>(ceil_div(p.n, kPrepKeys));
     uint32_t* hist = keys + (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 64;
-    if (p.n <= 32 * kThreads && p.U >= kFusedMinUnits && (p.pool == KVSEL_POOL_NONE || p.pool_k == 1) &&
-        p.slot_map == nullptr) {
-      // enough units to fill the device, no pooling and no dead slots: keys
-      // and all radix passes in the per-unit workgroup (pooled rows keep the
-      // two launches, whose key kernel spreads the window work over many
-      // workgroups)
+    if (select_single_launch(p)) {
       select_regs_kernel<32, true><<<p.U, kThreads, 0, st>>>(p, scores, nullptr, nullptr, 0);
       return hipGetLastError();
     }

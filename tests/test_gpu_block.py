@@ -11,7 +11,8 @@ from oracle import numerics
 from oracle import score as osc
 from oracle import select as osel
 from oracle.rope import rope_rotate
-from parity import assert_rope_close, assert_scores_close, check_selection, f64, require_gpu
+from parity import (assert_rope_close, assert_scores_close, block_score_tolerance, check_selection, f64,
+                    qbar_error_bound, require_gpu)
 
 import selection_score_amd as kv
 from selection_score_amd import workloads as wl
@@ -37,26 +38,33 @@ def test_block_scores_match_oracle(S, W, NB, n_begin, n_count, D):
     kv.score_block(q, mu, out, n_kv_heads=Hkv, n_begin=n_begin, n_count=n_count, qbar=qbar)
     torch.cuda.synchronize()
     qb = osc.query_reduce(f64(q), Hkv)
-    np.testing.assert_allclose(f64(qbar), qb, rtol=1e-5, atol=1e-4)
-    want = osc.block_scores(qb, f64(mu))[..., n_begin:n_begin + n_count].reshape(S, L * Hkv, n_count)
-    mag = osc.block_scores(np.abs(qb), np.abs(f64(mu)))[..., n_begin:n_begin + n_count]
-    assert_scores_close(f64(out).reshape(-1, n_count), want.reshape(-1, n_count), mag=mag)
+    qerr = qbar_error_bound(np.abs(qb), osc.query_reduce(np.abs(f64(q)), Hkv), (Hq // Hkv) * W)
+    assert np.all(np.abs(f64(qbar) - qb) <= qerr)
+    full = osc.block_scores(qb, f64(mu))
+    tol = block_score_tolerance(full, np.abs(qb), f64(mu), 1 / np.sqrt(D), qerr)
+    want = full[..., n_begin:n_begin + n_count]
+    assert_scores_close(f64(out).reshape(-1, n_count), want.reshape(-1, n_count),
+                        extra_tol=tol[..., n_begin:n_begin + n_count])
     # a second tile from the cached q-bar
     out2 = torch.empty((S, L * Hkv, 50), dtype=torch.float32, device=dev)
     kv.score_block(None, mu, out2, n_kv_heads=Hkv, n_begin=NB - 50, n_count=50, qbar=qbar, qbar_valid=True)
     torch.cuda.synchronize()
-    want2 = osc.block_scores(qb, f64(mu))[..., NB - 50:].reshape(S * L * Hkv, 50)
-    mag2 = osc.block_scores(np.abs(qb), np.abs(f64(mu)))[..., NB - 50:]
-    assert_scores_close(f64(out2).reshape(-1, 50), want2, mag=mag2)
+    assert_scores_close(f64(out2).reshape(-1, 50), full[..., NB - 50:].reshape(-1, 50),
+                        extra_tol=tol[..., NB - 50:])
 
 
 def _oracle_unit_scores(q, mu, s, u, Hkv):
-    """Oracle block scores of one (session, unit) and their sum of |terms|."""
+    """Oracle block scores of one (session, unit) and the float32 error bound
+    of the library's arithmetic for each."""
     l, g = divmod(u, Hkv)
     G = q.shape[2] // Hkv
-    qb = osc.query_reduce(f64(q[s:s + 1, l:l + 1, g * G:(g + 1) * G]), 1)     # [1][1][1][D]
+    qs = f64(q[s:s + 1, l:l + 1, g * G:(g + 1) * G])
+    qb = osc.query_reduce(qs, 1)                                              # [1][1][1][D]
+    qerr = qbar_error_bound(np.abs(qb), osc.query_reduce(np.abs(qs), 1), G * q.shape[3])
     m = f64(mu[l, g])[None, None]
-    return osc.block_scores(qb, m)[0, 0, 0], osc.block_scores(np.abs(qb), np.abs(m))[0, 0, 0]
+    want = osc.block_scores(qb, m)
+    tol = block_score_tolerance(want, np.abs(qb), m, 1 / np.sqrt(qb.shape[-1]), qerr)
+    return want[0, 0, 0], tol[0, 0, 0]
 
 
 def test_kvmem_1m_workload_full_size():
@@ -80,7 +88,7 @@ def test_kvmem_1m_workload_full_size():
     kept_h = kept.cpu().numpy()
     for u in [0, 300, U - 1]:
         want, mag = _oracle_unit_scores(q, mu, 0, u, cfg.Hkv)
-        assert_scores_close(f64(scores[0, u])[None], want[None], "unit %d" % u, mag=mag[None])
+        assert_scores_close(f64(scores[0, u])[None], want[None], "unit %d" % u, extra_tol=mag[None])
         s32 = numerics.round_to_f32(want)
         verdict = check_selection(kept_h[u], s32, k, cfg.n_sink, cfg.n_recent, what="unit %d" % u)
         if verdict == "exact":
@@ -137,7 +145,7 @@ def test_kvmem_10m_workload_full_size():
     for (s, u) in sample:
         got = np.concatenate(sampled_scores[(s, u)])
         want, mag = _oracle_unit_scores(qs, mu, s, u, cfg.Hkv)
-        assert_scores_close(got[None], want[None], "session %d unit %d" % (s, u), mag=mag[None])
+        assert_scores_close(got[None], want[None], "session %d unit %d" % (s, u), extra_tol=mag[None])
         s32 = numerics.round_to_f32(want)
         verdicts[(s, u)] = (check_selection(kept_h[s * U + u], s32, k, cfg.n_sink, cfg.n_recent,
                                             what="session %d unit %d" % (s, u)), s32)

@@ -61,7 +61,7 @@ def test_gather_rerope_matches_oracle(bt, rope, style, pos0):
     sk, sv = f64(src_k), f64(src_v)
     for u in range(U):
         ok, ov = om.gather_view(sk[u], sv[u], idx[u], bt, rope=rope, theta=1e6, pos0=pos0, style=style)
-        assert_rope_close(f64(dk[u]), ok, "unit %d" % u)
+        assert_rope_close(f64(dk[u]), ok, "unit %d" % u, style=style)
         np.testing.assert_array_equal(f64(dv[u]), ov)
 
 

@@ -96,6 +96,14 @@ def test_select_all_dead_and_empty():
     # U = 0 is a no-op
     kv.select(torch.zeros((0, 10), device=dev), torch.zeros((0, 4), dtype=torch.int32, device=dev),
               k_total=4, n_sink=0, n_recent=0)
+    # n = 0 with enough units for the single-launch path: the scores are an
+    # empty (NULL) buffer, nothing may be read, every unit keeps nothing
+    for U in (128, 300):
+        kept = torch.full((U, 6), 7, dtype=torch.int32, device=dev)
+        nk = torch.full((U,), 5, dtype=torch.int32, device=dev)
+        kv.select(torch.empty((U, 0), device=dev), kept, k_total=6, n_sink=2, n_recent=2, n_kept=nk)
+        torch.cuda.synchronize()
+        assert torch.all(kept == -1) and torch.all(nk == 0)
 
 
 def test_select_budget_error():

@@ -260,3 +260,14 @@ def test_keep_score_step_per_request():
         np.testing.assert_array_equal(ks2[r, :n], 0.5 * ks[r, :n] + np.where(h, a, 0.0))
         np.testing.assert_array_equal(ks2[r, n:], ks[r, n:])
         assert not hit[r, n:].any()
+
+
+def test_keep_score_step_rejects_lengths_beyond_the_row():
+    # a request cannot hold more entries than its row, nor fewer than none
+    state = np.ones((1, 2, 1, 5))
+    ks = np.zeros((2, 5))
+    for bad in (6, -1):
+        with pytest.raises(ValueError):
+            select.keep_score_step(state, ks, np.array([5, bad]), lam=0.5)
+    # requests not listed are not read
+    select.keep_score_step(state, ks, np.array([5, 99]), lam=0.5, req=[0])

@@ -128,7 +128,7 @@ CASES = [
      [T_sc.test_memory_scores_history_excludes_forced_and_dead]),
     ("select", "forced_mask", "(j >= n - n_recent)", "(j > n - n_recent)",
      [T_sel.test_budget_edge_cases, T_sel.test_topk_equals_max_sum_brute_force]),
-    ("select", "keep_score_step", "n = min(max(int(n_len[r]), 0), n_cap)", "n = n_cap",
+    ("select", "keep_score_step", "n = int(n_len[r])", "n = n_cap",
      [T_act.test_keep_score_step_per_request]),
     ("materialise", "decode_attention_slots", "s = (K @ q) * scale", "s = (K @ q)",
      [T_rm.test_decode_attention_two_key_closed_form]),

@@ -8,6 +8,7 @@ import pytest
 from oracle import materialise as om
 from oracle import numerics
 from oracle.rope import inv_freq, rope_rotate
+from parity import bf16_ulp, pair_norm
 
 
 # ---------------------------------------------------------------- RoPE
@@ -53,15 +54,18 @@ def test_rope_identity_norm_composition_relative():
         assert abs(d1 - d2) < 1e-9
 
 
-def _pair_ulp(x):
-    """bf16 ULP of each rotate-half pair's magnitude, per element.
+def _delta_bar(o):
+    """Bound on |R(dp) bf16(R(p_old) x) - bf16(R(p_new) x)| per element, both
+    sides rounded to bf16 at the end.
 
-    Rotation mixes a pair's two components, so a rounding error made in one
-    component shows up in the other: bounds are stated against the pair."""
-    h = x.shape[-1] // 2
-    r = np.sqrt(x[..., :h] ** 2 + x[..., h:] ** 2)
-    r = np.concatenate([r, r], axis=-1)
-    return np.ldexp(1.0, np.frexp(r)[1] - 8)
+    The baked K carries one rounding error per element, at most half a bf16
+    ULP, i.e. 2^-8 of the element; as a vector over the rotation pair that is
+    at most 2^-8 (1 + 2^-8) of the pair's magnitude, and the rotation by dp
+    moves it, unchanged in length, onto both components.  The two final
+    roundings of values that close differ by at most one step of the
+    element's own grid (its ULP) plus that carried error, which the ULP grid
+    of the larger of the two values stretches by at most 2^-7 of itself."""
+    return bf16_ulp(o) + 2.0 ** -8 * (1 + 2.0 ** -8) * (1 + 2.0 ** -7) * pair_norm(o)
 
 
 # ---------------------------------------------------------------- gather
@@ -101,7 +105,7 @@ def test_gather_delta_on_baked_matches_raw_within_two_ulp():
     idx = np.array([0, 3, 17, 39])
     k_raw, _ = om.gather_view(raw, raw, idx, bt, rope="raw")
     k_del, _ = om.gather_view(baked, baked, idx, bt, rope="delta")
-    assert np.all(np.abs(k_del - k_raw) <= 2 * _pair_ulp(k_raw))
+    assert np.all(np.abs(k_del - k_raw) <= _delta_bar(k_raw))
 
 
 # ---------------------------------------------------------------- incremental view
@@ -135,7 +139,7 @@ def test_incremental_equals_fresh_build(seed):
     view_k = pk[pt].reshape(-1, D)
     view_v = pv[pt].reshape(-1, D)
     np.testing.assert_array_equal(view_v, fv)
-    assert np.all(np.abs(view_k - fk) <= 2 * _pair_ulp(fk))
+    assert np.all(np.abs(view_k - fk) <= _delta_bar(fk))
     hits = np.intersect1d(prev_idx, new_idx)
     assert n_miss == len(new_idx) - len(hits)
     assert len(set(pt.tolist())) == len(pt)                       # each page once
