@@ -228,6 +228,25 @@ kvsel_status kvsel_select_workspace(const kvsel_select_args* args, size_t* bytes
 kvsel_status kvsel_select(const kvsel_select_args* args, void* workspace,
                           size_t workspace_bytes, void* stream);
 
+/* kvsel_select without a workspace argument, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments, validation and results
+ * as kvsel_select; the scratch kvsel_select_workspace() would report lives
+ * instead in a fixed array of KVSEL_NOALLOC_SCRATCH_BYTES per device inside
+ * the library, reserved on each GPU the library runs on until the process
+ * ends.  The call itself allocates nothing.
+ * Sharing: every call on one GPU uses that GPU's array, so calls that
+ * overlap on one GPU (different streams, or host threads racing on one
+ * device) race and give undefined results; serialise them.  Each call writes
+ * every scratch word it reads, so no state carries over between calls.
+ * Errors: as kvsel_select, plus KVSEL_E_WORKSPACE when
+ * kvsel_select_workspace() would exceed KVSEL_NOALLOC_SCRATCH_BYTES (about
+ * 4 bytes per score of an untiled call; tiled calls need none), and
+ * KVSEL_E_DEVICE if the array's device address cannot be resolved. */
+#define KVSEL_NOALLOC_SCRATCH_BYTES (64u << 20)
+
+kvsel_status kvsel_select_noalloc(const kvsel_select_args* args, void* stream);
+
 /* ------------------------------------------------------------------ gather
  *
  * Materialise a selection as a compact view -- KVMem (tiered movement):

@@ -125,7 +125,8 @@ EXPORTS = ["kvsel_version", "kvsel_last_error", "kvsel_score_workspace", "kvsel_
            "kvsel_select_workspace", "kvsel_select", "kvsel_gather_workspace", "kvsel_gather_rerope",
            "kvsel_redirect", "kvsel_memory_update", "kvsel_build_index", "kvsel_free_list_workspace",
            "kvsel_free_list", "kvsel_compact_workspace", "kvsel_compact", "kvsel_decode_score",
-           "kvsel_keep_score_workspace", "kvsel_keep_score"]
+           "kvsel_keep_score_workspace", "kvsel_keep_score", "kvsel_select_noalloc"]
+NOALLOC_SCRATCH_BYTES = 64 << 20
 
 _lib = None
 
@@ -160,6 +161,7 @@ def load(path=LIB_PATH):
     lib.kvsel_decode_score.argtypes = [P(DecodeArgs), c_vp]
     lib.kvsel_keep_score_workspace.argtypes = [P(KeepScoreArgs), P(ctypes.c_size_t)]
     lib.kvsel_keep_score.argtypes = [P(KeepScoreArgs), c_vp, ctypes.c_size_t, c_vp]
+    lib.kvsel_select_noalloc.argtypes = [P(SelectArgs), c_vp]
     for name in EXPORTS[2:]:
         getattr(lib, name).restype = c_i32
     _lib = lib

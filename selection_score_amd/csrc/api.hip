@@ -378,6 +378,64 @@ kvsel_status kvsel_select(const kvsel_select_args* a, void* ws, size_t ws_bytes,
   }
 }
 
+// ------------------------------------------------------------------ select, no allocation
+//
+// For callers that cannot allocate device memory: the select workspace lives
+// in a fixed array of the library, one per device, instead of a caller
+// buffer.  Host code never uses the array's name as an address (that is a
+// host-side stand-in); it resolves the device address once per device with
+// hipGetSymbolAddress and passes that pointer to the kernels.
+
+namespace {
+
+static __device__ __align__(256) unsigned char scratch[KVSEL_NOALLOC_SCRATCH_BYTES];
+
+// Device address of `scratch` on the current device, resolved on the first
+// call per device (with that device current) and kept for the process.
+kvsel_status noalloc_scratch(void** out) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return hip_fail(e, "hipGetDevice");
+  static std::mutex mu;
+  static std::vector<void*> ptrs;
+  std::lock_guard<std::mutex> lock(mu);
+  if (static_cast<int>(ptrs.size()) <= dev) ptrs.resize(dev + 1, nullptr);
+  if (ptrs[dev] == nullptr) {
+    void* ptr = nullptr;
+    e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return hip_fail(e, "hipGetSymbolAddress(scratch)");
+    if (ptr == nullptr) return fail(KVSEL_E_DEVICE, "hipGetSymbolAddress(scratch) returned NULL");
+    ptrs[dev] = ptr;
+  }
+  *out = ptrs[dev];
+  return KVSEL_OK;
+}
+
+}  // namespace
+
+kvsel_status kvsel_select_noalloc(const kvsel_select_args* a, void* stream) {
+  try {
+    kvsel_status s = validate_select(a);
+    if (s != KVSEL_OK) return s;
+    const SelectParams p = select_params(a);
+    const size_t need = select_workspace_bytes(p);
+    if (need > static_cast<size_t>(KVSEL_NOALLOC_SCRATCH_BYTES))
+      return fail(KVSEL_E_WORKSPACE, "select needs %zu bytes of scratch; the fixed scratch holds %zu", need,
+                  static_cast<size_t>(KVSEL_NOALLOC_SCRATCH_BYTES));
+    if ((s = check_device()) != KVSEL_OK) return s;
+    void* ws = nullptr;
+    if (need > 0 && (s = noalloc_scratch(&ws)) != KVSEL_OK) return s;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    if (p.U > 0 && p.n > 0 && (s = debug_scores(a->scores, p.U, p.n, p.row_stride, st, "scores")) != KVSEL_OK)
+      return s;
+    // every word of the scratch a launch reads is written earlier in the
+    // same call (keys and per-slice histograms), so nothing is cleared
+    return finish(launch_select(p, a->scores, ws, st), st, "select (no allocation)");
+  } catch (...) {
+    return fail(KVSEL_E_ARG, "internal error");
+  }
+}
+
 // ------------------------------------------------------------------ gather
 
 static kvsel_status validate_gather(const kvsel_gather_args* a, GatherParams* gp, RopeTable* rt) {

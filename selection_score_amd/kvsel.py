@@ -171,13 +171,8 @@ def score_block(q, mu, out, *, n_kv_heads, n_begin=0, n_count=None, qbar=None, q
 
 # ------------------------------------------------------------------ select
 
-def select(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0, keep_mask=None,
-           n_kept=None, slot_map=None, dead_slot=0, cand_score=None, cand_idx=None, cand_count=None,
-           finalize=True, pool="none", pool_k=1, workspace=None, stream=None):
-    """kvsel_select.  scores [U][n] float32 (rows may be a strided view of
-    contiguous memory: pass the 2-D tensor); kept_idx [U][k_total] int32.
-    pool/pool_k rank pooled scores (untiled calls).  Returns the workspace
-    (untiled calls need one; pass it back to reuse it)."""
+def _select_args(scores, kept_idx, *, k_total, n_sink, n_recent, n_total, base, keep_mask, n_kept, slot_map,
+                 dead_slot, cand_score, cand_idx, cand_count, finalize, pool, pool_k):
     U, n = scores.shape
     if n_total is None:
         n_total = base + n
@@ -202,12 +197,39 @@ def select(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0,
     a.finalize = 1 if finalize else 0
     a.kept_idx, a.keep_mask, a.n_kept = _ptr(kept_idx), _ptr(keep_mask), _ptr(n_kept)
     a.pool, a.pool_k = _abi.POOL[pool], pool_k
+    return a
+
+
+def select(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0, keep_mask=None,
+           n_kept=None, slot_map=None, dead_slot=0, cand_score=None, cand_idx=None, cand_count=None,
+           finalize=True, pool="none", pool_k=1, workspace=None, stream=None):
+    """kvsel_select.  scores [U][n] float32 (rows may be a strided view of
+    contiguous memory: pass the 2-D tensor); kept_idx [U][k_total] int32.
+    pool/pool_k rank pooled scores (untiled calls).  Returns the workspace
+    (untiled calls need one; pass it back to reuse it)."""
+    a = _select_args(scores, kept_idx, k_total=k_total, n_sink=n_sink, n_recent=n_recent, n_total=n_total,
+                     base=base, keep_mask=keep_mask, n_kept=n_kept, slot_map=slot_map, dead_slot=dead_slot,
+                     cand_score=cand_score, cand_idx=cand_idx, cand_count=cand_count, finalize=finalize,
+                     pool=pool, pool_k=pool_k)
     lib = _abi.load()
     nb = ctypes.c_size_t(0)
     _check(lib.kvsel_select_workspace(ctypes.byref(a), ctypes.byref(nb)))
     ws, wsz = _workspace(nb.value, scores.device, workspace)
     _check(lib.kvsel_select(ctypes.byref(a), _ptr(ws), wsz, _stream(stream)))
     return ws
+
+
+def select_noalloc(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0, keep_mask=None,
+                   n_kept=None, slot_map=None, dead_slot=0, cand_score=None, cand_idx=None, cand_count=None,
+                   finalize=True, pool="none", pool_k=1, stream=None):
+    """kvsel_select_noalloc: kvsel_select with its scratch in the library's
+    fixed per-device array (nothing is allocated, here or in the library).
+    Calls that overlap on one GPU share that array and race."""
+    a = _select_args(scores, kept_idx, k_total=k_total, n_sink=n_sink, n_recent=n_recent, n_total=n_total,
+                     base=base, keep_mask=keep_mask, n_kept=n_kept, slot_map=slot_map, dead_slot=dead_slot,
+                     cand_score=cand_score, cand_idx=cand_idx, cand_count=cand_count, finalize=finalize,
+                     pool=pool, pool_k=pool_k)
+    _check(_abi.load().kvsel_select_noalloc(ctypes.byref(a), _stream(stream)))
 
 
 # ------------------------------------------------------------------ gather
