@@ -148,6 +148,10 @@ struct SelectParams {
 // select_workspace_bytes(p): the keys and per-slice top-byte histograms of
 // the two-launch paths (0 for the single-launch path and empty calls).
 size_t select_workspace_bytes(const SelectParams& p);
+// Tiled calls whose tile and running set fit in LDS run one launch of
+// select_tile_kernel (no workspace).
+bool select_tile_fits(const SelectParams& p);
+hipError_t launch_select_tile(const SelectParams& p, const float* scores, hipStream_t st);
 hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, hipStream_t st);
 
 struct RopeTable {

@@ -126,6 +126,11 @@ __global__ __launch_bounds__(256) void block_scores_kernel(BlockParams p, const 
 typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
+// Each wavefront scores kTilesPerWave consecutive 16-row tiles of one unit
+// (a contiguous 32 KiB run of the index), loading the next tile's A
+// fragments while the current tile's MFMAs and stores run.
+constexpr int kTilesPerWave = 8;
+
 __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, const float* __restrict__ qbar,
                                                                 const uint16_t* __restrict__ mu,
                                                                 float* __restrict__ out) {
@@ -133,6 +138,10 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
   const int u = blockIdx.y;
   const int lane = threadIdx.x & 63;
   const int col = lane & 15, quarter = lane >> 4;
+  const int64_t n_tiles = (p.n_count + 15) / 16;
+  const int64_t t_begin = (static_cast<int64_t>(blockIdx.x) * 4 + (threadIdx.x >> 6)) * kTilesPerWave;
+  const int64_t t_end = min(n_tiles, t_begin + kTilesPerWave);
+  if (t_begin >= n_tiles) return;                // whole wavefront; the kernel has no barrier
   // B fragments: session `col`, d = 8*quarter + 32t + 4h + j; scaled by 2^-e
   const bool live = col < p.S;
   const float* qb = qbar + (static_cast<int64_t>(col < p.S ? col : 0) * U + u) * 128;
@@ -163,18 +172,16 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
         bl[t][h][j] = static_cast<_Float16>(x - static_cast<float>(hi));
       }
   const uint16_t* mu_u = mu + (static_cast<int64_t>(u) * p.NB + p.n_begin) * 128;
-  const int64_t n_tiles = (p.n_count + 15) / 16;
-  const int64_t wave = (static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x) / 64;
-  const int64_t n_waves = static_cast<int64_t>(gridDim.x) * blockDim.x / 64;
   float* out_s = out + (static_cast<int64_t>(col) * U + u) * p.n_count;
   const bool vec_out = (reinterpret_cast<uintptr_t>(out_s) & 15) == 0;
-  for (int64_t tile = wave; tile < n_tiles; tile += n_waves) {
+  auto load = [&](int64_t tile, uint4* a) {
     const int64_t r = tile * 16 + col;           // A row of this lane
-    uint4 a[4];
 #pragma unroll
     for (int t = 0; t < 4; ++t)
       a[t] = (r < p.n_count) ? *reinterpret_cast<const uint4*>(mu_u + r * 128 + 8 * quarter + 32 * t)
                              : make_uint4(0, 0, 0, 0);
+  };
+  auto score = [&](int64_t tile, const uint4* a) {
     f32x4 acc = {0.f, 0.f, 0.f, 0.f};
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
@@ -197,6 +204,16 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
         for (int i = 0; i < 4; ++i)
           if (rr0 + i < p.n_count) out_s[rr0 + i] = acc[i] * up;
       }
+    }
+  };
+  uint4 a0[4], a1[4];
+  load(t_begin, a0);
+  for (int64_t tile = t_begin; tile < t_end; tile += 2) {
+    if (tile + 1 < t_end) load(tile + 1, a1);
+    score(tile, a0);
+    if (tile + 1 < t_end) {
+      if (tile + 2 < t_end) load(tile + 2, a0);
+      score(tile + 1, a1);
     }
   }
 }
@@ -221,8 +238,9 @@ hipError_t launch_block_scores(const BlockParams& p, const float* qbar, const vo
   dim3 grid(static_cast<unsigned>(blocks_x < 1 ? 1 : (blocks_x > 4096 ? 4096 : blocks_x)), U);
   const uint16_t* m = static_cast<const uint16_t*>(mu);
   if (p.D == 128) {
-    const int64_t bx = ceil_div(ceil_div(p.n_count, 16), 4 * 4);   // ~4 tiles per wave
-    dim3 g2(static_cast<unsigned>(bx < 1 ? 1 : (bx > 8192 ? 8192 : bx)), U);
+    const int64_t bx = ceil_div(ceil_div(p.n_count, 16), 4 * kTilesPerWave);
+    if (bx > 2147483647) return hipErrorInvalidValue;
+    dim3 g2(static_cast<unsigned>(bx), U);
     block_scores_mfma_kernel<<<g2, 256, 0, st>>>(p, qbar, m, out);
     return hipGetLastError();
   }

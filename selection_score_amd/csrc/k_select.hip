@@ -679,7 +679,7 @@ static bool select_single_launch(const SelectParams& p) {
 }
 
 size_t select_workspace_bytes(const SelectParams& p) {
-  if (p.U == 0 || p.n == 0 || select_single_launch(p)) return 0;
+  if (p.U == 0 || p.n == 0 || select_single_launch(p) || select_tile_fits(p)) return 0;
   const int64_t slices = ceil_div(p.n, kPrepKeys);
   const int64_t key_bytes = (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 256;
   return static_cast<size_t>(key_bytes + static_cast<int64_t>(p.U) * slices * 256 * 4);
@@ -708,6 +708,7 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
       select_kernel<kPrepared><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
     return hipGetLastError();
   }
+  if (select_tile_fits(p)) return launch_select_tile(p, scores, st);
   const size_t cand_bytes = static_cast<size_t>(p.k_total) * 8;
   if (p.n > 0) {
     // tiled, prepared: keys and top-byte histograms of the tile, then the

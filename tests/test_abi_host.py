@@ -92,10 +92,14 @@ def test_select_validation_errors_without_device():
     assert b"workspace" in lib.kvsel_last_error()
     assert _status(lib.kvsel_select, _select_args(), ctypes.c_void_p(0x10000), ctypes.c_size_t(nb.value - 1),
                    None) == _abi.KVSEL_E_WORKSPACE
-    # a tile of a tiled call likewise
+    # a tile of a tiled call whose running set and tile fit in LDS needs none;
+    # a tile too wide for the LDS bitmap takes the two-launch path and does
     tiled = dict(cand_score=0x3000, cand_idx=0x4000, cand_count=0x5000, n=60, n_total=100, base=40)
     assert _status(lib.kvsel_select_workspace, _select_args(**tiled), ctypes.byref(nb)) == _abi.KVSEL_OK
-    assert nb.value >= 60 * 4
+    assert nb.value == 0
+    wide = dict(tiled, n=1 << 23, n_total=(1 << 23) + 40, row_stride=1 << 23)
+    assert _status(lib.kvsel_select_workspace, _select_args(**wide), ctypes.byref(nb)) == _abi.KVSEL_OK
+    assert nb.value >= (1 << 23) * 4
     # a partial range without candidate buffers, or an oversize range
     assert _status(lib.kvsel_select_workspace, _select_args(n=50), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
     assert _status(lib.kvsel_select_workspace, _select_args(base=60), ctypes.byref(nb)) == _abi.KVSEL_E_ARG

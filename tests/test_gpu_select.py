@@ -139,6 +139,68 @@ def test_select_tiled_equals_untiled(n, tile, k):
         np.testing.assert_array_equal(kept[u, : len(ok)], ok)
 
 
+def _tiled(dev, s, k, n_sink, n_recent, tile, slot_map=None, dead_slot=0, stride_pad=0):
+    """Tiled selection of every row of s (with an optional slot map), tiles
+    of `tile` columns in ascending order; the rows may sit in a wider
+    buffer (stride_pad extra columns) so that tile rows are misaligned."""
+    U, n = s.shape
+    buf = torch.zeros((U, n + stride_pad), dtype=torch.float32, device=dev)
+    buf[:, :n] = torch.from_numpy(s).to(dev)
+    cs = torch.full((U, k), 123.0, device=dev)
+    ci = torch.full((U, k), -9, dtype=torch.int32, device=dev)
+    cc = torch.zeros(U, dtype=torch.int32, device=dev)
+    kept = torch.full((U, k), -7, dtype=torch.int32, device=dev)
+    nk = torch.zeros(U, dtype=torch.int32, device=dev)
+    sm = None if slot_map is None else torch.from_numpy(slot_map.astype(np.int32)).to(dev)
+    for b in range(0, n, tile):
+        e = min(n, b + tile)
+        kv.select(buf[:, b:e], kept, k_total=k, n_sink=n_sink, n_recent=n_recent, n_total=n, base=b,
+                  cand_score=cs, cand_idx=ci, cand_count=cc, finalize=(e == n), n_kept=nk, slot_map=sm,
+                  dead_slot=dead_slot)
+    torch.cuda.synchronize()
+    return kept.cpu().numpy(), nk.cpu().numpy()
+
+
+@pytest.mark.parametrize("case", ["equal", "ascending", "descending", "coarse", "dead", "k8192", "misaligned"])
+def test_select_tiled_hard_cases(case):
+    """Tiles whose survivors overflow the LDS set (the first tile; rising
+    scores), plateaus of equal keys wider than any LDS set (every column
+    ranked by index), nothing surviving after the first tile, dead slots,
+    the largest budget, and tile rows that are not 16-byte aligned.  The
+    tiled result must equal the untiled oracle selection bit for bit."""
+    dev = require_gpu()
+    rng = np.random.default_rng(len(case))
+    U, n, tile, k, n_sink, n_recent = 3, 70000, 16384, 4096, 4, 64
+    slot_map, alive, dead_slot, pad = None, None, 0, 0
+    if case == "equal":
+        s = np.full((U, n), 0.75, np.float32)
+    elif case == "ascending":
+        s = np.tile(np.linspace(-3, 3, n, dtype=np.float32), (U, 1))
+    elif case == "descending":
+        s = np.tile(np.linspace(3, -3, n, dtype=np.float32), (U, 1))
+    elif case == "coarse":
+        s = (np.round(rng.standard_normal((U, n)) * 2) / 2).astype(np.float32)
+    elif case == "dead":
+        s = rng.standard_normal((U, n)).astype(np.float32)
+        dead_slot = 1 << 20
+        slot_map = np.arange(n, dtype=np.int64)
+        slot_map[rng.choice(n, n // 3, replace=False)] = dead_slot
+        slot_map[[0, n - 1]] = dead_slot
+        alive = slot_map != dead_slot
+    elif case == "k8192":
+        n, tile, k = 200000, 65536, 8192
+        s = rng.standard_normal((U, n)).astype(np.float32)
+    else:
+        n, tile, pad = 50001, 10001, 3
+        s = rng.standard_normal((U, n)).astype(np.float32)
+    got, nk = _tiled(dev, s, k, n_sink, n_recent, tile, slot_map, dead_slot, pad)
+    for u in range(U):
+        ok, _ = osel.select_topk(s[u].astype(np.float64), k, n_sink, n_recent, alive)
+        assert nk[u] == len(ok), case
+        np.testing.assert_array_equal(got[u, : len(ok)], ok, err_msg=case)
+        assert np.all(got[u, len(ok):] == -1)
+
+
 @pytest.mark.parametrize("pool,n", [("max", 4099), ("avg", 4097), ("max", 40000)])
 def test_select_pooled_slices(pool, n):
     """Pooling across the 4096-column slices of the key preparation (halo at
