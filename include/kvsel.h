@@ -272,9 +272,20 @@ kvsel_status kvsel_select_noalloc(const kvsel_select_args* args, void* stream);
  *   by (i_new - i_old)*bt when its position moved.  Pages of blocks that left
  *   the view are taken in ascending page order by the new blocks in
  *   ascending block order; those get K = R(pos0 + i_new*bt + o) raw K and
- *   V copied, both read from src (as in FRESH).  Out: page_table [U][k]
- *   (page of each kept block, chronological), n_miss [U].
- *   idx holds the new selection [U][k] (ascending, all valid).
+ *   V copied, both read from src (as in FRESH), or, when staged_k is given,
+ *   from packed staging buffers: the i-th miss of unit u (misses in
+ *   ascending block order) at entry i of staged_k/staged_v
+ *   [U][staged_cap][bt][D] (the state after KVMem's host gather and
+ *   host-to-device copy of the missed blocks); src_k/src_v may then be NULL.
+ *   Misses of rank >= staged_cap are skipped (their pages keep their bytes).
+ *   Out: page_table [U][k] (page of each kept block, chronological),
+ *   n_miss [U].  idx holds the new selection [U][k] (ascending, all valid).
+ * Workspace: INCREMENTAL needs kvsel_gather_workspace() bytes (4 per entry:
+ *   the plan that pairs every new entry with its previous position or its
+ *   miss rank, written by one launch and read by the next); FRESH needs none.
+ *   The call takes a workspace so that it allocates nothing itself.
+ * ABI: staged_k, staged_v and staged_cap were appended to the struct; a
+ *   caller whose struct_size ends before them gets the raw-source form.
  */
 typedef struct kvsel_gather_args {
   uint32_t struct_size;
@@ -305,6 +316,10 @@ typedef struct kvsel_gather_args {
   int64_t pool_pages;
   int32_t* page_table;        /* out [U][k] */
   int32_t* n_miss;            /* out [U] */
+  /* INCREMENTAL, optional: packed misses */
+  const void* staged_k;       /* [U][staged_cap][bt][D] or NULL (misses from src) */
+  const void* staged_v;
+  int64_t staged_cap;         /* entries per unit in the staging buffers */
 } kvsel_gather_args;
 
 kvsel_status kvsel_gather_workspace(const kvsel_gather_args* args, size_t* bytes);
@@ -316,8 +331,12 @@ kvsel_status kvsel_gather_rerope(const kvsel_gather_args* args, void* workspace,
  *
  * IntentKV §4 (redirect) and §2 Q2: every dropped logical position is
  * pointed at one sentinel dead slot; kept positions keep their slot ids and
- * nothing moves.  slot_map [N] int32 in/out; keep_mask [N] u8 (1 = keep).
- * Already-dead entries stay dead.
+ * nothing moves.  slot_map [N] int32 in/out; keep_mask [N] u8 (1 = keep),
+ * or, when keep_mask is NULL, the kept positions themselves: kept_idx [k]
+ * int32 in ascending order, entries < 0 ignored (the -1 tail kvsel_select
+ * writes past n_kept), entries >= N never match; k = 0 keeps nothing
+ * (kept_idx may then be NULL).  Already-dead entries stay dead.
+ * (struct_size ending before kept_idx: the keep_mask form only.)
  * Sentinel init (optional, when k_pool is non-NULL): writes the dead slot's
  * rows in every layer and KV head: K = -1e4 rounded to the pool dtype
  * (bf16 -9984, f16 -10000), V = 0.  Pools are [L][pool_slots][Hkv][D] with
@@ -334,6 +353,8 @@ typedef struct kvsel_redirect_args {
   int32_t L, Hkv, D;
   int32_t dtype;         /* BF16 or F16 */
   int64_t pool_slots;    /* slots per layer */
+  const int32_t* kept_idx; /* [k] ascending, or NULL (keep_mask form) */
+  int32_t k;
 } kvsel_redirect_args;
 
 kvsel_status kvsel_redirect(const kvsel_redirect_args* args, void* stream);

@@ -61,6 +61,7 @@ class GatherArgs(ctypes.Structure):
         ("rope", c_i32), ("style", c_i32), ("rotary_dim", c_i32), ("theta", c_f64), ("pos0", c_i64),
         ("prev_idx", c_vp), ("prev_page", c_vp), ("pool_k", c_vp), ("pool_v", c_vp),
         ("pool_pages", c_i64), ("page_table", c_vp), ("n_miss", c_vp),
+        ("staged_k", c_vp), ("staged_v", c_vp), ("staged_cap", c_i64),
     ]
 
 
@@ -69,6 +70,7 @@ class RedirectArgs(ctypes.Structure):
         ("struct_size", c_u32), ("N", c_i64), ("slot_map", c_vp), ("keep_mask", c_vp),
         ("dead_slot", c_i64), ("k_pool", c_vp), ("v_pool", c_vp),
         ("L", c_i32), ("Hkv", c_i32), ("D", c_i32), ("dtype", c_i32), ("pool_slots", c_i64),
+        ("kept_idx", c_vp), ("k", c_i32),
     ]
 
 

@@ -5,6 +5,7 @@
 // are then enqueued on the caller's stream; nothing synchronises unless
 // KVSEL_DEBUG=1.  No exception crosses the ABI.
 #include <math.h>
+#include <stddef.h>
 #include <stdarg.h>
 #include <stdio.h>
 #include <stdlib.h>
@@ -438,9 +439,29 @@ kvsel_status kvsel_select_noalloc(const kvsel_select_args* a, void* stream) {
 
 // ------------------------------------------------------------------ gather
 
+// The packed-miss fields were appended to kvsel_gather_args; a struct that
+// ends before them is the raw-source form.
+struct GatherStaging {
+  const void* k = nullptr;
+  const void* v = nullptr;
+  int64_t cap = 0;
+};
+
+static GatherStaging gather_staging(const kvsel_gather_args* a) {
+  GatherStaging g;
+  if (a->struct_size >= sizeof(kvsel_gather_args)) {
+    g.k = a->staged_k;
+    g.v = a->staged_v;
+    g.cap = a->staged_cap;
+  }
+  return g;
+}
+
 static kvsel_status validate_gather(const kvsel_gather_args* a, GatherParams* gp, RopeTable* rt) {
   if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
-  if (a->struct_size < sizeof(kvsel_gather_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->struct_size < offsetof(kvsel_gather_args, staged_k)) return fail(KVSEL_E_ARG, "struct_size too small");
+  const GatherStaging stg = gather_staging(a);
+  const bool staged = a->mode == KVSEL_GATHER_INCREMENTAL && stg.k != nullptr;
   if (a->mode != KVSEL_GATHER_FRESH && a->mode != KVSEL_GATHER_INCREMENTAL) return fail(KVSEL_E_ARG, "bad mode");
   if (!valid_dtype(a->dtype)) return fail(KVSEL_E_ARG, "bad dtype");
   if (a->U < 0 || a->k < 0 || a->bt < 1) return fail(KVSEL_E_ARG, "need U, k >= 0 and bt >= 1");
@@ -459,9 +480,15 @@ static kvsel_status validate_gather(const kvsel_gather_args* a, GatherParams* gp
     if (rd / 2 > 128) return fail(KVSEL_E_UNSUPPORTED, "rotary_dim must be <= 256");
     if (!(a->theta > 0.0)) return fail(KVSEL_E_ARG, "theta must be > 0");
   }
-  if (a->src_k == nullptr || a->src_v == nullptr || a->idx == nullptr)
-    return fail(KVSEL_E_ARG, "src_k, src_v or idx is NULL");
-  if (!aligned16(a->src_k) || !aligned16(a->src_v)) return fail(KVSEL_E_ARG, "sources must be 16-byte aligned");
+  if (a->idx == nullptr) return fail(KVSEL_E_ARG, "idx is NULL");
+  if (staged) {
+    if (stg.v == nullptr) return fail(KVSEL_E_ARG, "staged_v is NULL");
+    if (!aligned16(stg.k) || !aligned16(stg.v)) return fail(KVSEL_E_ARG, "staging buffers must be 16-byte aligned");
+    if (stg.cap < 0) return fail(KVSEL_E_ARG, "staged_cap < 0");
+  } else {
+    if (a->src_k == nullptr || a->src_v == nullptr) return fail(KVSEL_E_ARG, "src_k or src_v is NULL");
+    if (!aligned16(a->src_k) || !aligned16(a->src_v)) return fail(KVSEL_E_ARG, "sources must be 16-byte aligned");
+  }
   if (a->src_rows < 0) return fail(KVSEL_E_ARG, "src_rows < 0");
   if (a->mode == KVSEL_GATHER_FRESH) {
     if (a->dst_k == nullptr || a->dst_v == nullptr) return fail(KVSEL_E_ARG, "dst_k or dst_v is NULL");
@@ -481,6 +508,7 @@ static kvsel_status validate_gather(const kvsel_gather_args* a, GatherParams* gp
   gp->U = a->U; gp->D = a->D; gp->bt = a->bt; gp->k = a->k; gp->dtype = a->dtype; gp->rope = a->rope;
   gp->style = a->style; gp->rotary_dim = rd; gp->src_unit_stride = a->src_unit_stride;
   gp->src_rows = a->src_rows; gp->pos0 = a->pos0; gp->pool_pages = a->pool_pages; gp->src_offsets = a->src_offsets;
+  gp->staged_cap = staged ? stg.cap : -1;
   for (int m = 0; m < 128; ++m) rt->inv_freq[m] = (m < rd / 2) ? pow(a->theta, -2.0 * m / rd) : 0.0;
   return KVSEL_OK;
 }
@@ -509,7 +537,8 @@ static kvsel_status debug_incremental(const kvsel_gather_args* a, hipStream_t st
   if ((s = debug_fetch(a->idx, n, &idx, st)) != KVSEL_OK || (s = debug_fetch(a->prev_idx, n, &prev, st)) != KVSEL_OK ||
       (s = debug_fetch(a->prev_page, n, &page, st)) != KVSEL_OK)
     return s;
-  const int64_t blocks = a->src_rows / a->bt;
+  // with packed staging the block ids address no source, so any id is valid
+  const int64_t blocks = (gather_staging(a).k != nullptr) ? (int64_t(1) << 31) : a->src_rows / a->bt;
   for (int u = 0; u < a->U; ++u) {
     for (int i = 0; i < a->k; ++i) {
       const size_t o = static_cast<size_t>(u) * a->k + i;
@@ -544,8 +573,9 @@ kvsel_status kvsel_gather_rerope(const kvsel_gather_args* a, void* ws, size_t ws
     if (a->mode == KVSEL_GATHER_FRESH)
       e = launch_gather_fresh(gp, rt, a->src_k, a->src_v, a->idx, a->n_idx, a->dst_k, a->dst_v, st);
     else
-      e = launch_gather_incremental(gp, rt, a->src_k, a->src_v, a->idx, a->prev_idx, a->prev_page, a->pool_k,
-                                    a->pool_v, a->page_table, a->n_miss, ws, st);
+      e = launch_gather_incremental(gp, rt, gp.staged_cap >= 0 ? gather_staging(a).k : a->src_k,
+                                    gp.staged_cap >= 0 ? gather_staging(a).v : a->src_v, a->idx, a->prev_idx,
+                                    a->prev_page, a->pool_k, a->pool_v, a->page_table, a->n_miss, ws, st);
     return finish(e, st, "gather");
   } catch (...) {
     return fail(KVSEL_E_ARG, "internal error");
@@ -557,10 +587,16 @@ kvsel_status kvsel_gather_rerope(const kvsel_gather_args* a, void* ws, size_t ws
 kvsel_status kvsel_redirect(const kvsel_redirect_args* a, void* stream) {
   try {
     if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
-    if (a->struct_size < sizeof(kvsel_redirect_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+    if (a->struct_size < offsetof(kvsel_redirect_args, kept_idx)) return fail(KVSEL_E_ARG, "struct_size too small");
+    // the kept-index form was appended; a struct ending before it has only the mask form
+    const bool list_form = a->struct_size >= sizeof(kvsel_redirect_args) && a->keep_mask == nullptr;
+    const int32_t* kept_idx = list_form ? a->kept_idx : nullptr;
+    const int32_t n_list = list_form ? a->k : 0;
     if (a->N < 0 || a->N > kMaxN) return fail(KVSEL_E_ARG, "N must be in [0, 2^31)");
-    if (a->N > 0 && (a->slot_map == nullptr || a->keep_mask == nullptr))
-      return fail(KVSEL_E_ARG, "slot_map or keep_mask is NULL");
+    if (a->N > 0 && a->slot_map == nullptr) return fail(KVSEL_E_ARG, "slot_map is NULL");
+    if (a->N > 0 && a->keep_mask == nullptr && !(list_form && (kept_idx != nullptr || n_list == 0)))
+      return fail(KVSEL_E_ARG, "give keep_mask, or kept_idx with k");
+    if (list_form && n_list < 0) return fail(KVSEL_E_ARG, "k < 0");
     if (a->dead_slot < 0 || a->dead_slot > kMaxN) return fail(KVSEL_E_ARG, "dead_slot outside int32");
     const bool sentinel = a->k_pool != nullptr;
     if (sentinel) {
@@ -573,12 +609,21 @@ kvsel_status kvsel_redirect(const kvsel_redirect_args* a, void* stream) {
     kvsel_status s = check_device();
     if (s != KVSEL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
+    if (debug_mode() && list_form && n_list > 0) {
+      std::vector<int32_t> h;
+      if ((s = debug_fetch(kept_idx, static_cast<size_t>(n_list), &h, st)) != KVSEL_OK) return s;
+      for (int32_t i = 1; i < n_list && h[i] >= 0; ++i)
+        if (h[i] <= h[i - 1]) return fail(KVSEL_E_ARG, "kept_idx is not ascending at %d", i);
+      for (int32_t i = 1; i < n_list; ++i)
+        if (h[i - 1] < 0 && h[i] >= 0) return fail(KVSEL_E_ARG, "kept_idx has a valid entry after a negative one at %d", i);
+    }
     hipError_t e = hipSuccess;
     if (sentinel) {
       e = launch_sentinel(a->k_pool, a->v_pool, a->L, a->Hkv, a->D, a->dtype, a->pool_slots, a->dead_slot, st);
       if (e != hipSuccess) return hip_fail(e, "sentinel");
     }
-    e = launch_redirect(a->N, a->slot_map, a->keep_mask, a->dead_slot, st);
+    e = list_form ? launch_redirect_list(a->N, a->slot_map, kept_idx, n_list, a->dead_slot, st)
+                  : launch_redirect(a->N, a->slot_map, a->keep_mask, a->dead_slot, st);
     return finish(e, st, "redirect");
   } catch (...) {
     return fail(KVSEL_E_ARG, "internal error");

@@ -161,6 +161,7 @@ struct GatherParams {
   int U, D, bt, k, dtype, rope, style, rotary_dim;
   int64_t src_unit_stride, src_rows, pos0, pool_pages;
   const int64_t* src_offsets;
+  int64_t staged_cap;   // INCREMENTAL: >= 0 when misses come from packed staging (entries per unit)
 };
 hipError_t launch_gather_fresh(const GatherParams& p, const RopeTable& rt, const void* src_k,
                                const void* src_v, const int32_t* idx, const int32_t* n_idx,
@@ -221,6 +222,10 @@ hipError_t launch_keep_score(const KeepScoreParams& p, const float* state, float
 
 hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, int64_t dead,
                            hipStream_t st);
+// Redirect with the kept positions given as an ascending list (negative
+// entries ignored): membership by binary search.
+hipError_t launch_redirect_list(int64_t N, int32_t* slot_map, const int32_t* kept_idx, int32_t k, int64_t dead,
+                                hipStream_t st);
 hipError_t launch_sentinel(void* k_pool, void* v_pool, int L, int Hkv, int D, int dtype,
                            int64_t pool_slots, int64_t dead, hipStream_t st);
 hipError_t launch_memory_update(int L, int Hq, int D, int W, int dt, const void* q, float* M,

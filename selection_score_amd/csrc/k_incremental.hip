@@ -7,7 +7,10 @@
 //    the change of its logical position, (i_new - i_old) * bt;
 //  * pages of blocks that left the view are freed and handed, in ascending
 //    page order, to the missed blocks in ascending block order;
-//  * a missed block gets raw K rotated to pos0 + i_new*bt + o and V copied.
+//  * a missed block gets raw K rotated to pos0 + i_new*bt + o and V copied,
+//    both read from the raw source by block id or, when the caller passes
+//    packed staging buffers (the missed blocks after their host-to-device
+//    copy, in ascending block order), from entry `miss rank` of the staging.
 // Hit pages, freed pages and miss pages are disjoint, so all moves run in one
 // pass with no conflicts (the concern ActKV §7.2 plans around for in-place
 // compaction).
@@ -46,8 +49,10 @@ __device__ __forceinline__ uint64_t lanemask_lt(int lane) {
 }
 }  // namespace
 
+// The plan per new entry: its previous position i_old (a hit), or -1 - r
+// for the miss of rank r among the unit's misses (ascending block order).
 size_t incremental_workspace_bytes(const GatherParams& p) {
-  return static_cast<size_t>(p.U) * p.k * sizeof(int32_t);   // i_old per new entry (-1 = miss)
+  return static_cast<size_t>(p.U) * p.k * sizeof(int32_t);
 }
 
 __global__ __launch_bounds__(kPlanThreads) void incremental_plan_kernel(
@@ -132,7 +137,7 @@ __global__ __launch_bounds__(kPlanThreads) void incremental_plan_kernel(
       if (miss) {
         const uint32_t r = base + __popcll(b & lanemask_lt(lane));
         pt_u[i] = (r < static_cast<uint32_t>(k)) ? s_freed[r] : -1;
-        old_u[i] = -1;
+        old_u[i] = -1 - static_cast<int32_t>(r);
       } else {
         pt_u[i] = ppage_u[io];
         old_u[i] = io;
@@ -198,7 +203,14 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
     if (hit && (angle_pos == 0 || !kRot)) continue;
     const uint8_t* sk = nullptr;
     const uint8_t* sv = nullptr;
-    if (!hit) {
+    if (!hit && p.staged_cap >= 0) {
+      // packed staging: the miss of rank r is entry r of the unit's buffers
+      const int64_t r = -1 - static_cast<int64_t>(io);
+      if (r >= p.staged_cap) continue;
+      const int64_t e = static_cast<int64_t>(u) * p.staged_cap + r;
+      sk = static_cast<const uint8_t*>(src_k) + e * item_bytes;
+      sv = static_cast<const uint8_t*>(src_v) + e * item_bytes;
+    } else if (!hit) {
       const int32_t b = idx[it];
       if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
       const int64_t soff = p.src_offsets ? p.src_offsets[u] : static_cast<int64_t>(u) * p.src_unit_stride;

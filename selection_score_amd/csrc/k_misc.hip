@@ -13,6 +13,28 @@ __global__ void redirect_kernel(int64_t N, int32_t* __restrict__ slot_map,
   if (j < N && keep[j] == 0) slot_map[j] = dead;
 }
 
+// The same with the kept positions as an ascending list (kvsel_select's
+// kept_idx, -1 past its count): j is kept iff it is in the list, found by a
+// binary search where negative entries sort last.
+__global__ void redirect_list_kernel(int64_t N, int32_t* __restrict__ slot_map,
+                                     const int32_t* __restrict__ kept, int32_t k, int32_t dead) {
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
+  if (j >= N) return;
+  int lo = 0, hi = k - 1;
+  bool found = false;
+  while (lo <= hi) {
+    const int mid = (lo + hi) >> 1;
+    const int64_t v = kept[mid] < 0 ? INT64_MAX : static_cast<int64_t>(kept[mid]);
+    if (v == j) {
+      found = true;
+      break;
+    }
+    if (v < j) lo = mid + 1;
+    else hi = mid - 1;
+  }
+  if (!found) slot_map[j] = dead;
+}
+
 // IntentKV §2 Q2: the dead slot holds K = -1e4 (rounded to the pool's
 // 16-bit format) and V = 0 in every layer and KV head.
 __global__ void sentinel_kernel(uint16_t* __restrict__ k_pool, uint16_t* __restrict__ v_pool,
@@ -240,6 +262,14 @@ hipError_t launch_redirect(int64_t N, int32_t* slot_map, const uint8_t* keep, in
   if (N == 0) return hipSuccess;
   redirect_kernel<<<static_cast<int>(ceil_div(N, 256)), 256, 0, st>>>(N, slot_map, keep,
                                                                      static_cast<int32_t>(dead));
+  return hipGetLastError();
+}
+
+hipError_t launch_redirect_list(int64_t N, int32_t* slot_map, const int32_t* kept_idx, int32_t k, int64_t dead,
+                                hipStream_t st) {
+  if (N == 0) return hipSuccess;
+  redirect_list_kernel<<<static_cast<int>(ceil_div(N, 256)), 256, 0, st>>>(N, slot_map, kept_idx, k,
+                                                                          static_cast<int32_t>(dead));
   return hipGetLastError();
 }
 

@@ -235,11 +235,11 @@ def select_noalloc(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None,
 # ------------------------------------------------------------------ gather
 
 def _gather_args(src_k, src_v, idx, *, bt, D, src_rows, src_offsets, src_unit_stride, rope, theta,
-                 pos0, style, rotary_dim):
+                 pos0, style, rotary_dim, dtype_of=None):
     a = _abi.GatherArgs()
     a.struct_size = ctypes.sizeof(_abi.GatherArgs)
     a.U, a.k = idx.shape
-    a.D, a.dtype, a.bt = D, _dtype(src_k), bt
+    a.D, a.dtype, a.bt = D, _dtype(src_k if dtype_of is None else dtype_of), bt
     a.src_k, a.src_v = _ptr(src_k), _ptr(src_v)
     a.src_offsets = _wptr(src_offsets, "src_offsets", torch.int64, numel=a.U)
     a.src_unit_stride, a.src_rows = src_unit_stride, src_rows
@@ -266,14 +266,23 @@ def gather_rerope(src_k, src_v, idx, dst_k, dst_v, *, bt, D, src_rows, src_offse
 
 
 def gather_incremental(src_k, src_v, idx, prev_idx, prev_page, pool_k, pool_v, page_table, n_miss, *,
-                       bt, D, src_rows, src_offsets=None, src_unit_stride=0, rope="raw", theta=1e6,
-                       pos0=0, style="half", rotary_dim=0, workspace=None, stream=None):
+                       bt, D, src_rows=0, src_offsets=None, src_unit_stride=0, rope="raw", theta=1e6,
+                       pos0=0, style="half", rotary_dim=0, staged_k=None, staged_v=None, workspace=None,
+                       stream=None):
     """kvsel_gather_rerope, INCREMENTAL mode.  pool_k/pool_v
-    [U][pool_pages][bt][D] updated in place; page_table [U][k], n_miss [U] out."""
+    [U][pool_pages][bt][D] updated in place; page_table [U][k], n_miss [U] out.
+    Misses come from src (by block id) or, with staged_k/staged_v
+    [U][staged_cap][bt][D], from packed staging (the i-th miss of a unit at
+    entry i); src_k/src_v may then be None."""
     a = _gather_args(src_k, src_v, idx, bt=bt, D=D, src_rows=src_rows, src_offsets=src_offsets,
                      src_unit_stride=src_unit_stride, rope=rope, theta=theta, pos0=pos0, style=style,
-                     rotary_dim=rotary_dim)
+                     rotary_dim=rotary_dim, dtype_of=pool_k)
     a.mode = _abi.GATHER_INCREMENTAL
+    if staged_k is not None:
+        cap = staged_k.shape[1]
+        _want(staged_k, "staged_k", pool_k.dtype, (a.U, cap, bt, D))
+        _want(staged_v, "staged_v", pool_k.dtype, (a.U, cap, bt, D))
+        a.staged_k, a.staged_v, a.staged_cap = _ptr(staged_k), _ptr(staged_v), cap
     a.prev_idx = _wptr(prev_idx, "prev_idx", torch.int32, numel=a.U * a.k)
     a.prev_page = _wptr(prev_page, "prev_page", torch.int32, numel=a.U * a.k)
     a.pool_k, a.pool_v, a.pool_pages = _ptr(pool_k), _ptr(pool_v), pool_k.shape[1]
@@ -289,15 +298,21 @@ def gather_incremental(src_k, src_v, idx, prev_idx, prev_page, pool_k, pool_v, p
 
 # ------------------------------------------------------------------ redirect / memory
 
-def redirect(slot_map, keep_mask, dead_slot, *, k_pool=None, v_pool=None, stream=None):
-    """kvsel_redirect.  slot_map [N] int32 (in place), keep_mask [N] uint8.
-    With k_pool/v_pool ([L][pool_slots][Hkv][D] views of the paged pools)
-    the dead slot's sentinel rows are written first."""
+def redirect(slot_map, keep_mask, dead_slot, *, kept_idx=None, k_pool=None, v_pool=None, stream=None):
+    """kvsel_redirect.  slot_map [N] int32 (in place); the kept set as
+    keep_mask [N] uint8, or (keep_mask None) as kept_idx [k] int32, ascending
+    with a -1 tail allowed.  With k_pool/v_pool ([L][pool_slots][Hkv][D]
+    views of the paged pools) the dead slot's sentinel rows are written first."""
     a = _abi.RedirectArgs()
     a.struct_size = ctypes.sizeof(_abi.RedirectArgs)
     a.N = slot_map.numel()
     a.slot_map = _wptr(slot_map, "slot_map", torch.int32)
     a.keep_mask = _wptr(keep_mask, "keep_mask", torch.uint8, numel=a.N)
+    if keep_mask is None and kept_idx is None:
+        raise ValueError("give keep_mask or kept_idx")
+    if keep_mask is None:
+        a.kept_idx = _wptr(kept_idx.reshape(-1), "kept_idx", torch.int32)
+        a.k = kept_idx.numel()
     a.dead_slot = dead_slot
     if k_pool is not None:
         L, slots, Hkv, D = k_pool.shape

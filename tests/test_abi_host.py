@@ -166,6 +166,48 @@ def test_gather_and_redirect_validation_without_device():
     r.k_pool, r.v_pool, r.L, r.Hkv, r.D, r.dtype, r.pool_slots = 0x3000, 0x4000, 1, 1, 128, _abi.F32, 6
     assert lib.kvsel_redirect(ctypes.byref(r), None) == _abi.KVSEL_E_UNSUPPORTED
     assert b"fp8" in lib.kvsel_last_error()
+    # the kept-index form: no mask and no list is only an empty list (k = 0);
+    # a list with k > 0 needs its pointer, and k may not be negative
+    r.k_pool = None
+    r.keep_mask, r.kept_idx, r.k = None, None, 4
+    assert lib.kvsel_redirect(ctypes.byref(r), None) == _abi.KVSEL_E_ARG
+    r.k = -1
+    r.kept_idx = 0x5000
+    assert lib.kvsel_redirect(ctypes.byref(r), None) == _abi.KVSEL_E_ARG
+    # a struct that ends before kept_idx (the earlier layout) has the mask form only
+    r.struct_size = _abi.RedirectArgs.kept_idx.offset
+    r.k = 4
+    assert lib.kvsel_redirect(ctypes.byref(r), None) == _abi.KVSEL_E_ARG
+    assert b"keep_mask" in lib.kvsel_last_error()
+    r.struct_size = _abi.RedirectArgs.kept_idx.offset - 8
+    assert lib.kvsel_redirect(ctypes.byref(r), None) == _abi.KVSEL_E_ARG
+    assert b"struct_size" in lib.kvsel_last_error()
+
+
+def test_gather_staging_fields_are_optional_for_the_earlier_layout():
+    lib = _abi.load()
+    a = _abi.GatherArgs()
+    a.mode, a.U, a.D, a.dtype, a.bt, a.k = _abi.GATHER_INCREMENTAL, 4, 128, _abi.BF16, 32, 16
+    a.idx, a.prev_idx, a.prev_page, a.pool_k, a.pool_v = 0x3000, 0x4000, 0x5000, 0x6000, 0x7000
+    a.page_table, a.n_miss, a.pool_pages, a.rope, a.theta = 0x8000, 0x9000, 20, _abi.ROPE["raw"], 1e6
+    nb = ctypes.c_size_t(0)
+    call = lambda: lib.kvsel_gather_workspace(ctypes.byref(a), ctypes.byref(nb))
+    # staging without a raw source is fine; without either it is not
+    a.struct_size = ctypes.sizeof(a)
+    a.staged_k, a.staged_v, a.staged_cap = 0xA000, 0xB000, 16
+    assert call() == _abi.KVSEL_OK and nb.value == 4 * 16 * 4
+    a.staged_v = 0xB008
+    assert call() == _abi.KVSEL_E_ARG                 # misaligned staging
+    a.staged_k = a.staged_v = None
+    assert call() == _abi.KVSEL_E_ARG and b"src" in lib.kvsel_last_error()
+    # the earlier layout (ending before staged_k) reads no staging fields
+    a.staged_k, a.staged_v = 0xA000, 0xB000
+    a.struct_size = _abi.GatherArgs.staged_k.offset
+    assert call() == _abi.KVSEL_E_ARG and b"src" in lib.kvsel_last_error()
+    a.src_k, a.src_v = 0x1000, 0x2000
+    assert call() == _abi.KVSEL_OK
+    a.struct_size = _abi.GatherArgs.staged_k.offset - 8
+    assert call() == _abi.KVSEL_E_ARG
 
 
 def test_index_validation_without_device():

@@ -108,8 +108,11 @@ def test_gather_aliased_sources_and_partial_counts():
         assert np.all(got_k[m * bt:] == 3.0) and np.all(got_v[m * bt:] == 5.0)
 
 
-@pytest.mark.parametrize("overlap", [0.5, 1.0, 0.0])
-def test_incremental_view_matches_oracle(overlap):
+@pytest.mark.parametrize("overlap,staged", [(0.5, False), (1.0, False), (0.0, False), (0.5, True), (0.0, True)])
+def test_incremental_view_matches_oracle(overlap, staged):
+    """The incremental view against the oracle's, with the misses read from
+    the raw source by block id or from packed staging buffers (the i-th miss
+    of a unit, in ascending block order, at entry i; no raw source given)."""
     dev = require_gpu()
     rng = np.random.default_rng(int(overlap * 10) + 11)
     U, nb, k, D, bt, spare = 4, 2000, 96, 128, 32, 10
@@ -142,9 +145,22 @@ def test_incremental_view_matches_oracle(overlap):
     pv = torch.from_numpy(pool_v.astype(np.float32)).to(torch.bfloat16).to(dev)
     pt = torch.full((U, k), -5, dtype=torch.int32, device=dev)
     nm = torch.zeros(U, dtype=torch.int32, device=dev)
-    kv.gather_incremental(raw_k, raw_v, torch.from_numpy(new_idx).to(dev), torch.from_numpy(prev_idx).to(dev),
-                          torch.from_numpy(prev_page).to(dev), pk, pv, pt, nm, bt=bt, D=D,
-                          src_rows=nb * bt, src_unit_stride=nb * bt * D, rope="raw", theta=1e6)
+    if staged:
+        # the host side of the tiered movement: missed blocks packed in ascending block order
+        sk = torch.zeros((U, k, bt, D), dtype=torch.bfloat16, device=dev)
+        sv = torch.zeros_like(sk)
+        for u in range(U):
+            miss = np.setdiff1d(new_idx[u], prev_idx[u])
+            rows = torch.from_numpy((miss[:, None] * bt + np.arange(bt)).reshape(-1)).to(dev)
+            sk[u, :len(miss)] = raw_k[u][rows].view(len(miss), bt, D)
+            sv[u, :len(miss)] = raw_v[u][rows].view(len(miss), bt, D)
+        kv.gather_incremental(None, None, torch.from_numpy(new_idx).to(dev), torch.from_numpy(prev_idx).to(dev),
+                              torch.from_numpy(prev_page).to(dev), pk, pv, pt, nm, bt=bt, D=D, rope="raw",
+                              theta=1e6, staged_k=sk, staged_v=sv)
+    else:
+        kv.gather_incremental(raw_k, raw_v, torch.from_numpy(new_idx).to(dev), torch.from_numpy(prev_idx).to(dev),
+                              torch.from_numpy(prev_page).to(dev), pk, pv, pt, nm, bt=bt, D=D,
+                              src_rows=nb * bt, src_unit_stride=nb * bt * D, rope="raw", theta=1e6)
     torch.cuda.synchronize()
     gk, gv, gpt, gnm = f64(pk), f64(pv), pt.cpu().numpy(), nm.cpu().numpy()
     for u in range(U):
@@ -155,3 +171,44 @@ def test_incremental_view_matches_oracle(overlap):
         np.testing.assert_array_equal(gpt[u], opt)
         np.testing.assert_array_equal(gv[u], ov)
         assert_rope_close(gk[u], ok, "pool unit %d" % u)
+
+
+def test_incremental_staging_shorter_than_the_misses():
+    """Misses beyond the staging capacity are skipped: their pages keep their
+    bytes, every other page is as the oracle builds it."""
+    dev = require_gpu()
+    rng = np.random.default_rng(21)
+    nb, k, D, bt, cap = 300, 40, 128, 32, 7
+    raw_k = torch.randn((nb * bt, D), generator=torch.Generator(device=dev).manual_seed(3), device=dev).to(torch.bfloat16)
+    raw_v = torch.randn_like(raw_k)
+    new = np.sort(rng.choice(nb, k, replace=False))
+    prev = np.sort(np.concatenate([new[: k - 10], rng.choice(np.setdiff1d(np.arange(nb), new), 10, replace=False)]))
+    page = rng.permutation(k + 3)[:k].astype(np.int32)
+    miss = np.setdiff1d(new, prev)
+    assert len(miss) == 10 > cap
+    pool0 = numerics.round_to_bf16(np.random.default_rng(22).standard_normal((k + 3, bt, D)))
+    pk = torch.from_numpy(pool0.astype(np.float32)).to(torch.bfloat16).to(dev)[None].contiguous()
+    pv = pk.clone()
+    rows = torch.from_numpy((miss[:cap, None] * bt + np.arange(bt)).reshape(-1)).to(dev)
+    sk = raw_k[rows].view(1, cap, bt, D).contiguous()
+    sv = raw_v[rows].view(1, cap, bt, D).contiguous()
+    pt = torch.empty((1, k), dtype=torch.int32, device=dev)
+    nm = torch.empty(1, dtype=torch.int32, device=dev)
+    t = lambda x: torch.from_numpy(np.asarray(x, np.int32)[None]).to(dev)
+    kv.gather_incremental(None, None, t(new), t(prev), t(page), pk, pv, pt, nm, bt=bt, D=D, rope="raw", theta=1e6,
+                          staged_k=sk, staged_v=sv)
+    torch.cuda.synchronize()
+    ok, ov, opt, onm = om.incremental_view(prev, page, new, pool0, pool0, f64(raw_k).reshape(nb, bt, D),
+                                           f64(raw_v).reshape(nb, bt, D), bt, theta=1e6)
+    assert int(nm[0]) == onm == len(miss)
+    gpt = pt.cpu().numpy()[0]
+    np.testing.assert_array_equal(gpt, opt)
+    skipped = set(gpt[np.isin(new, miss[cap:])].tolist())
+    gk, gv = f64(pk[0]), f64(pv[0])
+    for pg in range(k + 3):
+        if pg in skipped:
+            np.testing.assert_array_equal(gk[pg], pool0[pg])
+            np.testing.assert_array_equal(gv[pg], pool0[pg])
+        else:
+            assert_rope_close(gk[pg], ok[pg], "page %d" % pg)
+            np.testing.assert_array_equal(gv[pg], ov[pg])

@@ -101,6 +101,21 @@ def test_redirect_and_sentinel():
         # other slots untouched
         assert torch.isfinite(k_pool[:, :dead].float()).all()
 
+    # the kept set given as kvsel_select's ascending list with its -1 tail
+    # (and a position past N, which never matches) instead of the mask
+    kept = np.flatnonzero(keep).astype(np.int32)
+    for tail in (0, 7):
+        lst = np.concatenate([kept, [N + 3] if tail else [], np.full(tail, -1)]).astype(np.int32)
+        sm = torch.from_numpy(slot_map.astype(np.int32)).to(dev)
+        kv.redirect(sm, None, dead, kept_idx=torch.from_numpy(lst).to(dev))
+        torch.cuda.synchronize()
+        np.testing.assert_array_equal(sm.cpu().numpy(), om.redirect(slot_map, keep, dead))
+    # an empty list drops everything
+    sm = torch.from_numpy(slot_map.astype(np.int32)).to(dev)
+    kv.redirect(sm, None, dead, kept_idx=torch.empty(0, dtype=torch.int32, device=dev))
+    torch.cuda.synchronize()
+    assert np.all(sm.cpu().numpy() == dead)
+
 
 def test_intentkv_workload_full_size():
     """The session-memory workload at full size: 8 turns of memory updates,
