@@ -149,6 +149,49 @@ def check_selection(gpu_kept, scores32, k_total, n_sink, n_recent, alive=None, w
     return "near-tie"
 
 
+def boundary_gap(scores32, k_total, n_sink, n_recent, alive=None):
+    """The oracle's float32 relative gap between the last kept and the first
+    dropped candidate of one unit (None when the selection does not depend on
+    the scores: everything alive fits the budget, or nothing is left to fill)."""
+    s = np.asarray(scores32, dtype=np.float64) + 0.0
+    n = s.shape[0]
+    alive_m = np.ones(n, bool) if alive is None else np.asarray(alive, bool)
+    forced = osel.forced_mask(n, n_sink, n_recent) & alive_m
+    cand = np.nonzero(alive_m & ~forced)[0]
+    room = k_total - int(forced.sum())
+    if not 0 < room < len(cand):
+        return None
+    top = np.partition(-s[cand], (room - 1, room))[[room - 1, room]]
+    last_in, first_out = -top[0], -top[1]
+    return (last_in - first_out) / max(abs(last_in), 1e-30)
+
+
+class Conditioning:
+    """How one configuration's selections compared with the oracle: units
+    bit-exact, units accepted under the near-tie rule, units whose oracle
+    boundary gap is below TIE_RTOL (near-tie) or exactly zero (exact tie),
+    and units whose materialisation (gather, page table, redirect) was
+    compared bit for bit.  report() is printed by the full-size tests."""
+
+    def __init__(self, name):
+        self.name = name
+        self.units = self.exact = self.accepted = self.near = self.ties = self.materialised = 0
+
+    def add(self, verdict, gap):
+        self.units += 1
+        self.exact += verdict == "exact"
+        self.accepted += verdict == "near-tie"
+        if gap is not None and gap < TIE_RTOL:
+            self.near += 1
+            self.ties += gap == 0.0
+
+    def report(self):
+        return ("conditioning %s: %d units compared, %d bit-exact, %d accepted as near-ties; oracle boundary "
+                "gap < %g in %d units (exactly 0 in %d); materialisation compared bit for bit on %d units"
+                % (self.name, self.units, self.exact, self.accepted, TIE_RTOL, self.near, self.ties,
+                   self.materialised))
+
+
 def _first_diff(a, b):
     m = min(len(a), len(b))
     for i in range(m):

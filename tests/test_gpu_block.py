@@ -11,8 +11,8 @@ from oracle import numerics
 from oracle import score as osc
 from oracle import select as osel
 from oracle.rope import rope_rotate
-from parity import (assert_rope_close, assert_scores_close, block_score_tolerance, check_selection, f64,
-                    qbar_error_bound, require_gpu)
+from parity import (Conditioning, assert_rope_close, assert_scores_close, block_score_tolerance, boundary_gap,
+                    check_selection, f64, qbar_error_bound, require_gpu)
 
 import selection_score_amd as kv
 from selection_score_amd import workloads as wl
@@ -67,9 +67,14 @@ def _oracle_unit_scores(q, mu, s, u, Hkv):
     return want[0, 0, 0], tol[0, 0, 0]
 
 
+@pytest.mark.timeout(900)
 def test_kvmem_1m_workload_full_size():
-    """64 layers x 8 KV heads x 32768 blocks: block scores, top-2048 with block 0
-    and the last 4 forced, raw-K gather re-RoPEd to contiguous positions."""
+    """64 layers x 8 KV heads x 32768 blocks in the launch sequence the
+    benchmark times (query reduction + block scores, the single-launch
+    select, the raw-K gather re-RoPEd to contiguous positions).  Every one
+    of the 512 units: scores element by element and kept blocks bit for bit
+    (or under the near-tie rule); the gathered K and V on 32 bit-exact units
+    drawn in a seeded order."""
     dev = require_gpu()
     cfg = wl.CONFIGS["kvmem1m"]
     mu, w, _ = wl.kvmem_index(cfg, dev)
@@ -77,7 +82,8 @@ def test_kvmem_1m_workload_full_size():
     raw_k, raw_v, offs = wl.kvmem_raw_store(cfg, dev)
     U, NB, k, D, bt = cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt
     scores = torch.empty((1, U, NB), dtype=torch.float32, device=dev)
-    kv.score_block(q, mu, scores, n_kv_heads=cfg.Hkv)
+    qbar = torch.empty((1, cfg.L, cfg.Hkv, D), dtype=torch.float32, device=dev)
+    kv.score_block(q, mu, scores, n_kv_heads=cfg.Hkv, qbar=qbar)
     kept = torch.empty((U, k), dtype=torch.int32, device=dev)
     kv.select(scores[0], kept, k_total=k, n_sink=cfg.n_sink, n_recent=cfg.n_recent)
     vk = torch.empty((U, k * bt, D), dtype=torch.bfloat16, device=dev)
@@ -86,32 +92,44 @@ def test_kvmem_1m_workload_full_size():
                      rope="raw", theta=cfg.theta)
     torch.cuda.synchronize()
     kept_h = kept.cpu().numpy()
-    for u in [0, 300, U - 1]:
-        want, mag = _oracle_unit_scores(q, mu, 0, u, cfg.Hkv)
-        assert_scores_close(f64(scores[0, u])[None], want[None], "unit %d" % u, extra_tol=mag[None])
+    cond = Conditioning("kvmem1m")
+    exact = []
+    for u in range(U):
+        want, tol = _oracle_unit_scores(q, mu, 0, u, cfg.Hkv)
+        assert_scores_close(f64(scores[0, u])[None], want[None], "unit %d" % u, extra_tol=tol[None])
         s32 = numerics.round_to_f32(want)
         verdict = check_selection(kept_h[u], s32, k, cfg.n_sink, cfg.n_recent, what="unit %d" % u)
+        cond.add(verdict, boundary_gap(s32, k, cfg.n_sink, cfg.n_recent))
         if verdict == "exact":
-            l, g = divmod(u, cfg.Hkv)
-            buf = l % cfg.raw_layers
-            ok, _ = osel.select_topk(s32, k, cfg.n_sink, cfg.n_recent)
-            # only the kept blocks, in kept order: raw-mode positions depend on
-            # the entry's rank in the view, not on its block id
-            sel = torch.from_numpy(ok).to(dev)
-            rk = f64(raw_k[buf, g][sel]).reshape(k * bt, D)
-            rv = f64(raw_v[buf, g][sel]).reshape(k * bt, D)
-            gk, gv = om.gather_view(rk, rv, np.arange(k), bt, rope="raw", theta=cfg.theta)
-            assert_rope_close(f64(vk[u]), gk, "unit %d" % u)
-            np.testing.assert_array_equal(f64(vv[u]), gv)
+            exact.append(u)
+    for u in np.random.default_rng(cfg.seed).permutation(exact)[:32]:
+        l, g = divmod(int(u), cfg.Hkv)
+        # only the kept blocks, in kept order: raw-mode positions depend on
+        # the entry's rank in the view, not on its block id
+        sel = torch.from_numpy(kept_h[u]).to(dev)
+        buf = l % cfg.raw_layers
+        rk = f64(raw_k[buf, g][sel]).reshape(k * bt, D)
+        rv = f64(raw_v[buf, g][sel]).reshape(k * bt, D)
+        gk, gv = om.gather_view(rk, rv, np.arange(k), bt, rope="raw", theta=cfg.theta)
+        assert_rope_close(f64(vk[u]), gk, "unit %d" % u)
+        np.testing.assert_array_equal(f64(vv[u]), gv)
+        cond.materialised += 1
+    print(cond.report(), flush=True)
+    assert cond.exact >= 0.8 * U and cond.materialised == min(32, len(exact))
     assert np.all(kept_h[:, 0] == 0) and np.all(kept_h[:, -4:] == np.arange(NB - 4, NB))
     assert np.all(np.diff(kept_h, axis=1) > 0)
 
 
-@pytest.mark.timeout(600)
+@pytest.mark.timeout(900)
 def test_kvmem_10m_workload_full_size():
     """312500 blocks per unit scored in 65536-block tiles for 4 sessions,
     tiled top-4096, and the in-place incremental update of each session's
-    4096-page view (previous view shares about half its blocks)."""
+    4096-page view (previous view shares about half its blocks), in the
+    launch sequence the benchmark times.  64 (session, unit) views drawn in
+    a seeded order are checked against the oracle: their scores over every
+    tile, their kept blocks, and on the bit-exact ones the whole updated view
+    (page table, re-RoPEd misses, hits rotated in place, V).  Invariants hold
+    for every view."""
     dev = require_gpu()
     cfg = wl.CONFIGS["kvmem10m"]
     S, U, NB, k, D, bt, tile = cfg.S, cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt, cfg.tile
@@ -126,7 +144,8 @@ def test_kvmem_10m_workload_full_size():
     kept = torch.empty((SU, k), dtype=torch.int32, device=dev)
     nk = torch.empty(SU, dtype=torch.int32, device=dev)
     tile_out = torch.empty((S, U, tile), dtype=torch.float32, device=dev)
-    sample = [(0, 0), (1, 257), (3, U - 1)]
+    pick = np.random.default_rng(cfg.seed).permutation(SU)[:62]
+    sample = sorted(set([(0, 0), (S - 1, U - 1)] + [divmod(int(i), U) for i in pick]))
     sampled_scores = {su: [] for su in sample}
     for b in range(0, NB, tile):
         n = min(tile, NB - b)
@@ -141,7 +160,9 @@ def test_kvmem_10m_workload_full_size():
     torch.cuda.synchronize()
     kept_h = kept.cpu().numpy()
     assert np.all(nk.cpu().numpy() == k)
+    assert len(sample) >= 63
     verdicts = {}
+    cond = Conditioning("kvmem10m")
     for (s, u) in sample:
         got = np.concatenate(sampled_scores[(s, u)])
         want, mag = _oracle_unit_scores(qs, mu, s, u, cfg.Hkv)
@@ -149,6 +170,7 @@ def test_kvmem_10m_workload_full_size():
         s32 = numerics.round_to_f32(want)
         verdicts[(s, u)] = (check_selection(kept_h[s * U + u], s32, k, cfg.n_sink, cfg.n_recent,
                                             what="session %d unit %d" % (s, u)), s32)
+        cond.add(verdicts[(s, u)][0], boundary_gap(s32, k, cfg.n_sink, cfg.n_recent))
     del tile_out, cs, ci
 
     # ---- incremental view update
@@ -192,9 +214,13 @@ def test_kvmem_10m_workload_full_size():
         rk, rv = f64(raw_k[g][sel]), f64(raw_v[g][sel])
         prev_r = np.searchsorted(need, prev_idx[i])
         new_r = np.searchsorted(need, new_idx)
-        pk = np.empty((k, bt, D))
-        pv = np.empty((k, bt, D))
-        for j, b in enumerate(prev_r):
+        # the previous view: hits baked at their old positions (pages the
+        # update overwrites keep the synthetic fill; the oracle reads them too)
+        pk = np.full((k, bt, D), 0.5)
+        pv = np.full((k, bt, D), -0.25)
+        hit = np.isin(prev_idx[i], new_idx)
+        for j in np.flatnonzero(hit):
+            b = prev_r[j]
             pk[prev_page[i, j]] = numerics.round_to_bf16(rope_rotate(rk[b], j * bt + o, cfg.theta))
             pv[prev_page[i, j]] = rv[b]
         pool_k[i] = torch.from_numpy(pk.astype(np.float32)).to(torch.bfloat16).to(dev)
@@ -217,3 +243,6 @@ def test_kvmem_10m_workload_full_size():
         np.testing.assert_array_equal(pt_h[i], opt)
         np.testing.assert_array_equal(f64(pool_v[i]), ov)
         assert_rope_close(f64(pool_k[i]), ok, "session %d unit %d" % (s, u))
+        cond.materialised += 1
+    print(cond.report(), flush=True)
+    assert cond.exact >= 0.8 * len(sample) and cond.materialised == cond.exact

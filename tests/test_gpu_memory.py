@@ -11,7 +11,7 @@ from oracle import materialise as om
 from oracle import numerics
 from oracle import score as osc
 from oracle import select as osel
-from parity import assert_scores_close, check_selection, f64, require_gpu
+from parity import Conditioning, boundary_gap, assert_scores_close, check_selection, f64, require_gpu
 
 import selection_score_amd as kv
 from selection_score_amd import workloads as wl
@@ -162,9 +162,13 @@ def test_intentkv_workload_full_size():
     s32 = numerics.round_to_f32(want)
     verdict = check_selection(kept.cpu().numpy()[0], s32, cfg.k, cfg.n_sink, cfg.n_recent,
                               alive=sm_h != dead)
+    cond = Conditioning("intentkv")
+    cond.add(verdict, boundary_gap(s32, cfg.k, cfg.n_sink, cfg.n_recent, sm_h != dead))
     if verdict == "exact":
         _, om_mask = osel.select_topk(s32, cfg.k, cfg.n_sink, cfg.n_recent, sm_h != dead)
         np.testing.assert_array_equal(sm_new.cpu().numpy(), om.redirect(sm_h, om_mask, dead))
+        cond.materialised += 1
+    print(cond.report(), flush=True)
     # survivors unmoved, the rest on the dead slot, sentinel rows written
     new_h = sm_new.cpu().numpy()
     keep_h = mask.cpu().numpy()[0].astype(bool)

@@ -7,7 +7,7 @@ import torch
 from oracle import materialise as om
 from oracle import numerics
 from oracle import score as osc
-from parity import assert_scores_close, check_selection, f64, require_gpu
+from parity import Conditioning, assert_scores_close, boundary_gap, check_selection, f64, require_gpu
 
 import selection_score_amd as kv
 from selection_score_amd import workloads as wl
@@ -123,29 +123,48 @@ def osel_topk(s32, cfg):
     return osel.select_topk(s32, cfg.k, cfg.n_sink, cfg.n_recent)
 
 
-def test_snapkv_workload_full_size_sampled_units():
-    # full 36 x 8 x 32768 x 128 bf16 workload in the launch configuration the
-    # benchmark times; the oracle checks three whole units
+@pytest.mark.timeout(900)
+def test_snapkv_workload_full_size():
+    """The full 36 x 8 x 32768 x 128 bf16 workload in the launch sequence
+    the benchmark times: the LSE pass, the score pass with that LSE, select
+    with max-pool 7 fused into its key preparation, and the gather.  Every
+    one of the 288 units is checked against the oracle: the LSE and the
+    scores element by element, the kept indices bit for bit (or under the
+    near-tie rule), and on every bit-exact unit the gathered K and V."""
     dev = require_gpu()
     cfg = wl.CONFIGS["snapkv"]
     inp = wl.snapkv_inputs(cfg, dev)
-    scores, kept, mask, dk, dv = _token_path(dev, cfg, inp)
     q, k, v = inp["q"], inp["k"], inp["v"]
-    kept_h = kept.cpu().numpy()
-    for u in [0, 137, cfg.U - 1]:
-        pooled = _oracle_unit(cfg, q, k, u)
-        assert_scores_close(f64(scores[u])[None], pooled[None], "unit %d" % u)
-        s32 = numerics.round_to_f32(pooled)
-        verdict = check_selection(kept_h[u], s32, cfg.k, cfg.n_sink, cfg.n_recent, what="unit %d" % u)
+    U, N, D = cfg.U, cfg.N, cfg.D
+    lse = torch.empty((cfg.L, cfg.Hq, cfg.W), dtype=torch.float32, device=dev)
+    scores = torch.empty((U, N), dtype=torch.float32, device=dev)
+    kept = torch.empty((U, cfg.k), dtype=torch.int32, device=dev)
+    dk = torch.empty((U, cfg.k, D), dtype=k.dtype, device=dev)
+    dv = torch.empty_like(dk)
+    kv.score_window(q, k, None, lse_out=lse)
+    kv.score_window(q, k, scores, lse_in=lse)
+    kv.select(scores, kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent, pool=cfg.pool,
+              pool_k=cfg.pool_k)
+    kv.gather_rerope(k.view(U, N, D), v.view(U, N, D), kept, dk, dv, bt=1, D=D, src_rows=N, src_unit_stride=N * D)
+    torch.cuda.synchronize()
+    kept_h, lse_h = kept.cpu().numpy(), f64(lse)
+    cond = Conditioning("snapkv")
+    for u in range(U):
         l, g = divmod(u, cfg.Hkv)
-        ku, vu = f64(k[l, g]), f64(v[l, g])
+        heads = slice(g * cfg.G, (g + 1) * cfg.G)
+        a, ol = osc.window_scores(f64(q[l:l + 1, heads]), f64(k[l:l + 1, g:g + 1]))
+        assert_scores_close(lse_h[l, heads].reshape(1, -1), ol.reshape(1, -1), "lse of unit %d" % u)
+        assert_scores_close(f64(scores[u])[None], a[0, 0][None], "unit %d" % u)
+        s32 = numerics.round_to_f32(osc.pool1d(a[0, 0], cfg.pool, cfg.pool_k))
+        verdict = check_selection(kept_h[u], s32, cfg.k, cfg.n_sink, cfg.n_recent, what="unit %d" % u)
+        cond.add(verdict, boundary_gap(s32, cfg.k, cfg.n_sink, cfg.n_recent))
         if verdict == "exact":
-            ok, _ = osel_topk(s32, cfg)
-            gk, gv = om.gather_view(ku, vu, ok, 1)
+            gk, gv = om.gather_view(f64(k[l, g]), f64(v[l, g]), kept_h[u], 1)
             np.testing.assert_array_equal(f64(dk[u]), gk)
             np.testing.assert_array_equal(f64(dv[u]), gv)
-    # properties that hold for every unit at full size
+            cond.materialised += 1
+    print(cond.report(), flush=True)
+    assert cond.exact >= 0.8 * U and cond.materialised == cond.exact
     assert np.all(kept_h[:, : cfg.n_sink] == np.arange(cfg.n_sink))
-    assert np.all(kept_h[:, -cfg.n_recent:] == np.arange(cfg.N - cfg.n_recent, cfg.N))
+    assert np.all(kept_h[:, -cfg.n_recent:] == np.arange(N - cfg.n_recent, N))
     assert np.all(np.diff(kept_h, axis=1) > 0)
-    assert int(mask.sum().item()) == cfg.U * cfg.k

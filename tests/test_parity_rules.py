@@ -14,8 +14,8 @@ import pytest
 
 from oracle import numerics
 from oracle.rope import inv_freq, rope_rotate
-from parity import (assert_rope_close, bf16_ulp, block_score_tolerance, gamma32, pair_norm,
-                    qbar_error_bound, rope_violations)
+from parity import (Conditioning, assert_rope_close, bf16_ulp, block_score_tolerance, boundary_gap, gamma32,
+                    pair_norm, qbar_error_bound, rope_violations)
 
 D, THETA = 128, 1e6
 
@@ -152,3 +152,19 @@ def test_qbar_error_bound_covers_float64_summation_rounded_once():
     for row in q.astype(np.float32):
         acc = (acc + row).astype(np.float32)
     assert np.any(np.abs(acc.astype(np.float64) - exact) > bound)
+
+
+def test_boundary_gap_and_conditioning_counts():
+    s = np.array([9.0, 1.0, 5.0, 5.0, 3.0, 2.0, 8.0, 7.0])      # forced: 0 (sink) and 7 (recent)
+    assert boundary_gap(s, 4, 1, 1) == 0.0                      # 2 of {1..6} by score: 5 and 5 tie at the edge
+    assert boundary_gap(s, 5, 1, 1) == (5.0 - 3.0) / 5.0        # 3 of them: 8, 5, 5 kept, 3 out
+    assert boundary_gap(s, 8, 1, 1) is None                     # everything fits
+    alive = np.array([1, 1, 0, 1, 1, 1, 1, 1], bool)
+    assert boundary_gap(s, 4, 1, 1, alive) == (5.0 - 3.0) / 5.0
+    c = Conditioning("x")
+    c.add("exact", 0.5)
+    c.add("near-tie", 0.0)
+    c.add("exact", 1e-7)
+    c.add("exact", None)
+    assert (c.units, c.exact, c.accepted, c.near, c.ties) == (4, 3, 1, 2, 1)
+    assert "4 units compared" in c.report()
