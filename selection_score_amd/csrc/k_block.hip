@@ -128,8 +128,13 @@ typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Each wavefront scores kTilesPerWave consecutive 16-row tiles of one unit
 // (a contiguous 32 KiB run of the index), loading the next tile's A
-// fragments while the current tile's MFMAs and stores run.
+// fragments while the current tile's MFMAs run.  The scores of its 128 rows
+// are staged in the wavefront's own LDS rows (one per session, padded to
+// avoid bank conflicts) and written at the end as whole 512-byte runs per
+// session: the MFMA layout would otherwise scatter them as 64-byte pieces,
+// which costs the HBM write path several times their bytes.
 constexpr int kTilesPerWave = 8;
+constexpr int kStageStride = kTilesPerWave * 16 + 4;    // floats per staged session row
 
 __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, const float* __restrict__ qbar,
                                                                 const uint16_t* __restrict__ mu,
@@ -172,8 +177,8 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
         bl[t][h][j] = static_cast<_Float16>(x - static_cast<float>(hi));
       }
   const uint16_t* mu_u = mu + (static_cast<int64_t>(u) * p.NB + p.n_begin) * 128;
-  float* out_s = out + (static_cast<int64_t>(col) * U + u) * p.n_count;
-  const bool vec_out = (reinterpret_cast<uintptr_t>(out_s) & 15) == 0;
+  extern __shared__ float stage_all[];
+  float* stage = stage_all + (threadIdx.x >> 6) * p.S * kStageStride;
   auto load = [&](int64_t tile, uint4* a) {
     const int64_t r = tile * 16 + col;           // A row of this lane
 #pragma unroll
@@ -193,18 +198,9 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
       acc = __builtin_amdgcn_mfma_f32_16x16x16f16(a1, bl[t][1], acc, 0, 0, 0);
     }
     // lane holds session `col`, index rows tile*16 + 4*quarter + i
-    if (live) {
-      const int64_t rr0 = tile * 16 + 4 * quarter;
-      if (vec_out && rr0 + 3 < p.n_count) {
-        // four consecutive scores in one non-temporal 16-byte store
-        __builtin_nontemporal_store(f32x4{acc[0] * up, acc[1] * up, acc[2] * up, acc[3] * up},
-                                    reinterpret_cast<f32x4*>(out_s + rr0));
-      } else {
-#pragma unroll
-        for (int i = 0; i < 4; ++i)
-          if (rr0 + i < p.n_count) out_s[rr0 + i] = acc[i] * up;
-      }
-    }
+    if (live)
+      *reinterpret_cast<f32x4*>(stage + col * kStageStride + (tile - t_begin) * 16 + 4 * quarter) =
+          f32x4{acc[0] * up, acc[1] * up, acc[2] * up, acc[3] * up};
   };
   uint4 a0[4], a1[4];
   load(t_begin, a0);
@@ -214,6 +210,21 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
     if (tile + 1 < t_end) {
       if (tile + 2 < t_end) load(tile + 2, a0);
       score(tile + 1, a1);
+    }
+  }
+  // the wavefront's own LDS rows: its LDS operations complete in order
+  __builtin_amdgcn_wave_barrier();
+  const int64_t row0 = t_begin * 16;
+  const int rows = static_cast<int>(min(p.n_count, t_end * 16) - row0);
+  for (int c = lane; c < p.S * (kTilesPerWave * 4); c += 64) {
+    const int sess = c / (kTilesPerWave * 4), j = 4 * (c % (kTilesPerWave * 4));
+    if (j >= rows) continue;
+    const f32x4 v = *reinterpret_cast<const f32x4*>(stage + sess * kStageStride + j);
+    float* o = out + (static_cast<int64_t>(sess) * U + u) * p.n_count + row0 + j;
+    if (j + 3 < rows && (reinterpret_cast<uintptr_t>(o) & 15) == 0) {
+      __builtin_nontemporal_store(v, reinterpret_cast<f32x4*>(o));
+    } else {
+      for (int i = 0; i < 4 && j + i < rows; ++i) o[i] = v[i];
     }
   }
 }
@@ -241,7 +252,8 @@ hipError_t launch_block_scores(const BlockParams& p, const float* qbar, const vo
     const int64_t bx = ceil_div(ceil_div(p.n_count, 16), 4 * kTilesPerWave);
     if (bx > 2147483647) return hipErrorInvalidValue;
     dim3 g2(static_cast<unsigned>(bx), U);
-    block_scores_mfma_kernel<<<g2, 256, 0, st>>>(p, qbar, m, out);
+    const size_t lds = static_cast<size_t>(4) * p.S * kStageStride * sizeof(float);
+    block_scores_mfma_kernel<<<g2, 256, lds, st>>>(p, qbar, m, out);
     return hipGetLastError();
   }
   if (p.S <= 1) block_scores_kernel<1><<<grid, 256, 0, st>>>(p, qbar, m, out);
