@@ -158,7 +158,13 @@ typedef struct kvsel_score_args {
   float* scores;        /* output, F32 */
 } kvsel_score_args;
 
-/* Bytes of device workspace kvsel_score needs for `args` (may be 0). */
+/* Bytes of device workspace kvsel_score needs for `args` (may be 0).
+ * Memory mode keeps a float32 logit scratch of whole layers (Hq * N * 4
+ * bytes per layer) at the end of its workspace and runs its logits -> LSE ->
+ * rule kernels in passes over as many layers as that scratch holds: the
+ * query asks for up to 512 MiB of scratch; a workspace shorter by whole
+ * layers is accepted down to one layer of scratch (more passes, the same
+ * results), and a shorter one fails with KVSEL_E_WORKSPACE. */
 kvsel_status kvsel_score_workspace(const kvsel_score_args* args, size_t* bytes);
 
 kvsel_status kvsel_score(const kvsel_score_args* args, void* workspace,

@@ -125,6 +125,8 @@ size_t round256(size_t b) { return (b + 255) / 256 * 256; }
 
 struct ScorePlan {
   size_t lse_off = 0, part_off = 0, raw_off = 0, mem_off = 0, qbar_off = 0, total = 0;
+  size_t logit_off = 0;   // memory mode: the logit scratch, last in the workspace
+  size_t min_total = 0;   // the least workspace accepted (memory mode: one layer of logit scratch)
   bool mfma = false;
   bool own_lse = false;
   bool pooled = false;
@@ -191,9 +193,12 @@ kvsel_status validate_score(const kvsel_score_args* a, ScorePlan* plan) {
     MemoryParams mp{};
     mp.L = a->L; mp.Hq = a->Hq; mp.Hkv = a->Hkv; mp.D = a->D; mp.page_size = a->page_size;
     mp.N = a->N; mp.pool_pages = a->pool_pages;
-    plan->mem_off = take(memory_workspace_bytes(mp));
+    plan->mem_off = take(memory_fixed_bytes(mp));
     const int64_t rows = a->reduce == KVSEL_REDUCE_GLOBAL ? 1 : U;
     if (plan->pooled) plan->raw_off = take(static_cast<size_t>(rows) * a->N * 4);
+    // the logit scratch comes last: a smaller workspace shortens only it
+    plan->logit_off = take(memory_logit_bytes(mp, false));
+    plan->min_total = plan->logit_off + memory_logit_bytes(mp, true);
   } else {
     if (a->k == nullptr) return fail(KVSEL_E_ARG, "index (k) is NULL");
     if (!aligned16(a->k)) return fail(KVSEL_E_ARG, "index must be 16-byte aligned");
@@ -212,6 +217,7 @@ kvsel_status validate_score(const kvsel_score_args* a, ScorePlan* plan) {
     if (a->qbar == nullptr) plan->qbar_off = take(static_cast<size_t>(a->S) * U * a->D * 4);
   }
   plan->total = off;
+  if (plan->min_total == 0) plan->min_total = plan->total;
   return KVSEL_OK;
 }
 
@@ -242,8 +248,9 @@ kvsel_status kvsel_score(const kvsel_score_args* a, void* ws, size_t ws_bytes, v
     ScorePlan plan;
     kvsel_status s = validate_score(a, &plan);
     if (s != KVSEL_OK) return s;
-    if (plan.total > 0 && (ws == nullptr || ws_bytes < plan.total))
-      return fail(KVSEL_E_WORKSPACE, "workspace needs %zu bytes, got %zu", plan.total, ws_bytes);
+    if (plan.total > 0 && (ws == nullptr || ws_bytes < plan.min_total))
+      return fail(KVSEL_E_WORKSPACE, "workspace needs %zu bytes (at least %zu), got %zu", plan.total, plan.min_total,
+                  ws == nullptr ? 0 : ws_bytes);
     if ((s = check_device()) != KVSEL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
     uint8_t* w = static_cast<uint8_t*>(ws);
@@ -277,7 +284,8 @@ kvsel_status kvsel_score(const kvsel_score_args* a, void* ws, size_t ws_bytes, v
       p.N = a->N; p.pool_pages = a->pool_pages; p.n_sink = a->n_sink; p.n_recent = a->n_recent;
       p.page_table = a->page_table; p.slot_map = a->slot_map; p.dead_slot = a->dead_slot;
       p.scale = scale; p.reduce = a->reduce;
-      e = launch_memory_scores(p, a->k_dtype, static_cast<const float*>(a->q), a->k, w + plan.mem_off, dst, st);
+      e = launch_memory_scores(p, a->k_dtype, static_cast<const float*>(a->q), a->k, w + plan.mem_off,
+                               reinterpret_cast<float*>(w + plan.logit_off), ws_bytes - plan.logit_off, dst, st);
       if (e != hipSuccess) return hip_fail(e, "memory scores");
       pool_rows = (a->reduce == KVSEL_REDUCE_GLOBAL) ? 1 : U;
     } else {

@@ -116,9 +116,13 @@ struct MemoryParams {
   float scale;
   int reduce;
 };
-size_t memory_workspace_bytes(const MemoryParams& p);
+// Memory-mode workspace: a fixed part (per-group LSE partials, LSE, per-layer
+// rule rows) and a logit scratch of whole layers; the scratch the caller
+// provides sets how many layers each pass covers (at least one).
+size_t memory_fixed_bytes(const MemoryParams& p);
+size_t memory_logit_bytes(const MemoryParams& p, bool minimum);
 hipError_t launch_memory_scores(const MemoryParams& p, int dt, const float* M, const void* pool,
-                                void* ws, float* out, hipStream_t st);
+                                void* ws, float* logits, size_t logit_bytes, float* out, hipStream_t st);
 
 struct BlockParams {
   int S, L, Hq, Hkv, D, W;

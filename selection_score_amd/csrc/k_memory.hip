@@ -18,6 +18,8 @@
 //     exp(logit - LSE) over H -> per-layer partial rule (or the per-unit
 //     output directly).
 //  4. global: rule[j] = sum over layers in ascending order (deterministic).
+// Kernels 1-3 run once per group of layers, reusing one bounded logit
+// scratch.
 #include "common.h"
 
 #include <math.h>
@@ -26,6 +28,16 @@ namespace kvsel {
 
 namespace {
 constexpr int kPagesPerGroup = 16;
+// Logits -> LSE -> rule run in passes over groups of layers that reuse one
+// logit scratch: as many layers per pass as the scratch the caller gave
+// holds.  The workspace query asks for up to kScratchBytes (32 heads x 65536
+// positions is 8 MiB per layer, so 36 layers take one pass).  Passes of a
+// few layers, so that the scratch would stay in the Infinity Cache, were
+// measured slower: the shorter launches lose more to their tails than the
+// cache saves.
+constexpr int64_t kScratchBytes = int64_t(512) << 20;
+
+int64_t layer_scratch_bytes(const MemoryParams& p) { return (static_cast<int64_t>(p.Hq) * p.N * 4 + 255) / 256 * 256; }
 constexpr float kLog2e = 1.4426950408889634f;
 constexpr int kMaxHq = 64;
 
@@ -35,7 +47,7 @@ __device__ __forceinline__ bool in_history(const MemoryParams& p, int64_t j) {
 }
 
 struct WsLayout {
-  size_t logits, part, lse, layer;   // byte offsets
+  size_t part, lse, layer;   // byte offsets of the fixed part
   size_t total;
 };
 
@@ -49,7 +61,6 @@ WsLayout ws_layout(const MemoryParams& p) {
     off += (bytes + 255) / 256 * 256;
     return o;
   };
-  w.logits = take(static_cast<size_t>(p.L) * p.Hq * p.N * 4);
   w.part = take(static_cast<size_t>(p.L) * p.Hq * n_groups * 8);
   w.lse = take(static_cast<size_t>(p.L) * p.Hq * 4);
   w.layer = take(static_cast<size_t>(p.L) * p.N * 4);
@@ -58,7 +69,15 @@ WsLayout ws_layout(const MemoryParams& p) {
 }
 }  // namespace
 
-size_t memory_workspace_bytes(const MemoryParams& p) { return ws_layout(p).total; }
+size_t memory_fixed_bytes(const MemoryParams& p) { return ws_layout(p).total; }
+
+size_t memory_logit_bytes(const MemoryParams& p, bool minimum) {
+  const int64_t per = layer_scratch_bytes(p);
+  if (minimum) return static_cast<size_t>(per);
+  const int64_t layers = max(static_cast<int64_t>(1), min(static_cast<int64_t>(p.L), kScratchBytes / per));
+  return static_cast<size_t>(layers * per);
+}
+
 
 template <int DT, int D>
 __global__ __launch_bounds__(256) void memory_logits_kernel(MemoryParams p, const float* __restrict__ M,
@@ -163,7 +182,10 @@ __global__ __launch_bounds__(256) void memory_logits_kernel(MemoryParams p, cons
 // ~2^-18 of the sum of |terms|).  Lane quarter q covers d = 32*ks + 8q .. +7
 // of k-step ks on both operands.  Each wavefront serves one block of 16
 // query heads (NG = 16 / G KV heads) and a share of the pages, reading all
-// NG rows of a page straight into its A operands before multiplying.
+// NG rows of a page straight into its A operands before multiplying.  The
+// workgroup's logits (its 256 positions x Hq heads) are staged in LDS and
+// written at the end as one 1 KiB run per head: the MFMA layout would
+// otherwise scatter them in 64-byte pieces.
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
@@ -174,7 +196,9 @@ __global__ __launch_bounds__(256) void memory_logits_mfma_kernel(MemoryParams p,
                                                                  float2* __restrict__ part) {
   constexpr int D = 128, PS = 16;
   constexpr int kWavesPerCb = 4 / NCB;
+  constexpr int kRow = kPagesPerGroup * PS + 4;      // staged floats per head (padded)
   __shared__ float2 red[4][64];
+  __shared__ __align__(16) float stage[32 * kRow];
   const int l = blockIdx.y, grp = blockIdx.x;
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   const int col = lane & 15, qd = lane >> 4;
@@ -253,13 +277,8 @@ __global__ __launch_bounds__(256) void memory_logits_mfma_kernel(MemoryParams p,
         float x[4];
 #pragma unroll
         for (int i = 0; i < 4; ++i) x[i] = acc[i] * p.scale;
-        float* dst = logits + (static_cast<int64_t>(l) * p.Hq + h) * p.N + j0;
-        if (j0 + 3 < p.N) {
-          *reinterpret_cast<float4*>(dst) = make_float4(x[0], x[1], x[2], x[3]);
-        } else {
-          for (int i = 0; i < 4; ++i)
-            if (j0 + i < p.N) dst[i] = x[i];
-        }
+        *reinterpret_cast<float4*>(&stage[h * kRow + (lp - lp_begin) * PS + 4 * qd]) =
+            make_float4(x[0], x[1], x[2], x[3]);
         for (int i = 0; i < 4; ++i) {
           if (!hist[i]) continue;
           if (x[i] > m) {
@@ -275,6 +294,24 @@ __global__ __launch_bounds__(256) void memory_logits_mfma_kernel(MemoryParams p,
   // combine the lane quarters and the wavefronts that share a head
   red[wave][lane] = make_float2(m, s);
   __syncthreads();
+  // the staged logits: whole rows of the group's positions, 16 bytes per lane
+  {
+    const int64_t j_begin = lp_begin * PS;
+    const int n_pos = static_cast<int>(min(p.N, lp_end * PS) - j_begin);
+    const int per_row = kRow / 4;                     // 16-byte pieces per staged row (incl. pad)
+    for (int c = threadIdx.x; c < p.Hq * per_row; c += 256) {
+      const int hh = c / per_row, jj = 4 * (c % per_row);
+      if (jj >= n_pos) continue;
+      const float4 v = *reinterpret_cast<const float4*>(&stage[hh * kRow + jj]);
+      float* dst = logits + (static_cast<int64_t>(l) * p.Hq + hh) * p.N + j_begin + jj;
+      if (jj + 3 < n_pos && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
+        *reinterpret_cast<float4*>(dst) = v;
+      } else {
+        const float vv[4] = {v.x, v.y, v.z, v.w};
+        for (int i = 0; i < 4 && jj + i < n_pos; ++i) dst[i] = vv[i];
+      }
+    }
+  }
   if (threadIdx.x < 16 * NCB) {
     const int cbh = threadIdx.x / 16, c = threadIdx.x % 16;
     const int hh = 16 * cbh + c;
@@ -387,43 +424,56 @@ static hipError_t launch_logits_t(const MemoryParams& p, int n_groups, const flo
 }
 
 hipError_t launch_memory_scores(const MemoryParams& p, int dt, const float* M, const void* pool,
-                                void* ws, float* out, hipStream_t st) {
+                                void* ws, float* logits, size_t logit_bytes, float* out, hipStream_t st) {
   if (p.N == 0 || p.L == 0) return hipSuccess;
   const WsLayout w = ws_layout(p);
   uint8_t* base = static_cast<uint8_t*>(ws);
-  float* logits = reinterpret_cast<float*>(base + w.logits);
-  float2* part = reinterpret_cast<float2*>(base + w.part);
-  float* lse = reinterpret_cast<float*>(base + w.lse);
+  float2* part_all = reinterpret_cast<float2*>(base + w.part);
+  float* lse_all = reinterpret_cast<float*>(base + w.lse);
   float* layer = reinterpret_cast<float*>(base + w.layer);
   const int n_groups = static_cast<int>(ceil_div(ceil_div(p.N, p.page_size), kPagesPerGroup));
-  hipError_t e;
   const int G = p.Hq / p.Hkv;
-  if (dt == KVSEL_BF16 && p.D == 128 && p.page_size == 16 && p.Hq <= 32 && (G == 4 || G == 8 || G == 16)) {
-    dim3 grid(n_groups, p.L);
+  const int64_t layer_pool_bytes = p.pool_pages * p.page_size * p.Hkv * p.D * 2;
+  hipError_t e;
+  const int lpp = static_cast<int>(min(static_cast<int64_t>(p.L),
+                                      static_cast<int64_t>(logit_bytes) / layer_scratch_bytes(p)));
+  if (lpp < 1) return hipErrorInvalidValue;           // the caller checks the scratch holds one layer
+  for (int l0 = 0; l0 < p.L; l0 += lpp) {
+    // layers [l0, l0 + Lg) as a call of Lg layers on offset pointers
+    MemoryParams q = p;
+    q.L = min(lpp, p.L - l0);
+    const float* Mq = M + static_cast<int64_t>(l0) * p.Hq * p.D;
+    const void* poolq = static_cast<const uint8_t*>(pool) + l0 * layer_pool_bytes;
+    float2* part = part_all + static_cast<int64_t>(l0) * p.Hq * n_groups;
+    float* lse = lse_all + static_cast<int64_t>(l0) * p.Hq;
+    if (dt == KVSEL_BF16 && p.D == 128 && p.page_size == 16 && p.Hq <= 32 && (G == 4 || G == 8 || G == 16)) {
+      dim3 grid(n_groups, q.L);
 #define KVSEL_MLM(NCB)                                                                     \
   do {                                                                                     \
-    if (G == 4) memory_logits_mfma_kernel<NCB, 4><<<grid, 256, 0, st>>>(p, M, pool, logits, part); \
-    else if (G == 8) memory_logits_mfma_kernel<NCB, 2><<<grid, 256, 0, st>>>(p, M, pool, logits, part); \
-    else memory_logits_mfma_kernel<NCB, 1><<<grid, 256, 0, st>>>(p, M, pool, logits, part); \
+    if (G == 4) memory_logits_mfma_kernel<NCB, 4><<<grid, 256, 0, st>>>(q, Mq, poolq, logits, part); \
+    else if (G == 8) memory_logits_mfma_kernel<NCB, 2><<<grid, 256, 0, st>>>(q, Mq, poolq, logits, part); \
+    else memory_logits_mfma_kernel<NCB, 1><<<grid, 256, 0, st>>>(q, Mq, poolq, logits, part); \
   } while (0)
-    if (p.Hq <= 16) KVSEL_MLM(1);
-    else KVSEL_MLM(2);
+      if (p.Hq <= 16) KVSEL_MLM(1);
+      else KVSEL_MLM(2);
 #undef KVSEL_MLM
-    e = hipGetLastError();
-  } else if (dt == KVSEL_BF16) {
-    e = (p.D == 64) ? launch_logits_t<KVSEL_BF16, 64>(p, n_groups, M, pool, logits, part, st)
-                    : launch_logits_t<KVSEL_BF16, 128>(p, n_groups, M, pool, logits, part, st);
-  } else {
-    e = (p.D == 64) ? launch_logits_t<KVSEL_F16, 64>(p, n_groups, M, pool, logits, part, st)
-                    : launch_logits_t<KVSEL_F16, 128>(p, n_groups, M, pool, logits, part, st);
+      e = hipGetLastError();
+    } else if (dt == KVSEL_BF16) {
+      e = (p.D == 64) ? launch_logits_t<KVSEL_BF16, 64>(q, n_groups, Mq, poolq, logits, part, st)
+                      : launch_logits_t<KVSEL_BF16, 128>(q, n_groups, Mq, poolq, logits, part, st);
+    } else {
+      e = (p.D == 64) ? launch_logits_t<KVSEL_F16, 64>(q, n_groups, Mq, poolq, logits, part, st)
+                      : launch_logits_t<KVSEL_F16, 128>(q, n_groups, Mq, poolq, logits, part, st);
+    }
+    if (e != hipSuccess) return e;
+    memory_lse_kernel<<<static_cast<int>(ceil_div(q.L * q.Hq, 4)), 256, 0, st>>>(q, n_groups, part, lse);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
+    dim3 grid(static_cast<unsigned>(ceil_div(p.N, 1024)), q.L);
+    float* dst = (p.reduce == KVSEL_REDUCE_GLOBAL) ? layer + static_cast<int64_t>(l0) * p.N
+                                                   : out + static_cast<int64_t>(l0) * p.Hkv * p.N;
+    memory_rule_kernel<<<grid, 256, 0, st>>>(q, logits, lse, dst);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (e != hipSuccess) return e;
-  memory_lse_kernel<<<static_cast<int>(ceil_div(p.L * p.Hq, 4)), 256, 0, st>>>(p, n_groups, part, lse);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
-  dim3 grid(static_cast<unsigned>(ceil_div(p.N, 1024)), p.L);
-  float* dst = (p.reduce == KVSEL_REDUCE_GLOBAL) ? layer : out;
-  memory_rule_kernel<<<grid, 256, 0, st>>>(p, logits, lse, dst);
-  if ((e = hipGetLastError()) != hipSuccess) return e;
   if (p.reduce == KVSEL_REDUCE_GLOBAL) {
     memory_layer_sum_kernel<<<static_cast<int>(ceil_div(p.N, 256)), 256, 0, st>>>(p.L, p.N, layer, out);
     e = hipGetLastError();

@@ -69,9 +69,13 @@ def _stream(stream):
 
 
 def _workspace(nbytes, device, workspace):
+    """The caller's workspace as it is (the library checks its size: a
+    memory-mode score runs in more passes on a shorter one, other calls
+    report KVSEL_E_WORKSPACE), or a new one of the size the query returned."""
     if nbytes == 0:
         return None, 0
-    if workspace is not None and workspace.numel() >= nbytes:
+    if workspace is not None:
+        _want(workspace, "workspace", torch.uint8)
         return workspace, workspace.numel()
     w = torch.empty(nbytes, dtype=torch.uint8, device=device)
     return w, nbytes

@@ -75,6 +75,20 @@ def test_memory_scores_match_oracle(reduce, Hq, Hkv, D, ps, dtype):
     assert_scores_close(f64(out).reshape(-1, N), want.reshape(-1, N))
     if reduce == "global":
         assert abs(float(out.sum()) - L * Hq) < 1e-3 * L * Hq
+    # a workspace one layer of logit scratch short: two passes, the same bits
+    full = kv.score_memory(torch.from_numpy(m32).to(dev), k_pool, perm, N, out, page_size=ps, slot_map=sm,
+                           dead_slot=dead, n_sink=4, n_recent=9, reduce=reduce)
+    layer = (Hq * N * 4 + 255) // 256 * 256
+    out2 = torch.full_like(out, -1.0)
+    kv.score_memory(torch.from_numpy(m32).to(dev), k_pool, perm, N, out2, page_size=ps, slot_map=sm,
+                    dead_slot=dead, n_sink=4, n_recent=9, reduce=reduce, workspace=full[: full.numel() - layer])
+    torch.cuda.synchronize()
+    assert torch.equal(out2, out)
+    with pytest.raises(kv.KvselError) as e:
+        kv.score_memory(torch.from_numpy(m32).to(dev), k_pool, perm, N, out2, page_size=ps, slot_map=sm,
+                        dead_slot=dead, n_sink=4, n_recent=9, reduce=reduce,
+                        workspace=full[: full.numel() - 2 * layer + 256])
+    assert e.value.status == 4
 
 
 def test_redirect_and_sentinel():
