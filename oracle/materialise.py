@@ -45,13 +45,17 @@ def gather_view(src_k, src_v, idx, bt, rope="none", theta=1e6, pos0=0,
 
 def incremental_view(prev_idx, prev_page, new_idx, pool_k, pool_v, raw_k, raw_v,
                      bt, theta=1e6, pos0=0, style="half", rotary_dim=None,
-                     out_round=round_to_bf16):
+                     out_round=round_to_bf16, hits="delta"):
     """Update a paged execution view in place from one selection to the next.
 
     KVMem (tiered movement): pages that overlap across consecutive steps stay
     on the GPU, and missed blocks are scattered in with re-RoPE.  Reading:
-    a hit keeps its physical page and V; its K is rotated by
-    (i_new - i_old) * bt when its logical position moved.  The pages of
+    a hit keeps its physical page and V; when its logical position moved its
+    K becomes the block's K at the new position, either by rotating the
+    page's K in place by (i_new - i_old) * bt (``hits="delta"``: the
+    rotation composes, and only the GPU copy is needed) or by rotating the
+    block's raw K to pos0 + i_new*bt + o (``hits="raw"``: raw K rotated once,
+    so repeated moves do not accumulate bf16 roundings).  The pages of
     blocks that left the view are freed and taken in ascending page order by
     the misses in ascending block order; a miss's K is raw K rotated to
     pos0 + i_new*bt + o and its V is copied.  The new page table lists the
@@ -61,6 +65,8 @@ def incremental_view(prev_idx, prev_page, new_idx, pool_k, pool_v, raw_k, raw_v,
     prev_idx[i]; pool_k/pool_v: [P][bt][D]; raw_k/raw_v: [NB][bt][D].
     Returns (pool_k', pool_v', page_table [k], n_miss).
     """
+    if hits not in ("delta", "raw"):
+        raise ValueError(hits)
     prev_idx = np.asarray(prev_idx, dtype=np.int64)
     prev_page = np.asarray(prev_page, dtype=np.int64)
     new_idx = np.asarray(new_idx, dtype=np.int64)
@@ -80,8 +86,11 @@ def incremental_view(prev_idx, prev_page, new_idx, pool_k, pool_v, raw_k, raw_v,
             i_old = where_prev[b]
             page = int(prev_page[i_old])
             delta = (i_new - i_old) * bt
-            if delta != 0:
+            if delta != 0 and hits == "delta":
                 pk[page] = out_round(rope_rotate(pk[page], np.full(bt, delta), theta,
+                                                 style, rotary_dim))
+            elif delta != 0:
+                pk[page] = out_round(rope_rotate(raw_k[b], pos0 + i_new * bt + o, theta,
                                                  style, rotary_dim))
         else:
             page = freed[n_miss]

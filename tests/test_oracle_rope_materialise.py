@@ -152,6 +152,68 @@ def test_incremental_equals_fresh_build(seed):
     np.testing.assert_array_equal(pk[other], pool_k[other])
 
 
+@pytest.mark.parametrize("seed", [44, 45])
+def test_incremental_raw_hits_equal_a_fresh_build_bit_for_bit(seed):
+    # moved hits re-rotated from raw K: the whole view is the fresh raw gather
+    raw_k, raw_v, new_idx, prev_idx, prev_page, pool_k, pool_v = _incremental_case(seed)
+    bt, D = raw_k.shape[1], raw_k.shape[2]
+    pk, pv, pt, n_miss = om.incremental_view(prev_idx, prev_page, new_idx, pool_k, pool_v,
+                                             raw_k, raw_v, bt, theta=1e6, hits="raw")
+    fk, fv = om.gather_view(raw_k.reshape(-1, D), raw_v.reshape(-1, D), new_idx, bt, rope="raw")
+    np.testing.assert_array_equal(pk[pt].reshape(-1, D), fk)
+    np.testing.assert_array_equal(pv[pt].reshape(-1, D), fv)
+    pk_d, _, pt_d, n_d = om.incremental_view(prev_idx, prev_page, new_idx, pool_k, pool_v,
+                                             raw_k, raw_v, bt, theta=1e6)
+    np.testing.assert_array_equal(pt_d, pt)
+    assert n_d == n_miss
+    with pytest.raises(ValueError):
+        om.incremental_view(prev_idx, prev_page, new_idx, pool_k, pool_v, raw_k, raw_v, bt, hits="both")
+
+
+def test_incremental_delta_hits_drift_over_steps_raw_hits_do_not():
+    """The drift of in-place delta rotation, step after step, against raw K
+    rotated once at the block's current position (D 128, 32-token blocks,
+    theta 1e6, a block that moves at every step).  One delta step carries
+    one extra bf16 rounding (relative row error about 2^-9 per rounding);
+    the errors of successive steps add up, while re-rotating from raw K
+    keeps every step at one rounding of the exact rotation."""
+    r = np.random.default_rng(46)
+    bt, D, nb, k = 32, 128, 64, 16
+    raw_k = numerics.round_to_bf16(r.standard_normal((nb, bt, D)))
+    raw_v = numerics.round_to_bf16(r.standard_normal((nb, bt, D)))
+    o = np.arange(bt)
+    target = 40                                    # stays selected; other blocks come and go before it
+    sel = np.sort(np.concatenate([[target], r.choice(np.setdiff1d(np.arange(nb), [target]), k - 1, replace=False)]))
+    page = np.arange(k)
+    state = {}
+    for hits in ("delta", "raw"):
+        pool_k = np.zeros((k, bt, D))
+        pool_v = np.zeros((k, bt, D))
+        for i, b in enumerate(sel):
+            pool_k[i] = numerics.round_to_bf16(rope_rotate(raw_k[b], i * bt + o, 1e6))
+            pool_v[i] = raw_v[b]
+        prev, prev_page, errs = sel, page, []
+        rs = np.random.default_rng(47)
+        for step in range(8):
+            below = np.arange(target)
+            lo = rs.choice(below, rs.integers(3, 12), replace=False)     # how many blocks precede the target
+            hi = np.setdiff1d(np.arange(target + 1, nb), [])
+            rest = rs.choice(hi, k - 1 - len(lo), replace=False)
+            new = np.sort(np.concatenate([lo, [target], rest]))
+            pool_k, pool_v, pt, _ = om.incremental_view(prev, prev_page, new, pool_k, pool_v, raw_k, raw_v, bt,
+                                                        theta=1e6, hits=hits)
+            i_t = int(np.searchsorted(new, target))
+            exact = rope_rotate(raw_k[target], i_t * bt + o, 1e6)
+            got = pool_k[pt[i_t]]
+            errs.append(float(np.linalg.norm(got - exact) / np.linalg.norm(exact)))
+            prev, prev_page = new, pt
+        state[hits] = errs
+    one = 2.0 ** -9 * np.sqrt(1.0)                 # a single bf16 rounding's relative row error is about this
+    assert max(state["raw"]) < 1.6 * one           # every step: one rounding of the exact rotation
+    assert state["delta"][-1] > 1.5 * max(state["raw"])   # eight moves: several roundings accumulated
+    assert state["delta"][-1] > state["delta"][0]
+
+
 def test_incremental_unmoved_hit_is_bitwise():
     raw_k, raw_v, new_idx, prev_idx, prev_page, pool_k, pool_v = _incremental_case(43, overlap=12)
     pk, pv, pt, n_miss = om.incremental_view(prev_idx, prev_page, new_idx, pool_k, pool_v,
