@@ -6,8 +6,8 @@ x 312500 32-token blocks (fp16, D 128) scored in 65536-block tiles for 4
 sessions with independent 512-token queries, a running top-4096 per
 (session, layer, KV head) with block 0 and the last 4 blocks forced, and the
 in-place incremental update of each session's 4096-page view (about half the
-blocks reused; misses re-RoPEd from the raw store, moved hits rotated in
-place).  One step is all of that over one batch of seeded synthetic inputs
+blocks reused in their pages, moved ones rotated in place; misses re-RoPEd
+from the HBM-resident raw store).  One step is all of that over one batch of seeded synthetic inputs
 resident in HBM before timing starts.
 
 Prints one JSON line.  Per-stage times come from HIP events recorded on the

@@ -274,8 +274,12 @@ kvsel_status kvsel_select_noalloc(const kvsel_select_args* args, void* stream);
  * INCREMENTAL (reuse of overlapping pages across steps): per unit the
  *   previous view holds blocks prev_idx[u][:k] (ascending) in pages
  *   prev_page[u][:k] of a pool [U][pool_pages][bt][D] (pool_k/pool_v, in/out).
- *   A block in both views keeps its page and V; its K is rotated in place
- *   by (i_new - i_old)*bt when its position moved.  Pages of blocks that left
+ *   A block in both views keeps its page and V; when its position moved its
+ *   K is rotated in place by (i_new - i_old)*bt (hit_raw = 0: the GPU copy
+ *   alone suffices, but each move adds one bf16 rounding to that block's K),
+ *   or, with hit_raw = 1, replaced by its raw K from src_k rotated to
+ *   pos0 + i_new*bt + o (one rounding, whatever the number of moves; needs
+ *   src_k, read by block id like a miss).  Pages of blocks that left
  *   the view are taken in ascending page order by the new blocks in
  *   ascending block order; those get K = R(pos0 + i_new*bt + o) raw K and
  *   V copied, both read from src (as in FRESH), or, when staged_k is given,
@@ -290,8 +294,9 @@ kvsel_status kvsel_select_noalloc(const kvsel_select_args* args, void* stream);
  *   the plan that pairs every new entry with its previous position or its
  *   miss rank, written by one launch and read by the next); FRESH needs none.
  *   The call takes a workspace so that it allocates nothing itself.
- * ABI: staged_k, staged_v and staged_cap were appended to the struct; a
- *   caller whose struct_size ends before them gets the raw-source form.
+ * ABI: staged_k, staged_v, staged_cap and hit_raw were appended to the
+ *   struct; a caller whose struct_size ends before them gets the raw-source
+ *   form with hits rotated in place.
  */
 typedef struct kvsel_gather_args {
   uint32_t struct_size;
@@ -326,6 +331,8 @@ typedef struct kvsel_gather_args {
   const void* staged_k;       /* [U][staged_cap][bt][D] or NULL (misses from src) */
   const void* staged_v;
   int64_t staged_cap;         /* entries per unit in the staging buffers */
+  int32_t hit_raw;            /* INCREMENTAL: 1 = moved hits re-rotated from src_k */
+  int32_t reserved;           /* 0 */
 } kvsel_gather_args;
 
 kvsel_status kvsel_gather_workspace(const kvsel_gather_args* args, size_t* bytes);

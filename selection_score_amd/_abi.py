@@ -61,7 +61,7 @@ class GatherArgs(ctypes.Structure):
         ("rope", c_i32), ("style", c_i32), ("rotary_dim", c_i32), ("theta", c_f64), ("pos0", c_i64),
         ("prev_idx", c_vp), ("prev_page", c_vp), ("pool_k", c_vp), ("pool_v", c_vp),
         ("pool_pages", c_i64), ("page_table", c_vp), ("n_miss", c_vp),
-        ("staged_k", c_vp), ("staged_v", c_vp), ("staged_cap", c_i64),
+        ("staged_k", c_vp), ("staged_v", c_vp), ("staged_cap", c_i64), ("hit_raw", c_i32), ("reserved", c_i32),
     ]
 
 

@@ -453,6 +453,7 @@ struct GatherStaging {
   const void* k = nullptr;
   const void* v = nullptr;
   int64_t cap = 0;
+  int hit_raw = 0;
 };
 
 static GatherStaging gather_staging(const kvsel_gather_args* a) {
@@ -461,6 +462,7 @@ static GatherStaging gather_staging(const kvsel_gather_args* a) {
     g.k = a->staged_k;
     g.v = a->staged_v;
     g.cap = a->staged_cap;
+    g.hit_raw = a->hit_raw;
   }
   return g;
 }
@@ -489,6 +491,10 @@ static kvsel_status validate_gather(const kvsel_gather_args* a, GatherParams* gp
     if (!(a->theta > 0.0)) return fail(KVSEL_E_ARG, "theta must be > 0");
   }
   if (a->idx == nullptr) return fail(KVSEL_E_ARG, "idx is NULL");
+  if (stg.hit_raw != 0 && stg.hit_raw != 1) return fail(KVSEL_E_ARG, "hit_raw must be 0 or 1");
+  const bool hit_raw = a->mode == KVSEL_GATHER_INCREMENTAL && stg.hit_raw == 1;
+  if (hit_raw && (a->src_k == nullptr || !aligned16(a->src_k)))
+    return fail(KVSEL_E_ARG, "hit_raw needs src_k (16-byte aligned) to re-rotate moved hits from");
   if (staged) {
     if (stg.v == nullptr) return fail(KVSEL_E_ARG, "staged_v is NULL");
     if (!aligned16(stg.k) || !aligned16(stg.v)) return fail(KVSEL_E_ARG, "staging buffers must be 16-byte aligned");
@@ -517,6 +523,8 @@ static kvsel_status validate_gather(const kvsel_gather_args* a, GatherParams* gp
   gp->style = a->style; gp->rotary_dim = rd; gp->src_unit_stride = a->src_unit_stride;
   gp->src_rows = a->src_rows; gp->pos0 = a->pos0; gp->pool_pages = a->pool_pages; gp->src_offsets = a->src_offsets;
   gp->staged_cap = staged ? stg.cap : -1;
+  gp->hit_raw = hit_raw ? 1 : 0;
+  gp->hit_src = hit_raw ? a->src_k : nullptr;
   for (int m = 0; m < 128; ++m) rt->inv_freq[m] = (m < rd / 2) ? pow(a->theta, -2.0 * m / rd) : 0.0;
   return KVSEL_OK;
 }

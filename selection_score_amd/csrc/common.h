@@ -166,6 +166,8 @@ struct GatherParams {
   int64_t src_unit_stride, src_rows, pos0, pool_pages;
   const int64_t* src_offsets;
   int64_t staged_cap;   // INCREMENTAL: >= 0 when misses come from packed staging (entries per unit)
+  int hit_raw;          // INCREMENTAL: moved hits re-rotated from the raw source hit_src
+  const void* hit_src;  //   (the raw K by block id, with src_offsets / src_unit_stride)
 };
 hipError_t launch_gather_fresh(const GatherParams& p, const RopeTable& rt, const void* src_k,
                                const void* src_v, const int32_t* idx, const int32_t* n_idx,

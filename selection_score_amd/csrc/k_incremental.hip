@@ -197,13 +197,21 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
     uint8_t* pk = static_cast<uint8_t*>(pool_k) + (static_cast<int64_t>(u) * p.pool_pages + page) * item_bytes;
     uint8_t* pv = static_cast<uint8_t*>(pool_v) + (static_cast<int64_t>(u) * p.pool_pages + page) * item_bytes;
     const bool hit = io >= 0;
-    // a hit moves by (i - io) * bt positions (V untouched); a miss is raw K
-    // rotated to its new position, with V copied
-    const int64_t angle_pos = hit ? (i - io) * p.bt : p.pos0 + i * p.bt;
-    if (hit && (angle_pos == 0 || !kRot)) continue;
+    // a hit whose position moved gets its K anew (V untouched): rotated in
+    // place by (i - io) * bt, or, with hit_raw, its raw K from the source
+    // rotated to the new position; a miss is raw K rotated to its new
+    // position, with V copied
+    if (hit && (i == io || !kRot)) continue;
+    const bool from_src = !hit || p.hit_raw;
+    const int64_t angle_pos = from_src ? p.pos0 + i * p.bt : (i - io) * p.bt;
     const uint8_t* sk = nullptr;
     const uint8_t* sv = nullptr;
-    if (!hit && p.staged_cap >= 0) {
+    if (hit && p.hit_raw) {
+      const int32_t b = idx[it];
+      if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
+      const int64_t soff = p.src_offsets ? p.src_offsets[u] : static_cast<int64_t>(u) * p.src_unit_stride;
+      sk = static_cast<const uint8_t*>(p.hit_src) + soff * esz + static_cast<int64_t>(b) * item_bytes;
+    } else if (!hit && p.staged_cap >= 0) {
       // packed staging: the miss of rank r is entry r of the unit's buffers
       const int64_t r = -1 - static_cast<int64_t>(io);
       if (r >= p.staged_cap) continue;
@@ -236,11 +244,11 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
         vv[j] = make_uint4(0, 0, 0, 0);
         if (q0 + j < passes && o < p.bt) {
           const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-          if (hit) {
+          if (!from_src) {
             kv[j] = *reinterpret_cast<const uint4*>(pk + off);
           } else {
             kv[j] = *reinterpret_cast<const uint4*>(sk + off);
-            vv[j] = *reinterpret_cast<const uint4*>(sv + off);
+            if (!hit) vv[j] = *reinterpret_cast<const uint4*>(sv + off);
           }
         }
       }
@@ -262,7 +270,7 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
         if constexpr (kRot) {
           const uint4 other = kInter ? kv[j] : shfl16(kv[j], partner);
           float cs[NP], sn[NP];
-          if (hit) {
+          if (!from_src) {
 #pragma unroll
             for (int e = 0; e < NP; ++e) {
               cs[e] = cb[e];

@@ -271,13 +271,14 @@ def gather_rerope(src_k, src_v, idx, dst_k, dst_v, *, bt, D, src_rows, src_offse
 
 def gather_incremental(src_k, src_v, idx, prev_idx, prev_page, pool_k, pool_v, page_table, n_miss, *,
                        bt, D, src_rows=0, src_offsets=None, src_unit_stride=0, rope="raw", theta=1e6,
-                       pos0=0, style="half", rotary_dim=0, staged_k=None, staged_v=None, workspace=None,
-                       stream=None):
+                       pos0=0, style="half", rotary_dim=0, staged_k=None, staged_v=None, hit_raw=False,
+                       workspace=None, stream=None):
     """kvsel_gather_rerope, INCREMENTAL mode.  pool_k/pool_v
     [U][pool_pages][bt][D] updated in place; page_table [U][k], n_miss [U] out.
     Misses come from src (by block id) or, with staged_k/staged_v
     [U][staged_cap][bt][D], from packed staging (the i-th miss of a unit at
-    entry i); src_k/src_v may then be None."""
+    entry i); src_k/src_v may then be None.  hit_raw re-rotates moved hits
+    from src_k at their new position instead of rotating the page in place."""
     a = _gather_args(src_k, src_v, idx, bt=bt, D=D, src_rows=src_rows, src_offsets=src_offsets,
                      src_unit_stride=src_unit_stride, rope=rope, theta=theta, pos0=pos0, style=style,
                      rotary_dim=rotary_dim, dtype_of=pool_k)
@@ -287,6 +288,7 @@ def gather_incremental(src_k, src_v, idx, prev_idx, prev_page, pool_k, pool_v, p
         _want(staged_k, "staged_k", pool_k.dtype, (a.U, cap, bt, D))
         _want(staged_v, "staged_v", pool_k.dtype, (a.U, cap, bt, D))
         a.staged_k, a.staged_v, a.staged_cap = _ptr(staged_k), _ptr(staged_v), cap
+    a.hit_raw = 1 if hit_raw else 0
     a.prev_idx = _wptr(prev_idx, "prev_idx", torch.int32, numel=a.U * a.k)
     a.prev_page = _wptr(prev_page, "prev_page", torch.int32, numel=a.U * a.k)
     a.pool_k, a.pool_v, a.pool_pages = _ptr(pool_k), _ptr(pool_v), pool_k.shape[1]

@@ -208,6 +208,14 @@ def test_gather_staging_fields_are_optional_for_the_earlier_layout():
     assert call() == _abi.KVSEL_OK
     a.struct_size = _abi.GatherArgs.staged_k.offset - 8
     assert call() == _abi.KVSEL_E_ARG
+    # moved hits re-rotated from raw K need that raw source
+    a.struct_size = ctypes.sizeof(a)
+    a.staged_k, a.staged_v, a.src_k, a.src_v, a.hit_raw = 0xA000, 0xB000, None, None, 1
+    assert call() == _abi.KVSEL_E_ARG and b"hit_raw" in lib.kvsel_last_error()
+    a.src_k = 0x1000
+    assert call() == _abi.KVSEL_OK
+    a.hit_raw = 2
+    assert call() == _abi.KVSEL_E_ARG
 
 
 def test_index_validation_without_device():

@@ -124,7 +124,8 @@ def test_kvmem_1m_workload_full_size():
 def test_kvmem_10m_workload_full_size():
     """312500 blocks per unit scored in 65536-block tiles for 4 sessions,
     tiled top-4096, and the in-place incremental update of each session's
-    4096-page view (previous view shares about half its blocks), in the
+    4096-page view (previous view shares about half its blocks; moved hits
+    rotated in place), in the
     launch sequence the benchmark times.  64 (session, unit) views drawn in
     a seeded order are checked against the oracle: their scores over every
     tile, their kept blocks, and on the bit-exact ones the whole updated view

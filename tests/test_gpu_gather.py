@@ -108,11 +108,15 @@ def test_gather_aliased_sources_and_partial_counts():
         assert np.all(got_k[m * bt:] == 3.0) and np.all(got_v[m * bt:] == 5.0)
 
 
-@pytest.mark.parametrize("overlap,staged", [(0.5, False), (1.0, False), (0.0, False), (0.5, True), (0.0, True)])
-def test_incremental_view_matches_oracle(overlap, staged):
+@pytest.mark.parametrize("overlap,staged,hits", [(0.5, False, "delta"), (1.0, False, "delta"), (0.0, False, "delta"),
+                                                 (0.5, True, "delta"), (0.0, True, "delta"), (0.5, False, "raw"),
+                                                 (1.0, True, "raw")])
+def test_incremental_view_matches_oracle(overlap, staged, hits):
     """The incremental view against the oracle's, with the misses read from
     the raw source by block id or from packed staging buffers (the i-th miss
-    of a unit, in ascending block order, at entry i; no raw source given)."""
+    of a unit, in ascending block order, at entry i; no raw source given
+    unless moved hits are re-rotated from it), and moved hits rotated in
+    place or re-rotated from raw K."""
     dev = require_gpu()
     rng = np.random.default_rng(int(overlap * 10) + 11)
     U, nb, k, D, bt, spare = 4, 2000, 96, 128, 32, 10
@@ -154,19 +158,22 @@ def test_incremental_view_matches_oracle(overlap, staged):
             rows = torch.from_numpy((miss[:, None] * bt + np.arange(bt)).reshape(-1)).to(dev)
             sk[u, :len(miss)] = raw_k[u][rows].view(len(miss), bt, D)
             sv[u, :len(miss)] = raw_v[u][rows].view(len(miss), bt, D)
-        kv.gather_incremental(None, None, torch.from_numpy(new_idx).to(dev), torch.from_numpy(prev_idx).to(dev),
+        src = (raw_k, raw_v) if hits == "raw" else (None, None)
+        kv.gather_incremental(*src, torch.from_numpy(new_idx).to(dev), torch.from_numpy(prev_idx).to(dev),
                               torch.from_numpy(prev_page).to(dev), pk, pv, pt, nm, bt=bt, D=D, rope="raw",
-                              theta=1e6, staged_k=sk, staged_v=sv)
+                              theta=1e6, staged_k=sk, staged_v=sv, hit_raw=hits == "raw", src_rows=nb * bt,
+                              src_unit_stride=nb * bt * D)
     else:
         kv.gather_incremental(raw_k, raw_v, torch.from_numpy(new_idx).to(dev), torch.from_numpy(prev_idx).to(dev),
                               torch.from_numpy(prev_page).to(dev), pk, pv, pt, nm, bt=bt, D=D,
-                              src_rows=nb * bt, src_unit_stride=nb * bt * D, rope="raw", theta=1e6)
+                              src_rows=nb * bt, src_unit_stride=nb * bt * D, rope="raw", theta=1e6,
+                              hit_raw=hits == "raw")
     torch.cuda.synchronize()
     gk, gv, gpt, gnm = f64(pk), f64(pv), pt.cpu().numpy(), nm.cpu().numpy()
     for u in range(U):
         ok, ov, opt, onm = om.incremental_view(prev_idx[u], prev_page[u], new_idx[u], pool_k[u], pool_v[u],
                                                rk[u].reshape(nb, bt, D), rv[u].reshape(nb, bt, D), bt,
-                                               theta=1e6)
+                                               theta=1e6, hits=hits)
         assert gnm[u] == onm
         np.testing.assert_array_equal(gpt[u], opt)
         np.testing.assert_array_equal(gv[u], ov)
