@@ -260,7 +260,7 @@ class Tiny:
     Cache (outside the step's events), and ms_per_step is the mean of the
     steps' own event spans."""
     stages = ["score", "select", "gather"]
-    dominant = ("score", [("scores_valu_kernel", "k_window.hip"), ("lse_valu_kernel", "k_window.hip"),
+    dominant = ("score", [("lse_valu_kernel", "k_window.hip"), ("scores_valu_kernel", "k_window.hip"),
                           ("pool1d_kernel", "k_window.hip")])
     score_stage = "score"
     materialise_stages = ["select", "gather"]
