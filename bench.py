@@ -642,7 +642,10 @@ class KVMem10M:
     65536-block tiles for 4 sessions with a running tiled top-4096, then the
     in-place incremental update of each session's 4096-page view (the
     previous view shares about half its blocks with the new selection).
-    The previous-view lists are inputs, so every step does the same work."""
+    Tiles after the first are scored in the packed form: only the blocks
+    above their running set's smallest score are written (the selection's
+    admission threshold), with a bit mask.  The previous-view lists are
+    inputs, so every step does the same work."""
     stages = ["tiles", "update"]
     dominant = ("update", [("incremental_data_kernel", "k_incremental.hip"),
                            ("incremental_plan_kernel", "k_incremental.hip")])
@@ -665,6 +668,9 @@ class KVMem10M:
         self.cc = torch.zeros(SU, dtype=torch.int32, device=dev)
         self.kept = torch.empty((SU, k), dtype=torch.int32, device=dev)
         self.tile_out = torch.empty((S, U, tile), dtype=torch.float32, device=dev)
+        self.mask = torch.empty((SU * ((tile + 63) // 64),), dtype=torch.int64, device=dev)
+        self.admit = torch.empty((SU,), dtype=torch.float32, device=dev)
+        self.admitted = None
         self.raw_k = torch.empty((cfg.Hkv, NB, bt, D), dtype=torch.bfloat16, device=dev)
         self.raw_v = torch.empty_like(self.raw_k)
         gen = torch.Generator(device=dev).manual_seed(cfg.seed + 77)
@@ -700,21 +706,37 @@ class KVMem10M:
         self.sel_ws = None
         self.inc_ws = None
 
-    def step(self, ev, stream, it):
+    def _tiles(self, count=False):
+        """The tile loop; with count, the admitted columns of every packed
+        tile (an untimed pass for the algorithmic bytes)."""
+        import numpy as np
         kv, cfg = self.kv, self.cfg
         S, U, NB, k, tile = cfg.S, cfg.U, cfg.N, cfg.k, cfg.tile
         SU = S * U
-        ev[0].record(stream)
+        admitted = []
         self.cc.zero_()
         for b in range(0, NB, tile):
             n = min(tile, NB - b)
             out = self.tile_out.view(-1)[: SU * n]
+            packed = b > 0
+            mask = self.mask[: SU * ((n + 63) // 64)] if packed else None
             self.ws = kv.score_block(self.qs if b == 0 else None, self.mu, out.view(S, U, n), n_kv_heads=cfg.Hkv,
-                                     n_begin=b, n_count=n, qbar=self.qbar, qbar_valid=b > 0, workspace=self.ws)
+                                     n_begin=b, n_count=n, qbar=self.qbar, qbar_valid=b > 0,
+                                     admit=self.admit.view(S, U) if packed else None, tile_mask=mask,
+                                     workspace=self.ws)
             self.sel_ws = kv.select(out.view(SU, n), self.kept, k_total=k, n_sink=cfg.n_sink,
                                     n_recent=cfg.n_recent, n_total=NB, base=b, cand_score=self.cs,
                                     cand_idx=self.ci, cand_count=self.cc, finalize=b + n == NB,
-                                    workspace=self.sel_ws)
+                                    tile_mask=None if mask is None else mask.view(SU, -1),
+                                    admit=self.admit if b + n < NB else None, workspace=self.sel_ws)
+            if count and packed:
+                admitted.append(int(np.unpackbits(mask.cpu().numpy().view(np.uint8)).sum()))
+        return admitted
+
+    def step(self, ev, stream, it):
+        kv, cfg, NB = self.kv, self.cfg, self.cfg.N
+        ev[0].record(stream)
+        self._tiles()
         ev[1].record(stream)
         self.inc_ws = kv.gather_incremental(self.raw_k, self.raw_v, self.kept, self.prev_idx, self.prev_page,
                                             self.pool_k, self.pool_v, self.pt, self.nm, bt=cfg.bt, D=cfg.D,
@@ -737,8 +759,17 @@ class KVMem10M:
         S, U, NB, k, D, bt, tile = cfg.S, cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt, cfg.tile
         SU = S * U
         misses, moved = self._moves()
+        if self.admitted is None:
+            self.admitted = self._tiles(count=True)
+        n_tiles = (NB + tile - 1) // tile
         blk = bt * D * 2
-        return {"tiles": U * NB * D * 2 + S * cfg.L * cfg.Hq * cfg.W * D * 2 + 2 * SU * NB * 4,
+        # index once, queries once; the first tile's scores written and read;
+        # later tiles: admitted scores written and read, mask words written
+        # and read; the running candidates (score + index) read and written
+        # by every select call
+        scores = 2 * SU * min(tile, NB) * 4 + 2 * sum(self.admitted) * 4 + 2 * SU * ((NB - tile + 63) // 64) * 8
+        cands = n_tiles * 2 * SU * k * 8
+        return {"tiles": U * NB * D * 2 + S * cfg.L * cfg.Hq * cfg.W * D * 2 + scores + cands,
                 "update": misses * 2 * 2 * blk + moved * 2 * blk + 3 * SU * k * 4}
 
     def cpu_baseline(self, seconds):
@@ -792,7 +823,8 @@ class KVMem10M:
 
     def extra(self):
         misses, moved = self._moves()
-        return {"update_misses": misses, "update_moved_hits": moved}
+        return {"update_misses": misses, "update_moved_hits": moved,
+                "admitted_per_packed_tile": self.admitted}
 
 
 class MeanK1M:

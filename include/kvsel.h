@@ -119,6 +119,18 @@ const char* kvsel_last_error(void);
  *   `qbar` ([S][L][Hkv][D] F32, or the workspace when NULL); with
  *   `qbar_valid` = 1 the call reads `qbar` instead and `q` may be NULL.
  *   Output `scores`: [S][L*Hkv][n_count] F32.
+ *   Packed output (D = 128; `admit` and `tile_mask` both given, or both
+ *   NULL for the dense output above): for tiled selection, where only
+ *   columns above the running set's smallest score can still be selected.
+ *   admit: [S][L*Hkv] F32, the thresholds a tiled kvsel_select call wrote
+ *   (NaN admits every column).  Column b of a row is admitted when its
+ *   score is greater than the row's threshold (-0.0 equals +0.0).  Each
+ *   row is cut into chunks of 256 columns: chunk c stores the scores of its
+ *   admitted columns, in ascending column order, at row positions
+ *   [256 c, 256 c + admitted); the other positions are left unwritten.
+ *   tile_mask: [S][L*Hkv][ceil(n_count / 64)] uint64, bit i of word w set
+ *   when column 64 w + i is admitted.  kvsel_select reads this form when
+ *   given the same tile_mask.
  *
  * Limits: L * Hkv <= 65535 (E_UNSUPPORTED beyond).
  * scale = 0 means 1/sqrt(D).  Pooling (window/memory-per-unit): centred,
@@ -156,6 +168,9 @@ typedef struct kvsel_score_args {
   int32_t pool, pool_k; /* kvsel_pool, odd kernel size */
   float scale;
   float* scores;        /* output, F32 */
+  /* block mode, packed output (struct_size ending before admit: dense) */
+  const float* admit;   /* [S][L*Hkv] F32 thresholds, or NULL */
+  uint64_t* tile_mask;  /* [S][L*Hkv][ceil(n_count / 64)] admission masks, or NULL */
 } kvsel_score_args;
 
 /* Bytes of device workspace kvsel_score needs for `args` (may be 0).
@@ -191,6 +206,15 @@ kvsel_status kvsel_score(const kvsel_score_args* args, void* workspace,
  * candidate buffers cand_score/cand_idx ([U][k_total] each) and cand_count
  * ([U], zeroed by the caller before the first tile); the last tile sets
  * `finalize` = 1.  The tiled result equals the untiled one.
+ * Admission (tiled calls): a call that does not finalize writes, with
+ * `admit` given ([U] F32), the score no later column can tie or beat and
+ * still enter: the running set's smallest score once it holds every slot
+ * left beside the forced set, NaN before.  Scored with that threshold
+ * (kvsel_score block mode, packed output), the next tile is passed as its
+ * packed scores plus `tile_mask` ([U][ceil(n / 64)] uint64, the same
+ * layout); the result equals the dense tile's.  Thresholds that are not
+ * above the previous call's `admit` (NaN included) keep that equality;
+ * higher ones may drop columns that belong to the result.
  * Outputs (written when finalize = 1, or on an untiled call): kept_idx
  * [U][k_total] int32 ascending, -1 past n_kept; n_kept [U] (nullable);
  * keep_mask [U][n_total] u8 (nullable; untiled calls only).
@@ -206,7 +230,9 @@ kvsel_status kvsel_score(const kvsel_score_args* args, void* workspace,
  * whose per-unit workgroups keep their keys in registers.
  * Errors: KVSEL_E_BUDGET if n_sink + n_recent > k_total and k_total < n_total;
  * KVSEL_E_WORKSPACE if the workspace is missing or too small; KVSEL_E_UNSUPPORTED
- * for U > 65535.
+ * for U > 65535, and for `tile_mask` or `admit` on a tiled call that needs
+ * the workspace (k_total above 8192, or tiles too wide for one workgroup's
+ * LDS); KVSEL_E_ARG for `tile_mask` or `admit` on an untiled call.
  */
 typedef struct kvsel_select_args {
   uint32_t struct_size;
@@ -227,6 +253,9 @@ typedef struct kvsel_select_args {
   uint8_t* keep_mask;        /* [U][n_total] or NULL */
   int32_t* n_kept;           /* [U] or NULL */
   int32_t pool, pool_k;      /* kvsel_pool and odd kernel size (untiled calls) */
+  /* tiled calls (struct_size ending before tile_mask: dense tiles, no admission output) */
+  const uint64_t* tile_mask; /* [U][ceil(n / 64)]: the tile is packed; NULL: dense */
+  float* admit;              /* [U] F32, written by calls that do not finalize; or NULL */
 } kvsel_select_args;
 
 kvsel_status kvsel_select_workspace(const kvsel_select_args* args, size_t* bytes);

@@ -37,6 +37,7 @@ class ScoreArgs(ctypes.Structure):
         ("causal", c_i32), ("lse_in", c_vp), ("lse_out", c_vp),
         ("head_agg", c_i32), ("row_agg", c_i32), ("reduce", c_i32),
         ("pool", c_i32), ("pool_k", c_i32), ("scale", c_f32), ("scores", c_vp),
+        ("admit", c_vp), ("tile_mask", c_vp),
     ]
 
 
@@ -49,6 +50,7 @@ class SelectArgs(ctypes.Structure):
         ("cand_score", c_vp), ("cand_idx", c_vp), ("cand_count", c_vp), ("finalize", c_i32),
         ("kept_idx", c_vp), ("keep_mask", c_vp), ("n_kept", c_vp),
         ("pool", c_i32), ("pool_k", c_i32),
+        ("tile_mask", c_vp), ("admit", c_vp),
     ]
 
 

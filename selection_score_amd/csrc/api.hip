@@ -131,12 +131,25 @@ struct ScorePlan {
   bool own_lse = false;
   bool pooled = false;
   bool lse_only = false;
+  const float* admit = nullptr;     // block mode, packed output
+  uint64_t* tile_mask = nullptr;
 };
 
 kvsel_status validate_score(const kvsel_score_args* a, ScorePlan* plan) {
   if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
-  if (a->struct_size < sizeof(kvsel_score_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->struct_size < offsetof(kvsel_score_args, admit)) return fail(KVSEL_E_ARG, "struct_size too small");
   if (a->mode < KVSEL_SCORE_WINDOW || a->mode > KVSEL_SCORE_BLOCK) return fail(KVSEL_E_ARG, "bad mode");
+  if (a->struct_size >= sizeof(kvsel_score_args)) {
+    plan->admit = a->admit;
+    plan->tile_mask = a->tile_mask;
+  }
+  if ((plan->admit == nullptr) != (plan->tile_mask == nullptr))
+    return fail(KVSEL_E_ARG, "give admit and tile_mask together (packed output) or neither");
+  if (plan->admit != nullptr) {
+    if (a->mode != KVSEL_SCORE_BLOCK) return fail(KVSEL_E_ARG, "admit and tile_mask are block-mode options");
+    if (a->D != 128) return fail(KVSEL_E_UNSUPPORTED, "packed block scores need D = 128");
+    if (!aligned16(plan->tile_mask)) return fail(KVSEL_E_ARG, "tile_mask must be 16-byte aligned");
+  }
   if (a->L <= 0 || a->Hq <= 0 || a->Hkv <= 0 || a->Hq % a->Hkv != 0)
     return fail(KVSEL_E_ARG, "need L, Hq, Hkv > 0 and Hkv dividing Hq");
   if (a->D != 64 && a->D != 128) return fail(KVSEL_E_UNSUPPORTED, "D must be 64 or 128");
@@ -289,7 +302,8 @@ kvsel_status kvsel_score(const kvsel_score_args* a, void* ws, size_t ws_bytes, v
       if (e != hipSuccess) return hip_fail(e, "memory scores");
       pool_rows = (a->reduce == KVSEL_REDUCE_GLOBAL) ? 1 : U;
     } else {
-      BlockParams p{a->S, a->L, a->Hq, a->Hkv, a->D, a->W, a->N, a->n_begin, a->n_count, scale};
+      BlockParams p{a->S, a->L, a->Hq, a->Hkv, a->D, a->W, a->N, a->n_begin, a->n_count, scale,
+                    plan.admit, plan.tile_mask};
       float* qbar = a->qbar ? a->qbar : reinterpret_cast<float*>(w + plan.qbar_off);
       if (!a->qbar_valid) {
         e = launch_query_reduce(p, a->q_dtype, a->q, qbar, st);
@@ -297,6 +311,7 @@ kvsel_status kvsel_score(const kvsel_score_args* a, void* ws, size_t ws_bytes, v
       }
       e = launch_block_scores(p, qbar, a->k, a->scores, st);
       if ((s = finish(e, st, "block scores")) != KVSEL_OK) return s;
+      if (plan.admit != nullptr) return KVSEL_OK;   // packed rows hold unwritten positions
       return debug_scores(a->scores, static_cast<int64_t>(a->S) * U, a->n_count, a->n_count, st,
                           "block scores (q or the index not finite?)");
     }
@@ -312,7 +327,7 @@ kvsel_status kvsel_score(const kvsel_score_args* a, void* ws, size_t ws_bytes, v
 
 static kvsel_status validate_select(const kvsel_select_args* a) {
   if (a == nullptr) return fail(KVSEL_E_ARG, "args is NULL");
-  if (a->struct_size < sizeof(kvsel_select_args)) return fail(KVSEL_E_ARG, "struct_size too small");
+  if (a->struct_size < offsetof(kvsel_select_args, tile_mask)) return fail(KVSEL_E_ARG, "struct_size too small");
   if (a->U < 0 || a->n < 0 || a->base < 0 || a->k_total < 0 || a->n_sink < 0 || a->n_recent < 0)
     return fail(KVSEL_E_ARG, "negative size");
   if (a->n_total > kMaxN || a->base + a->n > a->n_total)
@@ -338,6 +353,16 @@ static kvsel_status validate_select(const kvsel_select_args* a) {
   if (a->pool != KVSEL_POOL_NONE && tiled) return fail(KVSEL_E_ARG, "pooling needs an untiled call");
   if (tiled && static_cast<int64_t>(a->k_total) * 8 > 64 * 1024)
     return fail(KVSEL_E_UNSUPPORTED, "tiled selection supports k_total <= 8192");
+  if (a->struct_size >= sizeof(kvsel_select_args) && (a->tile_mask != nullptr || a->admit != nullptr)) {
+    if (!tiled) return fail(KVSEL_E_ARG, "tile_mask and admit need a tiled call");
+    if (!aligned16(a->tile_mask) || !aligned16(a->admit))
+      return fail(KVSEL_E_ARG, "tile_mask and admit must be 16-byte aligned");
+    // both live in the one-launch tile kernel only
+    SelectParams p{};
+    p.U = a->U; p.n = a->n; p.k_total = a->k_total; p.cand_count = a->cand_count;
+    if (!select_tile_fits(p))
+      return fail(KVSEL_E_UNSUPPORTED, "tile_mask and admit need a tile call that fits one workgroup's LDS");
+  }
   return KVSEL_OK;
 }
 
@@ -352,6 +377,10 @@ static SelectParams select_params(const kvsel_select_args* a) {
   p.kept_idx = a->kept_idx; p.keep_mask = a->keep_mask; p.n_kept = a->n_kept;
   p.pool = (a->pool_k > 1) ? a->pool : KVSEL_POOL_NONE;
   p.pool_k = a->pool_k;
+  if (a->struct_size >= sizeof(kvsel_select_args)) {
+    p.tile_mask = a->tile_mask;
+    p.admit = a->admit;
+  }
   return p;
 }
 
@@ -379,7 +408,8 @@ kvsel_status kvsel_select(const kvsel_select_args* a, void* ws, size_t ws_bytes,
     if (need > 0 && !aligned16(ws)) return fail(KVSEL_E_ARG, "workspace must be 16-byte aligned");
     if ((s = check_device()) != KVSEL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (p.U > 0 && p.n > 0 && (s = debug_scores(a->scores, p.U, p.n, p.row_stride, st, "scores")) != KVSEL_OK)
+    if (p.U > 0 && p.n > 0 && p.tile_mask == nullptr &&
+        (s = debug_scores(a->scores, p.U, p.n, p.row_stride, st, "scores")) != KVSEL_OK)
       return s;
     return finish(launch_select(p, a->scores, ws, st), st, "select");
   } catch (...) {
@@ -435,7 +465,8 @@ kvsel_status kvsel_select_noalloc(const kvsel_select_args* a, void* stream) {
     void* ws = nullptr;
     if (need > 0 && (s = noalloc_scratch(&ws)) != KVSEL_OK) return s;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    if (p.U > 0 && p.n > 0 && (s = debug_scores(a->scores, p.U, p.n, p.row_stride, st, "scores")) != KVSEL_OK)
+    if (p.U > 0 && p.n > 0 && p.tile_mask == nullptr &&
+        (s = debug_scores(a->scores, p.U, p.n, p.row_stride, st, "scores")) != KVSEL_OK)
       return s;
     // every word of the scratch a launch reads is written earlier in the
     // same call (keys and per-slice histograms), so nothing is cleared

@@ -124,10 +124,23 @@ size_t memory_logit_bytes(const MemoryParams& p, bool minimum);
 hipError_t launch_memory_scores(const MemoryParams& p, int dt, const float* M, const void* pool,
                                 void* ws, float* logits, size_t logit_bytes, float* out, hipStream_t st);
 
+// Packed tiles: a tile row is cut into chunks of kPackChunk columns; chunk c
+// keeps the scores of its admitted columns, in ascending column order, at
+// row positions [kPackChunk * c, kPackChunk * c + admitted), and admission
+// masks of ceil(n / 64) words per row mark them (bit b of word w is column
+// 64 w + b).
+constexpr int kPackChunk = 256;
+
+// Admission key of a threshold from kvsel_select's `admit` output: a column
+// is admitted when score_key(score) > the key; NaN admits every column.
+__device__ __forceinline__ uint32_t admit_key(float a) { return (a != a) ? 0u : score_key(a); }
+
 struct BlockParams {
   int S, L, Hq, Hkv, D, W;
   int64_t NB, n_begin, n_count;
   float scale;
+  const float* admit;     // [S][U] thresholds: packed output (D 128 only), or NULL: dense
+  uint64_t* mask;         // [S][U][ceil(n_count / 64)] admission masks of the packed output
 };
 hipError_t launch_query_reduce(const BlockParams& p, int dt, const void* q, float* qbar,
                                hipStream_t st);
@@ -148,6 +161,8 @@ struct SelectParams {
   uint8_t* keep_mask;
   int32_t* n_kept;
   int pool, pool_k;
+  const uint64_t* tile_mask;  // tiled: admission masks of a packed tile, or NULL (dense)
+  float* admit;               // tiled, not final: [U] admission threshold for the next tile, or NULL
 };
 // select_workspace_bytes(p): the keys and per-slice top-byte histograms of
 // the two-launch paths (0 for the single-launch path and empty calls).

@@ -127,13 +127,23 @@ typedef _Float16 f16x4 __attribute__((ext_vector_type(4)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
 
 // Each wavefront scores kTilesPerWave consecutive 16-row tiles of one unit
-// (a contiguous 32 KiB run of the index), loading the next tile's A
-// fragments while the current tile's MFMAs run.  The scores of its 128 rows
+// (a contiguous 64 KiB run of the index), loading the next tile's A
+// fragments while the current tile's MFMAs run.  The scores of its 256 rows
 // are staged in the wavefront's own LDS rows (one per session, padded to
-// avoid bank conflicts) and written at the end as whole 512-byte runs per
+// avoid bank conflicts) and written at the end as whole 1 KiB runs per
 // session: the MFMA layout would otherwise scatter them as 64-byte pieces,
 // which costs the HBM write path several times their bytes.
-constexpr int kTilesPerWave = 8;
+//
+// Packed output (a threshold per session and unit given): the wavefront's
+// 256 rows are one chunk of the packed tile format; only the scores whose
+// key is above the threshold are written, packed at the chunk's start in
+// row order, with the chunk's four mask words.  The tiled selection passes
+// the threshold from its running set, so after the first tile the stores
+// shrink to the few columns that can still enter it: score stores
+// interleaved with the index stream cost the read path far more than
+// their bytes.
+constexpr int kTilesPerWave = 16;
+static_assert(kTilesPerWave * 16 == kPackChunk, "one wavefront's rows form one packed chunk");
 constexpr int kStageStride = kTilesPerWave * 16 + 4;    // floats per staged session row
 
 __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, const float* __restrict__ qbar,
@@ -177,6 +187,9 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
         bl[t][h][j] = static_cast<_Float16>(x - static_cast<float>(hi));
       }
   const uint16_t* mu_u = mu + (static_cast<int64_t>(u) * p.NB + p.n_begin) * 128;
+  // packed output: lane s holds session s's admission key, loaded up front
+  uint32_t thr_lane = 0u;
+  if (p.admit != nullptr && lane < p.S) thr_lane = admit_key(p.admit[static_cast<int64_t>(lane) * U + u]);
   extern __shared__ float stage_all[];
   float* stage = stage_all + (threadIdx.x >> 6) * p.S * kStageStride;
   auto load = [&](int64_t tile, uint4* a) {
@@ -216,6 +229,46 @@ __global__ __launch_bounds__(256) void block_scores_mfma_kernel(BlockParams p, c
   __builtin_amdgcn_wave_barrier();
   const int64_t row0 = t_begin * 16;
   const int rows = static_cast<int>(min(p.n_count, t_end * 16) - row0);
+  if (p.admit != nullptr) {
+    // chunk row0 / kPackChunk of every session's row: the admitted scores
+    // are compacted within the wavefront's LDS row (in row order, behind
+    // the read position), then written as one run, and the chunk's four
+    // mask words as one 32-byte store (rows past the tile: none admitted)
+    const int64_t n_words = (p.n_count + 63) / 64;
+    const uint64_t lt = (lane == 0) ? 0ull : ((~0ull) >> (64 - lane));
+    for (int sess = 0; sess < p.S; ++sess) {
+      const int64_t orow = static_cast<int64_t>(sess) * U + u;
+      const uint32_t thr = static_cast<uint32_t>(__shfl(static_cast<int>(thr_lane), sess, 64));
+      float* srow = stage + sess * kStageStride;
+      uint64_t mw[kPackChunk / 64];
+      uint32_t before = 0;
+#pragma unroll
+      for (int j = 0; j < kPackChunk / 64; ++j) {
+        const int r = 64 * j + lane;
+        const float v = (r < rows) ? srow[r] : 0.f;
+        const bool adm = r < rows && score_key(v) > thr;
+        const uint64_t m = __ballot(adm);
+        // every lane has read its element of this word before any lane
+        // writes: the writes land at or below row 64 j + lane
+        __builtin_amdgcn_wave_barrier();
+        if (adm) srow[before + __popcll(m & lt)] = v;
+        mw[j] = m;
+        before += static_cast<uint32_t>(__popcll(m));
+      }
+      __builtin_amdgcn_wave_barrier();
+      float* o = out + orow * p.n_count + row0;
+      for (uint32_t i = lane; i < before; i += 64) o[i] = srow[i];
+      const int n_w = (rows + 63) / 64;
+      if (lane < n_w) {
+        uint64_t m = mw[0];
+#pragma unroll
+        for (int j = 1; j < kPackChunk / 64; ++j)
+          if (lane == j) m = mw[j];
+        p.mask[orow * n_words + row0 / 64 + lane] = m;
+      }
+    }
+    return;
+  }
   for (int c = lane; c < p.S * (kTilesPerWave * 4); c += 64) {
     const int sess = c / (kTilesPerWave * 4), j = 4 * (c % (kTilesPerWave * 4));
     if (j >= rows) continue;

@@ -19,6 +19,13 @@
 // second digit's bin); if even that does not fit, the remaining digits and
 // the placement read the tile from global memory each time.
 //
+// A packed tile (the block scorer's output when given the running set's
+// threshold) holds only the columns admitted above it: the same passes run
+// over the admitted columns, read through the chunk masks.  A call that
+// does not finalize can write that threshold for the next tile: the
+// smallest score of the running set once it holds `room` entries, NaN
+// (admit everything) before.
+//
 // Placement keeps ascending order without a sort: selected candidates come
 // first (all their indices precede the tile), in array order by a block
 // scan; selected tile columns are marked in a bitmap over the tile and
@@ -119,6 +126,7 @@ __device__ void find_bin_block(TileShared& sh, int nbins, uint32_t rem) {
 
 struct Tile {
   const float* row;
+  const uint64_t* mask;                  // packed tile: the row's admission masks; NULL: dense
   int n;                                 // columns of the tile; all positions are < 2^31
   int base, sink_end, rec_begin;
   const int32_t* slot_map;
@@ -136,11 +144,48 @@ __device__ __forceinline__ uint32_t tile_key(const Tile& t, int j, float s) {
 
 // Calls f(j, key) for every tile column, key = 0 unless the column is a
 // candidate with key >= lo (lo >= 1), reading the row from global memory.
-// Every thread runs the same number of iterations (f may use wave-wide
-// operations); columns past the tile come with key 0.
-template <typename F>
+// All lanes of a wavefront run the same number of iterations (f may use
+// wave-wide operations); columns past the tile come with key 0.  A packed
+// tile is visited one mask word per lane, over the word's set bits: an
+// admitted column's score sits at the rank of its bit among the chunk's
+// set bits.  Only admitted columns are visited; idle lanes call f with
+// column -1 and key 0.
+template <bool kPacked, typename F>
 __device__ __forceinline__ void for_tile(const Tile& t, uint32_t lo, F&& f) {
   const int tid = threadIdx.x;
+  if constexpr (kPacked) {
+    // one lane per mask word (64 columns); the four lanes of a chunk's
+    // words sit side by side, so a lane's first packed position is the
+    // chunk start plus the popcounts of the lanes before it in its chunk
+    const int lane = tid & 63;
+    const int n_words = (t.n + 63) / 64;
+    for (int wb = 0; wb < n_words; wb += kT) {
+      const int w = wb + tid;
+      uint64_t m = 0ull;
+      if (w < n_words) {
+        m = t.mask[w];
+        const int rest = t.n - 64 * w;                  // bits past the tile are ignored
+        if (rest < 64) m &= (1ull << rest) - 1ull;
+      }
+      const uint32_t pc = static_cast<uint32_t>(__popcll(m));
+      const int q = lane & 3;                           // word within the chunk (kPackChunk = 4 words)
+      const uint32_t p1 = __shfl_up(pc, 1, 64), p2 = __shfl_up(pc, 2, 64), p3 = __shfl_up(pc, 3, 64);
+      int at = (w / 4) * kPackChunk + static_cast<int>((q >= 1 ? p1 : 0u) + (q >= 2 ? p2 : 0u) + (q >= 3 ? p3 : 0u));
+      while (__ballot(m != 0ull) != 0ull) {             // uniform over the wavefront
+        int col = -1;
+        uint32_t key = 0u;
+        if (m != 0ull) {
+          const int b = __ffsll(static_cast<unsigned long long>(m)) - 1;
+          m &= m - 1ull;
+          col = 64 * w + b;
+          key = tile_key(t, col, t.row[at]);
+          ++at;
+        }
+        f(col, key >= lo ? key : 0u);
+      }
+    }
+    return;
+  }
   if (t.vec) {
     const float4* r4 = reinterpret_cast<const float4*>(t.row);
     const int n4 = t.n / 4;
@@ -175,7 +220,9 @@ __device__ __forceinline__ void for_tile(const Tile& t, uint32_t lo, F&& f) {
 
 }  // namespace
 
-// dyn LDS: ckey[k_total] | skey[cap] | scol[cap] | bits[nw]
+// dyn LDS: ckey[k_total] | skey[cap] | scol[cap] | bits[nw].  kPacked: the
+// tile is in the packed form (p.tile_mask).
+template <bool kPacked>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void select_tile_kernel(
     SelectParams p, const float* scores, int cap) {
   extern __shared__ uint32_t dyn[];
@@ -191,6 +238,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
 
   Tile t;
   t.row = scores + static_cast<int64_t>(u) * p.row_stride;
+  t.mask = p.tile_mask ? p.tile_mask + static_cast<int64_t>(u) * ((p.n + 63) / 64) : nullptr;
   t.n = static_cast<int>(p.n);
   t.base = static_cast<int>(p.base);
   t.sink_end = static_cast<int>(min(static_cast<int64_t>(p.n_sink), p.n_total));
@@ -242,7 +290,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     }
   };
   if (room > 0) {
-    for_tile(t, lo, [&](int j, uint32_t key) {
+    for_tile<kPacked>(t, lo, [&](int j, uint32_t key) {
       if (key != 0u) atomicAdd(&sh.hist[key >> 20], 1u);
       append(j, key);
     });
@@ -251,6 +299,14 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
   uint32_t n_tile = sh.n_surv;                    // tile entries >= lo (may exceed cap)
   bool in_lds = n_tile <= static_cast<uint32_t>(cap);
   const uint32_t n_all = static_cast<uint32_t>(c0) + n_tile;
+  // the admission threshold when every entry is taken and exactly fills the
+  // set: the smallest of them (survivors read back from LDS; 0 = none known)
+  uint32_t full_min = 0u;
+  if (!p.finalize && p.admit != nullptr && room > 0 && n_all == static_cast<uint32_t>(room) && in_lds) {
+    uint32_t m = 0xFFFFFFFFu;
+    for (uint32_t i = tid; i < n_tile; i += kT) m = min(m, skey[i]);
+    full_min = min(cmin, block_min_u32(m, sh));
+  }
 
   // ---- radix select of the room-th largest key over candidates + tile
   uint32_t T;
@@ -282,7 +338,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
             if (((key ^ prefix) & hi_mask) == 0u) atomicAdd(&sh.hist[(key >> sh_d) & dmask], 1u);
           }
         } else {
-          for_tile(t, lo, [&](int, uint32_t key) {
+          for_tile<kPacked>(t, lo, [&](int, uint32_t key) {
             if (key != 0u && ((key ^ prefix) & hi_mask) == 0u) atomicAdd(&sh.hist[(key >> sh_d) & dmask], 1u);
           });
         }
@@ -299,7 +355,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
         lo = max(lo0, prefix);
         if (tid == 0) sh.n_surv = 0u;
         __syncthreads();
-        for_tile(t, lo, [&](int j, uint32_t key) { append(j, key); });
+        for_tile<kPacked>(t, lo, [&](int j, uint32_t key) { append(j, key); });
         __syncthreads();
         n_tile = sh.n_surv;
         in_lds = true;                            // n_tile <= n_above + in_bin <= cap
@@ -307,6 +363,18 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     }
     T = prefix;
     remaining = static_cast<int32_t>(rem);
+  }
+
+  // The admission threshold for the next tile (nothing in this launch reads
+  // it): the new running set's smallest key once the set is full -- T when
+  // the radix select ran (room entries with keys >= T are taken, at least
+  // one equal to T), full_min when every entry is taken and fills it; a
+  // later column enters only above it.  NaN (admit everything) otherwise.
+  if (tid == 0 && !p.finalize && p.admit != nullptr) {
+    uint32_t thr = 0u;
+    if (room > 0 && n_all > static_cast<uint32_t>(room)) thr = T;
+    else if (room > 0 && n_all == static_cast<uint32_t>(room)) thr = full_min;
+    p.admit[u] = thr != 0u ? key_score(thr) : __uint_as_float(0x7FC00000u);
   }
 
   // ---- candidates: ranks among keys equal to T, then positions (array order)
@@ -344,7 +412,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     if (in_lds) {
       for (uint32_t s = tid; s < n_tile; s += kT) f(scol[s], skey[s]);
     } else {
-      for_tile(t, lo, [&](int j, uint32_t key) {
+      for_tile<kPacked>(t, lo, [&](int j, uint32_t key) {
         if (key != 0u) f(j, key);
       });
     }
@@ -460,7 +528,9 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     }
   });
   if (!fin) {
-    if (tid == 0) p.cand_count[u] = static_cast<int32_t>(n_sel);
+    if (tid == 0) {
+      p.cand_count[u] = static_cast<int32_t>(n_sel);
+    }
     return;
   }
   // ---- forced entries: alive sink first, alive recent last
@@ -519,10 +589,12 @@ bool select_tile_fits(const SelectParams& p) {
 hipError_t launch_select_tile(const SelectParams& p, const float* scores, hipStream_t st) {
   size_t dyn = 0;
   const int cap = tile_cap(p, &dyn);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&select_tile_kernel),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn));
+  const void* kern = p.tile_mask != nullptr ? reinterpret_cast<const void*>(&select_tile_kernel<true>)
+                                             : reinterpret_cast<const void*>(&select_tile_kernel<false>);
+  hipError_t e = hipFuncSetAttribute(kern, hipFuncAttributeMaxDynamicSharedMemorySize, static_cast<int>(dyn));
   if (e != hipSuccess) return e;
-  select_tile_kernel<<<p.U, kT, dyn, st>>>(p, scores, cap);
+  if (p.tile_mask != nullptr) select_tile_kernel<true><<<p.U, kT, dyn, st>>>(p, scores, cap);
+  else select_tile_kernel<false><<<p.U, kT, dyn, st>>>(p, scores, cap);
   return hipGetLastError();
 }
 

@@ -146,10 +146,12 @@ def score_memory(m, k_pool, page_table, n, out, *, page_size, slot_map=None, dea
 
 
 def score_block(q, mu, out, *, n_kv_heads, n_begin=0, n_count=None, qbar=None, qbar_valid=False,
-                scale=0.0, workspace=None, stream=None):
+                scale=0.0, admit=None, tile_mask=None, workspace=None, stream=None):
     """kvsel_score, block mode.  q [S][L][Hq][W][D] (or None with a valid qbar),
     mu [L][Hkv][NB][D] float16, out [S][L*Hkv][n_count] float32,
-    qbar [S][L][Hkv][D] float32 (optional)."""
+    qbar [S][L][Hkv][D] float32 (optional).  With admit ([S][L*Hkv] float32,
+    from a tiled select) and tile_mask ([S][L*Hkv][ceil(n_count/64)] int64,
+    the uint64 mask words) the output is the packed tile form."""
     L, Hkv, NB, D = mu.shape
     assert Hkv == n_kv_heads
     if n_count is None:
@@ -170,13 +172,15 @@ def score_block(q, mu, out, *, n_kv_heads, n_begin=0, n_count=None, qbar=None, q
     a.qbar, a.qbar_valid = _wptr(qbar, "qbar", torch.float32, (S, L, Hkv, D)), 1 if qbar_valid else 0
     a.scale = scale
     a.scores = _wptr(out, "out", torch.float32, numel=S * L * Hkv * n_count)
+    a.admit = _wptr(admit, "admit", torch.float32, numel=S * L * Hkv)
+    a.tile_mask = _wptr(tile_mask, "tile_mask", torch.int64, numel=S * L * Hkv * ((n_count + 63) // 64))
     return _score_call(a, mu.device, workspace, stream)
 
 
 # ------------------------------------------------------------------ select
 
 def _select_args(scores, kept_idx, *, k_total, n_sink, n_recent, n_total, base, keep_mask, n_kept, slot_map,
-                 dead_slot, cand_score, cand_idx, cand_count, finalize, pool, pool_k):
+                 dead_slot, cand_score, cand_idx, cand_count, finalize, pool, pool_k, tile_mask=None, admit=None):
     U, n = scores.shape
     if n_total is None:
         n_total = base + n
@@ -201,20 +205,24 @@ def _select_args(scores, kept_idx, *, k_total, n_sink, n_recent, n_total, base, 
     a.finalize = 1 if finalize else 0
     a.kept_idx, a.keep_mask, a.n_kept = _ptr(kept_idx), _ptr(keep_mask), _ptr(n_kept)
     a.pool, a.pool_k = _abi.POOL[pool], pool_k
+    a.tile_mask = _wptr(tile_mask, "tile_mask", torch.int64, numel=U * ((n + 63) // 64))
+    a.admit = _wptr(admit, "admit", torch.float32, numel=U)
     return a
 
 
 def select(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0, keep_mask=None,
            n_kept=None, slot_map=None, dead_slot=0, cand_score=None, cand_idx=None, cand_count=None,
-           finalize=True, pool="none", pool_k=1, workspace=None, stream=None):
+           finalize=True, pool="none", pool_k=1, tile_mask=None, admit=None, workspace=None, stream=None):
     """kvsel_select.  scores [U][n] float32 (rows may be a strided view of
     contiguous memory: pass the 2-D tensor); kept_idx [U][k_total] int32.
-    pool/pool_k rank pooled scores (untiled calls).  Returns the workspace
-    (untiled calls need one; pass it back to reuse it)."""
+    pool/pool_k rank pooled scores (untiled calls).  Tiled calls: tile_mask
+    ([U][ceil(n/64)] int64) marks a packed tile; admit ([U] float32)
+    receives the admission threshold for the next tile.  Returns the
+    workspace (untiled calls need one; pass it back to reuse it)."""
     a = _select_args(scores, kept_idx, k_total=k_total, n_sink=n_sink, n_recent=n_recent, n_total=n_total,
                      base=base, keep_mask=keep_mask, n_kept=n_kept, slot_map=slot_map, dead_slot=dead_slot,
                      cand_score=cand_score, cand_idx=cand_idx, cand_count=cand_count, finalize=finalize,
-                     pool=pool, pool_k=pool_k)
+                     pool=pool, pool_k=pool_k, tile_mask=tile_mask, admit=admit)
     lib = _abi.load()
     nb = ctypes.c_size_t(0)
     _check(lib.kvsel_select_workspace(ctypes.byref(a), ctypes.byref(nb)))
@@ -225,14 +233,14 @@ def select(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0,
 
 def select_noalloc(scores, kept_idx, *, k_total, n_sink, n_recent, n_total=None, base=0, keep_mask=None,
                    n_kept=None, slot_map=None, dead_slot=0, cand_score=None, cand_idx=None, cand_count=None,
-                   finalize=True, pool="none", pool_k=1, stream=None):
+                   finalize=True, pool="none", pool_k=1, tile_mask=None, admit=None, stream=None):
     """kvsel_select_noalloc: kvsel_select with its scratch in the library's
     fixed per-device array (nothing is allocated, here or in the library).
     Calls that overlap on one GPU share that array and race."""
     a = _select_args(scores, kept_idx, k_total=k_total, n_sink=n_sink, n_recent=n_recent, n_total=n_total,
                      base=base, keep_mask=keep_mask, n_kept=n_kept, slot_map=slot_map, dead_slot=dead_slot,
                      cand_score=cand_score, cand_idx=cand_idx, cand_count=cand_count, finalize=finalize,
-                     pool=pool, pool_k=pool_k)
+                     pool=pool, pool_k=pool_k, tile_mask=tile_mask, admit=admit)
     _check(_abi.load().kvsel_select_noalloc(ctypes.byref(a), _stream(stream)))
 
 

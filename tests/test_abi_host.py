@@ -145,6 +145,51 @@ def test_score_validation_and_workspace_without_device():
     assert lib.kvsel_score(ctypes.byref(_score_args()), None, 0, None) == _abi.KVSEL_E_WORKSPACE
 
 
+def test_packed_tile_options_are_validated_without_device():
+    """The admission threshold and packed-tile mask: optional for the earlier
+    struct layouts, tiled calls only (select), block mode with D 128 and
+    both given together (score)."""
+    lib = _abi.load()
+    nb = ctypes.c_size_t(0)
+    tiled = dict(cand_score=0x3000, cand_idx=0x4000, cand_count=0x5000, n=60, n_total=100, base=40)
+    ok = _select_args(tile_mask=0x6000, admit=0x7000, finalize=0, **tiled)
+    assert _status(lib.kvsel_select_workspace, ok, ctypes.byref(nb)) == _abi.KVSEL_OK and nb.value == 0
+    assert _status(lib.kvsel_select_workspace, _select_args(tile_mask=0x6000), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert b"tiled" in lib.kvsel_last_error()
+    assert _status(lib.kvsel_select_workspace, _select_args(admit=0x7000), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert _status(lib.kvsel_select_workspace, _select_args(tile_mask=0x6008, **tiled),
+                   ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    # a tile too wide for one workgroup's LDS takes the workspace path, which has neither option
+    wide = dict(tiled, n=1 << 23, n_total=(1 << 23) + 40, row_stride=1 << 23)
+    assert _status(lib.kvsel_select_workspace, _select_args(admit=0x7000, **wide),
+                   ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
+    # the layout that ends before tile_mask is accepted and ignores the fields' memory
+    old = _select_args(tile_mask=0x6008, admit=0x7000, **tiled)
+    old.struct_size = _abi.SelectArgs.tile_mask.offset
+    assert _status(lib.kvsel_select_workspace, old, ctypes.byref(nb)) == _abi.KVSEL_OK
+    old.struct_size = _abi.SelectArgs.tile_mask.offset - 8
+    assert _status(lib.kvsel_select_workspace, old, ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+
+    blk = dict(mode=_abi.SCORE_BLOCK, k_dtype=_abi.F16, N=1000, n_begin=0, n_count=1000, S=2)
+    assert _status(lib.kvsel_score_workspace, _score_args(admit=0x5000, tile_mask=0x6000, **blk),
+                   ctypes.byref(nb)) == _abi.KVSEL_OK
+    assert _status(lib.kvsel_score_workspace, _score_args(admit=0x5000, **blk), ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert b"together" in lib.kvsel_last_error()
+    assert _status(lib.kvsel_score_workspace, _score_args(tile_mask=0x6000, **blk),
+                   ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert _status(lib.kvsel_score_workspace, _score_args(admit=0x5000, tile_mask=0x6008, **blk),
+                   ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+    assert _status(lib.kvsel_score_workspace, _score_args(admit=0x5000, tile_mask=0x6000, D=64, **blk),
+                   ctypes.byref(nb)) == _abi.KVSEL_E_UNSUPPORTED
+    assert _status(lib.kvsel_score_workspace, _score_args(admit=0x5000, tile_mask=0x6000),
+                   ctypes.byref(nb)) == _abi.KVSEL_E_ARG          # window mode
+    old = _score_args(admit=0x5000, **blk)                            # would be refused if read
+    old.struct_size = _abi.ScoreArgs.admit.offset
+    assert _status(lib.kvsel_score_workspace, old, ctypes.byref(nb)) == _abi.KVSEL_OK
+    old.struct_size = _abi.ScoreArgs.admit.offset - 8
+    assert _status(lib.kvsel_score_workspace, old, ctypes.byref(nb)) == _abi.KVSEL_E_ARG
+
+
 def test_gather_and_redirect_validation_without_device():
     lib = _abi.load()
     a = _abi.GatherArgs()

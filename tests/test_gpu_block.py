@@ -53,6 +53,57 @@ def test_block_scores_match_oracle(S, W, NB, n_begin, n_count, D):
                         extra_tol=tol[..., NB - 50:])
 
 
+@pytest.mark.parametrize("S,NB,n_begin,n_count", [
+    (4, 70000, 0, 65536),                 # whole chunks
+    (2, 5000, 1000, 777),                 # ragged last chunk and word, tile inside the index
+    (3, 3000, 17, 1001),
+    (1, 300, 0, 40),                      # one partial word
+])
+def test_block_scores_packed_matches_dense(S, NB, n_begin, n_count):
+    """The packed output under per-row thresholds: the admission mask marks
+    exactly the columns whose dense score is above the row's threshold (NaN:
+    all; -0.0 equal to +0.0), and each 256-column chunk starts with the
+    admitted dense scores in column order, bit for bit; positions after
+    them stay as they were.  The dense scores themselves are held to the
+    oracle by test_block_scores_match_oracle."""
+    dev = require_gpu()
+    g = torch.Generator(device=dev).manual_seed(NB + S)
+    L, Hq, Hkv, W, D = 2, 8, 2, 16, 128
+    U = L * Hkv
+    q = torch.randn((S, L, Hq, W, D), generator=g, device=dev).to(torch.bfloat16)
+    mu = (torch.randn((L, Hkv, NB, D), generator=g, device=dev) * 0.3).to(torch.float16)
+    dense = torch.empty((S, U, n_count), dtype=torch.float32, device=dev)
+    kv.score_block(q, mu, dense, n_kv_heads=Hkv, n_begin=n_begin, n_count=n_count)
+    torch.cuda.synchronize()
+    d = dense.cpu().numpy().reshape(S * U, n_count)
+    rng = np.random.default_rng(NB)
+    # thresholds: NaN, below everything, above everything, a tie with a score, quantiles
+    thr = np.quantile(d, rng.uniform(0.5, 0.999, S * U), axis=1).diagonal().astype(np.float32)
+    thr[0] = np.nan
+    if S * U > 3:
+        thr[1], thr[2], thr[3] = -1e30, 1e30, d[3, n_count // 2]
+    sentinel = -12345.0
+    packed = torch.full((S, U, n_count), sentinel, dtype=torch.float32, device=dev)
+    n_words = (n_count + 63) // 64
+    mask = torch.full((S, U, n_words), -1, dtype=torch.int64, device=dev)
+    kv.score_block(q, mu, packed, n_kv_heads=Hkv, n_begin=n_begin, n_count=n_count,
+                   admit=torch.from_numpy(thr).to(dev).reshape(S, U), tile_mask=mask)
+    torch.cuda.synchronize()
+    pk = packed.cpu().numpy().reshape(S * U, n_count)
+    words = mask.cpu().numpy().reshape(S * U, n_words).view(np.uint64)
+    bits = ((words[:, :, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).astype(bool)
+    bits = bits.reshape(S * U, -1)
+    assert not bits[:, n_count:].any()
+    for r in range(S * U):
+        adm = np.ones(n_count, bool) if np.isnan(thr[r]) else d[r] > thr[r]
+        np.testing.assert_array_equal(bits[r, :n_count], adm, err_msg="row %d" % r)
+        for c0 in range(0, n_count, 256):
+            want = d[r, c0:c0 + 256][adm[c0:c0 + 256]]
+            got = pk[r, c0:c0 + 256]
+            np.testing.assert_array_equal(got[:len(want)].view(np.uint32), want.view(np.uint32))
+            assert np.all(got[len(want):] == sentinel)
+
+
 def _oracle_unit_scores(q, mu, s, u, Hkv):
     """Oracle block scores of one (session, unit) and the float32 error bound
     of the library's arithmetic for each."""
@@ -126,7 +177,10 @@ def test_kvmem_10m_workload_full_size():
     tiled top-4096, and the in-place incremental update of each session's
     4096-page view (previous view shares about half its blocks; moved hits
     rotated in place), in the
-    launch sequence the benchmark times.  64 (session, unit) views drawn in
+    launch sequence the benchmark times (tiles after the first scored in the
+    packed form under the running sets' admission thresholds; they are also
+    scored densely to hold every score to the oracle and each packed row to
+    its dense one).  64 (session, unit) views drawn in
     a seeded order are checked against the oracle: their scores over every
     tile, their kept blocks, and on the bit-exact ones the whole updated view
     (page table, re-RoPEd misses, hits rotated in place, V).  Invariants hold
@@ -145,20 +199,52 @@ def test_kvmem_10m_workload_full_size():
     kept = torch.empty((SU, k), dtype=torch.int32, device=dev)
     nk = torch.empty(SU, dtype=torch.int32, device=dev)
     tile_out = torch.empty((S, U, tile), dtype=torch.float32, device=dev)
+    dense_out = torch.empty((S, U, tile), dtype=torch.float32, device=dev)
+    mask = torch.empty((SU, tile // 64), dtype=torch.int64, device=dev)
+    admit = torch.empty(SU, dtype=torch.float32, device=dev)
     pick = np.random.default_rng(cfg.seed).permutation(SU)[:62]
     sample = sorted(set([(0, 0), (S - 1, U - 1)] + [divmod(int(i), U) for i in pick]))
+    rows = torch.tensor([s * U + u for (s, u) in sample], device=dev)
     sampled_scores = {su: [] for su in sample}
+    n_admitted = []
     for b in range(0, NB, tile):
         n = min(tile, NB - b)
-        out = tile_out[:, :, :n]
+        # the benchmark's sequence: the first tile dense, later ones packed
+        # under the previous call's admission thresholds
+        thr = admit.cpu().numpy()[rows.cpu().numpy()] if b > 0 else None
         kv.score_block(qs if b == 0 else None, mu, tile_out.view(-1)[: S * U * n].view(S, U, n),
-                       n_kv_heads=cfg.Hkv, n_begin=b, n_count=n, qbar=qbar, qbar_valid=b > 0)
+                       n_kv_heads=cfg.Hkv, n_begin=b, n_count=n, qbar=qbar, qbar_valid=b > 0,
+                       admit=admit.view(S, U) if b > 0 else None,
+                       tile_mask=mask.view(-1)[: SU * ((n + 63) // 64)] if b > 0 else None)
         out = tile_out.view(-1)[: S * U * n].view(SU, n)
+        tm = mask.view(-1)[: SU * ((n + 63) // 64)].view(SU, -1) if b > 0 else None
+        if b > 0:
+            # the same tile dense, to hold every score to the oracle and the
+            # packed rows to the dense ones
+            kv.score_block(None, mu, dense_out.view(-1)[: S * U * n].view(S, U, n), n_kv_heads=cfg.Hkv,
+                           n_begin=b, n_count=n, qbar=qbar, qbar_valid=True)
+            dense = dense_out.view(-1)[: S * U * n].view(SU, n)
+            d, pk = dense[rows].cpu().numpy(), out[rows].cpu().numpy()
+            words = tm[rows].cpu().numpy().view(np.uint64)
+            bits = ((words[:, :, None] >> np.arange(64, dtype=np.uint64)) & np.uint64(1)).astype(bool)
+            bits = bits.reshape(len(sample), -1)[:, :n]
+            for i in range(len(sample)):
+                adm = np.ones(n, bool) if np.isnan(thr[i]) else d[i] > thr[i]
+                np.testing.assert_array_equal(bits[i], adm)
+                for c0 in range(0, n, 256):
+                    want = d[i, c0:c0 + 256][adm[c0:c0 + 256]]
+                    np.testing.assert_array_equal(pk[i, c0:c0 + len(want)].view(np.uint32), want.view(np.uint32))
+            n_admitted.append(int(bits.sum()))
+        else:
+            dense = out
         kv.select(out, kept, k_total=k, n_sink=cfg.n_sink, n_recent=cfg.n_recent, n_total=NB, base=b,
-                  cand_score=cs, cand_idx=ci, cand_count=cc, finalize=b + n == NB, n_kept=nk)
+                  cand_score=cs, cand_idx=ci, cand_count=cc, finalize=b + n == NB, n_kept=nk,
+                  tile_mask=tm, admit=admit if b + n < NB else None)
         for (s, u) in sample:
-            sampled_scores[(s, u)].append(f64(out[s * U + u]))
+            sampled_scores[(s, u)].append(f64(dense[s * U + u]))
     torch.cuda.synchronize()
+    print("admitted per later tile over the sampled views: %s of %d columns" % (n_admitted, len(sample) * tile),
+          flush=True)
     kept_h = kept.cpu().numpy()
     assert np.all(nk.cpu().numpy() == k)
     assert len(sample) >= 63

@@ -139,10 +139,35 @@ def test_select_tiled_equals_untiled(n, tile, k):
         np.testing.assert_array_equal(kept[u, : len(ok)], ok)
 
 
-def _tiled(dev, s, k, n_sink, n_recent, tile, slot_map=None, dead_slot=0, stride_pad=0):
+def pack_tile(x, thr):
+    """Packed tile form of dense rows x [U][m] under per-row thresholds thr
+    [U] (NaN admits every column): per 256-column chunk the admitted scores
+    in column order at the chunk's start, every other position NaN (a read
+    of one would disturb the selection), and the uint64 mask words as int64."""
+    U, m = x.shape
+    adm = np.where(np.isnan(thr)[:, None], True, x > thr[:, None])
+    packed = np.full((U, m), np.nan, np.float32)
+    for c0 in range(0, m, 256):
+        a = adm[:, c0:c0 + 256]
+        for u in range(U):
+            v = x[u, c0:c0 + 256][a[u]]
+            packed[u, c0:c0 + len(v)] = v
+    n_words = (m + 63) // 64
+    bits = np.zeros((U, n_words * 64), bool)
+    bits[:, :m] = adm
+    words = (bits.reshape(U, n_words, 64).astype(np.uint64) << np.arange(64, dtype=np.uint64)).sum(axis=2,
+                                                                                                  dtype=np.uint64)
+    return packed, words.view(np.int64), adm
+
+
+def _tiled(dev, s, k, n_sink, n_recent, tile, slot_map=None, dead_slot=0, stride_pad=0, packed=None):
     """Tiled selection of every row of s (with an optional slot map), tiles
     of `tile` columns in ascending order; the rows may sit in a wider
-    buffer (stride_pad extra columns) so that tile rows are misaligned."""
+    buffer (stride_pad extra columns) so that tile rows are misaligned.
+    packed: None (dense tiles), "exact" (every tile after the first packed
+    under the threshold the previous call wrote, which is checked against
+    the running set), or "low" (packed under lower thresholds: NaN on even
+    rows, the next float below on odd rows)."""
     U, n = s.shape
     buf = torch.zeros((U, n + stride_pad), dtype=torch.float32, device=dev)
     buf[:, :n] = torch.from_numpy(s).to(dev)
@@ -152,22 +177,44 @@ def _tiled(dev, s, k, n_sink, n_recent, tile, slot_map=None, dead_slot=0, stride
     kept = torch.full((U, k), -7, dtype=torch.int32, device=dev)
     nk = torch.zeros(U, dtype=torch.int32, device=dev)
     sm = None if slot_map is None else torch.from_numpy(slot_map.astype(np.int32)).to(dev)
+    admit = torch.full((U,), 5.0, device=dev) if packed else None
+    alive = np.ones(n, bool) if slot_map is None else slot_map != dead_slot
+    room = k - int((osel.forced_mask(n, n_sink, n_recent) & alive).sum())
     for b in range(0, n, tile):
         e = min(n, b + tile)
-        kv.select(buf[:, b:e], kept, k_total=k, n_sink=n_sink, n_recent=n_recent, n_total=n, base=b,
+        rows, mask = buf[:, b:e], None
+        if packed and b > 0:
+            thr = admit.cpu().numpy()
+            # the threshold is the running set's smallest score once it is full
+            cnt, cand = cc.cpu().numpy(), cs.cpu().numpy()
+            for u in range(U):
+                if cnt[u] == room and room > 0:
+                    assert thr[u] == cand[u, :room].min(), (u, thr[u])
+                else:
+                    assert np.isnan(thr[u])
+            if packed == "low":
+                thr = np.where(np.arange(U) % 2 == 0, np.nan, np.nextafter(thr, np.float32(-np.inf)))
+            pk, words, _ = pack_tile(s[:, b:e], thr.astype(np.float32))
+            pbuf = torch.zeros((U, e - b + stride_pad), dtype=torch.float32, device=dev)
+            pbuf[:, :e - b] = torch.from_numpy(pk).to(dev)
+            rows, mask = pbuf[:, :e - b], torch.from_numpy(words).to(dev)
+        kv.select(rows, kept, k_total=k, n_sink=n_sink, n_recent=n_recent, n_total=n, base=b,
                   cand_score=cs, cand_idx=ci, cand_count=cc, finalize=(e == n), n_kept=nk, slot_map=sm,
-                  dead_slot=dead_slot)
+                  dead_slot=dead_slot, tile_mask=mask, admit=admit if e < n else None)
     torch.cuda.synchronize()
     return kept.cpu().numpy(), nk.cpu().numpy()
 
 
+@pytest.mark.parametrize("packed", [None, "exact", "low"])
 @pytest.mark.parametrize("case", ["equal", "ascending", "descending", "coarse", "dead", "k8192", "misaligned"])
-def test_select_tiled_hard_cases(case):
+def test_select_tiled_hard_cases(case, packed):
     """Tiles whose survivors overflow the LDS set (the first tile; rising
     scores), plateaus of equal keys wider than any LDS set (every column
     ranked by index), nothing surviving after the first tile, dead slots,
-    the largest budget, and tile rows that are not 16-byte aligned.  The
-    tiled result must equal the untiled oracle selection bit for bit."""
+    the largest budget, and tile rows that are not 16-byte aligned; with
+    dense tiles, and with tiles packed under the admission threshold the
+    previous call wrote (or a lower one).  The tiled result must equal the
+    untiled oracle selection bit for bit."""
     dev = require_gpu()
     rng = np.random.default_rng(len(case))
     U, n, tile, k, n_sink, n_recent = 3, 70000, 16384, 4096, 4, 64
@@ -193,7 +240,7 @@ def test_select_tiled_hard_cases(case):
     else:
         n, tile, pad = 50001, 10001, 3
         s = rng.standard_normal((U, n)).astype(np.float32)
-    got, nk = _tiled(dev, s, k, n_sink, n_recent, tile, slot_map, dead_slot, pad)
+    got, nk = _tiled(dev, s, k, n_sink, n_recent, tile, slot_map, dead_slot, pad, packed)
     for u in range(U):
         ok, _ = osel.select_topk(s[u].astype(np.float64), k, n_sink, n_recent, alive)
         assert nk[u] == len(ok), case
