@@ -186,7 +186,8 @@ kvsel_status validate_score(const kvsel_score_args* a, ScorePlan* plan) {
       return fail(KVSEL_E_UNSUPPORTED, "window of G*W*D > 32768 needs bf16/f16 with SUM/MEAN aggregation");
     plan->own_lse = a->lse_in == nullptr && a->lse_out == nullptr;
     if (plan->own_lse) plan->lse_off = take(static_cast<size_t>(a->L) * a->Hq * a->W * 4);
-    if (a->lse_in == nullptr && plan->mfma) plan->part_off = take(window_mfma_partials_bytes(p));
+    if (a->lse_in == nullptr)
+      plan->part_off = take(plan->mfma ? window_mfma_partials_bytes(p) : window_valu_partials_bytes(p));
     if (plan->pooled) plan->raw_off = take(static_cast<size_t>(U) * a->N * 4);
   } else if (a->mode == KVSEL_SCORE_MEMORY) {
     if (a->q == nullptr || a->k == nullptr || a->page_table == nullptr)
@@ -283,7 +284,7 @@ kvsel_status kvsel_score(const kvsel_score_args* a, void* ws, size_t ws_bytes, v
         if (plan.mfma)
           e = launch_window_lse_mfma(p, a->k_dtype, a->q, a->k, reinterpret_cast<float*>(w + plan.part_off), lo, st);
         else
-          e = launch_window_lse_valu(p, a->k_dtype, a->q, a->k, lo, st);
+          e = launch_window_lse_valu(p, a->k_dtype, a->q, a->k, reinterpret_cast<float*>(w + plan.part_off), lo, st);
         if (e != hipSuccess) return hip_fail(e, "window lse");
         lse = lo;
       }

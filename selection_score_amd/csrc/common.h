@@ -93,7 +93,8 @@ struct WindowParams {
 };
 
 hipError_t launch_window_lse_valu(const WindowParams& p, int dt, const void* q, const void* k,
-                                  float* lse, hipStream_t st);
+                                  float* partials, float* lse, hipStream_t st);
+size_t window_valu_partials_bytes(const WindowParams& p);
 hipError_t launch_window_scores_valu(const WindowParams& p, int dt, const void* q, const void* k,
                                      const float* lse, float* out, hipStream_t st);
 bool window_mfma_supported(const WindowParams& p, int dt);

@@ -141,6 +141,7 @@ __device__ uint3 block_sum3(uint32_t a, uint32_t b, uint32_t c, uint32_t* scratc
 
 constexpr int kPrepKeys = 4096;       // columns per select_keys_kernel workgroup
 constexpr int kFusedMinUnits = 128;   // unpooled untiled calls with this many units make their own keys
+constexpr int kFusedSmallN = 8192;    // ... as do calls of any unit count over rows this short
 constexpr int kPrepThreads = 256;
 constexpr int kMaxPoolR = 127;        // pool_k <= 255
 
@@ -667,14 +668,16 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
   if (tid == 0 && p.n_kept != nullptr) p.n_kept[u] = static_cast<int32_t>(total);
 }
 
-// Unpooled untiled calls without a slot map, with enough units to fill the
-// device and rows that fit the registers, run select_regs_kernel alone: each
-// unit's workgroup makes its keys from the scores, so no workspace is used.
+// Unpooled untiled calls without a slot map, with rows that fit the
+// registers and either enough units to fill the device or rows short enough
+// that one workgroup reads them at once, run select_regs_kernel alone: each
+// unit's workgroup makes its keys from the scores, so no workspace is used
+// (and a short call saves the second launch's latency).
 // (Pooled rows keep the two launches, whose key kernel spreads the window
 // work over many workgroups.)  An empty row (n = 0, scores possibly NULL)
 // takes the two-launch path, whose per-unit kernel reads no key when n is 0.
 static bool select_single_launch(const SelectParams& p) {
-  return p.cand_count == nullptr && p.n > 0 && p.n <= 32 * kThreads && p.U >= kFusedMinUnits &&
+  return p.cand_count == nullptr && p.n > 0 && p.n <= 32 * kThreads && (p.U >= kFusedMinUnits || p.n <= kFusedSmallN) &&
          (p.pool == KVSEL_POOL_NONE || p.pool_k == 1) && p.slot_map == nullptr;
 }
 

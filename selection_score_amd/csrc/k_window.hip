@@ -17,7 +17,8 @@
 // one cross-half shuffle; the LSE pass swaps the operands so each lane owns
 // one query row and keeps an online max/sum in registers.
 //
-// VALU path: any dtype/shape/aggregation, one lane per key.
+// VALU path: any dtype/shape/aggregation, one lane per key (the LSE pass:
+// one wavefront per chunk of keys, merged like the matrix-core partials).
 #include "common.h"
 
 #include <math.h>
@@ -32,58 +33,118 @@ constexpr float kLn2 = 0.6931471805599453f;
 
 // =================================================================== VALU path
 
+// 16 bytes of a row as floats (4 of F32, 8 of BF16/F16).
 template <int DT>
-__global__ __launch_bounds__(256) void lse_valu_kernel(WindowParams p, const void* __restrict__ q,
-                                                       const void* __restrict__ k,
-                                                       float* __restrict__ lse) {
-  __shared__ float qs[4][256];
-  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
-  const int64_t row = static_cast<int64_t>(blockIdx.x) * 4 + w;   // (l, h, t)
-  const int64_t n_rows = static_cast<int64_t>(p.L) * p.Hq * p.W;
-  const bool valid = row < n_rows;
-  const int64_t rr = valid ? row : 0;
-  const int t = static_cast<int>(rr % p.W);
-  const int h = static_cast<int>((rr / p.W) % p.Hq);
-  const int l = static_cast<int>(rr / (static_cast<int64_t>(p.W) * p.Hq));
-  const int g = h / p.G;
-  for (int d = lane; d < p.D; d += 64) qs[w][d] = load_elem<DT>(q, rr * p.D + d);
-  __syncthreads();
-  if (!valid) return;
-  const int64_t n_allowed = p.causal ? (p.N - p.W + t + 1) : p.N;
-  const int64_t kbase = (static_cast<int64_t>(l) * p.Hkv + g) * p.N * p.D;
-  float m = -INFINITY, s = 0.f;
-  for (int64_t j = lane; j < n_allowed; j += 64) {
-    float acc = 0.f;
-    for (int d = 0; d < p.D; ++d) acc += qs[w][d] * load_elem<DT>(k, kbase + j * p.D + d);
-    const float x = acc * p.scale;
-    if (x > m) {
-      s = s * expf(m - x) + 1.f;
-      m = x;
-    } else {
-      s += expf(x - m);
+__device__ __forceinline__ void load16_floats(const void* base, int64_t elem, float* out) {
+  const uint4 v = *reinterpret_cast<const uint4*>(static_cast<const uint8_t*>(base) + elem * (DT == KVSEL_F32 ? 4 : 2));
+  const uint32_t w[4] = {v.x, v.y, v.z, v.w};
+  if constexpr (DT == KVSEL_F32) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) out[i] = __uint_as_float(w[i]);
+  } else {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const uint16_t lo = static_cast<uint16_t>(w[i] & 0xFFFFu), hi = static_cast<uint16_t>(w[i] >> 16);
+      out[2 * i] = (DT == KVSEL_BF16) ? bf16_to_f32(lo) : f16_to_f32(lo);
+      out[2 * i + 1] = (DT == KVSEL_BF16) ? bf16_to_f32(hi) : f16_to_f32(hi);
     }
   }
-  for (int o = 32; o > 0; o >>= 1) {
-    const float m2 = __shfl_xor(m, o, 64);
-    const float s2 = __shfl_xor(s, o, 64);
-    const float mn = fmaxf(m, m2);
-    const float a = (m == -INFINITY) ? 0.f : s * expf(m - mn);
-    const float b = (m2 == -INFINITY) ? 0.f : s2 * expf(m2 - mn);
-    m = mn;
-    s = a + b;
-  }
-  if (lane == 0) lse[row] = m + logf(s);
 }
 
+// LSE pass: one wavefront per (chunk of keys, group of kRowGroup query
+// rows, unit).  The group's rows sit in LDS as floats; each lane owns keys
+// lane, lane + 64, ... of the chunk (its K row read with 16-byte loads) and
+// keeps an online max/sum of exp2(c1 * q.k) per row.  The wavefront's
+// (max, sum) per row, reduced in a fixed order, go to the partials that
+// lse_combine_kernel merges, as in the matrix-core path.  Short wavefronts
+// keep the dependent chain of each one short: small windows run on few
+// keys, where latency, not throughput, sets the time.
+constexpr int kLseValuRowGroup = 4;
+
+template <int DT, int D>
+__global__ __launch_bounds__(64) void lse_valu_kernel(WindowParams p, const void* __restrict__ q,
+                                                      const void* __restrict__ k, int chunk_keys,
+                                                      float2* __restrict__ partials) {
+  __shared__ float qs[kLseValuRowGroup * D];
+  constexpr int E = (DT == KVSEL_F32) ? 4 : 8;
+  const int u = blockIdx.z, chunk = blockIdx.x, n_chunks = gridDim.x;
+  const int r0 = blockIdx.y * kLseValuRowGroup;
+  const int lane = threadIdx.x;
+  const int l = u / p.Hkv, g = u % p.Hkv;
+  const int R = p.G * p.W;
+  for (int e = lane; e < kLseValuRowGroup * D; e += 64) {
+    const int r = r0 + e / D, d = e % D;
+    const int h = g * p.G + r / p.W, t = r % p.W;
+    qs[e] = (r < R) ? load_elem<DT>(q, ((static_cast<int64_t>(l) * p.Hq + h) * p.W + t) * D + d) : 0.f;
+  }
+  __syncthreads();
+  const int64_t key0 = static_cast<int64_t>(chunk) * chunk_keys;
+  const int64_t key1 = min(p.N, key0 + chunk_keys);
+  const int64_t kb = (static_cast<int64_t>(l) * p.Hkv + g) * p.N * D;
+  const float c1 = p.scale * kLog2e;
+  {
+    float m[kLseValuRowGroup], s[kLseValuRowGroup];
+#pragma unroll
+    for (int i = 0; i < kLseValuRowGroup; ++i) {
+      m[i] = -INFINITY;
+      s[i] = 0.f;
+    }
+    for (int64_t j = key0 + lane; j < key1; j += 64) {
+      float kr[D];
+#pragma unroll
+      for (int d = 0; d < D; d += E) load16_floats<DT>(k, kb + j * D + d, kr + d);
+#pragma unroll
+      for (int i = 0; i < kLseValuRowGroup; ++i) {
+        const int r = r0 + i;
+        if (r < R && (!p.causal || j <= p.N - p.W + r % p.W)) {
+          const float* qr = qs + i * D;
+          float acc = 0.f;
+#pragma unroll
+          for (int d = 0; d < D; ++d) acc = fmaf(qr[d], kr[d], acc);
+          const float x = acc * c1;
+          if (x > m[i]) {
+            s[i] = s[i] * exp2f(m[i] - x) + 1.f;
+            m[i] = x;
+          } else {
+            s[i] += exp2f(x - m[i]);
+          }
+        }
+      }
+    }
+#pragma unroll
+    for (int i = 0; i < kLseValuRowGroup; ++i) {
+      float mm = m[i], ss = s[i];
+      for (int o = 32; o > 0; o >>= 1) {
+        const float m2 = __shfl_xor(mm, o, 64);
+        const float s2 = __shfl_xor(ss, o, 64);
+        const float mn = fmaxf(mm, m2);
+        const float a = (mm == -INFINITY) ? 0.f : ss * exp2f(mm - mn);
+        const float b = (m2 == -INFINITY) ? 0.f : s2 * exp2f(m2 - mn);
+        mm = mn;
+        ss = a + b;
+      }
+      if (lane == 0 && r0 + i < R)
+        partials[(static_cast<int64_t>(u) * n_chunks + chunk) * R + r0 + i] = make_float2(mm, ss);
+    }
+  }
+}
+
+// Score pass: a workgroup per (64 keys, unit), one key per lane; its four
+// wavefronts split the window rows (wavefront w takes rows t = w, w + 4, ...)
+// and their per-key row aggregates are combined in wavefront order through
+// LDS, so each lane's dependent chain is a quarter of the window.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void scores_valu_kernel(WindowParams p, const void* __restrict__ q,
                                                           const void* __restrict__ k,
                                                           const float* __restrict__ lse,
                                                           float* __restrict__ out) {
   extern __shared__ float sm[];          // [G*W][D] queries, then [G*W] lse
+  __shared__ float part[4][64];
+  constexpr int E = (DT == KVSEL_F32) ? 4 : 8;
   const int u = blockIdx.y;
   const int l = u / p.Hkv, g = u % p.Hkv;
   const int R = p.G * p.W;
+  const int lane = threadIdx.x & 63, w = threadIdx.x >> 6;
   float* qs = sm;
   float* ls = sm + static_cast<int64_t>(R) * D;
   for (int64_t e = threadIdx.x; e < static_cast<int64_t>(R) * D; e += blockDim.x) {
@@ -96,13 +157,15 @@ __global__ __launch_bounds__(256) void scores_valu_kernel(WindowParams p, const 
     ls[r] = lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t];
   }
   __syncthreads();
-  const int64_t j = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
-  if (j >= p.N) return;
+  const int64_t j = static_cast<int64_t>(blockIdx.x) * 64 + lane;
+  const bool valid = j < p.N;
   float kr[D];
-  const int64_t kb = ((static_cast<int64_t>(l) * p.Hkv + g) * p.N + j) * D;
-  for (int d = 0; d < D; ++d) kr[d] = load_elem<DT>(k, kb + d);
+  const int64_t kb = ((static_cast<int64_t>(l) * p.Hkv + g) * p.N + (valid ? j : 0)) * D;
+#pragma unroll
+  for (int d = 0; d < D; d += E) load16_floats<DT>(k, kb + d, kr + d);
+  const bool rmax = p.row_agg == KVSEL_AGG_MAX;
   float racc = 0.f;
-  for (int t = 0; t < p.W; ++t) {
+  for (int t = w; t < p.W; t += 4) {
     const bool allowed = !p.causal || j <= p.N - p.W + t;
     float hacc = 0.f;
     for (int hl = 0; hl < p.G; ++hl) {
@@ -111,27 +174,23 @@ __global__ __launch_bounds__(256) void scores_valu_kernel(WindowParams p, const 
       if (allowed) {
         float acc = 0.f;
         const float* qr = qs + static_cast<int64_t>(r) * D;
-        for (int d = 0; d < D; ++d) acc += qr[d] * kr[d];
+#pragma unroll
+        for (int d = 0; d < D; ++d) acc = fmaf(qr[d], kr[d], acc);
         pr = expf(acc * p.scale - ls[r]);
       }
       hacc = (p.head_agg == KVSEL_AGG_MAX) ? fmaxf(hacc, pr) : hacc + pr;
     }
     if (p.head_agg == KVSEL_AGG_MEAN) hacc /= static_cast<float>(p.G);
-    racc = (p.row_agg == KVSEL_AGG_MAX) ? fmaxf(racc, hacc) : racc + hacc;
+    racc = rmax ? fmaxf(racc, hacc) : racc + hacc;
   }
-  if (p.row_agg == KVSEL_AGG_MEAN) racc /= static_cast<float>(p.W);
-  out[static_cast<int64_t>(u) * p.N + j] = racc;
-}
-
-hipError_t launch_window_lse_valu(const WindowParams& p, int dt, const void* q, const void* k,
-                                  float* lse, hipStream_t st) {
-  const int64_t rows = static_cast<int64_t>(p.L) * p.Hq * p.W;
-  const int grid = static_cast<int>(ceil_div(rows, 4));
-  if (grid == 0) return hipSuccess;
-  if (dt == KVSEL_F32) lse_valu_kernel<KVSEL_F32><<<grid, 256, 0, st>>>(p, q, k, lse);
-  else if (dt == KVSEL_BF16) lse_valu_kernel<KVSEL_BF16><<<grid, 256, 0, st>>>(p, q, k, lse);
-  else lse_valu_kernel<KVSEL_F16><<<grid, 256, 0, st>>>(p, q, k, lse);
-  return hipGetLastError();
+  part[w][lane] = racc;
+  __syncthreads();
+  if (w != 0 || !valid) return;
+  float tot = part[0][lane];
+#pragma unroll
+  for (int x = 1; x < 4; ++x) tot = rmax ? fmaxf(tot, part[x][lane]) : tot + part[x][lane];
+  if (p.row_agg == KVSEL_AGG_MEAN) tot /= static_cast<float>(p.W);
+  out[static_cast<int64_t>(u) * p.N + j] = tot;
 }
 
 template <int DT, int D>
@@ -142,7 +201,7 @@ static hipError_t launch_scores_valu_t(const WindowParams& p, const void* q, con
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(sh));
   if (e != hipSuccess) return e;
-  dim3 grid(static_cast<unsigned>(ceil_div(p.N, 256)), static_cast<unsigned>(p.L * p.Hkv));
+  dim3 grid(static_cast<unsigned>(ceil_div(p.N, 64)), static_cast<unsigned>(p.L * p.Hkv));
   scores_valu_kernel<DT, D><<<grid, 256, sh, st>>>(p, q, k, lse, out);
   return hipGetLastError();
 }
@@ -392,20 +451,33 @@ void lse_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __r
 #undef KVSEL_LSE_TILE
 
 // ---- combine chunk partials into LSE [L][Hq][W] (natural log)
-__global__ void lse_combine_kernel(WindowParams p, int n_chunks, const float2* __restrict__ partials,
-                                   float* __restrict__ lse) {
+// One thread per query row (adjacent rows read adjacent partials): the
+// chunks' (max, sum) pairs (log2 domain) merged online in chunk order, eight
+// loads in flight at a time; the row's LSE in natural-log units.
+__global__ __launch_bounds__(256) void lse_combine_kernel(WindowParams p, int n_chunks,
+                                                          const float2* __restrict__ partials,
+                                                          float* __restrict__ lse) {
+  constexpr int kBatch = 8;
   const int R = p.G * p.W;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t n = static_cast<int64_t>(p.L) * p.Hkv * R;
   if (i >= n) return;
   const int64_t u = i / R;
   const int r = static_cast<int>(i % R);
-  float m = -INFINITY;
-  for (int c = 0; c < n_chunks; ++c) m = fmaxf(m, partials[(u * n_chunks + c) * R + r].x);
-  float s = 0.f;
-  for (int c = 0; c < n_chunks; ++c) {
-    const float2 v = partials[(u * n_chunks + c) * R + r];
-    s += (v.x == -INFINITY) ? 0.f : v.y * exp2f(v.x - m);
+  const float2* pr = partials + u * n_chunks * R + r;
+  float m = -INFINITY, s = 0.f;
+  for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+    float2 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      v[j] = (c0 + j < n_chunks) ? pr[static_cast<int64_t>(c0 + j) * R] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (v[j].x == -INFINITY) continue;
+      const float mn = fmaxf(m, v[j].x);
+      s = ((m == -INFINITY) ? 0.f : s * exp2f(m - mn)) + v[j].y * exp2f(v[j].x - mn);
+      m = mn;
+    }
   }
   const int l = static_cast<int>(u / p.Hkv), g = static_cast<int>(u % p.Hkv);
   const int h = g * p.G + r / p.W, t = r % p.W;
@@ -560,6 +632,46 @@ hipError_t launch_window_lse_mfma(const WindowParams& p, int dt, const void* q, 
   const int64_t n = static_cast<int64_t>(U) * p.G * p.W;
   lse_combine_kernel<<<static_cast<int>(ceil_div(n, 256)), 256, 0, st>>>(p, n_chunks, part, lse);
   return hipGetLastError();
+}
+
+// Keys per wavefront of the VALU LSE pass: 64, or more so that there are at
+// most 256 chunks per unit.
+static int lse_valu_chunk_keys(const WindowParams& p) {
+  const int64_t c = ceil_div(ceil_div(p.N, 256), 64) * 64;
+  return static_cast<int>(max(static_cast<int64_t>(64), c));
+}
+
+size_t window_valu_partials_bytes(const WindowParams& p) {
+  const int64_t n_chunks = ceil_div(p.N, lse_valu_chunk_keys(p));
+  return static_cast<size_t>(p.L) * p.Hkv * n_chunks * p.G * p.W * sizeof(float2);
+}
+
+template <int DT, int D>
+static hipError_t launch_lse_valu_t(const WindowParams& p, const void* q, const void* k, float2* part,
+                                    float* lse, hipStream_t st) {
+  const int ck = lse_valu_chunk_keys(p);
+  const int n_chunks = static_cast<int>(ceil_div(p.N, ck));
+  const int U = p.L * p.Hkv;
+  const int groups = static_cast<int>(ceil_div(static_cast<int64_t>(p.G) * p.W, kLseValuRowGroup));
+  lse_valu_kernel<DT, D><<<dim3(n_chunks, groups, U), 64, 0, st>>>(p, q, k, ck, part);
+  hipError_t e = hipGetLastError();
+  if (e != hipSuccess) return e;
+  const int64_t n = static_cast<int64_t>(U) * p.G * p.W;
+  lse_combine_kernel<<<static_cast<int>(ceil_div(n, 256)), 256, 0, st>>>(p, n_chunks, part, lse);
+  return hipGetLastError();
+}
+
+hipError_t launch_window_lse_valu(const WindowParams& p, int dt, const void* q, const void* k,
+                                  float* partials, float* lse, hipStream_t st) {
+  if (p.N == 0 || p.L * p.Hkv == 0) return hipSuccess;
+  float2* part = reinterpret_cast<float2*>(partials);
+#define KVSEL_LV(DTV)                                                                   \
+  return (p.D == 64) ? launch_lse_valu_t<DTV, 64>(p, q, k, part, lse, st)               \
+                     : launch_lse_valu_t<DTV, 128>(p, q, k, part, lse, st)
+  if (dt == KVSEL_F32) { KVSEL_LV(KVSEL_F32); }
+  if (dt == KVSEL_BF16) { KVSEL_LV(KVSEL_BF16); }
+  KVSEL_LV(KVSEL_F16);
+#undef KVSEL_LV
 }
 
 hipError_t launch_window_scores_mfma(const WindowParams& p, int dt, const void* q, const void* k,

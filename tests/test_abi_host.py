@@ -85,13 +85,21 @@ def test_select_validation_errors_without_device():
     assert _status(lib.kvsel_select_workspace, _select_args(n_sink=6, n_recent=5), ctypes.byref(nb)) \
         == _abi.KVSEL_E_BUDGET
     assert b"exceeds" in lib.kvsel_last_error()
+    # short rows: one workgroup per unit makes its own keys, no workspace
     assert _status(lib.kvsel_select_workspace, _select_args(), ctypes.byref(nb)) == _abi.KVSEL_OK
-    # an untiled call keeps one 4-byte key per position in the workspace
-    assert nb.value >= 100 * 4
-    assert _status(lib.kvsel_select, _select_args(), None, ctypes.c_size_t(0), None) == _abi.KVSEL_E_WORKSPACE
+    assert nb.value == 0
+    # longer rows over few units keep one 4-byte key per position in the workspace
+    long_rows = dict(n=10000, row_stride=10000, n_total=10000)
+    assert _status(lib.kvsel_select_workspace, _select_args(**long_rows), ctypes.byref(nb)) == _abi.KVSEL_OK
+    assert nb.value >= 10000 * 4
+    assert _status(lib.kvsel_select, _select_args(**long_rows), None, ctypes.c_size_t(0), None) \
+        == _abi.KVSEL_E_WORKSPACE
     assert b"workspace" in lib.kvsel_last_error()
-    assert _status(lib.kvsel_select, _select_args(), ctypes.c_void_p(0x10000), ctypes.c_size_t(nb.value - 1),
-                   None) == _abi.KVSEL_E_WORKSPACE
+    assert _status(lib.kvsel_select, _select_args(**long_rows), ctypes.c_void_p(0x10000),
+                   ctypes.c_size_t(nb.value - 1), None) == _abi.KVSEL_E_WORKSPACE
+    # a pooled or slot-mapped call over short rows keeps the two launches
+    assert _status(lib.kvsel_select_workspace, _select_args(pool=_abi.POOL["max"], pool_k=3),
+                   ctypes.byref(nb)) == _abi.KVSEL_OK and nb.value >= 100 * 4
     # a tile of a tiled call whose running set and tile fit in LDS needs none;
     # a tile too wide for the LDS bitmap takes the two-launch path and does
     tiled = dict(cand_score=0x3000, cand_idx=0x4000, cand_count=0x5000, n=60, n_total=100, base=40)
