@@ -116,7 +116,7 @@ __device__ uint32_t block_sum(uint32_t v, uint32_t* scratch) {
 
 // Block-wide sums of three per-thread values with one exchange (all threads
 // must call).  scratch holds 3 * kWaves words.
-__device__ uint3 block_sum3(uint32_t a, uint32_t b, uint32_t c, uint32_t* scratch) {
+__device__ uint3 block_sum3(uint32_t a, uint32_t b, uint32_t c, uint32_t* scratch, int nw = kWaves) {
   const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
   for (int o = 32; o > 0; o >>= 1) {
     a += __shfl_xor(a, o, 64);
@@ -126,15 +126,15 @@ __device__ uint3 block_sum3(uint32_t a, uint32_t b, uint32_t c, uint32_t* scratc
   __syncthreads();
   if (lane == 0) {
     scratch[wave] = a;
-    scratch[kWaves + wave] = b;
-    scratch[2 * kWaves + wave] = c;
+    scratch[nw + wave] = b;
+    scratch[2 * nw + wave] = c;
   }
   __syncthreads();
   uint3 t = make_uint3(0u, 0u, 0u);
-  for (int w = 0; w < kWaves; ++w) {
+  for (int w = 0; w < nw; ++w) {
     t.x += scratch[w];
-    t.y += scratch[kWaves + w];
-    t.z += scratch[2 * kWaves + w];
+    t.y += scratch[nw + w];
+    t.z += scratch[2 * nw + w];
   }
   return t;
 }
@@ -493,14 +493,16 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
 // Per-unit selection over keys held in registers.  Wavefront w owns the
 // contiguous segment [w*seg, (w+1)*seg) of the unit in rows of 64 columns
 // (KPT rows), so the ballot sweeps see columns in ascending order.  Requires
-// n <= KPT * kThreads.  With kFused (unpooled calls) the keys are made here
+// n <= KPT * NT (NT threads per workgroup: 1024, or 256 for short rows,
+// whose barriers then wait on 4 wavefronts instead of 16).  With kFused (unpooled calls) the keys are made here
 // from the score row and the first radix pass runs here too; otherwise they
 // come prepared, with the slices' top-byte histograms, from
 // select_keys_kernel.
-template <int KPT, bool kFused>
-__global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, const float* scores,
+template <int KPT, bool kFused, int NT>
+__global__ __launch_bounds__(NT) void select_regs_kernel(SelectParams p, const float* scores,
                                                                const uint32_t* keys,
                                                                const uint32_t* hist, int n_slices) {
+  constexpr int NW = NT / 64;
   __shared__ SelShared sh;
   const int u = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
@@ -513,14 +515,14 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
 
   // ---- alive forced positions, top-byte histogram, candidate count
   uint32_t fs = 0, fr = 0, cc = 0;
-  for (int g = tid; g < sink_end; g += kThreads) fs += alive(g) ? 1u : 0u;
-  for (int g = rec_begin + tid; g < n; g += kThreads) fr += alive(g) ? 1u : 0u;
-  const int seg = ((n + kWaves - 1) / kWaves + 63) / 64 * 64;
+  for (int g = tid; g < sink_end; g += NT) fs += alive(g) ? 1u : 0u;
+  for (int g = rec_begin + tid; g < n; g += NT) fr += alive(g) ? 1u : 0u;
+  const int seg = ((n + NW - 1) / NW + 63) / 64 * 64;
   const int s_beg = min(n, wave * seg);
   const int s_end = min(n, s_beg + seg);
   uint32_t kr[KPT];
   if constexpr (!kFused) {
-    for (int b = tid; b < 256; b += kThreads) {
+    for (int b = tid; b < 256; b += NT) {
       uint32_t t = 0;
       for (int sl = 0; sl < n_slices; ++sl) t += hist[(static_cast<int64_t>(u) * n_slices + sl) * 256 + b];
       sh.hist[b] = t;
@@ -534,7 +536,7 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
       kr[i] = (e < s_end) ? ku[e] : 0u;
     }
   } else {
-    for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0u;
+    for (int b = tid; b < 256; b += NT) sh.hist[b] = 0u;
     const float* row = scores + static_cast<int64_t>(u) * p.row_stride;
     // unconditional loads (a clamped column past the segment) keep all KPT
     // in flight; a conditional load would wait for each one in turn
@@ -554,7 +556,7 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
       kr[i] = key;
     }
   }
-  const uint3 sums = block_sum3(fs, fr, cc, sh.wave_sums);
+  const uint3 sums = block_sum3(fs, fr, cc, sh.wave_sums, NW);
   const uint32_t fsum = sums.x, rsum = sums.y, n_cand = sums.z;
   const int32_t room = p.k_total - static_cast<int32_t>(fsum + rsum);
 
@@ -578,7 +580,7 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
     for (int shift = 16; shift >= 0; shift -= 8) {
       const uint32_t hi_mask = 0xFFFFFFFFu << (shift + 8);
       const uint32_t prefix = sh.prefix;
-      for (int b = tid; b < 256; b += kThreads) sh.hist[b] = 0u;
+      for (int b = tid; b < 256; b += NT) sh.hist[b] = 0u;
       __syncthreads();
 #pragma unroll
       for (int i = 0; i < KPT; ++i) {
@@ -609,7 +611,7 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
   uint32_t eq_base = 0, sel_base = 0, n_sel_total = 0;
   {
     uint32_t eb = 0;
-    for (int w = 0; w < kWaves; ++w) {
+    for (int w = 0; w < NW; ++w) {
       const int32_t take_eq = max(0, min(static_cast<int32_t>(sh.wave_eq[w]), remaining - static_cast<int32_t>(eb)));
       if (w == wave) {
         eq_base = eb;
@@ -664,7 +666,7 @@ __global__ __launch_bounds__(kThreads) void select_regs_kernel(SelectParams p, c
     }
   }
   const int64_t total = static_cast<int64_t>(fsum) + n_sel_total + rsum;
-  for (int64_t i = total + tid; i < p.k_total; i += kThreads) kept[i] = -1;
+  for (int64_t i = total + tid; i < p.k_total; i += NT) kept[i] = -1;
   if (tid == 0 && p.n_kept != nullptr) p.n_kept[u] = static_cast<int32_t>(total);
 }
 
@@ -696,7 +698,8 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
     const int n_slices = static_cast<int>(ceil_div(p.n, kPrepKeys));
     uint32_t* hist = keys + (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 64;
     if (select_single_launch(p)) {
-      select_regs_kernel<32, true><<<p.U, kThreads, 0, st>>>(p, scores, nullptr, nullptr, 0);
+      if (p.n <= 8 * 256) select_regs_kernel<8, true, 256><<<p.U, 256, 0, st>>>(p, scores, nullptr, nullptr, 0);
+      else select_regs_kernel<32, true, kThreads><<<p.U, kThreads, 0, st>>>(p, scores, nullptr, nullptr, 0);
       return hipGetLastError();
     }
     if (n_slices > 0) {
@@ -706,7 +709,7 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
     // up to 32 keys per thread stay in registers; larger units stream their
     // keys from the workspace (64 per thread no longer fit without spilling)
     if (p.n <= 32 * kThreads)
-      select_regs_kernel<32, false><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
+      select_regs_kernel<32, false, kThreads><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
     else
       select_kernel<kPrepared><<<p.U, kThreads, 0, st>>>(p, scores, keys, hist, n_slices);
     return hipGetLastError();
