@@ -45,8 +45,9 @@ def _check(s, kept, mask, nk, k, n_sink, n_recent, alive=None):
 
 
 @pytest.mark.parametrize("U,n,k,n_sink,n_recent,ties", [
-    (3, 1000, 100, 4, 64, False),        # ragged, several tiles of 64
-    (5, 2048, 512, 4, 64, True),         # ties and signed zeros
+    (3, 1000, 100, 4, 64, False),        # ragged, several tiles of 64 (256-thread single launch)
+    (5, 2048, 512, 4, 64, True),         # ties and signed zeros; the longest 256-thread row
+    (2, 5000, 700, 3, 9, True),          # few units of a short row: the 1024-thread single launch
     (4, 32768, 8192, 4, 256, False),     # 32 keys per thread in registers, full per-unit size
     (2, 40000, 5000, 3, 7, True),        # beyond 32 keys per thread: keys streamed from the workspace
     (2, 65536, 20000, 4, 64, True),      # the session-memory unit size
