@@ -6,8 +6,8 @@ x 312500 32-token blocks (fp16, D 128) scored in 65536-block tiles for 4
 sessions with independent 512-token queries, a running top-4096 per
 (session, layer, KV head) with block 0 and the last 4 blocks forced, and the
 in-place incremental update of each session's 4096-page view (about half the
-blocks reused in their pages, moved ones rotated in place; misses re-RoPEd
-from the HBM-resident raw store).  One step is all of that over one batch of seeded synthetic inputs
+blocks reused in their pages; moved ones and misses re-RoPEd from the
+HBM-resident raw store at their new positions).  One step is all of that over one batch of seeded synthetic inputs
 resident in HBM before timing starts.
 
 Prints one JSON line.  Per-stage times come from HIP events recorded on the
@@ -641,7 +641,9 @@ class KVMem10M:
     """Scale-out block retrieval: a 10M-token Mean-K index scored in
     65536-block tiles for 4 sessions with a running tiled top-4096, then the
     in-place incremental update of each session's 4096-page view (the
-    previous view shares about half its blocks with the new selection).
+    previous view shares about half its blocks with the new selection;
+    misses and moved hits are re-RoPEd from the raw store at their new
+    positions, V is copied for misses only).
     Tiles after the first are scored in the packed form: only the blocks
     above their running set's smallest score are written (the selection's
     admission threshold), with a bit mask.  The previous-view lists are
@@ -741,7 +743,7 @@ class KVMem10M:
         self.inc_ws = kv.gather_incremental(self.raw_k, self.raw_v, self.kept, self.prev_idx, self.prev_page,
                                             self.pool_k, self.pool_v, self.pt, self.nm, bt=cfg.bt, D=cfg.D,
                                             src_rows=NB * cfg.bt, src_offsets=self.offs, rope="raw",
-                                            theta=cfg.theta, workspace=self.inc_ws)
+                                            theta=cfg.theta, hit_raw=True, workspace=self.inc_ws)
         ev[2].record(stream)
 
     def _moves(self):
@@ -776,8 +778,8 @@ class KVMem10M:
         """Whole (session, unit) views in a seeded order: the query reduction,
         block scores over all 312500 blocks, the top-4096 (the tiled selection
         is defined equal to the untiled one, so the oracle selects once), and
-        the incremental update of that view (misses re-RoPEd from raw K, moved
-        hits rotated in place)."""
+        the incremental update of that view (misses and moved hits re-RoPEd
+        from raw K at their new positions)."""
         import numpy as np
         from oracle import materialise as om
         from oracle import numerics
@@ -805,7 +807,7 @@ class KVMem10M:
             pk, pv = _np64(self.pool_k[i]), _np64(self.pool_v[i])
             b0 = clock.busy
             clock.run(om.incremental_view, np.searchsorted(need, self.prev_idx_h[i]), prev_page[i],
-                      np.searchsorted(need, kept), pk, pv, rk, rv, bt, theta=cfg.theta)
+                      np.searchsorted(need, kept), pk, pv, rk, rv, bt, theta=cfg.theta, hits="raw")
             t_update += clock.busy - b0
             done += 1
             if clock.spent():
@@ -818,7 +820,8 @@ class KVMem10M:
         cfg = self.cfg
         return {"workload": "kvmem 10M-token scale-out retrieval: 64 layers x 8 KV heads, 312500 32-token "
                             "blocks per unit scored in 65536-block tiles for 4 sessions, tiled top 4096, "
-                            "in-place incremental update of 4096-page views with about half the blocks reused",
+                            "in-place incremental update of 4096-page views with about half the blocks reused "
+                            "(misses and moved hits re-RoPEd from raw K)",
                 "units": cfg.U, "sessions": cfg.S, "blocks_per_unit": cfg.N, "budget_blocks": cfg.k}
 
     def extra(self):

@@ -176,15 +176,14 @@ def test_kvmem_10m_workload_full_size():
     """312500 blocks per unit scored in 65536-block tiles for 4 sessions,
     tiled top-4096, and the in-place incremental update of each session's
     4096-page view (previous view shares about half its blocks; moved hits
-    rotated in place), in the
-    launch sequence the benchmark times (tiles after the first scored in the
-    packed form under the running sets' admission thresholds; they are also
-    scored densely to hold every score to the oracle and each packed row to
-    its dense one).  64 (session, unit) views drawn in
-    a seeded order are checked against the oracle: their scores over every
-    tile, their kept blocks, and on the bit-exact ones the whole updated view
-    (page table, re-RoPEd misses, hits rotated in place, V).  Invariants hold
-    for every view."""
+    re-rotated from raw K at their new positions), in the launch sequence
+    the benchmark times (tiles after the first scored in the packed form
+    under the running sets' admission thresholds; they are also scored
+    densely to hold every score to the oracle and each packed row to its
+    dense one).  64 (session, unit) views drawn in a seeded order are
+    checked against the oracle: their scores over every tile, their kept
+    blocks, and on the bit-exact ones the whole updated view (page table,
+    re-RoPEd misses and moved hits, V).  Invariants hold for every view."""
     dev = require_gpu()
     cfg = wl.CONFIGS["kvmem10m"]
     S, U, NB, k, D, bt, tile = cfg.S, cfg.U, cfg.N, cfg.k, cfg.D, cfg.bt, cfg.tile
@@ -317,7 +316,7 @@ def test_kvmem_10m_workload_full_size():
     nm = torch.empty(SU, dtype=torch.int32, device=dev)
     kv.gather_incremental(raw_k, raw_v, kept, torch.from_numpy(prev_idx).to(dev),
                           torch.from_numpy(prev_page).to(dev), pool_k, pool_v, pt, nm, bt=bt, D=D,
-                          src_rows=NB * bt, src_offsets=offs, rope="raw", theta=cfg.theta)
+                          src_rows=NB * bt, src_offsets=offs, rope="raw", theta=cfg.theta, hit_raw=True)
     torch.cuda.synchronize()
     pt_h, nm_h = pt.cpu().numpy(), nm.cpu().numpy()
     assert 0.4 * k < nm_h.mean() < 0.6 * k                 # about half the view is new
@@ -325,7 +324,7 @@ def test_kvmem_10m_workload_full_size():
     for (s, u), (pk, pv, rk, rv, prev_r, new_r) in baked.items():
         i = s * U + u
         ok, ov, opt, onm = om.incremental_view(prev_r, prev_page[i], new_r, pk, pv, rk, rv, bt,
-                                               theta=cfg.theta)
+                                               theta=cfg.theta, hits="raw")
         assert nm_h[i] == onm
         np.testing.assert_array_equal(pt_h[i], opt)
         np.testing.assert_array_equal(f64(pool_v[i]), ov)
