@@ -188,12 +188,23 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
   const int64_t item_bytes = row_bytes * p.bt;
   const int passes = (p.bt + rows_per_pass - 1) / rows_per_pass;
 
+  // the next item's plan entries are loaded while the current item moves
+  int32_t page_n = 0, io_n = 0, blk_n = 0;
+  if (wave_global < items) {
+    page_n = page_table[wave_global];
+    io_n = plan_old[wave_global];
+    blk_n = idx[wave_global];
+  }
   for (int64_t it = wave_global; it < items; it += n_waves) {
     const int u = static_cast<int>(it / p.k);
     const int64_t i = it - static_cast<int64_t>(u) * p.k;
-    const int32_t page = page_table[it];
+    const int32_t page = page_n, io = io_n, blk = blk_n;
+    if (it + n_waves < items) {
+      page_n = page_table[it + n_waves];
+      io_n = plan_old[it + n_waves];
+      blk_n = idx[it + n_waves];
+    }
     if (page < 0 || page >= p.pool_pages) continue;
-    const int32_t io = plan_old[it];
     uint8_t* pk = static_cast<uint8_t*>(pool_k) + (static_cast<int64_t>(u) * p.pool_pages + page) * item_bytes;
     uint8_t* pv = static_cast<uint8_t*>(pool_v) + (static_cast<int64_t>(u) * p.pool_pages + page) * item_bytes;
     const bool hit = io >= 0;
@@ -207,7 +218,7 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
     const uint8_t* sk = nullptr;
     const uint8_t* sv = nullptr;
     if (hit && p.hit_raw) {
-      const int32_t b = idx[it];
+      const int32_t b = blk;
       if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
       const int64_t soff = p.src_offsets ? p.src_offsets[u] : static_cast<int64_t>(u) * p.src_unit_stride;
       sk = static_cast<const uint8_t*>(p.hit_src) + soff * esz + static_cast<int64_t>(b) * item_bytes;
@@ -219,7 +230,7 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
       sk = static_cast<const uint8_t*>(src_k) + e * item_bytes;
       sv = static_cast<const uint8_t*>(src_v) + e * item_bytes;
     } else if (!hit) {
-      const int32_t b = idx[it];
+      const int32_t b = blk;
       if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
       const int64_t soff = p.src_offsets ? p.src_offsets[u] : static_cast<int64_t>(u) * p.src_unit_stride;
       sk = static_cast<const uint8_t*>(src_k) + soff * esz + static_cast<int64_t>(b) * item_bytes;
