@@ -200,10 +200,8 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
 #pragma unroll
             for (int e = 0; e < NP; e += 2) {
               const float4 t = t4[e / 2];
-              cs[e] = cb[e] * t.x - sb[e] * t.y;
-              sn[e] = sb[e] * t.x + cb[e] * t.y;
-              cs[e + 1] = cb[e + 1] * t.z - sb[e + 1] * t.w;
-              sn[e + 1] = sb[e + 1] * t.z + cb[e + 1] * t.w;
+              add_angles(cb[e], sb[e], t.x, t.y, &cs[e], &sn[e]);
+              add_angles(cb[e + 1], sb[e + 1], t.z, t.w, &cs[e + 1], &sn[e + 1]);
             }
           } else {
 #pragma unroll

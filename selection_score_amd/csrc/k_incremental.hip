@@ -18,7 +18,10 @@
 // plan kernel: one workgroup per unit.  Membership by binary search over the
 // two ascending index lists staged in LDS; freed pages ordered by a bitmap
 // over page ids and a prefix count of its words; misses ranked with a
-// ballot prefix.  data kernel: one wavefront per (unit, kept entry).
+// ballot prefix.  data kernel: one wavefront per (kept entry, K or V): a
+// miss's V copy and its K rotation go to different wavefronts, so each holds
+// 4 row passes of one stream in flight and the kernel runs 4 wavefronts per
+// SIMD (both measured faster than one wavefront moving K and V together).
 #include "rope_dev.h"
 
 namespace kvsel {
@@ -160,7 +163,7 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
   constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
   constexpr int E = Vec16<DT>::kElems;
   constexpr int NP = kInter ? E / 2 : E;     // pairs touched by this lane
-  constexpr int kBatch = 8;                  // row passes whose loads are in flight together
+  constexpr int kBatch = 4;                  // row passes whose loads are in flight together
   __shared__ float2 off_tab[kMaxOffTable];
   const int half = p.D / 2;
   if constexpr (kRot) {
@@ -188,21 +191,24 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
   const int64_t item_bytes = row_bytes * p.bt;
   const int passes = (p.bt + rows_per_pass - 1) / rows_per_pass;
 
-  // the next item's plan entries are loaded while the current item moves
+  // work item tt: entry tt / 2, its K (even) or V (odd).  The next item's
+  // plan entries are loaded while the current item moves.
   int32_t page_n = 0, io_n = 0, blk_n = 0;
-  if (wave_global < items) {
-    page_n = page_table[wave_global];
-    io_n = plan_old[wave_global];
-    blk_n = idx[wave_global];
+  if (wave_global < 2 * items) {
+    page_n = page_table[wave_global >> 1];
+    io_n = plan_old[wave_global >> 1];
+    blk_n = idx[wave_global >> 1];
   }
-  for (int64_t it = wave_global; it < items; it += n_waves) {
+  for (int64_t tt = wave_global; tt < 2 * items; tt += n_waves) {
+    const int64_t it = tt >> 1;
+    const bool vhalf = (tt & 1) != 0;
     const int u = static_cast<int>(it / p.k);
     const int64_t i = it - static_cast<int64_t>(u) * p.k;
     const int32_t page = page_n, io = io_n, blk = blk_n;
-    if (it + n_waves < items) {
-      page_n = page_table[it + n_waves];
-      io_n = plan_old[it + n_waves];
-      blk_n = idx[it + n_waves];
+    if (tt + n_waves < 2 * items) {
+      page_n = page_table[(tt + n_waves) >> 1];
+      io_n = plan_old[(tt + n_waves) >> 1];
+      blk_n = idx[(tt + n_waves) >> 1];
     }
     if (page < 0 || page >= p.pool_pages) continue;
     uint8_t* pk = static_cast<uint8_t*>(pool_k) + (static_cast<int64_t>(u) * p.pool_pages + page) * item_bytes;
@@ -236,6 +242,27 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
       sk = static_cast<const uint8_t*>(src_k) + soff * esz + static_cast<int64_t>(b) * item_bytes;
       sv = static_cast<const uint8_t*>(src_v) + soff * esz + static_cast<int64_t>(b) * item_bytes;
     }
+    if (vhalf) {
+      // V: copied for a miss, untouched for a hit
+      if (hit) continue;
+      for (int q0 = 0; q0 < passes; q0 += kBatch) {
+        uint4 vv[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int o = (q0 + j) * rows_per_pass + rsub;
+          vv[j] = make_uint4(0, 0, 0, 0);
+          if (q0 + j < passes && o < p.bt)
+            vv[j] = *reinterpret_cast<const uint4*>(sv + static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int o = (q0 + j) * rows_per_pass + rsub;
+          if (q0 + j < passes && o < p.bt)
+            store16_stream(pv + static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz, vv[j]);
+        }
+      }
+      continue;
+    }
     float cb[NP], sb[NP];
     if constexpr (kRot) {
       float cl = 1.f, sl = 0.f;
@@ -247,32 +274,17 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
       }
     }
     for (int q0 = 0; q0 < passes; q0 += kBatch) {
-      uint4 kv[kBatch], vv[kBatch];
+      uint4 kv[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int o = (q0 + j) * rows_per_pass + rsub;
         kv[j] = make_uint4(0, 0, 0, 0);
-        vv[j] = make_uint4(0, 0, 0, 0);
         if (q0 + j < passes && o < p.bt) {
           const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-          if (!from_src) {
-            kv[j] = *reinterpret_cast<const uint4*>(pk + off);
-          } else {
-            kv[j] = *reinterpret_cast<const uint4*>(sk + off);
-            if (!hit) vv[j] = *reinterpret_cast<const uint4*>(sv + off);
-          }
+          kv[j] = *reinterpret_cast<const uint4*>((from_src ? sk : pk) + off);
         }
       }
-      if (!hit) {
-#pragma unroll
-        for (int j = 0; j < kBatch; ++j) {
-          const int o = (q0 + j) * rows_per_pass + rsub;
-          if (q0 + j < passes && o < p.bt) {
-            const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-            store16_stream(pv + off, vv[j]);
-          }
-        }
-      }
+
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         if (q0 + j >= passes) break;                    // uniform
@@ -292,10 +304,8 @@ __global__ __launch_bounds__(256) void incremental_data_kernel(
 #pragma unroll
             for (int e = 0; e < NP; e += 2) {
               const float4 t = t4[e / 2];
-              cs[e] = cb[e] * t.x - sb[e] * t.y;
-              sn[e] = sb[e] * t.x + cb[e] * t.y;
-              cs[e + 1] = cb[e + 1] * t.z - sb[e + 1] * t.w;
-              sn[e + 1] = sb[e + 1] * t.z + cb[e + 1] * t.w;
+              add_angles(cb[e], sb[e], t.x, t.y, &cs[e], &sn[e]);
+              add_angles(cb[e + 1], sb[e + 1], t.z, t.w, &cs[e + 1], &sn[e + 1]);
             }
           }
           out = rotate16<DT, kInter>(kv[j], other, sgn, cs, sn);

@@ -115,6 +115,14 @@ __device__ __forceinline__ uint4 rotate_chunk(const uint4& own, const uint4& oth
 // holds dims [d0, d0+E) of one half, `other` the matching dims of the other
 // half, and `sgn` is -1 for the first half (x_m c - x_{m+D/2} s) and +1 for
 // the second (x_{m+D/2} c + x_m s).  Interleaved: pairs are adjacent in `own`.
+// cos and sin of a + b from those of a and b (angle addition), each with
+// one rounded product and one fused multiply-add in a fixed order, so the
+// bits do not depend on how the compiler contracts the expression.
+__device__ __forceinline__ void add_angles(float ca, float sa, float cb, float sb, float* c, float* s) {
+  *c = fmaf(ca, cb, -(sa * sb));
+  *s = fmaf(sa, cb, ca * sb);
+}
+
 template <int DT, bool kInter>
 __device__ __forceinline__ uint4 rotate16(const uint4& own, const uint4& other, float sgn, const float* c,
                                           const float* s) {
@@ -123,8 +131,8 @@ __device__ __forceinline__ uint4 rotate16(const uint4& own, const uint4& other, 
   unpack16<DT>(own, a);
   if constexpr (kInter) {
     for (int i = 0; i < E; i += 2) {
-      y[i] = a[i] * c[i / 2] - a[i + 1] * s[i / 2];
-      y[i + 1] = a[i] * s[i / 2] + a[i + 1] * c[i / 2];
+      y[i] = fmaf(a[i], c[i / 2], -(a[i + 1] * s[i / 2]));
+      y[i + 1] = fmaf(a[i], s[i / 2], a[i + 1] * c[i / 2]);
     }
   } else {
     float b[E];
