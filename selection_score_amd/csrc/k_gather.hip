@@ -7,7 +7,10 @@
 // Two kernels:
 //  * rows: one row (D elements) per group of D*esz/16 lanes, 16 bytes per
 //    lane.  Any bt; RoPE angles computed per lane.  Used for token gathers.
-//  * blocks: one wavefront per (unit, kept entry) of bt >= 8 rows with RoPE.
+//  * blocks: one wavefront per (kept entry, K or V) of bt >= 8 rows with
+//    RoPE: the V copy and the K rotation of an entry go to different
+//    wavefronts (measured 11 % faster than one wavefront moving both; for
+//    single rows the split measured slower, so the rows kernel keeps both).
 //    The rotation of row o at base position b is composed from a per-entry
 //    base rotation (one sincos per frequency and lane) and a per-workgroup
 //    table of the offsets o (angle addition), so trigonometry is amortised
@@ -116,7 +119,7 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
   constexpr int esz = (DT == KVSEL_F32) ? 4 : 2;
   constexpr int E = Vec16<DT>::kElems;
   constexpr int NP = kInter ? E / 2 : E;     // pairs touched by this lane
-  constexpr int kBatch = 8;                  // row passes whose loads are in flight together
+  constexpr int kBatch = 8;                 // row passes whose loads are in flight together
   __shared__ float2 off_tab[kMaxOffTable];   // (cos, sin) of o * inv_freq[m], [o][m]
   const int half = p.D / 2;
   if constexpr (kRaw) {
@@ -146,16 +149,38 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
   const int64_t item_bytes = row_bytes * p.bt;
   const int passes = (p.bt + rows_per_pass - 1) / rows_per_pass;
 
-  for (int64_t it = wave_global; it < items; it += n_waves) {
+  int32_t b_n = (wave_global < 2 * items) ? idx[wave_global >> 1] : 0;
+  for (int64_t tt = wave_global; tt < 2 * items; tt += n_waves) {
+    const int64_t it = tt >> 1;
     const int u = static_cast<int>(it / p.k);
     const int64_t i = it - static_cast<int64_t>(u) * p.k;
+    const int32_t b = b_n;
+    if (tt + n_waves < 2 * items) b_n = idx[(tt + n_waves) >> 1];
     if (n_idx != nullptr && i >= n_idx[u]) continue;
-    const int32_t b = idx[it];
     if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
+    if (tt & 1) {
+      const uint8_t* sv = unit_src(src_v, p, u, esz) + static_cast<int64_t>(b) * item_bytes;
+      uint8_t* dv = static_cast<uint8_t*>(dst_v) + it * item_bytes;
+      for (int q0 = 0; q0 < passes; q0 += kBatch) {
+        uint4 vv[kBatch];
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int o = (q0 + j) * rows_per_pass + rsub;
+          vv[j] = make_uint4(0, 0, 0, 0);
+          if (q0 + j < passes && o < p.bt)
+            vv[j] = *reinterpret_cast<const uint4*>(sv + static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz);
+        }
+#pragma unroll
+        for (int j = 0; j < kBatch; ++j) {
+          const int o = (q0 + j) * rows_per_pass + rsub;
+          if (q0 + j < passes && o < p.bt)
+            store16_stream(dv + static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz, vv[j]);
+        }
+      }
+      continue;
+    }
     const uint8_t* sk = unit_src(src_k, p, u, esz) + static_cast<int64_t>(b) * item_bytes;
-    const uint8_t* sv = unit_src(src_v, p, u, esz) + static_cast<int64_t>(b) * item_bytes;
     uint8_t* dk = static_cast<uint8_t*>(dst_k) + it * item_bytes;
-    uint8_t* dv = static_cast<uint8_t*>(dst_v) + it * item_bytes;
     // rotation of the item's base position: lane m evaluates frequency m once,
     // the lanes that need it read it across the wavefront
     const int64_t base_pos = kRaw ? p.pos0 + i * p.bt : p.pos0 + (i - b) * p.bt;
@@ -168,25 +193,13 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
       sb[e] = __shfl(sl, m0 + e, 64);
     }
     for (int q0 = 0; q0 < passes; q0 += kBatch) {
-      uint4 kv[kBatch], vv[kBatch];
+      uint4 kv[kBatch];
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
         const int o = (q0 + j) * rows_per_pass + rsub;
         kv[j] = make_uint4(0, 0, 0, 0);
-        vv[j] = make_uint4(0, 0, 0, 0);
-        if (q0 + j < passes && o < p.bt) {
-          const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-          kv[j] = *reinterpret_cast<const uint4*>(sk + off);
-          vv[j] = *reinterpret_cast<const uint4*>(sv + off);
-        }
-      }
-#pragma unroll
-      for (int j = 0; j < kBatch; ++j) {
-        const int o = (q0 + j) * rows_per_pass + rsub;
-        if (q0 + j < passes && o < p.bt) {
-          const int64_t off = static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz;
-          store16_stream(dv + off, vv[j]);
-        }
+        if (q0 + j < passes && o < p.bt)
+          kv[j] = *reinterpret_cast<const uint4*>(sk + static_cast<int64_t>(o) * row_bytes + static_cast<int64_t>(d0) * esz);
       }
 #pragma unroll
       for (int j = 0; j < kBatch; ++j) {
