@@ -305,7 +305,10 @@ __global__ __launch_bounds__(256) void memory_logits_mfma_kernel(MemoryParams p,
       const float4 v = *reinterpret_cast<const float4*>(&stage[hh * kRow + jj]);
       float* dst = logits + (static_cast<int64_t>(l) * p.Hq + hh) * p.N + j_begin + jj;
       if (jj + 3 < n_pos && (reinterpret_cast<uintptr_t>(dst) & 15) == 0) {
-        *reinterpret_cast<float4*>(dst) = v;
+        // non-temporal: the scratch (Hq * N floats per layer) is read back
+        // once per pass, and measured faster streamed past the caches
+        typedef float nt_f32x4 __attribute__((ext_vector_type(4)));
+        __builtin_nontemporal_store(nt_f32x4{v.x, v.y, v.z, v.w}, reinterpret_cast<nt_f32x4*>(dst));
       } else {
         const float vv[4] = {v.x, v.y, v.z, v.w};
         for (int i = 0; i < 4 && jj + i < n_pos; ++i) dst[i] = vv[i];
