@@ -65,6 +65,32 @@ def test_gather_rerope_matches_oracle(bt, rope, style, pos0):
         np.testing.assert_array_equal(f64(dv[u]), ov)
 
 
+@pytest.mark.parametrize("dtype,D,rope,style", [(torch.float16, 64, "raw", "interleaved"),
+                                               (torch.float32, 128, "delta", "half"),
+                                               (torch.float32, 64, "raw", "half"),
+                                               (torch.float16, 128, "delta", "interleaved")])
+def test_gather_blocks_dtypes(dtype, D, rope, style):
+    """The block gather (K rotation and V copy of an entry in separate
+    wavefronts) for fp16 and fp32 K/V and head dims 64 and 128."""
+    dev = require_gpu()
+    rnd = {torch.float16: numerics.round_to_f16, torch.float32: numerics.round_to_f32}[dtype]
+    rng = np.random.default_rng(D + len(rope) + len(style))
+    U, nb, k, bt = 4, 800, 97, 16
+    sk = rnd(rng.standard_normal((U, nb * bt, D)))
+    sv = rnd(rng.standard_normal((U, nb * bt, D)))
+    idx = _idx(rng, U, nb, k)
+    t = lambda x: torch.from_numpy(x.astype(np.float32)).to(dtype).to(dev)
+    dk = torch.empty((U, k * bt, D), dtype=dtype, device=dev)
+    dv = torch.empty_like(dk)
+    kv.gather_rerope(t(sk), t(sv), torch.from_numpy(idx).to(dev), dk, dv, bt=bt, D=D, src_rows=nb * bt,
+                     src_unit_stride=nb * bt * D, rope=rope, theta=1e6, pos0=9, style=style)
+    torch.cuda.synchronize()
+    for u in range(U):
+        ok, ov = om.gather_view(sk[u], sv[u], idx[u], bt, rope=rope, theta=1e6, pos0=9, style=style, out_round=rnd)
+        assert_rope_close(f64(dk[u]), ok, "unit %d" % u, style=style)
+        np.testing.assert_array_equal(f64(dv[u]), ov)
+
+
 def test_gather_zero_rotation_is_bitwise():
     # DELTA with every entry at its own position: R(0) must pass K through untouched
     dev = require_gpu()
@@ -106,6 +132,65 @@ def test_gather_aliased_sources_and_partial_counts():
             assert_rope_close(got_k[: m * bt], ok)
             np.testing.assert_array_equal(got_v[: m * bt], ov)
         assert np.all(got_k[m * bt:] == 3.0) and np.all(got_v[m * bt:] == 5.0)
+
+
+_ROUND = {torch.bfloat16: numerics.round_to_bf16, torch.float16: numerics.round_to_f16,
+          torch.float32: numerics.round_to_f32}
+
+
+@pytest.mark.parametrize("dtype,D,style,hits,pos0", [(torch.float16, 64, "interleaved", "raw", 0),
+                                                     (torch.float32, 128, "half", "delta", 300),
+                                                     (torch.bfloat16, 64, "interleaved", "delta", 17),
+                                                     (torch.float32, 64, "half", "raw", 5)])
+def test_incremental_view_dtypes_and_styles(dtype, D, style, hits, pos0):
+    """The incremental view (K and V of an entry moved by separate
+    wavefronts) for fp16/fp32/bf16 pools, head dims 64 and 128, both
+    rotation styles, a non-zero base position and both hit modes: page
+    table and V bit for bit, K within the re-RoPE bar (bf16's, which holds
+    the narrower formats too)."""
+    dev = require_gpu()
+    rnd = _ROUND[dtype]
+    rng = np.random.default_rng(D + len(style) + pos0)
+    U, nb, k, bt, spare = 3, 600, 64, 16, 6
+    P = k + spare
+    raw_k = rnd(rng.standard_normal((U, nb * bt, D)))
+    raw_v = rnd(rng.standard_normal((U, nb * bt, D)))
+    new_idx, prev_idx, prev_page = [], [], []
+    for u in range(U):
+        new = np.sort(rng.choice(nb, k, replace=False))
+        outside = np.setdiff1d(np.arange(nb), new)
+        prev = np.sort(np.concatenate([rng.choice(new, k // 2, replace=False),
+                                       rng.choice(outside, k - k // 2, replace=False)]))
+        new_idx.append(new)
+        prev_idx.append(prev)
+        prev_page.append(rng.permutation(P)[:k])
+    new_idx, prev_idx, prev_page = (np.stack(x).astype(np.int32) for x in (new_idx, prev_idx, prev_page))
+    o = np.arange(bt)
+    pool_k = rnd(rng.standard_normal((U, P, bt, D)))
+    pool_v = rnd(rng.standard_normal((U, P, bt, D)))
+    for u in range(U):
+        for i, b in enumerate(prev_idx[u]):
+            pool_k[u, prev_page[u, i]] = rnd(rope_rotate(raw_k[u, b * bt:(b + 1) * bt], pos0 + i * bt + o, 1e6,
+                                                         style=style))
+            pool_v[u, prev_page[u, i]] = raw_v[u, b * bt:(b + 1) * bt]
+    t = lambda x: torch.from_numpy(x.astype(np.float32)).to(dtype).to(dev)
+    rk_t, rv_t, pk, pv = t(raw_k), t(raw_v), t(pool_k), t(pool_v)
+    pt = torch.full((U, k), -5, dtype=torch.int32, device=dev)
+    nm = torch.zeros(U, dtype=torch.int32, device=dev)
+    kv.gather_incremental(rk_t, rv_t, torch.from_numpy(new_idx).to(dev), torch.from_numpy(prev_idx).to(dev),
+                          torch.from_numpy(prev_page).to(dev), pk, pv, pt, nm, bt=bt, D=D, src_rows=nb * bt,
+                          src_unit_stride=nb * bt * D, rope="raw", theta=1e6, pos0=pos0, style=style,
+                          hit_raw=hits == "raw")
+    torch.cuda.synchronize()
+    gk, gv, gpt, gnm = f64(pk), f64(pv), pt.cpu().numpy(), nm.cpu().numpy()
+    for u in range(U):
+        ok, ov, opt, onm = om.incremental_view(prev_idx[u], prev_page[u], new_idx[u], pool_k[u], pool_v[u],
+                                               raw_k[u].reshape(nb, bt, D), raw_v[u].reshape(nb, bt, D), bt,
+                                               theta=1e6, pos0=pos0, style=style, out_round=rnd, hits=hits)
+        assert gnm[u] == onm
+        np.testing.assert_array_equal(gpt[u], opt)
+        np.testing.assert_array_equal(gv[u], ov)
+        assert_rope_close(gk[u], ok, "unit %d" % u, style=style)
 
 
 @pytest.mark.parametrize("overlap,staged,hits", [(0.5, False, "delta"), (1.0, False, "delta"), (0.0, False, "delta"),
