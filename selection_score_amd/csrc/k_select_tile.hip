@@ -142,6 +142,14 @@ __device__ __forceinline__ uint32_t tile_key(const Tile& t, int j, float s) {
   return score_key(s);
 }
 
+// Key of tile column j of a tile without a slot map (in_row: j < n).
+__device__ __forceinline__ uint32_t dense_key(const Tile& t, bool in_row, int j, float s) {
+  const int g = t.base + j;
+  return (in_row && g >= t.sink_end && g < t.rec_begin) ? score_key(s) : 0u;
+}
+
+constexpr int kDenseBatch = 4;           // float4 loads in flight per thread on dense tiles
+
 // Calls f(j, key) for every tile column, key = 0 unless the column is a
 // candidate with key >= lo (lo >= 1), reading the row from global memory.
 // All lanes of a wavefront run the same number of iterations (f may use
@@ -150,7 +158,7 @@ __device__ __forceinline__ uint32_t tile_key(const Tile& t, int j, float s) {
 // admitted column's score sits at the rank of its bit among the chunk's
 // set bits.  Only admitted columns are visited; idle lanes call f with
 // column -1 and key 0.
-template <bool kPacked, typename F>
+template <bool kPacked, bool kFast = true, typename F>
 __device__ __forceinline__ void for_tile(const Tile& t, uint32_t lo, F&& f) {
   const int tid = threadIdx.x;
   if constexpr (kPacked) {
@@ -186,7 +194,30 @@ __device__ __forceinline__ void for_tile(const Tile& t, uint32_t lo, F&& f) {
     }
     return;
   }
-  if (t.vec) {
+  if (kFast && t.vec && t.slot_map == nullptr) {
+    // no slot map: a column's key depends on its position and score only,
+    // so it is formed without branches; the batch's loads are issued
+    // together (past the row they repeat its last 16 bytes, unused)
+    const float4* r4 = reinterpret_cast<const float4*>(t.row);
+    const int n4 = t.n / 4;
+    constexpr int kU = kDenseBatch;
+    for (int ib = 0; ib < n4; ib += kU * kT) {
+      float4 v[kU];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) v[q] = r4[min(ib + q * kT + tid, n4 - 1)];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        const int i = ib + q * kT + tid;
+        const float x[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int c = 0; c < 4; ++c) {
+          const int j = 4 * i + c;
+          const uint32_t key = dense_key(t, i < n4, j, x[c]);
+          f(j, key >= lo ? key : 0u);
+        }
+      }
+    }
+  } else if (t.vec) {
     const float4* r4 = reinterpret_cast<const float4*>(t.row);
     const int n4 = t.n / 4;
     constexpr int kU = 2;
@@ -218,22 +249,97 @@ __device__ __forceinline__ void for_tile(const Tile& t, uint32_t lo, F&& f) {
   }
 }
 
+// The tile's columns with key >= lo (lo >= 1) appended to the survivors
+// (skey, scol) from sh.n_surv on; those at or past cap are counted in
+// sh.n_surv but not stored.  With kHist their top-12-bit histogram is added
+// to sh.hist too.  The order of the survivors is unspecified.  All threads
+// call.
+template <bool kPacked, bool kHist>
+__device__ __forceinline__ void collect_tile(const Tile& t, uint32_t lo, TileShared& sh, uint32_t* skey,
+                                             int32_t* scol, int cap) {
+  const int tid = threadIdx.x, lane = tid & 63;
+  if (!kPacked && t.vec && t.slot_map == nullptr) {
+    // a batch of 4 * kDenseBatch columns per thread: one wavefront prefix
+    // sum and one LDS atomic per batch place the thread's survivors
+    const float4* r4 = reinterpret_cast<const float4*>(t.row);
+    const int n4 = t.n / 4;
+    constexpr int kU = kDenseBatch;
+    for (int ib = 0; ib < n4; ib += kU * kT) {
+      float4 v[kU];
+#pragma unroll
+      for (int q = 0; q < kU; ++q) v[q] = r4[min(ib + q * kT + tid, n4 - 1)];
+      uint32_t key[4 * kU];
+      uint32_t c = 0;
+#pragma unroll
+      for (int q = 0; q < kU; ++q) {
+        const int i = ib + q * kT + tid;
+        const float x[4] = {v[q].x, v[q].y, v[q].z, v[q].w};
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          uint32_t k = dense_key(t, i < n4, 4 * i + e, x[e]);
+          k = k >= lo ? k : 0u;
+          key[4 * q + e] = k;
+          c += k != 0u ? 1u : 0u;
+          if (kHist && k != 0u) atomicAdd(&sh.hist[k >> 20], 1u);
+        }
+      }
+      uint32_t incl = c;
+#pragma unroll
+      for (int o = 1; o < 64; o <<= 1) {
+        const uint32_t up = __shfl_up(incl, o, 64);
+        if (lane >= o) incl += up;
+      }
+      const uint32_t wtot = __shfl(incl, 63, 64);
+      if (wtot == 0u) continue;                          // uniform over the wavefront
+      uint32_t b = 0;
+      if (lane == 0) b = atomicAdd(&sh.n_surv, wtot);
+      uint32_t pos = __shfl(b, 0, 64) + incl - c;
+#pragma unroll
+      for (int e = 0; e < 4 * kU; ++e) {
+        if (key[e] != 0u) {
+          if (pos < static_cast<uint32_t>(cap)) {
+            skey[pos] = key[e];
+            scol[pos] = 4 * (ib + (e / 4) * kT + tid) + (e % 4);
+          }
+          ++pos;
+        }
+      }
+    }
+    return;
+  }
+  // one column per lane at a time: a ballot places the wavefront's survivors
+  for_tile<kPacked, false>(t, lo, [&](int j, uint32_t key) {
+    if (kHist && key != 0u) atomicAdd(&sh.hist[key >> 20], 1u);
+    const bool s = key != 0u;
+    const uint64_t m = __ballot(s);
+    if (m == 0ull) return;
+    uint32_t b = 0;
+    if (lane == 0) b = atomicAdd(&sh.n_surv, static_cast<uint32_t>(__popcll(m)));
+    b = __shfl(b, 0, 64);
+    const uint32_t pos = b + static_cast<uint32_t>(__popcll(m & lanemask_lt(lane)));
+    if (s && pos < static_cast<uint32_t>(cap)) {
+      skey[pos] = key;
+      scol[pos] = static_cast<int32_t>(j);
+    }
+  });
+}
+
 }  // namespace
 
-// dyn LDS: ckey[k_total] | skey[cap] | scol[cap] | bits[nw].  kPacked: the
-// tile is in the packed form (p.tile_mask).
+// dyn LDS: ckey[k_total] | 8 * cap_lds bytes | bits[nw].  The running
+// candidates' keys take ckey[0, c0); the survivors (key, column) take the
+// rest up to bits, so a call with fewer running candidates (the first tile)
+// holds more of them.  kPacked: the tile is in the packed form (p.tile_mask).
 template <bool kPacked>
 __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void select_tile_kernel(
-    SelectParams p, const float* scores, int cap) {
+    SelectParams p, const float* scores, int cap_lds) {
   extern __shared__ uint32_t dyn[];
   __shared__ TileShared sh;
   const int u = blockIdx.x;
   const int tid = threadIdx.x, lane = tid & 63;
   const int kcap = p.k_total;
   uint32_t* ckey = dyn;
-  uint32_t* skey = ckey + kcap;
-  int32_t* scol = reinterpret_cast<int32_t*>(skey + cap);
-  uint32_t* bits = reinterpret_cast<uint32_t*>(scol + cap);
+  uint32_t* bits = dyn + kcap + 2 * cap_lds;
   const int nw = static_cast<int>((p.n + 31) / 32);
 
   Tile t;
@@ -260,6 +366,11 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
 
   // ---- running candidates: keys to LDS (their indices are read at the end)
   const int c0 = min(max(p.cand_count[u], 0), max(room, 0));
+  // survivors after the c0 keys: [c0, c0 + cap) keys, then cap columns,
+  // ending at or before bits (c0 <= room <= k_total)
+  const int cap = cap_lds + (kcap - c0) / 2;
+  uint32_t* skey = ckey + c0;
+  int32_t* scol = reinterpret_cast<int32_t*>(skey + cap);
   const int cpt = (c0 + kT - 1) / kT;                       // <= kMaxCandPerThread
   const int e0 = min(c0, tid * cpt), e1 = min(c0, e0 + cpt);
   const int64_t cbase = static_cast<int64_t>(u) * kcap;
@@ -276,25 +387,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
   // ---- pass 1: survivors (key >= lo0) to LDS and the top-12-bit histogram
   uint32_t lo = lo0;
   for (int e = e0; e < e1; ++e) atomicAdd(&sh.hist[ckey[e] >> 20], 1u);
-  auto append = [&](int j, uint32_t key) {
-    const bool s = key != 0u;
-    const uint64_t m = __ballot(s);
-    if (m == 0ull) return;
-    uint32_t b = 0;
-    if (lane == 0) b = atomicAdd(&sh.n_surv, static_cast<uint32_t>(__popcll(m)));
-    b = __shfl(b, 0, 64);
-    const uint32_t pos = b + static_cast<uint32_t>(__popcll(m & lanemask_lt(lane)));
-    if (s && pos < static_cast<uint32_t>(cap)) {
-      skey[pos] = key;
-      scol[pos] = static_cast<int32_t>(j);
-    }
-  };
-  if (room > 0) {
-    for_tile<kPacked>(t, lo, [&](int j, uint32_t key) {
-      if (key != 0u) atomicAdd(&sh.hist[key >> 20], 1u);
-      append(j, key);
-    });
-  }
+  if (room > 0) collect_tile<kPacked, true>(t, lo, sh, skey, scol, cap);
   __syncthreads();
   uint32_t n_tile = sh.n_surv;                    // tile entries >= lo (may exceed cap)
   bool in_lds = n_tile <= static_cast<uint32_t>(cap);
@@ -355,7 +448,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
         lo = max(lo0, prefix);
         if (tid == 0) sh.n_surv = 0u;
         __syncthreads();
-        for_tile<kPacked>(t, lo, [&](int j, uint32_t key) { append(j, key); });
+        collect_tile<kPacked, false>(t, lo, sh, skey, scol, cap);
         __syncthreads();
         n_tile = sh.n_surv;
         in_lds = true;                            // n_tile <= n_above + in_bin <= cap
@@ -412,7 +505,7 @@ __global__ __launch_bounds__(kT) __attribute__((amdgpu_waves_per_eu(8, 8))) void
     if (in_lds) {
       for (uint32_t s = tid; s < n_tile; s += kT) f(scol[s], skey[s]);
     } else {
-      for_tile<kPacked>(t, lo, [&](int j, uint32_t key) {
+      for_tile<kPacked, false>(t, lo, [&](int j, uint32_t key) {
         if (key != 0u) f(j, key);
       });
     }

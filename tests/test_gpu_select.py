@@ -207,15 +207,21 @@ def _tiled(dev, s, k, n_sink, n_recent, tile, slot_map=None, dead_slot=0, stride
 
 
 @pytest.mark.parametrize("packed", [None, "exact", "low"])
-@pytest.mark.parametrize("case", ["equal", "ascending", "descending", "coarse", "dead", "k8192", "misaligned"])
+@pytest.mark.parametrize("case", ["equal", "ascending", "descending", "coarse", "dead", "k8192", "misaligned",
+                                  "bin5k", "bin9k"])
 def test_select_tiled_hard_cases(case, packed):
     """Tiles whose survivors overflow the LDS set (the first tile; rising
     scores), plateaus of equal keys wider than any LDS set (every column
     ranked by index), nothing surviving after the first tile, dead slots,
     the largest budget, and tile rows that are not 16-byte aligned; with
     dense tiles, and with tiles packed under the admission threshold the
-    previous call wrote (or a lower one).  The tiled result must equal the
-    untiled oracle selection bit for bit."""
+    previous call wrote (or a lower one).  bin5k / bin9k: normal scores
+    whose first 65536-column tile holds about 5000 / 8750 columns at or
+    above the top-12-bit bin of its threshold (3 + 0.7 z: the bin starts at
+    4.0 = 1.43 sigma; 4 + 0.9 z: at 5.0 = 1.11 sigma), more than a set
+    beside a full running set holds, fewer / more than the first tile's
+    (whose running set is empty).  The tiled result must equal the untiled
+    oracle selection bit for bit."""
     dev = require_gpu()
     rng = np.random.default_rng(len(case))
     U, n, tile, k, n_sink, n_recent = 3, 70000, 16384, 4096, 4, 64
@@ -238,6 +244,10 @@ def test_select_tiled_hard_cases(case, packed):
     elif case == "k8192":
         n, tile, k = 200000, 65536, 8192
         s = rng.standard_normal((U, n)).astype(np.float32)
+    elif case in ("bin5k", "bin9k"):
+        n, tile = 140000, 65536
+        mean, sd = (3.0, 0.7) if case == "bin5k" else (4.0, 0.9)
+        s = (mean + sd * rng.standard_normal((U, n))).astype(np.float32)
     else:
         n, tile, pad = 50001, 10001, 3
         s = rng.standard_normal((U, n)).astype(np.float32)
