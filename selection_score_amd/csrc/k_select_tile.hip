@@ -66,12 +66,18 @@ __device__ uint32_t block_exclusive(uint32_t v, TileShared& sh, uint32_t* total)
   __syncthreads();
   if (lane == 63) sh.wred[wave] = incl;
   __syncthreads();
-  uint32_t before = 0, all = 0;
-  for (int w = 0; w < kW; ++w) {
-    const uint32_t x = sh.wred[w];
-    if (w < wave) before += x;
-    all += x;
+  // lane w < kW holds wave w's total: the sums over all waves and over the
+  // waves before this one, by a butterfly over the first kW lanes (every
+  // lane of the wavefront is active here), read from lane 0
+  uint32_t all = (lane < kW) ? sh.wred[lane] : 0u;
+  uint32_t before = (lane < wave) ? all : 0u;
+#pragma unroll
+  for (int o = kW / 2; o > 0; o >>= 1) {
+    all += __shfl_xor(all, o, 64);
+    before += __shfl_xor(before, o, 64);
   }
+  all = __builtin_amdgcn_readfirstlane(all);
+  before = __builtin_amdgcn_readfirstlane(before);
   *total = all;
   return before + incl - v;
 }
@@ -88,9 +94,10 @@ __device__ uint32_t block_min_u32(uint32_t v, TileShared& sh) {
   __syncthreads();
   if (lane == 0) sh.wred[wave] = v;
   __syncthreads();
-  uint32_t m = 0xFFFFFFFFu;
-  for (int w = 0; w < kW; ++w) m = min(m, sh.wred[w]);
-  return m;
+  uint32_t m = (lane < kW) ? sh.wred[lane] : 0xFFFFFFFFu;
+#pragma unroll
+  for (int o = kW / 2; o > 0; o >>= 1) m = min(m, static_cast<uint32_t>(__shfl_xor(m, o, 64)));
+  return __builtin_amdgcn_readfirstlane(m);
 }
 
 // Over sh.hist[0, nbins): the bin holding the rem-th largest entry, the count
