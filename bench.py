@@ -1065,9 +1065,10 @@ def main():
     t_end.record(stream)
     torch.cuda.synchronize()
     per = {n: [e[i].elapsed_time(e[i + 1]) for e in evs] for i, n in enumerate(wk.stages)}
+    spans = [e[0].elapsed_time(e[-1]) for e in evs]         # each step's own span
     if flush:
         # latency: each step's own span, the cache flush before it excluded
-        ms_step = sum(e[0].elapsed_time(e[-1]) for e in evs) / args.steps
+        ms_step = sum(spans) / args.steps
     else:
         ms_step = t_start.elapsed_time(t_end) / args.steps
     stage = {n: sum(t) / len(t) for n, t in per.items()}
@@ -1092,6 +1093,8 @@ def main():
         "data": "synthetic",
         "config": wk.config(),
         "stages_ms": stage,
+        "step_ms_median": statistics.median(spans),
+        "step_ms_min": min(spans),
         "stages_ms_median": {n: statistics.median(t) for n, t in per.items()},
         "stages_ms_min": {n: min(t) for n, t in per.items()},
         "stage_gbps": {n: algo[n] / (stage[n] * 1e-3) / 1e9 for n in wk.stages},
