@@ -61,8 +61,9 @@ __device__ __forceinline__ void store_elem(void* p, int64_t i, float v) {
 // key); -0.0 is folded onto +0.0 first.  Key 0 never arises from a finite
 // value and marks "not a candidate".
 __device__ __forceinline__ uint32_t score_key(float s) {
-  uint32_t u = __float_as_uint(s + 0.0f);
-  return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+  // negative: every bit flipped; otherwise: the sign bit set
+  const uint32_t u = __float_as_uint(s + 0.0f);
+  return u ^ (static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u);
 }
 
 __device__ __forceinline__ float key_score(uint32_t k) {
