@@ -94,9 +94,29 @@ def _args():
 
 
 def _source_sha(name):
-    path = os.path.join(ROOT, "selection_score_amd", "csrc", name)
-    with open(path, "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    """SHA-256 (16 hex digits) of a kernel source and of every local header it
+    includes, recursively (the package's csrc/, then include/)."""
+    import re
+    h = hashlib.sha256()
+    seen = set()
+
+    def add(n):
+        if n in seen:
+            return
+        seen.add(n)
+        for d in (os.path.join(ROOT, "selection_score_amd", "csrc"), os.path.join(ROOT, "include")):
+            path = os.path.join(d, n)
+            if os.path.exists(path):
+                with open(path, "rb") as f:
+                    data = f.read()
+                h.update(n.encode() + b"\0" + data)
+                for inc in re.findall(rb'#include "([^"]+)"', data):
+                    add(inc.decode())
+                return
+        raise FileNotFoundError(n)
+
+    add(name)
+    return h.hexdigest()[:16]
 
 
 def _traffic(kernel, source, workload):
