@@ -149,13 +149,19 @@ __global__ __launch_bounds__(256) void gather_blocks_kernel(GatherParams p, Rope
   const int64_t item_bytes = row_bytes * p.bt;
   const int passes = (p.bt + rows_per_pass - 1) / rows_per_pass;
 
+  // work item tt: entry tt / 2, its K (even) or V (odd).  With an even
+  // n_waves a wavefront takes the other half of its entry on odd passes
+  // (tt0 ^ 1: the same entry, each item still taken once), so every
+  // wavefront alternates between K items (rotated) and V items (copied).
   int32_t b_n = (wave_global < 2 * items) ? idx[wave_global >> 1] : 0;
-  for (int64_t tt = wave_global; tt < 2 * items; tt += n_waves) {
+  int64_t pass = 0;
+  for (int64_t tt0 = wave_global; tt0 < 2 * items; tt0 += n_waves, ++pass) {
+    const int64_t tt = (n_waves & 1) ? tt0 : (tt0 ^ (pass & 1));
     const int64_t it = tt >> 1;
     const int u = static_cast<int>(it / p.k);
     const int64_t i = it - static_cast<int64_t>(u) * p.k;
     const int32_t b = b_n;
-    if (tt + n_waves < 2 * items) b_n = idx[(tt + n_waves) >> 1];
+    if (tt0 + n_waves < 2 * items) b_n = idx[(tt0 + n_waves) >> 1];
     if (n_idx != nullptr && i >= n_idx[u]) continue;
     if (b < 0 || (static_cast<int64_t>(b) + 1) * p.bt > p.src_rows) continue;
     if (tt & 1) {
