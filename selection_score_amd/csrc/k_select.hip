@@ -140,8 +140,9 @@ __device__ uint3 block_sum3(uint32_t a, uint32_t b, uint32_t c, uint32_t* scratc
 }
 
 constexpr int kPrepKeys = 4096;       // columns per select_keys_kernel workgroup
-constexpr int kFusedMinUnits = 128;   // unpooled untiled calls with this many units make their own keys
+constexpr int kFusedMinUnits = 128;   // untiled calls with this many units make their own keys
 constexpr int kFusedSmallN = 8192;    // ... as do calls of any unit count over rows this short
+constexpr int kFusedMaxPoolR = 4;     // ... with max pooling up to pool_k 9 done in registers
 constexpr int kPrepThreads = 256;
 constexpr int kMaxPoolR = 127;        // pool_k <= 255
 
@@ -498,6 +499,56 @@ __global__ __launch_bounds__(kThreads) void select_kernel(SelectParams p, const 
 // from the score row and the first radix pass runs here too; otherwise they
 // come prepared, with the slices' top-byte histograms, from
 // select_keys_kernel.
+// Max pooling of radius R over a wavefront's columns held in registers:
+// v[i] on lane l is column s_beg + 64 i + l.  The chunks are extended by the
+// 64 columns before and after them (b[0] and b[KPT + 1], loaded here);
+// columns outside the row count as -inf, so every window takes the maximum
+// of its in-range columns.  With P the largest power of two not above the
+// window 2R + 1, log2(P) doubling steps give b[c] = max of columns
+// [c, c + P), and the window of c is max(b[c - R], b[c + R + 1 - P]).  A
+// shift by d columns moves every chunk's values by one lane shuffle; lanes
+// that cross a chunk edge take the neighbouring chunk's shuffled values.
+template <int KPT>
+__device__ __forceinline__ void pool_max_regs(float (&v)[KPT], const float* row, int n, int s_beg, int lane,
+                                              int R) {
+  constexpr int C = KPT + 2;
+  const int P = (2 * R + 1 >= 8) ? 8 : (2 * R + 1 >= 4) ? 4 : 2;   // R in [1, 7]
+  const float kNegInf = -__builtin_huge_valf();
+  float b[C];
+  const int el = s_beg - 64 + lane, er = s_beg + 64 * KPT + lane;
+  const float fl = row[min(max(el, 0), n - 1)], fr = row[min(er, n - 1)];
+  b[0] = (el >= 0 && el < n) ? fl : kNegInf;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) b[i + 1] = (s_beg + 64 * i + lane < n) ? v[i] : kNegInf;
+  b[C - 1] = (er < n) ? fr : kNegInf;
+  for (int m = 1; m < P; m <<= 1) {                 // b[c] = max over [c, c + 2m)
+    const int src = (lane + m) & 63;
+    const bool wrap = lane + m >= 64;
+    // ascending: chunk j + 1 is shuffled before it is updated
+    float cur = __shfl(b[0], src, 64);
+#pragma unroll
+    for (int j = 0; j < C; ++j) {
+      const float nxt = (j + 1 < C) ? __shfl(b[j + 1], src, 64) : kNegInf;
+      b[j] = fmaxf(b[j], wrap ? nxt : cur);
+      cur = nxt;
+    }
+  }
+  // v[i] = max(b at c - R, b at c + R + 1 - P): both offsets are <= 0
+  const int d1 = -R, d2 = R + 1 - P;
+  const int src1 = (lane + d1) & 63, src2 = (lane + d2) & 63;
+  const bool wrap1 = lane + d1 < 0, wrap2 = lane + d2 < 0;
+  float p1 = __shfl(b[0], src1, 64);
+  float p2 = (d2 == 0) ? b[0] : __shfl(b[0], src2, 64);
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) {
+    const float c1 = __shfl(b[i + 1], src1, 64);
+    const float c2 = (d2 == 0) ? b[i + 1] : __shfl(b[i + 1], src2, 64);
+    v[i] = fmaxf(wrap1 ? p1 : c1, wrap2 ? p2 : c2);
+    p1 = c1;
+    p2 = c2;
+  }
+}
+
 template <int KPT, bool kFused, int NT>
 __global__ __launch_bounds__(NT) void select_regs_kernel(SelectParams p, const float* scores,
                                                                const uint32_t* keys,
@@ -543,6 +594,10 @@ __global__ __launch_bounds__(NT) void select_regs_kernel(SelectParams p, const f
     float v[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) v[i] = row[min(s_beg + 64 * i + lane, n - 1)];
+    // max pooling (the only pooling this path takes) on the registers
+    if (p.pool == KVSEL_POOL_MAX && p.pool_k > 1) {
+      pool_max_regs<KPT>(v, row, n, s_beg, lane, p.pool_k / 2);   // radius 1 .. kFusedMaxPoolR
+    }
     __syncthreads();                                // histogram cleared
 #pragma unroll
     for (int i = 0; i < KPT; ++i) {
@@ -680,7 +735,8 @@ __global__ __launch_bounds__(NT) void select_regs_kernel(SelectParams p, const f
 // takes the two-launch path, whose per-unit kernel reads no key when n is 0.
 static bool select_single_launch(const SelectParams& p) {
   return p.cand_count == nullptr && p.n > 0 && p.n <= 32 * kThreads && (p.U >= kFusedMinUnits || p.n <= kFusedSmallN) &&
-         (p.pool == KVSEL_POOL_NONE || p.pool_k == 1) && p.slot_map == nullptr;
+         (p.pool == KVSEL_POOL_NONE || p.pool_k == 1 || (p.pool == KVSEL_POOL_MAX && p.pool_k / 2 <= kFusedMaxPoolR)) &&
+         p.slot_map == nullptr;
 }
 
 size_t select_workspace_bytes(const SelectParams& p) {

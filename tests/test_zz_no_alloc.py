@@ -44,11 +44,11 @@ def _same(a, b):
 
 def test_noalloc_select_equals_workspace_select_on_consecutive_calls():
     dev = require_gpu()
-    # first call: 288 units x 32768 columns, max-pool 7 (the two-launch path,
+    # first call: 288 units x 32768 columns, avg-pool 7 (the two-launch path,
     # about 40 MB of scratch); second call: a smaller, ragged, avg-pooled one
     # with dead slots, which reuses the front of the same array
     big = _scores(dev, 288, 32768, 1)
-    ref, got = _both(dev, big, k_total=8192, n_sink=4, n_recent=256, pool="max", pool_k=7)
+    ref, got = _both(dev, big, k_total=8192, n_sink=4, n_recent=256, pool="avg", pool_k=7)
     _same(ref, got)
     assert torch.all(got[2] == 8192)
     small = _scores(dev, 37, 5003, 2)
@@ -60,15 +60,18 @@ def test_noalloc_select_equals_workspace_select_on_consecutive_calls():
     kept = got[0].cpu().numpy()
     assert np.all(kept[:, :700][kept[:, :700] >= 0] % 11 != 0)
     # the first shape again after the smaller one: no stale scratch
-    ref, got = _both(dev, big, k_total=8192, n_sink=4, n_recent=256, pool="max", pool_k=7)
+    ref, got = _both(dev, big, k_total=8192, n_sink=4, n_recent=256, pool="avg", pool_k=7)
     _same(ref, got)
 
 
 def test_noalloc_select_without_scratch_use_and_tiled():
     dev = require_gpu()
-    # unpooled, many units: the single-launch path reads no scratch at all
+    # unpooled or max-pooled over a short window, many units: the
+    # single-launch path reads no scratch at all
     s = _scores(dev, 512, 32768, 3)
     ref, got = _both(dev, s, k_total=2048, n_sink=1, n_recent=4)
+    _same(ref, got)
+    ref, got = _both(dev, s[:288], k_total=8192, n_sink=4, n_recent=256, pool="max", pool_k=7)
     _same(ref, got)
     # tiled with running candidates: no scratch either
     U, n_total, tile, k = 9, 100000, 30000, 1024
@@ -96,8 +99,8 @@ def test_noalloc_select_rejects_calls_beyond_its_scratch():
     s = torch.zeros((U, n), device=dev)
     kept = torch.empty((U, 64), dtype=torch.int32, device=dev)
     with pytest.raises(kv.KvselError) as e:
-        kv.select_noalloc(s, kept, k_total=64, n_sink=1, n_recent=1, pool="max", pool_k=3)
+        kv.select_noalloc(s, kept, k_total=64, n_sink=1, n_recent=1, pool="avg", pool_k=3)
     assert e.value.status == _abi.KVSEL_E_WORKSPACE
     # the same call with a caller workspace is fine
-    kv.select(s, kept, k_total=64, n_sink=1, n_recent=1, pool="max", pool_k=3)
+    kv.select(s, kept, k_total=64, n_sink=1, n_recent=1, pool="avg", pool_k=3)
     torch.cuda.synchronize()
