@@ -274,14 +274,14 @@ def _np64(t):
 class Tiny:
     """Token-level eviction at the tiny size (1 layer, 2 KV / 8 query heads,
     2048 fp32 keys of D 64, 16 planted high-norm keys): window scores over the
-    last 16 queries with the LSE computed and avg-pool 7, top-512 per KV head
-    with 4 sink + 64 recent, gather of the kept K and V rows.  A latency
-    measurement: before every step a 1 GiB fill evicts L2 and the Infinity
-    Cache (outside the step's events), and ms_per_step is the mean of the
-    steps' own event spans."""
+    last 16 queries with the LSE computed, top-512 per KV head of the avg-pool
+    7 scores (pooled inside the select's workgroup) with 4 sink + 64 recent,
+    gather of the kept K and V rows.  A latency measurement: before every
+    step a 1 GiB fill evicts L2 and the Infinity Cache (outside the step's
+    events), and ms_per_step is the mean of the steps' own event spans."""
     stages = ["score", "select", "gather"]
     dominant = ("score", [("lse_valu_kernel", "k_window.hip"), ("scores_valu_kernel", "k_window.hip"),
-                          ("pool1d_kernel", "k_window.hip")])
+                          ("lse_combine_kernel", "k_window.hip")])
     score_stage = "score"
     materialise_stages = ["select", "gather"]
     dtype = "f32"
@@ -297,8 +297,9 @@ class Tiny:
         self.dk = torch.empty((U, cfg.k, D), dtype=torch.float32, device=dev)
         self.dv = torch.empty_like(self.dk)
         self.k3, self.v3 = self.inp["k"].view(U, N, D), self.inp["v"].view(U, N, D)
-        self.ws = kv.score_window(self.inp["q"], self.inp["k"], self.scores, pool=cfg.pool, pool_k=cfg.pool_k)
-        self.sel_ws = kv.select(self.scores, self.kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent)
+        self.ws = kv.score_window(self.inp["q"], self.inp["k"], self.scores)
+        self.sel_ws = kv.select(self.scores, self.kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
+                                pool=cfg.pool, pool_k=cfg.pool_k)
         self.flush_buf = torch.empty(1 << 28, dtype=torch.float32, device=dev)
         self.tokens = cfg.L * cfg.Hkv * N
 
@@ -308,10 +309,10 @@ class Tiny:
     def step(self, ev, stream, it):
         kv, cfg, inp = self.kv, self.cfg, self.inp
         ev[0].record(stream)
-        kv.score_window(inp["q"], inp["k"], self.scores, pool=cfg.pool, pool_k=cfg.pool_k, workspace=self.ws)
+        kv.score_window(inp["q"], inp["k"], self.scores, workspace=self.ws)
         ev[1].record(stream)
         kv.select(self.scores, self.kept, k_total=cfg.k, n_sink=cfg.n_sink, n_recent=cfg.n_recent,
-                  workspace=self.sel_ws)
+                  pool=cfg.pool, pool_k=cfg.pool_k, workspace=self.sel_ws)
         ev[2].record(stream)
         kv.gather_rerope(self.k3, self.v3, self.kept, self.dk, self.dv, bt=1, D=cfg.D, src_rows=cfg.N,
                          src_unit_stride=cfg.N * cfg.D)
@@ -324,8 +325,8 @@ class Tiny:
         sb = cfg.U * cfg.N * 4
         kept_b = cfg.U * cfg.k * 4
         # the score call reads K twice (LSE pass, score pass) and writes the
-        # unpooled scores then the pooled ones
-        return {"score": 2 * (kb + qb) + 3 * sb, "select": sb + kept_b,
+        # scores; the select reads them and pools them in its workgroup
+        return {"score": 2 * (kb + qb) + sb, "select": sb + kept_b,
                 "gather": kept_b + 2 * 2 * cfg.U * cfg.k * cfg.D * 4}
 
     def cpu_baseline(self, seconds):

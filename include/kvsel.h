@@ -226,9 +226,10 @@ kvsel_status kvsel_score(const kvsel_score_args* args, void* workspace,
  * Workspace: kvsel_select_workspace() bytes, 16-byte aligned (the ordering
  * key of every position of the call and small per-slice histograms, about
  * 4 bytes per position); 0 when U or n is 0, and for untiled calls without a
- * slot map, unpooled or MAX-pooled with pool_k <= 9, over at least 128 units
- * of at most 32768 positions, or over any number of units of at most 8192
- * positions, whose per-unit workgroups keep their keys in registers.
+ * slot map, unpooled or MAX-pooled with pool_k <= 9 (AVG-pooled with pool_k
+ * <= 9 too when n <= 2048), over at least 128 units of at most 32768
+ * positions, or over any number of units of at most 8192 positions, whose
+ * per-unit workgroups keep their keys in registers.
  * Errors: KVSEL_E_BUDGET if n_sink + n_recent > k_total and k_total < n_total;
  * KVSEL_E_WORKSPACE if the workspace is missing or too small; KVSEL_E_UNSUPPORTED
  * for U > 65535, and for `tile_mask` or `admit` on a tiled call that needs

@@ -142,7 +142,8 @@ __device__ uint3 block_sum3(uint32_t a, uint32_t b, uint32_t c, uint32_t* scratc
 constexpr int kPrepKeys = 4096;       // columns per select_keys_kernel workgroup
 constexpr int kFusedMinUnits = 128;   // untiled calls with this many units make their own keys
 constexpr int kFusedSmallN = 8192;    // ... as do calls of any unit count over rows this short
-constexpr int kFusedMaxPoolR = 4;     // ... with max pooling up to pool_k 9 done in registers
+constexpr int kFusedMaxPoolR = 4;     // ... with pooling up to pool_k 9 done in registers (average
+constexpr int kFusedAvgKpt = 8;       //     windows only on rows of at most 8 keys per thread)
 constexpr int kPrepThreads = 256;
 constexpr int kMaxPoolR = 127;        // pool_k <= 255
 
@@ -549,6 +550,53 @@ __device__ __forceinline__ void pool_max_regs(float (&v)[KPT], const float* row,
   }
 }
 
+// Average pooling of radius R over the same register layout: each column's
+// window is summed from 0 in ascending column order, columns outside the row
+// counting as 0, then divided by 2R + 1 (the order the key preparation uses,
+// so the pooled values are the same bits).  One shift per window offset.
+template <int KPT>
+__device__ __forceinline__ void pool_avg_regs(float (&v)[KPT], const float* row, int n, int s_beg, int lane,
+                                              int R) {
+  constexpr int C = KPT + 2;
+  float b[C];
+  const int el = s_beg - 64 + lane, er = s_beg + 64 * KPT + lane;
+  const float fl = row[min(max(el, 0), n - 1)], fr = row[min(er, n - 1)];
+  b[0] = (el >= 0 && el < n) ? fl : 0.f;
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) b[i + 1] = (s_beg + 64 * i + lane < n) ? v[i] : 0.f;
+  b[C - 1] = (er < n) ? fr : 0.f;
+  float acc[KPT];
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) acc[i] = 0.f;
+  for (int d = -R; d <= R; ++d) {
+    const int src = (lane + d) & 63;
+    if (d == 0) {
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) acc[i] += b[i + 1];
+    } else if (d < 0) {
+      const bool wrap = lane + d < 0;                // from the chunk before
+      float prev = __shfl(b[0], src, 64);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const float cur = __shfl(b[i + 1], src, 64);
+        acc[i] += wrap ? prev : cur;
+        prev = cur;
+      }
+    } else {
+      const bool wrap = lane + d >= 64;              // from the chunk after
+      float cur = __shfl(b[1], src, 64);
+#pragma unroll
+      for (int i = 0; i < KPT; ++i) {
+        const float nxt = __shfl(b[i + 2], src, 64);
+        acc[i] += wrap ? nxt : cur;
+        cur = nxt;
+      }
+    }
+  }
+#pragma unroll
+  for (int i = 0; i < KPT; ++i) v[i] = acc[i] / static_cast<float>(2 * R + 1);
+}
+
 template <int KPT, bool kFused, int NT>
 __global__ __launch_bounds__(NT) void select_regs_kernel(SelectParams p, const float* scores,
                                                                const uint32_t* keys,
@@ -594,9 +642,12 @@ __global__ __launch_bounds__(NT) void select_regs_kernel(SelectParams p, const f
     float v[KPT];
 #pragma unroll
     for (int i = 0; i < KPT; ++i) v[i] = row[min(s_beg + 64 * i + lane, n - 1)];
-    // max pooling (the only pooling this path takes) on the registers
+    // pooling on the registers: max windows of radius 1 .. kFusedMaxPoolR;
+    // average windows of that radius on rows of at most 8 keys per thread
     if (p.pool == KVSEL_POOL_MAX && p.pool_k > 1) {
-      pool_max_regs<KPT>(v, row, n, s_beg, lane, p.pool_k / 2);   // radius 1 .. kFusedMaxPoolR
+      pool_max_regs<KPT>(v, row, n, s_beg, lane, p.pool_k / 2);
+    } else if constexpr (KPT <= kFusedAvgKpt) {
+      if (p.pool == KVSEL_POOL_AVG && p.pool_k > 1) pool_avg_regs<KPT>(v, row, n, s_beg, lane, p.pool_k / 2);
     }
     __syncthreads();                                // histogram cleared
 #pragma unroll
@@ -735,7 +786,8 @@ __global__ __launch_bounds__(NT) void select_regs_kernel(SelectParams p, const f
 // takes the two-launch path, whose per-unit kernel reads no key when n is 0.
 static bool select_single_launch(const SelectParams& p) {
   return p.cand_count == nullptr && p.n > 0 && p.n <= 32 * kThreads && (p.U >= kFusedMinUnits || p.n <= kFusedSmallN) &&
-         (p.pool == KVSEL_POOL_NONE || p.pool_k == 1 || (p.pool == KVSEL_POOL_MAX && p.pool_k / 2 <= kFusedMaxPoolR)) &&
+         (p.pool == KVSEL_POOL_NONE || p.pool_k == 1 || (p.pool == KVSEL_POOL_MAX && p.pool_k / 2 <= kFusedMaxPoolR) ||
+          (p.pool == KVSEL_POOL_AVG && p.pool_k / 2 <= kFusedMaxPoolR && p.n <= kFusedAvgKpt * 256)) &&
          p.slot_map == nullptr;
 }
 
@@ -754,6 +806,7 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
     const int n_slices = static_cast<int>(ceil_div(p.n, kPrepKeys));
     uint32_t* hist = keys + (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 64;
     if (select_single_launch(p)) {
+      static_assert(kFusedAvgKpt == 8, "average windows run on the 8-keys-per-thread kernel only");
       if (p.n <= 8 * 256) select_regs_kernel<8, true, 256><<<p.U, 256, 0, st>>>(p, scores, nullptr, nullptr, 0);
       else select_regs_kernel<32, true, kThreads><<<p.U, kThreads, 0, st>>>(p, scores, nullptr, nullptr, 0);
       return hipGetLastError();

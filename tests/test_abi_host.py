@@ -97,15 +97,18 @@ def test_select_validation_errors_without_device():
     assert b"workspace" in lib.kvsel_last_error()
     assert _status(lib.kvsel_select, _select_args(**long_rows), ctypes.c_void_p(0x10000),
                    ctypes.c_size_t(nb.value - 1), None) == _abi.KVSEL_E_WORKSPACE
-    # a max-pooled call with a short window makes its keys in registers too;
-    # an average-pooled one, a longer window or a slot map keeps the two launches
-    assert _status(lib.kvsel_select_workspace, _select_args(pool=_abi.POOL["max"], pool_k=3),
-                   ctypes.byref(nb)) == _abi.KVSEL_OK and nb.value == 0
-    assert _status(lib.kvsel_select_workspace, _select_args(pool=_abi.POOL["max"], pool_k=9),
-                   ctypes.byref(nb)) == _abi.KVSEL_OK and nb.value == 0
-    for kw in (dict(pool=_abi.POOL["max"], pool_k=11), dict(pool=_abi.POOL["avg"], pool_k=3)):
+    # a max-pooled call with a short window makes its keys in registers too,
+    # as does an average-pooled one over rows of at most 2048 positions; a
+    # longer window, a longer average-pooled row or a slot map keeps the two launches
+    for kw in (dict(pool=_abi.POOL["max"], pool_k=3), dict(pool=_abi.POOL["max"], pool_k=9),
+               dict(pool=_abi.POOL["avg"], pool_k=9)):
         assert _status(lib.kvsel_select_workspace, _select_args(**kw), ctypes.byref(nb)) == _abi.KVSEL_OK
-        assert nb.value >= 100 * 4
+        assert nb.value == 0
+    mid_rows = dict(n=3000, row_stride=3000, n_total=3000)
+    for kw in (dict(pool=_abi.POOL["max"], pool_k=11), dict(pool=_abi.POOL["avg"], pool_k=11),
+               dict(mid_rows, pool=_abi.POOL["avg"], pool_k=3)):
+        assert _status(lib.kvsel_select_workspace, _select_args(**kw), ctypes.byref(nb)) == _abi.KVSEL_OK
+        assert nb.value >= kw.get("n", 100) * 4
     # a tile of a tiled call whose running set and tile fit in LDS needs none;
     # a tile too wide for the LDS bitmap takes the two-launch path and does
     tiled = dict(cand_score=0x3000, cand_idx=0x4000, cand_count=0x5000, n=60, n_total=100, base=40)

@@ -295,12 +295,15 @@ def test_select_pooled_slices(pool, n):
     (131, 7001, 900, "max", 5, False, False),      # ties, ragged rows, every doubling depth and
     (128, 32768, 8192, "max", 9, False, False),    # second offset, the longest rows
     (128, 9000, 1000, "max", 11, False, False),    # a window of 11 keeps the two launches
+    (128, 2000, 300, "avg", 7, True, False),       # average windows in registers on short rows
+    (129, 1500, 200, "avg", 9, False, False),
 ])
 def test_select_many_units(U, n, k, pool, pool_k, ties, dead):
-    """Many units: unpooled rows (and windows of one), and max-pooled rows
-    with windows up to 9, without a slot map take the single-launch path
-    where each unit's workgroup makes its own keys; other pooled rows and
-    dead slots keep the two launches.  Against pool1d + select_topk."""
+    """Many units: unpooled rows (and windows of one), max-pooled rows with
+    windows up to 9, and average-pooled rows of at most 2048 columns with
+    windows up to 9, without a slot map, take the single-launch path where
+    each unit's workgroup makes its own keys; other pooled rows and dead
+    slots keep the two launches.  Against pool1d + select_topk."""
     from oracle import numerics
     from oracle import score as osc
     dev = require_gpu()
