@@ -94,11 +94,14 @@ def _args():
 
 
 def _source_sha(name):
-    """SHA-256 (16 hex digits) of a kernel source and of every local header it
-    includes, recursively (the package's csrc/, then include/)."""
+    """SHA-256 (16 hex digits) of the code of a kernel source and of every
+    local header it includes, recursively (the package's csrc/, then
+    include/), with comments and whitespace removed: an edit of the comments
+    keeps the summaries that were taken on the same code."""
     import re
     h = hashlib.sha256()
     seen = set()
+    comment = re.compile(rb'//[^\n]*|/\*.*?\*/', re.S)
 
     def add(n):
         if n in seen:
@@ -109,7 +112,8 @@ def _source_sha(name):
             if os.path.exists(path):
                 with open(path, "rb") as f:
                     data = f.read()
-                h.update(n.encode() + b"\0" + data)
+                code = re.sub(rb"\s+", b"", comment.sub(b" ", data))
+                h.update(n.encode() + b"\0" + code)
                 for inc in re.findall(rb'#include "([^"]+)"', data):
                     add(inc.decode())
                 return
