@@ -224,8 +224,9 @@ kvsel_status kvsel_score(const kvsel_score_args* args, void* workspace,
  * out-of-range terms as zero, MAX takes the in-range maximum), computed on
  * the fly while the keys are formed.
  * Workspace: kvsel_select_workspace() bytes, 16-byte aligned (the ordering
- * key of every position of the call and small per-slice histograms, about
- * 4 bytes per position); 0 when U or n is 0, and for untiled calls without a
+ * key of every position of the call, small per-slice histograms, and for at
+ * most 8 units of rows longer than 32768 positions a few more per-slice
+ * histograms and counts: about 4 bytes per position); 0 when U or n is 0, and for untiled calls without a
  * slot map, unpooled or MAX-pooled with pool_k <= 9 (AVG-pooled with pool_k
  * <= 9 too when n <= 2048), over at least 128 units of at most 32768
  * positions, or over any number of units of at most 8192 positions, whose

@@ -784,6 +784,274 @@ __global__ __launch_bounds__(NT) void select_regs_kernel(SelectParams p, const f
 // (Pooled rows keep the two launches, whose key kernel spreads the window
 // work over many workgroups.)  An empty row (n = 0, scores possibly NULL)
 // takes the two-launch path, whose per-unit kernel reads no key when n is 0.
+// ---- few units of long untiled rows: the radix passes spread over the
+// 4096-column slices of select_keys_kernel, one launch per step.  Each
+// digit launch sums the previous digit's per-slice histograms in slice
+// order (every workgroup the same way, so all find the same bin), slice 0's
+// workgroup records the state for the next launch, and every workgroup
+// histograms the next digit over its own slice.  The count launch fixes the
+// threshold key T and counts each slice's keys above and equal to it; the
+// placement launch writes each slice's selected positions in ascending
+// order after those of the slices before it (keys equal to T ranked by
+// position across the whole row, as the single-workgroup sweeps do).
+constexpr int kSliceMaxUnits = 8;     // units per call that take the slice-parallel path
+constexpr int kSliceState = 8;        // ints per unit and step: prefix, remaining, mode, fsum, rsum
+
+struct SliceWs {
+  uint32_t* keys;       // [U][n]
+  uint32_t* hist0;      // [U][slices][256] top byte (select_keys_kernel)
+  uint32_t* hist[2];    // [U][slices][256] later digits, alternating
+  int32_t* state;       // [4][U][kSliceState]
+  uint32_t* counts;     // [U][slices][2]: keys above T, keys equal to T
+};
+
+// Alive forced positions of unit u (sink, recent); all threads call.
+__device__ void slice_forced(const SelectParams& p, uint32_t* scratch, uint32_t* fsum, uint32_t* rsum) {
+  const int64_t sink_end = min(static_cast<int64_t>(p.n_sink), p.n_total);
+  const int64_t rec_begin = max(sink_end, p.n_total - static_cast<int64_t>(p.n_recent));
+  uint32_t fs = 0, fr = 0;
+  for (int64_t g = threadIdx.x; g < sink_end; g += kPrepThreads)
+    fs += (p.slot_map == nullptr || static_cast<int64_t>(p.slot_map[g]) != p.dead_slot) ? 1u : 0u;
+  for (int64_t g = rec_begin + threadIdx.x; g < p.n_total; g += kPrepThreads)
+    fr += (p.slot_map == nullptr || static_cast<int64_t>(p.slot_map[g]) != p.dead_slot) ? 1u : 0u;
+  const uint3 t = block_sum3(fs, fr, 0u, scratch, kPrepThreads / 64);
+  *fsum = t.x;
+  *rsum = t.y;
+}
+
+// Digit step `step` (1, 2, 3: histograms of the digits at 16, 8, 0 bits):
+// find the bin of the previous digit from `hin`, then histogram this digit.
+__global__ __launch_bounds__(kPrepThreads) void slice_digit_kernel(SelectParams p, SliceWs w, int n_slices,
+                                                                   int step, const uint32_t* hin,
+                                                                   uint32_t* hout) {
+  __shared__ SelShared sh;
+  const int u = blockIdx.y, slice = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  int32_t* st_out = w.state + (static_cast<int64_t>(step - 1) * p.U + u) * kSliceState;
+  uint32_t prefix, fsum, rsum;
+  int32_t rem, mode;
+  // the summed histogram of the previous digit, slices in order
+  uint32_t nc = 0;
+  for (int b = tid; b < 256; b += kPrepThreads) {
+    uint32_t t = 0;
+    for (int sl = 0; sl < n_slices; ++sl) t += hin[(static_cast<int64_t>(u) * n_slices + sl) * 256 + b];
+    sh.hist[b] = t;
+    nc += t;
+  }
+  if (step == 1) {
+    slice_forced(p, sh.wave_sums, &fsum, &rsum);
+    const uint32_t n_cand = block_sum3(nc, 0u, 0u, sh.wave_sums, kPrepThreads / 64).x;
+    const int32_t room = p.k_total - static_cast<int32_t>(fsum + rsum);
+    prefix = 0u;
+    rem = room;
+    mode = (static_cast<int64_t>(n_cand) <= static_cast<int64_t>(room)) ? 1 : (room <= 0) ? 2 : 0;
+  } else {
+    const int32_t* st_in = w.state + (static_cast<int64_t>(step - 2) * p.U + u) * kSliceState;
+    prefix = static_cast<uint32_t>(st_in[0]);
+    rem = st_in[1];
+    mode = st_in[2];
+    fsum = static_cast<uint32_t>(st_in[3]);
+    rsum = static_cast<uint32_t>(st_in[4]);
+  }
+  const int shift_in = 32 - 8 * step;          // the digit hin counts: 24, 16, 8
+  if (mode == 0) {                              // uniform over the workgroup
+    if (tid == 0) {
+      sh.prefix = prefix;
+      sh.remaining = rem;
+    }
+    __syncthreads();
+    if (wave == 0) find_bin(sh, prefix, shift_in, lane);
+    __syncthreads();
+    prefix = sh.prefix;
+    rem = sh.remaining;
+  }
+  if (slice == 0 && tid == 0) {
+    st_out[0] = static_cast<int32_t>(prefix);
+    st_out[1] = rem;
+    st_out[2] = mode;
+    st_out[3] = static_cast<int32_t>(fsum);
+    st_out[4] = static_cast<int32_t>(rsum);
+  }
+  if (hout == nullptr) return;                  // the count launch reads the state itself
+  // histogram of the next digit over this slice's keys that match the prefix
+  const int shift = shift_in - 8;
+  __syncthreads();
+  for (int b = tid; b < 256; b += kPrepThreads) sh.hist[b] = 0u;
+  __syncthreads();
+  if (mode == 0) {
+    const uint32_t hi_mask = 0xFFFFFFFFu << (shift + 8);
+    const int64_t j0 = static_cast<int64_t>(slice) * kPrepKeys;
+    const int jn = static_cast<int>(min(static_cast<int64_t>(kPrepKeys), p.n - j0));
+    const uint32_t* ks = w.keys + static_cast<int64_t>(u) * p.n + j0;
+    for (int i = tid; i < jn; i += kPrepThreads) {
+      const uint32_t key = ks[i];
+      if (key != 0u && ((key ^ prefix) & hi_mask) == 0u) atomicAdd(&sh.hist[(key >> shift) & 255u], 1u);
+    }
+  }
+  __syncthreads();
+  uint32_t* ho = hout + (static_cast<int64_t>(u) * n_slices + slice) * 256;
+  for (int b = tid; b < 256; b += kPrepThreads) ho[b] = sh.hist[b];
+}
+
+// The last digit's bin (from `hin`, the digit at 0 bits), the threshold key
+// T, and each slice's keys above and equal to T.
+__global__ __launch_bounds__(kPrepThreads) void slice_count_kernel(SelectParams p, SliceWs w, int n_slices,
+                                                                   const uint32_t* hin) {
+  __shared__ SelShared sh;
+  const int u = blockIdx.y, slice = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* st_in = w.state + (static_cast<int64_t>(2) * p.U + u) * kSliceState;
+  int32_t* st_out = w.state + (static_cast<int64_t>(3) * p.U + u) * kSliceState;
+  uint32_t prefix = static_cast<uint32_t>(st_in[0]);
+  int32_t rem = st_in[1];
+  const int32_t mode = st_in[2];
+  if (mode == 0) {
+    for (int b = tid; b < 256; b += kPrepThreads) {
+      uint32_t t = 0;
+      for (int sl = 0; sl < n_slices; ++sl) t += hin[(static_cast<int64_t>(u) * n_slices + sl) * 256 + b];
+      sh.hist[b] = t;
+    }
+    if (tid == 0) {
+      sh.prefix = prefix;
+      sh.remaining = rem;
+    }
+    __syncthreads();
+    if (wave == 0) find_bin(sh, prefix, 0, lane);
+    __syncthreads();
+    prefix = sh.prefix;
+    rem = sh.remaining;
+  }
+  // T as the single-workgroup select sets it: 1 (every candidate is above)
+  // or 0xFFFFFFFF (nothing is selected) outside the radix case
+  const uint32_t T = (mode == 1) ? 1u : (mode == 2) ? 0xFFFFFFFFu : prefix;
+  if (mode != 0) rem = 0;
+  if (slice == 0 && tid == 0) {
+    st_out[0] = static_cast<int32_t>(T);
+    st_out[1] = rem;
+    st_out[2] = mode;
+    st_out[3] = st_in[3];
+    st_out[4] = st_in[4];
+  }
+  const int64_t j0 = static_cast<int64_t>(slice) * kPrepKeys;
+  const int jn = static_cast<int>(min(static_cast<int64_t>(kPrepKeys), p.n - j0));
+  const uint32_t* ks = w.keys + static_cast<int64_t>(u) * p.n + j0;
+  uint32_t gt = 0, eq = 0;
+  for (int i = tid; i < jn; i += kPrepThreads) {
+    const uint32_t key = ks[i];
+    gt += (key != 0u && key > T) ? 1u : 0u;
+    eq += (key != 0u && key == T) ? 1u : 0u;
+  }
+  const uint3 t = block_sum3(gt, eq, 0u, sh.wave_sums, kPrepThreads / 64);
+  if (tid == 0) {
+    uint32_t* c = w.counts + (static_cast<int64_t>(u) * n_slices + slice) * 2;
+    c[0] = t.x;
+    c[1] = t.y;
+  }
+}
+
+// Places the selected positions of one slice, writes its keep mask; slice
+// 0's workgroup also places the forced positions and pads the list.
+__global__ __launch_bounds__(kPrepThreads) void slice_place_kernel(SelectParams p, SliceWs w, int n_slices) {
+  __shared__ SelShared sh;
+  constexpr int kW = kPrepThreads / 64;
+  const int u = blockIdx.y, slice = blockIdx.x;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  const int32_t* st = w.state + (static_cast<int64_t>(3) * p.U + u) * kSliceState;
+  const uint32_t T = static_cast<uint32_t>(st[0]);
+  const int32_t remaining = st[1];
+  const uint32_t fsum = static_cast<uint32_t>(st[3]), rsum = static_cast<uint32_t>(st[4]);
+  // bases from the slices before this one, and the total selected
+  const uint32_t* cu = w.counts + static_cast<int64_t>(u) * n_slices * 2;
+  uint32_t eq_base = 0, sel_base = 0, n_sel_total = 0, eb = 0;
+  for (int sl = 0; sl < n_slices; ++sl) {
+    const uint32_t g = cu[2 * sl], e = cu[2 * sl + 1];
+    const int32_t take = max(0, min(static_cast<int32_t>(e), remaining - static_cast<int32_t>(eb)));
+    if (sl < slice) {
+      eq_base += e;
+      sel_base += g + static_cast<uint32_t>(take);
+    }
+    n_sel_total += g + static_cast<uint32_t>(take);
+    eb += e;
+  }
+  const int64_t sink_end = min(static_cast<int64_t>(p.n_sink), p.n_total);
+  const int64_t rec_begin = max(sink_end, p.n_total - static_cast<int64_t>(p.n_recent));
+  auto alive = [&](int64_t g) {
+    return p.slot_map == nullptr || static_cast<int64_t>(p.slot_map[g]) != p.dead_slot;
+  };
+  // wavefront segments of the slice, in order: counts, then bases
+  const int64_t j0 = static_cast<int64_t>(slice) * kPrepKeys;
+  const int jn = static_cast<int>(min(static_cast<int64_t>(kPrepKeys), p.n - j0));
+  const int seg = kPrepKeys / kW;
+  const int s_beg = min(jn, wave * seg), s_end = min(jn, s_beg + seg);
+  const uint32_t* ks = w.keys + static_cast<int64_t>(u) * p.n + j0;
+  uint32_t n_eq = 0, n_gt = 0;
+  for (int i0 = s_beg; i0 < s_end; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t key = (i < s_end) ? ks[i] : 0u;
+    n_eq += __popcll(__ballot(key != 0u && key == T));
+    n_gt += __popcll(__ballot(key != 0u && key > T));
+  }
+  if (lane == 0) {
+    sh.wave_eq[wave] = n_eq;
+    sh.wave_gt[wave] = n_gt;
+  }
+  __syncthreads();
+  for (int v = 0; v < wave; ++v) {
+    const int32_t take = max(0, min(static_cast<int32_t>(sh.wave_eq[v]), remaining - static_cast<int32_t>(eq_base)));
+    sel_base += sh.wave_gt[v] + static_cast<uint32_t>(take);
+    eq_base += sh.wave_eq[v];
+  }
+  int32_t* kept = p.kept_idx + static_cast<int64_t>(u) * p.k_total;
+  uint8_t* mask = (p.keep_mask != nullptr) ? p.keep_mask + static_cast<int64_t>(u) * p.n_total : nullptr;
+  for (int i0 = s_beg; i0 < s_end; i0 += 64) {
+    const int i = i0 + lane;
+    const uint32_t key = (i < s_end) ? ks[i] : 0u;
+    const bool is_eq = key != 0u && key == T;
+    const bool is_gt = key != 0u && key > T;
+    const uint64_t beq = __ballot(is_eq);
+    const uint32_t eq_rank = eq_base + __popcll(beq & lanemask_lt(lane));
+    const bool sel = is_gt || (is_eq && static_cast<int32_t>(eq_rank) < remaining);
+    const uint64_t bsel = __ballot(sel);
+    const uint32_t pos = sel_base + __popcll(bsel & lanemask_lt(lane));
+    const int64_t g = j0 + i;
+    if (sel) kept[fsum + pos] = static_cast<int32_t>(g);
+    if (mask != nullptr && i < s_end) {
+      const bool forced = g < sink_end || g >= rec_begin;
+      mask[g] = (sel || (forced && alive(g))) ? 1 : 0;
+    }
+    eq_base += __popcll(beq);
+    sel_base += __popcll(bsel);
+  }
+  if (slice != 0) return;
+  // forced entries: alive sink first, alive recent after the selected ones
+  if (wave == 0) {
+    uint32_t r = 0;
+    for (int64_t g0 = 0; g0 < sink_end; g0 += 64) {
+      const int64_t g = g0 + lane;
+      const bool a = g < sink_end && alive(g);
+      const uint64_t b = __ballot(a);
+      if (a) kept[r + __popcll(b & lanemask_lt(lane))] = static_cast<int32_t>(g);
+      r += __popcll(b);
+    }
+  } else if (wave == 1) {
+    uint32_t r = fsum + n_sel_total;
+    for (int64_t g0 = rec_begin; g0 < p.n_total; g0 += 64) {
+      const int64_t g = g0 + lane;
+      const bool a = g < p.n_total && alive(g);
+      const uint64_t b = __ballot(a);
+      if (a) kept[r + __popcll(b & lanemask_lt(lane))] = static_cast<int32_t>(g);
+      r += __popcll(b);
+    }
+  }
+  const int64_t total = static_cast<int64_t>(fsum) + n_sel_total + rsum;
+  for (int64_t i = total + tid; i < p.k_total; i += kPrepThreads) kept[i] = -1;
+  if (tid == 0 && p.n_kept != nullptr) p.n_kept[u] = static_cast<int32_t>(total);
+}
+
+static bool select_slice_path(const SelectParams& p) {
+  return p.cand_count == nullptr && p.U <= kSliceMaxUnits && p.n > 32 * kThreads;
+}
+
 static bool select_single_launch(const SelectParams& p) {
   return p.cand_count == nullptr && p.n > 0 && p.n <= 32 * kThreads && (p.U >= kFusedMinUnits || p.n <= kFusedSmallN) &&
          (p.pool == KVSEL_POOL_NONE || p.pool_k == 1 || (p.pool == KVSEL_POOL_MAX && p.pool_k / 2 <= kFusedMaxPoolR) ||
@@ -791,11 +1059,21 @@ static bool select_single_launch(const SelectParams& p) {
          p.slot_map == nullptr;
 }
 
+// Bytes of the slice-parallel path's buffers after the keys and the top-byte
+// histograms: two more digit histograms, the per-step state and the counts.
+static int64_t slice_extra_bytes(const SelectParams& p, int64_t slices) {
+  const int64_t hist = (static_cast<int64_t>(p.U) * slices * 256 * 4 + 255) / 256 * 256;
+  const int64_t state = (static_cast<int64_t>(4) * p.U * kSliceState * 4 + 255) / 256 * 256;
+  const int64_t counts = (static_cast<int64_t>(p.U) * slices * 2 * 4 + 255) / 256 * 256;
+  return 2 * hist + state + counts;
+}
+
 size_t select_workspace_bytes(const SelectParams& p) {
   if (p.U == 0 || p.n == 0 || select_single_launch(p) || select_tile_fits(p)) return 0;
   const int64_t slices = ceil_div(p.n, kPrepKeys);
   const int64_t key_bytes = (static_cast<int64_t>(p.U) * p.n * 4 + 255) / 256 * 256;
-  return static_cast<size_t>(key_bytes + static_cast<int64_t>(p.U) * slices * 256 * 4);
+  const int64_t hist0 = (static_cast<int64_t>(p.U) * slices * 256 * 4 + 255) / 256 * 256;
+  return static_cast<size_t>(key_bytes + hist0 + (select_slice_path(p) ? slice_extra_bytes(p, slices) : 0));
 }
 
 hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, hipStream_t st) {
@@ -814,6 +1092,27 @@ hipError_t launch_select(const SelectParams& p, const float* scores, void* ws, h
     if (n_slices > 0) {
       dim3 grid(n_slices, p.U);
       select_keys_kernel<<<grid, kPrepThreads, 0, st>>>(p, scores, keys, hist);
+    }
+    if (select_slice_path(p)) {
+      // few units of long rows: the remaining radix steps spread over the slices
+      uint8_t* base = reinterpret_cast<uint8_t*>(hist) +
+                      (static_cast<int64_t>(p.U) * n_slices * 256 * 4 + 255) / 256 * 256;
+      const int64_t hb = (static_cast<int64_t>(p.U) * n_slices * 256 * 4 + 255) / 256 * 256;
+      const int64_t sb = (static_cast<int64_t>(4) * p.U * kSliceState * 4 + 255) / 256 * 256;
+      SliceWs w;
+      w.keys = keys;
+      w.hist0 = hist;
+      w.hist[0] = reinterpret_cast<uint32_t*>(base);
+      w.hist[1] = reinterpret_cast<uint32_t*>(base + hb);
+      w.state = reinterpret_cast<int32_t*>(base + 2 * hb);
+      w.counts = reinterpret_cast<uint32_t*>(base + 2 * hb + sb);
+      dim3 grid(n_slices, p.U);
+      slice_digit_kernel<<<grid, kPrepThreads, 0, st>>>(p, w, n_slices, 1, w.hist0, w.hist[0]);
+      slice_digit_kernel<<<grid, kPrepThreads, 0, st>>>(p, w, n_slices, 2, w.hist[0], w.hist[1]);
+      slice_digit_kernel<<<grid, kPrepThreads, 0, st>>>(p, w, n_slices, 3, w.hist[1], w.hist[0]);
+      slice_count_kernel<<<grid, kPrepThreads, 0, st>>>(p, w, n_slices, w.hist[0]);
+      slice_place_kernel<<<grid, kPrepThreads, 0, st>>>(p, w, n_slices);
+      return hipGetLastError();
     }
     // up to 32 keys per thread stay in registers; larger units stream their
     // keys from the workspace (64 per thread no longer fit without spilling)

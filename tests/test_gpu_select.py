@@ -62,6 +62,44 @@ def test_select_matches_oracle(U, n, k, n_sink, n_recent, ties):
     _check(s, kept, mask, nk, k, n_sink, n_recent)
 
 
+@pytest.mark.parametrize("case", ["plateau", "all", "forced_only", "dead", "units8", "units9"])
+def test_select_long_rows_of_few_units(case):
+    """Rows longer than 32768 over at most 8 units run the radix steps spread
+    over the 4096-column slices (one launch per step): a plateau of equal
+    keys spanning every slice that the budget cuts part-way (ties ranked by
+    position across slices), a budget that keeps every candidate, a budget
+    the forced set fills exactly, dead slots over several units, and 8 and 9
+    units (the last takes the single-workgroup path).  Kept list, keep mask
+    and count bit for bit against select_topk."""
+    dev = require_gpu()
+    rng = np.random.default_rng(len(case) + 900)
+    U, n, k, n_sink, n_recent = 2, 50001, 6000, 4, 64
+    slot_map, alive, dead = None, None, 0
+    s = rng.standard_normal((U, n)).astype(np.float32)
+    if case == "plateau":
+        k = 30000                                            # the cut falls in slice 9 of 13
+        s = np.where(rng.random((U, n)) < 0.7, np.float32(0.5), s).astype(np.float32)
+        s[:, ::97] = 2.0                                     # a few above the plateau
+    elif case == "all":
+        k = n + 10
+    elif case == "forced_only":
+        k, n_sink, n_recent = 100, 40, 60
+    elif case == "dead":
+        U, dead = 3, n
+        slot_map = np.arange(n, dtype=np.int64)
+        slot_map[rng.choice(n, n // 7, replace=False)] = dead
+        slot_map[[0, 5, n - 1]] = dead                       # dead inside the forced set too
+        alive = slot_map != dead
+    elif case == "units8":
+        U, n = 8, 40000
+        s = (np.round(rng.standard_normal((U, n)) * 4) / 4).astype(np.float32)
+    else:
+        U, n = 9, 40000
+        s = (np.round(rng.standard_normal((U, n)) * 4) / 4).astype(np.float32)
+    kept, mask, nk = _run(dev, s, k, n_sink, n_recent, slot_map, dead)
+    _check(s, kept, mask, nk, k, n_sink, n_recent, alive)
+
+
 def test_select_global_unit_with_dead_slots():
     # the session-memory shape: one unit of 65536 with redirected positions
     dev = require_gpu()
