@@ -58,6 +58,7 @@ KERNEL_SOURCES = {
     "scores_mfma_kernel": "k_window.hip", "lse_valu_kernel": "k_window.hip",
     "scores_valu_kernel": "k_window.hip", "pool1d_kernel": "k_window.hip",
     "select_keys_kernel": "k_select.hip", "select_regs_kernel": "k_select.hip", "select_kernel": "k_select.hip",
+    "slice_digit_kernel": "k_select.hip", "slice_count_kernel": "k_select.hip", "slice_place_kernel": "k_select.hip",
     "select_tile_kernel": "k_select_tile.hip",
     "gather_rows_kernel": "k_gather.hip", "gather_blocks_kernel": "k_gather.hip",
     "incremental_plan_kernel": "k_incremental.hip", "incremental_data_kernel": "k_incremental.hip",
