@@ -91,6 +91,21 @@ def test_noalloc_select_without_scratch_use_and_tiled():
     assert torch.equal(res[0], res[1])
 
 
+def test_noalloc_select_long_rows_of_one_unit():
+    dev = require_gpu()
+    # one unit of 65536 columns with a slot map: the radix steps spread over
+    # the key slices keep their histograms, state and counts in the array;
+    # then a shorter row of two units, whose steps must not read stale state
+    s = _scores(dev, 1, 65536, 5)
+    dead = torch.zeros(65536, dtype=torch.int32, device=dev)
+    dead[::13] = 7
+    ref, got = _both(dev, s, k_total=8192, n_sink=4, n_recent=64, slot_map=dead, dead_slot=7)
+    _same(ref, got)
+    s2 = _scores(dev, 2, 40001, 6)
+    ref, got = _both(dev, s2, k_total=3000, n_sink=2, n_recent=9)
+    _same(ref, got)
+
+
 def test_noalloc_select_rejects_calls_beyond_its_scratch():
     dev = require_gpu()
     # 4 bytes per score: 17M scores need more than the 64 MiB array
