@@ -279,18 +279,23 @@ kvsel_status kvsel_score(const kvsel_score_args* a, void* ws, size_t ws_bytes, v
       WindowParams p{a->L, a->Hq, a->Hkv, a->D, a->W, G, a->N, a->causal ? 1 : 0, scale,
                      a->head_agg, a->row_agg};
       const float* lse = a->lse_in;
+      // the VALU score pass merges the LSE partials itself when the caller
+      // asks for no LSE output (one launch fewer)
+      const bool fuse_lse = !plan.mfma && lse == nullptr && plan.own_lse && !plan.lse_only;
+      const float* part = reinterpret_cast<const float*>(w + plan.part_off);
       if (lse == nullptr) {
         float* lo = plan.own_lse ? reinterpret_cast<float*>(w + plan.lse_off) : a->lse_out;
         if (plan.mfma)
           e = launch_window_lse_mfma(p, a->k_dtype, a->q, a->k, reinterpret_cast<float*>(w + plan.part_off), lo, st);
         else
-          e = launch_window_lse_valu(p, a->k_dtype, a->q, a->k, reinterpret_cast<float*>(w + plan.part_off), lo, st);
+          e = launch_window_lse_valu(p, a->k_dtype, a->q, a->k, reinterpret_cast<float*>(w + plan.part_off),
+                                     fuse_lse ? nullptr : lo, st);
         if (e != hipSuccess) return hip_fail(e, "window lse");
         lse = lo;
       }
       if (plan.lse_only) return finish(hipSuccess, st, "window lse");
       if (plan.mfma) e = launch_window_scores_mfma(p, a->k_dtype, a->q, a->k, lse, dst, st);
-      else e = launch_window_scores_valu(p, a->k_dtype, a->q, a->k, lse, dst, st);
+      else e = launch_window_scores_valu(p, a->k_dtype, a->q, a->k, lse, fuse_lse ? part : nullptr, dst, st);
       if (e != hipSuccess) return hip_fail(e, "window scores");
     } else if (a->mode == KVSEL_SCORE_MEMORY) {
       MemoryParams p{};

@@ -93,11 +93,14 @@ struct WindowParams {
   int head_agg, row_agg;
 };
 
+// VALU window passes.  lse == nullptr: the LSE pass leaves only its chunk
+// partials, and the score pass, given them (partials != nullptr), merges
+// each row's LSE itself (same bits as the combine); else it reads `lse`.
 hipError_t launch_window_lse_valu(const WindowParams& p, int dt, const void* q, const void* k,
                                   float* partials, float* lse, hipStream_t st);
 size_t window_valu_partials_bytes(const WindowParams& p);
 hipError_t launch_window_scores_valu(const WindowParams& p, int dt, const void* q, const void* k,
-                                     const float* lse, float* out, hipStream_t st);
+                                     const float* lse, const float* partials, float* out, hipStream_t st);
 bool window_mfma_supported(const WindowParams& p, int dt);
 size_t window_mfma_partials_bytes(const WindowParams& p);
 hipError_t launch_window_lse_mfma(const WindowParams& p, int dt, const void* q, const void* k,

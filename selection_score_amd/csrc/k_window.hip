@@ -129,14 +129,41 @@ __global__ __launch_bounds__(64) void lse_valu_kernel(WindowParams p, const void
   }
 }
 
+// One row's LSE (natural log) from its chunks' (max, sum) partials (log2
+// domain, chunk c at pr[c * stride]): merged online in chunk order, eight
+// loads in flight at a time.  The combine kernel and the fused score-pass
+// prologue both call this, so the value has the same bits either way.
+__device__ __forceinline__ float merge_row_partials(const float2* __restrict__ pr, int n_chunks, int stride) {
+  constexpr int kBatch = 8;
+  float m = -INFINITY, s = 0.f;
+  for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
+    float2 v[kBatch];
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j)
+      v[j] = (c0 + j < n_chunks) ? pr[static_cast<int64_t>(c0 + j) * stride] : make_float2(-INFINITY, 0.f);
+#pragma unroll
+    for (int j = 0; j < kBatch; ++j) {
+      if (v[j].x == -INFINITY) continue;
+      const float mn = fmaxf(m, v[j].x);
+      s = ((m == -INFINITY) ? 0.f : s * exp2f(m - mn)) + v[j].y * exp2f(v[j].x - mn);
+      m = mn;
+    }
+  }
+  return (m + log2f(s)) * kLn2;
+}
+
 // Score pass: a workgroup per (64 keys, unit), one key per lane; its four
 // wavefronts split the window rows (wavefront w takes rows t = w, w + 4, ...)
 // and their per-key row aggregates are combined in wavefront order through
-// LDS, so each lane's dependent chain is a quarter of the window.
+// LDS, so each lane's dependent chain is a quarter of the window.  With the
+// LSE pass's chunk partials given (when the caller wants no LSE
+// output, `lse_part`), each workgroup merges its unit's rows itself instead
+// of reading `lse`, which saves the combine launch.
 template <int DT, int D>
 __global__ __launch_bounds__(256) void scores_valu_kernel(WindowParams p, const void* __restrict__ q,
                                                           const void* __restrict__ k,
                                                           const float* __restrict__ lse,
+                                                          const float2* __restrict__ lse_part, int n_chunks,
                                                           float* __restrict__ out) {
   extern __shared__ float sm[];          // [G*W][D] queries, then [G*W] lse
   __shared__ float part[4][64];
@@ -154,7 +181,9 @@ __global__ __launch_bounds__(256) void scores_valu_kernel(WindowParams p, const 
   }
   for (int r = threadIdx.x; r < R; r += blockDim.x) {
     const int h = g * p.G + r / p.W, t = r % p.W;
-    ls[r] = lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t];
+    ls[r] = (lse_part != nullptr)
+                ? merge_row_partials(lse_part + static_cast<int64_t>(u) * n_chunks * R + r, n_chunks, R)
+                : lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t];
   }
   __syncthreads();
   const int64_t j = static_cast<int64_t>(blockIdx.x) * 64 + lane;
@@ -195,23 +224,28 @@ __global__ __launch_bounds__(256) void scores_valu_kernel(WindowParams p, const 
 
 template <int DT, int D>
 static hipError_t launch_scores_valu_t(const WindowParams& p, const void* q, const void* k,
-                                       const float* lse, float* out, hipStream_t st) {
+                                       const float* lse, const float2* part, int n_chunks, float* out,
+                                       hipStream_t st) {
   const size_t sh = (static_cast<size_t>(p.G) * p.W * D + static_cast<size_t>(p.G) * p.W) * 4;
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&scores_valu_kernel<DT, D>),
                                      hipFuncAttributeMaxDynamicSharedMemorySize,
                                      static_cast<int>(sh));
   if (e != hipSuccess) return e;
   dim3 grid(static_cast<unsigned>(ceil_div(p.N, 64)), static_cast<unsigned>(p.L * p.Hkv));
-  scores_valu_kernel<DT, D><<<grid, 256, sh, st>>>(p, q, k, lse, out);
+  scores_valu_kernel<DT, D><<<grid, 256, sh, st>>>(p, q, k, lse, part, n_chunks, out);
   return hipGetLastError();
 }
 
+static int lse_valu_chunk_keys(const WindowParams& p);
+
 hipError_t launch_window_scores_valu(const WindowParams& p, int dt, const void* q, const void* k,
-                                     const float* lse, float* out, hipStream_t st) {
+                                     const float* lse, const float* partials, float* out, hipStream_t st) {
   if (p.N == 0 || p.L * p.Hkv == 0) return hipSuccess;
+  const float2* part = reinterpret_cast<const float2*>(partials);
+  const int n_chunks = static_cast<int>(ceil_div(p.N, lse_valu_chunk_keys(p)));
 #define KVSEL_SV(DTV)                                                                   \
-  return (p.D == 64) ? launch_scores_valu_t<DTV, 64>(p, q, k, lse, out, st)             \
-                     : launch_scores_valu_t<DTV, 128>(p, q, k, lse, out, st)
+  return (p.D == 64) ? launch_scores_valu_t<DTV, 64>(p, q, k, lse, part, n_chunks, out, st) \
+                     : launch_scores_valu_t<DTV, 128>(p, q, k, lse, part, n_chunks, out, st)
   if (dt == KVSEL_F32) { KVSEL_SV(KVSEL_F32); }
   if (dt == KVSEL_BF16) { KVSEL_SV(KVSEL_BF16); }
   KVSEL_SV(KVSEL_F16);
@@ -457,31 +491,15 @@ void lse_mfma_kernel(WindowParams p, const void* __restrict__ q, const void* __r
 __global__ __launch_bounds__(256) void lse_combine_kernel(WindowParams p, int n_chunks,
                                                           const float2* __restrict__ partials,
                                                           float* __restrict__ lse) {
-  constexpr int kBatch = 8;
   const int R = p.G * p.W;
   const int64_t i = static_cast<int64_t>(blockIdx.x) * blockDim.x + threadIdx.x;
   const int64_t n = static_cast<int64_t>(p.L) * p.Hkv * R;
   if (i >= n) return;
   const int64_t u = i / R;
   const int r = static_cast<int>(i % R);
-  const float2* pr = partials + u * n_chunks * R + r;
-  float m = -INFINITY, s = 0.f;
-  for (int c0 = 0; c0 < n_chunks; c0 += kBatch) {
-    float2 v[kBatch];
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j)
-      v[j] = (c0 + j < n_chunks) ? pr[static_cast<int64_t>(c0 + j) * R] : make_float2(-INFINITY, 0.f);
-#pragma unroll
-    for (int j = 0; j < kBatch; ++j) {
-      if (v[j].x == -INFINITY) continue;
-      const float mn = fmaxf(m, v[j].x);
-      s = ((m == -INFINITY) ? 0.f : s * exp2f(m - mn)) + v[j].y * exp2f(v[j].x - mn);
-      m = mn;
-    }
-  }
   const int l = static_cast<int>(u / p.Hkv), g = static_cast<int>(u % p.Hkv);
   const int h = g * p.G + r / p.W, t = r % p.W;
-  lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t] = (m + log2f(s)) * kLn2;
+  lse[(static_cast<int64_t>(l) * p.Hq + h) * p.W + t] = merge_row_partials(partials + u * n_chunks * R + r, n_chunks, R);
 }
 
 // ---- pass 2: recovered probabilities summed over the unit's rows, per key
@@ -649,13 +667,14 @@ size_t window_valu_partials_bytes(const WindowParams& p) {
 template <int DT, int D>
 static hipError_t launch_lse_valu_t(const WindowParams& p, const void* q, const void* k, float2* part,
                                     float* lse, hipStream_t st) {
+  // lse == nullptr: the partials only (the score pass merges them)
   const int ck = lse_valu_chunk_keys(p);
   const int n_chunks = static_cast<int>(ceil_div(p.N, ck));
   const int U = p.L * p.Hkv;
   const int groups = static_cast<int>(ceil_div(static_cast<int64_t>(p.G) * p.W, kLseValuRowGroup));
   lse_valu_kernel<DT, D><<<dim3(n_chunks, groups, U), 64, 0, st>>>(p, q, k, ck, part);
   hipError_t e = hipGetLastError();
-  if (e != hipSuccess) return e;
+  if (e != hipSuccess || lse == nullptr) return e;
   const int64_t n = static_cast<int64_t>(U) * p.G * p.W;
   lse_combine_kernel<<<static_cast<int>(ceil_div(n, 256)), 256, 0, st>>>(p, n_chunks, part, lse);
   return hipGetLastError();
