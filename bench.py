@@ -285,8 +285,7 @@ class Tiny:
     step a 1 GiB fill evicts L2 and the Infinity Cache (outside the step's
     events), and ms_per_step is the mean of the steps' own event spans."""
     stages = ["score", "select", "gather"]
-    dominant = ("score", [("lse_valu_kernel", "k_window.hip"), ("scores_valu_kernel", "k_window.hip"),
-                          ("lse_combine_kernel", "k_window.hip")])
+    dominant = ("score", [("lse_valu_kernel", "k_window.hip"), ("scores_valu_kernel", "k_window.hip")])
     score_stage = "score"
     materialise_stages = ["select", "gather"]
     dtype = "f32"
