@@ -23,9 +23,13 @@
 // runs the remaining passes and both sweeps: with up to 32 keys per thread
 // held in registers (select_regs_kernel, untiled calls), otherwise reading
 // the workspace (select_kernel; tiled calls stage their running candidates
-// in LDS ahead of the tile's keys).  Unpooled untiled calls without a slot
-// map, with at least 128 units of up to 32768 columns, skip the first
-// launch: each unit's workgroup reads its scores and makes its keys itself.
+// in LDS ahead of the tile's keys).  Untiled calls without a slot map --
+// unpooled, max-pooled with a window of up to 9, or average-pooled with a
+// window of up to 9 over rows of at most 2048 -- with at least 128 units of
+// up to 32768 columns or with rows of at most 8192 skip the first launch:
+// each unit's workgroup reads its scores, pools them in registers and makes
+// its keys itself.  At most 8 units of rows longer than 32768 spread the
+// later radix steps over the slices as well (slice_*_kernel).
 #include "common.h"
 
 namespace kvsel {
@@ -776,14 +780,6 @@ __global__ __launch_bounds__(NT) void select_regs_kernel(SelectParams p, const f
   if (tid == 0 && p.n_kept != nullptr) p.n_kept[u] = static_cast<int32_t>(total);
 }
 
-// Unpooled untiled calls without a slot map, with rows that fit the
-// registers and either enough units to fill the device or rows short enough
-// that one workgroup reads them at once, run select_regs_kernel alone: each
-// unit's workgroup makes its keys from the scores, so no workspace is used
-// (and a short call saves the second launch's latency).
-// (Pooled rows keep the two launches, whose key kernel spreads the window
-// work over many workgroups.)  An empty row (n = 0, scores possibly NULL)
-// takes the two-launch path, whose per-unit kernel reads no key when n is 0.
 // ---- few units of long untiled rows: the radix passes spread over the
 // 4096-column slices of select_keys_kernel, one launch per step.  Each
 // digit launch sums the previous digit's per-slice histograms in slice
@@ -1052,6 +1048,16 @@ static bool select_slice_path(const SelectParams& p) {
   return p.cand_count == nullptr && p.U <= kSliceMaxUnits && p.n > 32 * kThreads;
 }
 
+// Untiled calls without a slot map, with rows that fit the registers and
+// either enough units to fill the device or rows short enough that one
+// workgroup reads them at once, run select_regs_kernel alone when they are
+// unpooled or their window is short (max up to 9; average up to 9 on rows
+// of at most 2048, summed in the definition's order): each unit's
+// workgroup pools and makes its keys from the scores, so no workspace is
+// used (and a short call saves the second launch's latency).  Longer
+// windows keep the two launches, whose key kernel stages the window's halo
+// in LDS.  An empty row (n = 0, scores possibly NULL) takes the two-launch
+// path, whose per-unit kernel reads no key when n is 0.
 static bool select_single_launch(const SelectParams& p) {
   return p.cand_count == nullptr && p.n > 0 && p.n <= 32 * kThreads && (p.U >= kFusedMinUnits || p.n <= kFusedSmallN) &&
          (p.pool == KVSEL_POOL_NONE || p.pool_k == 1 || (p.pool == KVSEL_POOL_MAX && p.pool_k / 2 <= kFusedMaxPoolR) ||
